@@ -1,0 +1,208 @@
+"""Pins for the oracle GEMM (no GPU).
+
+The oracle (decode then float64 / int64 matmul) is checked against:
+  * brute force with exact rationals (fractions.Fraction) on tiny inputs;
+  * closed forms: all-ones, B = ones (row sums), identity B, permutation B,
+    power-of-two scales;
+  * subset selection (rows / cols) agreeing with the full result.
+A dropped term, a wrong sign or index, or a transposed operand fails one of
+these.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.formats import decode_e4m3, decode_e2m1, decode_e8m0, decode_bf16
+
+
+def _frac_e4m3(c):
+    c = int(c)
+    s = -1 if c & 0x80 else 1
+    e = (c >> 3) & 0xF
+    m = c & 7
+    if e == 0:
+        return s * Fraction(m, 8) * Fraction(1, 2 ** 6)
+    return s * (1 + Fraction(m, 8)) * (Fraction(2) ** (e - 7))
+
+
+def _frac_bf16(bits):
+    # exact value of an IEEE binary32 whose low 16 bits are zero
+    bits = int(bits)
+    s = -1 if bits & 0x8000 else 1
+    e = (bits >> 7) & 0xFF
+    m = bits & 0x7F
+    if e == 0:
+        return s * Fraction(m, 128) * Fraction(2) ** (-126)
+    return s * (1 + Fraction(m, 128)) * Fraction(2) ** (e - 127)
+
+
+def _frac_e2m1(c):
+    return Fraction([0, 1, 2, 3, 4, 6, 8, 12][c & 7], 2) * (-1 if c & 8 else 1)
+
+
+def _brute(A, B, f):
+    M, K = A.shape
+    N = B.shape[0]
+    return [[sum(f(A[m, k]) * f(B[n, k]) for k in range(K)) for n in range(N)] for m in range(M)]
+
+
+def test_int8_bruteforce():
+    rng = np.random.default_rng(1)
+    A = rng.integers(-128, 128, size=(5, 7), dtype=np.int8)
+    B = rng.integers(-128, 128, size=(6, 7), dtype=np.int8)
+    ref = [[sum(int(A[m, k]) * int(B[n, k]) for k in range(7)) for n in range(6)] for m in range(5)]
+    out = oracle.gemm_int8(A, B)
+    assert out.dtype == np.int32
+    assert out.tolist() == ref
+
+
+def test_int8_overflow_detected():
+    A = np.full((1, 2 ** 17 + 2), -128, dtype=np.int8)
+    with pytest.raises(OverflowError):
+        oracle.gemm_int8(A, A)
+
+
+def test_fp8_bruteforce_exact_including_subnormals():
+    rng = np.random.default_rng(2)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    A = rng.choice(finite, size=(4, 9))
+    B = rng.choice(finite, size=(3, 9))
+    A[0, :] = np.arange(1, 10)   # subnormals and small normals
+    ref = _brute(A, B, _frac_e4m3)
+    out = oracle.gemm_fp8(A, B, np.ones(4, np.float32), np.ones(3, np.float32))
+    assert [[Fraction(x) for x in row] for row in out.tolist()] == ref
+
+
+def test_fp8_scales_applied_per_row_and_col():
+    rng = np.random.default_rng(3)
+    A = rng.integers(0, 0x7E, size=(3, 8)).astype(np.uint8)
+    B = rng.integers(0, 0x7E, size=(5, 8)).astype(np.uint8)
+    sa = np.array([0.5, 2.0, 0.25], np.float32)
+    sb = np.array([1.0, 4.0, 0.125, 8.0, 2.0], np.float32)
+    ref = _brute(A, B, _frac_e4m3)
+    out = oracle.gemm_fp8(A, B, sa, sb)
+    for m in range(3):
+        for n in range(5):
+            assert Fraction(out[m, n]) == ref[m][n] * Fraction(float(sa[m])) * Fraction(float(sb[n]))
+
+
+def test_bf16_bruteforce():
+    rng = np.random.default_rng(4)
+    A = (rng.integers(0, 2 ** 16, size=(3, 6)).astype(np.uint16) & 0xBFFF) | 0x3000
+    B = (rng.integers(0, 2 ** 16, size=(4, 6)).astype(np.uint16) & 0xBFFF) | 0x3000
+    ref = _brute(A, B, _frac_bf16)
+    out = oracle.gemm_bf16(A, B)
+    for m in range(3):
+        for n in range(4):
+            assert abs(Fraction(out[m, n]) - ref[m][n]) <= abs(ref[m][n]) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 200)
+
+
+def test_mxfp4_bruteforce():
+    rng = np.random.default_rng(5)
+    M, N, K = 3, 2, 64
+    ca = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+    cb = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    sa = rng.integers(120, 135, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(120, 135, size=(N, K // 32)).astype(np.uint8)
+    pa = ca[:, 0::2] | (ca[:, 1::2] << 4)
+    pb = cb[:, 0::2] | (cb[:, 1::2] << 4)
+    out = oracle.gemm_mxfp4(pa, sa, pb, sb)
+    for m in range(M):
+        for n in range(N):
+            ref = sum(_frac_e2m1(ca[m, k]) * Fraction(2) ** (int(sa[m, k // 32]) - 127)
+                      * _frac_e2m1(cb[n, k]) * Fraction(2) ** (int(sb[n, k // 32]) - 127)
+                      for k in range(K))
+            assert Fraction(out[m, n]) == ref
+
+
+@pytest.mark.parametrize("K", [64, 512, 2048])
+def test_all_ones_closed_form(K):
+    M, N = 16, 32
+    one_i8 = np.ones((M, K), np.int8)
+    assert np.all(oracle.gemm_int8(one_i8, np.ones((N, K), np.int8)) == K)
+    one_fp8 = np.full((M, K), 0x38, np.uint8)
+    r = oracle.gemm_fp8(one_fp8, np.full((N, K), 0x38, np.uint8), np.ones(M, np.float32), np.ones(N, np.float32))
+    assert np.all(r == K)
+    one_bf = np.full((M, K), 0x3F80, np.uint16)
+    assert np.all(oracle.gemm_bf16(one_bf, np.full((N, K), 0x3F80, np.uint16)) == K)
+    # E2M1 code 2 is 1.0; scale 127 is 2^0
+    p = np.full((M, K // 2), 0x22, np.uint8)
+    s = np.full((M, K // 32), 127, np.uint8)
+    assert np.all(oracle.gemm_mxfp4(p, s, np.full((N, K // 2), 0x22, np.uint8),
+                                    np.full((N, K // 32), 127, np.uint8)) == K)
+
+
+def test_power_of_two_scales_closed_form():
+    K = 256
+    a = np.full((4, K), 0x38, np.uint8)
+    b = np.full((8, K), 0x38, np.uint8)
+    sa = np.array([1, 2, 0.5, 4], np.float32)
+    sb = np.array([1, 0.25, 8, 2, 1, 1, 0.5, 16], np.float32)
+    r = oracle.gemm_fp8(a, b, sa, sb)
+    assert np.array_equal(r, K * np.outer(sa.astype(np.float64), sb.astype(np.float64)))
+
+
+def test_b_ones_gives_row_sums():
+    rng = np.random.default_rng(6)
+    a = rng.integers(-8, 9, size=(8, 128), dtype=np.int8)
+    r = oracle.gemm_int8(a, np.ones((16, 128), np.int8))
+    assert np.array_equal(r, np.repeat(a.astype(np.int64).sum(1, keepdims=True), 16, 1))
+    af = rng.integers(0, 0x7E, size=(8, 128)).astype(np.uint8)
+    rf = oracle.gemm_fp8(af, np.full((16, 128), 0x38, np.uint8), np.ones(8, np.float32), np.ones(16, np.float32))
+    assert np.array_equal(rf[:, 3], decode_e4m3(af).sum(1))
+
+
+def test_constant_rows_of_a_give_scaled_col_sums():
+    rng = np.random.default_rng(7)
+    b = rng.integers(-8, 9, size=(16, 64), dtype=np.int8)
+    c = np.arange(-4, 4, dtype=np.int8)
+    a = np.repeat(c[:, None], 64, 1)
+    r = oracle.gemm_int8(a, b)
+    assert np.array_equal(r, np.outer(c.astype(np.int64), b.astype(np.int64).sum(1)))
+
+
+def test_identity_b_returns_a():
+    rng = np.random.default_rng(8)
+    K = 64
+    a = rng.integers(0, 0x7E, size=(5, K)).astype(np.uint8)
+    eye = np.where(np.eye(K, dtype=bool), 0x38, 0x00).astype(np.uint8)
+    r = oracle.gemm_fp8(a, eye, np.ones(5, np.float32), np.ones(K, np.float32))
+    assert np.array_equal(r, decode_e4m3(a))
+    ab = (rng.integers(0, 2 ** 16, size=(5, K)).astype(np.uint16) & 0xBFFF)
+    eyeb = np.where(np.eye(K, dtype=bool), 0x3F80, 0).astype(np.uint16)
+    assert np.array_equal(oracle.gemm_bf16(ab, eyeb), decode_bf16(ab))
+
+
+def test_permutation_b_selects_columns_of_a():
+    rng = np.random.default_rng(9)
+    K, N = 64, 48
+    perm = rng.integers(0, K, size=N)
+    a = rng.integers(-8, 9, size=(7, K), dtype=np.int8)
+    b = np.zeros((N, K), np.int8)
+    b[np.arange(N), perm] = 1
+    assert np.array_equal(oracle.gemm_int8(a, b), a[:, perm].astype(np.int32))
+
+
+def test_row_col_subset_matches_full():
+    rng = np.random.default_rng(10)
+    a = rng.integers(0, 0x7E, size=(20, 64)).astype(np.uint8)
+    b = rng.integers(0, 0x7E, size=(30, 64)).astype(np.uint8)
+    sa = rng.random(20).astype(np.float32)
+    sb = rng.random(30).astype(np.float32)
+    full = oracle.gemm_fp8(a, b, sa, sb)
+    rows, cols = [3, 0, 19], [29, 5, 5, 1]
+    assert np.array_equal(oracle.gemm_fp8(a, b, sa, sb, rows, cols), full[np.ix_(rows, cols)])
+
+
+def test_mxfp4_scale_blocks_are_32_wide():
+    # a scale change in block 1 must affect exactly elements 32..63
+    K = 128
+    codes = np.full((1, K), 2, np.uint8)                 # all 1.0
+    p = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    sa = np.array([[127, 130, 127, 127]], np.uint8)      # block 1 scaled by 8
+    sb = np.full((1, 4), 127, np.uint8)
+    r = oracle.gemm_mxfp4(p, sa, p, sb)
+    assert r[0, 0] == 32 + 32 * 8 + 32 + 32
+    assert decode_e8m0(np.uint8(130)) == 8.0 and decode_e2m1(2) == 1.0
