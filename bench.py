@@ -1,0 +1,202 @@
+"""Benchmark of the preshuffle GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
+
+A step is one GEMM call (A, preshuffled B and scales already resident in
+HBM) on the workload's synthetic inputs. The default workload is the FP8
+small-batch GEMM M=16, N=7168, K=2048, whose metric is HBM GB/s; the
+compute-bound workloads report TFLOP/s. To keep B from being served by the
+256 MB last-level cache, each step uses the next of R device-resident copies
+of the inputs, with R large enough that the copies together exceed 640 MB.
+
+One JSON line per workload carries the throughput, the roofline of the GEMM
+kernel (measured with HIP events on the launch stream over the timed
+region), the B preshuffle pass timed separately (a one-time weight
+preparation that the pages keep outside the per-call path), and the CPU
+oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+from oracle import formulas as F  # noqa: E402
+
+METRIC = "GEMM TFLOPS and % of dtype MFMA peak (large M); HBM GB/s and % at M=16"
+DEFAULT_WORKLOAD = "fp8_16x7168x2048"
+# MI355X published dense peaks (TFLOP/s or TOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"int8": 5000.0, "fp8": 5000.0, "bf16": 2500.0, "mxfp4": 10100.0}
+PEAK_HBM_GBPS = 8000.0
+DTYPE_NAME = {"int8": "i8", "fp8": "f8e4m3", "bf16": "bf16", "mxfp4": "mxfp4_e2m1"}
+ROTATE_BYTES = 640 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def workload_numbers(name):
+    dtype, M, N, K, seed, tile = workloads.CONFIGS[name]
+    out_bytes = 4 if dtype == "int8" else 2
+    flops = F.flops(M, N, K)
+    nbytes = F.bytes_moved(dtype, M, N, K, out_bytes=out_bytes)
+    ridge = PEAK_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    bound = "hbm" if flops / nbytes < ridge else "mfma"
+    return dtype, M, N, K, seed, flops, nbytes, bound
+
+
+def cpu_baseline(name, host, budget_s=12.0):
+    """Time the oracle (as it is) on a bounded sample of the workload."""
+    import oracle
+
+    dtype, M, N, K, seed, flops, nbytes, bound = workload_numbers(name)
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    # sample: a block of rows (all columns) sized to about one second per call
+    per_row = 2.0 * N * K
+    rows = int(min(M, max(16, 2e10 / per_row)))
+    sel = np.arange(rows)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemm(dtype, host, rows=sel)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or (calls >= 1 and el * (calls + 1) / calls > 2 * budget_s):
+            break
+    frac = rows / M
+    per_call_s = el / calls
+    if bound == "hbm":
+        value = nbytes * frac / per_call_s / 1e9
+        unit = "GB/s"
+    else:
+        value = flops * frac / per_call_s / 1e12
+        unit = "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows} of {M} rows x all {N} columns, K={K}, {calls} call(s) in {el:.1f} s "
+                      f"(decode + float64 matmul)"}
+
+
+def bench_one(name, steps, warmup, do_cpu=True, opts=None):
+    import torch
+
+    import dense_gemm_preshuffle_amd as gp
+    from dense_gemm_preshuffle_amd import workload
+
+    dtype, M, N, K, seed, flops, nbytes, bound = workload_numbers(name)
+    plan = gp.gemm_plan(dtype, M, N, K, opts)
+    log(f"[bench] {name}: plan {plan}")
+    host = workloads.make_inputs(dtype, M, N, K, seed)
+    dev = workload.to_device(dtype, host)
+    stream = torch.cuda.current_stream()
+
+    # preshuffle pass, timed on its own
+    p0 = workload.prepare(dtype, dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record(stream)
+    for _ in range(reps):
+        gp.gemm_preshuffle_b(dev["b"], dtype, out=p0["b_shuf"])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pre_us = e0.elapsed_time(e1) * 1e3 / reps
+    b_bytes = dev["b"].numel() * dev["b"].element_size()
+
+    # rotation copies so that every step reads its operands from HBM
+    set_bytes = nbytes
+    R = max(1, min(64, math.ceil(ROTATE_BYTES / set_bytes)))
+    sets = [p0]
+    for _ in range(R - 1):
+        q = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in p0.items()}
+        sets.append(q)
+    outs = [workload.run(dtype, s, opts=opts) for s in sets]
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: {R} rotating input sets, {set_bytes / 2**20:.1f} MiB each")
+
+    for i in range(warmup):
+        workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R])
+    torch.cuda.synchronize()
+
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+    sec = ms_per_step / 1e3
+
+    tflops = flops / sec / 1e12
+    gbps = nbytes / sec / 1e9
+    if bound == "hbm":
+        value, unit = gbps, "GB/s"
+        roof = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": gbps / PEAK_HBM_GBPS, "traffic": None}
+    else:
+        value, unit = tflops, "TFLOP/s"
+        pk = PEAK_TFLOPS[dtype]
+        roof = {"bound": "mfma", "achieved": tflops, "peak": pk, "unit": "TFLOP/s",
+                "frac": tflops / pk, "traffic": None}
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE_NAME[dtype], "data": "synthetic",
+        "config": {"workload": name, "M": M, "N": N, "K": K, "kernel": plan["kernel"],
+                   "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]], "grid": plan["grid"],
+                   "epilogue": plan["epilogue"], "rotating_sets": R},
+        "roofline": roof,
+        "tflops": tflops, "gbps": gbps, "us_per_gemm": sec * 1e6,
+        "preshuffle_b": {"us": pre_us, "GB/s": 2 * b_bytes / (pre_us * 1e-6) / 1e9,
+                         "note": "one-time B layout pass, not in the timed step"},
+        "host_wall_s": wall,
+    }
+    if do_cpu:
+        line["cpu_baseline"] = cpu_baseline(name, host)
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="one of %s, or 'all'" % ", ".join(sorted(workloads.CONFIGS)))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--opts", default=None, help="JSON gemm_opts override, e.g. '{\"tile_m\":64,...}'")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the GEMM here runs on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    names = sorted(workloads.CONFIGS) if args.workload == "all" else [args.workload]
+    opts = json.loads(args.opts) if args.opts else None
+    for name in names:
+        line = bench_one(name, args.steps, args.warmup, do_cpu=not args.no_cpu_baseline, opts=opts)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,374 @@
+// Host side of the preshuffle GEMM library: argument validation, the tile
+// planner, the B preshuffle kernel and the exported C entry points.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/gemm_preshuffle.h"
+#include "launch.hpp"
+#include "variants.hpp"
+
+namespace gp {
+namespace {
+
+constexpr int64_t kMaxBytes = (int64_t)1 << 31;  // 32-bit buffer offsets
+
+int elem_bits(int dt) {
+  switch (dt) {
+    case GP_I8:
+    case GP_FP8_E4M3: return 8;
+    case GP_BF16: return 16;
+    case GP_FP4_E2M1: return 4;
+    default: return 0;
+  }
+}
+
+// Kernel-side dtype tag of an input gp_dtype.
+int kdt(int dt) {
+  switch (dt) {
+    case GP_I8: return DT_I8;
+    case GP_FP8_E4M3: return DT_FP8;
+    case GP_BF16: return DT_BF16;
+    default: return DT_FP4;
+  }
+}
+
+struct TileVar { int dt, tm, tn, tkb; };
+struct SplitVar { int dt, nb, waves, kch; };
+
+#define GP_TILE_ENTRY(DT, TM, TN, TKB) {DT, TM, TN, TKB},
+#define GP_SPLIT_ENTRY(DT, NB, W, KCH) {DT, NB, W, KCH},
+constexpr TileVar kTiles[] = {GP_TILE_ALL(GP_TILE_ENTRY)};
+constexpr SplitVar kSplits[] = {GP_SPLITK_ALL(GP_SPLIT_ENTRY)};
+
+bool tile_compiled(int dt, int tm, int tn, int tkb) {
+  for (const auto& v : kTiles)
+    if (v.dt == dt && v.tm == tm && v.tn == tn && v.tkb == tkb) return true;
+  return false;
+}
+bool split_compiled(int dt, int nb, int waves, int kch) {
+  for (const auto& v : kSplits)
+    if (v.dt == dt && v.nb == nb && v.waves == waves && v.kch == kch) return true;
+  return false;
+}
+
+struct Plan {
+  int kernel = 0;
+  int tm = 0, tn = 0, tkb = 0;  // tile kernel (tkb in bytes)
+  int epi = EPI_DIRECT;
+  int xcd = 1;
+  int nb = 0, waves = 4, kch = 0;  // split-K kernel
+  int64_t Kb = 0;
+};
+
+int kernel_mfma_kb(int dt) { return dt == DT_FP8 ? 128 : 64; }
+
+// Default tile preference (largest first) per input type, tile_k in bytes.
+// Named shapes: FP8 medium 64x256x128 (GEMM Optimization Guide §1.3), BF16
+// large 128x256x64 elements, FP4 64-128 x 256 x 256 elements.
+int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
+  struct Cand { int tm, tn, tkb; };
+  static const Cand i8[] = {{128, 256, 128}, {64, 256, 128}, {64, 128, 128}, {128, 128, 128},
+                            {64, 64, 128}, {32, 64, 128}, {16, 64, 256}};
+  static const Cand fp8[] = {{128, 256, 128}, {64, 256, 128}, {32, 256, 128}, {128, 128, 128},
+                             {64, 128, 128}, {16, 64, 512}};
+  static const Cand bf16[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {64, 128, 128},
+                              {128, 256, 64}};
+  static const Cand fp4[] = {{128, 256, 128}, {64, 256, 128}, {32, 256, 128}, {128, 128, 128},
+                             {64, 128, 128}};
+  const Cand* list;
+  int n;
+  switch (dt) {
+    case DT_I8: list = i8; n = sizeof(i8) / sizeof(Cand); break;
+    case DT_FP8: list = fp8; n = sizeof(fp8) / sizeof(Cand); break;
+    case DT_BF16: list = bf16; n = sizeof(bf16) / sizeof(Cand); break;
+    default: list = fp4; n = sizeof(fp4) / sizeof(Cand); break;
+  }
+  // First choice: the largest tile that still gives >= 256 workgroups (one
+  // per CU); otherwise the dividing tile with the most workgroups.
+  int best = -1;
+  int64_t best_grid = -1;
+  for (int i = 0; i < n; ++i) {
+    const Cand& c = list[i];
+    if (M % c.tm || N % c.tn || Kb % c.tkb) continue;
+    const int64_t g = (M / c.tm) * (N / c.tn);
+    if (g >= 256) { best = i; break; }
+    if (g > best_grid) { best_grid = g; best = i; }
+  }
+  if (best < 0) return GP_ESHAPE;
+  p->tm = list[best].tm;
+  p->tn = list[best].tn;
+  p->tkb = list[best].tkb;
+  return GP_OK;
+}
+
+int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, const gemm_opts* o) {
+  const int waves = (o && o->waves > 0) ? o->waves : 4;
+  int nb = (o && o->tile_n > 0) ? o->tile_n / 16 : 0;
+  if (o && o->tile_k > 0 && ((int64_t)o->tile_k * bits) % 8) return GP_ESHAPE;
+  int kch = (o && o->tile_k > 0) ? (int)((int64_t)o->tile_k * bits / 8) : 0;
+  if (o && o->tile_n > 0 && o->tile_n % 16) return GP_ESHAPE;
+  if (o && o->tile_m > 0 && o->tile_m != 16) return GP_ESHAPE;
+  if (Kb % waves) return GP_ESHAPE;
+  const int64_t kw = Kb / waves;
+  if (nb == 0) nb = 1;
+  if (kch == 0) {
+    // largest compiled chunk that divides the wave's K range
+    for (const auto& v : kSplits)
+      if (v.dt == dt && v.nb == nb && v.waves == waves && kw % v.kch == 0 && v.kch > kch) kch = v.kch;
+    if (kch == 0) return GP_ESHAPE;
+  }
+  if (!split_compiled(dt, nb, waves, kch)) return GP_ESHAPE;
+  if (kw % kch || N % (16 * nb) || M % 16) return GP_ESHAPE;
+  p->nb = nb;
+  p->waves = waves;
+  p->kch = kch;
+  return GP_OK;
+}
+
+int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o, Plan* p) {
+  if (M <= 0 || N <= 0 || K <= 0) return GP_EINVAL;
+  const int bits = elem_bits(in_dtype);
+  if (bits == 0) return GP_EDTYPE;
+  if (o) {
+    if (o->tile_m < 0 || o->tile_n < 0 || o->tile_k < 0 || o->waves < 0) return GP_EINVAL;
+    if (o->epilogue < 0 || o->epilogue > 2 || o->kernel < 0 || o->kernel > 2) return GP_EINVAL;
+    if (o->xcd_swizzle < 0 || o->xcd_swizzle > 2) return GP_EINVAL;
+  }
+  if ((K * bits) % 8) return GP_ESHAPE;
+  const int64_t Kb = K * bits / 8;
+  if (N % 16 || Kb % 64 || M % 16) return GP_ESHAPE;
+  if (in_dtype == GP_FP4_E2M1 && K % 128) return GP_ESHAPE;
+  const int ob = in_dtype == GP_I8 ? 4 : 2;
+  if (M * Kb >= kMaxBytes || N * Kb >= kMaxBytes || M * N * ob >= kMaxBytes) return GP_ESHAPE;
+  const int dt = kdt(in_dtype);
+  p->Kb = Kb;
+  p->kernel = (o && o->kernel) ? o->kernel : (M <= 32 ? GP_KERNEL_SPLITK : GP_KERNEL_TILE);
+  if (p->kernel == GP_KERNEL_SPLITK) return choose_split(dt, bits, M, N, Kb, p, o);
+
+  const bool user_tile = o && (o->tile_m || o->tile_n || o->tile_k);
+  if (user_tile) {
+    if (!(o->tile_m && o->tile_n && o->tile_k)) return GP_EINVAL;
+    if (((int64_t)o->tile_k * bits) % 8) return GP_ESHAPE;
+    p->tm = o->tile_m;
+    p->tn = o->tile_n;
+    p->tkb = (int)((int64_t)o->tile_k * bits / 8);
+    if (!tile_compiled(dt, p->tm, p->tn, p->tkb)) return GP_ESHAPE;
+    if (M % p->tm || N % p->tn || Kb % p->tkb) return GP_ESHAPE;
+  } else {
+    const int r = choose_tile(dt, M, N, Kb, p);
+    if (r) return r;
+  }
+  p->epi = (o && o->epilogue) ? o->epilogue : EPI_DIRECT;
+  p->xcd = (o && o->xcd_swizzle) ? o->xcd_swizzle : 1;
+  return GP_OK;
+}
+
+void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gemm_plan_info* out) {
+  std::memset(out, 0, sizeof(*out));
+  const int bits = elem_bits(in_dtype);
+  const int dt = kdt(in_dtype);
+  const int kbm = kernel_mfma_kb(dt);
+  const int64_t kinstr = (int64_t)kbm * 8 / bits;   // K elements per MFMA
+  out->kernel = p.kernel;
+  out->mfma_total = (M / 16) * (N / 16) * (K / kinstr);
+  out->xcd_swizzle = p.kernel == GP_KERNEL_TILE ? p.xcd : 2;
+  if (p.kernel == GP_KERNEL_TILE) {
+    out->tile_m = p.tm;
+    out->tile_n = p.tn;
+    out->tile_k = (int)((int64_t)p.tkb * 8 / bits);
+    out->epilogue = p.epi;
+    out->waves = 4;
+    out->threads = 256;
+    const int ob = in_dtype == GP_I8 ? 4 : 2;
+    const int abuf = 2 * p.tm * p.tkb;
+    const int cbytes = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
+    out->lds_bytes = abuf > cbytes ? abuf : cbytes;
+    out->grid = (M / p.tm) * (N / p.tn);
+    out->k_tiles = p.Kb / p.tkb;
+    out->mfma_per_wave_tile = (int64_t)(p.tkb / kbm) * (p.tm / 16) * (p.tn / 64);
+  } else {
+    out->tile_m = 16;
+    out->tile_n = 16 * p.nb;
+    out->tile_k = (int)((int64_t)p.kch * 8 / bits);
+    out->epilogue = GP_EPI_DIRECT;
+    out->waves = p.waves;
+    out->threads = 64 * p.waves;
+    out->lds_bytes = p.waves * p.nb * 64 * 16;
+    out->grid = (N / (16 * p.nb)) * (M / 16);
+    out->k_tiles = p.Kb / p.waves / p.kch;
+    out->mfma_per_wave_tile = (int64_t)(p.kch / kbm) * p.nb;
+  }
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_arch[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GP_EHIP;
+  if (dev < 0 || dev >= 64) return GP_EHIP;
+  int v = g_arch[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GP_EHIP;
+    v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? GP_OK : GP_EARCH;
+}
+
+int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void* sa, const void* sb,
+           void* c, int64_t M, int64_t N, hipStream_t s) {
+  const int dt = kdt(in_dtype);
+  hipError_t e;
+  if (p.kernel == GP_KERNEL_TILE) {
+    TileArgs t;
+    t.a = (const char*)a;
+    t.b = (const char*)b;
+    t.sa = sa;
+    t.sb = sb;
+    t.c = (char*)c;
+    t.M = (uint32_t)M;
+    t.N = (uint32_t)N;
+    t.Kb = (uint32_t)p.Kb;
+    t.tiles_m = (uint32_t)(M / p.tm);
+    t.tiles_n = (uint32_t)(N / p.tn);
+    t.xcd = p.xcd == 1 ? 1u : 0u;
+    switch (dt) {
+      case DT_I8: e = launch_tile_i8(p.tm, p.tn, p.tkb, p.epi, t, s); break;
+      case DT_FP8: e = launch_tile_fp8(p.tm, p.tn, p.tkb, p.epi, t, s); break;
+      case DT_BF16: e = launch_tile_bf16(p.tm, p.tn, p.tkb, p.epi, t, s); break;
+      default: e = launch_tile_fp4(p.tm, p.tn, p.tkb, p.epi, t, s); break;
+    }
+  } else {
+    SplitArgs t;
+    t.a = (const char*)a;
+    t.b = (const char*)b;
+    t.sa = sa;
+    t.sb = sb;
+    t.c = (char*)c;
+    t.M = (uint32_t)M;
+    t.N = (uint32_t)N;
+    t.Kb = (uint32_t)p.Kb;
+    switch (dt) {
+      case DT_I8: e = launch_splitk_i8(p.nb, p.waves, p.kch, t, s); break;
+      case DT_FP8: e = launch_splitk_fp8(p.nb, p.waves, p.kch, t, s); break;
+      case DT_BF16: e = launch_splitk_bf16(p.nb, p.waves, p.kch, t, s); break;
+      default: e = launch_splitk_fp4(p.nb, p.waves, p.kch, t, s); break;
+    }
+  }
+  return e == hipSuccess ? GP_OK : GP_EHIP;
+}
+
+// B preshuffle: one thread per destination 16-byte chunk (writes coalesced;
+// a wave reads 16 rows x 64 contiguous bytes).
+__global__ __launch_bounds__(256) void preshuffle_kernel(const char* __restrict__ b, char* __restrict__ bs,
+                                                         uint32_t kb64, uint32_t Kb, uint32_t chunks) {
+  const uint32_t q = blockIdx.x * 256u + threadIdx.x;
+  if (q >= chunks) return;
+  const uint32_t j = q & 15u;
+  const uint32_t g = (q >> 4) & 3u;
+  const uint32_t t = q >> 6;
+  const uint32_t k0 = t % kb64;
+  const uint32_t n0 = t / kb64;
+  const size_t src = (size_t)(16u * n0 + j) * Kb + 64u * k0 + 16u * g;
+  *(v4i*)(bs + (size_t)q * 16u) = *(const v4i*)(b + src);
+}
+
+}  // namespace
+}  // namespace gp
+
+using namespace gp;
+
+extern "C" {
+
+const char* gemm_status_string(int status) {
+  switch (status) {
+    case GP_OK: return "ok";
+    case GP_EINVAL: return "invalid argument (null/misaligned pointer, non-positive size or bad option)";
+    case GP_ESHAPE: return "shape not supported (layout or tile divisibility, or size limit)";
+    case GP_EDTYPE: return "unsupported dtype or dtype/scale combination";
+    case GP_EARCH: return "current device is not gfx950";
+    case GP_EHIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+int gemm_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* opts, gemm_plan_info* out) {
+  if (!out) return GP_EINVAL;
+  Plan p;
+  const int r = make_plan(in_dtype, M, N, K, opts, &p);
+  if (r) return r;
+  fill_info(in_dtype, M, N, K, p, out);
+  return GP_OK;
+}
+
+int gemm_preshuffle_b(const void* b, void* b_shuf, int64_t N, int64_t K, int dtype, void* stream) {
+  if (!b || !b_shuf || !aligned16(b) || !aligned16(b_shuf) || N <= 0 || K <= 0) return GP_EINVAL;
+  const int bits = elem_bits(dtype);
+  if (bits == 0) return GP_EDTYPE;
+  if ((K * bits) % 8) return GP_ESHAPE;
+  const int64_t Kb = K * bits / 8;
+  if (N % 16 || Kb % 64 || N * Kb >= kMaxBytes) return GP_ESHAPE;
+  const char* bb = (const char*)b;
+  const char* be = bb + N * Kb;
+  const char* sb = (const char*)b_shuf;
+  if (sb < be && bb < sb + N * Kb) return GP_EINVAL;  // overlap
+  const int r = check_device();
+  if (r) return r;
+  const uint32_t chunks = (uint32_t)(N * Kb / 16);
+  hipLaunchKernelGGL(preshuffle_kernel, dim3((chunks + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                     (const char*)b, (char*)b_shuf, (uint32_t)(Kb / 64), (uint32_t)Kb, chunks);
+  return hipGetLastError() == hipSuccess ? GP_OK : GP_EHIP;
+}
+
+int gemm_a8w8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b, void* c,
+              int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, const gemm_opts* opts,
+              void* stream) {
+  if (!a || !b_shuf || !c || !aligned16(a) || !aligned16(b_shuf) || !aligned16(c)) return GP_EINVAL;
+  if (in_dtype == GP_I8) {
+    if (out_dtype != GP_I32 || scale_a || scale_b) return GP_EDTYPE;
+  } else if (in_dtype == GP_FP8_E4M3) {
+    if (out_dtype != GP_BF16 || !scale_a || !scale_b) return GP_EDTYPE;
+    if (!aligned16(scale_a) || !aligned16(scale_b)) return GP_EINVAL;
+  } else {
+    return GP_EDTYPE;
+  }
+  Plan p;
+  int r = make_plan(in_dtype, M, N, K, opts, &p);
+  if (r) return r;
+  r = check_device();
+  if (r) return r;
+  return launch(in_dtype, p, a, b_shuf, scale_a, scale_b, c, M, N, (hipStream_t)stream);
+}
+
+int gemm_bf16(const void* a, const void* b_shuf, void* c, int64_t M, int64_t N, int64_t K,
+              const gemm_opts* opts, void* stream) {
+  if (!a || !b_shuf || !c || !aligned16(a) || !aligned16(b_shuf) || !aligned16(c)) return GP_EINVAL;
+  Plan p;
+  int r = make_plan(GP_BF16, M, N, K, opts, &p);
+  if (r) return r;
+  r = check_device();
+  if (r) return r;
+  return launch(GP_BF16, p, a, b_shuf, nullptr, nullptr, c, M, N, (hipStream_t)stream);
+}
+
+int gemm_mxfp4(const void* a, const uint8_t* scale_a, const void* b_shuf, const uint8_t* scale_b, void* c,
+               int64_t M, int64_t N, int64_t K, const gemm_opts* opts, void* stream) {
+  if (!a || !b_shuf || !c || !scale_a || !scale_b) return GP_EINVAL;
+  if (!aligned16(a) || !aligned16(b_shuf) || !aligned16(c) || !aligned16(scale_a) || !aligned16(scale_b))
+    return GP_EINVAL;
+  Plan p;
+  int r = make_plan(GP_FP4_E2M1, M, N, K, opts, &p);
+  if (r) return r;
+  r = check_device();
+  if (r) return r;
+  return launch(GP_FP4_E2M1, p, a, b_shuf, scale_a, scale_b, c, M, N, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+// Small-M preshuffle GEMM kernel (memory-bound regime) for gfx950.
+//
+// For M of a few 16-row blocks the GEMM is bound by streaming B from HBM
+// (Kernel Tuning Guide §0 "Is the kernel memory-, compute-, or
+// latency-bound?", GEMM Optimization Guide §8.3). The pages' small-batch tile
+// (16 x 64-128 x 256-512, §1.3) walks K sequentially in one workgroup, which
+// leaves few workgroups and few bytes in flight per CU. Here a workgroup owns
+// 16 rows x (16*NB) columns and its WAVES waves split K: each wave issues the
+// loads for its whole K range up front (in chunks of KCH bytes, the next
+// chunk's loads issued before the current chunk's MFMAs), so that most of B
+// is in flight at once. Partial sums are reduced through LDS in a fixed order
+// (deterministic), then scaled, rounded and stored.
+//
+// Operands come straight from global memory in MFMA layout: B from the
+// preshuffled layout (one KiB per 16 columns x 64 K bytes), A as 16 bytes per
+// lane (row lane%16, K piece lane/16), which is L2-resident since every
+// workgroup reads the same few rows.
+#pragma once
+
+#include <type_traits>
+
+#include "gp_common.hpp"
+
+namespace gp {
+
+struct SplitArgs {
+  const char* a;
+  const char* b;
+  const void* sa;
+  const void* sb;
+  char* c;
+  uint32_t M, N, Kb;
+};
+
+template <int DT, int NB, int WAVES, int KCH>
+struct SplitCfg {
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int KB = Traits<DT>::KB;
+  static constexpr int FRAG = Traits<DT>::FRAG;
+  static constexpr int STEPS = KCH / KB;              // MFMA K steps per chunk
+  static constexpr int OB = (DT == DT_I8) ? 4 : 2;
+  static constexpr int NSC = (DT == DT_FP4) ? 1 : 0;
+  static constexpr int LDS = WAVES * NB * 64 * 16;    // partial accumulators
+  static_assert(KCH % KB == 0, "chunk must be whole MFMA steps");
+};
+
+template <int DT, int NB, int WAVES, int KCH>
+__global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
+  using C = SplitCfg<DT, NB, WAVES, KCH>;
+  using Acc = typename Traits<DT>::Acc;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lane_lo = lane & 15;
+  const int lane_hi = lane >> 4;
+
+  const uint32_t Kb = p.Kb;
+  const uint32_t n0 = blockIdx.x * (16 * NB);
+  const uint32_t m0 = blockIdx.y * 16;
+  const uint32_t kw = Kb / WAVES;            // K bytes per wave
+  const uint32_t k_begin = wave * kw;
+  const int chunks = (int)(kw / KCH);
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * Kb, 16 * Kb);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (size_t)n0 * Kb, 16 * NB * Kb);
+  const uint32_t a_off = lane_lo * Kb + lane_hi * 16;
+  uint32_t b_off[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) b_off[nb] = nb * 16 * Kb + lane * 16;
+
+  const uint32_t srow = Kb / 16;
+  __amdgpu_buffer_rsrc_t rsa = make_rsrc(nullptr, 0), rsb = make_rsrc(nullptr, 0);
+  if constexpr (DT == DT_FP4) {
+    rsa = make_rsrc((const char*)p.sa + (size_t)m0 * srow, 16 * srow);
+    rsb = make_rsrc((const char*)p.sb + (size_t)n0 * srow, 16 * NB * srow);
+  }
+
+  v4i af[2][C::STEPS][C::FRAG];
+  v4i bf[2][C::STEPS][NB][C::FRAG];
+  int sa_r[2][C::STEPS * C::NSC + 1 - C::NSC];
+  int sb_r[2][C::STEPS][NB * C::NSC + 1 - C::NSC];
+  Acc acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = Acc{0, 0, 0, 0};
+
+  auto load = [&](auto par_c, int ch) {
+    constexpr int par = decltype(par_c)::value;
+    const uint32_t kb = k_begin + (uint32_t)ch * KCH;  // K byte of this chunk
+#pragma unroll
+    for (int s = 0; s < C::STEPS; ++s)
+#pragma unroll
+      for (int f = 0; f < C::FRAG; ++f)
+        af[par][s][f] = buf_load16(ra, a_off + s * C::KB + f * 64, kb);
+    const uint32_t kblk = (kb / 64) * 1024u;
+#pragma unroll
+    for (int s = 0; s < C::STEPS; ++s)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int f = 0; f < C::FRAG; ++f)
+          bf[par][s][nb][f] = buf_load16(rb, b_off[nb] + (s * (C::KB / 64) + f) * 1024, kblk);
+    if constexpr (DT == DT_FP4) {
+      const uint32_t sbase = kb / 16;  // scale byte of this chunk's first 32-element block
+#pragma unroll
+      for (int s = 0; s < C::STEPS; ++s) {
+        sa_r[par][s] = buf_load4(rsa, lane_lo * srow + s * 4, sbase);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sb_r[par][s][nb] = buf_load4(rsb, (nb * 16 + lane_lo) * srow + s * 4, sbase);
+      }
+    }
+  };
+  auto compute = [&](auto par_c) {
+    constexpr int par = decltype(par_c)::value;
+#pragma unroll
+    for (int s = 0; s < C::STEPS; ++s) {
+      int sy = 0;
+      if constexpr (DT == DT_FP4) sy = sa_r[par][s] >> (8 * lane_hi);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        int sx = 0;
+        if constexpr (DT == DT_FP4) sx = sb_r[par][s][nb] >> (8 * lane_hi);
+        acc[nb] = mfma<DT>(bf[par][s][nb], af[par][s], acc[nb], sx, sy);
+      }
+    }
+  };
+
+  load(std::integral_constant<int, 0>{}, 0);
+  int ch = 0;
+  for (; ch + 2 <= chunks; ch += 2) {
+    load(std::integral_constant<int, 1>{}, ch + 1);
+    compute(std::integral_constant<int, 0>{});
+    if (ch + 2 < chunks) load(std::integral_constant<int, 0>{}, ch + 2);
+    compute(std::integral_constant<int, 1>{});
+  }
+  if (ch < chunks) compute(std::integral_constant<int, 0>{});
+
+  // ---- reduce the WAVES partial sums through LDS in wave order ----
+  Acc* red = (Acc*)lds;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) red[(wave * NB + nb) * 64 + lane] = acc[nb];
+  __syncthreads();
+
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c + ((size_t)m0 * p.N + n0) * C::OB, (15 * p.N + 16 * NB) * C::OB);
+  for (int nb = wave; nb < NB; nb += WAVES) {
+    Acc v = red[nb * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) v += red[(w * NB + nb) * 64 + lane];
+    // lane holds C[m0 + lane_lo][n0 + nb*16 + 4*lane_hi + r]
+    const uint32_t col = nb * 16 + 4 * lane_hi;
+    const uint32_t off = (lane_lo * p.N + col) * C::OB;
+    if constexpr (DT == DT_I8) {
+      buf_store16(v, rc, off);
+    } else {
+      if constexpr (DT == DT_FP8) {
+        const float sa = ((const float*)p.sa)[m0 + lane_lo];
+        const v4f sb = *(const v4f*)((const float*)p.sb + n0 + col);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (v[r] * sa) * sb[r];
+      }
+      v2i o;
+      o[0] = (int)pack_bf16x2(v[0], v[1]);
+      o[1] = (int)pack_bf16x2(v[2], v[3]);
+      buf_store8(o, rc, off);
+    }
+  }
+}
+
+}  // namespace gp

@@ -1,0 +1,313 @@
+// LDS ping-pong tile kernel for the preshuffle GEMM on gfx950.
+//
+// Structure (GEMM Optimization Guide §1-§7, Kernel Tuning Guide §1-§6):
+//   * one workgroup = 4 waves x 64 lanes computes a TM x TN tile of C; the
+//     waves split TN (each owns TN/4 columns) and share the A tile (§1.1);
+//   * A goes global -> VGPR -> LDS, into one of two LDS buffers (ping-pong,
+//     §2), with an XOR swizzle on 16-byte chunks (§3);
+//   * B goes global -> VGPR directly from the preshuffled layout (§4.2): for
+//     one 16-column block and one 64-byte K block a wave reads one
+//     contiguous KiB, lane l taking 16 bytes;
+//   * the next K tile's A and B loads are issued before the current tile's
+//     MFMAs (register double buffer for B, loop-carried, §4.1-§4.4); one
+//     barrier per K tile;
+//   * epilogue: direct store or CShuffle through LDS (§7).
+//
+// Differences from the pages' kernel, for gfx950:
+//   * gfx950 matrix instructions with doubled K: INT8 16x16x64, BF16
+//     16x16x32, FP8 16x16x128 (two 64-byte K blocks per instruction) and the
+//     scaled 16x16x128 FP4 form;
+//   * the MFMA takes B as its first operand and A as its second, so a lane
+//     ends up holding 4 consecutive COLUMNS of one row of C; the direct store
+//     is then one 8-byte (bf16) or 16-byte (int32) store per lane;
+//   * the swizzle folds (row / P) into the chunk index, P = rows per 256-byte
+//     LDS bank period: on 64 banks this makes the 16 rows read by one
+//     16-lane phase hit 16 distinct 16-byte bank groups for every row length.
+#pragma once
+
+#include <type_traits>
+
+#include "gp_common.hpp"
+
+namespace gp {
+
+struct TileArgs {
+  const char* a;      // [M][Kb]
+  const char* b;      // preshuffled [N/16][Kb/64][4][16][16]
+  const void* sa;     // FP8: fp32 [M]; FP4: u8 [M][Kb/16]; else unused
+  const void* sb;     // FP8: fp32 [N]; FP4: u8 [N][Kb/16]; else unused
+  char* c;            // [M][N] int32 or bf16
+  uint32_t M, N, Kb;  // Kb = bytes per row of A and B
+  uint32_t tiles_m, tiles_n;
+  uint32_t xcd;       // 1: XCD-aware, grouped tile order
+};
+
+template <int DT, int TM, int TN, int TKB, int EPI>
+struct TileCfg {
+  static constexpr int THREADS = 256;
+  static constexpr int WAVES = 4;
+  static constexpr int KB = Traits<DT>::KB;
+  static constexpr int FRAG = Traits<DT>::FRAG;
+  static constexpr int KSTEPS = TKB / KB;
+  static constexpr int MREP = TM / 16;
+  static constexpr int NPW = TN / WAVES;
+  static constexpr int NACC = NPW / 16;
+  static constexpr int CPR = TKB / 16;                    // 16-byte chunks per A row
+  static constexpr int ACHUNKS = TM * CPR;
+  static constexpr int ALOADS = (ACHUNKS + THREADS - 1) / THREADS;
+  static constexpr bool APART = (ACHUNKS % THREADS) != 0;
+  static constexpr int ABUF = TM * TKB;
+  static constexpr int OB = (DT == DT_I8) ? 4 : 2;        // output element bytes
+  static constexpr int CSTRIDE = TN * OB + 16;            // padded C row in LDS
+  static constexpr int CBYTES = (EPI == EPI_CSHUFFLE) ? TM * CSTRIDE : 0;
+  static constexpr int LDS = (2 * ABUF > CBYTES) ? 2 * ABUF : CBYTES;
+  static constexpr int SWP = (TKB >= 256) ? 1 : 256 / TKB;  // rows per 256-byte period
+  static constexpr int SWM = ((CPR < 16) ? CPR : 16) - 1;   // chunk xor mask
+  static constexpr int NSC = (DT == DT_FP4) ? 1 : 0;
+  static_assert(TM % 16 == 0 && TN % 64 == 0, "tile_m % 16, tile_n % 64");
+  static_assert(TKB % KB == 0 && TKB >= 64, "tile_k bytes must be a multiple of the MFMA K bytes");
+  static_assert(THREADS % CPR == 0, "A row chunks must divide the workgroup");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uint32_t& tn) {
+  uint32_t w = blockIdx.x;
+  const uint32_t G = p.tiles_m * p.tiles_n;
+  if (p.xcd && (G % 8u) == 0) {
+    // Workgroups go round-robin to the 8 XCDs; give each XCD a contiguous
+    // range of tiles, then walk it in groups of 8 M-tiles so that the tiles
+    // resident together on one XCD share A rows and B columns in its L2.
+    const uint32_t logical = (w % 8u) * (G / 8u) + (w / 8u);
+    const uint32_t GROUP = 8u;
+    const uint32_t per_group = GROUP * p.tiles_n;
+    const uint32_t g = logical / per_group;
+    const uint32_t first_m = g * GROUP;
+    const uint32_t gsz = min(GROUP, p.tiles_m - first_m);
+    const uint32_t r = logical % per_group;
+    tm = first_m + r % gsz;
+    tn = r / gsz;
+  } else {
+    tm = w / p.tiles_n;
+    tn = w % p.tiles_n;
+  }
+}
+
+template <int DT, int TM, int TN, int TKB, int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
+  using C = TileCfg<DT, TM, TN, TKB, EPI>;
+  using Acc = typename Traits<DT>::Acc;
+  __shared__ __attribute__((aligned(16))) char lds[C::LDS];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int lane_lo = lane & 15;
+  const int lane_hi = lane >> 4;
+
+  uint32_t tm, tn;
+  tile_coords(p, tm, tn);
+  const uint32_t m0 = tm * TM;
+  const uint32_t n0 = tn * TN;
+  const uint32_t Kb = p.Kb;
+  const int KT = (int)(Kb / TKB);
+
+  // Buffer resources based at this workgroup's first A row / first B block.
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * Kb, TM * Kb);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (size_t)(n0 / 16) * 16 * Kb, TN * Kb);
+
+  // ---- per-lane constant offsets ----
+  // A global -> LDS: thread tid moves chunk (tid % CPR) of rows tid / CPR + i * (256 / CPR).
+  uint32_t a_ld[C::ALOADS];
+  uint32_t a_wr[C::ALOADS];
+  bool a_on[C::ALOADS];
+#pragma unroll
+  for (int i = 0; i < C::ALOADS; ++i) {
+    const int q = i * C::THREADS + tid;
+    const int row = q / C::CPR;
+    const int ch = q % C::CPR;
+    a_on[i] = !C::APART || q < C::ACHUNKS;
+    a_ld[i] = row * Kb + ch * 16;
+    a_wr[i] = row * TKB + ((ch ^ ((row / C::SWP) & C::SWM)) * 16);
+  }
+  // A LDS -> VGPR: lane reads row mi*16 + lane_lo, chunk s*KB/16 + f*4 + lane_hi.
+  const int swz = (lane_lo / C::SWP) & C::SWM;
+  uint32_t a_rd[C::KSTEPS][C::FRAG];
+#pragma unroll
+  for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+    for (int f = 0; f < C::FRAG; ++f)
+      a_rd[s][f] = lane_lo * TKB + (((s * (C::KB / 16) + f * 4 + lane_hi) ^ swz) * 16);
+  // B: the wave's 16-column blocks, lane's 16 bytes within each KiB.
+  uint32_t b_off[C::NACC];
+#pragma unroll
+  for (int ni = 0; ni < C::NACC; ++ni)
+    b_off[ni] = (uint32_t)(wave * C::NACC + ni) * 16u * Kb + lane * 16;
+
+  // FP4 block scales: one E8M0 byte per 32 K elements (= 16 bytes of K).
+  const uint32_t srow = Kb / 16;  // scale bytes per row
+  __amdgpu_buffer_rsrc_t rsa = make_rsrc(nullptr, 0), rsb = make_rsrc(nullptr, 0);
+  uint32_t sa_off[C::MREP], sb_off[C::NACC];
+  if constexpr (DT == DT_FP4) {
+    rsa = make_rsrc((const char*)p.sa + (size_t)m0 * srow, TM * srow);
+    rsb = make_rsrc((const char*)p.sb + (size_t)n0 * srow, TN * srow);
+#pragma unroll
+    for (int mi = 0; mi < C::MREP; ++mi) sa_off[mi] = (mi * 16 + lane_lo) * srow;
+#pragma unroll
+    for (int ni = 0; ni < C::NACC; ++ni) sb_off[ni] = (wave * C::NPW + ni * 16 + lane_lo) * srow;
+  }
+
+  v4i a_st[C::ALOADS];
+  v4i bfr[2][C::KSTEPS][C::NACC][C::FRAG];
+  int sbr[2][C::KSTEPS][C::NACC * C::NSC + 1 - C::NSC];
+  int sar[2][C::KSTEPS][C::MREP * C::NSC + 1 - C::NSC];
+  Acc acc[C::MREP][C::NACC];
+#pragma unroll
+  for (int mi = 0; mi < C::MREP; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < C::NACC; ++ni) acc[mi][ni] = Acc{0, 0, 0, 0};
+
+  auto load_a = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < C::ALOADS; ++i)
+      if (a_on[i]) a_st[i] = buf_load16(ra, a_ld[i], kt * TKB);
+  };
+  auto store_a = [&](int par) {
+    char* base = lds + par * C::ABUF;
+#pragma unroll
+    for (int i = 0; i < C::ALOADS; ++i)
+      if (a_on[i]) *(v4i*)(base + a_wr[i]) = a_st[i];
+  };
+  auto load_b = [&](auto par_c, int kt) {
+    constexpr int par = decltype(par_c)::value;
+    const uint32_t kbase = (uint32_t)kt * (TKB / 64) * 1024u;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+      for (int ni = 0; ni < C::NACC; ++ni)
+#pragma unroll
+        for (int f = 0; f < C::FRAG; ++f)
+          bfr[par][s][ni][f] = buf_load16(rb, b_off[ni] + (s * (C::KB / 64) + f) * 1024, kbase);
+    if constexpr (DT == DT_FP4) {
+      const uint32_t sbase = (uint32_t)kt * (TKB / 16);
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) {
+#pragma unroll
+        for (int ni = 0; ni < C::NACC; ++ni) sbr[par][s][ni] = buf_load4(rsb, sb_off[ni] + s * 4, sbase);
+#pragma unroll
+        for (int mi = 0; mi < C::MREP; ++mi) sar[par][s][mi] = buf_load4(rsa, sa_off[mi] + s * 4, sbase);
+      }
+    }
+  };
+  auto compute = [&](auto par_c) {
+    constexpr int par = decltype(par_c)::value;
+    const char* base = lds + par * C::ABUF;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
+#pragma unroll
+      for (int mi = 0; mi < C::MREP; ++mi) {
+        v4i af[C::FRAG];
+#pragma unroll
+        for (int f = 0; f < C::FRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * 16 * TKB);
+        int sy = 0;
+        if constexpr (DT == DT_FP4) sy = sar[par][s][mi] >> (8 * lane_hi);
+#pragma unroll
+        for (int ni = 0; ni < C::NACC; ++ni) {
+          int sx = 0;
+          if constexpr (DT == DT_FP4) sx = sbr[par][s][ni] >> (8 * lane_hi);
+          acc[mi][ni] = mfma<DT>(bfr[par][s][ni], af, acc[mi][ni], sx, sy);
+        }
+      }
+    }
+  };
+  auto iter = [&](auto par_c, int kt) {
+    constexpr int par = decltype(par_c)::value;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      load_a(kt + 1);
+      load_b(std::integral_constant<int, par ^ 1>{}, kt + 1);
+    }
+    compute(par_c);
+    if (more) store_a(par ^ 1);
+    __syncthreads();
+  };
+
+  // ---- prologue: tile 0 ----
+  load_a(0);
+  load_b(std::integral_constant<int, 0>{}, 0);
+  store_a(0);
+  __syncthreads();
+
+  // ---- main loop, two K tiles per trip (ping, pong) ----
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    iter(std::integral_constant<int, 0>{}, kt);
+    iter(std::integral_constant<int, 1>{}, kt + 1);
+  }
+  if (kt < KT) iter(std::integral_constant<int, 0>{}, kt);
+
+  // ---- epilogue ----
+  // lane holds C[m0 + mi*16 + lane_lo][n0 + wave*NPW + ni*16 + 4*lane_hi + r], r = 0..3
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c + ((size_t)m0 * p.N + n0) * C::OB, ((TM - 1) * p.N + TN) * C::OB);
+  v4f sbv[C::NACC];
+  float sav[C::MREP];
+  if constexpr (DT == DT_FP8) {
+    const float* sa = (const float*)p.sa + m0;
+    const float* sb = (const float*)p.sb + n0;
+#pragma unroll
+    for (int mi = 0; mi < C::MREP; ++mi) sav[mi] = sa[mi * 16 + lane_lo];
+#pragma unroll
+    for (int ni = 0; ni < C::NACC; ++ni) sbv[ni] = *(const v4f*)(sb + wave * C::NPW + ni * 16 + 4 * lane_hi);
+  }
+  auto out_vec = [&](int mi, int ni, auto emit) {
+    if constexpr (DT == DT_I8) {
+      emit(acc[mi][ni]);
+    } else {
+      v4f v = acc[mi][ni];
+      if constexpr (DT == DT_FP8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (v[r] * sav[mi]) * sbv[ni][r];
+      }
+      v2i o;
+      o[0] = (int)pack_bf16x2(v[0], v[1]);
+      o[1] = (int)pack_bf16x2(v[2], v[3]);
+      emit(o);
+    }
+  };
+
+  if constexpr (EPI == EPI_DIRECT) {
+#pragma unroll
+    for (int mi = 0; mi < C::MREP; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::NACC; ++ni) {
+        const uint32_t off = ((mi * 16 + lane_lo) * p.N + wave * C::NPW + ni * 16 + 4 * lane_hi) * C::OB;
+        out_vec(mi, ni, [&](auto v) {
+          if constexpr (sizeof(v) == 16) buf_store16(v, rc, off);
+          else buf_store8(v, rc, off);
+        });
+      }
+  } else {
+    // CShuffle: stage the tile in LDS (the A buffers are dead after the last
+    // barrier), then write whole rows with 16-byte stores.
+#pragma unroll
+    for (int mi = 0; mi < C::MREP; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::NACC; ++ni) {
+        char* dst = lds + (mi * 16 + lane_lo) * C::CSTRIDE + (wave * C::NPW + ni * 16 + 4 * lane_hi) * C::OB;
+        out_vec(mi, ni, [&](auto v) { *(decltype(v)*)dst = v; });
+      }
+    __syncthreads();
+    constexpr int CH_ROW = TN * C::OB / 16;
+    constexpr int TOTAL = TM * CH_ROW;
+#pragma unroll
+    for (int i = 0; i < (TOTAL + C::THREADS - 1) / C::THREADS; ++i) {
+      const int q = i * C::THREADS + tid;
+      if (TOTAL % C::THREADS != 0 && q >= TOTAL) break;
+      const int row = q / CH_ROW;
+      const int ch = q % CH_ROW;
+      const v4i v = *(const v4i*)(lds + row * C::CSTRIDE + ch * 16);
+      buf_store16(v, rc, row * p.N * C::OB + ch * 16);
+    }
+  }
+}
+
+}  // namespace gp

@@ -1,0 +1,84 @@
+// Shared device helpers for the gfx950 preshuffle GEMM kernels.
+//
+// Vector types, buffer-resource loads/stores, the gfx950 MFMA wrappers for
+// each input type, and the bf16 round-to-nearest-even conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gp {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+enum DType : int { DT_I8 = 0, DT_FP8 = 1, DT_BF16 = 2, DT_FP4 = 3 };
+enum Epi : int { EPI_DIRECT = 1, EPI_CSHUFFLE = 2 };
+
+// gfx9 buffer resource word 3 (32-bit raw buffer, bounds checked on num_records).
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ v2i buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+}
+__device__ __forceinline__ int buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_store16(v4i v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(v2i v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
+}
+
+// Per-type traits. KB = K bytes one MFMA consumes per 16x16 block;
+// FRAG = 16-byte pieces per lane per MFMA (1, or 2 for the FP8 K=128 form).
+template <int DT> struct Traits;
+template <> struct Traits<DT_I8>   { static constexpr int KB = 64;  static constexpr int FRAG = 1; using Acc = v4i; };
+template <> struct Traits<DT_BF16> { static constexpr int KB = 64;  static constexpr int FRAG = 1; using Acc = v4f; };
+template <> struct Traits<DT_FP4>  { static constexpr int KB = 64;  static constexpr int FRAG = 1; using Acc = v4f; };
+template <> struct Traits<DT_FP8>  { static constexpr int KB = 128; static constexpr int FRAG = 2; using Acc = v4f; };
+
+// One 16x16 MFMA step. X supplies the first operand (its lane l gives row l%16,
+// K piece l/16), Y the second. The result in lane l is D[4*(l/16)+r][l%16].
+// sx / sy are the E8M0 block scales of the X / Y lanes (FP4 only).
+template <int DT>
+__device__ __forceinline__ typename Traits<DT>::Acc
+mfma(const v4i* x, const v4i* y, typename Traits<DT>::Acc acc, int sx = 0, int sy = 0) {
+  if constexpr (DT == DT_I8) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(x[0], y[0], acc, 0, 0, 0);
+  } else if constexpr (DT == DT_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x[0]),
+                                                   __builtin_bit_cast(v8bf, y[0]), acc, 0, 0, 0);
+  } else if constexpr (DT == DT_FP8) {
+    v8i xx = __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    v8i yy = __builtin_shufflevector(y[0], y[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    // format 0 = FP8 E4M3 for both operands; constant zero scales select the
+    // unscaled 16x16x128 f8f6f4 instruction.
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xx, yy, acc, 0, 0, 0, 0, 0, 0);
+  } else {
+    v8i xx = __builtin_shufflevector(x[0], x[0], 0, 1, 2, 3, -1, -1, -1, -1);
+    v8i yy = __builtin_shufflevector(y[0], y[0], 0, 1, 2, 3, -1, -1, -1, -1);
+    // format 4 = FP4 E2M1 for both operands; byte 0 of sx / sy is the E8M0 scale.
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xx, yy, acc, 4, 4, 0, sx, 0, sy);
+  }
+}
+
+// fp32 -> bf16 with round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+}  // namespace gp

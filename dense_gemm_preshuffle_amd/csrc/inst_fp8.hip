@@ -1,0 +1,17 @@
+// Kernel instantiations and launch tables for one input type.
+#include "launch.hpp"
+#include "variants.hpp"
+
+namespace gp {
+
+hipError_t launch_tile_fp8(int tm, int tn, int tkb, int epi, const TileArgs& a, hipStream_t s) {
+  GP_TILE_FP8(GP_TILE_CASE)
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_splitk_fp8(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s) {
+  GP_SPLITK_FP8(GP_SPLITK_CASE)
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gp

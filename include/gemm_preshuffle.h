@@ -1,0 +1,170 @@
+/*
+ * gemm_preshuffle.h -- C ABI of the MI355X (gfx950) preshuffle GEMM library.
+ *
+ *   C[M,N] = A[M,K] . B[N,K]^T
+ *
+ * The problem statement is the one of the GEMM Optimization Guide (rocm
+ * gemm-optimization skill), §1.1, read with §12.1 (B is N rows of K contiguous
+ * elements). B is consumed in the preshuffled layout of §1.4 / §12.1; A and C
+ * are plain row-major. Element types follow §6.2: INT8, FP8 (OCP E4M3FN),
+ * BF16 and gfx950 MXFP4 (E2M1 values, one E8M0 scale per 32 K elements).
+ * The FP8 epilogue applies fp32 per-row / per-column scales (§7.1, §8.2).
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every buffer; all data pointers are DEVICE
+ *     pointers (hipMalloc'd or equivalent) unless stated otherwise. The
+ *     library keeps no pointer after the call returns and allocates nothing.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream). Nothing synchronizes; results are ready when the stream
+ *     reaches that point.
+ *   - Layout: A is [M][K] and C is [M][N], row-major, contiguous. Sizes are
+ *     in ELEMENTS; an MXFP4 row of K elements is K/2 bytes (element 2i in
+ *     the low nibble of byte i).
+ *   - Alignment: every data pointer must be 16-byte aligned.
+ *   - Errors: arguments are validated on the host before any HIP call; a
+ *     non-zero gp_status is returned and nothing is launched. A failing
+ *     launch returns GP_EHIP. No C++ exception crosses this interface.
+ *   - Thread safety: no global mutable state besides a per-device cache of
+ *     the device's architecture; calls from several threads are safe.
+ */
+#ifndef GEMM_PRESHUFFLE_H
+#define GEMM_PRESHUFFLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gp_status {
+  GP_OK = 0,
+  GP_EINVAL = 1,  /* null or misaligned pointer, non-positive size, bad option value */
+  GP_ESHAPE = 2,  /* layout or tile divisibility violated, or size over 2^31 bytes   */
+  GP_EDTYPE = 3,  /* unsupported dtype or dtype/scale combination                    */
+  GP_EARCH = 4,   /* the current device is not gfx950                                */
+  GP_EHIP = 5     /* a HIP runtime call or kernel launch failed                      */
+} gp_status;
+
+typedef enum gp_dtype {
+  GP_I8 = 0,        /* int8, two's complement                      */
+  GP_FP8_E4M3 = 1,  /* OCP FP8 E4M3FN (max 448, no infinities)      */
+  GP_BF16 = 2,      /* bfloat16                                     */
+  GP_FP4_E2M1 = 3,  /* OCP MX FP4 E2M1, two per byte, low nibble first */
+  GP_I32 = 4        /* int32 (output of the INT8 path)              */
+} gp_dtype;
+
+enum {
+  GP_EPI_AUTO = 0,      /* planner's choice                                   */
+  GP_EPI_DIRECT = 1,    /* each lane stores its accumulators (GEMM Opt. §7.1) */
+  GP_EPI_CSHUFFLE = 2   /* re-map through LDS for coalesced stores (§7.2)     */
+};
+
+enum {
+  GP_KERNEL_AUTO = 0,
+  GP_KERNEL_TILE = 1,    /* LDS ping-pong tile kernel (GEMM Opt. §1-§7)            */
+  GP_KERNEL_SPLITK = 2   /* small-M kernel: waves of a workgroup split K,
+                            reduced through LDS (for the memory-bound small
+                            batch of GEMM Opt. §1.3 / §8.3)                      */
+};
+
+/* Tuning options. Pass NULL, or a zero-filled struct, for all-automatic;
+ * a zero field means "planner's choice". tile_k is in ELEMENTS (as on the
+ * pages). For the split-K kernel tile_m is 16, tile_n is 16 * (column blocks
+ * per workgroup) and tile_k is the K chunk each wave loads per step. A tile
+ * that is not compiled into the library is GP_ESHAPE. */
+typedef struct gemm_opts {
+  int tile_m, tile_n, tile_k;
+  int epilogue;     /* GP_EPI_*                                          */
+  int kernel;       /* GP_KERNEL_*                                       */
+  int xcd_swizzle;  /* 0 auto, 1 XCD-aware grouped tile order, 2 linear  */
+  int waves;        /* split-K kernel: waves per workgroup (0 auto)      */
+} gemm_opts;
+
+/* What the planner chose (host-side query, no GPU needed). */
+typedef struct gemm_plan_info {
+  int kernel;
+  int tile_m, tile_n, tile_k;       /* tile_k in elements                       */
+  int epilogue;
+  int xcd_swizzle;                  /* 1 XCD-aware, 2 linear                    */
+  int waves;                        /* waves per workgroup                      */
+  int threads;                      /* per workgroup                            */
+  int lds_bytes;                    /* static LDS per workgroup                 */
+  int64_t grid;                     /* workgroups                               */
+  int64_t k_tiles;                  /* K tiles per workgroup (tile kernel)      */
+  int64_t mfma_per_wave_tile;       /* MFMA instructions per wave per K tile    */
+  int64_t mfma_total;               /* MFMA instructions for the whole problem  */
+} gemm_plan_info;
+
+/*
+ * gemm_preshuffle_b -- B preshuffle pass (GEMM Optimization Guide §1.4, §12.1).
+ *
+ * Permutes the bytes of B ([N][Kb] row-major, Kb = K * element bytes) into
+ * the layout [N/16][Kb/64][4][16][16 bytes]:
+ *     b_shuf[(((n0*(Kb/64) + k0)*4 + g)*16 + j)*16 + b] = B[16*n0 + j][64*k0 + 16*g + b]
+ * so that one wave loads a 16-column x 64-byte block as one contiguous KiB,
+ * lane 16*g + j taking one dwordx4. The pages run this once on the CPU; here
+ * it is a device kernel, run once per B and amortised over GEMM calls.
+ *   b       device, [N][Kb] bytes, read only.
+ *   b_shuf  device, N*Kb bytes, written; must not overlap b.
+ *   dtype   GP_I8, GP_FP8_E4M3, GP_BF16 or GP_FP4_E2M1 (fixes Kb; MXFP4
+ *           block scales are NOT shuffled and stay [N][K/32]).
+ * Requires N % 16 == 0, Kb % 64 == 0 (GP_ESHAPE), N*Kb < 2^31.
+ */
+int gemm_preshuffle_b(const void* b, void* b_shuf, int64_t N, int64_t K, int dtype, void* stream);
+
+/*
+ * gemm_a8w8 -- INT8 or FP8 GEMM on preshuffled B.
+ *   a        device, [M][K] int8 / E4M3 codes.
+ *   b_shuf   device, output of gemm_preshuffle_b for the same in_dtype.
+ *   scale_a  device fp32 [M] or NULL; scale_b device fp32 [N] or NULL.
+ *   c        device [M][N]: int32 (out_dtype GP_I32) or bf16 (GP_BF16).
+ * Dtype pairs: in GP_I8 -> out GP_I32 with both scales NULL (exact integer
+ * accumulation); in GP_FP8_E4M3 -> out GP_BF16 with both scales given:
+ *     C[m][n] = bf16_rne((acc[m][n] * scale_a[m]) * scale_b[n]),
+ * acc accumulated in fp32 (GEMM Optimization Guide §7.1). Anything else is
+ * GP_EDTYPE. The chosen tile must divide M, N and K (GP_ESHAPE).
+ */
+int gemm_a8w8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b,
+              void* c, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
+              const gemm_opts* opts, void* stream);
+
+/*
+ * gemm_bf16 -- BF16 GEMM on preshuffled B, fp32 accumulation, bf16 output
+ * rounded to nearest even (GEMM Optimization Guide §6.2, §7).
+ *   a [M][K] bf16, b_shuf from gemm_preshuffle_b(GP_BF16), c [M][N] bf16.
+ */
+int gemm_bf16(const void* a, const void* b_shuf, void* c, int64_t M, int64_t N, int64_t K,
+              const gemm_opts* opts, void* stream);
+
+/*
+ * gemm_mxfp4 -- MXFP4 GEMM with gfx950 scaled MFMA (GEMM Optimization Guide
+ * §1.3 FP4 row, §6.2, §8.2).
+ *   a        device [M][K/2] bytes of E2M1 pairs.
+ *   scale_a  device [M][K/32] E8M0 bytes, row-major.
+ *   b_shuf   from gemm_preshuffle_b(GP_FP4_E2M1) of B [N][K/2].
+ *   scale_b  device [N][K/32] E8M0 bytes, row-major (not shuffled).
+ *   c        device [M][N] bf16:
+ *     C[m][n] = bf16_rne(sum_k e2m1(A[m][k]) 2^(sa[m][k/32]-127) e2m1(B[n][k]) 2^(sb[n][k/32]-127))
+ * with fp32 accumulation. K % 128 == 0.
+ */
+int gemm_mxfp4(const void* a, const uint8_t* scale_a, const void* b_shuf, const uint8_t* scale_b,
+               void* c, int64_t M, int64_t N, int64_t K, const gemm_opts* opts, void* stream);
+
+/*
+ * gemm_plan -- host-only: validate a problem and report the plan a GEMM
+ * call with the same arguments would launch (tile, kernel, grid, LDS, MFMA
+ * counts). in_dtype is GP_I8, GP_FP8_E4M3, GP_BF16 or GP_FP4_E2M1. Touches
+ * no device. Returns the same status the GEMM call would return for these
+ * sizes and options (before the device checks).
+ */
+int gemm_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* opts,
+              gemm_plan_info* out);
+
+/* Static, human-readable description of a gp_status value. */
+const char* gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_PRESHUFFLE_H */

@@ -1,0 +1,121 @@
+"""The C-ABI library: it loads, exports every function the header declares,
+and its host-side logic (validation, planner) behaves as documented. Nothing
+here launches GPU work: every call below fails validation or is the
+host-only planner query."""
+import ctypes
+
+import pytest
+
+import dense_gemm_preshuffle_amd as gp
+from oracle import formulas as F
+from workloads import CONFIGS
+
+GP_OK, GP_EINVAL, GP_ESHAPE, GP_EDTYPE = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gp.load_library()
+
+
+def test_exports_every_header_function(lib):
+    names = gp.header_functions()
+    assert set(names) >= {"gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4",
+                          "gemm_plan", "gemm_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.gemm_status_string(s)
+    assert b"unknown" in lib.gemm_status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x100000)   # aligned, never dereferenced: validation fails first
+MIS = ctypes.c_void_p(0x100008)    # misaligned
+
+
+def test_null_and_misaligned_pointers(lib):
+    assert lib.gemm_bf16(None, FAKE, FAKE, 128, 256, 64, None, None) == GP_EINVAL
+    assert lib.gemm_bf16(MIS, FAKE, FAKE, 128, 256, 64, None, None) == GP_EINVAL
+    assert lib.gemm_a8w8(FAKE, FAKE, None, None, None, 16, 16, 64, 0, 4, None, None) == GP_EINVAL
+    assert lib.gemm_mxfp4(FAKE, None, FAKE, FAKE, FAKE, 16, 16, 128, None, None) == GP_EINVAL
+    assert lib.gemm_preshuffle_b(FAKE, None, 16, 64, 0, None) == GP_EINVAL
+    # overlapping preshuffle buffers
+    assert lib.gemm_preshuffle_b(FAKE, ctypes.c_void_p(0x100000 + 512), 16, 64, 0, None) == GP_EINVAL
+
+
+def test_sizes_and_shapes(lib):
+    assert lib.gemm_bf16(FAKE, FAKE, FAKE, 0, 256, 64, None, None) == GP_EINVAL      # empty
+    assert lib.gemm_bf16(FAKE, FAKE, FAKE, 128, -16, 64, None, None) == GP_EINVAL
+    assert lib.gemm_bf16(FAKE, FAKE, FAKE, 128, 250, 64, None, None) == GP_ESHAPE    # N % 16
+    assert lib.gemm_bf16(FAKE, FAKE, FAKE, 120, 256, 64, None, None) == GP_ESHAPE    # M % 16 (ragged)
+    assert lib.gemm_bf16(FAKE, FAKE, FAKE, 128, 256, 48, None, None) == GP_ESHAPE    # Kb % 64
+    assert lib.gemm_a8w8(FAKE, FAKE, None, None, FAKE, 16, 16, 96, 0, 4, None, None) == GP_ESHAPE
+    assert lib.gemm_preshuffle_b(FAKE, ctypes.c_void_p(0x900000), 16, 32, 0, None) == GP_ESHAPE
+    assert lib.gemm_preshuffle_b(FAKE, ctypes.c_void_p(0x900000), 24, 64, 0, None) == GP_ESHAPE
+    # 2^31-byte limit of the 32-bit buffer offsets
+    assert lib.gemm_bf16(FAKE, FAKE, FAKE, 65536, 65536, 65536, None, None) == GP_ESHAPE
+
+
+def test_dtype_pairs(lib):
+    S = ctypes.c_void_p(0x200000)
+    # INT8 must have int32 output and no scales
+    assert lib.gemm_a8w8(FAKE, FAKE, None, None, FAKE, 16, 16, 64, 0, 2, None, None) == GP_EDTYPE
+    assert lib.gemm_a8w8(FAKE, FAKE, S, S, FAKE, 16, 16, 64, 0, 4, None, None) == GP_EDTYPE
+    # FP8 must have bf16 output and both scales
+    assert lib.gemm_a8w8(FAKE, FAKE, None, None, FAKE, 16, 16, 64, 1, 2, None, None) == GP_EDTYPE
+    assert lib.gemm_a8w8(FAKE, FAKE, S, S, FAKE, 16, 16, 64, 1, 4, None, None) == GP_EDTYPE
+    assert lib.gemm_a8w8(FAKE, FAKE, S, S, FAKE, 16, 16, 64, 2, 2, None, None) == GP_EDTYPE
+    assert lib.gemm_preshuffle_b(FAKE, ctypes.c_void_p(0x900000), 16, 64, 7, None) == GP_EDTYPE
+
+
+def test_options_validation():
+    with pytest.raises(gp.GemmError) as e:
+        gp.gemm_plan("fp8", 512, 4096, 4096, dict(tile_m=64, tile_n=256, tile_k=96, kernel=1))
+    assert e.value.status == GP_ESHAPE                  # tile not compiled
+    with pytest.raises(gp.GemmError) as e:
+        gp.gemm_plan("fp8", 512, 4096, 4096, dict(epilogue=7))
+    assert e.value.status == GP_EINVAL
+    with pytest.raises(gp.GemmError) as e:
+        gp.gemm_plan("fp8", 512, 4096, 4096, dict(tile_m=64))   # partial tile spec
+    assert e.value.status == GP_EINVAL
+    with pytest.raises(gp.GemmError) as e:
+        gp.gemm_plan("mxfp4", 64, 256, 192)             # FP4 needs K % 128
+    assert e.value.status == GP_ESHAPE
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_plan_mfma_count_and_flops(name):
+    dtype, M, N, K, _, _ = CONFIGS[name]
+    p = gp.gemm_plan(dtype, M, N, K)
+    assert p["mfma_total"] == F.mfma_count_gfx950(dtype, M, N, K)
+    assert p["mfma_total"] * F.flops_per_mfma_gfx950(dtype) == F.flops(M, N, K)
+    assert p["grid"] > 0 and p["threads"] in (256, 512)
+
+
+def test_named_tiles_plan():
+    p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128))
+    # the pages' formula counts gfx942 K=32 instructions; gfx950 FP8 takes K=128
+    assert p["mfma_per_wave_tile"] * 4 == F.mfma_per_tile_pages(64, 256, 128)
+    assert p["grid"] == 128 and p["k_tiles"] == 32
+    assert p["lds_bytes"] == F.lds_bytes(64, 256, 128, 1)
+    p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64))
+    assert p["grid"] == 2048 and p["k_tiles"] == 128
+    assert p["mfma_per_wave_tile"] == 64            # 2 K32 steps x 8 x 4
+    assert p["lds_bytes"] == F.lds_bytes(128, 256, 64, 2)
+    p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=2))
+    assert p["lds_bytes"] == 64 * (256 * 2 + 16)    # padded CShuffle tile
+
+
+def test_worked_example_plan():
+    # GEMM Optimization Guide §14: 5120 x 5120 x 8320, tile 64 x 256 x 128 FP8
+    p = gp.gemm_plan("fp8", 5120, 5120, 8320, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128))
+    assert p["grid"] == 1600 and p["k_tiles"] == 65
+    assert p["mfma_per_wave_tile"] * p["k_tiles"] * 4 == 4160   # in gfx942 K=32 instructions
+
+
+def test_small_m_uses_split_k():
+    p = gp.gemm_plan("fp8", 16, 7168, 2048)
+    assert p["kernel"] == gp.KERNEL_SPLITK and p["tile_m"] == 16

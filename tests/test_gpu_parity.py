@@ -1,0 +1,220 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+INT8 is bit-exact; FP8 / BF16 / MXFP4 with bf16 output are within
+normwise 2e-3 and floored elementwise 1e-2 of the float64 oracle; the
+closed-form cases (one-hot B, single products, exhaustive FP8 / FP4 codes,
+block-scale placement) are bit-exact for every type.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests._parity import check, gpu_run, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import dense_gemm_preshuffle_amd as gp
+
+    gp.load_library()
+    yield
+
+
+EB = {"int8": 1, "fp8": 1, "bf16": 2, "mxfp4": 0.5}
+
+
+# ---------------------------------------------------------------- preshuffle
+@pytest.mark.parametrize("dtype,N,K", [("int8", 16, 64), ("fp8", 48, 512), ("bf16", 64, 256),
+                                       ("mxfp4", 32, 512), ("fp8", 7168, 2048)])
+def test_preshuffle_bit_exact(dtype, N, K):
+    import torch
+    from dense_gemm_preshuffle_amd import gemm_preshuffle_b
+
+    say(f"preshuffle {dtype} N={N} K={K}")
+    Kb = int(K * EB[dtype])
+    b = np.random.default_rng(N + K).integers(0, 256, size=(N, Kb), dtype=np.uint8)
+    out = gemm_preshuffle_b(torch.from_numpy(b).cuda(), dtype)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), oracle.preshuffle(b))
+
+
+# ---------------------------------------------------------------- random parity over tile shapes
+TILE_CASES = [
+    # dtype, M, N, K, opts
+    ("int8", 64, 128, 128, dict(kernel=1, tile_m=64, tile_n=64, tile_k=128)),      # 1 K tile
+    ("int8", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128)),    # 2 K tiles
+    ("int8", 128, 256, 384, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128)),   # 3 K tiles (odd)
+    ("int8", 64, 192, 640, dict(kernel=1, tile_m=32, tile_n=64, tile_k=128, epilogue=2)),
+    ("int8", 32, 128, 512, dict(kernel=1, tile_m=16, tile_n=64, tile_k=256)),
+    ("fp8", 128, 512, 384, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128)),
+    ("fp8", 128, 512, 640, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, epilogue=2)),
+    ("fp8", 96, 256, 256, dict(kernel=1, tile_m=32, tile_n=256, tile_k=128)),
+    ("fp8", 64, 256, 1536, dict(kernel=1, tile_m=16, tile_n=64, tile_k=512, epilogue=2)),
+    ("fp8", 128, 256, 768, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256)),
+    ("bf16", 256, 512, 192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64)),
+    ("bf16", 128, 512, 320, dict(kernel=1, tile_m=128, tile_n=256, tile_k=32, epilogue=2)),
+    ("bf16", 128, 256, 192, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64)),
+    ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256)),
+    ("mxfp4", 256, 256, 512, dict(kernel=1, tile_m=128, tile_n=128, tile_k=256, epilogue=2)),
+    ("mxfp4", 64, 256, 1024, dict(kernel=1, tile_m=32, tile_n=256, tile_k=256)),
+    # small-M split-K kernel
+    ("fp8", 16, 512, 2048, dict(kernel=2)),
+    ("fp8", 32, 256, 1024, dict(kernel=2, tile_n=32)),
+    ("fp8", 16, 256, 2048, dict(kernel=2, waves=8, tile_k=256)),
+    ("fp8", 16, 128, 4096, dict(kernel=2, tile_k=128)),   # 8 chunks per wave
+    ("fp8", 16, 128, 1536, dict(kernel=2, tile_k=128)),   # 3 chunks (odd)
+    ("int8", 16, 64, 1024, dict(kernel=2)),
+    ("bf16", 32, 128, 512, dict(kernel=2, tile_n=32)),
+    ("mxfp4", 16, 128, 2048, dict(kernel=2)),
+]
+
+
+@pytest.mark.parametrize("case", TILE_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[4]}")
+def test_random_parity(case):
+    dtype, M, N, K, opts = case
+    say(f"parity {dtype} {M}x{N}x{K} {opts}")
+    host = workloads.make_inputs(dtype, M, N, K, seed=M * 7 + N * 3 + K)
+    out = gpu_run(dtype, host, opts)
+    check(dtype, host, out)
+
+
+@pytest.mark.parametrize("xcd", [1, 2])
+def test_xcd_order_does_not_change_result(xcd):
+    say(f"xcd {xcd}")
+    host = workloads.make_inputs("fp8", 512, 1024, 256, seed=11)
+    opts = dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, xcd_swizzle=xcd)
+    out = gpu_run("fp8", host, opts)
+    check("fp8", host, out)
+
+
+# ---------------------------------------------------------------- closed forms (bit-exact)
+def _one_hot_b(dtype, N, K, perm):
+    """B[n, k] = 1.0 at k = perm[n], else 0, in the input encoding."""
+    if dtype == "int8":
+        b = np.zeros((N, K), np.int8)
+        b[np.arange(N), perm] = 1
+        return {"b": b}
+    if dtype == "fp8":
+        b = np.zeros((N, K), np.uint8)
+        b[np.arange(N), perm] = 0x38
+        return {"b": b, "scale_b": np.ones(N, np.float32)}
+    if dtype == "bf16":
+        b = np.zeros((N, K), np.uint16)
+        b[np.arange(N), perm] = 0x3F80
+        return {"b": b}
+    codes = np.zeros((N, K), np.uint8)
+    codes[np.arange(N), perm] = 2            # E2M1 1.0
+    return {"b": codes[:, 0::2] | (codes[:, 1::2] << 4), "scale_b": np.full((N, K // 32), 127, np.uint8)}
+
+
+PERM_CASES = [("int8", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128)),
+              ("fp8", 128, 512, 384, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128)),
+              ("fp8", 16, 256, 1024, dict(kernel=2)),
+              ("bf16", 256, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64)),
+              ("mxfp4", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256)),
+              ("mxfp4", 16, 128, 1024, dict(kernel=2))]
+
+
+@pytest.mark.parametrize("case", PERM_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-k{c[4]['kernel']}")
+def test_permutation_b_bit_exact(case):
+    dtype, M, N, K, opts = case
+    say(f"perm {dtype} {M}x{N}x{K}")
+    rng = np.random.default_rng(3)
+    host = workloads.make_inputs(dtype, M, N, K, seed=5)
+    perm = rng.integers(0, K, size=N)
+    host.update(_one_hot_b(dtype, N, K, perm))
+    if dtype == "fp8":
+        host["scale_a"] = np.exp2(rng.integers(-3, 4, size=M)).astype(np.float32)
+    out = gpu_run(dtype, host, opts)
+    ref = oracle.gemm(dtype, host)
+    if dtype == "int8":
+        assert np.array_equal(out, ref)
+    else:
+        assert np.array_equal(oracle.decode_bf16(out), ref), "one-hot B must select columns exactly"
+
+
+def test_fp8_exhaustive_code_pairs_bit_exact():
+    say("fp8 exhaustive codes")
+    M = N = 256
+    K = 128
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0xFF]] = 0
+    a = np.zeros((M, K), np.uint8)
+    b = np.zeros((N, K), np.uint8)
+    a[:, 0] = codes
+    b[:, 0] = codes
+    host = {"a": a, "b": b, "scale_a": np.ones(M, np.float32), "scale_b": np.ones(N, np.float32)}
+    for opts in (dict(kernel=1, tile_m=64, tile_n=256, tile_k=128), dict(kernel=1, tile_m=128, tile_n=128, tile_k=128, epilogue=2)):
+        out = gpu_run("fp8", host, opts)
+        assert np.array_equal(oracle.decode_bf16(out), oracle.gemm("fp8", host)), opts
+
+
+def test_bf16_single_products_round_to_nearest_even():
+    say("bf16 single products")
+    rng = np.random.default_rng(9)
+    M, N, K = 128, 256, 64
+    a = np.zeros((M, K), np.uint16)
+    b = np.zeros((N, K), np.uint16)
+    a[:, 5] = (rng.integers(0, 2 ** 16, M).astype(np.uint16) & 0x3FFF) | 0x3C00
+    b[:, 5] = (rng.integers(0, 2 ** 16, N).astype(np.uint16) & 0xBFFF) | 0x3800
+    host = {"a": a, "b": b}
+    out = gpu_run("bf16", host, dict(kernel=1, tile_m=128, tile_n=256, tile_k=32))
+    assert np.array_equal(oracle.decode_bf16(out), oracle.bf16_rne(oracle.gemm("bf16", host)))
+
+
+def test_fp4_exhaustive_codes_and_scales_bit_exact():
+    say("fp4 exhaustive codes")
+    M = N = 16
+    K = 512
+    ca = np.zeros((M, K), np.uint8)
+    cb = np.zeros((N, K), np.uint8)
+    ca[:, 0] = np.arange(16)
+    cb[:, 0] = np.arange(16)
+    sa = np.full((M, K // 32), 127, np.uint8)
+    sb = np.full((N, K // 32), 127, np.uint8)
+    sa[:, 0] = 127 + (np.arange(M) % 5) - 2
+    sb[:, 0] = 127 + (np.arange(N) % 3) - 1
+    host = {"a": ca[:, 0::2] | (ca[:, 1::2] << 4), "scale_a": sa,
+            "b": cb[:, 0::2] | (cb[:, 1::2] << 4), "scale_b": sb}
+    out = gpu_run("mxfp4", host, dict(kernel=2))
+    assert np.array_equal(oracle.decode_bf16(out), oracle.gemm("mxfp4", host))
+
+
+@pytest.mark.parametrize("opts", [dict(kernel=1, tile_m=64, tile_n=256, tile_k=256),
+                                  dict(kernel=1, tile_m=128, tile_n=256, tile_k=256),
+                                  dict(kernel=2)], ids=["t64", "t128", "splitk"])
+def test_fp4_block_scale_placement_bit_exact(opts):
+    say(f"fp4 scale placement {opts}")
+    rng = np.random.default_rng(4)
+    M, N, K = (128, 256, 1024) if opts["kernel"] == 1 else (16, 64, 1024)
+    nblk = K // 32
+    blk = rng.integers(0, nblk, size=M)                  # row m is 1.0 on block blk[m] only
+    ca = np.zeros((M, K), np.uint8)
+    for m in range(M):
+        ca[m, blk[m] * 32:(blk[m] + 1) * 32] = 2
+    sa = rng.integers(120, 134, size=(M, nblk)).astype(np.uint8)
+    cb = np.full((N, K), 2, np.uint8)                     # B all ones
+    sb = np.full((N, nblk), 127, np.uint8)
+    sb[:, :] = 127 + (np.arange(N)[:, None] % 3)          # per-row power of two
+    host = {"a": ca[:, 0::2] | (ca[:, 1::2] << 4), "scale_a": sa,
+            "b": cb[:, 0::2] | (cb[:, 1::2] << 4), "scale_b": sb}
+    out = gpu_run("mxfp4", host, opts)
+    ref = oracle.gemm("mxfp4", host)
+    assert np.array_equal(oracle.decode_bf16(out), ref)
+
+
+# ---------------------------------------------------------------- determinism
+def test_bitwise_repeatable():
+    say("repeatability")
+    host = workloads.make_inputs("fp8", 16, 1024, 2048, seed=21)
+    o1, o2 = gpu_run("fp8", host, None, repeat=2)
+    assert np.array_equal(o1, o2)
+    host = workloads.make_inputs("bf16", 256, 512, 512, seed=22)
+    o1, o2 = gpu_run("bf16", host, None, repeat=2)
+    assert np.array_equal(o1, o2)
