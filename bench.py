@@ -91,7 +91,7 @@ def cpu_baseline(name, host, budget_s=12.0):
                       f"(decode + float64 matmul)"}
 
 
-def bench_one(name, steps, warmup, do_cpu=True, opts=None):
+def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True):
     import torch
 
     import dense_gemm_preshuffle_amd as gp
@@ -132,12 +132,34 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None):
         workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R])
     torch.cuda.synchronize()
 
+    # eager launches (host launch cost included)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
     t_start.record(stream)
     for i in range(steps):
         workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = t_start.elapsed_time(t_end) / steps
+
+    # timed region: the same K launches captured once in a HIP graph and
+    # replayed, so the GPU sees back-to-back GEMMs without host launch gaps
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R])
+        graph.replay()
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(steps):
+            workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -166,6 +188,9 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None):
         "tflops": tflops, "gbps": gbps, "us_per_gemm": sec * 1e6,
         "preshuffle_b": {"us": pre_us, "GB/s": 2 * b_bytes / (pre_us * 1e-6) / 1e9,
                          "note": "one-time B layout pass, not in the timed step"},
+        "timing": "hip graph of the K steps, HIP events on the launch stream" if use_graph
+                  else "eager launches, HIP events on the launch stream",
+        "eager_us_per_gemm": eager_ms * 1e3,
         "host_wall_s": wall,
     }
     if do_cpu:
@@ -181,6 +206,7 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="one of %s, or 'all'" % ", ".join(sorted(workloads.CONFIGS)))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--opts", default=None, help="JSON gemm_opts override, e.g. '{\"tile_m\":64,...}'")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -194,7 +220,8 @@ def main():
     names = sorted(workloads.CONFIGS) if args.workload == "all" else [args.workload]
     opts = json.loads(args.opts) if args.opts else None
     for name in names:
-        line = bench_one(name, args.steps, args.warmup, do_cpu=not args.no_cpu_baseline, opts=opts)
+        line = bench_one(name, args.steps, args.warmup, do_cpu=not args.no_cpu_baseline, opts=opts,
+                         use_graph=not args.eager)
         print(json.dumps(line), flush=True)
 
 

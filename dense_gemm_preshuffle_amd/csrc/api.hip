@@ -76,8 +76,8 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
                              {64, 128, 128}, {16, 64, 512}};
   static const Cand bf16[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {64, 128, 128},
                               {128, 256, 64}};
-  static const Cand fp4[] = {{128, 256, 128}, {64, 256, 128}, {32, 256, 128}, {128, 128, 128},
-                             {64, 128, 128}};
+  static const Cand fp4[] = {{128, 128, 128}, {64, 256, 128}, {32, 256, 128}, {64, 128, 128},
+                             {128, 256, 128}};
   const Cand* list;
   int n;
   switch (dt) {

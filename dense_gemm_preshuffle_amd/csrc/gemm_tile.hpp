@@ -116,19 +116,25 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (size_t)(n0 / 16) * 16 * Kb, TN * Kb);
 
   // ---- per-lane constant offsets ----
-  // A global -> LDS: thread tid moves chunk (tid % CPR) of rows tid / CPR + i * (256 / CPR).
-  uint32_t a_ld[C::ALOADS];
-  uint32_t a_wr[C::ALOADS];
-  bool a_on[C::ALOADS];
+  // A global -> LDS: thread tid moves chunk (tid % CPR) of rows tid / CPR + i * RPP.
+  constexpr int RPP = C::THREADS / C::CPR;  // A rows per pass of the workgroup
+  const int arow0 = tid / C::CPR;
+  const int ach = tid % C::CPR;
+  const uint32_t a_ld0 = arow0 * Kb + ach * 16;
+  // the XOR term of rows arow0 + i*RPP does not depend on i when RPP/SWP is a
+  // multiple of the swizzle period; then the LDS write offset is a constant step
+  constexpr bool AWR_STEP = ((RPP / C::SWP) % (C::SWM + 1)) == 0;
+  uint32_t a_wr[AWR_STEP ? 1 : C::ALOADS];
 #pragma unroll
-  for (int i = 0; i < C::ALOADS; ++i) {
-    const int q = i * C::THREADS + tid;
-    const int row = q / C::CPR;
-    const int ch = q % C::CPR;
-    a_on[i] = !C::APART || q < C::ACHUNKS;
-    a_ld[i] = row * Kb + ch * 16;
-    a_wr[i] = row * TKB + ((ch ^ ((row / C::SWP) & C::SWM)) * 16);
+  for (int i = 0; i < (AWR_STEP ? 1 : C::ALOADS); ++i) {
+    const int row = arow0 + i * RPP;
+    a_wr[i] = row * TKB + ((ach ^ ((row / C::SWP) & C::SWM)) * 16);
   }
+  auto a_wr_off = [&](int i) -> uint32_t {
+    if constexpr (AWR_STEP) return a_wr[0] + i * RPP * TKB;
+    else return a_wr[i];
+  };
+  auto a_on = [&](int i) { return !C::APART || i * C::THREADS + tid < C::ACHUNKS; };
   // A LDS -> VGPR: lane reads row mi*16 + lane_lo, chunk s*KB/16 + f*4 + lane_hi.
   const int swz = (lane_lo / C::SWP) & C::SWM;
   uint32_t a_rd[C::KSTEPS][C::FRAG];
@@ -137,29 +143,28 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
     for (int f = 0; f < C::FRAG; ++f)
       a_rd[s][f] = lane_lo * TKB + (((s * (C::KB / 16) + f * 4 + lane_hi) ^ swz) * 16);
-  // B: the wave's 16-column blocks, lane's 16 bytes within each KiB.
-  uint32_t b_off[C::NACC];
-#pragma unroll
-  for (int ni = 0; ni < C::NACC; ++ni)
-    b_off[ni] = (uint32_t)(wave * C::NACC + ni) * 16u * Kb + lane * 16;
+  // B: the wave's first 16-column block; block ni adds ni*16*Kb (uniform).
+  const uint32_t b_off0 = (uint32_t)(wave * C::NACC) * 16u * Kb + lane * 16;
+  const uint32_t b_step = 16u * Kb;
 
   // FP4 block scales: one E8M0 byte per 32 K elements (= 16 bytes of K).
   const uint32_t srow = Kb / 16;  // scale bytes per row
   __amdgpu_buffer_rsrc_t rsa = make_rsrc(nullptr, 0), rsb = make_rsrc(nullptr, 0);
-  uint32_t sa_off[C::MREP], sb_off[C::NACC];
+  uint32_t sa_off0 = 0, sb_off0 = 0, ssel = 0;
   if constexpr (DT == DT_FP4) {
+    static_assert(C::KSTEPS <= 2, "FP4 tile_k bytes <= 128");
     rsa = make_rsrc((const char*)p.sa + (size_t)m0 * srow, TM * srow);
     rsb = make_rsrc((const char*)p.sb + (size_t)n0 * srow, TN * srow);
-#pragma unroll
-    for (int mi = 0; mi < C::MREP; ++mi) sa_off[mi] = (mi * 16 + lane_lo) * srow;
-#pragma unroll
-    for (int ni = 0; ni < C::NACC; ++ni) sb_off[ni] = (wave * C::NPW + ni * 16 + lane_lo) * srow;
+    sa_off0 = lane_lo * srow;
+    sb_off0 = (wave * C::NPW + lane_lo) * srow;
+    // byte lane_hi of the first dword -> byte 0, of the second -> byte 1
+    ssel = (uint32_t)lane_hi | ((uint32_t)(4 + lane_hi) << 8) | 0x0c0c0000u;
   }
 
   v4i a_st[C::ALOADS];
   v4i bfr[2][C::KSTEPS][C::NACC][C::FRAG];
-  int sbr[2][C::KSTEPS][C::NACC * C::NSC + 1 - C::NSC];
-  int sar[2][C::KSTEPS][C::MREP * C::NSC + 1 - C::NSC];
+  v2i sbr[2][C::NACC * C::NSC + 1 - C::NSC];
+  v2i sar[2][C::MREP * C::NSC + 1 - C::NSC];
   Acc acc[C::MREP][C::NACC];
 #pragma unroll
   for (int mi = 0; mi < C::MREP; ++mi)
@@ -169,13 +174,13 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   auto load_a = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < C::ALOADS; ++i)
-      if (a_on[i]) a_st[i] = buf_load16(ra, a_ld[i], kt * TKB);
+      if (a_on(i)) a_st[i] = buf_load16(ra, a_ld0, kt * TKB + i * RPP * Kb);
   };
   auto store_a = [&](int par) {
     char* base = lds + par * C::ABUF;
 #pragma unroll
     for (int i = 0; i < C::ALOADS; ++i)
-      if (a_on[i]) *(v4i*)(base + a_wr[i]) = a_st[i];
+      if (a_on(i)) *(v4i*)(base + a_wr_off(i)) = a_st[i];
   };
   auto load_b = [&](auto par_c, int kt) {
     constexpr int par = decltype(par_c)::value;
@@ -186,48 +191,85 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
       for (int ni = 0; ni < C::NACC; ++ni)
 #pragma unroll
         for (int f = 0; f < C::FRAG; ++f)
-          bfr[par][s][ni][f] = buf_load16(rb, b_off[ni] + (s * (C::KB / 64) + f) * 1024, kbase);
+          bfr[par][s][ni][f] = buf_load16(rb, b_off0 + (s * (C::KB / 64) + f) * 1024, kbase + ni * b_step);
     if constexpr (DT == DT_FP4) {
       const uint32_t sbase = (uint32_t)kt * (TKB / 16);
 #pragma unroll
-      for (int s = 0; s < C::KSTEPS; ++s) {
+      for (int ni = 0; ni < C::NACC; ++ni) {
+        if constexpr (C::KSTEPS == 2) sbr[par][ni] = buf_load8(rsb, sb_off0, sbase + ni * 16 * srow);
+        else sbr[par][ni][0] = buf_load4(rsb, sb_off0, sbase + ni * 16 * srow);
+      }
 #pragma unroll
-        for (int ni = 0; ni < C::NACC; ++ni) sbr[par][s][ni] = buf_load4(rsb, sb_off[ni] + s * 4, sbase);
-#pragma unroll
-        for (int mi = 0; mi < C::MREP; ++mi) sar[par][s][mi] = buf_load4(rsa, sa_off[mi] + s * 4, sbase);
+      for (int mi = 0; mi < C::MREP; ++mi) {
+        if constexpr (C::KSTEPS == 2) sar[par][mi] = buf_load8(rsa, sa_off0, sbase + mi * 16 * srow);
+        else sar[par][mi][0] = buf_load4(rsa, sa_off0, sbase + mi * 16 * srow);
       }
     }
   };
-  auto compute = [&](auto par_c) {
-    constexpr int par = decltype(par_c)::value;
+  // ds_read of A fragment (s, mi) from buffer par
+  auto read_a = [&](int par, int s, int mi, v4i* af) {
     const char* base = lds + par * C::ABUF;
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
+    for (int f = 0; f < C::FRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * 16 * TKB);
+  };
+  auto compute = [&](auto par_c) {
+    constexpr int par = decltype(par_c)::value;
+    // packed E8M0 scales: byte s is the scale of K step s (selected by op_sel)
+    int psa[C::MREP * C::NSC + 1 - C::NSC], psb[C::NACC * C::NSC + 1 - C::NSC];
+    if constexpr (DT == DT_FP4) {
 #pragma unroll
-      for (int mi = 0; mi < C::MREP; ++mi) {
-        v4i af[C::FRAG];
+      for (int mi = 0; mi < C::MREP; ++mi)
+        psa[mi] = (int)__builtin_amdgcn_perm((uint32_t)sar[par][mi][1], (uint32_t)sar[par][mi][0], ssel);
 #pragma unroll
-        for (int f = 0; f < C::FRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * 16 * TKB);
-        int sy = 0;
-        if constexpr (DT == DT_FP4) sy = sar[par][s][mi] >> (8 * lane_hi);
+      for (int ni = 0; ni < C::NACC; ++ni)
+        psb[ni] = (int)__builtin_amdgcn_perm((uint32_t)sbr[par][ni][1], (uint32_t)sbr[par][ni][0], ssel);
+    }
+    constexpr int NF = C::KSTEPS * C::MREP;
+    v4i af[2][C::FRAG];
+    read_a(par, 0, 0, af[0]);
 #pragma unroll
-        for (int ni = 0; ni < C::NACC; ++ni) {
-          int sx = 0;
-          if constexpr (DT == DT_FP4) sx = sbr[par][s][ni] >> (8 * lane_hi);
-          acc[mi][ni] = mfma<DT>(bfr[par][s][ni], af, acc[mi][ni], sx, sy);
+    for (int i = 0; i < NF; ++i) {
+      const int s = i / C::MREP, mi = i % C::MREP;
+      if (i + 1 < NF) read_a(par, (i + 1) / C::MREP, (i + 1) % C::MREP, af[(i + 1) & 1]);
+#pragma unroll
+      for (int ni = 0; ni < C::NACC; ++ni) {
+        if constexpr (DT == DT_FP4) {
+          if (s == 0)
+            acc[mi][ni] = mfma_fp4_sel<0>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]);
+          else
+            acc[mi][ni] = mfma_fp4_sel<1>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]);
+        } else {
+          acc[mi][ni] = mfma<DT>(bfr[par][s][ni], af[i & 1], acc[mi][ni]);
         }
       }
     }
   };
+  // Instruction order of one K tile (hot-loop schedule): first A fragment
+  // read, then all global loads of the next tile (A, then B), then for every
+  // A fragment: read the next fragment, issue its NACC MFMAs; LDS writes of
+  // the next A tile last, ahead of the barrier.
+  auto schedule = [&]() {
+    constexpr int NF = C::KSTEPS * C::MREP;
+    constexpr int NVMEM = C::ALOADS + C::KSTEPS * C::NACC * C::FRAG + (C::NSC ? C::NACC + C::MREP : 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, C::FRAG, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, NVMEM, 0);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      if (i + 1 < NF) __builtin_amdgcn_sched_group_barrier(0x100, C::FRAG, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, C::NACC, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x200, C::ALOADS, 0);
+  };
   auto iter = [&](auto par_c, int kt) {
     constexpr int par = decltype(par_c)::value;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      load_a(kt + 1);
-      load_b(std::integral_constant<int, par ^ 1>{}, kt + 1);
-    }
+    // the last tile reloads itself instead of branching, keeping the body one
+    // straight-line block; its copy in the other LDS buffer is never read
+    const int kn = kt + 1 < KT ? kt + 1 : kt;
+    load_a(kn);
+    load_b(std::integral_constant<int, par ^ 1>{}, kn);
     compute(par_c);
-    if (more) store_a(par ^ 1);
+    store_a(par ^ 1);
+    schedule();
     __syncthreads();
   };
 

@@ -74,6 +74,14 @@ mfma(const v4i* x, const v4i* y, typename Traits<DT>::Acc acc, int sx = 0, int s
   }
 }
 
+// FP4 MFMA whose E8M0 scales sit in byte SEL of sx / sy (op_sel picks the byte).
+template <int SEL>
+__device__ __forceinline__ v4f mfma_fp4_sel(const v4i* x, const v4i* y, v4f acc, int sx, int sy) {
+  v8i xx = __builtin_shufflevector(x[0], x[0], 0, 1, 2, 3, -1, -1, -1, -1);
+  v8i yy = __builtin_shufflevector(y[0], y[0], 0, 1, 2, 3, -1, -1, -1, -1);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xx, yy, acc, 4, 4, SEL, sx, SEL, sy);
+}
+
 // fp32 -> bf16 with round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   __bf16 a = (__bf16)lo;

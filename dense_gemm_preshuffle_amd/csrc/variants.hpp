@@ -22,7 +22,7 @@
 
 #define GP_TILE_FP4(X)                                                                  \
   X(DT_FP4, 32, 256, 128) X(DT_FP4, 64, 128, 128) X(DT_FP4, 64, 256, 128)              \
-  X(DT_FP4, 128, 128, 128) X(DT_FP4, 128, 256, 128) X(DT_FP4, 64, 256, 256)
+  X(DT_FP4, 128, 128, 128) X(DT_FP4, 128, 256, 128)
 
 #define GP_SPLITK_I8(Y) Y(DT_I8, 1, 4, 64) Y(DT_I8, 1, 4, 256) Y(DT_I8, 2, 4, 256)
 #define GP_SPLITK_FP8(Y)                                                                \

@@ -218,3 +218,36 @@ def test_bitwise_repeatable():
     host = workloads.make_inputs("bf16", 256, 512, 512, seed=22)
     o1, o2 = gpu_run("bf16", host, None, repeat=2)
     assert np.array_equal(o1, o2)
+
+
+# ---------------------------------------------------------------- HIP graph replay
+def test_graph_replay_matches_eager():
+    """Launches captured in a HIP graph give the eager result on every replay,
+    with eager work and synchronizations between the replays."""
+    import torch
+
+    from dense_gemm_preshuffle_amd import workload
+
+    say("graph replay")
+    for dtype, M, N, K in [("fp8", 16, 7168, 2048), ("bf16", 256, 512, 256), ("mxfp4", 128, 256, 512)]:
+        host = workloads.make_inputs(dtype, M, N, K, seed=31)
+        p = workload.prepare(dtype, workload.to_device(dtype, host))
+        eager = workload.to_host(workload.run(dtype, p))
+        outs = [workload.run(dtype, p) for _ in range(3)]
+        torch.cuda.synchronize()
+        for o in outs:
+            o.zero_()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for o in outs:
+                workload.run(dtype, p, c=o)
+        for rep in range(3):
+            for o in outs:
+                o.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for o in outs:
+                assert np.array_equal(workload.to_host(o), eager), (dtype, rep)
+            workload.run(dtype, p)          # eager work between replays
+            torch.cuda.synchronize()
