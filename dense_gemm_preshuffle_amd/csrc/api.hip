@@ -76,8 +76,8 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
                              {64, 128, 128}, {16, 64, 512}};
   static const Cand bf16[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {64, 128, 128},
                               {128, 256, 64}};
-  static const Cand fp4[] = {{128, 128, 128}, {64, 256, 128}, {32, 256, 128}, {64, 128, 128},
-                             {128, 256, 128}};
+  static const Cand fp4[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {32, 256, 128},
+                             {64, 128, 128}};
   const Cand* list;
   int n;
   switch (dt) {
@@ -104,28 +104,45 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
   return GP_OK;
 }
 
+// Compiled split-K chunk for (dt, nb, waves) that divides the wave's K range:
+// the largest one up to 256 bytes (measured best for the M=16 FP8 shape),
+// else the smallest; 0 if none.
+int pick_chunk(int dt, int nb, int waves, int64_t kw) {
+  int kch = 0;
+  for (const auto& v : kSplits)
+    if (v.dt == dt && v.nb == nb && v.waves == waves && kw % v.kch == 0 && v.kch <= 256 && v.kch > kch)
+      kch = v.kch;
+  if (kch == 0)
+    for (const auto& v : kSplits)
+      if (v.dt == dt && v.nb == nb && v.waves == waves && kw % v.kch == 0 && (kch == 0 || v.kch < kch))
+        kch = v.kch;
+  return kch;
+}
+
 int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, const gemm_opts* o) {
   const int waves = (o && o->waves > 0) ? o->waves : 4;
-  int nb = (o && o->tile_n > 0) ? o->tile_n / 16 : 0;
-  if (o && o->tile_k > 0 && ((int64_t)o->tile_k * bits) % 8) return GP_ESHAPE;
-  int kch = (o && o->tile_k > 0) ? (int)((int64_t)o->tile_k * bits / 8) : 0;
   if (o && o->tile_n > 0 && o->tile_n % 16) return GP_ESHAPE;
   if (o && o->tile_m > 0 && o->tile_m != 16) return GP_ESHAPE;
-  if (Kb % waves) return GP_ESHAPE;
+  if (o && o->tile_k > 0 && ((int64_t)o->tile_k * bits) % 8) return GP_ESHAPE;
+  if (Kb % waves || M % 16) return GP_ESHAPE;
   const int64_t kw = Kb / waves;
-  if (nb == 0) nb = 1;
-  if (kch == 0) {
-    // largest compiled chunk that divides the wave's K range
-    for (const auto& v : kSplits)
-      if (v.dt == dt && v.nb == nb && v.waves == waves && kw % v.kch == 0 && v.kch > kch) kch = v.kch;
-    if (kch == 0) return GP_ESHAPE;
+  const int user_kch = (o && o->tile_k > 0) ? (int)((int64_t)o->tile_k * bits / 8) : 0;
+  // column blocks per workgroup: the caller's, else 2 (two blocks fill whole
+  // 128-byte lines of a bf16 C row), else 1
+  int cand[2] = {2, 1};
+  int ncand = 2;
+  if (o && o->tile_n > 0) { cand[0] = o->tile_n / 16; ncand = 1; }
+  for (int c = 0; c < ncand; ++c) {
+    const int nb = cand[c];
+    if (N % (16 * nb)) continue;
+    const int kch = user_kch ? user_kch : pick_chunk(dt, nb, waves, kw);
+    if (kch == 0 || kw % kch || !split_compiled(dt, nb, waves, kch)) continue;
+    p->nb = nb;
+    p->waves = waves;
+    p->kch = kch;
+    return GP_OK;
   }
-  if (!split_compiled(dt, nb, waves, kch)) return GP_ESHAPE;
-  if (kw % kch || N % (16 * nb) || M % 16) return GP_ESHAPE;
-  p->nb = nb;
-  p->waves = waves;
-  p->kch = kch;
-  return GP_OK;
+  return GP_ESHAPE;
 }
 
 int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o, Plan* p) {
@@ -161,7 +178,15 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     const int r = choose_tile(dt, M, N, Kb, p);
     if (r) return r;
   }
-  p->epi = (o && o->epilogue) ? o->epilogue : EPI_DIRECT;
+  if (o && o->epilogue) {
+    p->epi = o->epilogue;
+  } else {
+    // CShuffle (coalesced full-row stores) for tile_n >= 128 when its LDS
+    // tile still lets two workgroups share a CU; direct stores otherwise
+    const int ob = in_dtype == GP_I8 ? 4 : 2;
+    const int cbytes = p->tm * (p->tn * ob + 16);
+    p->epi = (p->tn >= 128 && cbytes <= 80 * 1024) ? EPI_CSHUFFLE : EPI_DIRECT;
+  }
   p->xcd = (o && o->xcd_swizzle) ? o->xcd_swizzle : 1;
   return GP_OK;
 }
@@ -183,7 +208,9 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     out->waves = 4;
     out->threads = 256;
     const int ob = in_dtype == GP_I8 ? 4 : 2;
-    const int abuf = 2 * p.tm * p.tkb;
+    const bool apart = (p.tm * (p.tkb / 16)) % 256 != 0;
+    int abuf = 2 * (p.tm * p.tkb + (apart ? 16 : 0));
+    if (dt == DT_FP4) abuf += 2 * ((p.tm + p.tn) * (p.tkb / 64) * 4 + 16);  // staged E8M0 scales
     const int cbytes = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
     out->lds_bytes = abuf > cbytes ? abuf : cbytes;
     out->grid = (M / p.tm) * (N / p.tn);

@@ -14,7 +14,8 @@
 // Operands come straight from global memory in MFMA layout: B from the
 // preshuffled layout (one KiB per 16 columns x 64 K bytes), A as 16 bytes per
 // lane (row lane%16, K piece lane/16), which is L2-resident since every
-// workgroup reads the same few rows.
+// workgroup reads the same few rows. B is read exactly once, so its loads and
+// the C stores carry the non-temporal cache policy and leave L2 to A.
 #pragma once
 
 #include <type_traits>
@@ -57,7 +58,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
   const int lane_hi = lane >> 4;
 
   const uint32_t Kb = p.Kb;
-  const uint32_t n0 = blockIdx.x * (16 * NB);
+  // Column tiles go round-robin to the 8 XCDs; remap so that each XCD owns a
+  // contiguous run of tiles. Neighbouring tiles then share whole 128-byte
+  // lines of C inside one XCD's L2 instead of writing halves from two XCDs.
+  uint32_t bx = blockIdx.x;
+  if (gridDim.x % 8u == 0) bx = (bx % 8u) * (gridDim.x / 8u) + bx / 8u;
+  const uint32_t n0 = bx * (16 * NB);
   const uint32_t m0 = blockIdx.y * 16;
   const uint32_t kw = Kb / WAVES;            // K bytes per wave
   const uint32_t k_begin = wave * kw;
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int f = 0; f < C::FRAG; ++f)
-          bf[par][s][nb][f] = buf_load16(rb, b_off[nb] + (s * (C::KB / 64) + f) * 1024, kblk);
+          bf[par][s][nb][f] = buf_load16_nt(rb, b_off[nb] + (s * (C::KB / 64) + f) * 1024, kblk);
     if constexpr (DT == DT_FP4) {
       const uint32_t sbase = kb / 16;  // scale byte of this chunk's first 32-element block
 #pragma unroll
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
     const uint32_t col = nb * 16 + 4 * lane_hi;
     const uint32_t off = (lane_lo * p.N + col) * C::OB;
     if constexpr (DT == DT_I8) {
-      buf_store16(v, rc, off);
+      buf_store16_nt(v, rc, off);
     } else {
       if constexpr (DT == DT_FP8) {
         const float sa = ((const float*)p.sa)[m0 + lane_lo];
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
       v2i o;
       o[0] = (int)pack_bf16x2(v[0], v[1]);
       o[1] = (int)pack_bf16x2(v[2], v[3]);
-      buf_store8(o, rc, off);
+      buf_store8_nt(o, rc, off);
     }
   }
 }

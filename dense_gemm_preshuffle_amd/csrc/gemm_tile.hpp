@@ -56,14 +56,23 @@ struct TileCfg {
   static constexpr int ACHUNKS = TM * CPR;
   static constexpr int ALOADS = (ACHUNKS + THREADS - 1) / THREADS;
   static constexpr bool APART = (ACHUNKS % THREADS) != 0;
-  static constexpr int ABUF = TM * TKB;
+  static constexpr int ABUF = TM * TKB + (APART ? 16 : 0);   // + a dummy slot for idle lanes
   static constexpr int OB = (DT == DT_I8) ? 4 : 2;        // output element bytes
   static constexpr int CSTRIDE = TN * OB + 16;            // padded C row in LDS
   static constexpr int CBYTES = (EPI == EPI_CSHUFFLE) ? TM * CSTRIDE : 0;
-  static constexpr int LDS = (2 * ABUF > CBYTES) ? 2 * ABUF : CBYTES;
   static constexpr int SWP = (TKB >= 256) ? 1 : 256 / TKB;  // rows per 256-byte period
   static constexpr int SWM = ((CPR < 16) ? CPR : 16) - 1;   // chunk xor mask
   static constexpr int NSC = (DT == DT_FP4) ? 1 : 0;
+  // FP4 E8M0 scales of one K tile: SCB bytes per row of A and of B, staged in
+  // LDS beside the A tile as [row][lane group] u16 (byte s = K step s).
+  static constexpr int SCB = NSC ? KSTEPS * 4 : 0;
+  static constexpr int SROWS = NSC ? TM + TN : 0;
+  static constexpr int SLA = NSC ? (TM + THREADS - 1) / THREADS : 0;   // A scale rows per thread
+  static constexpr int SLB = NSC ? (TN + THREADS - 1) / THREADS : 0;   // B scale rows per thread
+  static constexpr int SLOADS = SLA + SLB;
+  static constexpr int SAREA = NSC ? SROWS * SCB + 16 : 0;   // + a dummy slot for idle lanes
+  static constexpr int STAGE = 2 * ABUF + 2 * SAREA;
+  static constexpr int LDS = (STAGE > CBYTES) ? STAGE : CBYTES;
   static_assert(TM % 16 == 0 && TN % 64 == 0, "tile_m % 16, tile_n % 64");
   static_assert(TKB % KB == 0 && TKB >= 64, "tile_k bytes must be a multiple of the MFMA K bytes");
   static_assert(THREADS % CPR == 0, "A row chunks must divide the workgroup");
@@ -134,7 +143,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
     if constexpr (AWR_STEP) return a_wr[0] + i * RPP * TKB;
     else return a_wr[i];
   };
+  // Lanes past the last A chunk (partial passes only) load from an offset
+  // outside the buffer resource (the hardware returns zeros without a memory
+  // access) and write to a spare LDS slot, so the K-tile body has no branch.
   auto a_on = [&](int i) { return !C::APART || i * C::THREADS + tid < C::ACHUNKS; };
+  constexpr uint32_t kOOB = 0x80000000u;
   // A LDS -> VGPR: lane reads row mi*16 + lane_lo, chunk s*KB/16 + f*4 + lane_hi.
   const int swz = (lane_lo / C::SWP) & C::SWM;
   uint32_t a_rd[C::KSTEPS][C::FRAG];
@@ -150,21 +163,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   // FP4 block scales: one E8M0 byte per 32 K elements (= 16 bytes of K).
   const uint32_t srow = Kb / 16;  // scale bytes per row
   __amdgpu_buffer_rsrc_t rsa = make_rsrc(nullptr, 0), rsb = make_rsrc(nullptr, 0);
-  uint32_t sa_off0 = 0, sb_off0 = 0, ssel = 0;
   if constexpr (DT == DT_FP4) {
     static_assert(C::KSTEPS <= 2, "FP4 tile_k bytes <= 128");
     rsa = make_rsrc((const char*)p.sa + (size_t)m0 * srow, TM * srow);
     rsb = make_rsrc((const char*)p.sb + (size_t)n0 * srow, TN * srow);
-    sa_off0 = lane_lo * srow;
-    sb_off0 = (wave * C::NPW + lane_lo) * srow;
-    // byte lane_hi of the first dword -> byte 0, of the second -> byte 1
-    ssel = (uint32_t)lane_hi | ((uint32_t)(4 + lane_hi) << 8) | 0x0c0c0000u;
   }
-
   v4i a_st[C::ALOADS];
   v4i bfr[2][C::KSTEPS][C::NACC][C::FRAG];
-  v2i sbr[2][C::NACC * C::NSC + 1 - C::NSC];
-  v2i sar[2][C::MREP * C::NSC + 1 - C::NSC];
+  v2i sa_st[C::SLA + 1 - C::NSC], sb_st[C::SLB + 1 - C::NSC];
   Acc acc[C::MREP][C::NACC];
 #pragma unroll
   for (int mi = 0; mi < C::MREP; ++mi)
@@ -174,13 +180,13 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   auto load_a = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < C::ALOADS; ++i)
-      if (a_on(i)) a_st[i] = buf_load16(ra, a_ld0, kt * TKB + i * RPP * Kb);
+      a_st[i] = buf_load16(ra, a_on(i) ? a_ld0 : kOOB, kt * TKB + i * RPP * Kb);
   };
   auto store_a = [&](int par) {
     char* base = lds + par * C::ABUF;
 #pragma unroll
     for (int i = 0; i < C::ALOADS; ++i)
-      if (a_on(i)) *(v4i*)(base + a_wr_off(i)) = a_st[i];
+      *(v4i*)(base + (a_on(i) ? a_wr_off(i) : (uint32_t)(TM * TKB))) = a_st[i];
   };
   auto load_b = [&](auto par_c, int kt) {
     constexpr int par = decltype(par_c)::value;
@@ -192,17 +198,53 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
         for (int f = 0; f < C::FRAG; ++f)
           bfr[par][s][ni][f] = buf_load16(rb, b_off0 + (s * (C::KB / 64) + f) * 1024, kbase + ni * b_step);
+  };
+  // FP4: the WG's TM + TN scale rows of one K tile, SCB bytes each. A and B
+  // rows use separate loads so that each load's buffer resource is uniform.
+  auto load_s = [&](int kt) {
     if constexpr (DT == DT_FP4) {
-      const uint32_t sbase = (uint32_t)kt * (TKB / 16);
+      const uint32_t sbase = (uint32_t)kt * C::SCB;
 #pragma unroll
-      for (int ni = 0; ni < C::NACC; ++ni) {
-        if constexpr (C::KSTEPS == 2) sbr[par][ni] = buf_load8(rsb, sb_off0, sbase + ni * 16 * srow);
-        else sbr[par][ni][0] = buf_load4(rsb, sb_off0, sbase + ni * 16 * srow);
+      for (int i = 0; i < C::SLA; ++i) {
+        const int r = i * C::THREADS + tid;
+        const uint32_t off = r < TM ? r * srow : kOOB;
+        if constexpr (C::KSTEPS == 2) sa_st[i] = buf_load8(rsa, off, sbase);
+        else sa_st[i][0] = buf_load4(rsa, off, sbase);
       }
 #pragma unroll
-      for (int mi = 0; mi < C::MREP; ++mi) {
-        if constexpr (C::KSTEPS == 2) sar[par][mi] = buf_load8(rsa, sa_off0, sbase + mi * 16 * srow);
-        else sar[par][mi][0] = buf_load4(rsa, sa_off0, sbase + mi * 16 * srow);
+      for (int i = 0; i < C::SLB; ++i) {
+        const int r = i * C::THREADS + tid;
+        const uint32_t off = r < TN ? r * srow : kOOB;
+        if constexpr (C::KSTEPS == 2) sb_st[i] = buf_load8(rsb, off, sbase);
+        else sb_st[i][0] = buf_load4(rsb, off, sbase);
+      }
+    }
+  };
+  // scale row r (A rows first, then B rows) -> LDS as [row][lane group] u16;
+  // row SROWS is the spare slot of idle lanes
+  auto put_s = [&](char* base, int r, v2i v) {
+    if constexpr (C::KSTEPS == 2) {
+      // bytes b = 4*s + g  ->  u16 per lane group g: (s=0, s=1)
+      v2i w;
+      w[0] = (int)__builtin_amdgcn_perm((uint32_t)v[1], (uint32_t)v[0], 0x05010400u);
+      w[1] = (int)__builtin_amdgcn_perm((uint32_t)v[1], (uint32_t)v[0], 0x07030602u);
+      *(v2i*)(base + r * 8) = w;
+    } else {
+      *(int*)(base + r * 4) = v[0];
+    }
+  };
+  auto store_s = [&](int par) {
+    if constexpr (DT == DT_FP4) {
+      char* base = lds + 2 * C::ABUF + par * C::SAREA;
+#pragma unroll
+      for (int i = 0; i < C::SLA; ++i) {
+        const int r = i * C::THREADS + tid;
+        put_s(base, r < TM ? r : C::SROWS, sa_st[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < C::SLB; ++i) {
+        const int r = i * C::THREADS + tid;
+        put_s(base, r < TN ? TM + r : C::SROWS, sb_st[i]);
       }
     }
   };
@@ -214,15 +256,22 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   };
   auto compute = [&](auto par_c) {
     constexpr int par = decltype(par_c)::value;
-    // packed E8M0 scales: byte s is the scale of K step s (selected by op_sel)
+    // E8M0 scales from LDS: byte s of the value is the scale of K step s
     int psa[C::MREP * C::NSC + 1 - C::NSC], psb[C::NACC * C::NSC + 1 - C::NSC];
     if constexpr (DT == DT_FP4) {
+      const char* sb = lds + 2 * C::ABUF + par * C::SAREA;
 #pragma unroll
-      for (int mi = 0; mi < C::MREP; ++mi)
-        psa[mi] = (int)__builtin_amdgcn_perm((uint32_t)sar[par][mi][1], (uint32_t)sar[par][mi][0], ssel);
+      for (int mi = 0; mi < C::MREP; ++mi) {
+        const int r = mi * 16 + lane_lo;
+        if constexpr (C::KSTEPS == 2) psa[mi] = *(const uint16_t*)(sb + r * 8 + lane_hi * 2);
+        else psa[mi] = *(const uint8_t*)(sb + r * 4 + lane_hi);
+      }
 #pragma unroll
-      for (int ni = 0; ni < C::NACC; ++ni)
-        psb[ni] = (int)__builtin_amdgcn_perm((uint32_t)sbr[par][ni][1], (uint32_t)sbr[par][ni][0], ssel);
+      for (int ni = 0; ni < C::NACC; ++ni) {
+        const int r = TM + wave * C::NPW + ni * 16 + lane_lo;
+        if constexpr (C::KSTEPS == 2) psb[ni] = *(const uint16_t*)(sb + r * 8 + lane_hi * 2);
+        else psb[ni] = *(const uint8_t*)(sb + r * 4 + lane_hi);
+      }
     }
     constexpr int NF = C::KSTEPS * C::MREP;
     v4i af[2][C::FRAG];
@@ -250,15 +299,15 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   // the next A tile last, ahead of the barrier.
   auto schedule = [&]() {
     constexpr int NF = C::KSTEPS * C::MREP;
-    constexpr int NVMEM = C::ALOADS + C::KSTEPS * C::NACC * C::FRAG + (C::NSC ? C::NACC + C::MREP : 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, C::FRAG, 0);
+    constexpr int NVMEM = C::ALOADS + C::KSTEPS * C::NACC * C::FRAG + C::SLOADS;
+    __builtin_amdgcn_sched_group_barrier(0x100, C::FRAG + (C::NSC ? C::MREP + C::NACC : 0), 0);
     __builtin_amdgcn_sched_group_barrier(0x020, NVMEM, 0);
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
       if (i + 1 < NF) __builtin_amdgcn_sched_group_barrier(0x100, C::FRAG, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, C::NACC, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x200, C::ALOADS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, C::ALOADS + C::SLOADS, 0);
   };
   auto iter = [&](auto par_c, int kt) {
     constexpr int par = decltype(par_c)::value;
@@ -266,17 +315,21 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
     // straight-line block; its copy in the other LDS buffer is never read
     const int kn = kt + 1 < KT ? kt + 1 : kt;
     load_a(kn);
+    load_s(kn);
     load_b(std::integral_constant<int, par ^ 1>{}, kn);
     compute(par_c);
     store_a(par ^ 1);
+    store_s(par ^ 1);
     schedule();
     __syncthreads();
   };
 
   // ---- prologue: tile 0 ----
   load_a(0);
+  load_s(0);
   load_b(std::integral_constant<int, 0>{}, 0);
   store_a(0);
+  store_s(0);
   __syncthreads();
 
   // ---- main loop, two K tiles per trip (ping, pong) ----

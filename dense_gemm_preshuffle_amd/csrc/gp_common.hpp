@@ -34,12 +34,31 @@ __device__ __forceinline__ v2i buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff
 __device__ __forceinline__ int buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+// Non-temporal (streaming) variants: cache policy bit 1 (nt) on gfx950.
+constexpr int kPolicyNT = 2;
+__device__ __forceinline__ v4i buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kPolicyNT);
+}
+__device__ __forceinline__ void buf_store16_nt(v4i v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, kPolicyNT);
+}
+__device__ __forceinline__ void buf_store8_nt(v2i v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, kPolicyNT);
+}
 __device__ __forceinline__ void buf_store16(v4i v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
 }
 __device__ __forceinline__ void buf_store8(v2i v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
 }
+
+// The scaled f8f6f4 MFMA with 4-dword (FP4) operands. The clang builtin types
+// both sources as 8 dwords, which makes the register allocator reserve 8-VGPR
+// tuples for FP4 operands; the LLVM intrinsic is overloaded on the source
+// vector type, so it is declared here with 4-dword sources.
+__device__ v4f mfma_scale_16x16x128_v4(v4i a, v4i b, v4f c, int cbsz, int blgp, int opsel_a, int scale_a,
+                                       int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v4i32");
 
 // Per-type traits. KB = K bytes one MFMA consumes per 16x16 block;
 // FRAG = 16-byte pieces per lane per MFMA (1, or 2 for the FP8 K=128 form).
@@ -67,19 +86,15 @@ mfma(const v4i* x, const v4i* y, typename Traits<DT>::Acc acc, int sx = 0, int s
     // unscaled 16x16x128 f8f6f4 instruction.
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xx, yy, acc, 0, 0, 0, 0, 0, 0);
   } else {
-    v8i xx = __builtin_shufflevector(x[0], x[0], 0, 1, 2, 3, -1, -1, -1, -1);
-    v8i yy = __builtin_shufflevector(y[0], y[0], 0, 1, 2, 3, -1, -1, -1, -1);
     // format 4 = FP4 E2M1 for both operands; byte 0 of sx / sy is the E8M0 scale.
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xx, yy, acc, 4, 4, 0, sx, 0, sy);
+    return mfma_scale_16x16x128_v4(x[0], y[0], acc, 4, 4, 0, sx, 0, sy);
   }
 }
 
 // FP4 MFMA whose E8M0 scales sit in byte SEL of sx / sy (op_sel picks the byte).
 template <int SEL>
 __device__ __forceinline__ v4f mfma_fp4_sel(const v4i* x, const v4i* y, v4f acc, int sx, int sy) {
-  v8i xx = __builtin_shufflevector(x[0], x[0], 0, 1, 2, 3, -1, -1, -1, -1);
-  v8i yy = __builtin_shufflevector(y[0], y[0], 0, 1, 2, 3, -1, -1, -1, -1);
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xx, yy, acc, 4, 4, SEL, sx, SEL, sy);
+  return mfma_scale_16x16x128_v4(x[0], y[0], acc, 4, 4, SEL, sx, SEL, sy);
 }
 
 // fp32 -> bf16 with round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
