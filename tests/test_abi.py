@@ -96,17 +96,20 @@ def test_plan_mfma_count_and_flops(name):
 
 
 def test_named_tiles_plan():
-    p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128))
+    p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=1))
     # the pages' formula counts gfx942 K=32 instructions; gfx950 FP8 takes K=128
     assert p["mfma_per_wave_tile"] * 4 == F.mfma_per_tile_pages(64, 256, 128)
     assert p["grid"] == 128 and p["k_tiles"] == 32
     assert p["lds_bytes"] == F.lds_bytes(64, 256, 128, 1)
-    p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64))
+    p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, epilogue=1))
     assert p["grid"] == 2048 and p["k_tiles"] == 128
     assert p["mfma_per_wave_tile"] == 64            # 2 K32 steps x 8 x 4
     assert p["lds_bytes"] == F.lds_bytes(128, 256, 64, 2)
     p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=2))
     assert p["lds_bytes"] == 64 * (256 * 2 + 16)    # padded CShuffle tile
+    # default epilogue: CShuffle for tile_n >= 128 while two workgroups fit a CU
+    assert gp.gemm_plan("bf16", 8192, 8192, 8192)["epilogue"] == gp.EPI_CSHUFFLE
+    assert gp.gemm_plan("int8", 4096, 4096, 4096, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128))["epilogue"] == gp.EPI_DIRECT
 
 
 def test_worked_example_plan():
