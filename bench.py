@@ -91,7 +91,7 @@ def cpu_baseline(name, host, budget_s=12.0):
                       f"(decode + float64 matmul)"}
 
 
-def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True):
+def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib_mib=0):
     import torch
 
     import dense_gemm_preshuffle_amd as gp
@@ -193,9 +193,39 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True):
         "eager_us_per_gemm": eager_ms * 1e3,
         "host_wall_s": wall,
     }
+    tr = _traffic(name, plan)
+    if tr is not None:
+        roof["traffic"] = tr
+    if calib_mib:
+        # a plain device-to-device copy of known size, for scaling the HBM
+        # byte counters of a profiler run (read calib_mib MiB, write calib_mib MiB)
+        src = torch.ones(calib_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     if do_cpu:
         line["cpu_baseline"] = cpu_baseline(name, host)
     return line
+
+
+def _traffic(name, plan):
+    """HBM bytes per launch measured with rocprofv3 counters for this exact
+    kernel source (profiles/traffic.json), or None when stale or absent."""
+    import dense_gemm_preshuffle_amd as gp
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(name)
+    except ValueError:
+        return None
+    if not rec or rec.get("source_hash") != gp.source_hash():
+        return None
+    if rec.get("tile") != [plan["tile_m"], plan["tile_n"], plan["tile_k"]] or rec.get("kernel") != plan["kernel"]:
+        return None
+    return rec.get("traffic_bytes")
 
 
 def main():
@@ -207,6 +237,8 @@ def main():
                     help="one of %s, or 'all'" % ", ".join(sorted(workloads.CONFIGS)))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--opts", default=None, help="JSON gemm_opts override, e.g. '{\"tile_m\":64,...}'")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -221,7 +253,7 @@ def main():
     opts = json.loads(args.opts) if args.opts else None
     for name in names:
         line = bench_one(name, args.steps, args.warmup, do_cpu=not args.no_cpu_baseline, opts=opts,
-                         use_graph=not args.eager)
+                         use_graph=not args.eager, calib_mib=args.calib_copy)
         print(json.dumps(line), flush=True)
 
 

@@ -24,7 +24,7 @@ import re
 __all__ = [
     "GemmError", "GemmLibraryMissing", "GemmOpts", "lib_path", "load_library",
     "gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_plan",
-    "gemm_status_string", "DTYPES", "EPI_DIRECT", "EPI_CSHUFFLE", "KERNEL_TILE", "KERNEL_SPLITK",
+    "gemm_status_string", "source_hash", "DTYPES", "EPI_DIRECT", "EPI_CSHUFFLE", "KERNEL_TILE", "KERNEL_SPLITK",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +92,19 @@ def load_library():
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
+
+
+def source_hash() -> str:
+    """SHA-256 over the HIP sources of the library (identifies a kernel build)."""
+    import hashlib
+
+    csrc = os.path.join(_PKG, "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
 
 
 def header_functions() -> list:
