@@ -35,17 +35,17 @@ int kdt(int dt) {
   }
 }
 
-struct TileVar { int dt, tm, tn, tkb; };
+struct TileVar { int dt, ms, tm, tn, tkb; };
 struct SplitVar { int dt, nb, waves, kch; };
 
-#define GP_TILE_ENTRY(DT, TM, TN, TKB) {DT, TM, TN, TKB},
+#define GP_TILE_ENTRY(DT, MS, TM, TN, TKB) {DT, MS, TM, TN, TKB},
 #define GP_SPLIT_ENTRY(DT, NB, W, KCH) {DT, NB, W, KCH},
 constexpr TileVar kTiles[] = {GP_TILE_ALL(GP_TILE_ENTRY)};
 constexpr SplitVar kSplits[] = {GP_SPLITK_ALL(GP_SPLIT_ENTRY)};
 
-bool tile_compiled(int dt, int tm, int tn, int tkb) {
+bool tile_compiled(int dt, int ms, int tm, int tn, int tkb) {
   for (const auto& v : kTiles)
-    if (v.dt == dt && v.tm == tm && v.tn == tn && v.tkb == tkb) return true;
+    if (v.dt == dt && v.ms == ms && v.tm == tm && v.tn == tn && v.tkb == tkb) return true;
   return false;
 }
 bool split_compiled(int dt, int nb, int waves, int kch) {
@@ -56,6 +56,7 @@ bool split_compiled(int dt, int nb, int waves, int kch) {
 
 struct Plan {
   int kernel = 0;
+  int ms = 16;                  // MFMA block (16 or 32)
   int tm = 0, tn = 0, tkb = 0;  // tile kernel (tkb in bytes)
   int epi = EPI_DIRECT;
   int xcd = 1;
@@ -63,12 +64,25 @@ struct Plan {
   int64_t Kb = 0;
 };
 
-int kernel_mfma_kb(int dt) { return dt == DT_FP8 ? 128 : 64; }
+// K bytes one MFMA consumes (per MS x MS block)
+int kernel_mfma_kb(int dt, int ms) { return ms == 32 ? 32 : (dt == DT_FP8 ? 128 : 64); }
+
+// MFMA block for a tile: 32x32 where it is compiled and asked for (or, by
+// default, for BF16 and FP4, whose 32x32 instructions issue at twice the
+// rate of the 16x16 ones on gfx950), else 16x16.
+int pick_ms(int dt, int tm, int tn, int tkb, int want) {
+  if (want == 16 || want == 32) return tile_compiled(dt, want, tm, tn, tkb) ? want : 0;
+  const bool prefer32 = dt == DT_BF16 || dt == DT_FP4;
+  if (prefer32 && tile_compiled(dt, 32, tm, tn, tkb)) return 32;
+  if (tile_compiled(dt, 16, tm, tn, tkb)) return 16;
+  if (tile_compiled(dt, 32, tm, tn, tkb)) return 32;
+  return 0;
+}
 
 // Default tile preference (largest first) per input type, tile_k in bytes.
 // Named shapes: FP8 medium 64x256x128 (GEMM Optimization Guide §1.3), BF16
 // large 128x256x64 elements, FP4 64-128 x 256 x 256 elements.
-int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
+int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) {
   struct Cand { int tm, tn, tkb; };
   static const Cand i8[] = {{128, 256, 128}, {64, 256, 128}, {64, 128, 128}, {128, 128, 128},
                             {64, 64, 128}, {32, 64, 128}, {16, 64, 256}};
@@ -93,6 +107,7 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
   for (int i = 0; i < n; ++i) {
     const Cand& c = list[i];
     if (M % c.tm || N % c.tn || Kb % c.tkb) continue;
+    if (!pick_ms(dt, c.tm, c.tn, c.tkb, want_ms)) continue;
     const int64_t g = (M / c.tm) * (N / c.tn);
     if (g >= 256) { best = i; break; }
     if (g > best_grid) { best_grid = g; best = i; }
@@ -101,6 +116,7 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
   p->tm = list[best].tm;
   p->tn = list[best].tn;
   p->tkb = list[best].tkb;
+  p->ms = pick_ms(dt, p->tm, p->tn, p->tkb, want_ms);
   return GP_OK;
 }
 
@@ -153,6 +169,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     if (o->tile_m < 0 || o->tile_n < 0 || o->tile_k < 0 || o->waves < 0) return GP_EINVAL;
     if (o->epilogue < 0 || o->epilogue > 2 || o->kernel < 0 || o->kernel > 2) return GP_EINVAL;
     if (o->xcd_swizzle < 0 || o->xcd_swizzle > 2) return GP_EINVAL;
+    if (o->mfma != 0 && o->mfma != 16 && o->mfma != 32) return GP_EINVAL;
   }
   if ((K * bits) % 8) return GP_ESHAPE;
   const int64_t Kb = K * bits / 8;
@@ -172,10 +189,11 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     p->tm = o->tile_m;
     p->tn = o->tile_n;
     p->tkb = (int)((int64_t)o->tile_k * bits / 8);
-    if (!tile_compiled(dt, p->tm, p->tn, p->tkb)) return GP_ESHAPE;
+    p->ms = pick_ms(dt, p->tm, p->tn, p->tkb, o->mfma);
+    if (!p->ms) return GP_ESHAPE;
     if (M % p->tm || N % p->tn || Kb % p->tkb) return GP_ESHAPE;
   } else {
-    const int r = choose_tile(dt, M, N, Kb, p);
+    const int r = choose_tile(dt, M, N, Kb, p, o ? o->mfma : 0);
     if (r) return r;
   }
   if (o && o->epilogue) {
@@ -195,10 +213,12 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
   std::memset(out, 0, sizeof(*out));
   const int bits = elem_bits(in_dtype);
   const int dt = kdt(in_dtype);
-  const int kbm = kernel_mfma_kb(dt);
+  const int ms = p.kernel == GP_KERNEL_TILE ? p.ms : 16;
+  const int kbm = kernel_mfma_kb(dt, ms);
   const int64_t kinstr = (int64_t)kbm * 8 / bits;   // K elements per MFMA
   out->kernel = p.kernel;
-  out->mfma_total = (M / 16) * (N / 16) * (K / kinstr);
+  out->mfma = ms;
+  out->mfma_total = (M / ms) * (N / ms) * (K / kinstr);
   out->xcd_swizzle = p.kernel == GP_KERNEL_TILE ? p.xcd : 2;
   if (p.kernel == GP_KERNEL_TILE) {
     out->tile_m = p.tm;
@@ -215,7 +235,7 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     out->lds_bytes = abuf > cbytes ? abuf : cbytes;
     out->grid = (M / p.tm) * (N / p.tn);
     out->k_tiles = p.Kb / p.tkb;
-    out->mfma_per_wave_tile = (int64_t)(p.tkb / kbm) * (p.tm / 16) * (p.tn / 64);
+    out->mfma_per_wave_tile = (int64_t)(p.tkb / kbm) * (p.tm / ms) * (p.tn / 4 / ms);
   } else {
     out->tile_m = 16;
     out->tile_n = 16 * p.nb;
@@ -267,10 +287,10 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
     t.tiles_n = (uint32_t)(N / p.tn);
     t.xcd = p.xcd == 1 ? 1u : 0u;
     switch (dt) {
-      case DT_I8: e = launch_tile_i8(p.tm, p.tn, p.tkb, p.epi, t, s); break;
-      case DT_FP8: e = launch_tile_fp8(p.tm, p.tn, p.tkb, p.epi, t, s); break;
-      case DT_BF16: e = launch_tile_bf16(p.tm, p.tn, p.tkb, p.epi, t, s); break;
-      default: e = launch_tile_fp4(p.tm, p.tn, p.tkb, p.epi, t, s); break;
+      case DT_I8: e = launch_tile_i8(p.ms, p.tm, p.tn, p.tkb, p.epi, t, s); break;
+      case DT_FP8: e = launch_tile_fp8(p.ms, p.tm, p.tn, p.tkb, p.epi, t, s); break;
+      case DT_BF16: e = launch_tile_bf16(p.ms, p.tm, p.tn, p.tkb, p.epi, t, s); break;
+      default: e = launch_tile_fp4(p.ms, p.tm, p.tn, p.tkb, p.epi, t, s); break;
     }
   } else {
     SplitArgs t;

@@ -5,21 +5,19 @@
 //     waves split TN (each owns TN/4 columns) and share the A tile (§1.1);
 //   * A goes global -> VGPR -> LDS, into one of two LDS buffers (ping-pong,
 //     §2), with an XOR swizzle on 16-byte chunks (§3);
-//   * B goes global -> VGPR directly from the preshuffled layout (§4.2): for
-//     one 16-column block and one 64-byte K block a wave reads one
-//     contiguous KiB, lane l taking 16 bytes;
+//   * B goes global -> VGPR directly from the preshuffled layout (§4.2);
 //   * the next K tile's A and B loads are issued before the current tile's
 //     MFMAs (register double buffer for B, loop-carried, §4.1-§4.4); one
 //     barrier per K tile;
 //   * epilogue: direct store or CShuffle through LDS (§7).
 //
 // Differences from the pages' kernel, for gfx950:
-//   * gfx950 matrix instructions with doubled K: INT8 16x16x64, BF16
-//     16x16x32, FP8 16x16x128 (two 64-byte K blocks per instruction) and the
-//     scaled 16x16x128 FP4 form;
+//   * MS x MS MFMA blocks with MS = 16 or 32 (see Mma<> in gp_common.hpp):
+//     the K-doubled gfx950 instructions, and the 32x32 forms for BF16 / FP4,
+//     which issue at twice the rate of the 16x16 forms on this part;
 //   * the MFMA takes B as its first operand and A as its second, so a lane
-//     ends up holding 4 consecutive COLUMNS of one row of C; the direct store
-//     is then one 8-byte (bf16) or 16-byte (int32) store per lane;
+//     ends up holding runs of 4 consecutive COLUMNS of one row of C; the
+//     direct store is then one 8-byte (bf16) or 16-byte (int32) store;
 //   * the swizzle folds (row / P) into the chunk index, P = rows per 256-byte
 //     LDS bank period: on 64 banks this makes the 16 rows read by one
 //     16-lane phase hit 16 distinct 16-byte bank groups for every row length.
@@ -42,40 +40,45 @@ struct TileArgs {
   uint32_t xcd;       // 1: XCD-aware, grouped tile order
 };
 
-template <int DT, int TM, int TN, int TKB, int EPI>
+template <int DT, int MS, int TM, int TN, int TKB, int EPI>
 struct TileCfg {
+  using S = Mma<DT, MS>;
   static constexpr int THREADS = 256;
   static constexpr int WAVES = 4;
-  static constexpr int KB = Traits<DT>::KB;
-  static constexpr int FRAG = Traits<DT>::FRAG;
+  static constexpr int KB = S::KB;                        // K bytes per MFMA
+  static constexpr int FRAG = S::FRAG;                    // 16-byte pieces per lane per MFMA
   static constexpr int KSTEPS = TKB / KB;
-  static constexpr int MREP = TM / 16;
+  static constexpr int MREP = TM / MS;
   static constexpr int NPW = TN / WAVES;
-  static constexpr int NACC = NPW / 16;
+  static constexpr int NACC = NPW / MS;
+  static constexpr int NREG = S::NREG;
   static constexpr int CPR = TKB / 16;                    // 16-byte chunks per A row
   static constexpr int ACHUNKS = TM * CPR;
   static constexpr int ALOADS = (ACHUNKS + THREADS - 1) / THREADS;
   static constexpr bool APART = (ACHUNKS % THREADS) != 0;
-  static constexpr int ABUF = TM * TKB + (APART ? 16 : 0);   // + a dummy slot for idle lanes
+  static constexpr int ABUF = TM * TKB + (APART ? 16 : 0);   // + a spare slot for idle lanes
   static constexpr int OB = (DT == DT_I8) ? 4 : 2;        // output element bytes
   static constexpr int CSTRIDE = TN * OB + 16;            // padded C row in LDS
   static constexpr int CBYTES = (EPI == EPI_CSHUFFLE) ? TM * CSTRIDE : 0;
   static constexpr int SWP = (TKB >= 256) ? 1 : 256 / TKB;  // rows per 256-byte period
   static constexpr int SWM = ((CPR < 16) ? CPR : 16) - 1;   // chunk xor mask
   static constexpr int NSC = (DT == DT_FP4) ? 1 : 0;
-  // FP4 E8M0 scales of one K tile: SCB bytes per row of A and of B, staged in
-  // LDS beside the A tile as [row][lane group] u16 (byte s = K step s).
-  static constexpr int SCB = NSC ? KSTEPS * 4 : 0;
+  // FP4 E8M0 scales of one K tile: one byte per 16 K-bytes (32 elements), so
+  // SCB = TKB/16 bytes per row of A and of B, staged in LDS beside the A tile
+  // as [row][lane group] entries whose byte s is the scale of K step s:
+  //   MS = 16: 4 lane groups x 2 bytes (KSTEPS <= 2); MS = 32: 2 x 4 bytes.
+  static constexpr int SCB = NSC ? TKB / 16 : 0;
   static constexpr int SROWS = NSC ? TM + TN : 0;
   static constexpr int SLA = NSC ? (TM + THREADS - 1) / THREADS : 0;   // A scale rows per thread
   static constexpr int SLB = NSC ? (TN + THREADS - 1) / THREADS : 0;   // B scale rows per thread
   static constexpr int SLOADS = SLA + SLB;
-  static constexpr int SAREA = NSC ? SROWS * SCB + 16 : 0;   // + a dummy slot for idle lanes
+  static constexpr int SAREA = NSC ? SROWS * SCB + 16 : 0;   // + a spare slot for idle lanes
   static constexpr int STAGE = 2 * ABUF + 2 * SAREA;
   static constexpr int LDS = (STAGE > CBYTES) ? STAGE : CBYTES;
-  static_assert(TM % 16 == 0 && TN % 64 == 0, "tile_m % 16, tile_n % 64");
+  static_assert(TM % MS == 0 && NPW % MS == 0 && TN % 64 == 0, "tile shape");
   static_assert(TKB % KB == 0 && TKB >= 64, "tile_k bytes must be a multiple of the MFMA K bytes");
   static_assert(THREADS % CPR == 0, "A row chunks must divide the workgroup");
+  static_assert(!NSC || TKB == 128 || (MS == 16 && TKB == 64), "FP4 scale staging: 8 (or 4) bytes per row");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -101,17 +104,18 @@ __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uin
   }
 }
 
-template <int DT, int TM, int TN, int TKB, int EPI>
+template <int DT, int MS, int TM, int TN, int TKB, int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
-  using C = TileCfg<DT, TM, TN, TKB, EPI>;
-  using Acc = typename Traits<DT>::Acc;
+  using C = TileCfg<DT, MS, TM, TN, TKB, EPI>;
+  using Acc = typename Mma<DT, MS>::Acc;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int lane_lo = lane & 15;
-  const int lane_hi = lane >> 4;
+  // lane's row / column inside an MFMA block and its K lane group
+  const int lrow = lane & (MS - 1);
+  const int lgrp = lane / MS;
 
   uint32_t tm, tn;
   tile_coords(p, tm, tn);
@@ -148,26 +152,39 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   // access) and write to a spare LDS slot, so the K-tile body has no branch.
   auto a_on = [&](int i) { return !C::APART || i * C::THREADS + tid < C::ACHUNKS; };
   constexpr uint32_t kOOB = 0x80000000u;
-  // A LDS -> VGPR: lane reads row mi*16 + lane_lo, chunk s*KB/16 + f*4 + lane_hi.
-  const int swz = (lane_lo / C::SWP) & C::SWM;
+  // K byte (within one MFMA step) of the lane's 16-byte piece f
+  auto lane_k = [&](int f) -> int { return MS == 16 ? f * 64 + 16 * lgrp : 16 * lgrp; };
+  // A LDS -> VGPR: lane reads row mi*MS + lrow, chunk (s*KB + lane_k(f)) / 16.
+  // The XOR term depends on the row only through lrow (MS*mi/SWP is a whole
+  // number of swizzle periods), so one address per (s, f) serves every mi.
+  const int swz = (lrow / C::SWP) & C::SWM;
   uint32_t a_rd[C::KSTEPS][C::FRAG];
 #pragma unroll
   for (int s = 0; s < C::KSTEPS; ++s)
 #pragma unroll
     for (int f = 0; f < C::FRAG; ++f)
-      a_rd[s][f] = lane_lo * TKB + (((s * (C::KB / 16) + f * 4 + lane_hi) ^ swz) * 16);
-  // B: the wave's first 16-column block; block ni adds ni*16*Kb (uniform).
-  const uint32_t b_off0 = (uint32_t)(wave * C::NACC) * 16u * Kb + lane * 16;
-  const uint32_t b_step = 16u * Kb;
+      a_rd[s][f] = lrow * TKB + ((((s * C::KB + lane_k(f)) / 16) ^ swz) * 16);
+  // B: column c = wave*NPW + lrow of the wave's first MFMA block lies in
+  // 16-column block c/16, lane j = c%16 of it; the lane's K piece is 16-byte
+  // group g of a 64-byte K block: offset blk*16*Kb + k0*1024 + g*256 + j*16.
+  const int bcol = wave * C::NPW + lrow;
+  const uint32_t b_off0 = (uint32_t)(bcol / 16) * 16u * Kb + (uint32_t)(bcol % 16) * 16u + (uint32_t)lgrp * 256u;
+  const uint32_t b_step = (uint32_t)(MS / 16) * 16u * Kb;  // next MFMA column block
+  // K-step part of the B offset (uniform): MS = 16: K block s*(KB/64)+f; MS = 32:
+  // step s covers K bytes [32s, 32s+32) = block s/2, groups 2*(s%2) + lgrp.
+  auto b_koff = [&](int s, int f) -> uint32_t {
+    if constexpr (MS == 16) return (uint32_t)(s * (C::KB / 64) + f) * 1024u;
+    else return (uint32_t)s * 512u;
+  };
 
   // FP4 block scales: one E8M0 byte per 32 K elements (= 16 bytes of K).
   const uint32_t srow = Kb / 16;  // scale bytes per row
   __amdgpu_buffer_rsrc_t rsa = make_rsrc(nullptr, 0), rsb = make_rsrc(nullptr, 0);
   if constexpr (DT == DT_FP4) {
-    static_assert(C::KSTEPS <= 2, "FP4 tile_k bytes <= 128");
     rsa = make_rsrc((const char*)p.sa + (size_t)m0 * srow, TM * srow);
     rsb = make_rsrc((const char*)p.sb + (size_t)n0 * srow, TN * srow);
   }
+
   v4i a_st[C::ALOADS];
   v4i bfr[2][C::KSTEPS][C::NACC][C::FRAG];
   v2i sa_st[C::SLA + 1 - C::NSC], sb_st[C::SLB + 1 - C::NSC];
@@ -175,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
   for (int mi = 0; mi < C::MREP; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < C::NACC; ++ni) acc[mi][ni] = Acc{0, 0, 0, 0};
+    for (int ni = 0; ni < C::NACC; ++ni) acc[mi][ni] = Acc{};
 
   auto load_a = [&](int kt) {
 #pragma unroll
@@ -197,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
       for (int ni = 0; ni < C::NACC; ++ni)
 #pragma unroll
         for (int f = 0; f < C::FRAG; ++f)
-          bfr[par][s][ni][f] = buf_load16(rb, b_off0 + (s * (C::KB / 64) + f) * 1024, kbase + ni * b_step);
+          bfr[par][s][ni][f] = buf_load16(rb, b_off0 + b_koff(s, f), kbase + ni * b_step);
   };
   // FP4: the WG's TM + TN scale rows of one K tile, SCB bytes each. A and B
   // rows use separate loads so that each load's buffer resource is uniform.
@@ -208,26 +225,33 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
       for (int i = 0; i < C::SLA; ++i) {
         const int r = i * C::THREADS + tid;
         const uint32_t off = r < TM ? r * srow : kOOB;
-        if constexpr (C::KSTEPS == 2) sa_st[i] = buf_load8(rsa, off, sbase);
+        if constexpr (C::SCB == 8) sa_st[i] = buf_load8(rsa, off, sbase);
         else sa_st[i][0] = buf_load4(rsa, off, sbase);
       }
 #pragma unroll
       for (int i = 0; i < C::SLB; ++i) {
         const int r = i * C::THREADS + tid;
         const uint32_t off = r < TN ? r * srow : kOOB;
-        if constexpr (C::KSTEPS == 2) sb_st[i] = buf_load8(rsb, off, sbase);
+        if constexpr (C::SCB == 8) sb_st[i] = buf_load8(rsb, off, sbase);
         else sb_st[i][0] = buf_load4(rsb, off, sbase);
       }
     }
   };
-  // scale row r (A rows first, then B rows) -> LDS as [row][lane group] u16;
-  // row SROWS is the spare slot of idle lanes
+  // scale row r (A rows first, then B rows) -> LDS as [row][lane group];
+  // row SROWS is the spare slot of idle lanes. Byte b of the row is the scale
+  // of K bytes [16b, 16b+16) of the tile.
   auto put_s = [&](char* base, int r, v2i v) {
-    if constexpr (C::KSTEPS == 2) {
-      // bytes b = 4*s + g  ->  u16 per lane group g: (s=0, s=1)
+    if constexpr (C::SCB == 8) {
       v2i w;
-      w[0] = (int)__builtin_amdgcn_perm((uint32_t)v[1], (uint32_t)v[0], 0x05010400u);
-      w[1] = (int)__builtin_amdgcn_perm((uint32_t)v[1], (uint32_t)v[0], 0x07030602u);
+      if constexpr (MS == 16) {
+        // group g (K step s uses block 4s+g): u16 (b_g, b_{4+g})
+        w[0] = (int)__builtin_amdgcn_perm((uint32_t)v[1], (uint32_t)v[0], 0x05010400u);
+        w[1] = (int)__builtin_amdgcn_perm((uint32_t)v[1], (uint32_t)v[0], 0x07030602u);
+      } else {
+        // group q (K step s uses block 2s+q): u32 (b_q, b_{2+q}, b_{4+q}, b_{6+q})
+        w[0] = (int)__builtin_amdgcn_perm((uint32_t)v[1], (uint32_t)v[0], 0x06040200u);
+        w[1] = (int)__builtin_amdgcn_perm((uint32_t)v[1], (uint32_t)v[0], 0x07050301u);
+      }
       *(v2i*)(base + r * 8) = w;
     } else {
       *(int*)(base + r * 4) = v[0];
@@ -248,11 +272,20 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
       }
     }
   };
+  // lane's scale entry of staged row r
+  auto read_s = [&](const char* sbase, int r) -> int {
+    if constexpr (C::SCB == 8) {
+      if constexpr (MS == 16) return *(const uint16_t*)(sbase + r * 8 + lgrp * 2);
+      else return *(const int*)(sbase + r * 8 + lgrp * 4);
+    } else {
+      return *(const uint8_t*)(sbase + r * 4 + lgrp);
+    }
+  };
   // ds_read of A fragment (s, mi) from buffer par
   auto read_a = [&](int par, int s, int mi, v4i* af) {
     const char* base = lds + par * C::ABUF;
 #pragma unroll
-    for (int f = 0; f < C::FRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * 16 * TKB);
+    for (int f = 0; f < C::FRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * MS * TKB);
   };
   auto compute = [&](auto par_c) {
     constexpr int par = decltype(par_c)::value;
@@ -261,17 +294,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
     if constexpr (DT == DT_FP4) {
       const char* sb = lds + 2 * C::ABUF + par * C::SAREA;
 #pragma unroll
-      for (int mi = 0; mi < C::MREP; ++mi) {
-        const int r = mi * 16 + lane_lo;
-        if constexpr (C::KSTEPS == 2) psa[mi] = *(const uint16_t*)(sb + r * 8 + lane_hi * 2);
-        else psa[mi] = *(const uint8_t*)(sb + r * 4 + lane_hi);
-      }
+      for (int mi = 0; mi < C::MREP; ++mi) psa[mi] = read_s(sb, mi * MS + lrow);
 #pragma unroll
-      for (int ni = 0; ni < C::NACC; ++ni) {
-        const int r = TM + wave * C::NPW + ni * 16 + lane_lo;
-        if constexpr (C::KSTEPS == 2) psb[ni] = *(const uint16_t*)(sb + r * 8 + lane_hi * 2);
-        else psb[ni] = *(const uint8_t*)(sb + r * 4 + lane_hi);
-      }
+      for (int ni = 0; ni < C::NACC; ++ni) psb[ni] = read_s(sb, TM + wave * C::NPW + ni * MS + lrow);
     }
     constexpr int NF = C::KSTEPS * C::MREP;
     v4i af[2][C::FRAG];
@@ -283,12 +308,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
       for (int ni = 0; ni < C::NACC; ++ni) {
         if constexpr (DT == DT_FP4) {
-          if (s == 0)
-            acc[mi][ni] = mfma_fp4_sel<0>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]);
-          else
-            acc[mi][ni] = mfma_fp4_sel<1>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]);
+          switch (s) {
+            case 0: acc[mi][ni] = mma<DT, MS, 0>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]); break;
+            case 1: acc[mi][ni] = mma<DT, MS, 1>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]); break;
+            case 2: acc[mi][ni] = mma<DT, MS, 2>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]); break;
+            default: acc[mi][ni] = mma<DT, MS, 3>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]); break;
+          }
         } else {
-          acc[mi][ni] = mfma<DT>(bfr[par][s][ni], af[i & 1], acc[mi][ni]);
+          acc[mi][ni] = mma<DT, MS>(bfr[par][s][ni], af[i & 1], acc[mi][ni]);
         }
       }
     }
@@ -341,26 +368,36 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   if (kt < KT) iter(std::integral_constant<int, 0>{}, kt);
 
   // ---- epilogue ----
-  // lane holds C[m0 + mi*16 + lane_lo][n0 + wave*NPW + ni*16 + 4*lane_hi + r], r = 0..3
+  // For every (mi, ni) the lane holds NREG/4 runs of 4 consecutive columns
+  // of row mi*MS + lrow: run h covers columns ni*MS + col_run(h) + 0..3.
+  auto col_run = [&](int h) -> int { return MS == 16 ? 4 * lgrp : 8 * h + 4 * lgrp; };
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c + ((size_t)m0 * p.N + n0) * C::OB, ((TM - 1) * p.N + TN) * C::OB);
-  v4f sbv[C::NACC];
+  v4f sbv[C::NACC][C::NREG / 4];
   float sav[C::MREP];
   if constexpr (DT == DT_FP8) {
     const float* sa = (const float*)p.sa + m0;
     const float* sb = (const float*)p.sb + n0;
 #pragma unroll
-    for (int mi = 0; mi < C::MREP; ++mi) sav[mi] = sa[mi * 16 + lane_lo];
+    for (int mi = 0; mi < C::MREP; ++mi) sav[mi] = sa[mi * MS + lrow];
 #pragma unroll
-    for (int ni = 0; ni < C::NACC; ++ni) sbv[ni] = *(const v4f*)(sb + wave * C::NPW + ni * 16 + 4 * lane_hi);
+    for (int ni = 0; ni < C::NACC; ++ni)
+#pragma unroll
+      for (int h = 0; h < C::NREG / 4; ++h)
+        sbv[ni][h] = *(const v4f*)(sb + wave * C::NPW + ni * MS + col_run(h));
   }
-  auto out_vec = [&](int mi, int ni, auto emit) {
+  auto out_vec = [&](int mi, int ni, int h, auto emit) {
     if constexpr (DT == DT_I8) {
-      emit(acc[mi][ni]);
+      v4i v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * h + r];
+      emit(v);
     } else {
-      v4f v = acc[mi][ni];
+      v4f v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * h + r];
       if constexpr (DT == DT_FP8) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (v[r] * sav[mi]) * sbv[ni][r];
+        for (int r = 0; r < 4; ++r) v[r] = (v[r] * sav[mi]) * sbv[ni][h][r];
       }
       v2i o;
       o[0] = (int)pack_bf16x2(v[0], v[1]);
@@ -373,23 +410,27 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
     for (int mi = 0; mi < C::MREP; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < C::NACC; ++ni) {
-        const uint32_t off = ((mi * 16 + lane_lo) * p.N + wave * C::NPW + ni * 16 + 4 * lane_hi) * C::OB;
-        out_vec(mi, ni, [&](auto v) {
-          if constexpr (sizeof(v) == 16) buf_store16(v, rc, off);
-          else buf_store8(v, rc, off);
-        });
-      }
+      for (int ni = 0; ni < C::NACC; ++ni)
+#pragma unroll
+        for (int h = 0; h < C::NREG / 4; ++h) {
+          const uint32_t off = ((mi * MS + lrow) * p.N + wave * C::NPW + ni * MS + col_run(h)) * C::OB;
+          out_vec(mi, ni, h, [&](auto v) {
+            if constexpr (sizeof(v) == 16) buf_store16(v, rc, off);
+            else buf_store8(v, rc, off);
+          });
+        }
   } else {
     // CShuffle: stage the tile in LDS (the A buffers are dead after the last
     // barrier), then write whole rows with 16-byte stores.
 #pragma unroll
     for (int mi = 0; mi < C::MREP; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < C::NACC; ++ni) {
-        char* dst = lds + (mi * 16 + lane_lo) * C::CSTRIDE + (wave * C::NPW + ni * 16 + 4 * lane_hi) * C::OB;
-        out_vec(mi, ni, [&](auto v) { *(decltype(v)*)dst = v; });
-      }
+      for (int ni = 0; ni < C::NACC; ++ni)
+#pragma unroll
+        for (int h = 0; h < C::NREG / 4; ++h) {
+          char* dst = lds + (mi * MS + lrow) * C::CSTRIDE + (wave * C::NPW + ni * MS + col_run(h)) * C::OB;
+          out_vec(mi, ni, h, [&](auto v) { *(decltype(v)*)dst = v; });
+        }
     __syncthreads();
     constexpr int CH_ROW = TN * C::OB / 16;
     constexpr int TOTAL = TM * CH_ROW;

@@ -7,12 +7,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gp {
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 enum DType : int { DT_I8 = 0, DT_FP8 = 1, DT_BF16 = 2, DT_FP4 = 3 };
@@ -95,6 +99,52 @@ mfma(const v4i* x, const v4i* y, typename Traits<DT>::Acc acc, int sx = 0, int s
 template <int SEL>
 __device__ __forceinline__ v4f mfma_fp4_sel(const v4i* x, const v4i* y, v4f acc, int sx, int sy) {
   return mfma_scale_16x16x128_v4(x[0], y[0], acc, 4, 4, SEL, sx, SEL, sy);
+}
+
+__device__ v16f mfma_scale_32x32x64_v4(v4i a, v4i b, v16f c, int cbsz, int blgp, int opsel_a, int scale_a,
+                                       int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v4i32.v4i32");
+
+// MFMA shape: MS x MS output block per instruction.
+//   MS = 16: lane l supplies row/column l%16 and the 16-byte K piece(s) of
+//            lane group l/16; result D[4*(l/16)+r][l%16] in 4 registers.
+//   MS = 32: lane l supplies row/column l%32 and the 16-byte K piece of lane
+//            group l/32; result D[8*i+4*(l/32)+j][l%32] in register 4*i+j.
+// On gfx950 the 32x32 BF16 (32x32x16) and FP4 (32x32x64) forms issue at twice
+// the rate of their 16x16 forms; FP8 16x16x128 already runs at full rate.
+template <int DT, int MS> struct Mma;
+template <int DT> struct Mma<DT, 16> {
+  static constexpr int KB = Traits<DT>::KB;     // K bytes per instruction
+  static constexpr int FRAG = Traits<DT>::FRAG; // 16-byte pieces per lane
+  static constexpr int NREG = 4;                // result registers per lane
+  using Acc = typename Traits<DT>::Acc;
+};
+template <int DT> struct Mma<DT, 32> {
+  static_assert(DT != DT_FP8, "FP8 uses the 16x16x128 instruction");
+  static constexpr int KB = 32;
+  static constexpr int FRAG = 1;
+  static constexpr int NREG = 16;
+  using Acc = std::conditional_t<DT == DT_I8, v16i, v16f>;
+};
+
+// One MS x MS MFMA. X is the first operand, Y the second; FP4 scales sx / sy
+// sit in byte SEL of their registers.
+template <int DT, int MS, int SEL = 0>
+__device__ __forceinline__ typename Mma<DT, MS>::Acc mma(const v4i* x, const v4i* y, typename Mma<DT, MS>::Acc acc,
+                                                         int sx = 0, int sy = 0) {
+  if constexpr (MS == 16) {
+    if constexpr (DT == DT_FP4) return mfma_scale_16x16x128_v4(x[0], y[0], acc, 4, 4, SEL, sx, SEL, sy);
+    else return mfma<DT>(x, y, acc);
+  } else {
+    if constexpr (DT == DT_I8) {
+      return __builtin_amdgcn_mfma_i32_32x32x32_i8(x[0], y[0], acc, 0, 0, 0);
+    } else if constexpr (DT == DT_BF16) {
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, x[0]), __builtin_bit_cast(v8bf, y[0]), acc,
+                                                     0, 0, 0);
+    } else {
+      return mfma_scale_32x32x64_v4(x[0], y[0], acc, 4, 4, SEL, sx, SEL, sy);
+    }
+  }
 }
 
 // fp32 -> bf16 with round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).

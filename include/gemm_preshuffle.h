@@ -78,6 +78,7 @@ typedef struct gemm_opts {
   int kernel;       /* GP_KERNEL_*                                       */
   int xcd_swizzle;  /* 0 auto, 1 XCD-aware grouped tile order, 2 linear  */
   int waves;        /* split-K kernel: waves per workgroup (0 auto)      */
+  int mfma;         /* tile kernel: MFMA block 16 (16x16) or 32 (32x32), 0 auto */
 } gemm_opts;
 
 /* What the planner chose (host-side query, no GPU needed). */
@@ -93,6 +94,7 @@ typedef struct gemm_plan_info {
   int64_t k_tiles;                  /* K tiles per workgroup (tile kernel)      */
   int64_t mfma_per_wave_tile;       /* MFMA instructions per wave per K tile    */
   int64_t mfma_total;               /* MFMA instructions for the whole problem  */
+  int mfma;                         /* MFMA block: 16 (16x16) or 32 (32x32)     */
 } gemm_plan_info;
 
 /*

@@ -11,15 +11,18 @@ GEMM Optimization Guide:
   §14   the worked 5120 x 5120 x 8320 FP8 example.
 
 gfx950 instruction counts: the gfx950 matrix cores take 64 K-bytes per
-instruction for INT8 (16x16x64), BF16 (16x16x32) and FP4 (16x16x128 at half a
-byte), and 128 K-bytes for FP8 (16x16x128). Whatever the instruction, the
-count of 16x16xK instructions for a whole problem is (M/16)(N/16)(K/K_instr)
-and each does 2*16*16*K_instr flops, which must add up to 2MNK.
+16x16 instruction for INT8 (16x16x64), BF16 (16x16x32) and FP4 (16x16x128 at
+half a byte), and 128 K-bytes for FP8 (16x16x128); the 32x32 forms take half
+the K (32x32x32 INT8, 32x32x16 BF16, 32x32x64 FP8/FP4). Whatever the
+instruction, the count of ms x ms x K_instr instructions for a whole problem
+is (M/ms)(N/ms)(K/K_instr) and each does 2*ms*ms*K_instr flops, which must add
+up to 2MNK.
 """
 from __future__ import annotations
 
 ELEM_BYTES = {"int8": 1.0, "fp8": 1.0, "bf16": 2.0, "fp16": 2.0, "mxfp4": 0.5, "int4": 0.5}
-K_INSTR_GFX950 = {"int8": 64, "fp8": 128, "bf16": 32, "mxfp4": 128}
+K_INSTR_GFX950 = {"int8": 64, "fp8": 128, "bf16": 32, "mxfp4": 128}          # 16x16 blocks
+K_INSTR_GFX950_32 = {"int8": 32, "fp8": 64, "bf16": 16, "mxfp4": 64}         # 32x32 blocks
 
 
 def derived(tile_m: int, tile_n: int, tile_k: int, elem_bytes: float = 1.0) -> dict:
@@ -97,10 +100,14 @@ def bytes_moved(dtype: str, M: int, N: int, K: int, out_bytes: int = 2) -> int:
     raise ValueError(dtype)
 
 
-def mfma_count_gfx950(dtype: str, M: int, N: int, K: int) -> int:
-    """Number of 16x16xK_instr gfx950 MFMA instructions for the whole problem."""
-    return (M // 16) * (N // 16) * (K // K_INSTR_GFX950[dtype])
+def _k_instr(dtype: str, ms: int) -> int:
+    return K_INSTR_GFX950[dtype] if ms == 16 else K_INSTR_GFX950_32[dtype]
 
 
-def flops_per_mfma_gfx950(dtype: str) -> int:
-    return 2 * 16 * 16 * K_INSTR_GFX950[dtype]
+def mfma_count_gfx950(dtype: str, M: int, N: int, K: int, ms: int = 16) -> int:
+    """Number of ms x ms x K_instr gfx950 MFMA instructions for the whole problem."""
+    return (M // ms) * (N // ms) * (K // _k_instr(dtype, ms))
+
+
+def flops_per_mfma_gfx950(dtype: str, ms: int = 16) -> int:
+    return 2 * ms * ms * _k_instr(dtype, ms)

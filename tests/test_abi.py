@@ -90,8 +90,8 @@ def test_options_validation():
 def test_plan_mfma_count_and_flops(name):
     dtype, M, N, K, _, _ = CONFIGS[name]
     p = gp.gemm_plan(dtype, M, N, K)
-    assert p["mfma_total"] == F.mfma_count_gfx950(dtype, M, N, K)
-    assert p["mfma_total"] * F.flops_per_mfma_gfx950(dtype) == F.flops(M, N, K)
+    assert p["mfma_total"] == F.mfma_count_gfx950(dtype, M, N, K, p["mfma"])
+    assert p["mfma_total"] * F.flops_per_mfma_gfx950(dtype, p["mfma"]) == F.flops(M, N, K)
     assert p["grid"] > 0 and p["threads"] in (256, 512)
 
 
@@ -99,11 +99,13 @@ def test_named_tiles_plan():
     p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=1))
     # the pages' formula counts gfx942 K=32 instructions; gfx950 FP8 takes K=128
     assert p["mfma_per_wave_tile"] * 4 == F.mfma_per_tile_pages(64, 256, 128)
-    assert p["grid"] == 128 and p["k_tiles"] == 32
+    assert p["grid"] == 128 and p["k_tiles"] == 32 and p["mfma"] == 16
     assert p["lds_bytes"] == F.lds_bytes(64, 256, 128, 1)
-    p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, epilogue=1))
+    p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, epilogue=1, mfma=16))
     assert p["grid"] == 2048 and p["k_tiles"] == 128
     assert p["mfma_per_wave_tile"] == 64            # 2 K32 steps x 8 x 4
+    p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, epilogue=1))
+    assert p["mfma"] == 32 and p["mfma_per_wave_tile"] == 32   # 4 K16 steps x 4 x 2 (32x32 blocks)
     assert p["lds_bytes"] == F.lds_bytes(128, 256, 64, 2)
     p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=2))
     assert p["lds_bytes"] == 64 * (256 * 2 + 16)    # padded CShuffle tile

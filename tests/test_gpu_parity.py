@@ -63,6 +63,16 @@ TILE_CASES = [
     ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256)),
     ("mxfp4", 256, 256, 512, dict(kernel=1, tile_m=128, tile_n=128, tile_k=256, epilogue=2)),
     ("mxfp4", 64, 256, 1024, dict(kernel=1, tile_m=32, tile_n=256, tile_k=256)),
+    # 32x32 MFMA blocks (BF16, FP4, INT8)
+    ("bf16", 128, 512, 192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32)),
+    ("bf16", 128, 256, 320, dict(kernel=1, tile_m=128, tile_n=256, tile_k=32, mfma=32, epilogue=1)),
+    ("bf16", 128, 256, 192, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64, mfma=32, epilogue=2)),
+    ("bf16", 256, 256, 128, dict(kernel=1, tile_m=128, tile_n=128, tile_k=64, mfma=32)),
+    ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32)),
+    ("mxfp4", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=32, epilogue=1)),
+    ("mxfp4", 256, 256, 768, dict(kernel=1, tile_m=128, tile_n=128, tile_k=256, mfma=32)),
+    ("int8", 128, 256, 384, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, mfma=32)),
+    ("int8", 128, 512, 256, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, mfma=32, epilogue=2)),
     # small-M split-K kernel
     ("fp8", 16, 512, 2048, dict(kernel=2)),
     ("fp8", 32, 256, 1024, dict(kernel=2, tile_n=32)),
@@ -114,6 +124,9 @@ def _one_hot_b(dtype, N, K, perm):
 
 
 PERM_CASES = [("int8", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128)),
+              ("int8", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, mfma=32)),
+              ("bf16", 128, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32)),
+              ("mxfp4", 128, 256, 512, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32)),
               ("fp8", 128, 512, 384, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128)),
               ("fp8", 16, 256, 1024, dict(kernel=2)),
               ("bf16", 256, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64)),
@@ -164,8 +177,10 @@ def test_bf16_single_products_round_to_nearest_even():
     a[:, 5] = (rng.integers(0, 2 ** 16, M).astype(np.uint16) & 0x3FFF) | 0x3C00
     b[:, 5] = (rng.integers(0, 2 ** 16, N).astype(np.uint16) & 0xBFFF) | 0x3800
     host = {"a": a, "b": b}
-    out = gpu_run("bf16", host, dict(kernel=1, tile_m=128, tile_n=256, tile_k=32))
-    assert np.array_equal(oracle.decode_bf16(out), oracle.bf16_rne(oracle.gemm("bf16", host)))
+    for opts in (dict(kernel=1, tile_m=128, tile_n=256, tile_k=32, mfma=16),
+                 dict(kernel=1, tile_m=128, tile_n=256, tile_k=32, mfma=32)):
+        out = gpu_run("bf16", host, opts)
+        assert np.array_equal(oracle.decode_bf16(out), oracle.bf16_rne(oracle.gemm("bf16", host))), opts
 
 
 def test_fp4_exhaustive_codes_and_scales_bit_exact():
@@ -186,9 +201,11 @@ def test_fp4_exhaustive_codes_and_scales_bit_exact():
     assert np.array_equal(oracle.decode_bf16(out), oracle.gemm("mxfp4", host))
 
 
-@pytest.mark.parametrize("opts", [dict(kernel=1, tile_m=64, tile_n=256, tile_k=256),
-                                  dict(kernel=1, tile_m=128, tile_n=256, tile_k=256),
-                                  dict(kernel=2)], ids=["t64", "t128", "splitk"])
+@pytest.mark.parametrize("opts", [dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=16),
+                                  dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=16),
+                                  dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32),
+                                  dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, mfma=32),
+                                  dict(kernel=2)], ids=["t64", "t128", "t128m32", "t64x128m32", "splitk"])
 def test_fp4_block_scale_placement_bit_exact(opts):
     say(f"fp4 scale placement {opts}")
     rng = np.random.default_rng(4)
