@@ -51,7 +51,7 @@ class GemmLibraryMissing(ImportError):
 class GemmOpts(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
                 ("epilogue", ctypes.c_int), ("kernel", ctypes.c_int), ("xcd_swizzle", ctypes.c_int),
-                ("waves", ctypes.c_int), ("mfma", ctypes.c_int)]
+                ("waves", ctypes.c_int), ("mfma", ctypes.c_int), ("pipeline", ctypes.c_int)]
 
 
 class GemmPlanInfo(ctypes.Structure):
@@ -60,7 +60,7 @@ class GemmPlanInfo(ctypes.Structure):
                 ("waves", ctypes.c_int), ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
                 ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64),
                 ("mfma_per_wave_tile", ctypes.c_int64), ("mfma_total", ctypes.c_int64),
-                ("mfma", ctypes.c_int)]
+                ("mfma", ctypes.c_int), ("pipeline", ctypes.c_int)]
 
 
 _lib = None

@@ -35,18 +35,34 @@ int kdt(int dt) {
   }
 }
 
-struct TileVar { int dt, ms, tm, tn, tkb; };
+struct TileVar { int dt, ms, tm, tn, tkb, pipe; };
 struct SplitVar { int dt, nb, waves, kch; };
 
-#define GP_TILE_ENTRY(DT, MS, TM, TN, TKB) {DT, MS, TM, TN, TKB},
+#define GP_TILE_ENTRY(DT, MS, TM, TN, TKB, PIPE) {DT, MS, TM, TN, TKB, PIPE},
 #define GP_SPLIT_ENTRY(DT, NB, W, KCH) {DT, NB, W, KCH},
 constexpr TileVar kTiles[] = {GP_TILE_ALL(GP_TILE_ENTRY)};
 constexpr SplitVar kSplits[] = {GP_SPLITK_ALL(GP_SPLIT_ENTRY)};
 
-bool tile_compiled(int dt, int ms, int tm, int tn, int tkb) {
+bool tile_compiled(int dt, int ms, int tm, int tn, int tkb, int pipe = -1) {
   for (const auto& v : kTiles)
-    if (v.dt == dt && v.ms == ms && v.tm == tm && v.tn == tn && v.tkb == tkb) return true;
+    if (v.dt == dt && v.ms == ms && v.tm == tm && v.tn == tn && v.tkb == tkb && (pipe < 0 || v.pipe == pipe))
+      return true;
   return false;
+}
+
+// Pipeline for a compiled tile: the caller's (opts.pipeline 1 = VGPR-staged
+// A, 2 / 3 = LDS DMA with 2 / 3 stages), else the deepest compiled one.
+int pick_pipe(int dt, int ms, int tm, int tn, int tkb, int want) {
+  if (want > 0) {
+    const int pipe = want == 1 ? 0 : want;
+    return tile_compiled(dt, ms, tm, tn, tkb, pipe) ? pipe : -1;
+  }
+  // FP4's 3-stage variant spills at 128x256; elsewhere the deepest wins
+  const int order[3][3] = {{3, 2, 0}, {2, 3, 0}, {0, 0, 0}};
+  const int* ord = dt == DT_FP4 ? order[1] : order[0];
+  for (int k = 0; k < 3; ++k)
+    if (tile_compiled(dt, ms, tm, tn, tkb, ord[k])) return ord[k];
+  return -1;
 }
 bool split_compiled(int dt, int nb, int waves, int kch) {
   for (const auto& v : kSplits)
@@ -57,6 +73,7 @@ bool split_compiled(int dt, int nb, int waves, int kch) {
 struct Plan {
   int kernel = 0;
   int ms = 16;                  // MFMA block (16 or 32)
+  int pipe = 0;                 // 0 VGPR-staged A, 2 / 3 LDS DMA stages
   int tm = 0, tn = 0, tkb = 0;  // tile kernel (tkb in bytes)
   int epi = EPI_DIRECT;
   int xcd = 1;
@@ -67,12 +84,13 @@ struct Plan {
 // K bytes one MFMA consumes (per MS x MS block)
 int kernel_mfma_kb(int dt, int ms) { return ms == 32 ? 32 : (dt == DT_FP8 ? 128 : 64); }
 
-// MFMA block for a tile: 32x32 where it is compiled and asked for (or, by
-// default, for BF16 and FP4, whose 32x32 instructions issue at twice the
-// rate of the 16x16 ones on gfx950), else 16x16.
+// MFMA block for a tile: the caller's, else 32x32 for FP4 (measured faster
+// on the MXFP4 4096x4096x8192 shape), else 16x16 where compiled. (BF16
+// measures the same with either block at 128x256: its loop is bound by the
+// operand loads, not by the MFMA issue rate.)
 int pick_ms(int dt, int tm, int tn, int tkb, int want) {
   if (want == 16 || want == 32) return tile_compiled(dt, want, tm, tn, tkb) ? want : 0;
-  const bool prefer32 = dt == DT_BF16 || dt == DT_FP4;
+  const bool prefer32 = dt == DT_FP4;
   if (prefer32 && tile_compiled(dt, 32, tm, tn, tkb)) return 32;
   if (tile_compiled(dt, 16, tm, tn, tkb)) return 16;
   if (tile_compiled(dt, 32, tm, tn, tkb)) return 32;
@@ -170,6 +188,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     if (o->epilogue < 0 || o->epilogue > 2 || o->kernel < 0 || o->kernel > 2) return GP_EINVAL;
     if (o->xcd_swizzle < 0 || o->xcd_swizzle > 2) return GP_EINVAL;
     if (o->mfma != 0 && o->mfma != 16 && o->mfma != 32) return GP_EINVAL;
+    if (o->pipeline < 0 || o->pipeline > 3) return GP_EINVAL;
   }
   if ((K * bits) % 8) return GP_ESHAPE;
   const int64_t Kb = K * bits / 8;
@@ -191,10 +210,14 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     p->tkb = (int)((int64_t)o->tile_k * bits / 8);
     p->ms = pick_ms(dt, p->tm, p->tn, p->tkb, o->mfma);
     if (!p->ms) return GP_ESHAPE;
+    p->pipe = pick_pipe(dt, p->ms, p->tm, p->tn, p->tkb, o->pipeline);
+    if (p->pipe < 0) return GP_ESHAPE;
     if (M % p->tm || N % p->tn || Kb % p->tkb) return GP_ESHAPE;
   } else {
     const int r = choose_tile(dt, M, N, Kb, p, o ? o->mfma : 0);
     if (r) return r;
+    p->pipe = pick_pipe(dt, p->ms, p->tm, p->tn, p->tkb, o ? o->pipeline : 0);
+    if (p->pipe < 0) return GP_ESHAPE;
   }
   if (o && o->epilogue) {
     p->epi = o->epilogue;
@@ -218,6 +241,7 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
   const int64_t kinstr = (int64_t)kbm * 8 / bits;   // K elements per MFMA
   out->kernel = p.kernel;
   out->mfma = ms;
+  out->pipeline = p.kernel == GP_KERNEL_TILE ? (p.pipe ? p.pipe : 1) : 0;
   out->mfma_total = (M / ms) * (N / ms) * (K / kinstr);
   out->xcd_swizzle = p.kernel == GP_KERNEL_TILE ? p.xcd : 2;
   if (p.kernel == GP_KERNEL_TILE) {
@@ -229,8 +253,9 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     out->threads = 256;
     const int ob = in_dtype == GP_I8 ? 4 : 2;
     const bool apart = (p.tm * (p.tkb / 16)) % 256 != 0;
-    int abuf = 2 * (p.tm * p.tkb + (apart ? 16 : 0));
-    if (dt == DT_FP4) abuf += 2 * ((p.tm + p.tn) * (p.tkb / 64) * 4 + 16);  // staged E8M0 scales
+    const int stages = p.pipe ? p.pipe : 2;
+    int abuf = stages * (p.tm * p.tkb + (apart ? 16 : 0));
+    if (dt == DT_FP4) abuf += stages * ((p.tm + p.tn) * (p.tkb / 16) + 16);  // staged E8M0 scales
     const int cbytes = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
     out->lds_bytes = abuf > cbytes ? abuf : cbytes;
     out->grid = (M / p.tm) * (N / p.tn);
@@ -287,10 +312,10 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
     t.tiles_n = (uint32_t)(N / p.tn);
     t.xcd = p.xcd == 1 ? 1u : 0u;
     switch (dt) {
-      case DT_I8: e = launch_tile_i8(p.ms, p.tm, p.tn, p.tkb, p.epi, t, s); break;
-      case DT_FP8: e = launch_tile_fp8(p.ms, p.tm, p.tn, p.tkb, p.epi, t, s); break;
-      case DT_BF16: e = launch_tile_bf16(p.ms, p.tm, p.tn, p.tkb, p.epi, t, s); break;
-      default: e = launch_tile_fp4(p.ms, p.tm, p.tn, p.tkb, p.epi, t, s); break;
+      case DT_I8: e = launch_tile_i8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;
+      case DT_FP8: e = launch_tile_fp8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;
+      case DT_BF16: e = launch_tile_bf16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;
+      default: e = launch_tile_fp4(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;
     }
   } else {
     SplitArgs t;

@@ -40,7 +40,10 @@ struct TileArgs {
   uint32_t xcd;       // 1: XCD-aware, grouped tile order
 };
 
-template <int DT, int MS, int TM, int TN, int TKB, int EPI>
+// PIPE: 0 = A staged through VGPRs, two LDS buffers (prefetch one tile
+// ahead); 2 / 3 = A copied global -> LDS by the buffer-load LDS DMA, with 2
+// or 3 LDS buffers and B register sets (prefetch PIPE-1 tiles ahead).
+template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE>
 struct TileCfg {
   using S = Mma<DT, MS>;
   static constexpr int THREADS = 256;
@@ -56,6 +59,8 @@ struct TileCfg {
   static constexpr int ACHUNKS = TM * CPR;
   static constexpr int ALOADS = (ACHUNKS + THREADS - 1) / THREADS;
   static constexpr bool APART = (ACHUNKS % THREADS) != 0;
+  static constexpr bool ASYNC = PIPE != 0;
+  static constexpr int ST = ASYNC ? PIPE : 2;              // pipeline stages
   static constexpr int ABUF = TM * TKB + (APART ? 16 : 0);   // + a spare slot for idle lanes
   static constexpr int OB = (DT == DT_I8) ? 4 : 2;        // output element bytes
   static constexpr int CSTRIDE = TN * OB + 16;            // padded C row in LDS
@@ -73,13 +78,15 @@ struct TileCfg {
   static constexpr int SLB = NSC ? (TN + THREADS - 1) / THREADS : 0;   // B scale rows per thread
   static constexpr int SLOADS = SLA + SLB;
   static constexpr int SAREA = NSC ? SROWS * SCB + 16 : 0;   // + a spare slot for idle lanes
-  static constexpr int STAGE = 2 * ABUF + 2 * SAREA;
+  static constexpr int STAGE = ST * ABUF + ST * SAREA;
   static constexpr int LDS = (STAGE > CBYTES) ? STAGE : CBYTES;
   static_assert(TM % MS == 0 && NPW % MS == 0 && TN % 64 == 0, "tile shape");
   static_assert(TKB % KB == 0 && TKB >= 64, "tile_k bytes must be a multiple of the MFMA K bytes");
   static_assert(THREADS % CPR == 0, "A row chunks must divide the workgroup");
   static_assert(!NSC || TKB == 128 || (MS == 16 && TKB == 64), "FP4 scale staging: 8 (or 4) bytes per row");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(!ASYNC || (!APART && (TM * CPR) % (THREADS * 1) == 0), "LDS DMA covers whole 1 KiB wave blocks");
+  static_assert(PIPE == 0 || PIPE == 2 || PIPE == 3, "pipeline");
 };
 
 __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uint32_t& tn) {
@@ -104,9 +111,9 @@ __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uin
   }
 }
 
-template <int DT, int MS, int TM, int TN, int TKB, int EPI>
+template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE>
 __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
-  using C = TileCfg<DT, MS, TM, TN, TKB, EPI>;
+  using C = TileCfg<DT, MS, TM, TN, TKB, EPI, PIPE>;
   using Acc = typename Mma<DT, MS>::Acc;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
 
@@ -152,6 +159,19 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   // access) and write to a spare LDS slot, so the K-tile body has no branch.
   auto a_on = [&](int i) { return !C::APART || i * C::THREADS + tid < C::ACHUNKS; };
   constexpr uint32_t kOOB = 0x80000000u;
+  // LDS DMA of A: instruction i of wave w fills the 1 KiB block i*WAVES + w of
+  // the A buffer, lane l landing at byte 16*l of it. So lane l fetches the
+  // global chunk that belongs at LDS chunk p = (i*WAVES + w)*64 + l: row p/CPR,
+  // physical chunk p%CPR, i.e. logical chunk (p%CPR) ^ swizzle(row). The rows
+  // of instruction i are those of instruction 0 plus i*RPD, RPD = 256/CPR.
+  constexpr int RPD = C::THREADS / C::CPR;
+  uint32_t a_dma0 = 0;
+  if constexpr (C::ASYNC) {
+    const int pch = wave * 64 + lane;
+    const int row = pch / C::CPR;
+    a_dma0 = row * Kb + (((pch % C::CPR) ^ ((row / C::SWP) & C::SWM)) * 16);
+  }
+  static_assert(!C::ASYNC || ((RPD / C::SWP) % (C::SWM + 1)) == 0, "DMA swizzle step");
   // K byte (within one MFMA step) of the lane's 16-byte piece f
   auto lane_k = [&](int f) -> int { return MS == 16 ? f * 64 + 16 * lgrp : 16 * lgrp; };
   // A LDS -> VGPR: lane reads row mi*MS + lrow, chunk (s*KB + lane_k(f)) / 16.
@@ -185,8 +205,8 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
     rsb = make_rsrc((const char*)p.sb + (size_t)n0 * srow, TN * srow);
   }
 
-  v4i a_st[C::ALOADS];
-  v4i bfr[2][C::KSTEPS][C::NACC][C::FRAG];
+  v4i a_st[C::ASYNC ? 1 : C::ALOADS];
+  v4i bfr[C::ST][C::KSTEPS][C::NACC][C::FRAG];
   v2i sa_st[C::SLA + 1 - C::NSC], sb_st[C::SLB + 1 - C::NSC];
   Acc acc[C::MREP][C::NACC];
 #pragma unroll
@@ -195,15 +215,27 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
     for (int ni = 0; ni < C::NACC; ++ni) acc[mi][ni] = Acc{};
 
   auto load_a = [&](int kt) {
+    if constexpr (C::ASYNC) return;
 #pragma unroll
     for (int i = 0; i < C::ALOADS; ++i)
       a_st[i] = buf_load16(ra, a_on(i) ? a_ld0 : kOOB, kt * TKB + i * RPP * Kb);
   };
   auto store_a = [&](int par) {
+    if constexpr (C::ASYNC) return;
     char* base = lds + par * C::ABUF;
 #pragma unroll
     for (int i = 0; i < C::ALOADS; ++i)
       *(v4i*)(base + (a_on(i) ? a_wr_off(i) : (uint32_t)(TM * TKB))) = a_st[i];
+  };
+  auto load_a_dma = [&](int stage, int kt) {
+    if constexpr (C::ASYNC) {
+#pragma unroll
+      for (int i = 0; i < C::ALOADS; ++i) {
+        char* dst = lds + stage * C::ABUF + (i * C::WAVES + wave) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_dma0,
+                                                 kt * TKB + i * RPD * Kb, 0, 0);
+      }
+    }
   };
   auto load_b = [&](auto par_c, int kt) {
     constexpr int par = decltype(par_c)::value;
@@ -259,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   };
   auto store_s = [&](int par) {
     if constexpr (DT == DT_FP4) {
-      char* base = lds + 2 * C::ABUF + par * C::SAREA;
+      char* base = lds + C::ST * C::ABUF + par * C::SAREA;
 #pragma unroll
       for (int i = 0; i < C::SLA; ++i) {
         const int r = i * C::THREADS + tid;
@@ -292,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
     // E8M0 scales from LDS: byte s of the value is the scale of K step s
     int psa[C::MREP * C::NSC + 1 - C::NSC], psb[C::NACC * C::NSC + 1 - C::NSC];
     if constexpr (DT == DT_FP4) {
-      const char* sb = lds + 2 * C::ABUF + par * C::SAREA;
+      const char* sb = lds + C::ST * C::ABUF + par * C::SAREA;
 #pragma unroll
       for (int mi = 0; mi < C::MREP; ++mi) psa[mi] = read_s(sb, mi * MS + lrow);
 #pragma unroll
@@ -321,12 +353,13 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
     }
   };
   // Instruction order of one K tile (hot-loop schedule): first A fragment
-  // read, then all global loads of the next tile (A, then B), then for every
-  // A fragment: read the next fragment, issue its NACC MFMAs; LDS writes of
-  // the next A tile last, ahead of the barrier.
+  // read, then all global loads of the tile PIPE-1 ahead (scales, A, B), then
+  // for every A fragment: read the next fragment, issue its NACC MFMAs; LDS
+  // writes of staged data last, ahead of the barrier.
+  constexpr int NBL = C::KSTEPS * C::NACC * C::FRAG;       // B loads per tile
+  constexpr int NVMEM = C::ALOADS + NBL + C::SLOADS;        // global loads per tile
   auto schedule = [&]() {
     constexpr int NF = C::KSTEPS * C::MREP;
-    constexpr int NVMEM = C::ALOADS + C::KSTEPS * C::NACC * C::FRAG + C::SLOADS;
     __builtin_amdgcn_sched_group_barrier(0x100, C::FRAG + (C::NSC ? C::MREP + C::NACC : 0), 0);
     __builtin_amdgcn_sched_group_barrier(0x020, NVMEM, 0);
 #pragma unroll
@@ -334,38 +367,71 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
       if (i + 1 < NF) __builtin_amdgcn_sched_group_barrier(0x100, C::FRAG, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, C::NACC, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x200, C::ALOADS + C::SLOADS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, (C::ASYNC ? 0 : C::ALOADS) + C::SLOADS, 0);
   };
-  auto iter = [&](auto par_c, int kt) {
-    constexpr int par = decltype(par_c)::value;
-    // the last tile reloads itself instead of branching, keeping the body one
-    // straight-line block; its copy in the other LDS buffer is never read
-    const int kn = kt + 1 < KT ? kt + 1 : kt;
-    load_a(kn);
-    load_s(kn);
-    load_b(std::integral_constant<int, par ^ 1>{}, kn);
-    compute(par_c);
-    store_a(par ^ 1);
-    store_s(par ^ 1);
+  // s_waitcnt vmcnt(n) alone (expcnt / lgkmcnt left alone)
+  auto wait_vm = [&](auto n_c) {
+    constexpr int n = decltype(n_c)::value;
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  };
+  auto loads = [&](auto stage_c, int kt) {
+    constexpr int st = decltype(stage_c)::value;
+    // order: scales, A, B (the wait for A below counts on it)
+    load_s(kt);
+    load_a(kt);
+    load_a_dma(st, kt);
+    load_b(stage_c, kt);
+  };
+  auto iter = [&](auto r_c, int kt) {
+    constexpr int r = decltype(r_c)::value;
+    constexpr int rn = (r + C::ST - 1) % C::ST;  // stage of the tile ST-1 ahead
+    // past the end the last tile reloads itself into a free stage instead of
+    // branching, keeping the body one straight-line block
+    const int kn = kt + C::ST - 1 < KT ? kt + C::ST - 1 : KT - 1;
+    loads(std::integral_constant<int, rn>{}, kn);
+    compute(r_c);
+    store_a(rn);
+    store_s(rn);
     schedule();
+    if constexpr (C::ASYNC) {
+      // tile kt+1's DMA was issued ST-2 iterations ago, before that
+      // iteration's B loads: everything issued after it may stay in flight
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm(std::integral_constant<int, NBL + (C::ST - 2) * NVMEM>{});
+    }
     __syncthreads();
   };
 
-  // ---- prologue: tile 0 ----
-  load_a(0);
-  load_s(0);
-  load_b(std::integral_constant<int, 0>{}, 0);
-  store_a(0);
-  store_s(0);
+  // ---- prologue: tiles 0 .. ST-2 ----
+#pragma unroll
+  for (int j = 0; j + 1 < C::ST; ++j) {
+    const int kj = j < KT ? j : KT - 1;
+    if (j == 0) loads(std::integral_constant<int, 0>{}, kj);
+    else loads(std::integral_constant<int, (C::ST > 2 ? 1 : 0)>{}, kj);
+    store_a(j);
+    store_s(j);
+  }
+  if constexpr (C::ASYNC) {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm(std::integral_constant<int, NBL + (C::ST - 2) * NVMEM>{});
+  }
   __syncthreads();
 
-  // ---- main loop, two K tiles per trip (ping, pong) ----
+  // ---- main loop, ST K tiles per trip ----
   int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
+  for (; kt + C::ST <= KT; kt += C::ST) {
     iter(std::integral_constant<int, 0>{}, kt);
     iter(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (C::ST == 3) iter(std::integral_constant<int, 2>{}, kt + 2);
   }
   if (kt < KT) iter(std::integral_constant<int, 0>{}, kt);
+  if (kt + 1 < KT) iter(std::integral_constant<int, 1>{}, kt + 1);
+  // no DMA may still be writing LDS when the epilogue reuses it
+  if constexpr (C::ASYNC) {
+    wait_vm(std::integral_constant<int, 0>{});
+    __syncthreads();
+  }
 
   // ---- epilogue ----
   // For every (mi, ni) the lane holds NREG/4 runs of 4 consecutive columns

@@ -4,7 +4,7 @@
 
 namespace gp {
 
-hipError_t launch_tile_i8(int ms, int tm, int tn, int tkb, int epi, const TileArgs& a, hipStream_t s) {
+hipError_t launch_tile_i8(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s) {
   GP_TILE_I8(GP_TILE_CASE)
   return hipErrorInvalidValue;
 }

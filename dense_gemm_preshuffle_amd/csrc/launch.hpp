@@ -10,10 +10,10 @@
 namespace gp {
 
 // Each returns hipErrorInvalidValue if the variant is not compiled.
-hipError_t launch_tile_i8(int ms, int tm, int tn, int tkb, int epi, const TileArgs& a, hipStream_t s);
-hipError_t launch_tile_fp8(int ms, int tm, int tn, int tkb, int epi, const TileArgs& a, hipStream_t s);
-hipError_t launch_tile_bf16(int ms, int tm, int tn, int tkb, int epi, const TileArgs& a, hipStream_t s);
-hipError_t launch_tile_fp4(int ms, int tm, int tn, int tkb, int epi, const TileArgs& a, hipStream_t s);
+hipError_t launch_tile_i8(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s);
+hipError_t launch_tile_fp8(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s);
+hipError_t launch_tile_bf16(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s);
+hipError_t launch_tile_fp4(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s);
 hipError_t launch_splitk_i8(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
 hipError_t launch_splitk_fp8(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
 hipError_t launch_splitk_bf16(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
@@ -22,13 +22,13 @@ hipError_t launch_splitk_fp4(int nb, int waves, int kch, const SplitArgs& a, hip
 }  // namespace gp
 
 // Body of one dtype's launch tables.
-#define GP_TILE_CASE(DT, MS, TM, TN, TKB)                                                  \
-  if (ms == MS && tm == TM && tn == TN && tkb == TKB) {                                    \
+#define GP_TILE_CASE(DT, MS, TM, TN, TKB, PIPE)                                            \
+  if (ms == MS && tm == TM && tn == TN && tkb == TKB && pipe == PIPE) {                    \
     const dim3 grid(a.tiles_m * a.tiles_n);                                                \
     if (epi == EPI_CSHUFFLE)                                                               \
-      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_CSHUFFLE>), grid, dim3(256), 0, s, a); \
+      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_CSHUFFLE, PIPE>), grid, dim3(256), 0, s, a); \
     else                                                                                   \
-      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_DIRECT>), grid, dim3(256), 0, s, a);   \
+      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_DIRECT, PIPE>), grid, dim3(256), 0, s, a);   \
     return hipGetLastError();                                                              \
   }
 #define GP_SPLITK_CASE(DT, NB, W, KCH)                                                     \

@@ -1,30 +1,35 @@
 // Compiled kernel variants. The host planner and the launch tables both read
 // these lists, so a tile the planner may pick is always instantiated.
 //
-// Tile kernel: X(dtype, mfma, tile_m, tile_n, tile_k_bytes), mfma = 16 or 32
-// (the MFMA block); each is built with the direct and the CShuffle epilogue.
+// Tile kernel: X(dtype, mfma, tile_m, tile_n, tile_k_bytes, pipe): mfma = 16 or
+// 32 (the MFMA block); pipe 0 = A staged through VGPRs (2 stages), 2 / 3 = A
+// by LDS DMA with 2 / 3 stages. Each is built with the direct and the
+// CShuffle epilogue.
 // Split-K kernel: Y(dtype, n_blocks_of_16, waves, chunk_bytes_per_wave).
 #pragma once
 
 #define GP_TILE_I8(X)                                                                              \
-  X(DT_I8, 16, 16, 64, 256) X(DT_I8, 16, 32, 64, 128) X(DT_I8, 16, 64, 64, 128)                     \
-  X(DT_I8, 16, 64, 128, 128) X(DT_I8, 16, 64, 256, 128) X(DT_I8, 16, 128, 128, 128)                 \
-  X(DT_I8, 16, 128, 256, 128) X(DT_I8, 32, 128, 256, 128) X(DT_I8, 32, 64, 256, 128)
+  X(DT_I8, 16, 16, 64, 256, 0) X(DT_I8, 16, 32, 64, 128, 0) X(DT_I8, 16, 64, 64, 128, 0)                     \
+  X(DT_I8, 16, 64, 128, 128, 0) X(DT_I8, 16, 64, 256, 128, 0) X(DT_I8, 16, 128, 128, 128, 0)                 \
+  X(DT_I8, 16, 128, 256, 128, 0) X(DT_I8, 32, 128, 256, 128, 0) X(DT_I8, 32, 64, 256, 128, 0)
 
 #define GP_TILE_FP8(X)                                                                             \
-  X(DT_FP8, 16, 16, 64, 512) X(DT_FP8, 16, 32, 256, 128) X(DT_FP8, 16, 64, 128, 128)               \
-  X(DT_FP8, 16, 64, 256, 128) X(DT_FP8, 16, 128, 128, 128) X(DT_FP8, 16, 128, 256, 128)            \
-  X(DT_FP8, 16, 64, 256, 256)
+  X(DT_FP8, 16, 16, 64, 512, 0) X(DT_FP8, 16, 32, 256, 128, 0) X(DT_FP8, 16, 64, 128, 128, 0)               \
+  X(DT_FP8, 16, 64, 256, 128, 0) X(DT_FP8, 16, 128, 128, 128, 0) X(DT_FP8, 16, 128, 256, 128, 0)            \
+  X(DT_FP8, 16, 64, 256, 256, 0) X(DT_FP8, 16, 128, 256, 128, 2) X(DT_FP8, 16, 128, 256, 128, 3)  \
+  X(DT_FP8, 16, 64, 256, 128, 3) X(DT_FP8, 16, 32, 256, 128, 3)
 
 #define GP_TILE_BF16(X)                                                                            \
-  X(DT_BF16, 16, 64, 128, 128) X(DT_BF16, 16, 128, 256, 128) X(DT_BF16, 16, 128, 256, 64)          \
-  X(DT_BF16, 32, 64, 128, 128) X(DT_BF16, 32, 64, 256, 128) X(DT_BF16, 32, 128, 128, 128)          \
-  X(DT_BF16, 32, 128, 256, 128) X(DT_BF16, 32, 128, 256, 64)
+  X(DT_BF16, 16, 64, 128, 128, 0) X(DT_BF16, 16, 128, 256, 128, 0) X(DT_BF16, 16, 128, 256, 64, 0)          \
+  X(DT_BF16, 32, 64, 128, 128, 0) X(DT_BF16, 32, 64, 256, 128, 0) X(DT_BF16, 32, 128, 128, 128, 0)          \
+  X(DT_BF16, 32, 128, 256, 128, 0) X(DT_BF16, 32, 128, 256, 64, 0)                                \
+  X(DT_BF16, 32, 128, 256, 128, 2) X(DT_BF16, 32, 128, 256, 128, 3) X(DT_BF16, 16, 128, 256, 128, 3)
 
 #define GP_TILE_FP4(X)                                                                             \
-  X(DT_FP4, 16, 32, 256, 128) X(DT_FP4, 16, 64, 128, 128) X(DT_FP4, 16, 64, 256, 128)              \
-  X(DT_FP4, 16, 128, 256, 128) X(DT_FP4, 32, 64, 128, 128) X(DT_FP4, 32, 64, 256, 128)             \
-  X(DT_FP4, 32, 128, 128, 128) X(DT_FP4, 32, 128, 256, 128)
+  X(DT_FP4, 16, 32, 256, 128, 0) X(DT_FP4, 16, 64, 128, 128, 0) X(DT_FP4, 16, 64, 256, 128, 0)              \
+  X(DT_FP4, 16, 128, 256, 128, 0) X(DT_FP4, 32, 64, 128, 128, 0) X(DT_FP4, 32, 64, 256, 128, 0)             \
+  X(DT_FP4, 32, 128, 128, 128, 0) X(DT_FP4, 32, 128, 256, 128, 0)                                  \
+  X(DT_FP4, 32, 128, 256, 128, 2) X(DT_FP4, 32, 128, 256, 128, 3)
 
 #define GP_SPLITK_I8(Y) Y(DT_I8, 1, 4, 64) Y(DT_I8, 1, 4, 256) Y(DT_I8, 2, 4, 256)
 #define GP_SPLITK_FP8(Y)                                                                           \

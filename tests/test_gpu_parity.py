@@ -73,6 +73,22 @@ TILE_CASES = [
     ("mxfp4", 256, 256, 768, dict(kernel=1, tile_m=128, tile_n=128, tile_k=256, mfma=32)),
     ("int8", 128, 256, 384, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, mfma=32)),
     ("int8", 128, 512, 256, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, mfma=32, epilogue=2)),
+    # A by LDS DMA, 2 or 3 pipeline stages, K-tile counts 1..5
+    ("bf16", 128, 256, 64, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
+    ("bf16", 128, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
+    ("bf16", 256, 512, 192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
+    ("bf16", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3, epilogue=1)),
+    ("bf16", 128, 256, 320, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
+    ("bf16", 128, 256, 320, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=16, pipeline=3)),
+    ("bf16", 128, 256, 192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=2)),
+    ("fp8", 128, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, pipeline=3)),
+    ("fp8", 128, 512, 640, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, pipeline=3)),
+    ("fp8", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, pipeline=2)),
+    ("fp8", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, pipeline=3)),
+    ("fp8", 64, 512, 384, dict(kernel=1, tile_m=32, tile_n=256, tile_k=128, pipeline=3)),
+    ("mxfp4", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
+    ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
+    ("mxfp4", 128, 256, 1024, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=3)),
     # small-M split-K kernel
     ("fp8", 16, 512, 2048, dict(kernel=2)),
     ("fp8", 32, 256, 1024, dict(kernel=2, tile_n=32)),
@@ -126,6 +142,8 @@ def _one_hot_b(dtype, N, K, perm):
 PERM_CASES = [("int8", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128)),
               ("int8", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, mfma=32)),
               ("bf16", 128, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32)),
+              ("bf16", 128, 256, 320, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
+              ("fp8", 128, 256, 640, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, pipeline=3)),
               ("mxfp4", 128, 256, 512, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32)),
               ("fp8", 128, 512, 384, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128)),
               ("fp8", 16, 256, 1024, dict(kernel=2)),
@@ -205,7 +223,8 @@ def test_fp4_exhaustive_codes_and_scales_bit_exact():
                                   dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=16),
                                   dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32),
                                   dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, mfma=32),
-                                  dict(kernel=2)], ids=["t64", "t128", "t128m32", "t64x128m32", "splitk"])
+                                  dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2),
+                                  dict(kernel=2)], ids=["t64", "t128", "t128m32", "t64x128m32", "t128m32dma", "splitk"])
 def test_fp4_block_scale_placement_bit_exact(opts):
     say(f"fp4 scale placement {opts}")
     rng = np.random.default_rng(4)
