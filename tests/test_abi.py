@@ -107,7 +107,7 @@ def test_named_tiles_plan():
     assert p["grid"] == 2048 and p["k_tiles"] == 128
     assert p["mfma_per_wave_tile"] == 64            # 2 K32 steps x 8 x 4
     p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, epilogue=1,
-                                                     pipeline=1))
+                                                     pipeline=1, mfma=32))
     assert p["mfma"] == 32 and p["mfma_per_wave_tile"] == 32   # 4 K16 steps x 4 x 2 (32x32 blocks)
     assert p["lds_bytes"] == F.lds_bytes(128, 256, 64, 2)
     p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=2))
