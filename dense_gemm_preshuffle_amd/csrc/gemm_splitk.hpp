@@ -52,7 +52,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index: uniform across the wave; readfirstlane puts it in a scalar
+  // register so that offsets derived from it stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lane_lo = lane & 15;
   const int lane_hi = lane >> 4;

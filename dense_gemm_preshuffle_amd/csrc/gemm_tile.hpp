@@ -118,7 +118,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index: uniform across the wave; readfirstlane puts it in a scalar
+  // register so that offsets derived from it stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   // lane's row / column inside an MFMA block and its K lane group
   const int lrow = lane & (MS - 1);
@@ -375,8 +377,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   };
-  auto loads = [&](auto stage_c, int kt) {
+  auto loads = [&](auto stage_c, int kt_in) {
     constexpr int st = decltype(stage_c)::value;
+    // the tile index is wave-uniform; say so, so that every offset built from
+    // it stays in scalar registers (a VGPR offset would need a waterfall loop)
+    const int kt = __builtin_amdgcn_readfirstlane(kt_in);
     // order: scales, A, B (the wait for A below counts on it)
     load_s(kt);
     load_a(kt);
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
     constexpr int rn = (r + C::ST - 1) % C::ST;  // stage of the tile ST-1 ahead
     // past the end the last tile reloads itself into a free stage instead of
     // branching, keeping the body one straight-line block
-    const int kn = kt + C::ST - 1 < KT ? kt + C::ST - 1 : KT - 1;
+    const int kn = min(kt + C::ST - 1, KT - 1);
     loads(std::integral_constant<int, rn>{}, kn);
     compute(r_c);
     store_a(rn);
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   // ---- prologue: tiles 0 .. ST-2 ----
 #pragma unroll
   for (int j = 0; j + 1 < C::ST; ++j) {
-    const int kj = j < KT ? j : KT - 1;
+    const int kj = min(j, KT - 1);
     if (j == 0) loads(std::integral_constant<int, 0>{}, kj);
     else loads(std::integral_constant<int, (C::ST > 2 ? 1 : 0)>{}, kj);
     store_a(j);
