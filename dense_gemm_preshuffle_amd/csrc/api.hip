@@ -144,7 +144,7 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
 int pick_chunk(int dt, int nb, int waves, int64_t kw) {
   int kch = 0;
   for (const auto& v : kSplits)
-    if (v.dt == dt && v.nb == nb && v.waves == waves && kw % v.kch == 0 && v.kch <= 256 && v.kch > kch)
+    if (v.dt == dt && v.nb == nb && v.waves == waves && kw % v.kch == 0 && v.kch <= 512 && v.kch > kch)
       kch = v.kch;
   if (kch == 0)
     for (const auto& v : kSplits)
@@ -258,6 +258,7 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     if (dt == DT_FP4) abuf += stages * ((p.tm + p.tn) * (p.tkb / 16) + 16);  // staged E8M0 scales
     const int cbytes = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
     out->lds_bytes = abuf > cbytes ? abuf : cbytes;
+    if (dt == DT_FP8) out->lds_bytes += 256 * ((p.tm + 63) / 64 + p.tn / 64);  // FP8 scales
     out->grid = (M / p.tm) * (N / p.tn);
     out->k_tiles = p.Kb / p.tkb;
     out->mfma_per_wave_tile = (int64_t)(p.tkb / kbm) * (p.tm / ms) * (p.tn / 4 / ms);

@@ -85,6 +85,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
     rsb = make_rsrc((const char*)p.sb + (size_t)n0 * srow, 16 * NB * srow);
   }
 
+  // FP8 scales: issued before any operand load, so that the epilogue does not
+  // wait one more memory round trip for them. Wave w stores column block w
+  // (NB <= WAVES), so each wave needs its rows' and its block's scales only.
+  float sa_v = 1.f;
+  v4f sb_v = v4f{1.f, 1.f, 1.f, 1.f};
+  if constexpr (DT == DT_FP8) {
+    static_assert(NB <= WAVES, "one column block per wave in the epilogue");
+    const uint32_t nbw = (uint32_t)min(wave, NB - 1);
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc((const float*)p.sa + m0, 16 * 4);
+    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc((const float*)p.sb + n0, 16 * NB * 4);
+    sa_v = __builtin_bit_cast(float, buf_load4_early(rs_a, lane_lo * 4, 0));
+    sb_v = __builtin_bit_cast(v4f, buf_load16_early(rs_b, (nbw * 16 + 4 * lane_hi) * 4, 0));
+  }
+
   v4i af[2][C::STEPS][C::FRAG];
   v4i bf[2][C::STEPS][NB][C::FRAG];
   int sa_r[2][C::STEPS * C::NSC + 1 - C::NSC];
@@ -162,10 +176,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
       buf_store16_nt(v, rc, off);
     } else {
       if constexpr (DT == DT_FP8) {
-        const float sa = ((const float*)p.sa)[m0 + lane_lo];
-        const v4f sb = *(const v4f*)((const float*)p.sb + n0 + col);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (v[r] * sa) * sb[r];
+        for (int r = 0; r < 4; ++r) v[r] = (v[r] * sa_v) * sb_v[r];
       }
       v2i o;
       o[0] = (int)pack_bf16x2(v[0], v[1]);

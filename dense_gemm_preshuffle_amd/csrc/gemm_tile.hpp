@@ -79,7 +79,13 @@ struct TileCfg {
   static constexpr int SLOADS = SLA + SLB;
   static constexpr int SAREA = NSC ? SROWS * SCB + 16 : 0;   // + a spare slot for idle lanes
   static constexpr int STAGE = ST * ABUF + ST * SAREA;
-  static constexpr int LDS = (STAGE > CBYTES) ? STAGE : CBYTES;
+  // FP8 per-row / per-column scales, fetched into LDS by DMA when the kernel
+  // starts (so the epilogue does not wait a memory round trip for them):
+  // 256-byte blocks of A scales (TM floats, padded to 64) then B scales.
+  static constexpr int NSA = (DT == DT_FP8) ? (TM + 63) / 64 : 0;
+  static constexpr int NSB = (DT == DT_FP8) ? TN / 64 : 0;
+  static constexpr int FSC_OFF = (STAGE > CBYTES) ? STAGE : CBYTES;
+  static constexpr int LDS = FSC_OFF + (NSA + NSB) * 256;
   static_assert(TM % MS == 0 && NPW % MS == 0 && TN % 64 == 0, "tile shape");
   static_assert(TKB % KB == 0 && TKB >= 64, "tile_k bytes must be a multiple of the MFMA K bytes");
   static_assert(THREADS % CPR == 0, "A row chunks must divide the workgroup");
@@ -205,6 +211,21 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   if constexpr (DT == DT_FP4) {
     rsa = make_rsrc((const char*)p.sa + (size_t)m0 * srow, TM * srow);
     rsb = make_rsrc((const char*)p.sb + (size_t)n0 * srow, TN * srow);
+  }
+
+  // FP8 scales -> LDS, before any operand load: block i by wave i % WAVES,
+  // lane l carrying float l of the block (lanes past TM read zeros).
+  if constexpr (DT == DT_FP8) {
+    const __amdgpu_buffer_rsrc_t rfa = make_rsrc((const float*)p.sa + m0, TM * 4);
+    const __amdgpu_buffer_rsrc_t rfb = make_rsrc((const float*)p.sb + n0, TN * 4);
+#pragma unroll
+    for (int i = 0; i < C::NSA + C::NSB; ++i) {
+      if (i % C::WAVES != wave) continue;
+      char* dst = lds + C::FSC_OFF + i * 256;
+      const bool is_a = i < C::NSA;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rfa : rfb, (__attribute__((address_space(3))) void*)dst, 4,
+                                               lane * 4, (is_a ? i : i - C::NSA) * 256, 0, 0);
+    }
   }
 
   v4i a_st[C::ASYNC ? 1 : C::ALOADS];
@@ -446,8 +467,12 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
   v4f sbv[C::NACC][C::NREG / 4];
   float sav[C::MREP];
   if constexpr (DT == DT_FP8) {
-    const float* sa = (const float*)p.sa + m0;
-    const float* sb = (const float*)p.sb + n0;
+    // The scale DMA was each wave's first memory instruction, so it completed
+    // before the wave's wait for any later load (vmcnt counts in order): with
+    // DMA A the wait for zero above, with A through VGPRs the wait for the
+    // last tile's A. Every wave passed a barrier after that wait.
+    const float* sa = (const float*)(lds + C::FSC_OFF);
+    const float* sb = sa + C::NSA * 64;
 #pragma unroll
     for (int mi = 0; mi < C::MREP; ++mi) sav[mi] = sa[mi * MS + lrow];
 #pragma unroll

@@ -38,6 +38,17 @@ __device__ __forceinline__ v2i buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff
 __device__ __forceinline__ int buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+// Loads marked volatile (bit 31 of the aux operand, honoured by the compiler
+// only): issued where they stand in program order, never sunk towards their
+// first use. For small values needed only at the end of a kernel whose memory
+// latency should overlap the main loads.
+constexpr int kAuxVolatile = (int)0x80000000u;
+__device__ __forceinline__ int buf_load4_early(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kAuxVolatile);
+}
+__device__ __forceinline__ v4i buf_load16_early(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAuxVolatile);
+}
 // Non-temporal (streaming) variants: cache policy bit 1 (nt) on gfx950.
 constexpr int kPolicyNT = 2;
 __device__ __forceinline__ v4i buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {

@@ -101,7 +101,8 @@ def test_named_tiles_plan():
     # the pages' formula counts gfx942 K=32 instructions; gfx950 FP8 takes K=128
     assert p["mfma_per_wave_tile"] * 4 == F.mfma_per_tile_pages(64, 256, 128)
     assert p["grid"] == 128 and p["k_tiles"] == 32 and p["mfma"] == 16
-    assert p["lds_bytes"] == F.lds_bytes(64, 256, 128, 1)
+    fp8_scales = 256 * (1 + 256 // 64)              # FP8 row / column scales staged in LDS
+    assert p["lds_bytes"] == F.lds_bytes(64, 256, 128, 1) + fp8_scales
     p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, epilogue=1, mfma=16,
                                                      pipeline=1))
     assert p["grid"] == 2048 and p["k_tiles"] == 128
@@ -111,9 +112,9 @@ def test_named_tiles_plan():
     assert p["mfma"] == 32 and p["mfma_per_wave_tile"] == 32   # 4 K16 steps x 4 x 2 (32x32 blocks)
     assert p["lds_bytes"] == F.lds_bytes(128, 256, 64, 2)
     p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=2))
-    assert p["lds_bytes"] == 64 * (256 * 2 + 16)    # padded CShuffle tile (above 3 stages of A)
+    assert p["lds_bytes"] == 64 * (256 * 2 + 16) + fp8_scales   # padded CShuffle tile (above 3 stages of A)
     p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=1, pipeline=3))
-    assert p["lds_bytes"] == 3 * 64 * 128 and p["pipeline"] == 3
+    assert p["lds_bytes"] == 3 * 64 * 128 + fp8_scales and p["pipeline"] == 3
     # default epilogue: CShuffle for tile_n >= 128 while two workgroups fit a CU
     assert gp.gemm_plan("bf16", 8192, 8192, 8192)["epilogue"] == gp.EPI_CSHUFFLE
     assert gp.gemm_plan("int8", 4096, 4096, 4096, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128))["epilogue"] == gp.EPI_DIRECT
