@@ -139,7 +139,7 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
 }
 
 // Compiled split-K chunk for (dt, nb, waves) that divides the wave's K range:
-// the largest one up to 256 bytes (measured best for the M=16 FP8 shape),
+// the largest one up to 512 bytes (measured best for the M=16 FP8 shape),
 // else the smallest; 0 if none.
 int pick_chunk(int dt, int nb, int waves, int64_t kw) {
   int kch = 0;
@@ -223,10 +223,13 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     p->epi = o->epilogue;
   } else {
     // CShuffle (coalesced full-row stores) for tile_n >= 128 when its LDS
-    // tile still lets two workgroups share a CU; direct stores otherwise
+    // tile fits the share of the 160 KiB LDS each resident workgroup gets
+    // (two per CU, or one for tiles whose accumulators fill half the
+    // registers); direct stores otherwise
     const int ob = in_dtype == GP_I8 ? 4 : 2;
     const int cbytes = p->tm * (p->tn * ob + 16);
-    p->epi = (p->tn >= 128 && cbytes <= 80 * 1024) ? EPI_CSHUFFLE : EPI_DIRECT;
+    const int wgs_per_cu = (p->tm * p->tn / 256 > 128) ? 1 : 2;
+    p->epi = (p->tn >= 128 && cbytes <= 160 * 1024 / wgs_per_cu) ? EPI_CSHUFFLE : EPI_DIRECT;
   }
   p->xcd = (o && o->xcd_swizzle) ? o->xcd_swizzle : 1;
   return GP_OK;

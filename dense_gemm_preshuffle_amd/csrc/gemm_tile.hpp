@@ -86,6 +86,16 @@ struct TileCfg {
   static constexpr int NSB = (DT == DT_FP8) ? TN / 64 : 0;
   static constexpr int FSC_OFF = (STAGE > CBYTES) ? STAGE : CBYTES;
   static constexpr int LDS = FSC_OFF + (NSA + NSB) * 256;
+  // A fragments read ahead of their MFMAs: the most (2, 1 or 0) for which
+  // the register estimate (accumulators unless they sit in AGPRs, B stages,
+  // FP4 scales, the fragment ring) stays within 236 of the 256 VGPRs. FP8
+  // stops at 1: one FP8 fragment feeds NACC 32-cycle MFMAs, which covers an
+  // LDS read on its own.
+  static constexpr int ACCR = TM * TN / 256;
+  static constexpr int BREG = ST * KSTEPS * NACC * FRAG * 4;
+  static constexpr int SREG = NSC ? MREP + NACC + 2 * (SLA + SLB) : 0;
+  static constexpr int RBASE = (ACCR > 128 ? 0 : ACCR) + BREG + SREG;
+  static constexpr int RA = (FRAG == 1 && RBASE + 12 <= 236) ? 2 : (RBASE + 2 * FRAG * 4 <= 236) ? 1 : 0;
   static_assert(TM % MS == 0 && NPW % MS == 0 && TN % 64 == 0, "tile shape");
   static_assert(TKB % KB == 0 && TKB >= 64, "tile_k bytes must be a multiple of the MFMA K bytes");
   static_assert(THREADS % CPR == 0, "A row chunks must divide the workgroup");
@@ -118,7 +128,9 @@ __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uin
 }
 
 template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE>
-__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
+// One workgroup per CU once the accumulators alone take more than half of the
+// 256 registers two workgroups would leave each wave; two otherwise.
+__global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_kernel(TileArgs p) {
   using C = TileCfg<DT, MS, TM, TN, TKB, EPI, PIPE>;
   using Acc = typename Mma<DT, MS>::Acc;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
@@ -342,7 +354,15 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
 #pragma unroll
     for (int f = 0; f < C::FRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * MS * TKB);
   };
-  auto compute = [&](auto par_c) {
+  // Hot-loop order of one K tile: the first RA A-fragment reads, then all
+  // global loads of the tile PIPE-1 ahead (scales, A, B), then for every A
+  // fragment i: read fragment i+RA, issue fragment i's NACC MFMAs. The A
+  // fragments live in a ring of RA+1 register sets, so each ds_read has RA
+  // groups of MFMAs to land in. Scheduling fences pin this order: left free,
+  // the compiler folds the ring into one register set and waits for every
+  // read right before its MFMAs.
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto compute = [&](auto par_c, auto&& issue_loads) {
     constexpr int par = decltype(par_c)::value;
     // E8M0 scales from LDS: byte s of the value is the scale of K step s
     int psa[C::MREP * C::NSC + 1 - C::NSC], psb[C::NACC * C::NSC + 1 - C::NSC];
@@ -354,44 +374,37 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
       for (int ni = 0; ni < C::NACC; ++ni) psb[ni] = read_s(sb, TM + wave * C::NPW + ni * MS + lrow);
     }
     constexpr int NF = C::KSTEPS * C::MREP;
-    v4i af[2][C::FRAG];
-    read_a(par, 0, 0, af[0]);
+    constexpr int RA = C::RA < NF ? C::RA : NF;
+    v4i af[RA + 1][C::FRAG];
+#pragma unroll
+    for (int j = 0; j < RA; ++j) read_a(par, j / C::MREP, j % C::MREP, af[j]);
+    fence();
+    issue_loads();
+    fence();
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
       const int s = i / C::MREP, mi = i % C::MREP;
-      if (i + 1 < NF) read_a(par, (i + 1) / C::MREP, (i + 1) % C::MREP, af[(i + 1) & 1]);
+      if (i + RA < NF) read_a(par, (i + RA) / C::MREP, (i + RA) % C::MREP, af[(i + RA) % (RA + 1)]);
+      fence();
+      const v4i* a = af[i % (RA + 1)];
 #pragma unroll
       for (int ni = 0; ni < C::NACC; ++ni) {
         if constexpr (DT == DT_FP4) {
           switch (s) {
-            case 0: acc[mi][ni] = mma<DT, MS, 0>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]); break;
-            case 1: acc[mi][ni] = mma<DT, MS, 1>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]); break;
-            case 2: acc[mi][ni] = mma<DT, MS, 2>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]); break;
-            default: acc[mi][ni] = mma<DT, MS, 3>(bfr[par][s][ni], af[i & 1], acc[mi][ni], psb[ni], psa[mi]); break;
+            case 0: acc[mi][ni] = mma<DT, MS, 0>(bfr[par][s][ni], a, acc[mi][ni], psb[ni], psa[mi]); break;
+            case 1: acc[mi][ni] = mma<DT, MS, 1>(bfr[par][s][ni], a, acc[mi][ni], psb[ni], psa[mi]); break;
+            case 2: acc[mi][ni] = mma<DT, MS, 2>(bfr[par][s][ni], a, acc[mi][ni], psb[ni], psa[mi]); break;
+            default: acc[mi][ni] = mma<DT, MS, 3>(bfr[par][s][ni], a, acc[mi][ni], psb[ni], psa[mi]); break;
           }
         } else {
-          acc[mi][ni] = mma<DT, MS>(bfr[par][s][ni], af[i & 1], acc[mi][ni]);
+          acc[mi][ni] = mma<DT, MS>(bfr[par][s][ni], a, acc[mi][ni]);
         }
       }
+      fence();
     }
   };
-  // Instruction order of one K tile (hot-loop schedule): first A fragment
-  // read, then all global loads of the tile PIPE-1 ahead (scales, A, B), then
-  // for every A fragment: read the next fragment, issue its NACC MFMAs; LDS
-  // writes of staged data last, ahead of the barrier.
   constexpr int NBL = C::KSTEPS * C::NACC * C::FRAG;       // B loads per tile
   constexpr int NVMEM = C::ALOADS + NBL + C::SLOADS;        // global loads per tile
-  auto schedule = [&]() {
-    constexpr int NF = C::KSTEPS * C::MREP;
-    __builtin_amdgcn_sched_group_barrier(0x100, C::FRAG + (C::NSC ? C::MREP + C::NACC : 0), 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, NVMEM, 0);
-#pragma unroll
-    for (int i = 0; i < NF; ++i) {
-      if (i + 1 < NF) __builtin_amdgcn_sched_group_barrier(0x100, C::FRAG, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, C::NACC, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x200, (C::ASYNC ? 0 : C::ALOADS) + C::SLOADS, 0);
-  };
   // s_waitcnt vmcnt(n) alone (expcnt / lgkmcnt left alone)
   auto wait_vm = [&](auto n_c) {
     constexpr int n = decltype(n_c)::value;
@@ -415,11 +428,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(TileArgs p) {
     // past the end the last tile reloads itself into a free stage instead of
     // branching, keeping the body one straight-line block
     const int kn = min(kt + C::ST - 1, KT - 1);
-    loads(std::integral_constant<int, rn>{}, kn);
-    compute(r_c);
+    compute(r_c, [&] { loads(std::integral_constant<int, rn>{}, kn); });
     store_a(rn);
     store_s(rn);
-    schedule();
     if constexpr (C::ASYNC) {
       // tile kt+1's DMA was issued ST-2 iterations ago, before that
       // iteration's B loads: everything issued after it may stay in flight

@@ -17,19 +17,22 @@
   X(DT_FP8, 16, 16, 64, 512, 0) X(DT_FP8, 16, 32, 256, 128, 0) X(DT_FP8, 16, 64, 128, 128, 0)               \
   X(DT_FP8, 16, 64, 256, 128, 0) X(DT_FP8, 16, 128, 128, 128, 0) X(DT_FP8, 16, 128, 256, 128, 0)            \
   X(DT_FP8, 16, 64, 256, 256, 0) X(DT_FP8, 16, 128, 256, 128, 2) X(DT_FP8, 16, 128, 256, 128, 3)  \
-  X(DT_FP8, 16, 64, 256, 128, 3) X(DT_FP8, 16, 32, 256, 128, 3)
+  X(DT_FP8, 16, 64, 256, 128, 3) X(DT_FP8, 16, 32, 256, 128, 3) X(DT_FP8, 16, 256, 256, 128, 3)
 
 #define GP_TILE_BF16(X)                                                                            \
   X(DT_BF16, 16, 64, 128, 128, 0) X(DT_BF16, 16, 128, 256, 128, 0) X(DT_BF16, 16, 128, 256, 64, 0)          \
   X(DT_BF16, 32, 64, 128, 128, 0) X(DT_BF16, 32, 64, 256, 128, 0) X(DT_BF16, 32, 128, 128, 128, 0)          \
   X(DT_BF16, 32, 128, 256, 128, 0) X(DT_BF16, 32, 128, 256, 64, 0)                                \
-  X(DT_BF16, 32, 128, 256, 128, 2) X(DT_BF16, 32, 128, 256, 128, 3) X(DT_BF16, 16, 128, 256, 128, 3)
+  X(DT_BF16, 32, 128, 256, 128, 2) X(DT_BF16, 32, 128, 256, 128, 3) X(DT_BF16, 16, 128, 256, 128, 3) \
+  X(DT_BF16, 16, 256, 256, 128, 3) X(DT_BF16, 32, 256, 256, 128, 3) X(DT_BF16, 32, 256, 256, 128, 2) \
+  X(DT_BF16, 32, 256, 256, 64, 3)
 
 #define GP_TILE_FP4(X)                                                                             \
   X(DT_FP4, 16, 32, 256, 128, 0) X(DT_FP4, 16, 64, 128, 128, 0) X(DT_FP4, 16, 64, 256, 128, 0)              \
   X(DT_FP4, 16, 128, 256, 128, 0) X(DT_FP4, 32, 64, 128, 128, 0) X(DT_FP4, 32, 64, 256, 128, 0)             \
   X(DT_FP4, 32, 128, 128, 128, 0) X(DT_FP4, 32, 128, 256, 128, 0)                                  \
-  X(DT_FP4, 32, 128, 256, 128, 2) X(DT_FP4, 32, 128, 256, 128, 3)
+  X(DT_FP4, 32, 128, 256, 128, 2) X(DT_FP4, 32, 128, 256, 128, 3) X(DT_FP4, 32, 256, 256, 128, 2)  \
+  X(DT_FP4, 32, 256, 256, 128, 3)
 
 #define GP_SPLITK_I8(Y) Y(DT_I8, 1, 4, 64) Y(DT_I8, 1, 4, 256) Y(DT_I8, 2, 4, 256)
 #define GP_SPLITK_FP8(Y)                                                                           \

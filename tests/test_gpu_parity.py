@@ -89,6 +89,14 @@ TILE_CASES = [
     ("mxfp4", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
     ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
     ("mxfp4", 128, 256, 1024, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=3)),
+    # 256x256 tiles, one workgroup per CU (accumulators in AGPRs)
+    ("bf16", 256, 512, 192, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=3)),
+    ("bf16", 512, 256, 320, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
+    ("bf16", 256, 256, 64, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=32, pipeline=2, epilogue=1)),
+    ("bf16", 256, 512, 160, dict(kernel=1, tile_m=256, tile_n=256, tile_k=32, mfma=32, pipeline=3)),
+    ("fp8", 256, 512, 640, dict(kernel=1, tile_m=256, tile_n=256, tile_k=128, pipeline=3)),
+    ("mxfp4", 256, 512, 768, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
+    ("mxfp4", 512, 256, 1024, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=3)),
     # small-M split-K kernel
     ("fp8", 16, 512, 2048, dict(kernel=2)),
     ("fp8", 32, 256, 1024, dict(kernel=2, tile_n=32)),
