@@ -249,11 +249,8 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
 #pragma unroll
     for (int ni = 0; ni < C::NACC; ++ni) acc[mi][ni] = Acc{};
 
-  auto load_a = [&](int kt) {
-    if constexpr (C::ASYNC) return;
-#pragma unroll
-    for (int i = 0; i < C::ALOADS; ++i)
-      a_st[i] = buf_load16(ra, a_on(i) ? a_ld0 : kOOB, kt * TKB + i * RPP * Kb);
+  auto load_a = [&](int kt, int i) {
+    if constexpr (!C::ASYNC) a_st[i] = buf_load16(ra, a_on(i) ? a_ld0 : kOOB, kt * TKB + i * RPP * Kb);
   };
   auto store_a = [&](int par) {
     if constexpr (C::ASYNC) return;
@@ -262,45 +259,36 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
     for (int i = 0; i < C::ALOADS; ++i)
       *(v4i*)(base + (a_on(i) ? a_wr_off(i) : (uint32_t)(TM * TKB))) = a_st[i];
   };
-  auto load_a_dma = [&](int stage, int kt) {
+  auto load_a_dma = [&](int stage, int kt, int i) {
     if constexpr (C::ASYNC) {
-#pragma unroll
-      for (int i = 0; i < C::ALOADS; ++i) {
-        char* dst = lds + stage * C::ABUF + (i * C::WAVES + wave) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_dma0,
-                                                 kt * TKB + i * RPD * Kb, 0, 0);
-      }
+      char* dst = lds + stage * C::ABUF + (i * C::WAVES + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_dma0,
+                                               kt * TKB + i * RPD * Kb, 0, 0);
     }
   };
-  auto load_b = [&](auto par_c, int kt) {
+  // B load q of a tile: K step q / (NACC*FRAG), column block (q / FRAG) % NACC, piece q % FRAG
+  auto load_b = [&](auto par_c, int kt, int q) {
     constexpr int par = decltype(par_c)::value;
+    const int s = q / (C::NACC * C::FRAG), ni = (q / C::FRAG) % C::NACC, f = q % C::FRAG;
     const uint32_t kbase = (uint32_t)kt * (TKB / 64) * 1024u;
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s)
-#pragma unroll
-      for (int ni = 0; ni < C::NACC; ++ni)
-#pragma unroll
-        for (int f = 0; f < C::FRAG; ++f)
-          bfr[par][s][ni][f] = buf_load16(rb, b_off0 + b_koff(s, f), kbase + ni * b_step);
+    bfr[par][s][ni][f] = buf_load16(rb, b_off0 + b_koff(s, f), kbase + ni * b_step);
   };
   // FP4: the WG's TM + TN scale rows of one K tile, SCB bytes each. A and B
   // rows use separate loads so that each load's buffer resource is uniform.
-  auto load_s = [&](int kt) {
+  // scale load i of a tile: A rows for i < SLA, then B rows
+  auto load_s = [&](int kt, int i) {
     if constexpr (DT == DT_FP4) {
       const uint32_t sbase = (uint32_t)kt * C::SCB;
-#pragma unroll
-      for (int i = 0; i < C::SLA; ++i) {
+      if (i < C::SLA) {
         const int r = i * C::THREADS + tid;
         const uint32_t off = r < TM ? r * srow : kOOB;
         if constexpr (C::SCB == 8) sa_st[i] = buf_load8(rsa, off, sbase);
         else sa_st[i][0] = buf_load4(rsa, off, sbase);
-      }
-#pragma unroll
-      for (int i = 0; i < C::SLB; ++i) {
-        const int r = i * C::THREADS + tid;
+      } else {
+        const int r = (i - C::SLA) * C::THREADS + tid;
         const uint32_t off = r < TN ? r * srow : kOOB;
-        if constexpr (C::SCB == 8) sb_st[i] = buf_load8(rsb, off, sbase);
-        else sb_st[i][0] = buf_load4(rsb, off, sbase);
+        if constexpr (C::SCB == 8) sb_st[i - C::SLA] = buf_load8(rsb, off, sbase);
+        else sb_st[i - C::SLA][0] = buf_load4(rsb, off, sbase);
       }
     }
   };
@@ -354,14 +342,17 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
 #pragma unroll
     for (int f = 0; f < C::FRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * MS * TKB);
   };
-  // Hot-loop order of one K tile: the first RA A-fragment reads, then all
-  // global loads of the tile PIPE-1 ahead (scales, A, B), then for every A
-  // fragment i: read fragment i+RA, issue fragment i's NACC MFMAs. The A
+  // Hot-loop order of one K tile: the first RA A-fragment reads, then for
+  // every A fragment i: in the first half of the tile an even share of the
+  // global loads of the tile PIPE-1 ahead (scales, A, B), the read of
+  // fragment i+RA, fragment i's NACC MFMAs. The A
   // fragments live in a ring of RA+1 register sets, so each ds_read has RA
   // groups of MFMAs to land in. Scheduling fences pin this order: left free,
   // the compiler folds the ring into one register set and waits for every
   // read right before its MFMAs.
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  constexpr int NBL = C::KSTEPS * C::NACC * C::FRAG;       // B loads per tile
+  constexpr int NVMEM = C::ALOADS + NBL + C::SLOADS;        // global loads per tile
   auto compute = [&](auto par_c, auto&& issue_loads) {
     constexpr int par = decltype(par_c)::value;
     // E8M0 scales from LDS: byte s of the value is the scale of K step s
@@ -375,60 +366,64 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
     }
     constexpr int NF = C::KSTEPS * C::MREP;
     constexpr int RA = C::RA < NF ? C::RA : NF;
+    constexpr int LH = NF > 1 ? NF / 2 : 1;  // groups that carry global loads
     v4i af[RA + 1][C::FRAG];
 #pragma unroll
     for (int j = 0; j < RA; ++j) read_a(par, j / C::MREP, j % C::MREP, af[j]);
     fence();
-    issue_loads();
-    fence();
-#pragma unroll
-    for (int i = 0; i < NF; ++i) {
-      const int s = i / C::MREP, mi = i % C::MREP;
-      if (i + RA < NF) read_a(par, (i + RA) / C::MREP, (i + RA) % C::MREP, af[(i + RA) % (RA + 1)]);
+    static_for<0, NF>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      constexpr int s = i / C::MREP, mi = i % C::MREP;
+      // this group's share of the tile's global loads
+      if constexpr (i < LH) issue_loads(std::integral_constant<int, i * NVMEM / LH>{}, std::integral_constant<int, (i + 1) * NVMEM / LH>{});
+      if constexpr (i + RA < NF) read_a(par, (i + RA) / C::MREP, (i + RA) % C::MREP, af[(i + RA) % (RA + 1)]);
       fence();
       const v4i* a = af[i % (RA + 1)];
 #pragma unroll
       for (int ni = 0; ni < C::NACC; ++ni) {
         if constexpr (DT == DT_FP4) {
-          switch (s) {
-            case 0: acc[mi][ni] = mma<DT, MS, 0>(bfr[par][s][ni], a, acc[mi][ni], psb[ni], psa[mi]); break;
-            case 1: acc[mi][ni] = mma<DT, MS, 1>(bfr[par][s][ni], a, acc[mi][ni], psb[ni], psa[mi]); break;
-            case 2: acc[mi][ni] = mma<DT, MS, 2>(bfr[par][s][ni], a, acc[mi][ni], psb[ni], psa[mi]); break;
-            default: acc[mi][ni] = mma<DT, MS, 3>(bfr[par][s][ni], a, acc[mi][ni], psb[ni], psa[mi]); break;
-          }
+          acc[mi][ni] = mma<DT, MS, s>(bfr[par][s][ni], a, acc[mi][ni], psb[ni], psa[mi]);
         } else {
           acc[mi][ni] = mma<DT, MS>(bfr[par][s][ni], a, acc[mi][ni]);
         }
       }
       fence();
-    }
+    });
   };
-  constexpr int NBL = C::KSTEPS * C::NACC * C::FRAG;       // B loads per tile
-  constexpr int NVMEM = C::ALOADS + NBL + C::SLOADS;        // global loads per tile
   // s_waitcnt vmcnt(n) alone (expcnt / lgkmcnt left alone)
   auto wait_vm = [&](auto n_c) {
     constexpr int n = decltype(n_c)::value;
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   };
-  auto loads = [&](auto stage_c, int kt_in) {
+  // global loads [J0, J1) of one tile, in the fixed order scales, A, B (the
+  // wait for A at the end of an iteration counts on that order)
+  auto loads = [&](auto stage_c, int kt_in, auto j0_c, auto j1_c) {
     constexpr int st = decltype(stage_c)::value;
     // the tile index is wave-uniform; say so, so that every offset built from
     // it stays in scalar registers (a VGPR offset would need a waterfall loop)
     const int kt = __builtin_amdgcn_readfirstlane(kt_in);
-    // order: scales, A, B (the wait for A below counts on it)
-    load_s(kt);
-    load_a(kt);
-    load_a_dma(st, kt);
-    load_b(stage_c, kt);
+    static_for<decltype(j0_c)::value, decltype(j1_c)::value>([&](auto j_c) {
+      constexpr int j = decltype(j_c)::value;
+      if constexpr (j < C::SLOADS) {
+        load_s(kt, j);
+      } else if constexpr (j < C::SLOADS + C::ALOADS) {
+        if constexpr (C::ASYNC) load_a_dma(st, kt, j - C::SLOADS);
+        else load_a(kt, j - C::SLOADS);
+      } else {
+        load_b(stage_c, kt, j - C::SLOADS - C::ALOADS);
+      }
+    });
   };
+  using J0 = std::integral_constant<int, 0>;
+  using JALL = std::integral_constant<int, NVMEM>;
   auto iter = [&](auto r_c, int kt) {
     constexpr int r = decltype(r_c)::value;
     constexpr int rn = (r + C::ST - 1) % C::ST;  // stage of the tile ST-1 ahead
     // past the end the last tile reloads itself into a free stage instead of
     // branching, keeping the body one straight-line block
     const int kn = min(kt + C::ST - 1, KT - 1);
-    compute(r_c, [&] { loads(std::integral_constant<int, rn>{}, kn); });
+    compute(r_c, [&](auto j0_c, auto j1_c) { loads(std::integral_constant<int, rn>{}, kn, j0_c, j1_c); });
     store_a(rn);
     store_s(rn);
     if constexpr (C::ASYNC) {
@@ -444,8 +439,8 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
 #pragma unroll
   for (int j = 0; j + 1 < C::ST; ++j) {
     const int kj = min(j, KT - 1);
-    if (j == 0) loads(std::integral_constant<int, 0>{}, kj);
-    else loads(std::integral_constant<int, (C::ST > 2 ? 1 : 0)>{}, kj);
+    if (j == 0) loads(std::integral_constant<int, 0>{}, kj, J0{}, JALL{});
+    else loads(std::integral_constant<int, (C::ST > 2 ? 1 : 0)>{}, kj, J0{}, JALL{});
     store_a(j);
     store_s(j);
   }

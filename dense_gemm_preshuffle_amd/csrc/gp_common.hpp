@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace gp {
 
@@ -18,6 +19,16 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// f(std::integral_constant<int, j>) for j = J0 .. J1-1, unrolled at compile time
+template <int J0, class F, int... Js>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Js...>) {
+  (f(std::integral_constant<int, J0 + Js>{}), ...);
+}
+template <int J0, int J1, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<J0>(f, std::make_integer_sequence<int, (J1 > J0 ? J1 - J0 : 0)>{});
+}
 
 enum DType : int { DT_I8 = 0, DT_FP8 = 1, DT_BF16 = 2, DT_FP4 = 3 };
 enum Epi : int { EPI_DIRECT = 1, EPI_CSHUFFLE = 2 };
