@@ -51,7 +51,7 @@ bool tile_compiled(int dt, int ms, int tm, int tn, int tkb, int pipe = -1) {
 }
 
 // Pipeline for a compiled tile: the caller's (opts.pipeline 1 = VGPR-staged
-// A, 2 / 3 = LDS DMA with 2 / 3 stages), else the deepest compiled one.
+// A, 2 .. 6 = LDS DMA with that many stages), else by the default order.
 int pick_pipe(int dt, int ms, int tm, int tn, int tkb, int want) {
   if (want > 0) {
     const int pipe = want == 1 ? 0 : want;
@@ -188,7 +188,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     if (o->epilogue < 0 || o->epilogue > 2 || o->kernel < 0 || o->kernel > 2) return GP_EINVAL;
     if (o->xcd_swizzle < 0 || o->xcd_swizzle > 2) return GP_EINVAL;
     if (o->mfma != 0 && o->mfma != 16 && o->mfma != 32) return GP_EINVAL;
-    if (o->pipeline < 0 || o->pipeline > 3) return GP_EINVAL;
+    if (o->pipeline < 0 || o->pipeline > 6) return GP_EINVAL;
   }
   if ((K * bits) % 8) return GP_ESHAPE;
   const int64_t Kb = K * bits / 8;

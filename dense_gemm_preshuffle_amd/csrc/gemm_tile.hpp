@@ -41,8 +41,8 @@ struct TileArgs {
 };
 
 // PIPE: 0 = A staged through VGPRs, two LDS buffers (prefetch one tile
-// ahead); 2 / 3 = A copied global -> LDS by the buffer-load LDS DMA, with 2
-// or 3 LDS buffers and B register sets (prefetch PIPE-1 tiles ahead).
+// ahead); 2 .. 6 = A copied global -> LDS by the buffer-load LDS DMA, with
+// PIPE LDS buffers and B register sets (prefetch PIPE-1 tiles ahead).
 template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE>
 struct TileCfg {
   using S = Mma<DT, MS>;
@@ -102,7 +102,7 @@ struct TileCfg {
   static_assert(!NSC || TKB == 128 || (MS == 16 && TKB == 64), "FP4 scale staging: 8 (or 4) bytes per row");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(!ASYNC || (!APART && (TM * CPR) % (THREADS * 1) == 0), "LDS DMA covers whole 1 KiB wave blocks");
-  static_assert(PIPE == 0 || PIPE == 2 || PIPE == 3, "pipeline");
+  static_assert(PIPE == 0 || (PIPE >= 2 && PIPE <= 6), "pipeline");
 };
 
 __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uint32_t& tn) {
@@ -242,7 +242,8 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
 
   v4i a_st[C::ASYNC ? 1 : C::ALOADS];
   v4i bfr[C::ST][C::KSTEPS][C::NACC][C::FRAG];
-  v2i sa_st[C::SLA + 1 - C::NSC], sb_st[C::SLB + 1 - C::NSC];
+  // FP4 scales of each in-flight tile, by stage (stored to LDS one tile ahead)
+  v2i sa_st[C::ST][C::SLA + 1 - C::NSC], sb_st[C::ST][C::SLB + 1 - C::NSC];
   Acc acc[C::MREP][C::NACC];
 #pragma unroll
   for (int mi = 0; mi < C::MREP; ++mi)
@@ -260,11 +261,9 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
       *(v4i*)(base + (a_on(i) ? a_wr_off(i) : (uint32_t)(TM * TKB))) = a_st[i];
   };
   auto load_a_dma = [&](int stage, int kt, int i) {
-    if constexpr (C::ASYNC) {
-      char* dst = lds + stage * C::ABUF + (i * C::WAVES + wave) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16, a_dma0,
-                                               kt * TKB + i * RPD * Kb, 0, 0);
-    }
+    if constexpr (C::ASYNC)
+      lds_dma16(p.a + (size_t)m0 * Kb, TM * Kb, lds + stage * C::ABUF + (i * C::WAVES + wave) * 1024,
+                a_dma0 + kt * TKB + i * RPD * Kb);
   };
   // B load q of a tile: K step q / (NACC*FRAG), column block (q / FRAG) % NACC, piece q % FRAG
   auto load_b = [&](auto par_c, int kt, int q) {
@@ -276,19 +275,19 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
   // FP4: the WG's TM + TN scale rows of one K tile, SCB bytes each. A and B
   // rows use separate loads so that each load's buffer resource is uniform.
   // scale load i of a tile: A rows for i < SLA, then B rows
-  auto load_s = [&](int kt, int i) {
+  auto load_s = [&](int st, int kt, int i) {
     if constexpr (DT == DT_FP4) {
       const uint32_t sbase = (uint32_t)kt * C::SCB;
       if (i < C::SLA) {
         const int r = i * C::THREADS + tid;
         const uint32_t off = r < TM ? r * srow : kOOB;
-        if constexpr (C::SCB == 8) sa_st[i] = buf_load8(rsa, off, sbase);
-        else sa_st[i][0] = buf_load4(rsa, off, sbase);
+        if constexpr (C::SCB == 8) sa_st[st][i] = buf_load8(rsa, off, sbase);
+        else sa_st[st][i][0] = buf_load4(rsa, off, sbase);
       } else {
         const int r = (i - C::SLA) * C::THREADS + tid;
         const uint32_t off = r < TN ? r * srow : kOOB;
-        if constexpr (C::SCB == 8) sb_st[i - C::SLA] = buf_load8(rsb, off, sbase);
-        else sb_st[i - C::SLA][0] = buf_load4(rsb, off, sbase);
+        if constexpr (C::SCB == 8) sb_st[st][i - C::SLA] = buf_load8(rsb, off, sbase);
+        else sb_st[st][i - C::SLA][0] = buf_load4(rsb, off, sbase);
       }
     }
   };
@@ -318,12 +317,12 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
 #pragma unroll
       for (int i = 0; i < C::SLA; ++i) {
         const int r = i * C::THREADS + tid;
-        put_s(base, r < TM ? r : C::SROWS, sa_st[i]);
+        put_s(base, r < TM ? r : C::SROWS, sa_st[par][i]);
       }
 #pragma unroll
       for (int i = 0; i < C::SLB; ++i) {
         const int r = i * C::THREADS + tid;
-        put_s(base, r < TN ? TM + r : C::SROWS, sb_st[i]);
+        put_s(base, r < TN ? TM + r : C::SROWS, sb_st[par][i]);
       }
     }
   };
@@ -406,7 +405,7 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
     static_for<decltype(j0_c)::value, decltype(j1_c)::value>([&](auto j_c) {
       constexpr int j = decltype(j_c)::value;
       if constexpr (j < C::SLOADS) {
-        load_s(kt, j);
+        load_s(st, kt, j);
       } else if constexpr (j < C::SLOADS + C::ALOADS) {
         if constexpr (C::ASYNC) load_a_dma(st, kt, j - C::SLOADS);
         else load_a(kt, j - C::SLOADS);
@@ -425,7 +424,9 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
     const int kn = min(kt + C::ST - 1, KT - 1);
     compute(r_c, [&](auto j0_c, auto j1_c) { loads(std::integral_constant<int, rn>{}, kn, j0_c, j1_c); });
     store_a(rn);
-    store_s(rn);
+    // FP4 scales of the next tile, loaded ST-2 iterations ago (its stage is
+    // free: its last reader was tile kt+1-ST)
+    store_s((r + 1) % C::ST);
     if constexpr (C::ASYNC) {
       // tile kt+1's DMA was issued ST-2 iterations ago, before that
       // iteration's B loads: everything issued after it may stay in flight
@@ -435,15 +436,13 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
     __syncthreads();
   };
 
-  // ---- prologue: tiles 0 .. ST-2 ----
-#pragma unroll
-  for (int j = 0; j + 1 < C::ST; ++j) {
-    const int kj = min(j, KT - 1);
-    if (j == 0) loads(std::integral_constant<int, 0>{}, kj, J0{}, JALL{});
-    else loads(std::integral_constant<int, (C::ST > 2 ? 1 : 0)>{}, kj, J0{}, JALL{});
+  // ---- prologue: tiles 0 .. ST-2 into stages 0 .. ST-2 ----
+  static_for<0, C::ST - 1>([&](auto j_c) {
+    constexpr int j = decltype(j_c)::value;
+    loads(j_c, min(j, KT - 1), J0{}, JALL{});
     store_a(j);
-    store_s(j);
-  }
+  });
+  store_s(0);
   if constexpr (C::ASYNC) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vm(std::integral_constant<int, NBL + (C::ST - 2) * NVMEM>{});
@@ -452,13 +451,11 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
 
   // ---- main loop, ST K tiles per trip ----
   int kt = 0;
-  for (; kt + C::ST <= KT; kt += C::ST) {
-    iter(std::integral_constant<int, 0>{}, kt);
-    iter(std::integral_constant<int, 1>{}, kt + 1);
-    if constexpr (C::ST == 3) iter(std::integral_constant<int, 2>{}, kt + 2);
-  }
-  if (kt < KT) iter(std::integral_constant<int, 0>{}, kt);
-  if (kt + 1 < KT) iter(std::integral_constant<int, 1>{}, kt + 1);
+  for (; kt + C::ST <= KT; kt += C::ST)
+    static_for<0, C::ST>([&](auto r_c) { iter(r_c, kt + decltype(r_c)::value); });
+  static_for<0, C::ST - 1>([&](auto r_c) {
+    if (kt + decltype(r_c)::value < KT) iter(r_c, kt + decltype(r_c)::value);
+  });
   // no DMA may still be writing LDS when the epilogue reuses it
   if constexpr (C::ASYNC) {
     wait_vm(std::integral_constant<int, 0>{});

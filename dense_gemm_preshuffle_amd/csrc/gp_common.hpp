@@ -60,6 +60,33 @@ __device__ __forceinline__ int buf_load4_early(__amdgpu_buffer_rsrc_t r, uint32_
 __device__ __forceinline__ v4i buf_load16_early(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kAuxVolatile);
 }
+// Global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane
+// l's bytes land at LDS byte lds_addr + 16*l. Issued from inline assembly so
+// that the compiler does not track the copy: its own tracking cannot tell LDS
+// buffers apart and makes the next LDS read wait for every copy in flight,
+// which would cap a multi-stage pipeline at one stage of latency. Callers wait
+// for the copy with an explicit s_waitcnt vmcnt that counts it in program
+// order. The compiler's own vmcnt waits only get stricter from loads it does
+// not count, never looser. M0 is set here; no compiler-generated code in these
+// kernels uses M0 (LDS instructions on gfx9 and later do not need it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t bytes, const void* lds_dst, uint32_t voff) {
+  // buffer resource of [base, base + bytes), every dword made explicitly
+  // wave-uniform so that the asm operand can live in SGPRs
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  v4i d;
+  d[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  d[1] = (int)(__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffff);
+  d[2] = (int)__builtin_amdgcn_readfirstlane(bytes);
+  d[3] = kRsrcWord3;
+  const uint32_t m0v =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(voff), "s"(d)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Non-temporal (streaming) variants: cache policy bit 1 (nt) on gfx950.
 constexpr int kPolicyNT = 2;
 __device__ __forceinline__ v4i buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {

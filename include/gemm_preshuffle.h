@@ -79,8 +79,8 @@ typedef struct gemm_opts {
   int xcd_swizzle;  /* 0 auto, 1 XCD-aware grouped tile order, 2 linear  */
   int waves;        /* split-K kernel: waves per workgroup (0 auto)      */
   int mfma;         /* tile kernel: MFMA block 16 (16x16) or 32 (32x32), 0 auto */
-  int pipeline;     /* tile kernel: 1 A staged through VGPRs (2 stages), 2 / 3 A by
-                       LDS DMA with 2 / 3 stages, 0 auto                      */
+  int pipeline;     /* tile kernel: 1 A staged through VGPRs (2 stages), 2 .. 6 A
+                       by LDS DMA with that many stages (where compiled), 0 auto */
 } gemm_opts;
 
 /* What the planner chose (host-side query, no GPU needed). */
@@ -97,7 +97,7 @@ typedef struct gemm_plan_info {
   int64_t mfma_per_wave_tile;       /* MFMA instructions per wave per K tile    */
   int64_t mfma_total;               /* MFMA instructions for the whole problem  */
   int mfma;                         /* MFMA block: 16 (16x16) or 32 (32x32)     */
-  int pipeline;                     /* 1 VGPR-staged A; 2 / 3 LDS DMA stages    */
+  int pipeline;                     /* 1 VGPR-staged A; 2 .. 6 LDS DMA stages   */
 } gemm_plan_info;
 
 /*

@@ -86,6 +86,17 @@ TILE_CASES = [
     ("fp8", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, pipeline=2)),
     ("fp8", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, pipeline=3)),
     ("fp8", 64, 512, 384, dict(kernel=1, tile_m=32, tile_n=256, tile_k=128, pipeline=3)),
+    ("fp8", 64, 256, 640, dict(kernel=1, tile_m=32, tile_n=128, tile_k=128, pipeline=3)),
+    ("fp8", 96, 384, 768, dict(kernel=1, tile_m=32, tile_n=128, tile_k=256, pipeline=3)),
+    ("fp8", 64, 512, 1280, dict(kernel=1, tile_m=32, tile_n=256, tile_k=256, pipeline=3)),
+    # 4- and 6-stage pipelines, K-tile counts 1 .. 13 (prologue clamp, tails)
+    ("fp8", 64, 256, 128, dict(kernel=1, tile_m=32, tile_n=256, tile_k=128, pipeline=6)),
+    ("fp8", 64, 256, 384, dict(kernel=1, tile_m=32, tile_n=256, tile_k=128, pipeline=6)),
+    ("fp8", 64, 512, 896, dict(kernel=1, tile_m=32, tile_n=256, tile_k=128, pipeline=6)),
+    ("fp8", 32, 256, 1664, dict(kernel=1, tile_m=32, tile_n=256, tile_k=128, pipeline=4)),
+    ("fp8", 96, 256, 768, dict(kernel=1, tile_m=32, tile_n=128, tile_k=256, pipeline=6)),
+    ("fp8", 64, 384, 1280, dict(kernel=1, tile_m=32, tile_n=128, tile_k=256, pipeline=4)),
+    ("fp8", 128, 512, 640, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, pipeline=4)),
     ("mxfp4", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
     ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
     ("mxfp4", 128, 256, 1024, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=3)),
