@@ -104,8 +104,8 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
   struct Cand { int tm, tn, tkb; };
   static const Cand i8[] = {{128, 256, 128}, {64, 256, 128}, {64, 128, 128}, {128, 128, 128},
                             {64, 64, 128}, {32, 64, 128}, {16, 64, 256}};
-  static const Cand fp8[] = {{128, 256, 128}, {64, 256, 128}, {32, 256, 128}, {128, 128, 128},
-                             {64, 128, 128}, {16, 64, 512}};
+  static const Cand fp8[] = {{128, 256, 128}, {64, 256, 128}, {32, 256, 256}, {32, 256, 128},
+                             {128, 128, 128}, {64, 128, 128}, {16, 64, 512}};
   static const Cand bf16[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {64, 128, 128},
                               {128, 256, 64}};
   static const Cand fp4[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {32, 256, 128},

@@ -40,7 +40,7 @@
 #define GP_SPLITK_I8(Y) Y(DT_I8, 1, 4, 64) Y(DT_I8, 1, 4, 256) Y(DT_I8, 2, 4, 256)
 #define GP_SPLITK_FP8(Y)                                                                           \
   Y(DT_FP8, 1, 4, 128) Y(DT_FP8, 1, 4, 256) Y(DT_FP8, 1, 4, 512) Y(DT_FP8, 2, 4, 256)             \
-  Y(DT_FP8, 2, 4, 512) Y(DT_FP8, 1, 8, 256) Y(DT_FP8, 4, 4, 256)
+  Y(DT_FP8, 2, 4, 512) Y(DT_FP8, 1, 8, 256) Y(DT_FP8, 4, 4, 256) Y(DT_FP8, 2, 8, 256) Y(DT_FP8, 4, 8, 256)
 #define GP_SPLITK_BF16(Y) Y(DT_BF16, 1, 4, 64) Y(DT_BF16, 1, 4, 256) Y(DT_BF16, 2, 4, 256)
 #define GP_SPLITK_FP4(Y) Y(DT_FP4, 1, 4, 64) Y(DT_FP4, 1, 4, 256) Y(DT_FP4, 2, 4, 256)
 

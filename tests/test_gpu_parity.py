@@ -112,6 +112,8 @@ TILE_CASES = [
     ("fp8", 16, 512, 2048, dict(kernel=2)),
     ("fp8", 32, 256, 1024, dict(kernel=2, tile_n=32)),
     ("fp8", 16, 256, 2048, dict(kernel=2, waves=8, tile_k=256)),
+    ("fp8", 16, 512, 2048, dict(kernel=2, tile_n=32, waves=8, tile_k=256)),
+    ("fp8", 32, 256, 4096, dict(kernel=2, tile_n=64, waves=8, tile_k=256)),   # 2 chunks per wave
     ("fp8", 16, 128, 4096, dict(kernel=2, tile_k=128)),   # 8 chunks per wave
     ("fp8", 16, 128, 1536, dict(kernel=2, tile_k=128)),   # 3 chunks (odd)
     ("int8", 16, 64, 1024, dict(kernel=2)),
