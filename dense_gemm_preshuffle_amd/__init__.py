@@ -25,6 +25,7 @@ __all__ = [
     "GemmError", "GemmLibraryMissing", "GemmOpts", "lib_path", "load_library",
     "gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_plan",
     "gemm_status_string", "source_hash", "DTYPES", "EPI_DIRECT", "EPI_CSHUFFLE", "KERNEL_TILE", "KERNEL_SPLITK",
+    "KERNEL_WIDE",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -35,7 +36,7 @@ GP_I8, GP_FP8_E4M3, GP_BF16, GP_FP4_E2M1, GP_I32 = 0, 1, 2, 3, 4
 DTYPES = {"int8": GP_I8, "fp8": GP_FP8_E4M3, "bf16": GP_BF16, "mxfp4": GP_FP4_E2M1}
 _ELEM_BITS = {GP_I8: 8, GP_FP8_E4M3: 8, GP_BF16: 16, GP_FP4_E2M1: 4}
 EPI_AUTO, EPI_DIRECT, EPI_CSHUFFLE = 0, 1, 2
-KERNEL_AUTO, KERNEL_TILE, KERNEL_SPLITK = 0, 1, 2
+KERNEL_AUTO, KERNEL_TILE, KERNEL_SPLITK, KERNEL_WIDE = 0, 1, 2, 3
 
 
 class GemmError(RuntimeError):

@@ -37,11 +37,14 @@ int kdt(int dt) {
 
 struct TileVar { int dt, ms, tm, tn, tkb, pipe; };
 struct SplitVar { int dt, nb, waves, kch; };
+struct WideVar { int dt, ms, tkb, pipe; };
 
 #define GP_TILE_ENTRY(DT, MS, TM, TN, TKB, PIPE) {DT, MS, TM, TN, TKB, PIPE},
 #define GP_SPLIT_ENTRY(DT, NB, W, KCH) {DT, NB, W, KCH},
+#define GP_WIDE_ENTRY(DT, MS, TKB, PIPE) {DT, MS, TKB, PIPE},
 constexpr TileVar kTiles[] = {GP_TILE_ALL(GP_TILE_ENTRY)};
 constexpr SplitVar kSplits[] = {GP_SPLITK_ALL(GP_SPLIT_ENTRY)};
+constexpr WideVar kWides[] = {GP_WIDE_ALL(GP_WIDE_ENTRY)};
 
 bool tile_compiled(int dt, int ms, int tm, int tn, int tkb, int pipe = -1) {
   for (const auto& v : kTiles)
@@ -73,8 +76,8 @@ bool split_compiled(int dt, int nb, int waves, int kch) {
 struct Plan {
   int kernel = 0;
   int ms = 16;                  // MFMA block (16 or 32)
-  int pipe = 0;                 // 0 VGPR-staged A, 2 / 3 LDS DMA stages
-  int tm = 0, tn = 0, tkb = 0;  // tile kernel (tkb in bytes)
+  int pipe = 0;                 // 0 VGPR-staged A, 2 .. 6 LDS DMA stages
+  int tm = 0, tn = 0, tkb = 0;  // tile and wide kernels (tkb in bytes)
   int epi = EPI_DIRECT;
   int xcd = 1;
   int nb = 0, waves = 4, kch = 0;  // split-K kernel
@@ -179,13 +182,46 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
   return GP_ESHAPE;
 }
 
+// Wide kernel (256x256 tiles, 8 waves, A and B through LDS): the caller's
+// MFMA block (default 16), tile_k and pipeline where given; otherwise the
+// compiled variant with the largest tile_k dividing K, then the most stages.
+int choose_wide(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, const gemm_opts* o) {
+  if (o && ((o->tile_m && o->tile_m != 256) || (o->tile_n && o->tile_n != 256))) return GP_ESHAPE;
+  if (o && o->waves && o->waves != 8) return GP_ESHAPE;
+  if (o && o->pipeline == 1) return GP_ESHAPE;   // both operands always go by LDS DMA
+  if (M % 256 || N % 256) return GP_ESHAPE;
+  const int ms = (o && o->mfma) ? o->mfma : 16;
+  int want_tkb = 0;
+  if (o && o->tile_k) {
+    if (((int64_t)o->tile_k * bits) % 8) return GP_ESHAPE;
+    want_tkb = (int)((int64_t)o->tile_k * bits / 8);
+  }
+  const int want_pipe = o ? o->pipeline : 0;
+  int best = -1;
+  for (int i = 0; i < (int)(sizeof(kWides) / sizeof(kWides[0])); ++i) {
+    const WideVar& v = kWides[i];
+    if (v.dt != dt || v.ms != ms || Kb % v.tkb) continue;
+    if ((want_tkb && v.tkb != want_tkb) || (want_pipe && v.pipe != want_pipe)) continue;
+    if (best < 0 || v.tkb > kWides[best].tkb || (v.tkb == kWides[best].tkb && v.pipe > kWides[best].pipe)) best = i;
+  }
+  if (best < 0) return GP_ESHAPE;
+  p->tm = p->tn = 256;
+  p->ms = ms;
+  p->tkb = kWides[best].tkb;
+  p->pipe = kWides[best].pipe;
+  p->epi = dt == DT_I8 ? EPI_DIRECT : EPI_CSHUFFLE;   // an int32 C tile does not fit LDS
+  if (o && o->epilogue && o->epilogue != p->epi) return GP_ESHAPE;
+  p->xcd = (o && o->xcd_swizzle) ? o->xcd_swizzle : 1;
+  return GP_OK;
+}
+
 int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o, Plan* p) {
   if (M <= 0 || N <= 0 || K <= 0) return GP_EINVAL;
   const int bits = elem_bits(in_dtype);
   if (bits == 0) return GP_EDTYPE;
   if (o) {
     if (o->tile_m < 0 || o->tile_n < 0 || o->tile_k < 0 || o->waves < 0) return GP_EINVAL;
-    if (o->epilogue < 0 || o->epilogue > 2 || o->kernel < 0 || o->kernel > 2) return GP_EINVAL;
+    if (o->epilogue < 0 || o->epilogue > 2 || o->kernel < 0 || o->kernel > 3) return GP_EINVAL;
     if (o->xcd_swizzle < 0 || o->xcd_swizzle > 2) return GP_EINVAL;
     if (o->mfma != 0 && o->mfma != 16 && o->mfma != 32) return GP_EINVAL;
     if (o->pipeline < 0 || o->pipeline > 6) return GP_EINVAL;
@@ -200,6 +236,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   p->Kb = Kb;
   p->kernel = (o && o->kernel) ? o->kernel : (M <= 32 ? GP_KERNEL_SPLITK : GP_KERNEL_TILE);
   if (p->kernel == GP_KERNEL_SPLITK) return choose_split(dt, bits, M, N, Kb, p, o);
+  if (p->kernel == GP_KERNEL_WIDE) return choose_wide(dt, bits, M, N, Kb, p, o);
 
   const bool user_tile = o && (o->tile_m || o->tile_n || o->tile_k);
   if (user_tile) {
@@ -239,15 +276,27 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
   std::memset(out, 0, sizeof(*out));
   const int bits = elem_bits(in_dtype);
   const int dt = kdt(in_dtype);
-  const int ms = p.kernel == GP_KERNEL_TILE ? p.ms : 16;
+  const int ms = p.kernel != GP_KERNEL_SPLITK ? p.ms : 16;
   const int kbm = kernel_mfma_kb(dt, ms);
   const int64_t kinstr = (int64_t)kbm * 8 / bits;   // K elements per MFMA
   out->kernel = p.kernel;
   out->mfma = ms;
-  out->pipeline = p.kernel == GP_KERNEL_TILE ? (p.pipe ? p.pipe : 1) : 0;
+  out->pipeline = p.kernel != GP_KERNEL_SPLITK ? (p.pipe ? p.pipe : 1) : 0;
   out->mfma_total = (M / ms) * (N / ms) * (K / kinstr);
-  out->xcd_swizzle = p.kernel == GP_KERNEL_TILE ? p.xcd : 2;
-  if (p.kernel == GP_KERNEL_TILE) {
+  out->xcd_swizzle = p.kernel != GP_KERNEL_SPLITK ? p.xcd : 2;
+  if (p.kernel == GP_KERNEL_WIDE) {
+    out->tile_m = out->tile_n = 256;
+    out->tile_k = (int)((int64_t)p.tkb * 8 / bits);
+    out->epilogue = p.epi;
+    out->waves = 8;
+    out->threads = 512;
+    const int stages = p.pipe * 512 * p.tkb;                 // A and B tiles per stage
+    const int cbytes = p.epi == EPI_CSHUFFLE ? 256 * (256 * 2 + 16) : 0;
+    out->lds_bytes = (stages > cbytes ? stages : cbytes) + (dt == DT_FP8 ? 512 * 4 : 0);
+    out->grid = (M / 256) * (N / 256);
+    out->k_tiles = p.Kb / p.tkb;
+    out->mfma_per_wave_tile = (int64_t)(p.tkb / kbm) * (128 / ms) * (64 / ms);
+  } else if (p.kernel == GP_KERNEL_TILE) {
     out->tile_m = p.tm;
     out->tile_n = p.tn;
     out->tile_k = (int)((int64_t)p.tkb * 8 / bits);
@@ -302,7 +351,7 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
            void* c, int64_t M, int64_t N, hipStream_t s) {
   const int dt = kdt(in_dtype);
   hipError_t e;
-  if (p.kernel == GP_KERNEL_TILE) {
+  if (p.kernel == GP_KERNEL_TILE || p.kernel == GP_KERNEL_WIDE) {
     TileArgs t;
     t.a = (const char*)a;
     t.b = (const char*)b;
@@ -315,7 +364,14 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
     t.tiles_m = (uint32_t)(M / p.tm);
     t.tiles_n = (uint32_t)(N / p.tn);
     t.xcd = p.xcd == 1 ? 1u : 0u;
-    switch (dt) {
+    if (p.kernel == GP_KERNEL_WIDE) {
+      switch (dt) {
+        case DT_I8: e = launch_wide_i8(p.ms, p.tkb, p.pipe, t, s); break;
+        case DT_FP8: e = launch_wide_fp8(p.ms, p.tkb, p.pipe, t, s); break;
+        case DT_BF16: e = launch_wide_bf16(p.ms, p.tkb, p.pipe, t, s); break;
+        default: e = hipErrorInvalidValue; break;
+      }
+    } else switch (dt) {
       case DT_I8: e = launch_tile_i8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;
       case DT_FP8: e = launch_tile_fp8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;
       case DT_BF16: e = launch_tile_bf16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;

@@ -14,4 +14,9 @@ hipError_t launch_splitk_bf16(int nb, int waves, int kch, const SplitArgs& a, hi
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_wide_bf16(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s) {
+  GP_WIDE_BF16(GP_WIDE_CASE)
+  return hipErrorInvalidValue;
+}
+
 }  // namespace gp

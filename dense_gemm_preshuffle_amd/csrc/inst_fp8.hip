@@ -14,4 +14,9 @@ hipError_t launch_splitk_fp8(int nb, int waves, int kch, const SplitArgs& a, hip
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_wide_fp8(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s) {
+  GP_WIDE_FP8(GP_WIDE_CASE)
+  return hipErrorInvalidValue;
+}
+
 }  // namespace gp

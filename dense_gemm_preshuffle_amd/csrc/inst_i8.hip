@@ -14,4 +14,9 @@ hipError_t launch_splitk_i8(int nb, int waves, int kch, const SplitArgs& a, hipS
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_wide_i8(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s) {
+  GP_WIDE_I8(GP_WIDE_CASE)
+  return hipErrorInvalidValue;
+}
+
 }  // namespace gp

@@ -6,6 +6,7 @@
 
 #include "gemm_splitk.hpp"
 #include "gemm_tile.hpp"
+#include "gemm_wide.hpp"
 
 namespace gp {
 
@@ -18,6 +19,9 @@ hipError_t launch_splitk_i8(int nb, int waves, int kch, const SplitArgs& a, hipS
 hipError_t launch_splitk_fp8(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
 hipError_t launch_splitk_bf16(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
 hipError_t launch_splitk_fp4(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
+hipError_t launch_wide_i8(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s);
+hipError_t launch_wide_fp8(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s);
+hipError_t launch_wide_bf16(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s);
 
 }  // namespace gp
 
@@ -35,5 +39,10 @@ hipError_t launch_splitk_fp4(int nb, int waves, int kch, const SplitArgs& a, hip
   if (nb == NB && waves == W && kch == KCH) {                                              \
     const dim3 grid(a.N / (16 * NB), a.M / 16);                                            \
     hipLaunchKernelGGL((gemm_splitk_kernel<DT, NB, W, KCH>), grid, dim3(W * 64), 0, s, a); \
+    return hipGetLastError();                                                              \
+  }
+#define GP_WIDE_CASE(DT, MS, TKB, PIPE)                                                     \
+  if (ms == MS && tkb == TKB && pipe == PIPE) {                                            \
+    hipLaunchKernelGGL((gemm_wide_kernel<DT, MS, TKB, PIPE>), dim3(a.tiles_m * a.tiles_n), dim3(512), 0, s, a); \
     return hipGetLastError();                                                              \
   }

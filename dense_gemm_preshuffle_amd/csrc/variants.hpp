@@ -6,6 +6,8 @@
 // by LDS DMA with 2 / 3 stages. Each is built with the direct and the
 // CShuffle epilogue.
 // Split-K kernel: Y(dtype, n_blocks_of_16, waves, chunk_bytes_per_wave).
+// Wide kernel (256x256 tiles, 8 waves): W(dtype, mfma, tile_k_bytes, pipe),
+// pipe = LDS DMA stages of A and B.
 #pragma once
 
 #define GP_TILE_I8(X)                                                                              \
@@ -44,5 +46,12 @@
 #define GP_SPLITK_BF16(Y) Y(DT_BF16, 1, 4, 64) Y(DT_BF16, 1, 4, 256) Y(DT_BF16, 2, 4, 256)
 #define GP_SPLITK_FP4(Y) Y(DT_FP4, 1, 4, 64) Y(DT_FP4, 1, 4, 256) Y(DT_FP4, 2, 4, 256)
 
+#define GP_WIDE_I8(W) W(DT_I8, 16, 128, 2) W(DT_I8, 32, 128, 2)
+#define GP_WIDE_FP8(W) W(DT_FP8, 16, 128, 2)
+#define GP_WIDE_BF16(W) W(DT_BF16, 16, 128, 2) W(DT_BF16, 32, 128, 2) W(DT_BF16, 16, 64, 3) W(DT_BF16, 32, 64, 3) \
+  W(DT_BF16, 16, 64, 4) W(DT_BF16, 32, 64, 4)
+#define GP_WIDE_FP4(W)
+
 #define GP_TILE_ALL(X) GP_TILE_I8(X) GP_TILE_FP8(X) GP_TILE_BF16(X) GP_TILE_FP4(X)
 #define GP_SPLITK_ALL(Y) GP_SPLITK_I8(Y) GP_SPLITK_FP8(Y) GP_SPLITK_BF16(Y) GP_SPLITK_FP4(Y)
+#define GP_WIDE_ALL(W) GP_WIDE_I8(W) GP_WIDE_FP8(W) GP_WIDE_BF16(W) GP_WIDE_FP4(W)

@@ -62,9 +62,11 @@ enum {
 enum {
   GP_KERNEL_AUTO = 0,
   GP_KERNEL_TILE = 1,    /* LDS ping-pong tile kernel (GEMM Opt. §1-§7)            */
-  GP_KERNEL_SPLITK = 2   /* small-M kernel: waves of a workgroup split K,
+  GP_KERNEL_SPLITK = 2,  /* small-M kernel: waves of a workgroup split K,
                             reduced through LDS (for the memory-bound small
                             batch of GEMM Opt. §1.3 / §8.3)                      */
+  GP_KERNEL_WIDE = 3     /* 256x256 tiles, 8 waves, A and B both through LDS
+                            (INT8, FP8, BF16; M and N multiples of 256)          */
 };
 
 /* Tuning options. Pass NULL, or a zero-filled struct, for all-automatic;

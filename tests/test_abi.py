@@ -127,6 +127,29 @@ def test_worked_example_plan():
     assert p["mfma_per_wave_tile"] * p["k_tiles"] * 4 == 4160   # in gfx942 K=32 instructions
 
 
+def test_wide_kernel_plan():
+    p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=3))
+    assert p["kernel"] == gp.KERNEL_WIDE and (p["tile_m"], p["tile_n"]) == (256, 256)
+    assert p["waves"] == 8 and p["threads"] == 512 and p["grid"] == 1024
+    # every MFMA of the problem is issued once: per wave per K tile x waves x workgroups x K tiles
+    assert p["mfma_per_wave_tile"] * 8 * p["grid"] * p["k_tiles"] == p["mfma_total"]
+    assert p["mfma_total"] == F.mfma_count_gfx950("bf16", 8192, 8192, 8192, p["mfma"])
+    # A and B stages (256 rows each) or the padded bf16 C tile, whichever is larger
+    assert p["lds_bytes"] == max(p["pipeline"] * 512 * p["tile_k"] * 2, 256 * (256 * 2 + 16))
+    q = gp.gemm_plan("int8", 512, 512, 512, dict(kernel=3, mfma=32))
+    assert q["epilogue"] == gp.EPI_DIRECT and q["mfma"] == 32
+    assert q["mfma_per_wave_tile"] * 8 * q["grid"] * q["k_tiles"] == q["mfma_total"]
+    for bad in (dict(kernel=3, tile_m=128, tile_n=256, tile_k=64), dict(kernel=3, pipeline=1),
+                dict(kernel=3, epilogue=1)):
+        with pytest.raises(gp.GemmError) as e:
+            gp.gemm_plan("bf16", 512, 512, 512, bad)
+        assert e.value.status == GP_ESHAPE
+    with pytest.raises(gp.GemmError):
+        gp.gemm_plan("mxfp4", 512, 512, 512, dict(kernel=3))     # FP4 runs on the 4-wave kernel
+    with pytest.raises(gp.GemmError):
+        gp.gemm_plan("bf16", 384, 512, 512, dict(kernel=3))      # M not a multiple of 256
+
+
 def test_small_m_uses_split_k():
     p = gp.gemm_plan("fp8", 16, 7168, 2048)
     assert p["kernel"] == gp.KERNEL_SPLITK and p["tile_m"] == 16

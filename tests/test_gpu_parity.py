@@ -108,6 +108,17 @@ TILE_CASES = [
     ("fp8", 256, 512, 640, dict(kernel=1, tile_m=256, tile_n=256, tile_k=128, pipeline=3)),
     ("mxfp4", 256, 512, 768, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
     ("mxfp4", 512, 256, 1024, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=3)),
+    # wide kernel: 256x256 tiles, 8 waves, A and B through LDS; K-tile counts 1 .. 7
+    ("bf16", 256, 256, 64, dict(kernel=3)),
+    ("bf16", 512, 256, 320, dict(kernel=3)),
+    ("bf16", 256, 512, 448, dict(kernel=3, mfma=32)),
+    ("bf16", 256, 512, 160, dict(kernel=3, tile_k=32, pipeline=3)),
+    ("bf16", 512, 256, 224, dict(kernel=3, tile_k=32, mfma=32, pipeline=4)),
+    ("bf16", 256, 256, 96, dict(kernel=3, tile_k=32, pipeline=4)),
+    ("fp8", 512, 512, 640, dict(kernel=3)),
+    ("fp8", 256, 256, 128, dict(kernel=3)),
+    ("int8", 256, 512, 384, dict(kernel=3)),
+    ("int8", 512, 256, 256, dict(kernel=3, mfma=32)),
     # small-M split-K kernel
     ("fp8", 16, 512, 2048, dict(kernel=2)),
     ("fp8", 32, 256, 1024, dict(kernel=2, tile_n=32)),
