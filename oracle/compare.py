@@ -1,6 +1,7 @@
-"""Comparison of a bf16 GPU result with the float64 oracle (test infrastructure).
+"""Comparison of a bf16 / fp16 GPU result with the float64 oracle (test infrastructure).
 
-Tolerances for the floating-point paths (FP8, BF16, MXFP4 with bf16 output):
+Tolerances for the floating-point paths (FP8, BF16, MXFP4, W4A8 with bf16
+output; FP16 with fp16 output):
   * normwise   ||C - R||_F / ||R||_F <= 2e-3
   * elementwise max_i |C_i - R_i| / max(|R_i|, tau) <= 1e-2,
     tau = 1e-2 * RMS(R).
@@ -8,14 +9,15 @@ The floor tau is needed because the literal |C_i - R_i| / |R_i| is unbounded
 for outputs that cancel to nearly zero: fp32 accumulation leaves an absolute
 error of order sqrt(K) * 2^-24 * RMS(products), which is a large relative
 error when |R_i| is tiny, even for a correctly rounded kernel. For every other
-output, bf16 round-to-nearest-even alone contributes at most 2^-9 relative.
+output, bf16 round-to-nearest-even alone contributes at most 2^-9 relative
+(fp16: 2^-12).
 The literal value is reported alongside.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .formats import decode_bf16
+from .formats import decode_bf16, decode_f16
 
 NORMWISE_TOL = 2e-3
 ELEM_TOL = 1e-2
@@ -35,9 +37,27 @@ def bf16_rne(x: np.ndarray) -> np.ndarray:
     return np.ldexp(r, e - 8)
 
 
+def f16_rne(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest fp16 (ties to even, normal range), as float64."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    scaled = np.ldexp(m, 11)               # 11 significant bits of fp16
+    return np.ldexp(np.round(scaled), e - 11)
+
+
 def compare_bf16(c_bits: np.ndarray, ref: np.ndarray) -> dict:
     """Metrics of a bf16 result (uint16 bit patterns) against float64 ref."""
-    c = decode_bf16(np.asarray(c_bits).view(np.uint16))
+    return compare_values(decode_bf16(np.asarray(c_bits).view(np.uint16)), ref)
+
+
+def compare_f16(c_bits: np.ndarray, ref: np.ndarray) -> dict:
+    """Metrics of an fp16 result (uint16 bit patterns) against float64 ref."""
+    return compare_values(decode_f16(np.asarray(c_bits).view(np.uint16)), ref)
+
+
+def compare_values(c: np.ndarray, ref: np.ndarray) -> dict:
+    """Metrics of decoded result values (float64) against float64 ref."""
+    c = np.asarray(c, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     if c.shape != r.shape:
         raise ValueError(f"shape mismatch {c.shape} vs {r.shape}")

@@ -21,8 +21,9 @@ up to 2MNK.
 from __future__ import annotations
 
 ELEM_BYTES = {"int8": 1.0, "fp8": 1.0, "bf16": 2.0, "fp16": 2.0, "mxfp4": 0.5, "int4": 0.5}
-K_INSTR_GFX950 = {"int8": 64, "fp8": 128, "bf16": 32, "mxfp4": 128}          # 16x16 blocks
-K_INSTR_GFX950_32 = {"int8": 32, "fp8": 64, "bf16": 16, "mxfp4": 64}         # 32x32 blocks
+# K elements per gfx950 instruction; W4A8 widens INT4 to int8 and runs the int8 ones
+K_INSTR_GFX950 = {"int8": 64, "fp8": 128, "bf16": 32, "fp16": 32, "mxfp4": 128, "w4a8": 64}   # 16x16 blocks
+K_INSTR_GFX950_32 = {"int8": 32, "fp8": 64, "bf16": 16, "fp16": 16, "mxfp4": 64, "w4a8": 32}  # 32x32 blocks
 
 
 def derived(tile_m: int, tile_n: int, tile_k: int, elem_bytes: float = 1.0) -> dict:
@@ -91,11 +92,11 @@ def bytes_moved(dtype: str, M: int, N: int, K: int, out_bytes: int = 2) -> int:
         return M * K + N * K + M * N * out_bytes + (M + N) * 4
     if dtype == "int8":
         return M * K + N * K + M * N * out_bytes
-    if dtype == "int4":
+    if dtype in ("int4", "w4a8"):
         return M * K + (N * K) // 2 + M * N * out_bytes + (M + N) * 4
     if dtype == "mxfp4":
         return (M * K) // 2 + (N * K) // 2 + M * N * out_bytes + (M + N) * (K // 32)
-    if dtype == "bf16":
+    if dtype in ("bf16", "fp16"):
         return 2 * M * K + 2 * N * K + M * N * out_bytes
     raise ValueError(dtype)
 

@@ -17,6 +17,18 @@ K * 2^-53 relative error, far below the bf16 output rounding. The float64
 product is numpy's matmul, used as a library primitive; there is no blocking,
 reordering or fusion beyond decode-then-multiply.
 
+FP16 (§6.2's f16 instruction) decodes IEEE binary16; W4A8 (§8.2's INT4
+weights) multiplies int8 A by int4 B exactly in int64 and applies fp32
+per-row / per-column scales like FP8.
+
+Fused epilogues (Kernel Tuning Guide §6 lists bias, bias+ReLU, bias+SiLU and
+bias+GELU): after the scales, an fp32 bias per output column is added and
+the activation applied, all in float64:
+    relu(x) = max(x, 0)
+    silu(x) = x * sigmoid(x) = x / (1 + exp(-x))
+    gelu(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt(2)))     (the exact, erf form)
+The pages name the activations only; these are their standard definitions.
+
 `rows` / `cols` select a subset of outputs (used to check sampled outputs of
 large problems): the result is C[rows][:, cols].
 """
@@ -24,7 +36,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import decode_int8, decode_bf16, decode_e4m3, decode_e2m1, decode_e8m0, unpack_fp4
+from .formats import (decode_int8, decode_bf16, decode_e4m3, decode_e2m1, decode_e8m0, decode_f16,
+                      decode_int4, unpack_fp4, unpack_nibbles)
+
+ACTS = ("none", "relu", "silu", "gelu")
 
 
 def _take(x, idx):
@@ -57,6 +72,47 @@ def gemm_bf16(a, b, rows=None, cols=None) -> np.ndarray:
     return A @ B.T
 
 
+def gemm_f16(a, b, rows=None, cols=None) -> np.ndarray:
+    """fp16 bits [M,K] x [N,K]^T -> float64."""
+    A = decode_f16(_take(a, rows))
+    B = decode_f16(_take(b, cols))
+    return A @ B.T
+
+
+def gemm_w4a8(a, b, scale_a, scale_b, rows=None, cols=None) -> np.ndarray:
+    """int8 [M,K] x packed int4 [N,K/2]^T (exact int64), times scale_a[m] * scale_b[n] -> float64."""
+    A = decode_int8(_take(a, rows))
+    B = decode_int4(unpack_nibbles(_take(b, cols)))
+    sa = np.asarray(_take(scale_a, rows), dtype=np.float32).astype(np.float64)
+    sb = np.asarray(_take(scale_b, cols), dtype=np.float32).astype(np.float64)
+    return (A @ B.T).astype(np.float64) * sa[:, None] * sb[None, :]
+
+
+def activation(x: np.ndarray, act: str) -> np.ndarray:
+    """The epilogue activation in float64 (definitions in the module docstring)."""
+    from scipy.special import erf
+
+    x = np.asarray(x, dtype=np.float64)
+    if act == "none":
+        return x
+    if act == "relu":
+        return np.maximum(x, 0.0)
+    if act == "silu":
+        with np.errstate(over="ignore"):
+            return x / (1.0 + np.exp(-x))
+    if act == "gelu":
+        return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+    raise ValueError(act)
+
+
+def apply_epilogue(r: np.ndarray, bias=None, act: str = "none", cols=None) -> np.ndarray:
+    """act(R + bias[n]) with bias fp32 [N] (or None)."""
+    out = np.asarray(r, dtype=np.float64)
+    if bias is not None:
+        out = out + np.asarray(_take(bias, cols), dtype=np.float32).astype(np.float64)[None, :]
+    return activation(out, act)
+
+
 def _dec_mx(packed, scale):
     vals = decode_e2m1(unpack_fp4(packed))                  # [R, K]
     s = decode_e8m0(scale)                                  # [R, K/32]
@@ -70,14 +126,30 @@ def gemm_mxfp4(a, scale_a, b, scale_b, rows=None, cols=None) -> np.ndarray:
     return A @ B.T
 
 
-def gemm(dtype: str, inputs: dict, rows=None, cols=None) -> np.ndarray:
-    """Dispatch on the workload dtype with the input dict of workloads.make_inputs."""
+def _gemm(dtype, inputs, rows, cols):
     if dtype == "int8":
         return gemm_int8(inputs["a"], inputs["b"], rows, cols)
     if dtype == "fp8":
         return gemm_fp8(inputs["a"], inputs["b"], inputs["scale_a"], inputs["scale_b"], rows, cols)
     if dtype == "bf16":
         return gemm_bf16(inputs["a"], inputs["b"], rows, cols)
+    if dtype == "fp16":
+        return gemm_f16(inputs["a"], inputs["b"], rows, cols)
     if dtype == "mxfp4":
         return gemm_mxfp4(inputs["a"], inputs["scale_a"], inputs["b"], inputs["scale_b"], rows, cols)
+    if dtype == "w4a8":
+        return gemm_w4a8(inputs["a"], inputs["b"], inputs["scale_a"], inputs["scale_b"], rows, cols)
     raise ValueError(dtype)
+
+
+def gemm(dtype: str, inputs: dict, rows=None, cols=None, act=None) -> np.ndarray:
+    """Dispatch on the workload dtype with the input dict of workloads.make_inputs.
+
+    With `act` given (one of ACTS), the fused epilogue is applied: the bias
+    inputs["bias"] (if present) is added and the activation taken."""
+    r = _gemm(dtype, inputs, rows, cols)
+    if act is None:
+        return r
+    if dtype == "int8":
+        raise ValueError("the INT8 -> int32 path has no fused epilogue")
+    return apply_epilogue(r, inputs.get("bias"), act, cols)

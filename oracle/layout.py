@@ -40,3 +40,45 @@ def unshuffle(bs: np.ndarray, N: int, Kb: int) -> np.ndarray:
     """Inverse of preshuffle: flat bytes -> [N, Kb] bytes."""
     t = np.ascontiguousarray(bs).view(np.uint8).reshape(N // 16, Kb // 64, 4, 16, 16)
     return np.ascontiguousarray(t.transpose(0, 3, 1, 2, 4)).reshape(N, Kb)
+
+
+# INT4 weights (W4A8). The byte permutation above gives each lane 16 bytes =
+# 32 consecutive K elements of one column. The int8 matrix instruction takes
+# 16 K elements per lane, so a lane's 32 elements feed two instructions. The
+# INT4 layout additionally reorders the nibbles inside every 16-byte piece so
+# that its low nibbles hold elements 0..15 of the piece and its high nibbles
+# elements 16..31 (element t in byte t % 16, nibble t // 16): each half then
+# widens to 16 int8 values in K order with a mask and a shift per dword. The
+# pages fix no INT4 nibble order; this one is the layout's own definition.
+
+def repack_int4_pieces(b: np.ndarray) -> np.ndarray:
+    """Row-major packed INT4 bytes [N, Kb] (element 2i in the low nibble of
+    byte i) -> [N, Kb] bytes with every 16-byte piece reordered as above."""
+    bb = np.ascontiguousarray(b).view(np.uint8)
+    N, Kb = bb.shape
+    if Kb % 16:
+        raise ValueError("INT4 rows must be whole 16-byte pieces")
+    nib = np.empty((N, Kb * 2), dtype=np.uint8)           # element order
+    nib[:, 0::2] = bb & 0xF
+    nib[:, 1::2] = bb >> 4
+    t = nib.reshape(N, Kb // 16, 2, 16)                    # piece, half (t // 16), t % 16
+    out = t[:, :, 0, :] | (t[:, :, 1, :] << 4)
+    return np.ascontiguousarray(out.reshape(N, Kb))
+
+
+def unpack_int4_pieces(r: np.ndarray) -> np.ndarray:
+    """Inverse of repack_int4_pieces."""
+    rr = np.ascontiguousarray(r).view(np.uint8)
+    N, Kb = rr.shape
+    t = rr.reshape(N, Kb // 16, 16)
+    nib = np.stack([t & 0xF, t >> 4], axis=2).reshape(N, Kb * 2)   # element order
+    return np.ascontiguousarray((nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8))
+
+
+def preshuffle_int4(b: np.ndarray) -> np.ndarray:
+    """Packed INT4 B [N, Kb] -> the W4A8 preshuffled flat bytes."""
+    return preshuffle(repack_int4_pieces(b))
+
+
+def unshuffle_int4(bs: np.ndarray, N: int, Kb: int) -> np.ndarray:
+    return unpack_int4_pieces(unshuffle(bs, N, Kb))

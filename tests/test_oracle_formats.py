@@ -84,3 +84,36 @@ def test_decoder_rejects_nothing_silently(name):
         assert oracle.decode_e4m3(np.arange(256, dtype=np.uint8)).dtype == np.float64
     else:
         assert oracle.decode_bf16(np.arange(16, dtype=np.uint16)).dtype == np.float64
+
+
+def test_f16_matches_numpy_all_codes():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = oracle.decode_f16(codes)
+    ref = codes.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+
+
+def test_f16_spot_values():
+    d = oracle.decode_f16
+    assert d(np.uint16(0x3C00)) == 1.0
+    assert d(np.uint16(0xC000)) == -2.0
+    assert d(np.uint16(0x7BFF)) == 65504.0            # largest finite
+    assert d(np.uint16(0x0001)) == 2.0 ** -24         # smallest subnormal
+    assert d(np.uint16(0x0400)) == 2.0 ** -14         # smallest normal
+    assert d(np.uint16(0x7C00)) == np.inf
+    assert np.isnan(d(np.uint16(0x7E00)))
+
+
+def test_int4_codes_are_twos_complement():
+    codes = np.arange(16, dtype=np.uint8)
+    # sign extension by an arithmetic shift of the nibble placed in the top of a byte
+    ref = (codes << 4).astype(np.uint8).view(np.int8).astype(np.int64) >> 4
+    assert np.array_equal(oracle.decode_int4(codes), ref)
+    assert oracle.decode_int4(codes).tolist() == [0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1]
+
+
+def test_unpack_nibbles_order():
+    packed = np.array([[0x21, 0x43, 0xF5]], np.uint8)
+    assert oracle.unpack_nibbles(packed).tolist() == [[1, 2, 3, 4, 5, 15]]

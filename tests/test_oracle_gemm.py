@@ -206,3 +206,82 @@ def test_mxfp4_scale_blocks_are_32_wide():
     r = oracle.gemm_mxfp4(p, sa, p, sb)
     assert r[0, 0] == 32 + 32 * 8 + 32 + 32
     assert decode_e8m0(np.uint8(130)) == 8.0 and decode_e2m1(2) == 1.0
+
+
+def _frac_f16(bits):
+    bits = int(bits)
+    s = -1 if bits & 0x8000 else 1
+    e = (bits >> 10) & 0x1F
+    m = bits & 0x3FF
+    if e == 0:
+        return s * Fraction(m, 1024) * Fraction(2) ** (-14)
+    return s * (1 + Fraction(m, 1024)) * Fraction(2) ** (e - 15)
+
+
+def test_f16_bruteforce_including_subnormals():
+    rng = np.random.default_rng(11)
+    A = (rng.integers(0, 2 ** 16, size=(3, 7)).astype(np.uint16) & 0xBBFF)   # finite, |x| < 2^15
+    B = (rng.integers(0, 2 ** 16, size=(4, 7)).astype(np.uint16) & 0xBBFF)
+    A[0, :4] = [1, 2, 0x3FF, 0x8001]                                          # subnormals
+    ref = _brute(A, B, _frac_f16)
+    out = oracle.gemm_f16(A, B)
+    for m in range(3):
+        for n in range(4):
+            # every product is a multiple of 2^-48 below 2^31: the float64 sum of 7 is exact
+            assert Fraction(out[m, n]) == ref[m][n]
+
+
+def _int4_val(c):
+    c = int(c) & 0xF
+    return c - 16 if c >= 8 else c
+
+
+def test_w4a8_bruteforce():
+    rng = np.random.default_rng(12)
+    M, N, K = 3, 5, 12
+    A = rng.integers(-128, 128, size=(M, K), dtype=np.int8)
+    codes = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    sa = np.array([0.5, 0.25, 3.0], np.float32)
+    sb = np.array([1.0, 2.0, 0.125, 0.75, 4.0], np.float32)
+    out = oracle.gemm_w4a8(A, packed, sa, sb)
+    for m in range(M):
+        for n in range(N):
+            acc = sum(int(A[m, k]) * _int4_val(codes[n, k]) for k in range(K))
+            assert Fraction(out[m, n]) == acc * Fraction(float(sa[m])) * Fraction(float(sb[n]))
+
+
+def test_w4a8_closed_forms():
+    rng = np.random.default_rng(13)
+    K = 256
+    a = rng.integers(-127, 128, size=(6, K), dtype=np.int8)
+    ones = np.full((8, K // 2), 0x11, np.uint8)                    # every int4 = 1
+    r = oracle.gemm_w4a8(a, ones, np.ones(6, np.float32), np.ones(8, np.float32))
+    assert np.array_equal(r, np.repeat(a.astype(np.float64).sum(1, keepdims=True), 8, 1))
+    minus8 = np.full((2, K // 2), 0x88, np.uint8)                  # every int4 = -8
+    r = oracle.gemm_w4a8(np.ones((1, K), np.int8), minus8, np.ones(1, np.float32), np.ones(2, np.float32))
+    assert np.all(r == -8 * K)
+    # one-hot B at odd / even k selects the matching column of A
+    perm = rng.integers(0, K, size=16)
+    codes = np.zeros((16, K), np.uint8)
+    codes[np.arange(16), perm] = 1
+    b = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    r = oracle.gemm_w4a8(a, b, np.ones(6, np.float32), np.ones(16, np.float32))
+    assert np.array_equal(r, a[:, perm].astype(np.float64))
+
+
+def test_fp16_identity_b_returns_a():
+    rng = np.random.default_rng(14)
+    K = 64
+    a = rng.integers(0, 2 ** 16, size=(5, K)).astype(np.uint16) & 0xBBFF
+    eye = np.where(np.eye(K, dtype=bool), 0x3C00, 0).astype(np.uint16)
+    assert np.array_equal(oracle.gemm_f16(a, eye), oracle.decode_f16(a))
+
+
+def test_dispatch_new_types():
+    import workloads
+
+    h = workloads.make_inputs("w4a8", 16, 32, 128, 1)
+    assert np.array_equal(oracle.gemm("w4a8", h), oracle.gemm_w4a8(h["a"], h["b"], h["scale_a"], h["scale_b"]))
+    h = workloads.make_inputs("fp16", 16, 32, 128, 1)
+    assert np.array_equal(oracle.gemm("fp16", h), oracle.gemm_f16(h["a"], h["b"]))

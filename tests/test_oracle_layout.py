@@ -66,3 +66,47 @@ def test_bytes_not_elements():
     b = np.random.default_rng(2).integers(0, 2 ** 16, size=(16, 32), dtype=np.uint16)
     s = oracle.preshuffle(b.view(np.uint8))
     assert np.array_equal(oracle.unshuffle(s, 16, 64).view(np.uint16), b)
+
+
+def test_int4_piece_repack_positions():
+    """Element t of a 16-byte piece (32 INT4 values) lands in byte t % 16,
+    low nibble for t < 16, high nibble otherwise."""
+    rng = np.random.default_rng(5)
+    N, Kb = 16, 128
+    vals = rng.integers(0, 16, size=(N, 2 * Kb)).astype(np.uint8)     # element order
+    packed = (vals[:, 0::2] | (vals[:, 1::2] << 4)).astype(np.uint8)
+    r = oracle.repack_int4_pieces(packed)
+    for n in (0, 7, 15):
+        for k in (0, 1, 15, 16, 17, 31, 32, 100, 255):
+            piece, t = divmod(k, 32)
+            byte = r[n, piece * 16 + t % 16]
+            nib = (byte & 0xF) if t < 16 else (byte >> 4)
+            assert nib == vals[n, k], (n, k)
+
+
+def test_int4_layout_lane_view():
+    """In the INT4 preshuffled layout, lane (g, j) of the KiB block (n0, k0)
+    holds column 16 n0 + j: its low nibbles are K elements
+    128 k0 + 32 g + 0..15 and its high nibbles 128 k0 + 32 g + 16..31."""
+    rng = np.random.default_rng(6)
+    N, K = 32, 512
+    Kb = K // 2
+    vals = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    packed = (vals[:, 0::2] | (vals[:, 1::2] << 4)).astype(np.uint8)
+    bs = oracle.preshuffle_int4(packed)
+    for n0 in range(N // 16):
+        for k0 in range(Kb // 64):
+            blk = bs[(n0 * (Kb // 64) + k0) * 1024:][:1024].reshape(4, 16, 16)
+            for g in range(4):
+                for j in range(16):
+                    lane = blk[g, j]
+                    k = 128 * k0 + 32 * g
+                    assert np.array_equal(lane & 0xF, vals[16 * n0 + j, k:k + 16])
+                    assert np.array_equal(lane >> 4, vals[16 * n0 + j, k + 16:k + 32])
+
+
+def test_int4_layout_round_trip():
+    rng = np.random.default_rng(7)
+    b = rng.integers(0, 256, size=(48, 192), dtype=np.uint8)
+    assert np.array_equal(oracle.unpack_int4_pieces(oracle.repack_int4_pieces(b)), b)
+    assert np.array_equal(oracle.unshuffle_int4(oracle.preshuffle_int4(b), 48, 192), b)

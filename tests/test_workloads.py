@@ -50,3 +50,26 @@ def test_config_table(name):
     dtype, M, N, K, seed, tile = workloads.CONFIGS[name]
     assert M % 16 == 0 and N % 16 == 0
     assert (K * workloads.elem_bytes(dtype)) % 64 == 0
+
+
+def test_w4a8_ranges():
+    x = workloads.make_inputs("w4a8", 16, 32, 256, 6)
+    assert x["a"].dtype == np.int8 and x["a"].shape == (16, 256)
+    assert np.all(np.abs(x["a"].astype(int)).max(1) == 127) and x["a"].min() >= -127
+    vb = oracle.decode_int4(oracle.unpack_nibbles(x["b"]))
+    assert x["b"].shape == (32, 128) and vb.shape == (32, 256)
+    assert np.all(np.abs(vb).max(1) >= 7) and vb.min() >= -8 and vb.max() <= 7
+    assert x["scale_a"].dtype == np.float32 and x["scale_b"].shape == (32,)
+
+
+def test_fp16_is_rounded_normal():
+    x = workloads.make_inputs("fp16", 16, 16, 512, 4)
+    v = oracle.decode_f16(x["a"])
+    assert 0.9 < v.std() < 1.1 and abs(v.mean()) < 0.1
+    assert np.array_equal(v, v.astype(np.float16).astype(np.float64))
+
+
+def test_bias_scale():
+    x = workloads.make_inputs("bf16", 16, 4096, 1024, 4, bias=True)
+    assert x["bias"].dtype == np.float32 and x["bias"].shape == (4096,)
+    assert 0.9 * 32 < x["bias"].std() < 1.1 * 32
