@@ -8,11 +8,16 @@ points have the names of the C ABI (include/gemm_preshuffle.h):
     gemm_a8w8(a, b_shuf, scale_a, scale_b, ...)      -> C int32 (INT8) or bf16 (FP8)
     gemm_bf16(a, b_shuf, ...)                        -> C bf16
     gemm_mxfp4(a, scale_a, b_shuf, scale_b, ...)     -> C bf16
+    gemm_f16(a, b_shuf, ...)                         -> C fp16
+    gemm_w4a8(a, b_shuf, scale_a, scale_b, ...)      -> C bf16 (int8 A, INT4 B)
+    gemm_ex(dtype, a, b_shuf, ..., bias, act)        -> any type with the fused
+                                                        bias / activation epilogue
     gemm_plan(dtype, M, N, K, opts)                  -> dict (host-only planner query)
 
-Tensors: A is [M, K] (INT8 / FP8 as any 1-byte dtype, BF16 as bfloat16 or a
-2-byte integer view, MXFP4 as uint8 [M, K/2]); B before the shuffle is
-[N, K] the same way. If the library has not been built the first call raises
+Tensors: A is [M, K] (INT8 / FP8 as any 1-byte dtype, BF16 / FP16 as
+bfloat16 / float16 or a 2-byte integer view, MXFP4 as uint8 [M, K/2]; W4A8:
+int8 [M, K]); B before the shuffle is [N, K] the same way (W4A8: packed INT4
+uint8 [N, K/2]). If the library has not been built the first call raises
 GemmLibraryMissing: there is no fallback of any kind.
 """
 from __future__ import annotations
@@ -23,7 +28,8 @@ import re
 
 __all__ = [
     "GemmError", "GemmLibraryMissing", "GemmOpts", "lib_path", "load_library",
-    "gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_plan",
+    "gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_f16", "gemm_w4a8", "gemm_ex",
+    "gemm_plan", "ACTS",
     "gemm_status_string", "source_hash", "DTYPES", "EPI_DIRECT", "EPI_CSHUFFLE", "KERNEL_TILE", "KERNEL_SPLITK",
     "KERNEL_WIDE",
 ]
@@ -32,9 +38,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libgemm_preshuffle.so"
 
 # gp_dtype values of the C ABI
-GP_I8, GP_FP8_E4M3, GP_BF16, GP_FP4_E2M1, GP_I32 = 0, 1, 2, 3, 4
-DTYPES = {"int8": GP_I8, "fp8": GP_FP8_E4M3, "bf16": GP_BF16, "mxfp4": GP_FP4_E2M1}
-_ELEM_BITS = {GP_I8: 8, GP_FP8_E4M3: 8, GP_BF16: 16, GP_FP4_E2M1: 4}
+GP_I8, GP_FP8_E4M3, GP_BF16, GP_FP4_E2M1, GP_I32, GP_F16, GP_I4 = 0, 1, 2, 3, 4, 5, 6
+DTYPES = {"int8": GP_I8, "fp8": GP_FP8_E4M3, "bf16": GP_BF16, "mxfp4": GP_FP4_E2M1,
+          "fp16": GP_F16, "w4a8": GP_I4}
+_ELEM_BITS = {GP_I8: 8, GP_FP8_E4M3: 8, GP_BF16: 16, GP_FP4_E2M1: 4, GP_F16: 16, GP_I4: 4}   # of B
+_OUT = {GP_I8: GP_I32, GP_FP8_E4M3: GP_BF16, GP_BF16: GP_BF16, GP_FP4_E2M1: GP_BF16, GP_F16: GP_F16,
+        GP_I4: GP_BF16}
+# gp_act values of the C ABI
+ACTS = {"none": 0, "relu": 1, "silu": 2, "gelu": 3}
 EPI_AUTO, EPI_DIRECT, EPI_CSHUFFLE = 0, 1, 2
 KERNEL_AUTO, KERNEL_TILE, KERNEL_SPLITK, KERNEL_WIDE = 0, 1, 2, 3
 
@@ -87,10 +98,14 @@ def load_library():
     lib.gemm_a8w8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, ctypes.POINTER(GemmOpts), vp]
     lib.gemm_bf16.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.POINTER(GemmOpts), vp]
     lib.gemm_mxfp4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.POINTER(GemmOpts), vp]
+    lib.gemm_f16.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.POINTER(GemmOpts), vp]
+    lib.gemm_w4a8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.POINTER(GemmOpts), vp]
+    lib.gemm_ex.argtypes = [ci, ci, vp, vp, vp, vp, vp, ci, vp, i64, i64, i64, ctypes.POINTER(GemmOpts), vp]
     lib.gemm_plan.argtypes = [ci, i64, i64, i64, ctypes.POINTER(GemmOpts), ctypes.POINTER(GemmPlanInfo)]
     lib.gemm_status_string.argtypes = [ci]
     lib.gemm_status_string.restype = ctypes.c_char_p
-    for f in ("gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_plan"):
+    for f in ("gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_f16", "gemm_w4a8", "gemm_ex",
+              "gemm_plan"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -225,4 +240,52 @@ def gemm_mxfp4(a, scale_a, b_shuf, scale_b, c=None, N=None, opts=None, stream=No
         c = torch.empty(M, N, dtype=torch.bfloat16, device=a.device)
     _check(load_library().gemm_mxfp4(_ptr(a), _ptr(scale_a), _ptr(b_shuf), _ptr(scale_b), _ptr(c),
                                      M, N, K, _opts(opts), _stream(stream)), "gemm_mxfp4")
+    return c
+
+
+def gemm_f16(a, b_shuf, c=None, N=None, opts=None, stream=None):
+    """FP16 GEMM, fp16 output."""
+    import torch
+
+    M, K = a.shape[0], a.shape[1]
+    if N is None:
+        N = b_shuf.numel() * b_shuf.element_size() // (2 * K)
+    if c is None:
+        c = torch.empty(M, N, dtype=torch.float16, device=a.device)
+    _check(load_library().gemm_f16(_ptr(a), _ptr(b_shuf), _ptr(c), M, N, K, _opts(opts), _stream(stream)),
+           "gemm_f16")
+    return c
+
+
+def gemm_w4a8(a, b_shuf, scale_a, scale_b, c=None, N=None, opts=None, stream=None):
+    """int8 A [M, K] x INT4 B (preshuffled as GP_I4), fp32 scales, bf16 output."""
+    import torch
+
+    M, K = a.shape[0], _row_bytes(a)
+    if N is None:
+        N = b_shuf.numel() * b_shuf.element_size() * 2 // K
+    if c is None:
+        c = torch.empty(M, N, dtype=torch.bfloat16, device=a.device)
+    _check(load_library().gemm_w4a8(_ptr(a), _ptr(b_shuf), _ptr(scale_a), _ptr(scale_b), _ptr(c),
+                                    M, N, K, _opts(opts), _stream(stream)), "gemm_w4a8")
+    return c
+
+
+def gemm_ex(dtype, a, b_shuf, scale_a=None, scale_b=None, bias=None, act="none", c=None, N=None,
+            opts=None, stream=None):
+    """Any input type with the fused epilogue: C = act(scaled accumulator + bias[n])."""
+    import torch
+
+    dt = _dt(dtype)
+    out_dt = _OUT[dt]
+    M = a.shape[0]
+    K = _row_bytes(a) * 8 // (8 if dt == GP_I4 else _ELEM_BITS[dt])
+    if N is None:
+        N = b_shuf.numel() * b_shuf.element_size() * 8 // (K * _ELEM_BITS[dt])
+    if c is None:
+        tdt = {GP_I32: torch.int32, GP_BF16: torch.bfloat16, GP_F16: torch.float16}[out_dt]
+        c = torch.empty(M, N, dtype=tdt, device=a.device)
+    a_ = ACTS[act] if isinstance(act, str) else int(act)
+    _check(load_library().gemm_ex(dt, out_dt, _ptr(a), _ptr(b_shuf), _ptr(scale_a), _ptr(scale_b), _ptr(bias),
+                                  a_, _ptr(c), M, N, K, _opts(opts), _stream(stream)), "gemm_ex")
     return c

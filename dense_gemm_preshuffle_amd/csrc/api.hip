@@ -15,15 +15,19 @@ namespace {
 
 constexpr int64_t kMaxBytes = (int64_t)1 << 31;  // 32-bit buffer offsets
 
+// Bits per element of B (and of A, except W4A8 whose A is int8).
 int elem_bits(int dt) {
   switch (dt) {
     case GP_I8:
     case GP_FP8_E4M3: return 8;
-    case GP_BF16: return 16;
-    case GP_FP4_E2M1: return 4;
+    case GP_BF16:
+    case GP_F16: return 16;
+    case GP_FP4_E2M1:
+    case GP_I4: return 4;
     default: return 0;
   }
 }
+int a_bits(int dt) { return dt == GP_I4 ? 8 : elem_bits(dt); }
 
 // Kernel-side dtype tag of an input gp_dtype.
 int kdt(int dt) {
@@ -31,6 +35,8 @@ int kdt(int dt) {
     case GP_I8: return DT_I8;
     case GP_FP8_E4M3: return DT_FP8;
     case GP_BF16: return DT_BF16;
+    case GP_F16: return DT_F16;
+    case GP_I4: return DT_I4;
     default: return DT_FP4;
   }
 }
@@ -84,8 +90,9 @@ struct Plan {
   int64_t Kb = 0;
 };
 
-// K bytes one MFMA consumes (per MS x MS block)
-int kernel_mfma_kb(int dt, int ms) { return ms == 32 ? 32 : (dt == DT_FP8 ? 128 : 64); }
+// K bytes of B one MFMA consumes (per MS x MS block); a W4A8 piece of 64
+// B bytes feeds two int8 MFMAs
+int kernel_mfma_kb(int dt, int ms) { return ms == 32 ? 32 : (dt == DT_FP8 ? 128 : dt == DT_I4 ? 32 : 64); }
 
 // MFMA block for a tile: the caller's, else 32x32 for FP4 (measured faster
 // on the MXFP4 4096x4096x8192 shape), else 16x16 where compiled. (BF16
@@ -109,8 +116,8 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
                             {64, 64, 128}, {32, 64, 128}, {16, 64, 256}};
   static const Cand fp8[] = {{128, 256, 128}, {64, 256, 128}, {32, 256, 256}, {32, 256, 128},
                              {128, 128, 128}, {64, 128, 128}, {16, 64, 512}};
-  static const Cand bf16[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {64, 128, 128},
-                              {128, 256, 64}};
+  static const Cand b16[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {64, 128, 128},
+                             {128, 256, 64}, {32, 128, 128}};
   static const Cand fp4[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {32, 256, 128},
                              {64, 128, 128}};
   const Cand* list;
@@ -118,27 +125,36 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
   switch (dt) {
     case DT_I8: list = i8; n = sizeof(i8) / sizeof(Cand); break;
     case DT_FP8: list = fp8; n = sizeof(fp8) / sizeof(Cand); break;
-    case DT_BF16: list = bf16; n = sizeof(bf16) / sizeof(Cand); break;
+    case DT_BF16:
+    case DT_F16: list = b16; n = sizeof(b16) / sizeof(Cand); break;
     default: list = fp4; n = sizeof(fp4) / sizeof(Cand); break;
   }
   // First choice: the largest tile that still gives >= 256 workgroups (one
-  // per CU); otherwise the dividing tile with the most workgroups.
-  int best = -1;
-  int64_t best_grid = -1;
-  for (int i = 0; i < n; ++i) {
-    const Cand& c = list[i];
-    if (M % c.tm || N % c.tn || Kb % c.tkb) continue;
-    if (!pick_ms(dt, c.tm, c.tn, c.tkb, want_ms)) continue;
-    const int64_t g = (M / c.tm) * (N / c.tn);
-    if (g >= 256) { best = i; break; }
-    if (g > best_grid) { best_grid = g; best = i; }
+  // per CU); otherwise the tile with the most workgroups. Tiles that divide M
+  // and N are preferred; if none does, edge tiles overlap their neighbours
+  // (the tile must still fit inside M x N).
+  for (int pass = 0; pass < 2; ++pass) {
+    int best = -1;
+    int64_t best_grid = -1;
+    for (int i = 0; i < n; ++i) {
+      const Cand& c = list[i];
+      if (c.tm > M || c.tn > N || Kb % c.tkb) continue;
+      const bool exact = M % c.tm == 0 && N % c.tn == 0;
+      if (exact != (pass == 0)) continue;
+      if (!pick_ms(dt, c.tm, c.tn, c.tkb, want_ms)) continue;
+      const int64_t g = ((M + c.tm - 1) / c.tm) * ((N + c.tn - 1) / c.tn);
+      if (g >= 256) { best = i; break; }
+      if (g > best_grid) { best_grid = g; best = i; }
+    }
+    if (best >= 0) {
+      p->tm = list[best].tm;
+      p->tn = list[best].tn;
+      p->tkb = list[best].tkb;
+      p->ms = pick_ms(dt, p->tm, p->tn, p->tkb, want_ms);
+      return GP_OK;
+    }
   }
-  if (best < 0) return GP_ESHAPE;
-  p->tm = list[best].tm;
-  p->tn = list[best].tn;
-  p->tkb = list[best].tkb;
-  p->ms = pick_ms(dt, p->tm, p->tn, p->tkb, want_ms);
-  return GP_OK;
+  return GP_ESHAPE;
 }
 
 // Compiled split-K chunk for (dt, nb, waves) that divides the wave's K range:
@@ -161,7 +177,7 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
   if (o && o->tile_n > 0 && o->tile_n % 16) return GP_ESHAPE;
   if (o && o->tile_m > 0 && o->tile_m != 16) return GP_ESHAPE;
   if (o && o->tile_k > 0 && ((int64_t)o->tile_k * bits) % 8) return GP_ESHAPE;
-  if (Kb % waves || M % 16) return GP_ESHAPE;
+  if (Kb % waves) return GP_ESHAPE;
   const int64_t kw = Kb / waves;
   const int user_kch = (o && o->tile_k > 0) ? (int)((int64_t)o->tile_k * bits / 8) : 0;
   // column blocks per workgroup: the caller's, else 2 (two blocks fill whole
@@ -189,7 +205,7 @@ int choose_wide(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, con
   if (o && ((o->tile_m && o->tile_m != 256) || (o->tile_n && o->tile_n != 256))) return GP_ESHAPE;
   if (o && o->waves && o->waves != 8) return GP_ESHAPE;
   if (o && o->pipeline == 1) return GP_ESHAPE;   // both operands always go by LDS DMA
-  if (M % 256 || N % 256) return GP_ESHAPE;
+  if (M < 256 || N < 256) return GP_ESHAPE;   // edge tiles overlap inside M x N
   const int ms = (o && o->mfma) ? o->mfma : 16;
   int want_tkb = 0;
   if (o && o->tile_k) {
@@ -228,13 +244,17 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   }
   if ((K * bits) % 8) return GP_ESHAPE;
   const int64_t Kb = K * bits / 8;
-  if (N % 16 || Kb % 64 || M % 16) return GP_ESHAPE;
-  if (in_dtype == GP_FP4_E2M1 && K % 128) return GP_ESHAPE;
+  const int64_t Ka = K * a_bits(in_dtype) / 8;
+  if (N % 16 || Kb % 64) return GP_ESHAPE;
+  if ((in_dtype == GP_FP4_E2M1 || in_dtype == GP_I4) && K % 128) return GP_ESHAPE;
+  // W4A8 accumulates 16 x the products in int32 (|a| <= 128, |b| <= 8)
+  if (in_dtype == GP_I4 && K > 65536) return GP_ESHAPE;
   const int ob = in_dtype == GP_I8 ? 4 : 2;
-  if (M * Kb >= kMaxBytes || N * Kb >= kMaxBytes || M * N * ob >= kMaxBytes) return GP_ESHAPE;
+  if (M * Ka >= kMaxBytes || N * Kb >= kMaxBytes || M * N * ob >= kMaxBytes) return GP_ESHAPE;
   const int dt = kdt(in_dtype);
   p->Kb = Kb;
-  p->kernel = (o && o->kernel) ? o->kernel : (M <= 32 ? GP_KERNEL_SPLITK : GP_KERNEL_TILE);
+  p->kernel = (o && o->kernel) ? o->kernel : (M <= 32 || dt == DT_I4 ? GP_KERNEL_SPLITK : GP_KERNEL_TILE);
+  if (dt == DT_I4 && p->kernel != GP_KERNEL_SPLITK) return GP_EDTYPE;   // W4A8 runs on the small-M kernel
   if (p->kernel == GP_KERNEL_SPLITK) return choose_split(dt, bits, M, N, Kb, p, o);
   if (p->kernel == GP_KERNEL_WIDE) return choose_wide(dt, bits, M, N, Kb, p, o);
 
@@ -249,10 +269,15 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     if (!p->ms) return GP_ESHAPE;
     p->pipe = pick_pipe(dt, p->ms, p->tm, p->tn, p->tkb, o->pipeline);
     if (p->pipe < 0) return GP_ESHAPE;
-    if (M % p->tm || N % p->tn || Kb % p->tkb) return GP_ESHAPE;
+    if (M < p->tm || N < p->tn || Kb % p->tkb) return GP_ESHAPE;
   } else {
-    const int r = choose_tile(dt, M, N, Kb, p, o ? o->mfma : 0);
-    if (r) return r;
+    int r = choose_tile(dt, M, N, Kb, p, o ? o->mfma : 0);
+    if (r) {
+      // no tile fits inside M x N: the small-M kernel takes any M
+      if (o && o->kernel == GP_KERNEL_TILE) return r;
+      p->kernel = GP_KERNEL_SPLITK;
+      return choose_split(dt, bits, M, N, Kb, p, o);
+    }
     p->pipe = pick_pipe(dt, p->ms, p->tm, p->tn, p->tkb, o ? o->pipeline : 0);
     if (p->pipe < 0) return GP_ESHAPE;
   }
@@ -263,7 +288,6 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     // tile fits the share of the 160 KiB LDS each resident workgroup gets
     // (two per CU, or one for tiles whose accumulators fill half the
     // registers); direct stores otherwise
-    const int ob = in_dtype == GP_I8 ? 4 : 2;
     const int cbytes = p->tm * (p->tn * ob + 16);
     const int wgs_per_cu = (p->tm * p->tn / 256 > 128) ? 1 : 2;
     p->epi = (p->tn >= 128 && cbytes <= 160 * 1024 / wgs_per_cu) ? EPI_CSHUFFLE : EPI_DIRECT;
@@ -278,11 +302,11 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
   const int dt = kdt(in_dtype);
   const int ms = p.kernel != GP_KERNEL_SPLITK ? p.ms : 16;
   const int kbm = kernel_mfma_kb(dt, ms);
-  const int64_t kinstr = (int64_t)kbm * 8 / bits;   // K elements per MFMA
+  const int ob = in_dtype == GP_I8 ? 4 : 2;
+  const int bias_lds = dt == DT_I8 ? 0 : 1;   // the fused-epilogue bias is staged in LDS
   out->kernel = p.kernel;
   out->mfma = ms;
   out->pipeline = p.kernel != GP_KERNEL_SPLITK ? (p.pipe ? p.pipe : 1) : 0;
-  out->mfma_total = (M / ms) * (N / ms) * (K / kinstr);
   out->xcd_swizzle = p.kernel != GP_KERNEL_SPLITK ? p.xcd : 2;
   if (p.kernel == GP_KERNEL_WIDE) {
     out->tile_m = out->tile_n = 256;
@@ -292,8 +316,8 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     out->threads = 512;
     const int stages = p.pipe * 512 * p.tkb;                 // A and B tiles per stage
     const int cbytes = p.epi == EPI_CSHUFFLE ? 256 * (256 * 2 + 16) : 0;
-    out->lds_bytes = (stages > cbytes ? stages : cbytes) + (dt == DT_FP8 ? 512 * 4 : 0);
-    out->grid = (M / 256) * (N / 256);
+    out->lds_bytes = (stages > cbytes ? stages : cbytes) + (dt == DT_FP8 ? 512 * 4 : 0) + bias_lds * 256 * 4;
+    out->grid = ((M + 255) / 256) * ((N + 255) / 256);
     out->k_tiles = p.Kb / p.tkb;
     out->mfma_per_wave_tile = (int64_t)(p.tkb / kbm) * (128 / ms) * (64 / ms);
   } else if (p.kernel == GP_KERNEL_TILE) {
@@ -303,7 +327,6 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     out->epilogue = p.epi;
     out->waves = 4;
     out->threads = 256;
-    const int ob = in_dtype == GP_I8 ? 4 : 2;
     const bool apart = (p.tm * (p.tkb / 16)) % 256 != 0;
     const int stages = p.pipe ? p.pipe : 2;
     int abuf = stages * (p.tm * p.tkb + (apart ? 16 : 0));
@@ -311,7 +334,8 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     const int cbytes = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
     out->lds_bytes = abuf > cbytes ? abuf : cbytes;
     if (dt == DT_FP8) out->lds_bytes += 256 * ((p.tm + 63) / 64 + p.tn / 64);  // FP8 scales
-    out->grid = (M / p.tm) * (N / p.tn);
+    out->lds_bytes += bias_lds * p.tn * 4;
+    out->grid = ((M + p.tm - 1) / p.tm) * ((N + p.tn - 1) / p.tn);
     out->k_tiles = p.Kb / p.tkb;
     out->mfma_per_wave_tile = (int64_t)(p.tkb / kbm) * (p.tm / ms) * (p.tn / 4 / ms);
   } else {
@@ -322,10 +346,13 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     out->waves = p.waves;
     out->threads = 64 * p.waves;
     out->lds_bytes = p.waves * p.nb * 64 * 16;
-    out->grid = (N / (16 * p.nb)) * (M / 16);
+    out->grid = (N / (16 * p.nb)) * ((M + 15) / 16);
     out->k_tiles = p.Kb / p.waves / p.kch;
     out->mfma_per_wave_tile = (int64_t)(p.kch / kbm) * p.nb;
   }
+  // MFMAs the launch issues (the algorithmic (M/ms)(N/ms)(K/K_instr) when
+  // the tile divides M and N; edge tiles and partial row blocks add to it)
+  out->mfma_total = out->grid * out->waves * out->k_tiles * out->mfma_per_wave_tile;
 }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -348,7 +375,7 @@ int check_device() {
 }
 
 int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void* sa, const void* sb,
-           void* c, int64_t M, int64_t N, hipStream_t s) {
+           const float* bias, int act, void* c, int64_t M, int64_t N, hipStream_t s) {
   const int dt = kdt(in_dtype);
   hipError_t e;
   if (p.kernel == GP_KERNEL_TILE || p.kernel == GP_KERNEL_WIDE) {
@@ -357,25 +384,31 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
     t.b = (const char*)b;
     t.sa = sa;
     t.sb = sb;
+    t.bias = bias;
     t.c = (char*)c;
     t.M = (uint32_t)M;
     t.N = (uint32_t)N;
     t.Kb = (uint32_t)p.Kb;
-    t.tiles_m = (uint32_t)(M / p.tm);
-    t.tiles_n = (uint32_t)(N / p.tn);
+    t.tiles_m = (uint32_t)((M + p.tm - 1) / p.tm);
+    t.tiles_n = (uint32_t)((N + p.tn - 1) / p.tn);
     t.xcd = p.xcd == 1 ? 1u : 0u;
+    t.act = act;
+    const bool fused = bias != nullptr || act != GP_ACT_NONE;
     if (p.kernel == GP_KERNEL_WIDE) {
       switch (dt) {
-        case DT_I8: e = launch_wide_i8(p.ms, p.tkb, p.pipe, t, s); break;
-        case DT_FP8: e = launch_wide_fp8(p.ms, p.tkb, p.pipe, t, s); break;
-        case DT_BF16: e = launch_wide_bf16(p.ms, p.tkb, p.pipe, t, s); break;
+        case DT_I8: e = launch_wide_i8(p.ms, p.tkb, p.pipe, false, t, s); break;
+        case DT_FP8: e = launch_wide_fp8(p.ms, p.tkb, p.pipe, fused, t, s); break;
+        case DT_BF16: e = launch_wide_bf16(p.ms, p.tkb, p.pipe, fused, t, s); break;
+        case DT_F16: e = launch_wide_f16(p.ms, p.tkb, p.pipe, fused, t, s); break;
         default: e = hipErrorInvalidValue; break;
       }
     } else switch (dt) {
-      case DT_I8: e = launch_tile_i8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;
-      case DT_FP8: e = launch_tile_fp8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;
-      case DT_BF16: e = launch_tile_bf16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;
-      default: e = launch_tile_fp4(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, t, s); break;
+      case DT_I8: e = launch_tile_i8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, false, t, s); break;
+      case DT_FP8: e = launch_tile_fp8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, fused, t, s); break;
+      case DT_BF16: e = launch_tile_bf16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, fused, t, s); break;
+      case DT_F16: e = launch_tile_f16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, fused, t, s); break;
+      case DT_FP4: e = launch_tile_fp4(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, fused, t, s); break;
+      default: e = hipErrorInvalidValue; break;
     }
   } else {
     SplitArgs t;
@@ -383,14 +416,18 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
     t.b = (const char*)b;
     t.sa = sa;
     t.sb = sb;
+    t.bias = bias;
     t.c = (char*)c;
     t.M = (uint32_t)M;
     t.N = (uint32_t)N;
     t.Kb = (uint32_t)p.Kb;
+    t.act = act;
     switch (dt) {
       case DT_I8: e = launch_splitk_i8(p.nb, p.waves, p.kch, t, s); break;
       case DT_FP8: e = launch_splitk_fp8(p.nb, p.waves, p.kch, t, s); break;
       case DT_BF16: e = launch_splitk_bf16(p.nb, p.waves, p.kch, t, s); break;
+      case DT_F16: e = launch_splitk_f16(p.nb, p.waves, p.kch, t, s); break;
+      case DT_I4: e = launch_splitk_i4(p.nb, p.waves, p.kch, t, s); break;
       default: e = launch_splitk_fp4(p.nb, p.waves, p.kch, t, s); break;
     }
   }
@@ -398,9 +435,11 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
 }
 
 // B preshuffle: one thread per destination 16-byte chunk (writes coalesced;
-// a wave reads 16 rows x 64 contiguous bytes).
+// a wave reads 16 rows x 64 contiguous bytes). For INT4 weights the nibbles
+// of each 16-byte piece are also reordered: element t of the piece's 32 goes
+// to byte t % 16, low nibble for t < 16, high nibble otherwise.
 __global__ __launch_bounds__(256) void preshuffle_kernel(const char* __restrict__ b, char* __restrict__ bs,
-                                                         uint32_t kb64, uint32_t Kb, uint32_t chunks) {
+                                                         uint32_t kb64, uint32_t Kb, uint32_t chunks, int int4) {
   const uint32_t q = blockIdx.x * 256u + threadIdx.x;
   if (q >= chunks) return;
   const uint32_t j = q & 15u;
@@ -409,7 +448,61 @@ __global__ __launch_bounds__(256) void preshuffle_kernel(const char* __restrict_
   const uint32_t k0 = t % kb64;
   const uint32_t n0 = t / kb64;
   const size_t src = (size_t)(16u * n0 + j) * Kb + 64u * k0 + 16u * g;
-  *(v4i*)(bs + (size_t)q * 16u) = *(const v4i*)(b + src);
+  v4i v = *(const v4i*)(b + src);
+  if (int4) {
+    // source byte i holds elements 2i (low nibble) and 2i+1 (high nibble)
+    v4i o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int e_lo = 4 * d + bb, e_hi = 16 + 4 * d + bb;   // elements of output byte 4d + bb
+        const uint32_t lo = ((uint32_t)v[e_lo >> 3] >> (4 * (e_lo & 7))) & 0xFu;
+        const uint32_t hi = ((uint32_t)v[e_hi >> 3] >> (4 * (e_hi & 7))) & 0xFu;
+        w |= (lo | (hi << 4)) << (8 * bb);
+      }
+      o[d] = (int)w;
+    }
+    v = o;
+  }
+  *(v4i*)(bs + (size_t)q * 16u) = v;
+}
+
+// Every GEMM entry point lands here: validation (pointers, dtype pair,
+// scales, epilogue), the plan, the device check, the launch.
+int run_gemm(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
+             const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
+             const gemm_opts* opts, void* stream) {
+  if (!a || !b_shuf || !c || !aligned16(a) || !aligned16(b_shuf) || !aligned16(c)) return GP_EINVAL;
+  if (act < GP_ACT_NONE || act > GP_ACT_GELU) return GP_EINVAL;
+  if (bias && !aligned16(bias)) return GP_EINVAL;
+  bool scales;   // the type takes (required) scale vectors
+  switch (in_dtype) {
+    case GP_I8:
+      // exact int32 result: no scales and no fused epilogue
+      if (out_dtype != GP_I32 || bias || act != GP_ACT_NONE) return GP_EDTYPE;
+      scales = false;
+      break;
+    case GP_FP8_E4M3:
+    case GP_FP4_E2M1:
+    case GP_I4: if (out_dtype != GP_BF16) return GP_EDTYPE; scales = true; break;
+    case GP_BF16: if (out_dtype != GP_BF16) return GP_EDTYPE; scales = false; break;
+    case GP_F16: if (out_dtype != GP_F16) return GP_EDTYPE; scales = false; break;
+    default: return GP_EDTYPE;
+  }
+  if (scales) {
+    if (!scale_a || !scale_b) return GP_EDTYPE;
+    if (!aligned16(scale_a) || !aligned16(scale_b)) return GP_EINVAL;
+  } else if (scale_a || scale_b) {
+    return GP_EDTYPE;
+  }
+  Plan p;
+  int r = make_plan(in_dtype, M, N, K, opts, &p);
+  if (r) return r;
+  r = check_device();
+  if (r) return r;
+  return launch(in_dtype, p, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -455,52 +548,44 @@ int gemm_preshuffle_b(const void* b, void* b_shuf, int64_t N, int64_t K, int dty
   if (r) return r;
   const uint32_t chunks = (uint32_t)(N * Kb / 16);
   hipLaunchKernelGGL(preshuffle_kernel, dim3((chunks + 255) / 256), dim3(256), 0, (hipStream_t)stream,
-                     (const char*)b, (char*)b_shuf, (uint32_t)(Kb / 64), (uint32_t)Kb, chunks);
+                     (const char*)b, (char*)b_shuf, (uint32_t)(Kb / 64), (uint32_t)Kb, chunks,
+                     dtype == GP_I4 ? 1 : 0);
   return hipGetLastError() == hipSuccess ? GP_OK : GP_EHIP;
 }
 
 int gemm_a8w8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b, void* c,
               int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype, const gemm_opts* opts,
               void* stream) {
-  if (!a || !b_shuf || !c || !aligned16(a) || !aligned16(b_shuf) || !aligned16(c)) return GP_EINVAL;
-  if (in_dtype == GP_I8) {
-    if (out_dtype != GP_I32 || scale_a || scale_b) return GP_EDTYPE;
-  } else if (in_dtype == GP_FP8_E4M3) {
-    if (out_dtype != GP_BF16 || !scale_a || !scale_b) return GP_EDTYPE;
-    if (!aligned16(scale_a) || !aligned16(scale_b)) return GP_EINVAL;
-  } else {
-    return GP_EDTYPE;
-  }
-  Plan p;
-  int r = make_plan(in_dtype, M, N, K, opts, &p);
-  if (r) return r;
-  r = check_device();
-  if (r) return r;
-  return launch(in_dtype, p, a, b_shuf, scale_a, scale_b, c, M, N, (hipStream_t)stream);
+  if (in_dtype != GP_I8 && in_dtype != GP_FP8_E4M3) return GP_EDTYPE;
+  return run_gemm(in_dtype, out_dtype, a, b_shuf, scale_a, scale_b, nullptr, GP_ACT_NONE, c, M, N, K, opts, stream);
 }
 
 int gemm_bf16(const void* a, const void* b_shuf, void* c, int64_t M, int64_t N, int64_t K,
               const gemm_opts* opts, void* stream) {
-  if (!a || !b_shuf || !c || !aligned16(a) || !aligned16(b_shuf) || !aligned16(c)) return GP_EINVAL;
-  Plan p;
-  int r = make_plan(GP_BF16, M, N, K, opts, &p);
-  if (r) return r;
-  r = check_device();
-  if (r) return r;
-  return launch(GP_BF16, p, a, b_shuf, nullptr, nullptr, c, M, N, (hipStream_t)stream);
+  return run_gemm(GP_BF16, GP_BF16, a, b_shuf, nullptr, nullptr, nullptr, GP_ACT_NONE, c, M, N, K, opts, stream);
 }
 
 int gemm_mxfp4(const void* a, const uint8_t* scale_a, const void* b_shuf, const uint8_t* scale_b, void* c,
                int64_t M, int64_t N, int64_t K, const gemm_opts* opts, void* stream) {
-  if (!a || !b_shuf || !c || !scale_a || !scale_b) return GP_EINVAL;
-  if (!aligned16(a) || !aligned16(b_shuf) || !aligned16(c) || !aligned16(scale_a) || !aligned16(scale_b))
-    return GP_EINVAL;
-  Plan p;
-  int r = make_plan(GP_FP4_E2M1, M, N, K, opts, &p);
-  if (r) return r;
-  r = check_device();
-  if (r) return r;
-  return launch(GP_FP4_E2M1, p, a, b_shuf, scale_a, scale_b, c, M, N, (hipStream_t)stream);
+  if (!scale_a || !scale_b) return GP_EINVAL;
+  return run_gemm(GP_FP4_E2M1, GP_BF16, a, b_shuf, scale_a, scale_b, nullptr, GP_ACT_NONE, c, M, N, K, opts,
+                  stream);
+}
+
+int gemm_f16(const void* a, const void* b_shuf, void* c, int64_t M, int64_t N, int64_t K,
+             const gemm_opts* opts, void* stream) {
+  return run_gemm(GP_F16, GP_F16, a, b_shuf, nullptr, nullptr, nullptr, GP_ACT_NONE, c, M, N, K, opts, stream);
+}
+
+int gemm_w4a8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b, void* c,
+              int64_t M, int64_t N, int64_t K, const gemm_opts* opts, void* stream) {
+  return run_gemm(GP_I4, GP_BF16, a, b_shuf, scale_a, scale_b, nullptr, GP_ACT_NONE, c, M, N, K, opts, stream);
+}
+
+int gemm_ex(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
+            const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
+            const gemm_opts* opts, void* stream) {
+  return run_gemm(in_dtype, out_dtype, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, K, opts, stream);
 }
 
 }  // extern "C"

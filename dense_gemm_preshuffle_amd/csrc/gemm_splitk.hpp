@@ -9,13 +9,22 @@
 // loads for its whole K range up front (in chunks of KCH bytes, the next
 // chunk's loads issued before the current chunk's MFMAs), so that most of B
 // is in flight at once. Partial sums are reduced through LDS in a fixed order
-// (deterministic), then scaled, rounded and stored.
+// (deterministic), then scaled, biased, activated, rounded and stored.
 //
 // Operands come straight from global memory in MFMA layout: B from the
 // preshuffled layout (one KiB per 16 columns x 64 K bytes), A as 16 bytes per
 // lane (row lane%16, K piece lane/16), which is L2-resident since every
 // workgroup reads the same few rows. B is read exactly once, so its loads and
 // the C stores carry the non-temporal cache policy and leave L2 to A.
+//
+// M needs no particular multiple: the last 16-row block reads its missing
+// rows of A (and of the FP8 / W4A8 row scales, FP4 block scales) as zeros
+// through the bounds of its buffer resources and stores only its real rows.
+//
+// W4A8 (DT_I4): each 16-byte piece of the INT4 B layout holds K elements
+// 0..15 of the piece in its low nibbles and 16..31 in its high nibbles; it is
+// widened to two int8 operands (16 x the value, see widen_int4) and
+// multiplied with the matching two 16-byte pieces of the int8 A row.
 #pragma once
 
 #include <type_traits>
@@ -29,8 +38,10 @@ struct SplitArgs {
   const char* b;
   const void* sa;
   const void* sb;
+  const float* bias;  // fp32 [N] or null (fused epilogue)
   char* c;
-  uint32_t M, N, Kb;
+  uint32_t M, N, Kb;  // Kb = bytes per row of B (A rows are 2 Kb bytes for W4A8)
+  int act;            // Act
 };
 
 template <int DT, int NB, int WAVES, int KCH>
@@ -38,9 +49,12 @@ struct SplitCfg {
   static constexpr int THREADS = WAVES * 64;
   static constexpr int KB = Traits<DT>::KB;
   static constexpr int FRAG = Traits<DT>::FRAG;
-  static constexpr int STEPS = KCH / KB;              // MFMA K steps per chunk
+  static constexpr int STEPS = KCH / KB;              // B pieces (K steps) per chunk
+  static constexpr int AW = (DT == DT_I4) ? 2 : 1;    // A bytes per B byte
+  static constexpr int AFR = FRAG * AW;               // A pieces per lane per step
   static constexpr int OB = (DT == DT_I8) ? 4 : 2;
   static constexpr int NSC = (DT == DT_FP4) ? 1 : 0;
+  static constexpr bool FSC = DT == DT_FP8 || DT == DT_I4;   // fp32 row / column scales
   static constexpr int LDS = WAVES * NB * 64 * 16;    // partial accumulators
   static_assert(KCH % KB == 0, "chunk must be whole MFMA steps");
 };
@@ -60,6 +74,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
   const int lane_hi = lane >> 4;
 
   const uint32_t Kb = p.Kb;
+  const uint32_t Ka = Kb * C::AW;           // bytes per row of A
   // Column tiles go round-robin to the 8 XCDs; remap so that each XCD owns a
   // contiguous run of tiles. Neighbouring tiles then share whole 128-byte
   // lines of C inside one XCD's L2 instead of writing halves from two XCDs.
@@ -67,13 +82,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
   if (gridDim.x % 8u == 0) bx = (bx % 8u) * (gridDim.x / 8u) + bx / 8u;
   const uint32_t n0 = bx * (16 * NB);
   const uint32_t m0 = blockIdx.y * 16;
-  const uint32_t kw = Kb / WAVES;            // K bytes per wave
+  const uint32_t mrows = min(16u, p.M - m0);  // real rows of this block
+  const uint32_t kw = Kb / WAVES;            // B bytes per wave
   const uint32_t k_begin = wave * kw;
   const int chunks = (int)(kw / KCH);
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * Kb, 16 * Kb);
+  // A resource covers the block's real rows only; the row is always part of
+  // the per-lane offset, so a missing row reads zeros without a memory access.
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * Ka, mrows * Ka);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (size_t)n0 * Kb, 16 * NB * Kb);
-  const uint32_t a_off = lane_lo * Kb + lane_hi * 16;
+  // W4A8: the B piece of lane group g covers K elements [32g, 32g+32) of a
+  // 128-element block, i.e. A bytes 32g + 16h for its two halves h
+  const uint32_t a_off = lane_lo * Ka + lane_hi * 16 * C::AW;
   uint32_t b_off[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) b_off[nb] = nb * 16 * Kb + lane * 16;
@@ -81,25 +101,33 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
   const uint32_t srow = Kb / 16;
   __amdgpu_buffer_rsrc_t rsa = make_rsrc(nullptr, 0), rsb = make_rsrc(nullptr, 0);
   if constexpr (DT == DT_FP4) {
-    rsa = make_rsrc((const char*)p.sa + (size_t)m0 * srow, 16 * srow);
+    rsa = make_rsrc((const char*)p.sa + (size_t)m0 * srow, mrows * srow);
     rsb = make_rsrc((const char*)p.sb + (size_t)n0 * srow, 16 * NB * srow);
   }
 
-  // FP8 scales: issued before any operand load, so that the epilogue does not
-  // wait one more memory round trip for them. Wave w stores column block w
-  // (NB <= WAVES), so each wave needs its rows' and its block's scales only.
+  // Epilogue vectors (row / column scales, bias): issued before any operand
+  // load, so that the epilogue does not wait one more memory round trip for
+  // them. Wave w stores column block w (NB <= WAVES), so each wave needs its
+  // rows' scales and its block's column values only.
+  static_assert(NB <= WAVES, "one column block per wave in the epilogue");
+  const uint32_t nbw = (uint32_t)min(wave, NB - 1);
   float sa_v = 1.f;
   v4f sb_v = v4f{1.f, 1.f, 1.f, 1.f};
-  if constexpr (DT == DT_FP8) {
-    static_assert(NB <= WAVES, "one column block per wave in the epilogue");
-    const uint32_t nbw = (uint32_t)min(wave, NB - 1);
-    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc((const float*)p.sa + m0, 16 * 4);
+  if constexpr (C::FSC) {
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc((const float*)p.sa + m0, mrows * 4);
     const __amdgpu_buffer_rsrc_t rs_b = make_rsrc((const float*)p.sb + n0, 16 * NB * 4);
     sa_v = __builtin_bit_cast(float, buf_load4_early(rs_a, lane_lo * 4, 0));
     sb_v = __builtin_bit_cast(v4f, buf_load16_early(rs_b, (nbw * 16 + 4 * lane_hi) * 4, 0));
   }
+  // without a bias the resource is empty: the load returns zeros, no branch
+  v4f bias_v = v4f{0.f, 0.f, 0.f, 0.f};
+  if constexpr (DT != DT_I8) {
+    const bool has_bias = p.bias != nullptr;
+    const __amdgpu_buffer_rsrc_t rbias = make_rsrc(has_bias ? p.bias + n0 : p.bias, has_bias ? 16 * NB * 4 : 0);
+    bias_v = __builtin_bit_cast(v4f, buf_load16_early(rbias, (nbw * 16 + 4 * lane_hi) * 4, 0));
+  }
 
-  v4i af[2][C::STEPS][C::FRAG];
+  v4i af[2][C::STEPS][C::AFR];
   v4i bf[2][C::STEPS][NB][C::FRAG];
   int sa_r[2][C::STEPS * C::NSC + 1 - C::NSC];
   int sb_r[2][C::STEPS][NB * C::NSC + 1 - C::NSC];
@@ -109,12 +137,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
 
   auto load = [&](auto par_c, int ch) {
     constexpr int par = decltype(par_c)::value;
-    const uint32_t kb = k_begin + (uint32_t)ch * KCH;  // K byte of this chunk
+    const uint32_t kb = k_begin + (uint32_t)ch * KCH;  // B byte of this chunk
 #pragma unroll
     for (int s = 0; s < C::STEPS; ++s)
 #pragma unroll
-      for (int f = 0; f < C::FRAG; ++f)
-        af[par][s][f] = buf_load16(ra, a_off + s * C::KB + f * 64, kb);
+      for (int f = 0; f < C::AFR; ++f) {
+        if constexpr (DT == DT_I4) af[par][s][f] = buf_load16(ra, a_off + s * 128 + f * 16, kb * 2);
+        else af[par][s][f] = buf_load16(ra, a_off + s * C::KB + f * 64, kb);
+      }
     const uint32_t kblk = (kb / 64) * 1024u;
 #pragma unroll
     for (int s = 0; s < C::STEPS; ++s)
@@ -141,9 +171,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
       if constexpr (DT == DT_FP4) sy = sa_r[par][s] >> (8 * lane_hi);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        int sx = 0;
-        if constexpr (DT == DT_FP4) sx = sb_r[par][s][nb] >> (8 * lane_hi);
-        acc[nb] = mfma<DT>(bf[par][s][nb], af[par][s], acc[nb], sx, sy);
+        if constexpr (DT == DT_I4) {
+          v4i lo, hi;
+          widen_int4(bf[par][s][nb][0], lo, hi);
+          acc[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(lo, af[par][s][0], acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(hi, af[par][s][1], acc[nb], 0, 0, 0);
+        } else {
+          int sx = 0;
+          if constexpr (DT == DT_FP4) sx = sb_r[par][s][nb] >> (8 * lane_hi);
+          acc[nb] = mfma<DT>(bf[par][s][nb], af[par][s], acc[nb], sx, sy);
+        }
       }
     }
   };
@@ -164,27 +201,39 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
   for (int nb = 0; nb < NB; ++nb) red[(wave * NB + nb) * 64 + lane] = acc[nb];
   __syncthreads();
 
-  const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c + ((size_t)m0 * p.N + n0) * C::OB, (15 * p.N + 16 * NB) * C::OB);
-  for (int nb = wave; nb < NB; nb += WAVES) {
-    Acc v = red[nb * 64 + lane];
+  const __amdgpu_buffer_rsrc_t rc =
+      make_rsrc(p.c + ((size_t)m0 * p.N + n0) * C::OB, ((mrows - 1) * p.N + 16 * NB) * C::OB);
+  with_act(p.act, [&](auto act_c) {
+    constexpr int A = decltype(act_c)::value;
+    for (int nb = wave; nb < NB; nb += WAVES) {
+      Acc v = red[nb * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) v += red[(w * NB + nb) * 64 + lane];
-    // lane holds C[m0 + lane_lo][n0 + nb*16 + 4*lane_hi + r]
-    const uint32_t col = nb * 16 + 4 * lane_hi;
-    const uint32_t off = (lane_lo * p.N + col) * C::OB;
-    if constexpr (DT == DT_I8) {
-      buf_store16_nt(v, rc, off);
-    } else {
-      if constexpr (DT == DT_FP8) {
+      for (int w = 1; w < WAVES; ++w) v += red[(w * NB + nb) * 64 + lane];
+      // lane holds C[m0 + lane_lo][n0 + nb*16 + 4*lane_hi + r]; rows past M are
+      // not stored (offset outside the resource)
+      const uint32_t col = nb * 16 + 4 * lane_hi;
+      const uint32_t off = (uint32_t)lane_lo < mrows ? (lane_lo * p.N + col) * C::OB : 0x80000000u;
+      if constexpr (DT == DT_I8) {
+        buf_store16_nt(v, rc, off);
+      } else {
+        v4f x;
+        if constexpr (DT == DT_I4) {
+          // the widened products are 16 x the INT4 ones (exact multiples of 16)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (v[r] * sa_v) * sb_v[r];
+          for (int r = 0; r < 4; ++r) x[r] = (float)(v[r] >> 4);
+        } else {
+          x = v;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float y = x[r];
+          if constexpr (C::FSC) y = (y * sa_v) * sb_v[r];
+          x[r] = activate<A>(y + bias_v[r]);
+        }
+        buf_store8_nt(pack_out4<DT>(x), rc, off);
       }
-      v2i o;
-      o[0] = (int)pack_bf16x2(v[0], v[1]);
-      o[1] = (int)pack_bf16x2(v[2], v[3]);
-      buf_store8_nt(o, rc, off);
     }
-  }
+  });
 }
 
 }  // namespace gp

@@ -9,7 +9,12 @@
 //   * the next K tile's A and B loads are issued before the current tile's
 //     MFMAs (register double buffer for B, loop-carried, §4.1-§4.4); one
 //     barrier per K tile;
-//   * epilogue: direct store or CShuffle through LDS (§7).
+//   * epilogue: direct store or CShuffle through LDS (§7), with the fused
+//     bias and activation of Kernel Tuning Guide §6;
+//   * M and N need not be multiples of the tile: an edge tile is moved back
+//     to end at the last row / column (it overlaps its neighbour) and stores
+//     only the rows / columns its neighbour did not, so every load stays
+//     inside the operands and the K loop is the same for every tile.
 //
 // Differences from the pages' kernel, for gfx950:
 //   * MS x MS MFMA blocks with MS = 16 or 32 (see Mma<> in gp_common.hpp):
@@ -34,16 +39,32 @@ struct TileArgs {
   const char* b;      // preshuffled [N/16][Kb/64][4][16][16]
   const void* sa;     // FP8: fp32 [M]; FP4: u8 [M][Kb/16]; else unused
   const void* sb;     // FP8: fp32 [N]; FP4: u8 [N][Kb/16]; else unused
-  char* c;            // [M][N] int32 or bf16
+  const float* bias;  // fp32 [N] or null (fused epilogue; not INT8)
+  char* c;            // [M][N] int32, bf16 or fp16
   uint32_t M, N, Kb;  // Kb = bytes per row of A and B
-  uint32_t tiles_m, tiles_n;
+  uint32_t tiles_m, tiles_n;  // ceil(M / TM), ceil(N / TN)
   uint32_t xcd;       // 1: XCD-aware, grouped tile order
+  int act;            // Act
 };
+
+// Edge tiles: a tile that would run past M (or N) starts TM (TN) before the
+// end instead; `skip` rows (columns) at its start belong to the previous
+// tile and are not stored again.
+// Both results are wave-uniform; readfirstlane keeps them in scalar registers
+// (left alone, the compiler may pick a vector saturating subtract, and every
+// buffer resource built from x0 would then need a waterfall loop).
+__device__ __forceinline__ void edge_shift(uint32_t& x0, uint32_t& skip, uint32_t T, uint32_t X) {
+  const uint32_t s = x0 + T > X ? x0 + T - X : 0u;
+  skip = __builtin_amdgcn_readfirstlane(s);
+  x0 = __builtin_amdgcn_readfirstlane(x0 - s);
+}
 
 // PIPE: 0 = A staged through VGPRs, two LDS buffers (prefetch one tile
 // ahead); 2 .. 6 = A copied global -> LDS by the buffer-load LDS DMA, with
 // PIPE LDS buffers and B register sets (prefetch PIPE-1 tiles ahead).
-template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE>
+// FUSED: the variant with the fused bias / activation epilogue; without it
+// the epilogue carries no bias slot and no activation code.
+template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED = false>
 struct TileCfg {
   using S = Mma<DT, MS>;
   static constexpr int THREADS = 256;
@@ -82,10 +103,13 @@ struct TileCfg {
   // FP8 per-row / per-column scales, fetched into LDS by DMA when the kernel
   // starts (so the epilogue does not wait a memory round trip for them):
   // 256-byte blocks of A scales (TM floats, padded to 64) then B scales.
+  // The fused-epilogue bias (TN floats) follows them.
   static constexpr int NSA = (DT == DT_FP8) ? (TM + 63) / 64 : 0;
   static constexpr int NSB = (DT == DT_FP8) ? TN / 64 : 0;
+  static constexpr int NBI = (FUSED && DT != DT_I8) ? TN / 64 : 0;
   static constexpr int FSC_OFF = (STAGE > CBYTES) ? STAGE : CBYTES;
-  static constexpr int LDS = FSC_OFF + (NSA + NSB) * 256;
+  static constexpr int BIAS_OFF = FSC_OFF + (NSA + NSB) * 256;
+  static constexpr int LDS = BIAS_OFF + NBI * 256;
   // A fragments read ahead of their MFMAs: the most (2, 1 or 0) for which
   // the register estimate (accumulators unless they sit in AGPRs, B stages,
   // FP4 scales, the fragment ring) stays within 236 of the 256 VGPRs. FP8
@@ -127,11 +151,11 @@ __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uin
   }
 }
 
-template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE>
+template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED>
 // One workgroup per CU once the accumulators alone take more than half of the
 // 256 registers two workgroups would leave each wave; two otherwise.
 __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_kernel(TileArgs p) {
-  using C = TileCfg<DT, MS, TM, TN, TKB, EPI, PIPE>;
+  using C = TileCfg<DT, MS, TM, TN, TKB, EPI, PIPE, FUSED>;
   using Acc = typename Mma<DT, MS>::Acc;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
 
@@ -146,8 +170,9 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
 
   uint32_t tm, tn;
   tile_coords(p, tm, tn);
-  const uint32_t m0 = tm * TM;
-  const uint32_t n0 = tn * TN;
+  uint32_t m0 = tm * TM, n0 = tn * TN, mskip, nskip;
+  edge_shift(m0, mskip, TM, p.M);
+  edge_shift(n0, nskip, TN, p.N);
   const uint32_t Kb = p.Kb;
   const int KT = (int)(Kb / TKB);
 
@@ -225,8 +250,8 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
     rsb = make_rsrc((const char*)p.sb + (size_t)n0 * srow, TN * srow);
   }
 
-  // FP8 scales -> LDS, before any operand load: block i by wave i % WAVES,
-  // lane l carrying float l of the block (lanes past TM read zeros).
+  // FP8 scales and the bias -> LDS, before any operand load: block i by wave
+  // i % WAVES, lane l carrying float l of the block (lanes past TM read zeros).
   if constexpr (DT == DT_FP8) {
     const __amdgpu_buffer_rsrc_t rfa = make_rsrc((const float*)p.sa + m0, TM * 4);
     const __amdgpu_buffer_rsrc_t rfb = make_rsrc((const float*)p.sb + n0, TN * 4);
@@ -236,7 +261,22 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
       char* dst = lds + C::FSC_OFF + i * 256;
       const bool is_a = i < C::NSA;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rfa : rfb, (__attribute__((address_space(3))) void*)dst, 4,
-                                               lane * 4, (is_a ? i : i - C::NSA) * 256, 0, 0);
+                                               lane * 4 + (is_a ? i : i - C::NSA) * 256, 0, 0, 0);
+    }
+  }
+  // Without a bias its LDS slot holds zeros, so the epilogue adds it without
+  // a branch (written before the first barrier, read after the last).
+  if constexpr (C::NBI > 0) {
+#pragma unroll
+    for (int i = 0; i < C::NBI; ++i) {
+      if ((C::NSA + C::NSB + i) % C::WAVES != wave) continue;
+      if (p.bias) {
+        const __amdgpu_buffer_rsrc_t rbi = make_rsrc(p.bias + n0, TN * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbi, (__attribute__((address_space(3))) void*)(lds + C::BIAS_OFF + i * 256),
+                                                 4, lane * 4 + i * 256, 0, 0, 0);
+      } else {
+        *(float*)(lds + C::BIAS_OFF + i * 256 + lane * 4) = 0.f;
+      }
     }
   }
 
@@ -463,28 +503,43 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
   }
 
   // ---- epilogue ----
+  // Lane indices re-derived from an opaque copy of the thread index, so that
+  // no epilogue address is computed before (and kept live through) the K loop.
+  const int etid = opaque(tid);
+  const int elrow = etid & (MS - 1), elgrp = (etid & 63) / MS;
   // For every (mi, ni) the lane holds NREG/4 runs of 4 consecutive columns
-  // of row mi*MS + lrow: run h covers columns ni*MS + col_run(h) + 0..3.
-  auto col_run = [&](int h) -> int { return MS == 16 ? 4 * lgrp : 8 * h + 4 * lgrp; };
+  // of row mi*MS + elrow: run h covers columns ni*MS + col_run(h) + 0..3.
+  auto col_run = [&](int h) -> int { return MS == 16 ? 4 * elgrp : 8 * h + 4 * elgrp; };
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c + ((size_t)m0 * p.N + n0) * C::OB, ((TM - 1) * p.N + TN) * C::OB);
+  // C offset of tile row r, column c; rows / columns an edge tile shares with
+  // its neighbour get an offset outside the resource (the store is dropped)
+  auto c_off = [&](uint32_t r, uint32_t c) -> uint32_t {
+    return (r >= mskip && c >= nskip) ? (r * p.N + c) * C::OB : 0x80000000u;
+  };
+  // The scale and bias DMAs were each wave's first memory instructions, so
+  // they completed before the wave's wait for any later load (vmcnt counts in
+  // order): with DMA A the wait for zero above, with A through VGPRs the wait
+  // for the last tile's A. Every wave passed a barrier after that wait.
   v4f sbv[C::NACC][C::NREG / 4];
   float sav[C::MREP];
   if constexpr (DT == DT_FP8) {
-    // The scale DMA was each wave's first memory instruction, so it completed
-    // before the wave's wait for any later load (vmcnt counts in order): with
-    // DMA A the wait for zero above, with A through VGPRs the wait for the
-    // last tile's A. Every wave passed a barrier after that wait.
     const float* sa = (const float*)(lds + C::FSC_OFF);
     const float* sb = sa + C::NSA * 64;
 #pragma unroll
-    for (int mi = 0; mi < C::MREP; ++mi) sav[mi] = sa[mi * MS + lrow];
+    for (int mi = 0; mi < C::MREP; ++mi) sav[mi] = sa[mi * MS + elrow];
 #pragma unroll
     for (int ni = 0; ni < C::NACC; ++ni)
 #pragma unroll
       for (int h = 0; h < C::NREG / 4; ++h)
         sbv[ni][h] = *(const v4f*)(sb + wave * C::NPW + ni * MS + col_run(h));
   }
-  auto out_vec = [&](int mi, int ni, int h, auto emit) {
+  // bias of a run of 4 columns (read from LDS where it is used)
+  auto bias4 = [&](int ni, int h) -> v4f {
+    if constexpr (C::NBI > 0) return *(const v4f*)(lds + C::BIAS_OFF + (wave * C::NPW + ni * MS + col_run(h)) * 4);
+    else return v4f{0.f, 0.f, 0.f, 0.f};
+  };
+  auto out_vec = [&](auto act_c, int mi, int ni, int h, auto emit) {
+    constexpr int A = decltype(act_c)::value;
     if constexpr (DT == DT_I8) {
       v4i v;
 #pragma unroll
@@ -492,57 +547,60 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
       emit(v);
     } else {
       v4f v;
+      const v4f bv = bias4(ni, h);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * h + r];
-      if constexpr (DT == DT_FP8) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (v[r] * sav[mi]) * sbv[ni][h][r];
+      for (int r = 0; r < 4; ++r) {
+        float x = acc[mi][ni][4 * h + r];
+        if constexpr (DT == DT_FP8) x = (x * sav[mi]) * sbv[ni][h][r];
+        v[r] = activate<A>(x + bv[r]);
       }
-      v2i o;
-      o[0] = (int)pack_bf16x2(v[0], v[1]);
-      o[1] = (int)pack_bf16x2(v[2], v[3]);
-      emit(o);
+      emit(pack_out4<DT>(v));
     }
   };
 
-  if constexpr (EPI == EPI_DIRECT) {
+  auto store_tile = [&](auto act_c) {
+    if constexpr (EPI == EPI_DIRECT) {
 #pragma unroll
-    for (int mi = 0; mi < C::MREP; ++mi)
+      for (int mi = 0; mi < C::MREP; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < C::NACC; ++ni)
+        for (int ni = 0; ni < C::NACC; ++ni)
 #pragma unroll
-        for (int h = 0; h < C::NREG / 4; ++h) {
-          const uint32_t off = ((mi * MS + lrow) * p.N + wave * C::NPW + ni * MS + col_run(h)) * C::OB;
-          out_vec(mi, ni, h, [&](auto v) {
-            if constexpr (sizeof(v) == 16) buf_store16(v, rc, off);
-            else buf_store8(v, rc, off);
-          });
-        }
-  } else {
-    // CShuffle: stage the tile in LDS (the A buffers are dead after the last
-    // barrier), then write whole rows with 16-byte stores.
+          for (int h = 0; h < C::NREG / 4; ++h) {
+            const uint32_t off = c_off(mi * MS + elrow, wave * C::NPW + ni * MS + col_run(h));
+            out_vec(act_c, mi, ni, h, [&](auto v) {
+              if constexpr (sizeof(v) == 16) buf_store16(v, rc, off);
+              else buf_store8(v, rc, off);
+            });
+          }
+    } else {
+      // CShuffle: stage the tile in LDS (the A buffers are dead after the last
+      // barrier), then write whole rows with 16-byte stores.
 #pragma unroll
-    for (int mi = 0; mi < C::MREP; ++mi)
+      for (int mi = 0; mi < C::MREP; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < C::NACC; ++ni)
+        for (int ni = 0; ni < C::NACC; ++ni)
 #pragma unroll
-        for (int h = 0; h < C::NREG / 4; ++h) {
-          char* dst = lds + (mi * MS + lrow) * C::CSTRIDE + (wave * C::NPW + ni * MS + col_run(h)) * C::OB;
-          out_vec(mi, ni, h, [&](auto v) { *(decltype(v)*)dst = v; });
-        }
-    __syncthreads();
-    constexpr int CH_ROW = TN * C::OB / 16;
-    constexpr int TOTAL = TM * CH_ROW;
+          for (int h = 0; h < C::NREG / 4; ++h) {
+            char* dst = lds + (mi * MS + elrow) * C::CSTRIDE + (wave * C::NPW + ni * MS + col_run(h)) * C::OB;
+            out_vec(act_c, mi, ni, h, [&](auto v) { *(decltype(v)*)dst = v; });
+          }
+      __syncthreads();
+      constexpr int CH_ROW = TN * C::OB / 16;
+      constexpr int TOTAL = TM * CH_ROW;
 #pragma unroll
-    for (int i = 0; i < (TOTAL + C::THREADS - 1) / C::THREADS; ++i) {
-      const int q = i * C::THREADS + tid;
-      if (TOTAL % C::THREADS != 0 && q >= TOTAL) break;
-      const int row = q / CH_ROW;
-      const int ch = q % CH_ROW;
-      const v4i v = *(const v4i*)(lds + row * C::CSTRIDE + ch * 16);
-      buf_store16(v, rc, row * p.N * C::OB + ch * 16);
+      for (int i = 0; i < (TOTAL + C::THREADS - 1) / C::THREADS; ++i) {
+        const int q = i * C::THREADS + etid;
+        if (TOTAL % C::THREADS != 0 && q >= TOTAL) break;
+        const int row = q / CH_ROW;
+        const int ch = q % CH_ROW;
+        const v4i v = *(const v4i*)(lds + row * C::CSTRIDE + ch * 16);
+        // a 16-byte chunk lies inside one 16-column block: stored whole or not at all
+        buf_store16(v, rc, c_off(row, ch * 16 / C::OB));
+      }
     }
-  }
+  };
+  if constexpr (FUSED) with_act(p.act, store_tile);
+  else store_tile(std::integral_constant<int, ACT_NONE>{});
 }
 
 }  // namespace gp

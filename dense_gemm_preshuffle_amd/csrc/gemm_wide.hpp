@@ -19,9 +19,11 @@
 // tile a share of the next tile's DMAs, the read of A fragment i+RA (a ring of
 // RA+1 register sets) and, at the start of each MFMA K step, of the next
 // step's B fragments, then fragment i's NACC MFMAs; one explicit vmcnt wait
-// and one barrier close the tile. Epilogue: FP8 scales (DMA'd into LDS at the
-// start), bf16 rounding, CShuffle through LDS and full-row stores; INT8
-// stores its int32 results directly.
+// and one barrier close the tile. Epilogue: FP8 scales and the fused bias
+// (DMA'd into LDS at the start), activation, bf16 / fp16 rounding, CShuffle
+// through LDS and full-row stores; INT8 stores its int32 results directly.
+// Edge tiles of M or N not divisible by 256 are moved back to end at the last
+// row / column and store only what their neighbour does not (edge_shift).
 #pragma once
 
 #include <type_traits>
@@ -30,7 +32,7 @@
 
 namespace gp {
 
-template <int DT, int MS, int TKB, int PIPE>
+template <int DT, int MS, int TKB, int PIPE, bool FUSED = false>
 struct WideCfg {
   using S = Mma<DT, MS>;
   static constexpr int TM = 256, TN = 256;
@@ -55,7 +57,9 @@ struct WideCfg {
   static constexpr int CBYTES = CSHUF ? TM * CSTRIDE : 0;
   static constexpr int PBYTES = ST * STAGE;
   static constexpr int FSC_OFF = PBYTES > CBYTES ? PBYTES : CBYTES;
-  static constexpr int LDS = FSC_OFF + (DT == DT_FP8 ? (TM + TN) * 4 : 0);
+  static constexpr int BIAS_OFF = FSC_OFF + (DT == DT_FP8 ? (TM + TN) * 4 : 0);
+  static constexpr bool BIAS = FUSED && DT != DT_I8;   // bias slot of the fused epilogue
+  static constexpr int LDS = BIAS_OFF + (BIAS ? TN * 4 : 0);
   // A fragments read ahead; one FP8 fragment feeds NACC 32-cycle MFMAs,
   // which covers an LDS read on its own
   static constexpr int RA = FRAG == 2 ? 1 : 2;
@@ -67,9 +71,9 @@ struct WideCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int DT, int MS, int TKB, int PIPE>
+template <int DT, int MS, int TKB, int PIPE, bool FUSED>
 __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(TileArgs p) {
-  using C = WideCfg<DT, MS, TKB, PIPE>;
+  using C = WideCfg<DT, MS, TKB, PIPE, FUSED>;
   using Acc = typename Mma<DT, MS>::Acc;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
 
@@ -82,7 +86,9 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(TileArgs p) {
 
   uint32_t tm, tn;
   tile_coords(p, tm, tn);
-  const uint32_t m0 = tm * C::TM, n0 = tn * C::TN;
+  uint32_t m0 = tm * C::TM, n0 = tn * C::TN, mskip, nskip;
+  edge_shift(m0, mskip, C::TM, p.M);
+  edge_shift(n0, nskip, C::TN, p.N);
   const uint32_t Kb = p.Kb;
   const int KT = (int)(Kb / TKB);
   const char* ga = p.a + (size_t)m0 * Kb;   // the workgroup's 256 A rows
@@ -146,6 +152,14 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(TileArgs p) {
   if constexpr (DT == DT_FP8) {
     if (wave == 0) lds_dma16((const float*)p.sa + m0, C::TM * 4, lds + C::FSC_OFF, lane * 16);
     if (wave == 1) lds_dma16((const float*)p.sb + n0, C::TN * 4, lds + C::FSC_OFF + C::TM * 4, lane * 16);
+  }
+  // the fused-epilogue bias (wave 2, one KiB); without one its LDS slot
+  // holds zeros (written before the first barrier, read after the last)
+  if constexpr (C::BIAS) {
+    if (wave == 2) {
+      if (p.bias) lds_dma16(p.bias + n0, C::TN * 4, lds + C::BIAS_OFF, lane * 16);
+      else *(v4f*)(lds + C::BIAS_OFF + lane * 16) = v4f{0.f, 0.f, 0.f, 0.f};
+    }
   }
 
   Acc acc[C::MREP][C::NACC];
@@ -238,6 +252,10 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(TileArgs p) {
   const int col0 = wn * C::WTN;
   const __amdgpu_buffer_rsrc_t rc =
       make_rsrc(p.c + ((size_t)m0 * p.N + n0) * C::OB, ((C::TM - 1) * p.N + C::TN) * C::OB);
+  // rows / columns an edge tile shares with its neighbour: offset outside the resource
+  auto c_off = [&](uint32_t r, uint32_t c) -> uint32_t {
+    return (r >= mskip && c >= nskip) ? (r * p.N + c) * C::OB : 0x80000000u;
+  };
   float sav[C::MREP];
   v4f sbv[C::NACC][C::NREG / 4];
   if constexpr (DT == DT_FP8) {
@@ -250,6 +268,11 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(TileArgs p) {
 #pragma unroll
       for (int h = 0; h < C::NREG / 4; ++h) sbv[ni][h] = *(const v4f*)(fsb + col0 + ni * MS + col_run(h));
   }
+  // bias of a run of 4 columns (read from LDS where it is used)
+  auto bias4 = [&](int ni, int h) -> v4f {
+    if constexpr (C::BIAS) return *(const v4f*)(lds + C::BIAS_OFF + (col0 + ni * MS + col_run(h)) * 4);
+    else return v4f{0.f, 0.f, 0.f, 0.f};
+  };
   if constexpr (!C::CSHUF) {
 #pragma unroll
     for (int mi = 0; mi < C::MREP; ++mi)
@@ -260,27 +283,30 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(TileArgs p) {
           v4i v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * h + r];
-          buf_store16(v, rc, ((row0 + mi * MS) * p.N + col0 + ni * MS + col_run(h)) * C::OB);
+          buf_store16(v, rc, c_off(row0 + mi * MS, col0 + ni * MS + col_run(h)));
         }
   } else {
+    auto stage_tile = [&](auto act_c) {
+      constexpr int A = decltype(act_c)::value;
 #pragma unroll
-    for (int mi = 0; mi < C::MREP; ++mi)
+      for (int mi = 0; mi < C::MREP; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < C::NACC; ++ni)
+        for (int ni = 0; ni < C::NACC; ++ni)
 #pragma unroll
-        for (int h = 0; h < C::NREG / 4; ++h) {
-          v4f v;
+          for (int h = 0; h < C::NREG / 4; ++h) {
+            v4f v;
+            const v4f bv = bias4(ni, h);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * h + r];
-          if constexpr (DT == DT_FP8) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = (v[r] * sav[mi]) * sbv[ni][h][r];
+            for (int r = 0; r < 4; ++r) {
+              float x = acc[mi][ni][4 * h + r];
+              if constexpr (DT == DT_FP8) x = (x * sav[mi]) * sbv[ni][h][r];
+              v[r] = activate<A>(x + bv[r]);
+            }
+            *(v2i*)(lds + (row0 + mi * MS) * C::CSTRIDE + (col0 + ni * MS + col_run(h)) * C::OB) = pack_out4<DT>(v);
           }
-          v2i o;
-          o[0] = (int)pack_bf16x2(v[0], v[1]);
-          o[1] = (int)pack_bf16x2(v[2], v[3]);
-          *(v2i*)(lds + (row0 + mi * MS) * C::CSTRIDE + (col0 + ni * MS + col_run(h)) * C::OB) = o;
-        }
+    };
+    if constexpr (FUSED) with_act(p.act, stage_tile);
+    else stage_tile(std::integral_constant<int, ACT_NONE>{});
     __syncthreads();
     constexpr int CH_ROW = C::TN * C::OB / 16;
     constexpr int TOTAL = C::TM * CH_ROW;
@@ -289,7 +315,7 @@ __global__ __launch_bounds__(512, 1) void gemm_wide_kernel(TileArgs p) {
     for (int i = 0; i < TOTAL / C::THREADS; ++i) {
       const int q = i * C::THREADS + tid;
       const int row = q / CH_ROW, ch = q % CH_ROW;
-      buf_store16(*(const v4i*)(lds + row * C::CSTRIDE + ch * 16), rc, row * p.N * C::OB + ch * 16);
+      buf_store16(*(const v4i*)(lds + row * C::CSTRIDE + ch * 16), rc, c_off(row, ch * 16 / C::OB));
     }
   }
 }

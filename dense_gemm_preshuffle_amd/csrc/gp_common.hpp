@@ -1,7 +1,8 @@
 // Shared device helpers for the gfx950 preshuffle GEMM kernels.
 //
 // Vector types, buffer-resource loads/stores, the gfx950 MFMA wrappers for
-// each input type, and the bf16 round-to-nearest-even conversion.
+// each input type, the bf16 / fp16 round-to-nearest-even conversions, the
+// fused-epilogue activations and the INT4 widening of the W4A8 path.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,6 +20,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // f(std::integral_constant<int, j>) for j = J0 .. J1-1, unrolled at compile time
 template <int J0, class F, int... Js>
@@ -30,7 +32,12 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl<J0>(f, std::make_integer_sequence<int, (J1 > J0 ? J1 - J0 : 0)>{});
 }
 
-enum DType : int { DT_I8 = 0, DT_FP8 = 1, DT_BF16 = 2, DT_FP4 = 3 };
+// DT_I4: int8 A times INT4 B (W4A8); B is widened to int8 in registers and
+// multiplied on the int8 instructions.
+enum DType : int { DT_I8 = 0, DT_FP8 = 1, DT_BF16 = 2, DT_FP4 = 3, DT_F16 = 4, DT_I4 = 5 };
+
+// Activations of the fused epilogue (values of the C ABI's GP_ACT_*).
+enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_SILU = 2, ACT_GELU = 3 };
 enum Epi : int { EPI_DIRECT = 1, EPI_CSHUFFLE = 2 };
 
 // gfx9 buffer resource word 3 (32-bit raw buffer, bounds checked on num_records).
@@ -118,8 +125,12 @@ __device__ v4f mfma_scale_16x16x128_v4(v4i a, v4i b, v4f c, int cbsz, int blgp, 
 template <int DT> struct Traits;
 template <> struct Traits<DT_I8>   { static constexpr int KB = 64;  static constexpr int FRAG = 1; using Acc = v4i; };
 template <> struct Traits<DT_BF16> { static constexpr int KB = 64;  static constexpr int FRAG = 1; using Acc = v4f; };
+template <> struct Traits<DT_F16>  { static constexpr int KB = 64;  static constexpr int FRAG = 1; using Acc = v4f; };
 template <> struct Traits<DT_FP4>  { static constexpr int KB = 64;  static constexpr int FRAG = 1; using Acc = v4f; };
 template <> struct Traits<DT_FP8>  { static constexpr int KB = 128; static constexpr int FRAG = 2; using Acc = v4f; };
+// W4A8 (small-M kernel only): KB counts bytes of B; one 16-byte INT4 piece
+// (32 K elements) feeds two int8 MFMAs.
+template <> struct Traits<DT_I4>   { static constexpr int KB = 64;  static constexpr int FRAG = 1; using Acc = v4i; };
 
 // One 16x16 MFMA step. X supplies the first operand (its lane l gives row l%16,
 // K piece l/16), Y the second. The result in lane l is D[4*(l/16)+r][l%16].
@@ -132,6 +143,9 @@ mfma(const v4i* x, const v4i* y, typename Traits<DT>::Acc acc, int sx = 0, int s
   } else if constexpr (DT == DT_BF16) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x[0]),
                                                    __builtin_bit_cast(v8bf, y[0]), acc, 0, 0, 0);
+  } else if constexpr (DT == DT_F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x[0]),
+                                                  __builtin_bit_cast(v8h, y[0]), acc, 0, 0, 0);
   } else if constexpr (DT == DT_FP8) {
     v8i xx = __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7);
     v8i yy = __builtin_shufflevector(y[0], y[1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -190,6 +204,9 @@ __device__ __forceinline__ typename Mma<DT, MS>::Acc mma(const v4i* x, const v4i
     } else if constexpr (DT == DT_BF16) {
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, x[0]), __builtin_bit_cast(v8bf, y[0]), acc,
                                                      0, 0, 0);
+    } else if constexpr (DT == DT_F16) {
+      return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, x[0]), __builtin_bit_cast(v8h, y[0]), acc,
+                                                    0, 0, 0);
     } else {
       return mfma_scale_32x32x64_v4(x[0], y[0], acc, 4, 4, SEL, sx, SEL, sy);
     }
@@ -201,6 +218,85 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   __bf16 a = (__bf16)lo;
   __bf16 b = (__bf16)hi;
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// fp32 -> fp16 with round-to-nearest-even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  _Float16 a = (_Float16)lo;
+  _Float16 b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Four fp32 results -> 8 bytes of the output type.
+template <int DT>
+__device__ __forceinline__ v2i pack_out4(v4f v) {
+  v2i o;
+  if constexpr (DT == DT_F16) {
+    o[0] = (int)pack_f16x2(v[0], v[1]);
+    o[1] = (int)pack_f16x2(v[2], v[3]);
+  } else {
+    o[0] = (int)pack_bf16x2(v[0], v[1]);
+    o[1] = (int)pack_bf16x2(v[2], v[3]);
+  }
+  return o;
+}
+
+// erf for the GELU epilogue: Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26, erf(x) = 1 - (a1 t + ... + a5 t^5) e^(-x^2),
+// t = 1 / (1 + p x), for x >= 0 (absolute error <= 1.5e-7, well below the
+// bf16 / fp16 output rounding), odd symmetry for x < 0. About 15 VALU
+// operations, a fraction of a library erf, which matters where the epilogue
+// sits on the critical path (the small-M kernel).
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.f + 0.3275911f * ax);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  return copysignf(1.f - poly * __expf(-ax * ax), x);
+}
+
+// The value of x, hidden from the optimizer: every quantity derived from the
+// result is computed where this call stands. Used at the start of epilogues
+// so that their per-lane addresses are not hoisted above the K loop, where
+// they would occupy registers through it.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Fused epilogue activation (Kernel Tuning Guide §6: bias, bias+ReLU,
+// bias+SiLU, bias+GELU), chosen at compile time; with_act() dispatches a
+// kernel's uniform `act` once, so no per-element branch is left.
+//   relu(x) = max(x, 0); silu(x) = x / (1 + e^-x); gelu(x) = x/2 (1 + erf(x / sqrt 2)).
+// The reciprocal is the hardware's (1 ulp), again far below the output rounding.
+template <int A>
+__device__ __forceinline__ float activate(float x) {
+  if constexpr (A == ACT_RELU) return fmaxf(x, 0.f);
+  else if constexpr (A == ACT_SILU) return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+  else if constexpr (A == ACT_GELU) return 0.5f * x * (1.f + erf_as7126(x * 0.70710678118654752f));
+  else return x;
+}
+template <class F>
+__device__ __forceinline__ void with_act(int act, F&& f) {
+  switch (act) {
+    case ACT_RELU: f(std::integral_constant<int, ACT_RELU>{}); break;
+    case ACT_SILU: f(std::integral_constant<int, ACT_SILU>{}); break;
+    case ACT_GELU: f(std::integral_constant<int, ACT_GELU>{}); break;
+    default: f(std::integral_constant<int, ACT_NONE>{}); break;
+  }
+}
+
+// W4A8: one 16-byte piece of the INT4 layout holds 32 K elements of a
+// column, elements 0..15 in the low nibbles and 16..31 in the high nibbles
+// of its 16 bytes. Widening keeps each nibble in the top half of its byte,
+// i.e. the int8 value 16 * v: two masks (and a shift) per dword, and the
+// int8 products come out exactly 16 times too large (undone in the epilogue).
+__device__ __forceinline__ void widen_int4(v4i w, v4i& lo, v4i& hi) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    lo[d] = (int)(((uint32_t)w[d] << 4) & 0xF0F0F0F0u);
+    hi[d] = (int)((uint32_t)w[d] & 0xF0F0F0F0u);
+  }
 }
 
 }  // namespace gp

@@ -1,21 +1,13 @@
-// Kernel instantiations and launch tables for one input type.
+// Kernel instantiations and launch tables for one input type (plain epilogue).
 #include "launch.hpp"
 #include "variants.hpp"
 
 namespace gp {
 
-hipError_t launch_tile_bf16(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s) {
-  GP_TILE_BF16(GP_TILE_CASE)
-  return hipErrorInvalidValue;
-}
+GP_DEFINE_PLAIN(bf16, GP_TILE_BF16, GP_WIDE_BF16)
 
 hipError_t launch_splitk_bf16(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s) {
   GP_SPLITK_BF16(GP_SPLITK_CASE)
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_wide_bf16(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s) {
-  GP_WIDE_BF16(GP_WIDE_CASE)
   return hipErrorInvalidValue;
 }
 

@@ -1,13 +1,10 @@
-// Kernel instantiations and launch tables for one input type.
+// Kernel instantiations and launch tables for one input type (plain epilogue).
 #include "launch.hpp"
 #include "variants.hpp"
 
 namespace gp {
 
-hipError_t launch_tile_fp4(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s) {
-  GP_TILE_FP4(GP_TILE_CASE)
-  return hipErrorInvalidValue;
-}
+GP_DEFINE_PLAIN(fp4, GP_TILE_FP4, GP_WIDE_FP4)
 
 hipError_t launch_splitk_fp4(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s) {
   GP_SPLITK_FP4(GP_SPLITK_CASE)

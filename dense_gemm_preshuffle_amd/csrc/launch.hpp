@@ -1,5 +1,7 @@
 // Launch-table interface between the host API and the per-dtype kernel
-// translation units.
+// translation units. Every tile and wide variant is built twice: plain, and
+// with the fused bias / activation epilogue (its own translation unit, so
+// the two halves compile in parallel).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -11,38 +13,71 @@
 namespace gp {
 
 // Each returns hipErrorInvalidValue if the variant is not compiled.
-hipError_t launch_tile_i8(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s);
-hipError_t launch_tile_fp8(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s);
-hipError_t launch_tile_bf16(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s);
-hipError_t launch_tile_fp4(int ms, int tm, int tn, int tkb, int pipe, int epi, const TileArgs& a, hipStream_t s);
+#define GP_DECLARE_TILE(NAME)                                                                       \
+  hipError_t launch_tile_##NAME(int ms, int tm, int tn, int tkb, int pipe, int epi, bool fused,    \
+                                const TileArgs& a, hipStream_t s);                                  \
+  hipError_t launch_tile_##NAME##_fused(int ms, int tm, int tn, int tkb, int pipe, int epi,        \
+                                        const TileArgs& a, hipStream_t s);
+#define GP_DECLARE_WIDE(NAME)                                                                       \
+  hipError_t launch_wide_##NAME(int ms, int tkb, int pipe, bool fused, const TileArgs& a, hipStream_t s); \
+  hipError_t launch_wide_##NAME##_fused(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s);
+GP_DECLARE_TILE(i8) GP_DECLARE_TILE(fp8) GP_DECLARE_TILE(bf16) GP_DECLARE_TILE(fp4) GP_DECLARE_TILE(f16)
+GP_DECLARE_WIDE(i8) GP_DECLARE_WIDE(fp8) GP_DECLARE_WIDE(bf16) GP_DECLARE_WIDE(f16) GP_DECLARE_WIDE(fp4)
 hipError_t launch_splitk_i8(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
 hipError_t launch_splitk_fp8(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
 hipError_t launch_splitk_bf16(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
 hipError_t launch_splitk_fp4(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
-hipError_t launch_wide_i8(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s);
-hipError_t launch_wide_fp8(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s);
-hipError_t launch_wide_bf16(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s);
+hipError_t launch_splitk_f16(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
+hipError_t launch_splitk_i4(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
 
 }  // namespace gp
 
-// Body of one dtype's launch tables.
-#define GP_TILE_CASE(DT, MS, TM, TN, TKB, PIPE)                                            \
-  if (ms == MS && tm == TM && tn == TN && tkb == TKB && pipe == PIPE) {                    \
-    const dim3 grid(a.tiles_m * a.tiles_n);                                                \
-    if (epi == EPI_CSHUFFLE)                                                               \
-      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_CSHUFFLE, PIPE>), grid, dim3(256), 0, s, a); \
-    else                                                                                   \
-      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_DIRECT, PIPE>), grid, dim3(256), 0, s, a);   \
-    return hipGetLastError();                                                              \
+// Bodies of one dtype's launch tables.
+#define GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, FU)                                           \
+  if (ms == MS && tm == TM && tn == TN && tkb == TKB && pipe == PIPE) {                            \
+    const dim3 grid(a.tiles_m * a.tiles_n);                                                        \
+    if (epi == EPI_CSHUFFLE)                                                                       \
+      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_CSHUFFLE, PIPE, FU>), grid, dim3(256), 0, s, a); \
+    else                                                                                           \
+      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_DIRECT, PIPE, FU>), grid, dim3(256), 0, s, a);   \
+    return hipGetLastError();                                                                      \
   }
+#define GP_TILE_CASE(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false)
+#define GP_TILE_CASE_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true)
 #define GP_SPLITK_CASE(DT, NB, W, KCH)                                                     \
   if (nb == NB && waves == W && kch == KCH) {                                              \
-    const dim3 grid(a.N / (16 * NB), a.M / 16);                                            \
+    const dim3 grid(a.N / (16 * NB), (a.M + 15) / 16);                                     \
     hipLaunchKernelGGL((gemm_splitk_kernel<DT, NB, W, KCH>), grid, dim3(W * 64), 0, s, a); \
     return hipGetLastError();                                                              \
   }
-#define GP_WIDE_CASE(DT, MS, TKB, PIPE)                                                     \
-  if (ms == MS && tkb == TKB && pipe == PIPE) {                                            \
-    hipLaunchKernelGGL((gemm_wide_kernel<DT, MS, TKB, PIPE>), dim3(a.tiles_m * a.tiles_n), dim3(512), 0, s, a); \
-    return hipGetLastError();                                                              \
+#define GP_WIDE_CASE_IMPL(DT, MS, TKB, PIPE, FU)                                                  \
+  if (ms == MS && tkb == TKB && pipe == PIPE) {                                                   \
+    hipLaunchKernelGGL((gemm_wide_kernel<DT, MS, TKB, PIPE, FU>), dim3(a.tiles_m * a.tiles_n), dim3(512), 0, s, a); \
+    return hipGetLastError();                                                                     \
+  }
+#define GP_WIDE_CASE(DT, MS, TKB, PIPE) GP_WIDE_CASE_IMPL(DT, MS, TKB, PIPE, false)
+#define GP_WIDE_CASE_FUSED(DT, MS, TKB, PIPE) GP_WIDE_CASE_IMPL(DT, MS, TKB, PIPE, true)
+
+// Plain launch tables of one dtype (the fused ones are in inst_<name>_fused.hip).
+#define GP_DEFINE_PLAIN(NAME, TILES, WIDES)                                                         \
+  hipError_t launch_tile_##NAME(int ms, int tm, int tn, int tkb, int pipe, int epi, bool fused,    \
+                                const TileArgs& a, hipStream_t s) {                                 \
+    if (fused) return launch_tile_##NAME##_fused(ms, tm, tn, tkb, pipe, epi, a, s);                \
+    TILES(GP_TILE_CASE)                                                                             \
+    return hipErrorInvalidValue;                                                                    \
+  }                                                                                                 \
+  hipError_t launch_wide_##NAME(int ms, int tkb, int pipe, bool fused, const TileArgs& a, hipStream_t s) { \
+    if (fused) return launch_wide_##NAME##_fused(ms, tkb, pipe, a, s);                              \
+    WIDES(GP_WIDE_CASE)                                                                             \
+    return hipErrorInvalidValue;                                                                    \
+  }
+#define GP_DEFINE_FUSED(NAME, TILES, WIDES)                                                         \
+  hipError_t launch_tile_##NAME##_fused(int ms, int tm, int tn, int tkb, int pipe, int epi,        \
+                                        const TileArgs& a, hipStream_t s) {                         \
+    TILES(GP_TILE_CASE_FUSED)                                                                       \
+    return hipErrorInvalidValue;                                                                    \
+  }                                                                                                 \
+  hipError_t launch_wide_##NAME##_fused(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s) { \
+    WIDES(GP_WIDE_CASE_FUSED)                                                                       \
+    return hipErrorInvalidValue;                                                                    \
   }

@@ -5,7 +5,8 @@
 // 32 (the MFMA block); pipe 0 = A staged through VGPRs (2 stages), 2 / 3 = A
 // by LDS DMA with 2 / 3 stages. Each is built with the direct and the
 // CShuffle epilogue.
-// Split-K kernel: Y(dtype, n_blocks_of_16, waves, chunk_bytes_per_wave).
+// Split-K kernel: Y(dtype, n_blocks_of_16, waves, chunk_bytes_per_wave);
+// the only kernel of the W4A8 type (DT_I4).
 // Wide kernel (256x256 tiles, 8 waves): W(dtype, mfma, tile_k_bytes, pipe),
 // pipe = LDS DMA stages of A and B.
 #pragma once
@@ -25,12 +26,17 @@
   X(DT_FP8, 16, 32, 128, 256, 4) X(DT_FP8, 16, 32, 128, 256, 6) X(DT_FP8, 16, 64, 256, 128, 4)
 
 #define GP_TILE_BF16(X)                                                                            \
-  X(DT_BF16, 16, 64, 128, 128, 0) X(DT_BF16, 16, 128, 256, 128, 0) X(DT_BF16, 16, 128, 256, 64, 0)          \
+  X(DT_BF16, 16, 32, 128, 128, 0) X(DT_BF16, 16, 64, 128, 128, 0) X(DT_BF16, 16, 128, 256, 128, 0) X(DT_BF16, 16, 128, 256, 64, 0)          \
   X(DT_BF16, 32, 64, 128, 128, 0) X(DT_BF16, 32, 64, 256, 128, 0) X(DT_BF16, 32, 128, 128, 128, 0)          \
   X(DT_BF16, 32, 128, 256, 128, 0) X(DT_BF16, 32, 128, 256, 64, 0)                                \
   X(DT_BF16, 32, 128, 256, 128, 2) X(DT_BF16, 32, 128, 256, 128, 3) X(DT_BF16, 16, 128, 256, 128, 3) \
   X(DT_BF16, 16, 256, 256, 128, 3) X(DT_BF16, 32, 256, 256, 128, 3) X(DT_BF16, 32, 256, 256, 128, 2) \
   X(DT_BF16, 32, 256, 256, 64, 3)
+
+#define GP_TILE_F16(X)                                                                             \
+  X(DT_F16, 16, 32, 128, 128, 0) X(DT_F16, 16, 64, 128, 128, 0) X(DT_F16, 16, 64, 256, 128, 0)             \
+  X(DT_F16, 16, 128, 128, 128, 0) X(DT_F16, 16, 128, 256, 128, 0) X(DT_F16, 16, 128, 256, 128, 3)          \
+  X(DT_F16, 32, 128, 256, 128, 3) X(DT_F16, 32, 64, 128, 128, 0)
 
 #define GP_TILE_FP4(X)                                                                             \
   X(DT_FP4, 16, 32, 256, 128, 0) X(DT_FP4, 16, 64, 128, 128, 0) X(DT_FP4, 16, 64, 256, 128, 0)              \
@@ -45,13 +51,20 @@
   Y(DT_FP8, 2, 4, 512) Y(DT_FP8, 1, 8, 256) Y(DT_FP8, 4, 4, 256) Y(DT_FP8, 2, 8, 256) Y(DT_FP8, 4, 8, 256)
 #define GP_SPLITK_BF16(Y) Y(DT_BF16, 1, 4, 64) Y(DT_BF16, 1, 4, 256) Y(DT_BF16, 2, 4, 256)
 #define GP_SPLITK_FP4(Y) Y(DT_FP4, 1, 4, 64) Y(DT_FP4, 1, 4, 256) Y(DT_FP4, 2, 4, 256)
+#define GP_SPLITK_F16(Y) Y(DT_F16, 1, 4, 64) Y(DT_F16, 1, 4, 256) Y(DT_F16, 2, 4, 256)
+// W4A8: chunk bytes are bytes of B (the int8 A chunk is twice as long)
+#define GP_SPLITK_I4(Y)                                                                            \
+  Y(DT_I4, 1, 4, 64) Y(DT_I4, 1, 4, 128) Y(DT_I4, 1, 4, 256) Y(DT_I4, 2, 4, 64) Y(DT_I4, 2, 4, 128)  \
+  Y(DT_I4, 2, 4, 256) Y(DT_I4, 2, 8, 128)
 
 #define GP_WIDE_I8(W) W(DT_I8, 16, 128, 2) W(DT_I8, 32, 128, 2)
 #define GP_WIDE_FP8(W) W(DT_FP8, 16, 128, 2)
 #define GP_WIDE_BF16(W) W(DT_BF16, 16, 128, 2) W(DT_BF16, 32, 128, 2) W(DT_BF16, 16, 64, 3) W(DT_BF16, 32, 64, 3) \
   W(DT_BF16, 16, 64, 4) W(DT_BF16, 32, 64, 4)
-#define GP_WIDE_FP4(W)
+#define GP_WIDE_F16(W) W(DT_F16, 16, 128, 2) W(DT_F16, 16, 64, 4)
+#define GP_WIDE_FP4(W)  /* FP4 runs on the 4-wave kernel */
 
-#define GP_TILE_ALL(X) GP_TILE_I8(X) GP_TILE_FP8(X) GP_TILE_BF16(X) GP_TILE_FP4(X)
-#define GP_SPLITK_ALL(Y) GP_SPLITK_I8(Y) GP_SPLITK_FP8(Y) GP_SPLITK_BF16(Y) GP_SPLITK_FP4(Y)
-#define GP_WIDE_ALL(W) GP_WIDE_I8(W) GP_WIDE_FP8(W) GP_WIDE_BF16(W) GP_WIDE_FP4(W)
+#define GP_TILE_ALL(X) GP_TILE_I8(X) GP_TILE_FP8(X) GP_TILE_BF16(X) GP_TILE_FP4(X) GP_TILE_F16(X)
+#define GP_SPLITK_ALL(Y) \
+  GP_SPLITK_I8(Y) GP_SPLITK_FP8(Y) GP_SPLITK_BF16(Y) GP_SPLITK_FP4(Y) GP_SPLITK_F16(Y) GP_SPLITK_I4(Y)
+#define GP_WIDE_ALL(W) GP_WIDE_I8(W) GP_WIDE_FP8(W) GP_WIDE_BF16(W) GP_WIDE_FP4(W) GP_WIDE_F16(W)

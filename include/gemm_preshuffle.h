@@ -7,8 +7,11 @@
  * gemm-optimization skill), §1.1, read with §12.1 (B is N rows of K contiguous
  * elements). B is consumed in the preshuffled layout of §1.4 / §12.1; A and C
  * are plain row-major. Element types follow §6.2: INT8, FP8 (OCP E4M3FN),
- * BF16 and gfx950 MXFP4 (E2M1 values, one E8M0 scale per 32 K elements).
- * The FP8 epilogue applies fp32 per-row / per-column scales (§7.1, §8.2).
+ * BF16, FP16 and gfx950 MXFP4 (E2M1 values, one E8M0 scale per 32 K
+ * elements), plus INT4 weights with int8 activations (W4A8, the INT4 bytes
+ * formula of §8.2). The FP8 and W4A8 epilogues apply fp32 per-row /
+ * per-column scales (§7.1, §8.2); every floating-point output can take the
+ * fused bias / activation epilogues of the Kernel Tuning Guide, §6.
  *
  * Conventions shared by every entry point
  *   - Ownership: the caller owns every buffer; all data pointers are DEVICE
@@ -18,8 +21,11 @@
  *     null stream). Nothing synchronizes; results are ready when the stream
  *     reaches that point.
  *   - Layout: A is [M][K] and C is [M][N], row-major, contiguous. Sizes are
- *     in ELEMENTS; an MXFP4 row of K elements is K/2 bytes (element 2i in
- *     the low nibble of byte i).
+ *     in ELEMENTS; an MXFP4 or INT4 row of K elements is K/2 bytes (element
+ *     2i in the low nibble of byte i).
+ *   - Shapes: N % 16 == 0 and K * (bits of a B element) % 512 == 0 (the B
+ *     layout); M is free. When the tile does not divide M or N, the edge
+ *     tiles overlap their neighbours inside M x N (no padding is needed).
  *   - Alignment: every data pointer must be 16-byte aligned.
  *   - Errors: arguments are validated on the host before any HIP call; a
  *     non-zero gp_status is returned and nothing is launched. A failing
@@ -50,8 +56,22 @@ typedef enum gp_dtype {
   GP_FP8_E4M3 = 1,  /* OCP FP8 E4M3FN (max 448, no infinities)      */
   GP_BF16 = 2,      /* bfloat16                                     */
   GP_FP4_E2M1 = 3,  /* OCP MX FP4 E2M1, two per byte, low nibble first */
-  GP_I32 = 4        /* int32 (output of the INT8 path)              */
+  GP_I32 = 4,       /* int32 (output of the INT8 path)              */
+  GP_F16 = 5,       /* IEEE binary16                                */
+  GP_I4 = 6         /* as an input type: int8 A with INT4 B (W4A8); INT4 is
+                       two's complement, two per byte, low nibble first */
 } gp_dtype;
+
+/* Fused epilogue activations (Kernel Tuning Guide §6: bias, bias_relu,
+ * bias_silu, bias_gelu), applied in fp32 after the scales and the bias:
+ *   relu(x) = max(x, 0)   silu(x) = x / (1 + exp(-x))
+ *   gelu(x) = x/2 * (1 + erf(x / sqrt 2))   (the exact, erf form)        */
+typedef enum gp_act {
+  GP_ACT_NONE = 0,
+  GP_ACT_RELU = 1,
+  GP_ACT_SILU = 2,
+  GP_ACT_GELU = 3
+} gp_act;
 
 enum {
   GP_EPI_AUTO = 0,      /* planner's choice                                   */
@@ -66,7 +86,7 @@ enum {
                             reduced through LDS (for the memory-bound small
                             batch of GEMM Opt. §1.3 / §8.3)                      */
   GP_KERNEL_WIDE = 3     /* 256x256 tiles, 8 waves, A and B both through LDS
-                            (INT8, FP8, BF16; M and N multiples of 256)          */
+                            (INT8, FP8, BF16, FP16; M and N at least 256)        */
 };
 
 /* Tuning options. Pass NULL, or a zero-filled struct, for all-automatic;
@@ -97,7 +117,7 @@ typedef struct gemm_plan_info {
   int64_t grid;                     /* workgroups                               */
   int64_t k_tiles;                  /* K tiles per workgroup (tile kernel)      */
   int64_t mfma_per_wave_tile;       /* MFMA instructions per wave per K tile    */
-  int64_t mfma_total;               /* MFMA instructions for the whole problem  */
+  int64_t mfma_total;               /* MFMA instructions the launch issues      */
   int mfma;                         /* MFMA block: 16 (16x16) or 32 (32x32)     */
   int pipeline;                     /* 1 VGPR-staged A; 2 .. 6 LDS DMA stages   */
 } gemm_plan_info;
@@ -113,8 +133,12 @@ typedef struct gemm_plan_info {
  * it is a device kernel, run once per B and amortised over GEMM calls.
  *   b       device, [N][Kb] bytes, read only.
  *   b_shuf  device, N*Kb bytes, written; must not overlap b.
- *   dtype   GP_I8, GP_FP8_E4M3, GP_BF16 or GP_FP4_E2M1 (fixes Kb; MXFP4
- *           block scales are NOT shuffled and stay [N][K/32]).
+ *   dtype   GP_I8, GP_FP8_E4M3, GP_BF16, GP_F16, GP_FP4_E2M1 or GP_I4 (fixes
+ *           Kb; MXFP4 block scales are NOT shuffled and stay [N][K/32]).
+ *           GP_I4 (W4A8 weights) also reorders the nibbles of every 16-byte
+ *           piece: element t of the piece's 32 goes to byte t % 16, the low
+ *           nibble for t < 16 and the high nibble otherwise, so that a lane
+ *           widens its piece to two int8 operands with masks alone.
  * Requires N % 16 == 0, Kb % 64 == 0 (GP_ESHAPE), N*Kb < 2^31.
  */
 int gemm_preshuffle_b(const void* b, void* b_shuf, int64_t N, int64_t K, int dtype, void* stream);
@@ -129,7 +153,7 @@ int gemm_preshuffle_b(const void* b, void* b_shuf, int64_t N, int64_t K, int dty
  * accumulation); in GP_FP8_E4M3 -> out GP_BF16 with both scales given:
  *     C[m][n] = bf16_rne((acc[m][n] * scale_a[m]) * scale_b[n]),
  * acc accumulated in fp32 (GEMM Optimization Guide §7.1). Anything else is
- * GP_EDTYPE. The chosen tile must divide M, N and K (GP_ESHAPE).
+ * GP_EDTYPE. The chosen tile_k must divide K (GP_ESHAPE).
  */
 int gemm_a8w8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b,
               void* c, int64_t M, int64_t N, int64_t K, int in_dtype, int out_dtype,
@@ -158,9 +182,55 @@ int gemm_mxfp4(const void* a, const uint8_t* scale_a, const void* b_shuf, const 
                void* c, int64_t M, int64_t N, int64_t K, const gemm_opts* opts, void* stream);
 
 /*
+ * gemm_f16 -- FP16 GEMM on preshuffled B (GEMM Optimization Guide §6.2, f16
+ * instruction), fp32 accumulation, fp16 output rounded to nearest even.
+ *   a [M][K] fp16, b_shuf from gemm_preshuffle_b(GP_F16), c [M][N] fp16.
+ */
+int gemm_f16(const void* a, const void* b_shuf, void* c, int64_t M, int64_t N, int64_t K,
+             const gemm_opts* opts, void* stream);
+
+/*
+ * gemm_w4a8 -- INT4 weights with int8 activations (GEMM Optimization Guide
+ * §8.2, INT4 bytes formula), for the memory-bound small-M regime.
+ *   a        device [M][K] int8.
+ *   b_shuf   from gemm_preshuffle_b(GP_I4) of B [N][K/2] packed INT4.
+ *   scale_a  device fp32 [M]; scale_b device fp32 [N] (both required).
+ *   c        device [M][N] bf16:
+ *     C[m][n] = bf16_rne((acc[m][n] * scale_a[m]) * scale_b[n]),
+ * acc = sum_k A[m][k] B[n][k] exact in int32. Runs on the small-M kernel
+ * (GP_KERNEL_SPLITK) for any M; K % 512 == 0 and K <= 65536.
+ */
+int gemm_w4a8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b, void* c,
+              int64_t M, int64_t N, int64_t K, const gemm_opts* opts, void* stream);
+
+/*
+ * gemm_ex -- any input type, with the fused epilogue of the Kernel Tuning
+ * Guide §6 (bias, bias+ReLU, bias+SiLU, bias+GELU).
+ *   in_dtype / out_dtype  GP_I8 -> GP_I32, GP_FP8_E4M3 -> GP_BF16,
+ *                         GP_BF16 -> GP_BF16, GP_F16 -> GP_F16,
+ *                         GP_FP4_E2M1 -> GP_BF16, GP_I4 -> GP_BF16;
+ *                         any other pair is GP_EDTYPE.
+ *   a, b_shuf, c, scales  as in the type's own entry point (FP8 / W4A8: fp32
+ *                         [M] and [N]; MXFP4: E8M0 [M][K/32] and [N][K/32];
+ *                         BF16 / FP16 / INT8: both NULL, else GP_EDTYPE).
+ *   bias                  device fp32 [N] or NULL (no bias).
+ *   act                   GP_ACT_* (GP_EINVAL outside the enum).
+ * Floating-point outputs:  C[m][n] = round(act(y[m][n] + bias[n])), y the
+ * scaled fp32 accumulator of the type's own entry point, round = RNE to
+ * the output type. The INT8 -> int32 path takes neither bias nor
+ * activation (GP_EDTYPE).
+ */
+int gemm_ex(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
+            const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
+            const gemm_opts* opts, void* stream);
+
+/*
  * gemm_plan -- host-only: validate a problem and report the plan a GEMM
  * call with the same arguments would launch (tile, kernel, grid, LDS, MFMA
- * counts). in_dtype is GP_I8, GP_FP8_E4M3, GP_BF16 or GP_FP4_E2M1. Touches
+ * counts). in_dtype is GP_I8, GP_FP8_E4M3, GP_BF16, GP_F16, GP_FP4_E2M1 or
+ * GP_I4 (W4A8). mfma_total counts the MFMAs the launch issues (edge tiles
+ * included); it is the problem's (M/ms)(N/ms)(K/K_instr) when the tile
+ * divides M and N. Touches
  * no device. Returns the same status the GEMM call would return for these
  * sizes and options (before the device checks).
  */

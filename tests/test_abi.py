@@ -20,8 +20,8 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = gp.header_functions()
-    assert set(names) >= {"gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4",
-                          "gemm_plan", "gemm_status_string"}
+    assert set(names) >= {"gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_f16",
+                          "gemm_w4a8", "gemm_ex", "gemm_plan", "gemm_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -50,7 +50,6 @@ def test_sizes_and_shapes(lib):
     assert lib.gemm_bf16(FAKE, FAKE, FAKE, 0, 256, 64, None, None) == GP_EINVAL      # empty
     assert lib.gemm_bf16(FAKE, FAKE, FAKE, 128, -16, 64, None, None) == GP_EINVAL
     assert lib.gemm_bf16(FAKE, FAKE, FAKE, 128, 250, 64, None, None) == GP_ESHAPE    # N % 16
-    assert lib.gemm_bf16(FAKE, FAKE, FAKE, 120, 256, 64, None, None) == GP_ESHAPE    # M % 16 (ragged)
     assert lib.gemm_bf16(FAKE, FAKE, FAKE, 128, 256, 48, None, None) == GP_ESHAPE    # Kb % 64
     assert lib.gemm_a8w8(FAKE, FAKE, None, None, FAKE, 16, 16, 96, 0, 4, None, None) == GP_ESHAPE
     assert lib.gemm_preshuffle_b(FAKE, ctypes.c_void_p(0x900000), 16, 32, 0, None) == GP_ESHAPE
@@ -102,7 +101,8 @@ def test_named_tiles_plan():
     assert p["mfma_per_wave_tile"] * 4 == F.mfma_per_tile_pages(64, 256, 128)
     assert p["grid"] == 128 and p["k_tiles"] == 32 and p["mfma"] == 16
     fp8_scales = 256 * (1 + 256 // 64)              # FP8 row / column scales staged in LDS
-    assert p["lds_bytes"] == F.lds_bytes(64, 256, 128, 1) + fp8_scales
+    bias = 256 * 4                                  # fused-epilogue bias staged in LDS (tile_n floats)
+    assert p["lds_bytes"] == F.lds_bytes(64, 256, 128, 1) + fp8_scales + bias
     p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, epilogue=1, mfma=16,
                                                      pipeline=1))
     assert p["grid"] == 2048 and p["k_tiles"] == 128
@@ -110,11 +110,11 @@ def test_named_tiles_plan():
     p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, epilogue=1,
                                                      pipeline=1, mfma=32))
     assert p["mfma"] == 32 and p["mfma_per_wave_tile"] == 32   # 4 K16 steps x 4 x 2 (32x32 blocks)
-    assert p["lds_bytes"] == F.lds_bytes(128, 256, 64, 2)
+    assert p["lds_bytes"] == F.lds_bytes(128, 256, 64, 2) + bias
     p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=2))
-    assert p["lds_bytes"] == 64 * (256 * 2 + 16) + fp8_scales   # padded CShuffle tile (above 3 stages of A)
+    assert p["lds_bytes"] == 64 * (256 * 2 + 16) + fp8_scales + bias   # padded CShuffle tile (above 3 stages of A)
     p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=1, pipeline=3))
-    assert p["lds_bytes"] == 3 * 64 * 128 + fp8_scales and p["pipeline"] == 3
+    assert p["lds_bytes"] == 3 * 64 * 128 + fp8_scales + bias and p["pipeline"] == 3
     # default epilogue: CShuffle for tile_n >= 128 while two workgroups fit a CU
     assert gp.gemm_plan("bf16", 8192, 8192, 8192)["epilogue"] == gp.EPI_CSHUFFLE
     assert gp.gemm_plan("int8", 4096, 4096, 4096, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128))["epilogue"] == gp.EPI_DIRECT
@@ -135,7 +135,7 @@ def test_wide_kernel_plan():
     assert p["mfma_per_wave_tile"] * 8 * p["grid"] * p["k_tiles"] == p["mfma_total"]
     assert p["mfma_total"] == F.mfma_count_gfx950("bf16", 8192, 8192, 8192, p["mfma"])
     # A and B stages (256 rows each) or the padded bf16 C tile, whichever is larger
-    assert p["lds_bytes"] == max(p["pipeline"] * 512 * p["tile_k"] * 2, 256 * (256 * 2 + 16))
+    assert p["lds_bytes"] == max(p["pipeline"] * 512 * p["tile_k"] * 2, 256 * (256 * 2 + 16)) + 256 * 4
     q = gp.gemm_plan("int8", 512, 512, 512, dict(kernel=3, mfma=32))
     assert q["epilogue"] == gp.EPI_DIRECT and q["mfma"] == 32
     assert q["mfma_per_wave_tile"] * 8 * q["grid"] * q["k_tiles"] == q["mfma_total"]
@@ -147,7 +147,7 @@ def test_wide_kernel_plan():
     with pytest.raises(gp.GemmError):
         gp.gemm_plan("mxfp4", 512, 512, 512, dict(kernel=3))     # FP4 runs on the 4-wave kernel
     with pytest.raises(gp.GemmError):
-        gp.gemm_plan("bf16", 384, 512, 512, dict(kernel=3))      # M not a multiple of 256
+        gp.gemm_plan("bf16", 192, 512, 512, dict(kernel=3))      # M below one 256-row tile
 
 
 def test_small_m_uses_split_k():
@@ -166,3 +166,65 @@ def test_every_gpu_case_has_a_plan():
     for opts in (dict(kernel=1, tile_m=64, tile_n=256, tile_k=256), dict(kernel=1, tile_m=128, tile_n=256, tile_k=256)):
         gp.gemm_plan("mxfp4", 128, 256, 1024, opts)
     gp.gemm_plan("mxfp4", 16, 64, 1024, dict(kernel=2))
+
+
+def test_gemm_ex_validation(lib):
+    S = ctypes.c_void_p(0x200000)
+    B = ctypes.c_void_p(0x300000)
+    GP_I8, GP_FP8, GP_BF16, GP_FP4, GP_I32, GP_F16, GP_I4 = 0, 1, 2, 3, 4, 5, 6
+    ex = lib.gemm_ex
+    # activation outside the enum; misaligned bias
+    assert ex(GP_BF16, GP_BF16, FAKE, FAKE, None, None, B, 4, FAKE, 128, 256, 64, None, None) == GP_EINVAL
+    assert ex(GP_BF16, GP_BF16, FAKE, FAKE, None, None, B, -1, FAKE, 128, 256, 64, None, None) == GP_EINVAL
+    assert ex(GP_BF16, GP_BF16, FAKE, FAKE, None, None, MIS, 1, FAKE, 128, 256, 64, None, None) == GP_EINVAL
+    # the exact INT8 -> int32 path takes no bias and no activation
+    assert ex(GP_I8, GP_I32, FAKE, FAKE, None, None, B, 0, FAKE, 16, 16, 64, None, None) == GP_EDTYPE
+    assert ex(GP_I8, GP_I32, FAKE, FAKE, None, None, None, 1, FAKE, 16, 16, 64, None, None) == GP_EDTYPE
+    # output types: FP16 -> fp16 only, the others -> bf16
+    assert ex(GP_F16, GP_BF16, FAKE, FAKE, None, None, None, 0, FAKE, 16, 16, 64, None, None) == GP_EDTYPE
+    assert ex(GP_BF16, GP_F16, FAKE, FAKE, None, None, None, 0, FAKE, 16, 16, 64, None, None) == GP_EDTYPE
+    assert ex(GP_I4, GP_I32, FAKE, FAKE, S, S, None, 0, FAKE, 16, 16, 512, None, None) == GP_EDTYPE
+    # scale vectors: required for FP8 / MXFP4 / W4A8, refused for BF16 / FP16
+    assert ex(GP_I4, GP_BF16, FAKE, FAKE, None, S, None, 0, FAKE, 16, 16, 512, None, None) == GP_EDTYPE
+    assert ex(GP_BF16, GP_BF16, FAKE, FAKE, S, None, None, 0, FAKE, 16, 16, 64, None, None) == GP_EDTYPE
+    assert ex(9, GP_BF16, FAKE, FAKE, None, None, None, 0, FAKE, 16, 16, 64, None, None) == GP_EDTYPE
+    # named wrappers validate the same way
+    assert lib.gemm_w4a8(FAKE, FAKE, None, S, FAKE, 16, 16, 512, None, None) == GP_EDTYPE
+    assert lib.gemm_f16(FAKE, FAKE, None, 16, 16, 64, None, None) == GP_EINVAL
+    assert lib.gemm_w4a8(FAKE, FAKE, S, S, FAKE, 16, 16, 384, None, None) == GP_ESHAPE   # K % 128 (INT4 layout)
+
+
+def test_w4a8_plan():
+    p = gp.gemm_plan("w4a8", 16, 7168, 2048)
+    assert p["kernel"] == gp.KERNEL_SPLITK
+    assert p["mfma_total"] == F.mfma_count_gfx950("w4a8", 16, 7168, 2048)
+    with pytest.raises(gp.GemmError) as e:
+        gp.gemm_plan("w4a8", 256, 256, 2048, dict(kernel=1))   # W4A8 runs on the small-M kernel only
+    assert e.value.status == GP_EDTYPE
+    with pytest.raises(gp.GemmError) as e:
+        gp.gemm_plan("w4a8", 16, 256, 2 * 65536)               # int32 range of the 16x widened products
+    assert e.value.status == GP_ESHAPE
+    q = gp.gemm_plan("w4a8", 300, 512, 4096)                   # any M: 19 row blocks, the last partial
+    assert q["grid"] == (512 // q["tile_n"]) * 19
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 100, 256, 256), ("fp8", 200, 272, 512), ("int8", 77, 208, 256),
+                                         ("mxfp4", 130, 4096, 1024), ("fp16", 40, 128, 128), ("fp8", 5, 512, 2048)])
+def test_ragged_plans(dtype, M, N, K):
+    """M and N not multiples of the tile: edge tiles overlap inside M x N,
+    the grid is the ceiling, and the issued MFMAs cover every output."""
+    p = gp.gemm_plan(dtype, M, N, K)
+    tm, tn = p["tile_m"], p["tile_n"]
+    if p["kernel"] == gp.KERNEL_TILE:
+        assert tm <= M and tn <= N
+    assert p["grid"] == -(-M // tm) * -(-N // tn)
+    assert p["mfma_total"] * F.flops_per_mfma_gfx950(dtype, p["mfma"]) >= F.flops(M, N, K)
+    assert p["mfma_total"] == p["grid"] * p["waves"] * p["k_tiles"] * p["mfma_per_wave_tile"]
+
+
+def test_tile_must_fit_inside_the_problem():
+    with pytest.raises(gp.GemmError) as e:
+        gp.gemm_plan("bf16", 100, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64))
+    assert e.value.status == GP_ESHAPE
+    # no tile fits a 48-column problem: the small-M kernel takes it for any M
+    assert gp.gemm_plan("fp8", 200, 48, 1024)["kernel"] == gp.KERNEL_SPLITK

@@ -26,12 +26,13 @@ def _gpu():
     yield
 
 
-EB = {"int8": 1, "fp8": 1, "bf16": 2, "mxfp4": 0.5}
+EB = {"int8": 1, "fp8": 1, "bf16": 2, "mxfp4": 0.5, "fp16": 2, "w4a8": 0.5}
 
 
 # ---------------------------------------------------------------- preshuffle
 @pytest.mark.parametrize("dtype,N,K", [("int8", 16, 64), ("fp8", 48, 512), ("bf16", 64, 256),
-                                       ("mxfp4", 32, 512), ("fp8", 7168, 2048)])
+                                       ("mxfp4", 32, 512), ("fp8", 7168, 2048), ("fp16", 32, 128),
+                                       ("w4a8", 48, 512), ("w4a8", 7168, 2048)])
 def test_preshuffle_bit_exact(dtype, N, K):
     import torch
     from dense_gemm_preshuffle_amd import gemm_preshuffle_b
@@ -41,7 +42,8 @@ def test_preshuffle_bit_exact(dtype, N, K):
     b = np.random.default_rng(N + K).integers(0, 256, size=(N, Kb), dtype=np.uint8)
     out = gemm_preshuffle_b(torch.from_numpy(b).cuda(), dtype)
     torch.cuda.synchronize()
-    assert np.array_equal(out.cpu().numpy(), oracle.preshuffle(b))
+    ref = oracle.preshuffle_int4(b) if dtype == "w4a8" else oracle.preshuffle(b)
+    assert np.array_equal(out.cpu().numpy(), ref)
 
 
 # ---------------------------------------------------------------- random parity over tile shapes
@@ -130,6 +132,19 @@ TILE_CASES = [
     ("int8", 16, 64, 1024, dict(kernel=2)),
     ("bf16", 32, 128, 512, dict(kernel=2, tile_n=32)),
     ("mxfp4", 16, 128, 2048, dict(kernel=2)),
+    # FP16 (fp16 output): tile, DMA pipeline, 32x32 blocks, split-K, wide
+    ("fp16", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64)),
+    ("fp16", 128, 512, 320, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, pipeline=3)),
+    ("fp16", 128, 256, 192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
+    ("fp16", 64, 256, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64, epilogue=1)),
+    ("fp16", 32, 128, 512, dict(kernel=2, tile_n=32)),
+    ("fp16", 512, 256, 320, dict(kernel=3)),
+    # W4A8 (int8 A, INT4 B) on the small-M kernel
+    ("w4a8", 16, 512, 2048, dict(kernel=2)),
+    ("w4a8", 32, 256, 1024, dict(kernel=2, tile_n=16)),
+    ("w4a8", 16, 256, 4096, dict(kernel=2, tile_n=32, waves=8, tile_k=256)),
+    ("w4a8", 48, 128, 512, dict(kernel=2, tile_k=128)),
+    ("w4a8", 16, 128, 4096, dict(kernel=2, tile_n=32, tile_k=128)),   # 4 chunks per wave
 ]
 
 
@@ -151,6 +166,78 @@ def test_xcd_order_does_not_change_result(xcd):
     check("fp8", host, out)
 
 
+# ---------------------------------------------------------------- M / N not multiples of the tile
+RAGGED_CASES = [
+    # edge tiles overlap their neighbours; split-K takes partial 16-row blocks
+    ("bf16", 100, 272, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64)),
+    ("bf16", 200, 400, 192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, pipeline=3)),
+    ("bf16", 130, 304, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, epilogue=1)),
+    ("fp8", 77, 336, 512, dict(kernel=1, tile_m=32, tile_n=256, tile_k=128, pipeline=3)),
+    ("fp8", 150, 528, 384, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=2)),
+    ("int8", 90, 208, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128)),
+    ("int8", 33, 80, 256, dict(kernel=1, tile_m=32, tile_n=64, tile_k=128)),
+    ("mxfp4", 160, 288, 512, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32)),
+    ("fp16", 70, 144, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64)),
+    ("bf16", 300, 272, 128, dict(kernel=3)),
+    ("fp8", 1, 512, 2048, dict(kernel=2)),
+    ("fp8", 5, 256, 1024, dict(kernel=2, tile_n=16)),
+    ("bf16", 17, 128, 512, dict(kernel=2)),
+    ("int8", 29, 64, 1024, dict(kernel=2)),
+    ("mxfp4", 7, 128, 2048, dict(kernel=2)),
+    ("w4a8", 3, 256, 2048, dict(kernel=2)),
+    ("fp8", 200, 48, 1024, None),          # no tile fits 48 columns: the planner takes split-K
+    ("bf16", 100, 272, 256, None),         # planner's own choice
+]
+
+
+@pytest.mark.parametrize("case", RAGGED_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[4]}")
+def test_ragged_parity(case):
+    dtype, M, N, K, opts = case
+    say(f"ragged {dtype} {M}x{N}x{K} {opts}")
+    host = workloads.make_inputs(dtype, M, N, K, seed=M + N + K)
+    out = gpu_run(dtype, host, opts)
+    check(dtype, host, out)
+
+
+# ---------------------------------------------------------------- fused epilogues
+EPI_CASES = [
+    ("fp8", 16, 512, 2048, dict(kernel=2)),
+    ("fp8", 128, 512, 640, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, pipeline=3, epilogue=2)),
+    ("fp8", 96, 256, 256, dict(kernel=1, tile_m=32, tile_n=256, tile_k=128, epilogue=1)),
+    ("bf16", 256, 512, 192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, pipeline=3)),
+    ("bf16", 128, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, epilogue=1)),
+    ("mxfp4", 128, 256, 512, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
+    ("mxfp4", 16, 128, 2048, dict(kernel=2)),
+    ("fp16", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64)),
+    ("bf16", 512, 256, 320, dict(kernel=3)),
+    ("fp8", 512, 512, 640, dict(kernel=3)),
+    ("w4a8", 16, 512, 2048, dict(kernel=2)),
+    ("bf16", 100, 272, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64)),   # with edge tiles
+]
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "silu", "gelu"])
+@pytest.mark.parametrize("case", EPI_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-k{c[4]['kernel']}")
+def test_fused_epilogue_parity(case, act):
+    dtype, M, N, K, opts = case
+    say(f"epilogue {act} {dtype} {M}x{N}x{K} {opts}")
+    host = workloads.make_inputs(dtype, M, N, K, seed=M + 3 * N + K, bias=True)
+    out = gpu_run(dtype, host, opts, act=act)
+    check(dtype, host, out, act=act)
+
+
+def test_activation_without_bias_and_int8_refused():
+    say("epilogue without bias")
+    host = workloads.make_inputs("fp8", 128, 256, 256, seed=41)
+    out = gpu_run("fp8", host, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128), act="gelu")
+    check("fp8", host, out, act="gelu")
+    out = gpu_run("bf16", workloads.make_inputs("bf16", 16, 256, 1024, seed=42), dict(kernel=2), act="silu")
+    check("bf16", workloads.make_inputs("bf16", 16, 256, 1024, seed=42), out, act="silu")
+    import dense_gemm_preshuffle_amd as gp
+    with pytest.raises(gp.GemmError):
+        gpu_run("int8", workloads.make_inputs("int8", 64, 128, 128, seed=1), act="relu")
+
+
 # ---------------------------------------------------------------- closed forms (bit-exact)
 def _one_hot_b(dtype, N, K, perm):
     """B[n, k] = 1.0 at k = perm[n], else 0, in the input encoding."""
@@ -166,6 +253,14 @@ def _one_hot_b(dtype, N, K, perm):
         b = np.zeros((N, K), np.uint16)
         b[np.arange(N), perm] = 0x3F80
         return {"b": b}
+    if dtype == "fp16":
+        b = np.zeros((N, K), np.uint16)
+        b[np.arange(N), perm] = 0x3C00
+        return {"b": b}
+    if dtype == "w4a8":
+        codes = np.zeros((N, K), np.uint8)
+        codes[np.arange(N), perm] = 1            # INT4 1
+        return {"b": codes[:, 0::2] | (codes[:, 1::2] << 4), "scale_b": np.exp2(np.arange(N) % 3 - 1).astype(np.float32)}
     codes = np.zeros((N, K), np.uint8)
     codes[np.arange(N), perm] = 2            # E2M1 1.0
     return {"b": codes[:, 0::2] | (codes[:, 1::2] << 4), "scale_b": np.full((N, K // 32), 127, np.uint8)}
@@ -181,7 +276,11 @@ PERM_CASES = [("int8", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=256, tile
               ("fp8", 16, 256, 1024, dict(kernel=2)),
               ("bf16", 256, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64)),
               ("mxfp4", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256)),
-              ("mxfp4", 16, 128, 1024, dict(kernel=2))]
+              ("mxfp4", 16, 128, 1024, dict(kernel=2)),
+              ("fp16", 128, 256, 320, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, pipeline=3)),
+              ("fp16", 128, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
+              ("w4a8", 16, 256, 2048, dict(kernel=2)),
+              ("w4a8", 32, 512, 1024, dict(kernel=2, tile_n=16, tile_k=128))]
 
 
 @pytest.mark.parametrize("case", PERM_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-k{c[4]['kernel']}")
@@ -192,14 +291,15 @@ def test_permutation_b_bit_exact(case):
     host = workloads.make_inputs(dtype, M, N, K, seed=5)
     perm = rng.integers(0, K, size=N)
     host.update(_one_hot_b(dtype, N, K, perm))
-    if dtype == "fp8":
+    if dtype in ("fp8", "w4a8"):
         host["scale_a"] = np.exp2(rng.integers(-3, 4, size=M)).astype(np.float32)
     out = gpu_run(dtype, host, opts)
     ref = oracle.gemm(dtype, host)
     if dtype == "int8":
         assert np.array_equal(out, ref)
     else:
-        assert np.array_equal(oracle.decode_bf16(out), ref), "one-hot B must select columns exactly"
+        dec = oracle.decode_f16 if dtype == "fp16" else oracle.decode_bf16
+        assert np.array_equal(dec(out), ref), "one-hot B must select columns exactly"
 
 
 def test_fp8_exhaustive_code_pairs_bit_exact():
@@ -275,6 +375,29 @@ def test_fp4_block_scale_placement_bit_exact(opts):
     out = gpu_run("mxfp4", host, opts)
     ref = oracle.gemm("mxfp4", host)
     assert np.array_equal(oracle.decode_bf16(out), ref)
+
+
+def test_fp16_single_products_round_to_nearest_even():
+    say("fp16 single products")
+    rng = np.random.default_rng(10)
+    M, N, K = 128, 256, 64
+    a = np.zeros((M, K), np.uint16)
+    b = np.zeros((N, K), np.uint16)
+    a[:, 9] = (rng.integers(0, 2 ** 16, M).astype(np.uint16) & 0x83FF) | 0x3800     # [0.5, 1) and negatives
+    b[:, 9] = (rng.integers(0, 2 ** 16, N).astype(np.uint16) & 0x83FF) | 0x3C00     # [1, 2)
+    host = {"a": a, "b": b}
+    for opts in (dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=16),
+                 dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3), dict(kernel=3)):
+        if opts.get("kernel") == 3:
+            host3 = {"a": np.zeros((256, K), np.uint16), "b": np.zeros((256, K), np.uint16)}
+            host3["a"][:128] = a
+            host3["b"][:] = b
+            out = gpu_run("fp16", host3, opts)
+            ref = oracle.gemm("fp16", host3)
+        else:
+            out = gpu_run("fp16", host, opts)
+            ref = oracle.gemm("fp16", host)
+        assert np.array_equal(oracle.decode_f16(out), oracle.f16_rne(ref)), opts
 
 
 # ---------------------------------------------------------------- determinism
