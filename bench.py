@@ -1,6 +1,7 @@
 """Benchmark of the preshuffle GEMM on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
+                    [--act none|relu|silu|gelu]
 
 A step is one GEMM call (A, preshuffled B and scales already resident in
 HBM) on the workload's synthetic inputs. The default workload is the FP8
@@ -13,7 +14,9 @@ One JSON line per workload carries the throughput, the roofline of the GEMM
 kernel (measured with HIP events on the launch stream over the timed
 region), the B preshuffle pass timed separately (a one-time weight
 preparation that the pages keep outside the per-call path), and the CPU
-oracle timed on a bounded sample on this host.
+oracle timed on a bounded sample on this host. With --act the GEMM runs with
+the fused epilogue (an fp32 bias per column plus the activation) through
+gemm_ex; the bytes then include the bias (4 N).
 """
 from __future__ import annotations
 
@@ -36,9 +39,11 @@ from oracle import formulas as F  # noqa: E402
 METRIC = "GEMM TFLOPS and % of dtype MFMA peak (large M); HBM GB/s and % at M=16"
 DEFAULT_WORKLOAD = "fp8_16x7168x2048"
 # MI355X published dense peaks (TFLOP/s or TOP/s) and HBM bandwidth (GB/s)
-PEAK_TFLOPS = {"int8": 5000.0, "fp8": 5000.0, "bf16": 2500.0, "mxfp4": 10100.0}
+PEAK_TFLOPS = {"int8": 5000.0, "fp8": 5000.0, "bf16": 2500.0, "fp16": 2500.0, "mxfp4": 10100.0,
+               "w4a8": 5000.0}   # W4A8 runs on the int8 matrix instructions
 PEAK_HBM_GBPS = 8000.0
-DTYPE_NAME = {"int8": "i8", "fp8": "f8e4m3", "bf16": "bf16", "mxfp4": "mxfp4_e2m1"}
+DTYPE_NAME = {"int8": "i8", "fp8": "f8e4m3", "bf16": "bf16", "fp16": "f16", "mxfp4": "mxfp4_e2m1",
+              "w4a8": "i8xi4"}
 ROTATE_BYTES = 640 << 20
 
 
@@ -46,21 +51,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def workload_numbers(name):
+def workload_numbers(name, act=None):
     dtype, M, N, K, seed, tile = workloads.CONFIGS[name]
     out_bytes = 4 if dtype == "int8" else 2
     flops = F.flops(M, N, K)
-    nbytes = F.bytes_moved(dtype, M, N, K, out_bytes=out_bytes)
+    nbytes = F.bytes_moved(dtype, M, N, K, out_bytes=out_bytes) + (4 * N if act else 0)
     ridge = PEAK_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBPS * 1e9)
     bound = "hbm" if flops / nbytes < ridge else "mfma"
     return dtype, M, N, K, seed, flops, nbytes, bound
 
 
-def cpu_baseline(name, host, budget_s=12.0):
+def cpu_baseline(name, host, budget_s=12.0, act=None):
     """Time the oracle (as it is) on a bounded sample of the workload."""
     import oracle
 
-    dtype, M, N, K, seed, flops, nbytes, bound = workload_numbers(name)
+    dtype, M, N, K, seed, flops, nbytes, bound = workload_numbers(name, act)
     try:
         from threadpoolctl import threadpool_info
 
@@ -73,7 +78,7 @@ def cpu_baseline(name, host, budget_s=12.0):
     sel = np.arange(rows)
     calls, t0 = 0, time.perf_counter()
     while True:
-        oracle.gemm(dtype, host, rows=sel)
+        oracle.gemm(dtype, host, rows=sel, act=act)
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s or (calls >= 1 and el * (calls + 1) / calls > 2 * budget_s):
@@ -91,16 +96,16 @@ def cpu_baseline(name, host, budget_s=12.0):
                       f"(decode + float64 matmul)"}
 
 
-def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib_mib=0):
+def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib_mib=0, act=None):
     import torch
 
     import dense_gemm_preshuffle_amd as gp
     from dense_gemm_preshuffle_amd import workload
 
-    dtype, M, N, K, seed, flops, nbytes, bound = workload_numbers(name)
+    dtype, M, N, K, seed, flops, nbytes, bound = workload_numbers(name, act)
     plan = gp.gemm_plan(dtype, M, N, K, opts)
-    log(f"[bench] {name}: plan {plan}")
-    host = workloads.make_inputs(dtype, M, N, K, seed)
+    log(f"[bench] {name}: plan {plan}" + (f", fused epilogue bias + {act}" if act else ""))
+    host = workloads.make_inputs(dtype, M, N, K, seed, bias=act is not None)
     dev = workload.to_device(dtype, host)
     stream = torch.cuda.current_stream()
 
@@ -124,12 +129,12 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
     for _ in range(R - 1):
         q = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in p0.items()}
         sets.append(q)
-    outs = [workload.run(dtype, s, opts=opts) for s in sets]
+    outs = [workload.run(dtype, s, opts=opts, act=act) for s in sets]
     torch.cuda.synchronize()
     log(f"[bench] {name}: {R} rotating input sets, {set_bytes / 2**20:.1f} MiB each")
 
     for i in range(warmup):
-        workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R])
+        workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R], act=act)
     torch.cuda.synchronize()
 
     # eager launches (host launch cost included)
@@ -137,7 +142,7 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(steps):
-        workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R])
+        workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R], act=act)
     t_end.record(stream)
     torch.cuda.synchronize()
     eager_ms = t_start.elapsed_time(t_end) / steps
@@ -149,7 +154,7 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(steps):
-                workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R])
+                workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R], act=act)
         graph.replay()
         torch.cuda.synchronize()
     torch.cuda.synchronize()
@@ -159,7 +164,7 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
         graph.replay()
     else:
         for i in range(steps):
-            workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R])
+            workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R], act=act)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -183,7 +188,8 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
         "dtype": DTYPE_NAME[dtype], "data": "synthetic",
         "config": {"workload": name, "M": M, "N": N, "K": K, "kernel": plan["kernel"],
                    "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]], "grid": plan["grid"],
-                   "epilogue": plan["epilogue"], "rotating_sets": R},
+                   "epilogue": plan["epilogue"], "fused_epilogue": f"bias+{act}" if act else None,
+                   "rotating_sets": R},
         "roofline": roof,
         "tflops": tflops, "gbps": gbps, "us_per_gemm": sec * 1e6,
         "preshuffle_b": {"us": pre_us, "GB/s": 2 * b_bytes / (pre_us * 1e-6) / 1e9,
@@ -193,7 +199,7 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
         "eager_us_per_gemm": eager_ms * 1e3,
         "host_wall_s": wall,
     }
-    tr = _traffic(name, plan)
+    tr = _traffic(name + (f"+{act}" if act else ""), plan)
     if tr is not None:
         roof["traffic"] = tr
     if calib_mib:
@@ -205,7 +211,7 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
             dst.copy_(src)
         torch.cuda.synchronize()
     if do_cpu:
-        line["cpu_baseline"] = cpu_baseline(name, host)
+        line["cpu_baseline"] = cpu_baseline(name, host, act=act)
     return line
 
 
@@ -240,6 +246,8 @@ def main():
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--opts", default=None, help="JSON gemm_opts override, e.g. '{\"tile_m\":64,...}'")
+    ap.add_argument("--act", default=None, choices=["none", "relu", "silu", "gelu"],
+                    help="run with the fused epilogue: a per-column bias, then this activation")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the GEMM here runs on a single MI355X and has no "
@@ -253,7 +261,7 @@ def main():
     opts = json.loads(args.opts) if args.opts else None
     for name in names:
         line = bench_one(name, args.steps, args.warmup, do_cpu=not args.no_cpu_baseline, opts=opts,
-                         use_graph=not args.eager, calib_mib=args.calib_copy)
+                         use_graph=not args.eager, calib_mib=args.calib_copy, act=args.act)
         print(json.dumps(line), flush=True)
 
 
