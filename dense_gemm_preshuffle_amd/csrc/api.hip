@@ -114,7 +114,11 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
   struct Cand { int tm, tn, tkb; };
   static const Cand i8[] = {{128, 256, 128}, {64, 256, 128}, {64, 128, 128}, {128, 128, 128},
                             {64, 64, 128}, {32, 64, 128}, {16, 64, 256}};
-  static const Cand fp8[] = {{128, 256, 128}, {64, 256, 128}, {32, 256, 256}, {32, 256, 128},
+  // FP8: 64 x 128 x 256 before 32 x 256 x 256: where both give one tile per
+  // CU (e.g. 512 x 4096), it pulls a third fewer bytes from L2 per FLOP
+  // ((64 + 128) vs (32 + 256) bytes per K byte); measured 15.4 vs 20.0 us on
+  // 512 x 4096 x 4096.
+  static const Cand fp8[] = {{128, 256, 128}, {64, 256, 128}, {64, 128, 256}, {32, 256, 256}, {32, 256, 128},
                              {128, 128, 128}, {64, 128, 128}, {16, 64, 512}};
   static const Cand b16[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {64, 128, 128},
                              {128, 256, 64}, {32, 128, 128}};
