@@ -96,7 +96,7 @@ def cpu_baseline(name, host, budget_s=12.0, act=None):
                       f"(decode + float64 matmul)"}
 
 
-def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib_mib=0, act=None):
+def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib_mib=0, act=None, data="randn"):
     import torch
 
     import dense_gemm_preshuffle_amd as gp
@@ -107,6 +107,11 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
     log(f"[bench] {name}: plan {plan}" + (f", fused epilogue bias + {act}" if act else ""))
     host = workloads.make_inputs(dtype, M, N, K, seed, bias=act is not None)
     dev = workload.to_device(dtype, host)
+    if data == "zeros":
+        # diagnostic only: the same launches on all-zero operands (no bit
+        # toggles in the matrix cores) to expose data-dependent clock throttling
+        for k in ("a", "b"):
+            dev[k].zero_()
     stream = torch.cuda.current_stream()
 
     # preshuffle pass, timed on its own
@@ -185,7 +190,8 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": DTYPE_NAME[dtype], "data": "synthetic",
+        "dtype": DTYPE_NAME[dtype],
+        "data": "synthetic" if data == "randn" else "synthetic, operands zeroed (power diagnostic, not a result)",
         "config": {"workload": name, "M": M, "N": N, "K": K, "kernel": plan["kernel"],
                    "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]], "grid": plan["grid"],
                    "epilogue": plan["epilogue"], "fused_epilogue": f"bias+{act}" if act else None,
@@ -210,7 +216,7 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
         for _ in range(10):
             dst.copy_(src)
         torch.cuda.synchronize()
-    if do_cpu:
+    if do_cpu and data == "randn":
         line["cpu_baseline"] = cpu_baseline(name, host, act=act)
     return line
 
@@ -246,6 +252,8 @@ def main():
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--opts", default=None, help="JSON gemm_opts override, e.g. '{\"tile_m\":64,...}'")
+    ap.add_argument("--data", default="randn", choices=["randn", "zeros"],
+                    help="zeros: same launches on all-zero A and B (diagnostic of data-dependent clocks)")
     ap.add_argument("--act", default=None, choices=["none", "relu", "silu", "gelu"],
                     help="run with the fused epilogue: a per-column bias, then this activation")
     args = ap.parse_args()
@@ -261,7 +269,7 @@ def main():
     opts = json.loads(args.opts) if args.opts else None
     for name in names:
         line = bench_one(name, args.steps, args.warmup, do_cpu=not args.no_cpu_baseline, opts=opts,
-                         use_graph=not args.eager, calib_mib=args.calib_copy, act=args.act)
+                         use_graph=not args.eager, calib_mib=args.calib_copy, act=args.act, data=args.data)
         print(json.dumps(line), flush=True)
 
 
