@@ -307,7 +307,7 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
   const int ms = p.kernel != GP_KERNEL_SPLITK ? p.ms : 16;
   const int kbm = kernel_mfma_kb(dt, ms);
   const int ob = in_dtype == GP_I8 ? 4 : 2;
-  const int bias_lds = dt == DT_I8 ? 0 : 1;   // the fused-epilogue bias is staged in LDS
+  const int bias_lds = 0;   // the plain variant; the fused-epilogue one stages tile_n floats of bias more
   out->kernel = p.kernel;
   out->mfma = ms;
   out->pipeline = p.kernel != GP_KERNEL_SPLITK ? (p.pipe ? p.pipe : 1) : 0;
@@ -334,7 +334,10 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     const bool apart = (p.tm * (p.tkb / 16)) % 256 != 0;
     const int stages = p.pipe ? p.pipe : 2;
     int abuf = stages * (p.tm * p.tkb + (apart ? 16 : 0));
-    if (dt == DT_FP4) abuf += stages * ((p.tm + p.tn) * (p.tkb / 16) + 16);  // staged E8M0 scales
+    if (dt == DT_FP4) {   // staged E8M0 scales: per stage, or a ring of 4-tile groups (2 slots + discard)
+      if (stages == 2 && p.tkb == 128) abuf += 3 * (4 * (p.tm + p.tn) * 8 + 16);
+      else abuf += stages * ((p.tm + p.tn) * (p.tkb / 16) + 16);
+    }
     const int cbytes = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
     out->lds_bytes = abuf > cbytes ? abuf : cbytes;
     if (dt == DT_FP8) out->lds_bytes += 256 * ((p.tm + 63) / 64 + p.tn / 64);  // FP8 scales

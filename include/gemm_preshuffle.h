@@ -113,7 +113,8 @@ typedef struct gemm_plan_info {
   int xcd_swizzle;                  /* 1 XCD-aware, 2 linear                    */
   int waves;                        /* waves per workgroup                      */
   int threads;                      /* per workgroup                            */
-  int lds_bytes;                    /* static LDS per workgroup                 */
+  int lds_bytes;                    /* static LDS per workgroup (without a fused
+                                       epilogue; with one, + 4 * tile_n)        */
   int64_t grid;                     /* workgroups                               */
   int64_t k_tiles;                  /* K tiles per workgroup (tile kernel)      */
   int64_t mfma_per_wave_tile;       /* MFMA instructions per wave per K tile    */

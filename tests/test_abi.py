@@ -101,8 +101,7 @@ def test_named_tiles_plan():
     assert p["mfma_per_wave_tile"] * 4 == F.mfma_per_tile_pages(64, 256, 128)
     assert p["grid"] == 128 and p["k_tiles"] == 32 and p["mfma"] == 16
     fp8_scales = 256 * (1 + 256 // 64)              # FP8 row / column scales staged in LDS
-    bias = 256 * 4                                  # fused-epilogue bias staged in LDS (tile_n floats)
-    assert p["lds_bytes"] == F.lds_bytes(64, 256, 128, 1) + fp8_scales + bias
+    assert p["lds_bytes"] == F.lds_bytes(64, 256, 128, 1) + fp8_scales
     p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, epilogue=1, mfma=16,
                                                      pipeline=1))
     assert p["grid"] == 2048 and p["k_tiles"] == 128
@@ -110,11 +109,11 @@ def test_named_tiles_plan():
     p = gp.gemm_plan("bf16", 8192, 8192, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, epilogue=1,
                                                      pipeline=1, mfma=32))
     assert p["mfma"] == 32 and p["mfma_per_wave_tile"] == 32   # 4 K16 steps x 4 x 2 (32x32 blocks)
-    assert p["lds_bytes"] == F.lds_bytes(128, 256, 64, 2) + bias
+    assert p["lds_bytes"] == F.lds_bytes(128, 256, 64, 2)
     p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=2))
-    assert p["lds_bytes"] == 64 * (256 * 2 + 16) + fp8_scales + bias   # padded CShuffle tile (above 3 stages of A)
+    assert p["lds_bytes"] == 64 * (256 * 2 + 16) + fp8_scales   # padded CShuffle tile (above 3 stages of A)
     p = gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=1, pipeline=3))
-    assert p["lds_bytes"] == 3 * 64 * 128 + fp8_scales + bias and p["pipeline"] == 3
+    assert p["lds_bytes"] == 3 * 64 * 128 + fp8_scales and p["pipeline"] == 3
     # default epilogue: CShuffle for tile_n >= 128 while two workgroups fit a CU
     assert gp.gemm_plan("bf16", 8192, 8192, 8192)["epilogue"] == gp.EPI_CSHUFFLE
     assert gp.gemm_plan("int8", 4096, 4096, 4096, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128))["epilogue"] == gp.EPI_DIRECT
@@ -135,7 +134,7 @@ def test_wide_kernel_plan():
     assert p["mfma_per_wave_tile"] * 8 * p["grid"] * p["k_tiles"] == p["mfma_total"]
     assert p["mfma_total"] == F.mfma_count_gfx950("bf16", 8192, 8192, 8192, p["mfma"])
     # A and B stages (256 rows each) or the padded bf16 C tile, whichever is larger
-    assert p["lds_bytes"] == max(p["pipeline"] * 512 * p["tile_k"] * 2, 256 * (256 * 2 + 16)) + 256 * 4
+    assert p["lds_bytes"] == max(p["pipeline"] * 512 * p["tile_k"] * 2, 256 * (256 * 2 + 16))
     q = gp.gemm_plan("int8", 512, 512, 512, dict(kernel=3, mfma=32))
     assert q["epilogue"] == gp.EPI_DIRECT and q["mfma"] == 32
     assert q["mfma_per_wave_tile"] * 8 * q["grid"] * q["k_tiles"] == q["mfma_total"]
@@ -228,3 +227,13 @@ def test_tile_must_fit_inside_the_problem():
     assert e.value.status == GP_ESHAPE
     # no tile fits a 48-column problem: the small-M kernel takes it for any M
     assert gp.gemm_plan("fp8", 200, 48, 1024)["kernel"] == gp.KERNEL_SPLITK
+
+
+def test_fp4_plan_lds_matches_scale_groups():
+    """MXFP4 with a 2-stage pipeline stages scales as a ring of 4-tile groups
+    (two slots and a discard slot of 4 x (TM+TN) x 8 bytes) beside the A stages."""
+    p = gp.gemm_plan("mxfp4", 4096, 4096, 8192)
+    assert p["pipeline"] == 2 and p["tile_k"] == 256
+    stages = 2 * p["tile_m"] * 128 + 3 * (4 * (p["tile_m"] + p["tile_n"]) * 8 + 16)
+    cshuffle = p["tile_m"] * (p["tile_n"] * 2 + 16) if p["epilogue"] == gp.EPI_CSHUFFLE else 0
+    assert p["lds_bytes"] == max(stages, cshuffle)
