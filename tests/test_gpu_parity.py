@@ -110,8 +110,6 @@ TILE_CASES = [
     ("bf16", 256, 256, 64, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=32, pipeline=2, epilogue=1)),
     ("bf16", 256, 512, 160, dict(kernel=1, tile_m=256, tile_n=256, tile_k=32, mfma=32, pipeline=3)),
     ("fp8", 256, 512, 640, dict(kernel=1, tile_m=256, tile_n=256, tile_k=128, pipeline=3)),
-    ("mxfp4", 256, 512, 768, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
-    ("mxfp4", 512, 256, 1024, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=3)),
     # wide kernel: 256x256 tiles, 8 waves, A and B through LDS; K-tile counts 1 .. 7
     ("bf16", 256, 256, 64, dict(kernel=3)),
     ("bf16", 512, 256, 320, dict(kernel=3)),
