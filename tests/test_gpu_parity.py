@@ -412,6 +412,26 @@ def test_bitwise_repeatable():
     assert np.array_equal(o1, o2)
 
 
+@pytest.mark.parametrize("dtype,M,N,K,act", [("fp8", 16, 7168, 2048, None), ("w4a8", 16, 7168, 2048, "gelu"),
+                                            ("bf16", 512, 512, 1024, None), ("mxfp4", 256, 512, 1024, None),
+                                            ("fp8", 512, 1024, 1024, "silu"), ("fp16", 300, 272, 512, None)])
+def test_bitwise_repeatable_20_runs(dtype, M, N, K, act):
+    """Twenty launches on the same inputs give bitwise-identical outputs: no
+    atomics, a fixed reduction order in every kernel."""
+    import torch
+
+    from dense_gemm_preshuffle_amd import workload
+
+    say(f"repeat x20 {dtype} {M}x{N}x{K} {act}")
+    host = workloads.make_inputs(dtype, M, N, K, seed=51, bias=act is not None)
+    p = workload.prepare(dtype, workload.to_device(dtype, host))
+    outs = [workload.run(dtype, p, act=act) for _ in range(20)]
+    torch.cuda.synchronize()
+    first = workload.to_host(outs[0])
+    for o in outs[1:]:
+        assert np.array_equal(workload.to_host(o), first)
+
+
 # ---------------------------------------------------------------- HIP graph replay
 def test_graph_replay_matches_eager():
     """Launches captured in a HIP graph give the eager result on every replay,
