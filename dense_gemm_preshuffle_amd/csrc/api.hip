@@ -41,20 +41,22 @@ int kdt(int dt) {
   }
 }
 
-struct TileVar { int dt, ms, tm, tn, tkb, pipe; };
+struct TileVar { int dt, ms, tm, tn, tkb, pipe, kg; };
 struct SplitVar { int dt, nb, waves, kch; };
 struct WideVar { int dt, ms, tkb, pipe; };
 
-#define GP_TILE_ENTRY(DT, MS, TM, TN, TKB, PIPE) {DT, MS, TM, TN, TKB, PIPE},
+#define GP_TILE_ENTRY(DT, MS, TM, TN, TKB, PIPE) {DT, MS, TM, TN, TKB, PIPE, 1},
+#define GP_TILE_KG2_ENTRY(DT, MS, TM, TN, TKB, PIPE) {DT, MS, TM, TN, TKB, PIPE, 2},
 #define GP_SPLIT_ENTRY(DT, NB, W, KCH) {DT, NB, W, KCH},
 #define GP_WIDE_ENTRY(DT, MS, TKB, PIPE) {DT, MS, TKB, PIPE},
-constexpr TileVar kTiles[] = {GP_TILE_ALL(GP_TILE_ENTRY)};
+constexpr TileVar kTiles[] = {GP_TILE_ALL(GP_TILE_ENTRY) GP_TILE_KG2_ALL(GP_TILE_KG2_ENTRY)};
 constexpr SplitVar kSplits[] = {GP_SPLITK_ALL(GP_SPLIT_ENTRY)};
 constexpr WideVar kWides[] = {GP_WIDE_ALL(GP_WIDE_ENTRY)};
 
-bool tile_compiled(int dt, int ms, int tm, int tn, int tkb, int pipe = -1) {
+bool tile_compiled(int dt, int ms, int tm, int tn, int tkb, int pipe = -1, int kg = 1) {
   for (const auto& v : kTiles)
-    if (v.dt == dt && v.ms == ms && v.tm == tm && v.tn == tn && v.tkb == tkb && (pipe < 0 || v.pipe == pipe))
+    if (v.dt == dt && v.ms == ms && v.tm == tm && v.tn == tn && v.tkb == tkb && (pipe < 0 || v.pipe == pipe) &&
+        v.kg == kg)
       return true;
   return false;
 }
@@ -84,6 +86,7 @@ struct Plan {
   int ms = 16;                  // MFMA block (16 or 32)
   int pipe = 0;                 // 0 VGPR-staged A, 2 .. 6 LDS DMA stages
   int tm = 0, tn = 0, tkb = 0;  // tile and wide kernels (tkb in bytes)
+  int kg = 1;                   // tile kernel: K groups of 4 waves
   int epi = EPI_DIRECT;
   int xcd = 1;
   int nb = 0, waves = 4, kch = 0;  // split-K kernel
@@ -285,6 +288,12 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     p->pipe = pick_pipe(dt, p->ms, p->tm, p->tn, p->tkb, o ? o->pipeline : 0);
     if (p->pipe < 0) return GP_ESHAPE;
   }
+  // K groups: 8 waves asked for (two groups of 4 splitting the K tiles)
+  if (o && o->waves && o->waves != 4) {
+    if (o->waves != 8 || (Kb / p->tkb) % 2 || !tile_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe, 2))
+      return GP_ESHAPE;
+    p->kg = 2;
+  }
   if (o && o->epilogue) {
     p->epi = o->epilogue;
   } else {
@@ -329,16 +338,17 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     out->tile_n = p.tn;
     out->tile_k = (int)((int64_t)p.tkb * 8 / bits);
     out->epilogue = p.epi;
-    out->waves = 4;
-    out->threads = 256;
+    out->waves = 4 * p.kg;
+    out->threads = 256 * p.kg;
     const bool apart = (p.tm * (p.tkb / 16)) % 256 != 0;
     const int stages = p.pipe ? p.pipe : 2;
-    int abuf = stages * (p.tm * p.tkb + (apart ? 16 : 0));
+    int abuf = p.kg * stages * (p.tm * p.tkb + (apart ? 16 : 0));
     if (dt == DT_FP4) {   // staged E8M0 scales: per stage, or a ring of 4-tile groups (2 slots + discard)
       if (stages == 2 && p.tkb == 128) abuf += 3 * (4 * (p.tm + p.tn) * 8 + 16);
       else abuf += stages * ((p.tm + p.tn) * (p.tkb / 16) + 16);
     }
-    const int cbytes = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
+    int cbytes = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
+    if (p.kg > 1 && p.tm * p.tn * 4 > cbytes) cbytes = p.tm * p.tn * 4;   // K-group reduction
     out->lds_bytes = abuf > cbytes ? abuf : cbytes;
     if (dt == DT_FP8) out->lds_bytes += 256 * ((p.tm + 63) / 64 + p.tn / 64);  // FP8 scales
     out->lds_bytes += bias_lds * p.tn * 4;
@@ -359,7 +369,8 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
   }
   // MFMAs the launch issues (the algorithmic (M/ms)(N/ms)(K/K_instr) when
   // the tile divides M and N; edge tiles and partial row blocks add to it)
-  out->mfma_total = out->grid * out->waves * out->k_tiles * out->mfma_per_wave_tile;
+  out->mfma_total = out->grid * out->waves * (out->k_tiles / (p.kernel == GP_KERNEL_TILE ? p.kg : 1)) *
+                    out->mfma_per_wave_tile;
 }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -410,11 +421,11 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
         default: e = hipErrorInvalidValue; break;
       }
     } else switch (dt) {
-      case DT_I8: e = launch_tile_i8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, false, t, s); break;
-      case DT_FP8: e = launch_tile_fp8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, fused, t, s); break;
-      case DT_BF16: e = launch_tile_bf16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, fused, t, s); break;
-      case DT_F16: e = launch_tile_f16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, fused, t, s); break;
-      case DT_FP4: e = launch_tile_fp4(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, fused, t, s); break;
+      case DT_I8: e = launch_tile_i8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, false, t, s); break;
+      case DT_FP8: e = launch_tile_fp8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, t, s); break;
+      case DT_BF16: e = launch_tile_bf16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, t, s); break;
+      case DT_F16: e = launch_tile_f16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, t, s); break;
+      case DT_FP4: e = launch_tile_fp4(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, t, s); break;
       default: e = hipErrorInvalidValue; break;
     }
   } else {

@@ -64,7 +64,12 @@ __device__ __forceinline__ void edge_shift(uint32_t& x0, uint32_t& skip, uint32_
 // PIPE LDS buffers and B register sets (prefetch PIPE-1 tiles ahead).
 // FUSED: the variant with the fused bias / activation epilogue; without it
 // the epilogue carries no bias slot and no activation code.
-template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED = false>
+// KG: K groups. With KG = 2 the workgroup is two groups of 4 waves that run
+// the same tile pipeline on the two halves of the K tiles, each with its own
+// LDS stages, and add their accumulators through LDS at the end: twice the
+// waves and loads in flight per CU at the same bytes per FLOP, for grids of
+// about one tile per CU (THREADS, WAVES and `tid` below are per group).
+template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED = false, int KG = 1>
 struct TileCfg {
   using S = Mma<DT, MS>;
   static constexpr int THREADS = 256;
@@ -113,7 +118,8 @@ struct TileCfg {
   static constexpr int SLB = PERTILE ? (TN + THREADS - 1) / THREADS : 0;   // B scale rows per thread
   static constexpr int SLOADS = SLA + SLB;
   static constexpr int SAREA = PERTILE ? SROWS * SCB + 16 : 0;   // + a spare slot for idle lanes
-  static constexpr int STAGE = ST * ABUF + ST * SAREA + 3 * GSLOT;   // ring of 2 + a discard slot
+  static constexpr int GSTAGE = ST * ABUF;                            // A stages of one K group
+  static constexpr int STAGE = KG * GSTAGE + ST * SAREA + 3 * GSLOT;  // scale ring: 2 + a discard slot
   // FP8 per-row / per-column scales, fetched into LDS by DMA when the kernel
   // starts (so the epilogue does not wait a memory round trip for them):
   // 256-byte blocks of A scales (TM floats, padded to 64) then B scales.
@@ -121,7 +127,10 @@ struct TileCfg {
   static constexpr int NSA = (DT == DT_FP8) ? (TM + 63) / 64 : 0;
   static constexpr int NSB = (DT == DT_FP8) ? TN / 64 : 0;
   static constexpr int NBI = (FUSED && DT != DT_I8) ? TN / 64 : 0;
-  static constexpr int FSC_OFF = (STAGE > CBYTES) ? STAGE : CBYTES;
+  // K groups: the second group's accumulators, [register chunk][lane] v4 entries
+  static constexpr int REDB = KG > 1 ? 256 * (TM * TN / 256) * 4 : 0;
+  static constexpr int EPIB = CBYTES > REDB ? CBYTES : REDB;
+  static constexpr int FSC_OFF = (STAGE > EPIB) ? STAGE : EPIB;
   static constexpr int BIAS_OFF = FSC_OFF + (NSA + NSB) * 256;
   static constexpr int LDS = BIAS_OFF + NBI * 256;
   // A fragments read ahead of their MFMAs: the most (2, 1 or 0) for which
@@ -141,6 +150,7 @@ struct TileCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(!ASYNC || (!APART && (TM * CPR) % (THREADS * 1) == 0), "LDS DMA covers whole 1 KiB wave blocks");
   static_assert(PIPE == 0 || (PIPE >= 2 && PIPE <= 6), "pipeline");
+  static_assert(KG == 1 || (KG == 2 && !NSC), "K groups: not with FP4's staged scales");
 };
 
 __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uint32_t& tn) {
@@ -165,15 +175,20 @@ __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uin
   }
 }
 
-template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED>
+template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED, int KG>
 // One workgroup per CU once the accumulators alone take more than half of the
-// 256 registers two workgroups would leave each wave; two otherwise.
-__global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_kernel(TileArgs p) {
-  using C = TileCfg<DT, MS, TM, TN, TKB, EPI, PIPE, FUSED>;
+// 256 registers two workgroups would leave each wave, or with two K groups;
+// two otherwise.
+__global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_kernel(TileArgs p) {
+  using C = TileCfg<DT, MS, TM, TN, TKB, EPI, PIPE, FUSED, KG>;
   using Acc = typename Mma<DT, MS>::Acc;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
 
-  const int tid = threadIdx.x;
+  // K group of this wave and the thread index inside its group; everything
+  // below indexes by the group-local thread and wave
+  const int grp = KG > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 8) : 0;
+  const int tid = threadIdx.x & 255;
+  char* const glds = lds + grp * C::GSTAGE;   // the group's A stages
   // wave index: uniform across the wave; readfirstlane puts it in a scalar
   // register so that offsets derived from it stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -188,7 +203,9 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
   edge_shift(m0, mskip, TM, p.M);
   edge_shift(n0, nskip, TN, p.N);
   const uint32_t Kb = p.Kb;
-  const int KT = (int)(Kb / TKB);
+  // K tiles of this group: [kt0, kt0 + KT) (the planner makes KG divide them)
+  const int KT = (int)(Kb / TKB) / KG;
+  const int kt0 = grp * KT;
 
   // Buffer resources based at this workgroup's first A row / first B block.
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * Kb, TM * Kb);
@@ -271,7 +288,7 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
     const __amdgpu_buffer_rsrc_t rfb = make_rsrc((const float*)p.sb + n0, TN * 4);
 #pragma unroll
     for (int i = 0; i < C::NSA + C::NSB; ++i) {
-      if (i % C::WAVES != wave) continue;
+      if (i % C::WAVES != wave || grp != 0) continue;
       char* dst = lds + C::FSC_OFF + i * 256;
       const bool is_a = i < C::NSA;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? rfa : rfb, (__attribute__((address_space(3))) void*)dst, 4,
@@ -283,7 +300,7 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
   if constexpr (C::NBI > 0) {
 #pragma unroll
     for (int i = 0; i < C::NBI; ++i) {
-      if ((C::NSA + C::NSB + i) % C::WAVES != wave) continue;
+      if ((C::NSA + C::NSB + i) % C::WAVES != wave || grp != 0) continue;
       if (p.bias) {
         const __amdgpu_buffer_rsrc_t rbi = make_rsrc(p.bias + n0, TN * 4);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rbi, (__attribute__((address_space(3))) void*)(lds + C::BIAS_OFF + i * 256),
@@ -311,14 +328,14 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
   };
   auto store_a = [&](int par) {
     if constexpr (C::ASYNC) return;
-    char* base = lds + par * C::ABUF;
+    char* base = glds + par * C::ABUF;
 #pragma unroll
     for (int i = 0; i < C::ALOADS; ++i)
       *(v4i*)(base + (a_on(i) ? a_wr_off(i) : (uint32_t)(TM * TKB))) = a_st[i];
   };
   auto load_a_dma = [&](int stage, int kt, int i) {
     if constexpr (C::ASYNC)
-      lds_dma16(p.a + (size_t)m0 * Kb, TM * Kb, lds + stage * C::ABUF + (i * C::WAVES + wave) * 1024,
+      lds_dma16(p.a + (size_t)m0 * Kb, TM * Kb, glds + stage * C::ABUF + (i * C::WAVES + wave) * 1024,
                 a_dma0 + kt * TKB + i * RPD * Kb);
   };
   // B load q of a tile: K step q / (NACC*FRAG), column block (q / FRAG) % NACC, piece q % FRAG
@@ -437,7 +454,7 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
   };
   // ds_read of A fragment (s, mi) from buffer par
   auto read_a = [&](int par, int s, int mi, v4i* af) {
-    const char* base = lds + par * C::ABUF;
+    const char* base = glds + par * C::ABUF;
 #pragma unroll
     for (int f = 0; f < C::FRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * MS * TKB);
   };
@@ -500,9 +517,10 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
   // wait for A at the end of an iteration counts on that order)
   auto loads = [&](auto stage_c, int kt_in, auto j0_c, auto j1_c) {
     constexpr int st = decltype(stage_c)::value;
-    // the tile index is wave-uniform; say so, so that every offset built from
-    // it stays in scalar registers (a VGPR offset would need a waterfall loop)
-    const int kt = __builtin_amdgcn_readfirstlane(kt_in);
+    // the tile index (made global: the group's first tile + the local one) is
+    // wave-uniform; say so, so that every offset built from it stays in
+    // scalar registers (a VGPR offset would need a waterfall loop)
+    const int kt = __builtin_amdgcn_readfirstlane(kt0 + kt_in);
     static_for<decltype(j0_c)::value, decltype(j1_c)::value>([&](auto j_c) {
       constexpr int j = decltype(j_c)::value;
       if constexpr (j < C::SLOADS) {
@@ -570,7 +588,45 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
     __syncthreads();
   }
 
-  // ---- epilogue ----
+  // ---- K groups: the second group's accumulators are added into the first's
+  // through LDS (the stages are dead: every DMA has landed and every wave
+  // passed the barrier above), in a fixed order ----
+  if constexpr (KG > 1) {
+    constexpr int NCH = C::MREP * C::NACC * (C::NREG / 4);   // 4-register chunks per lane
+    using V4 = std::conditional_t<DT == DT_I8, v4i, v4f>;
+    V4* red = (V4*)lds;
+    if (grp == 1) {
+#pragma unroll
+      for (int mi = 0; mi < C::MREP; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NACC; ++ni)
+#pragma unroll
+          for (int h = 0; h < C::NREG / 4; ++h) {
+            V4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * h + r];
+            red[((mi * C::NACC + ni) * (C::NREG / 4) + h) * 256 + tid] = v;
+          }
+    }
+    __syncthreads();
+    if (grp == 0) {
+#pragma unroll
+      for (int mi = 0; mi < C::MREP; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NACC; ++ni)
+#pragma unroll
+          for (int h = 0; h < C::NREG / 4; ++h) {
+            const V4 v = red[((mi * C::NACC + ni) * (C::NREG / 4) + h) * 256 + tid];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[mi][ni][4 * h + r] += v[r];
+          }
+    }
+    static_assert(NCH * 256 * 16 <= C::REDB, "K-group reduction buffer");
+    __syncthreads();
+  }
+
+  // ---- epilogue ---- (the first K group's waves store; a second group only
+  // takes part in the barriers)
   // Lane indices re-derived from an opaque copy of the thread index, so that
   // no epilogue address is computed before (and kept live through) the K loop.
   const int etid = opaque(tid);
@@ -626,8 +682,10 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
     }
   };
 
+  const bool storer = grp == 0;
   auto store_tile = [&](auto act_c) {
     if constexpr (EPI == EPI_DIRECT) {
+      if (!storer) return;
 #pragma unroll
       for (int mi = 0; mi < C::MREP; ++mi)
 #pragma unroll
@@ -643,6 +701,7 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
     } else {
       // CShuffle: stage the tile in LDS (the A buffers are dead after the last
       // barrier), then write whole rows with 16-byte stores.
+      if (storer)
 #pragma unroll
       for (int mi = 0; mi < C::MREP; ++mi)
 #pragma unroll
@@ -658,7 +717,7 @@ __global__ __launch_bounds__(256, (TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_
 #pragma unroll
       for (int i = 0; i < (TOTAL + C::THREADS - 1) / C::THREADS; ++i) {
         const int q = i * C::THREADS + etid;
-        if (TOTAL % C::THREADS != 0 && q >= TOTAL) break;
+        if ((TOTAL % C::THREADS != 0 && q >= TOTAL) || !storer) break;
         const int row = q / CH_ROW;
         const int ch = q % CH_ROW;
         const v4i v = *(const v4i*)(lds + row * C::CSTRIDE + ch * 16);

@@ -14,9 +14,9 @@ namespace gp {
 
 // Each returns hipErrorInvalidValue if the variant is not compiled.
 #define GP_DECLARE_TILE(NAME)                                                                       \
-  hipError_t launch_tile_##NAME(int ms, int tm, int tn, int tkb, int pipe, int epi, bool fused,    \
+  hipError_t launch_tile_##NAME(int ms, int tm, int tn, int tkb, int pipe, int epi, int kg, bool fused, \
                                 const TileArgs& a, hipStream_t s);                                  \
-  hipError_t launch_tile_##NAME##_fused(int ms, int tm, int tn, int tkb, int pipe, int epi,        \
+  hipError_t launch_tile_##NAME##_fused(int ms, int tm, int tn, int tkb, int pipe, int epi, int kg, \
                                         const TileArgs& a, hipStream_t s);
 #define GP_DECLARE_WIDE(NAME)                                                                       \
   hipError_t launch_wide_##NAME(int ms, int tkb, int pipe, bool fused, const TileArgs& a, hipStream_t s); \
@@ -33,17 +33,19 @@ hipError_t launch_splitk_i4(int nb, int waves, int kch, const SplitArgs& a, hipS
 }  // namespace gp
 
 // Bodies of one dtype's launch tables.
-#define GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, FU)                                           \
-  if (ms == MS && tm == TM && tn == TN && tkb == TKB && pipe == PIPE) {                            \
+#define GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, FU, KGV)                                      \
+  if (ms == MS && tm == TM && tn == TN && tkb == TKB && pipe == PIPE && kg == KGV) {               \
     const dim3 grid(a.tiles_m * a.tiles_n);                                                        \
     if (epi == EPI_CSHUFFLE)                                                                       \
-      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_CSHUFFLE, PIPE, FU>), grid, dim3(256), 0, s, a); \
+      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_CSHUFFLE, PIPE, FU, KGV>), grid, dim3(256 * KGV), 0, s, a); \
     else                                                                                           \
-      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_DIRECT, PIPE, FU>), grid, dim3(256), 0, s, a);   \
+      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_DIRECT, PIPE, FU, KGV>), grid, dim3(256 * KGV), 0, s, a);   \
     return hipGetLastError();                                                                      \
   }
-#define GP_TILE_CASE(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false)
-#define GP_TILE_CASE_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true)
+#define GP_TILE_CASE(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 1)
+#define GP_TILE_CASE_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true, 1)
+#define GP_TILE_CASE_KG2(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 2)
+#define GP_TILE_CASE_KG2_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true, 2)
 #define GP_SPLITK_CASE(DT, NB, W, KCH)                                                     \
   if (nb == NB && waves == W && kch == KCH) {                                              \
     const dim3 grid(a.N / (16 * NB), (a.M + 15) / 16);                                     \
@@ -59,11 +61,12 @@ hipError_t launch_splitk_i4(int nb, int waves, int kch, const SplitArgs& a, hipS
 #define GP_WIDE_CASE_FUSED(DT, MS, TKB, PIPE) GP_WIDE_CASE_IMPL(DT, MS, TKB, PIPE, true)
 
 // Plain launch tables of one dtype (the fused ones are in inst_<name>_fused.hip).
-#define GP_DEFINE_PLAIN(NAME, TILES, WIDES)                                                         \
-  hipError_t launch_tile_##NAME(int ms, int tm, int tn, int tkb, int pipe, int epi, bool fused,    \
+#define GP_DEFINE_PLAIN(NAME, TILES, KG2TILES, WIDES)                                               \
+  hipError_t launch_tile_##NAME(int ms, int tm, int tn, int tkb, int pipe, int epi, int kg, bool fused, \
                                 const TileArgs& a, hipStream_t s) {                                 \
-    if (fused) return launch_tile_##NAME##_fused(ms, tm, tn, tkb, pipe, epi, a, s);                \
+    if (fused) return launch_tile_##NAME##_fused(ms, tm, tn, tkb, pipe, epi, kg, a, s);            \
     TILES(GP_TILE_CASE)                                                                             \
+    KG2TILES(GP_TILE_CASE_KG2)                                                                      \
     return hipErrorInvalidValue;                                                                    \
   }                                                                                                 \
   hipError_t launch_wide_##NAME(int ms, int tkb, int pipe, bool fused, const TileArgs& a, hipStream_t s) { \
@@ -71,10 +74,11 @@ hipError_t launch_splitk_i4(int nb, int waves, int kch, const SplitArgs& a, hipS
     WIDES(GP_WIDE_CASE)                                                                             \
     return hipErrorInvalidValue;                                                                    \
   }
-#define GP_DEFINE_FUSED(NAME, TILES, WIDES)                                                         \
-  hipError_t launch_tile_##NAME##_fused(int ms, int tm, int tn, int tkb, int pipe, int epi,        \
+#define GP_DEFINE_FUSED(NAME, TILES, KG2TILES, WIDES)                                               \
+  hipError_t launch_tile_##NAME##_fused(int ms, int tm, int tn, int tkb, int pipe, int epi, int kg, \
                                         const TileArgs& a, hipStream_t s) {                         \
     TILES(GP_TILE_CASE_FUSED)                                                                       \
+    KG2TILES(GP_TILE_CASE_KG2_FUSED)                                                                \
     return hipErrorInvalidValue;                                                                    \
   }                                                                                                 \
   hipError_t launch_wide_##NAME##_fused(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s) { \

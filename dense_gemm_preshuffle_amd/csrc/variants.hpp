@@ -66,7 +66,16 @@
 #define GP_WIDE_F16(W) W(DT_F16, 16, 128, 2) W(DT_F16, 16, 64, 4)
 #define GP_WIDE_FP4(W)  /* FP4 runs on the 4-wave kernel */
 
+// Tile kernel with two K groups (8 waves, 512 threads): X2(dtype, mfma,
+// tile_m, tile_n, tile_k_bytes, pipe), for grids of about one tile per CU.
+#define GP_TILE_KG2_I8(X) X(DT_I8, 16, 64, 128, 128, 0)
+#define GP_TILE_KG2_FP8(X) X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 32, 256, 256, 3) X(DT_FP8, 16, 64, 256, 128, 3)
+#define GP_TILE_KG2_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3) X(DT_BF16, 16, 64, 128, 128, 0)
+#define GP_TILE_KG2_F16(X)
+#define GP_TILE_KG2_FP4(X)
+
 #define GP_TILE_ALL(X) GP_TILE_I8(X) GP_TILE_FP8(X) GP_TILE_BF16(X) GP_TILE_FP4(X) GP_TILE_F16(X)
+#define GP_TILE_KG2_ALL(X) GP_TILE_KG2_I8(X) GP_TILE_KG2_FP8(X) GP_TILE_KG2_BF16(X) GP_TILE_KG2_F16(X) GP_TILE_KG2_FP4(X)
 #define GP_SPLITK_ALL(Y) \
   GP_SPLITK_I8(Y) GP_SPLITK_FP8(Y) GP_SPLITK_BF16(Y) GP_SPLITK_FP4(Y) GP_SPLITK_F16(Y) GP_SPLITK_I4(Y)
 #define GP_WIDE_ALL(W) GP_WIDE_I8(W) GP_WIDE_FP8(W) GP_WIDE_BF16(W) GP_WIDE_FP4(W) GP_WIDE_F16(W)

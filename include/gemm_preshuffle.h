@@ -99,7 +99,9 @@ typedef struct gemm_opts {
   int epilogue;     /* GP_EPI_*                                          */
   int kernel;       /* GP_KERNEL_*                                       */
   int xcd_swizzle;  /* 0 auto, 1 XCD-aware grouped tile order, 2 linear  */
-  int waves;        /* split-K kernel: waves per workgroup (0 auto)      */
+  int waves;        /* split-K kernel: waves per workgroup (0 auto); tile
+                       kernel: 4, or 8 = two groups of 4 waves that split the
+                       K tiles and add their results (where compiled)      */
   int mfma;         /* tile kernel: MFMA block 16 (16x16) or 32 (32x32), 0 auto */
   int pipeline;     /* tile kernel: 1 A staged through VGPRs (2 stages), 2 .. 6 A
                        by LDS DMA with that many stages (where compiled), 0 auto */

@@ -237,3 +237,28 @@ def test_fp4_plan_lds_matches_scale_groups():
     stages = 2 * p["tile_m"] * 128 + 3 * (4 * (p["tile_m"] + p["tile_n"]) * 8 + 16)
     cshuffle = p["tile_m"] * (p["tile_n"] * 2 + 16) if p["epilogue"] == gp.EPI_CSHUFFLE else 0
     assert p["lds_bytes"] == max(stages, cshuffle)
+
+
+def test_k_group_plan():
+    """waves=8 on the tile kernel: two groups of 4 waves split the K tiles
+    (an even count), each with its own A stages; the issued MFMAs still
+    cover the problem exactly once."""
+    opts = dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3, waves=8)
+    p = gp.gemm_plan("fp8", 512, 4096, 4096, opts)
+    assert p["waves"] == 8 and p["threads"] == 512 and p["k_tiles"] == 16
+    assert p["mfma_total"] == F.mfma_count_gfx950("fp8", 512, 4096, 4096, p["mfma"])
+    q = gp.gemm_plan("fp8", 512, 4096, 4096, dict(opts, waves=4))
+    assert q["waves"] == 4 and q["mfma_total"] == p["mfma_total"]
+    # two groups' A stages (plus the FP8 scale blocks) against one group's
+    assert p["lds_bytes"] == 2 * 3 * 64 * 256 + 256 * (1 + 2)
+    assert q["lds_bytes"] == 3 * 64 * 256 + 256 * (1 + 2)
+    for bad_k in (3 * 256, 1280):   # odd K-tile counts
+        with pytest.raises(gp.GemmError) as e:
+            gp.gemm_plan("fp8", 512, 4096, bad_k, opts)
+        assert e.value.status == GP_ESHAPE
+    with pytest.raises(gp.GemmError):   # a tile without a two-group build
+        gp.gemm_plan("fp8", 512, 4096, 4096, dict(opts, tile_m=128, tile_n=256, tile_k=128))
+    with pytest.raises(gp.GemmError):   # FP4 stages its scales per group: not built
+        gp.gemm_plan("mxfp4", 512, 4096, 4096, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, waves=8))
+    with pytest.raises(gp.GemmError):
+        gp.gemm_plan("fp8", 512, 4096, 4096, dict(opts, waves=6))

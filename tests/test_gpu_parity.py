@@ -121,6 +121,14 @@ TILE_CASES = [
     ("fp8", 256, 256, 128, dict(kernel=3)),
     ("int8", 256, 512, 384, dict(kernel=3)),
     ("int8", 512, 256, 256, dict(kernel=3, mfma=32)),
+    # two K groups of 4 waves (waves=8): K-tile counts 2 .. 12 split in halves
+    ("fp8", 128, 256, 1024, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3, waves=8)),
+    ("fp8", 64, 384, 3072, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3, waves=8, epilogue=1)),
+    ("fp8", 64, 512, 512, dict(kernel=1, tile_m=32, tile_n=256, tile_k=256, pipeline=3, waves=8)),
+    ("fp8", 128, 512, 1536, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, pipeline=3, waves=8)),
+    ("int8", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128, pipeline=0, waves=8)),
+    ("bf16", 256, 512, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, pipeline=3, waves=8)),
+    ("bf16", 128, 256, 384, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64, pipeline=0, waves=8)),
     # small-M split-K kernel
     ("fp8", 16, 512, 2048, dict(kernel=2)),
     ("fp8", 32, 256, 1024, dict(kernel=2, tile_n=32)),
@@ -180,6 +188,8 @@ RAGGED_CASES = [
     ("mxfp4", 160, 288, 512, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32)),
     ("fp16", 70, 144, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64)),
     ("bf16", 300, 272, 128, dict(kernel=3)),
+    ("fp8", 100, 208, 1024, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3, waves=8)),
+    ("bf16", 200, 400, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, pipeline=3, waves=8)),
     ("fp8", 1, 512, 2048, dict(kernel=2)),
     ("fp8", 5, 256, 1024, dict(kernel=2, tile_n=16)),
     ("bf16", 17, 128, 512, dict(kernel=2)),
@@ -214,6 +224,8 @@ EPI_CASES = [
     ("fp8", 512, 512, 640, dict(kernel=3)),
     ("w4a8", 16, 512, 2048, dict(kernel=2)),
     ("bf16", 100, 272, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64)),   # with edge tiles
+    ("fp8", 100, 208, 1024, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3, waves=8)),
+    ("bf16", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64, pipeline=0, waves=8)),
 ]
 
 
