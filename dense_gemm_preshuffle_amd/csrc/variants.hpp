@@ -20,7 +20,7 @@
   X(DT_FP8, 16, 16, 64, 512, 0) X(DT_FP8, 16, 32, 256, 128, 0) X(DT_FP8, 16, 64, 128, 128, 0)               \
   X(DT_FP8, 16, 64, 256, 128, 0) X(DT_FP8, 16, 128, 128, 128, 0) X(DT_FP8, 16, 128, 256, 128, 0)            \
   X(DT_FP8, 16, 64, 256, 256, 0) X(DT_FP8, 16, 128, 256, 128, 2) X(DT_FP8, 16, 128, 256, 128, 3)  \
-  X(DT_FP8, 16, 64, 256, 128, 3) X(DT_FP8, 16, 32, 256, 128, 3) X(DT_FP8, 16, 256, 256, 128, 3)  \
+  X(DT_FP8, 16, 64, 256, 128, 3) X(DT_FP8, 16, 32, 256, 128, 3)  \
   X(DT_FP8, 16, 32, 128, 128, 3) X(DT_FP8, 16, 32, 128, 256, 3) X(DT_FP8, 16, 32, 256, 256, 3)  \
   X(DT_FP8, 16, 32, 256, 128, 4) X(DT_FP8, 16, 32, 256, 128, 6)   \
   X(DT_FP8, 16, 32, 128, 256, 4) X(DT_FP8, 16, 32, 128, 256, 6) X(DT_FP8, 16, 64, 256, 128, 4)   \
@@ -31,8 +31,8 @@
   X(DT_BF16, 32, 64, 128, 128, 0) X(DT_BF16, 32, 64, 256, 128, 0) X(DT_BF16, 32, 128, 128, 128, 0)          \
   X(DT_BF16, 32, 128, 256, 128, 0) X(DT_BF16, 32, 128, 256, 64, 0)                                \
   X(DT_BF16, 32, 128, 256, 128, 2) X(DT_BF16, 32, 128, 256, 128, 3) X(DT_BF16, 16, 128, 256, 128, 3) \
-  X(DT_BF16, 16, 256, 256, 128, 3) X(DT_BF16, 32, 256, 256, 128, 3) X(DT_BF16, 32, 256, 256, 128, 2) \
-  X(DT_BF16, 32, 256, 256, 64, 3)
+  X(DT_BF16, 32, 256, 256, 128, 3) X(DT_BF16, 32, 256, 256, 128, 2) \
+  X(DT_BF16, 32, 256, 256, 64, 3) X(DT_BF16, 16, 256, 256, 64, 3) X(DT_BF16, 16, 256, 256, 64, 4)
 
 #define GP_TILE_F16(X)                                                                             \
   X(DT_F16, 16, 32, 128, 128, 0) X(DT_F16, 16, 64, 128, 128, 0) X(DT_F16, 16, 64, 256, 128, 0)             \
@@ -41,11 +41,14 @@
 
 #define GP_TILE_FP4(X)                                                                             \
   X(DT_FP4, 16, 32, 256, 128, 0) X(DT_FP4, 16, 64, 128, 128, 0) X(DT_FP4, 16, 64, 256, 128, 0)              \
-  X(DT_FP4, 16, 128, 256, 128, 0) X(DT_FP4, 32, 64, 128, 128, 0) X(DT_FP4, 32, 64, 256, 128, 0)             \
-  X(DT_FP4, 32, 128, 128, 128, 0) X(DT_FP4, 32, 128, 256, 128, 0)                                  \
-  X(DT_FP4, 32, 128, 256, 128, 2) X(DT_FP4, 32, 128, 256, 128, 3)
-// (no 256 x 256 FP4 tile: its 256 accumulator registers per lane do not fit
-// beside the scaled MFMA's operands, and the compiler moved them to scratch)
+  X(DT_FP4, 32, 64, 128, 128, 0) X(DT_FP4, 32, 64, 256, 128, 0)                                    \
+  X(DT_FP4, 32, 128, 128, 128, 0) X(DT_FP4, 32, 128, 256, 128, 0) X(DT_FP4, 32, 128, 256, 128, 2)
+// (No FP4 128 x 256 tile with 16 x 16 blocks, nor with a 3-stage pipeline:
+// the first put its accumulators in scratch memory, the second spilled.)
+// (No 256 x 256 tile for FP4 or FP8, nor for BF16 with 16 x 16 blocks and
+// 128-byte K tiles: beside 256 accumulator registers per lane, their B stages
+// do not fit the remaining registers and the compiler moved values, or the
+// whole accumulator array, to scratch memory, at 50x the run time.)
 
 #define GP_SPLITK_I8(Y) Y(DT_I8, 1, 4, 64) Y(DT_I8, 1, 4, 256) Y(DT_I8, 2, 4, 256)
 #define GP_SPLITK_FP8(Y)                                                                           \

@@ -103,13 +103,13 @@ TILE_CASES = [
     ("fp8", 64, 384, 2560, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3, epilogue=1)),  # 10 K tiles
     ("mxfp4", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
     ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
-    ("mxfp4", 128, 256, 1024, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=3)),
+    ("mxfp4", 128, 256, 1280, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),   # 5 K tiles: two scale groups, the second partial
     # 256x256 tiles, one workgroup per CU (accumulators in AGPRs)
-    ("bf16", 256, 512, 192, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=3)),
+    ("bf16", 256, 512, 192, dict(kernel=1, tile_m=256, tile_n=256, tile_k=32, mfma=16, pipeline=3)),
+    ("bf16", 512, 256, 224, dict(kernel=1, tile_m=256, tile_n=256, tile_k=32, mfma=16, pipeline=4)),
     ("bf16", 512, 256, 320, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
     ("bf16", 256, 256, 64, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=32, pipeline=2, epilogue=1)),
     ("bf16", 256, 512, 160, dict(kernel=1, tile_m=256, tile_n=256, tile_k=32, mfma=32, pipeline=3)),
-    ("fp8", 256, 512, 640, dict(kernel=1, tile_m=256, tile_n=256, tile_k=128, pipeline=3)),
     # wide kernel: 256x256 tiles, 8 waves, A and B through LDS; K-tile counts 1 .. 7
     ("bf16", 256, 256, 64, dict(kernel=3)),
     ("bf16", 512, 256, 320, dict(kernel=3)),
