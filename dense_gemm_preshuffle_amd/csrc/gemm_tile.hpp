@@ -35,13 +35,13 @@
 namespace gp {
 
 struct TileArgs {
-  const char* a;      // [M][Kb]
+  const char* a;      // [M][Kb] (W4A8: [M][2 Kb])
   const char* b;      // preshuffled [N/16][Kb/64][4][16][16]
-  const void* sa;     // FP8: fp32 [M]; FP4: u8 [M][Kb/16]; else unused
-  const void* sb;     // FP8: fp32 [N]; FP4: u8 [N][Kb/16]; else unused
+  const void* sa;     // FP8, W4A8: fp32 [M]; FP4: u8 [M][Kb/16]; else unused
+  const void* sb;     // FP8, W4A8: fp32 [N]; FP4: u8 [N][Kb/16]; else unused
   const float* bias;  // fp32 [N] or null (fused epilogue; not INT8)
   char* c;            // [M][N] int32, bf16 or fp16
-  uint32_t M, N, Kb;  // Kb = bytes per row of A and B
+  uint32_t M, N, Kb;  // Kb = bytes per row of B (and of A, except W4A8: 2 Kb)
   uint32_t tiles_m, tiles_n;  // ceil(M / TM), ceil(N / TN)
   uint32_t xcd;       // 1: XCD-aware, grouped tile order
   int act;            // Act
@@ -74,24 +74,30 @@ struct TileCfg {
   using S = Mma<DT, MS>;
   static constexpr int THREADS = 256;
   static constexpr int WAVES = 4;
-  static constexpr int KB = S::KB;                        // K bytes per MFMA
-  static constexpr int FRAG = S::FRAG;                    // 16-byte pieces per lane per MFMA
+  // W4A8 (DT_I4): TKB counts bytes of B; A holds two bytes (int8) per B byte
+  // (two INT4), and one 16-byte B piece feeds two int8 MFMAs.
+  static constexpr int AKB = (DT == DT_I4) ? 2 : 1;        // A bytes per B byte of K
+  static constexpr int KB = S::KB;                        // B K bytes per MFMA step
+  static constexpr int FRAG = S::FRAG;                    // 16-byte B pieces per lane per step
+  static constexpr int AFRAG = (DT == DT_I4) ? 2 : FRAG;  // 16-byte A pieces per lane per step
+  static constexpr int TKA = TKB * AKB;                   // A bytes per row of one K tile
   static constexpr int KSTEPS = TKB / KB;
   static constexpr int MREP = TM / MS;
   static constexpr int NPW = TN / WAVES;
   static constexpr int NACC = NPW / MS;
   static constexpr int NREG = S::NREG;
-  static constexpr int CPR = TKB / 16;                    // 16-byte chunks per A row
+  static constexpr int CPR = TKA / 16;                    // 16-byte chunks per A row
   static constexpr int ACHUNKS = TM * CPR;
   static constexpr int ALOADS = (ACHUNKS + THREADS - 1) / THREADS;
   static constexpr bool APART = (ACHUNKS % THREADS) != 0;
   static constexpr bool ASYNC = PIPE != 0;
   static constexpr int ST = ASYNC ? PIPE : 2;              // pipeline stages
-  static constexpr int ABUF = TM * TKB + (APART ? 16 : 0);   // + a spare slot for idle lanes
+  static constexpr int ABUF = TM * TKA + (APART ? 16 : 0);   // + a spare slot for idle lanes
   static constexpr int OB = (DT == DT_I8) ? 4 : 2;        // output element bytes
+  static constexpr bool FSC = DT == DT_FP8 || DT == DT_I4;  // fp32 row / column scales
   static constexpr int CSTRIDE = TN * OB + 16;            // padded C row in LDS
   static constexpr int CBYTES = (EPI == EPI_CSHUFFLE) ? TM * CSTRIDE : 0;
-  static constexpr int SWP = (TKB >= 256) ? 1 : 256 / TKB;  // rows per 256-byte period
+  static constexpr int SWP = (TKA >= 256) ? 1 : 256 / TKA;  // rows per 256-byte period
   static constexpr int SWM = ((CPR < 16) ? CPR : 16) - 1;   // chunk xor mask
   static constexpr int NSC = (DT == DT_FP4) ? 1 : 0;
   // FP4 E8M0 scales of one K tile: one byte per 16 K-bytes (32 elements), so
@@ -120,12 +126,12 @@ struct TileCfg {
   static constexpr int SAREA = PERTILE ? SROWS * SCB + 16 : 0;   // + a spare slot for idle lanes
   static constexpr int GSTAGE = ST * ABUF;                            // A stages of one K group
   static constexpr int STAGE = KG * GSTAGE + ST * SAREA + 3 * GSLOT;  // scale ring: 2 + a discard slot
-  // FP8 per-row / per-column scales, fetched into LDS by DMA when the kernel
+  // FP8 / W4A8 per-row / per-column scales, fetched into LDS by DMA when the kernel
   // starts (so the epilogue does not wait a memory round trip for them):
   // 256-byte blocks of A scales (TM floats, padded to 64) then B scales.
   // The fused-epilogue bias (TN floats) follows them.
-  static constexpr int NSA = (DT == DT_FP8) ? (TM + 63) / 64 : 0;
-  static constexpr int NSB = (DT == DT_FP8) ? TN / 64 : 0;
+  static constexpr int NSA = FSC ? (TM + 63) / 64 : 0;
+  static constexpr int NSB = FSC ? TN / 64 : 0;
   static constexpr int NBI = (FUSED && DT != DT_I8) ? TN / 64 : 0;
   // K groups: the second group's accumulators, [register chunk][lane] v4 entries
   static constexpr int REDB = KG > 1 ? 256 * (TM * TN / 256) * 4 : 0;
@@ -139,10 +145,10 @@ struct TileCfg {
   // stops at 1: one FP8 fragment feeds NACC 32-cycle MFMAs, which covers an
   // LDS read on its own.
   static constexpr int ACCR = TM * TN / 256;
-  static constexpr int BREG = ST * KSTEPS * NACC * FRAG * 4;
+  static constexpr int BREG = ST * KSTEPS * NACC * FRAG * 4 + (DT == DT_I4 ? NACC * 8 : 0);  // + widened INT4
   static constexpr int SREG = NSC ? MREP + NACC + 2 * ST * (SLA + SLB) + 4 * (GLA + GLB) : 0;
   static constexpr int RBASE = (ACCR > 128 ? 0 : ACCR) + BREG + SREG;
-  static constexpr int RA = (FRAG == 1 && RBASE + 12 <= 236) ? 2 : (RBASE + 2 * FRAG * 4 <= 236) ? 1 : 0;
+  static constexpr int RA = (AFRAG == 1 && RBASE + 12 <= 236) ? 2 : (RBASE + 2 * AFRAG * 4 <= 236) ? 1 : 0;
   static_assert(TM % MS == 0 && NPW % MS == 0 && TN % 64 == 0, "tile shape");
   static_assert(TKB % KB == 0 && TKB >= 64, "tile_k bytes must be a multiple of the MFMA K bytes");
   static_assert(THREADS % CPR == 0, "A row chunks must divide the workgroup");
@@ -151,6 +157,7 @@ struct TileCfg {
   static_assert(!ASYNC || (!APART && (TM * CPR) % (THREADS * 1) == 0), "LDS DMA covers whole 1 KiB wave blocks");
   static_assert(PIPE == 0 || (PIPE >= 2 && PIPE <= 6), "pipeline");
   static_assert(KG == 1 || (KG == 2 && !NSC), "K groups: not with FP4's staged scales");
+  static_assert(DT != DT_I4 || MS == 16, "W4A8: 16 x 16 blocks");
 };
 
 __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uint32_t& tn) {
@@ -203,12 +210,13 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
   edge_shift(m0, mskip, TM, p.M);
   edge_shift(n0, nskip, TN, p.N);
   const uint32_t Kb = p.Kb;
+  const uint32_t Ka = Kb * C::AKB;   // bytes per row of A
   // K tiles of this group: [kt0, kt0 + KT) (the planner makes KG divide them)
   const int KT = (int)(Kb / TKB) / KG;
   const int kt0 = grp * KT;
 
   // Buffer resources based at this workgroup's first A row / first B block.
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * Kb, TM * Kb);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * Ka, TM * Ka);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.b + (size_t)(n0 / 16) * 16 * Kb, TN * Kb);
 
   // ---- per-lane constant offsets ----
@@ -216,7 +224,7 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
   constexpr int RPP = C::THREADS / C::CPR;  // A rows per pass of the workgroup
   const int arow0 = tid / C::CPR;
   const int ach = tid % C::CPR;
-  const uint32_t a_ld0 = arow0 * Kb + ach * 16;
+  const uint32_t a_ld0 = arow0 * Ka + ach * 16;
   // the XOR term of rows arow0 + i*RPP does not depend on i when RPP/SWP is a
   // multiple of the swizzle period; then the LDS write offset is a constant step
   constexpr bool AWR_STEP = ((RPP / C::SWP) % (C::SWM + 1)) == 0;
@@ -224,10 +232,10 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
 #pragma unroll
   for (int i = 0; i < (AWR_STEP ? 1 : C::ALOADS); ++i) {
     const int row = arow0 + i * RPP;
-    a_wr[i] = row * TKB + ((ach ^ ((row / C::SWP) & C::SWM)) * 16);
+    a_wr[i] = row * C::TKA + ((ach ^ ((row / C::SWP) & C::SWM)) * 16);
   }
   auto a_wr_off = [&](int i) -> uint32_t {
-    if constexpr (AWR_STEP) return a_wr[0] + i * RPP * TKB;
+    if constexpr (AWR_STEP) return a_wr[0] + i * RPP * C::TKA;
     else return a_wr[i];
   };
   // Lanes past the last A chunk (partial passes only) load from an offset
@@ -245,21 +253,26 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
   if constexpr (C::ASYNC) {
     const int pch = wave * 64 + lane;
     const int row = pch / C::CPR;
-    a_dma0 = row * Kb + (((pch % C::CPR) ^ ((row / C::SWP) & C::SWM)) * 16);
+    a_dma0 = row * Ka + (((pch % C::CPR) ^ ((row / C::SWP) & C::SWM)) * 16);
   }
   static_assert(!C::ASYNC || ((RPD / C::SWP) % (C::SWM + 1)) == 0, "DMA swizzle step");
-  // K byte (within one MFMA step) of the lane's 16-byte piece f
-  auto lane_k = [&](int f) -> int { return MS == 16 ? f * 64 + 16 * lgrp : 16 * lgrp; };
+  // A K byte (within one MFMA step) of the lane's 16-byte piece f. W4A8: the
+  // B piece of lane group g holds K elements [32g, 32g+32) of the step's 128,
+  // its low nibbles the first 16 (first MFMA), its high nibbles the rest.
+  auto lane_k = [&](int f) -> int {
+    if constexpr (DT == DT_I4) return 32 * lgrp + 16 * f;
+    return MS == 16 ? f * 64 + 16 * lgrp : 16 * lgrp;
+  };
   // A LDS -> VGPR: lane reads row mi*MS + lrow, chunk (s*KB + lane_k(f)) / 16.
   // The XOR term depends on the row only through lrow (MS*mi/SWP is a whole
   // number of swizzle periods), so one address per (s, f) serves every mi.
   const int swz = (lrow / C::SWP) & C::SWM;
-  uint32_t a_rd[C::KSTEPS][C::FRAG];
+  uint32_t a_rd[C::KSTEPS][C::AFRAG];
 #pragma unroll
   for (int s = 0; s < C::KSTEPS; ++s)
 #pragma unroll
-    for (int f = 0; f < C::FRAG; ++f)
-      a_rd[s][f] = lrow * TKB + ((((s * C::KB + lane_k(f)) / 16) ^ swz) * 16);
+    for (int f = 0; f < C::AFRAG; ++f)
+      a_rd[s][f] = lrow * C::TKA + ((((s * C::KB * C::AKB + lane_k(f)) / 16) ^ swz) * 16);
   // B: column c = wave*NPW + lrow of the wave's first MFMA block lies in
   // 16-column block c/16, lane j = c%16 of it; the lane's K piece is 16-byte
   // group g of a 64-byte K block: offset blk*16*Kb + k0*1024 + g*256 + j*16.
@@ -283,7 +296,7 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
 
   // FP8 scales and the bias -> LDS, before any operand load: block i by wave
   // i % WAVES, lane l carrying float l of the block (lanes past TM read zeros).
-  if constexpr (DT == DT_FP8) {
+  if constexpr (C::FSC) {
     const __amdgpu_buffer_rsrc_t rfa = make_rsrc((const float*)p.sa + m0, TM * 4);
     const __amdgpu_buffer_rsrc_t rfb = make_rsrc((const float*)p.sb + n0, TN * 4);
 #pragma unroll
@@ -324,19 +337,19 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
     for (int ni = 0; ni < C::NACC; ++ni) acc[mi][ni] = Acc{};
 
   auto load_a = [&](int kt, int i) {
-    if constexpr (!C::ASYNC) a_st[i] = buf_load16(ra, a_on(i) ? a_ld0 : kOOB, kt * TKB + i * RPP * Kb);
+    if constexpr (!C::ASYNC) a_st[i] = buf_load16(ra, a_on(i) ? a_ld0 : kOOB, kt * C::TKA + i * RPP * Ka);
   };
   auto store_a = [&](int par) {
     if constexpr (C::ASYNC) return;
     char* base = glds + par * C::ABUF;
 #pragma unroll
     for (int i = 0; i < C::ALOADS; ++i)
-      *(v4i*)(base + (a_on(i) ? a_wr_off(i) : (uint32_t)(TM * TKB))) = a_st[i];
+      *(v4i*)(base + (a_on(i) ? a_wr_off(i) : (uint32_t)(TM * C::TKA))) = a_st[i];
   };
   auto load_a_dma = [&](int stage, int kt, int i) {
     if constexpr (C::ASYNC)
-      lds_dma16(p.a + (size_t)m0 * Kb, TM * Kb, glds + stage * C::ABUF + (i * C::WAVES + wave) * 1024,
-                a_dma0 + kt * TKB + i * RPD * Kb);
+      lds_dma16(p.a + (size_t)m0 * Ka, TM * Ka, glds + stage * C::ABUF + (i * C::WAVES + wave) * 1024,
+                a_dma0 + kt * C::TKA + i * RPD * Ka);
   };
   // B load q of a tile: K step q / (NACC*FRAG), column block (q / FRAG) % NACC, piece q % FRAG
   auto load_b = [&](auto par_c, int kt, int q) {
@@ -456,7 +469,7 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
   auto read_a = [&](int par, int s, int mi, v4i* af) {
     const char* base = glds + par * C::ABUF;
 #pragma unroll
-    for (int f = 0; f < C::FRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * MS * TKB);
+    for (int f = 0; f < C::AFRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * MS * C::TKA);
   };
   // Hot-loop order of one K tile: the first RA A-fragment reads, then for
   // every A fragment i: in the first half of the tile an even share of the
@@ -484,7 +497,9 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
     constexpr int NF = C::KSTEPS * C::MREP;
     constexpr int RA = C::RA < NF ? C::RA : NF;
     constexpr int LH = NF > 1 ? NF / 2 : 1;  // groups that carry global loads
-    v4i af[RA + 1][C::FRAG];
+    v4i af[RA + 1][C::AFRAG];
+    // W4A8: the step's B pieces widened to int8 (once per step, at its first A fragment)
+    v4i blo[C::NACC * (DT == DT_I4) + (DT != DT_I4)], bhi[C::NACC * (DT == DT_I4) + (DT != DT_I4)];
 #pragma unroll
     for (int j = 0; j < RA; ++j) read_a(par, j / C::MREP, j % C::MREP, af[j]);
     fence();
@@ -496,10 +511,18 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
       if constexpr (i + RA < NF) read_a(par, (i + RA) / C::MREP, (i + RA) % C::MREP, af[(i + RA) % (RA + 1)]);
       fence();
       const v4i* a = af[i % (RA + 1)];
+      if constexpr (DT == DT_I4 && mi == 0) {
+#pragma unroll
+        for (int ni = 0; ni < C::NACC; ++ni) widen_int4(bfr[par][s][ni][0], blo[ni], bhi[ni]);
+      }
 #pragma unroll
       for (int ni = 0; ni < C::NACC; ++ni) {
         if constexpr (DT == DT_FP4) {
           acc[mi][ni] = mma<DT, MS, s>(bfr[par][s][ni], a, acc[mi][ni], psb[ni], psa[mi]);
+        } else if constexpr (DT == DT_I4) {
+          // the widened values are 16 x the INT4 ones; the epilogue divides by 16
+          acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(blo[ni], a[0], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bhi[ni], a[1], acc[mi][ni], 0, 0, 0);
         } else {
           acc[mi][ni] = mma<DT, MS>(bfr[par][s][ni], a, acc[mi][ni]);
         }
@@ -593,7 +616,7 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
   // passed the barrier above), in a fixed order ----
   if constexpr (KG > 1) {
     constexpr int NCH = C::MREP * C::NACC * (C::NREG / 4);   // 4-register chunks per lane
-    using V4 = std::conditional_t<DT == DT_I8, v4i, v4f>;
+    using V4 = std::conditional_t<DT == DT_I8 || DT == DT_I4, v4i, v4f>;
     V4* red = (V4*)lds;
     if (grp == 1) {
 #pragma unroll
@@ -646,7 +669,7 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
   // for the last tile's A. Every wave passed a barrier after that wait.
   v4f sbv[C::NACC][C::NREG / 4];
   float sav[C::MREP];
-  if constexpr (DT == DT_FP8) {
+  if constexpr (C::FSC) {
     const float* sa = (const float*)(lds + C::FSC_OFF);
     const float* sb = sa + C::NSA * 64;
 #pragma unroll
@@ -674,8 +697,10 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
       const v4f bv = bias4(ni, h);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = acc[mi][ni][4 * h + r];
-        if constexpr (DT == DT_FP8) x = (x * sav[mi]) * sbv[ni][h][r];
+        float x;
+        if constexpr (DT == DT_I4) x = (float)(acc[mi][ni][4 * h + r] >> 4);   // exact: a multiple of 16
+        else x = acc[mi][ni][4 * h + r];
+        if constexpr (C::FSC) x = (x * sav[mi]) * sbv[ni][h][r];
         v[r] = activate<A>(x + bv[r]);
       }
       emit(pack_out4<DT>(v));

@@ -22,7 +22,9 @@ namespace gp {
   hipError_t launch_wide_##NAME(int ms, int tkb, int pipe, bool fused, const TileArgs& a, hipStream_t s); \
   hipError_t launch_wide_##NAME##_fused(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s);
 GP_DECLARE_TILE(i8) GP_DECLARE_TILE(fp8) GP_DECLARE_TILE(bf16) GP_DECLARE_TILE(fp4) GP_DECLARE_TILE(f16)
+GP_DECLARE_TILE(i4)
 GP_DECLARE_WIDE(i8) GP_DECLARE_WIDE(fp8) GP_DECLARE_WIDE(bf16) GP_DECLARE_WIDE(f16) GP_DECLARE_WIDE(fp4)
+GP_DECLARE_WIDE(i4)
 hipError_t launch_splitk_i8(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
 hipError_t launch_splitk_fp8(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
 hipError_t launch_splitk_bf16(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);

@@ -14,7 +14,8 @@
 #define GP_TILE_I8(X)                                                                              \
   X(DT_I8, 16, 16, 64, 256, 0) X(DT_I8, 16, 32, 64, 128, 0) X(DT_I8, 16, 64, 64, 128, 0)                     \
   X(DT_I8, 16, 64, 128, 128, 0) X(DT_I8, 16, 64, 256, 128, 0) X(DT_I8, 16, 128, 128, 128, 0)                 \
-  X(DT_I8, 16, 128, 256, 128, 0) X(DT_I8, 32, 128, 256, 128, 0) X(DT_I8, 32, 64, 256, 128, 0)
+  X(DT_I8, 16, 128, 256, 128, 0) X(DT_I8, 32, 128, 256, 128, 0) X(DT_I8, 32, 64, 256, 128, 0)              \
+  X(DT_I8, 16, 64, 128, 256, 3) X(DT_I8, 16, 64, 256, 128, 3) X(DT_I8, 16, 128, 256, 128, 3)
 
 #define GP_TILE_FP8(X)                                                                             \
   X(DT_FP8, 16, 16, 64, 512, 0) X(DT_FP8, 16, 32, 256, 128, 0) X(DT_FP8, 16, 64, 128, 128, 0)               \
@@ -77,8 +78,16 @@
 #define GP_TILE_KG2_F16(X)
 #define GP_TILE_KG2_FP4(X)
 
-#define GP_TILE_ALL(X) GP_TILE_I8(X) GP_TILE_FP8(X) GP_TILE_BF16(X) GP_TILE_FP4(X) GP_TILE_F16(X)
-#define GP_TILE_KG2_ALL(X) GP_TILE_KG2_I8(X) GP_TILE_KG2_FP8(X) GP_TILE_KG2_BF16(X) GP_TILE_KG2_F16(X) GP_TILE_KG2_FP4(X)
+// W4A8 on the tile kernel (tile_k in bytes of B; A tiles are twice as long)
+#define GP_TILE_I4(X)                                                                              \
+  X(DT_I4, 16, 128, 256, 64, 3) X(DT_I4, 16, 64, 256, 64, 3) X(DT_I4, 16, 64, 128, 128, 3)         \
+  X(DT_I4, 16, 64, 128, 64, 3) X(DT_I4, 16, 32, 128, 64, 3) X(DT_I4, 16, 32, 64, 64, 0)
+#define GP_TILE_KG2_I4(X)
+#define GP_WIDE_I4(W)
+
+#define GP_TILE_ALL(X) GP_TILE_I8(X) GP_TILE_FP8(X) GP_TILE_BF16(X) GP_TILE_FP4(X) GP_TILE_F16(X) GP_TILE_I4(X)
+#define GP_TILE_KG2_ALL(X) GP_TILE_KG2_I8(X) GP_TILE_KG2_FP8(X) GP_TILE_KG2_BF16(X) GP_TILE_KG2_F16(X) GP_TILE_KG2_FP4(X) \
+  GP_TILE_KG2_I4(X)
 #define GP_SPLITK_ALL(Y) \
   GP_SPLITK_I8(Y) GP_SPLITK_FP8(Y) GP_SPLITK_BF16(Y) GP_SPLITK_FP4(Y) GP_SPLITK_F16(Y) GP_SPLITK_I4(Y)
 #define GP_WIDE_ALL(W) GP_WIDE_I8(W) GP_WIDE_FP8(W) GP_WIDE_BF16(W) GP_WIDE_FP4(W) GP_WIDE_F16(W)

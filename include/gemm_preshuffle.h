@@ -194,14 +194,17 @@ int gemm_f16(const void* a, const void* b_shuf, void* c, int64_t M, int64_t N, i
 
 /*
  * gemm_w4a8 -- INT4 weights with int8 activations (GEMM Optimization Guide
- * §8.2, INT4 bytes formula), for the memory-bound small-M regime.
+ * §8.2, INT4 bytes formula): half the weight bytes of INT8 in the
+ * memory-bound small-M regime.
  *   a        device [M][K] int8.
  *   b_shuf   from gemm_preshuffle_b(GP_I4) of B [N][K/2] packed INT4.
  *   scale_a  device fp32 [M]; scale_b device fp32 [N] (both required).
  *   c        device [M][N] bf16:
  *     C[m][n] = bf16_rne((acc[m][n] * scale_a[m]) * scale_b[n]),
- * acc = sum_k A[m][k] B[n][k] exact in int32. Runs on the small-M kernel
- * (GP_KERNEL_SPLITK) for any M; K % 512 == 0 and K <= 65536.
+ * acc = sum_k A[m][k] B[n][k] exact in int32. K % 128 == 0 and K <= 65536.
+ * M <= 32 runs on the small-M kernel (GP_KERNEL_SPLITK, which needs
+ * K % 512 == 0 with its 4 waves); larger M on the tile kernel, which widens
+ * each INT4 piece of B to int8 in registers for two int8 MFMAs.
  */
 int gemm_w4a8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b, void* c,
               int64_t M, int64_t N, int64_t K, const gemm_opts* opts, void* stream);

@@ -198,13 +198,20 @@ def test_w4a8_plan():
     assert p["kernel"] == gp.KERNEL_SPLITK
     assert p["mfma_total"] == F.mfma_count_gfx950("w4a8", 16, 7168, 2048)
     with pytest.raises(gp.GemmError) as e:
-        gp.gemm_plan("w4a8", 256, 256, 2048, dict(kernel=1))   # W4A8 runs on the small-M kernel only
+        gp.gemm_plan("w4a8", 512, 512, 2048, dict(kernel=3))   # no 256 x 256 W4A8 kernel
     assert e.value.status == GP_EDTYPE
     with pytest.raises(gp.GemmError) as e:
         gp.gemm_plan("w4a8", 16, 256, 2 * 65536)               # int32 range of the 16x widened products
     assert e.value.status == GP_ESHAPE
-    q = gp.gemm_plan("w4a8", 300, 512, 4096)                   # any M: 19 row blocks, the last partial
+    q = gp.gemm_plan("w4a8", 300, 512, 4096, dict(kernel=2))   # small-M kernel, any M: 19 row blocks
     assert q["grid"] == (512 // q["tile_n"]) * 19
+    # larger M: the tile kernel, two int8 MFMAs per 64-byte INT4 piece; A
+    # tiles (int8) are twice the bytes of the B tile's K extent
+    t = gp.gemm_plan("w4a8", 512, 4096, 4096)
+    assert t["kernel"] == gp.KERNEL_TILE and (t["tile_m"], t["tile_n"], t["tile_k"]) == (64, 128, 256)
+    assert t["mfma_total"] == F.mfma_count_gfx950("w4a8", 512, 4096, 4096)
+    assert t["lds_bytes"] == t["pipeline"] * 64 * 256 + 256 * (1 + 2)   # A stages + fp32 scale blocks
+    assert gp.gemm_plan("w4a8", 4096, 4096, 128)["k_tiles"] == 1     # K % 128 on the tile kernel
 
 
 @pytest.mark.parametrize("dtype,M,N,K", [("bf16", 100, 256, 256), ("fp8", 200, 272, 512), ("int8", 77, 208, 256),

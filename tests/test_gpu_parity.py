@@ -76,6 +76,9 @@ TILE_CASES = [
     ("int8", 128, 256, 384, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, mfma=32)),
     ("int8", 128, 512, 256, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, mfma=32, epilogue=2)),
     # A by LDS DMA, 2 or 3 pipeline stages, K-tile counts 1..5
+    ("int8", 128, 256, 768, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3)),
+    ("int8", 128, 512, 384, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, pipeline=3, epilogue=2)),
+    ("int8", 256, 512, 640, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, pipeline=3)),
     ("bf16", 128, 256, 64, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
     ("bf16", 128, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
     ("bf16", 256, 512, 192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
@@ -153,6 +156,14 @@ TILE_CASES = [
     ("w4a8", 16, 256, 4096, dict(kernel=2, tile_n=32, waves=8, tile_k=256)),
     ("w4a8", 48, 128, 512, dict(kernel=2, tile_k=128)),
     ("w4a8", 16, 128, 4096, dict(kernel=2, tile_n=32, tile_k=128)),   # 4 chunks per wave
+    # W4A8 on the tile kernel (tile_k in INT4 elements; A tiles twice the B bytes)
+    ("w4a8", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128, pipeline=3)),
+    ("w4a8", 256, 512, 1024, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128)),
+    ("w4a8", 128, 256, 768, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256)),        # 3 K tiles
+    ("w4a8", 64, 256, 384, dict(kernel=1, tile_m=32, tile_n=128, tile_k=128, epilogue=1)),
+    ("w4a8", 64, 128, 512, dict(kernel=1, tile_m=32, tile_n=64, tile_k=128)),          # A through VGPRs
+    ("w4a8", 256, 512, 640, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, epilogue=2)),
+    ("w4a8", 128, 384, 128, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128)),        # one K tile
 ]
 
 
@@ -196,6 +207,8 @@ RAGGED_CASES = [
     ("int8", 29, 64, 1024, dict(kernel=2)),
     ("mxfp4", 7, 128, 2048, dict(kernel=2)),
     ("w4a8", 3, 256, 2048, dict(kernel=2)),
+    ("w4a8", 150, 400, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128)),
+    ("w4a8", 100, 208, 1024, None),        # planner's choice: the tile kernel with edge tiles
     ("fp8", 200, 48, 1024, None),          # no tile fits 48 columns: the planner takes split-K
     ("bf16", 100, 272, 256, None),         # planner's own choice
 ]
@@ -226,6 +239,8 @@ EPI_CASES = [
     ("bf16", 100, 272, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64)),   # with edge tiles
     ("fp8", 100, 208, 1024, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3, waves=8)),
     ("bf16", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64, pipeline=0, waves=8)),
+    ("w4a8", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128)),
+    ("w4a8", 150, 400, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128, epilogue=1)),
 ]
 
 
@@ -293,7 +308,9 @@ PERM_CASES = [("int8", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=256, tile
               ("fp16", 128, 256, 320, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, pipeline=3)),
               ("fp16", 128, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
               ("w4a8", 16, 256, 2048, dict(kernel=2)),
-              ("w4a8", 32, 512, 1024, dict(kernel=2, tile_n=16, tile_k=128))]
+              ("w4a8", 32, 512, 1024, dict(kernel=2, tile_n=16, tile_k=128)),
+              ("w4a8", 128, 256, 768, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256)),
+              ("w4a8", 128, 512, 512, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128))]
 
 
 @pytest.mark.parametrize("case", PERM_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-k{c[4]['kernel']}")
