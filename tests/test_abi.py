@@ -157,11 +157,13 @@ def test_small_m_uses_split_k():
 def test_every_gpu_case_has_a_plan():
     """Every option set the GPU parity tests use is accepted by the planner
     (host-only check, so planner mistakes show up without a GPU)."""
-    from tests.test_gpu_parity import PERM_CASES, TILE_CASES
+    from tests.test_gpu_parity import EPI_CASES, FP4_PLACEMENT_OPTS, PERM_CASES, RAGGED_CASES, TILE_CASES
 
-    for dtype, M, N, K, opts in TILE_CASES + PERM_CASES:
+    for dtype, M, N, K, opts in TILE_CASES + PERM_CASES + RAGGED_CASES + EPI_CASES:
         p = gp.gemm_plan(dtype, M, N, K, opts)
         assert p["grid"] > 0, (dtype, M, N, K, opts)
+    for opts in FP4_PLACEMENT_OPTS:
+        gp.gemm_plan("mxfp4", 128, 256, 1024, opts)
     for opts in (dict(kernel=1, tile_m=64, tile_n=256, tile_k=256), dict(kernel=1, tile_m=128, tile_n=256, tile_k=256)):
         gp.gemm_plan("mxfp4", 128, 256, 1024, opts)
     gp.gemm_plan("mxfp4", 16, 64, 1024, dict(kernel=2))

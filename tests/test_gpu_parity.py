@@ -381,12 +381,15 @@ def test_fp4_exhaustive_codes_and_scales_bit_exact():
     assert np.array_equal(oracle.decode_bf16(out), oracle.gemm("mxfp4", host))
 
 
-@pytest.mark.parametrize("opts", [dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=16),
-                                  dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=16),
-                                  dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32),
-                                  dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, mfma=32),
-                                  dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2),
-                                  dict(kernel=2)], ids=["t64", "t128", "t128m32", "t64x128m32", "t128m32dma", "splitk"])
+FP4_PLACEMENT_OPTS = [dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=16),
+                      dict(kernel=1, tile_m=32, tile_n=256, tile_k=256, mfma=16),
+                      dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32),
+                      dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, mfma=32),
+                      dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2),
+                      dict(kernel=2)]
+
+
+@pytest.mark.parametrize("opts", FP4_PLACEMENT_OPTS, ids=["t64", "t32", "t128m32", "t64x128m32", "t128m32dma", "splitk"])
 def test_fp4_block_scale_placement_bit_exact(opts):
     say(f"fp4 scale placement {opts}")
     rng = np.random.default_rng(4)
