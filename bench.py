@@ -12,7 +12,8 @@ of the inputs, with R large enough that the copies together exceed 640 MB.
 
 One JSON line per workload carries the throughput, the roofline of the GEMM
 kernel (measured with HIP events on the launch stream over the timed
-region), the B preshuffle pass timed separately (a one-time weight
+region; for MFMA-bound shapes also the fraction of the dense peak at the
+shader clock sampled from sysfs while the same launches repeat), the B preshuffle pass timed separately (a one-time weight
 preparation that the pages keep outside the per-call path), and the CPU
 oracle timed on a bounded sample on this host. With --act the GEMM runs with
 the fused epilogue (an fp32 bias per column plus the activation) through
@@ -21,10 +22,13 @@ gemm_ex; the bytes then include the bias (4 N).
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import math
 import os
+import re
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -96,7 +100,8 @@ def cpu_baseline(name, host, budget_s=12.0, act=None):
                       f"(decode + float64 matmul)"}
 
 
-def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib_mib=0, act=None, data="randn"):
+def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib_mib=0, act=None, data="randn",
+              telemetry_s=0.4):
     import torch
 
     import dense_gemm_preshuffle_amd as gp
@@ -208,6 +213,18 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
     tr = _traffic(name + (f"+{act}" if act else ""), plan)
     if tr is not None:
         roof["traffic"] = tr
+    if telemetry_s > 0:
+        def replay():
+            if graph is not None:
+                graph.replay()
+            else:
+                for i in range(steps):
+                    workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R], act=act)
+        tel = telemetry(replay, telemetry_s)
+        line["telemetry"] = tel
+        if tel and bound == "mfma":
+            # the dense peak scales with the shader clock (2.4 GHz nominal)
+            roof["clock_normalised_frac"] = roof["achieved"] / (roof["peak"] * tel["sclk_mhz"] / 2400.0)
     if calib_mib:
         # a plain device-to-device copy of known size, for scaling the HBM
         # byte counters of a profiler run (read calib_mib MiB, write calib_mib MiB)
@@ -219,6 +236,71 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
     if do_cpu and data == "randn":
         line["cpu_baseline"] = cpu_baseline(name, host, act=act)
     return line
+
+
+def _gpu_sysfs():
+    """sysfs device directory of the GPU when the host has exactly one, else None."""
+    cards = [d for d in sorted(glob.glob("/sys/class/drm/card*/device")) if os.path.exists(os.path.join(d, "pp_dpm_sclk"))]
+    return cards[0] if len(cards) == 1 else None
+
+
+def _sclk_mhz(dev):
+    """Current shader clock: the pp_dpm_sclk line marked '*'."""
+    for line in open(os.path.join(dev, "pp_dpm_sclk")):
+        if line.rstrip().endswith("*"):
+            return float(re.search(r"(\d+)\s*[Mm][Hh]z", line).group(1))
+    return None
+
+
+def _power_w(dev, name="power1_input"):
+    files = glob.glob(os.path.join(dev, "hwmon", "hwmon*", name))
+    return int(open(files[0]).read()) / 1e6 if files else None
+
+
+def telemetry(replay, min_s=0.4):
+    """Shader clock and socket power while the timed launches run back to back.
+
+    `replay` runs the timed region once; it is repeated for at least min_s
+    seconds (after the timed measurement, so the measurement itself is not
+    disturbed) while a host thread reads sysfs every 2 ms. The first fifth
+    of the samples (clock ramp) is dropped; medians are reported. None when
+    the host exposes no single GPU in sysfs.
+    """
+    import torch
+
+    dev = _gpu_sysfs()
+    if dev is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                samples.append((_sclk_mhz(dev), _power_w(dev)))
+            except (OSError, ValueError, AttributeError):
+                pass
+            time.sleep(0.002)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_s:
+        replay()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    samples = samples[len(samples) // 5:]
+    clk = sorted(c for c, _ in samples if c)
+    pw = sorted(w for _, w in samples if w)
+    if not clk:
+        return None
+    try:
+        cap = _power_w(dev, "power1_cap")
+    except (OSError, ValueError):
+        cap = None
+    return {"sclk_mhz": clk[len(clk) // 2], "sclk_min_mhz": clk[0], "sclk_max_mhz": clk[-1],
+            "power_w": pw[len(pw) // 2] if pw else None, "power_cap_w": cap, "samples": len(samples),
+            "source": "sysfs pp_dpm_sclk and hwmon power1_input, sampled while the timed launches repeat"}
 
 
 def _traffic(name, plan):
@@ -256,6 +338,10 @@ def main():
                     help="zeros: same launches on all-zero A and B (diagnostic of data-dependent clocks)")
     ap.add_argument("--act", default=None, choices=["none", "relu", "silu", "gelu"],
                     help="run with the fused epilogue: a per-column bias, then this activation")
+    ap.add_argument("--telemetry-s", type=float, default=0.4, metavar="S",
+                    help="after timing, repeat the timed launches for S seconds while sampling the "
+                         "shader clock and power (0: skip; profiler runs use 0 so that the trace "
+                         "ends with the timed region)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the GEMM here runs on a single MI355X and has no "
@@ -269,7 +355,8 @@ def main():
     opts = json.loads(args.opts) if args.opts else None
     for name in names:
         line = bench_one(name, args.steps, args.warmup, do_cpu=not args.no_cpu_baseline, opts=opts,
-                         use_graph=not args.eager, calib_mib=args.calib_copy, act=args.act, data=args.data)
+                         use_graph=not args.eager, calib_mib=args.calib_copy, act=args.act, data=args.data,
+                         telemetry_s=args.telemetry_s)
         print(json.dumps(line), flush=True)
 
 

@@ -1,0 +1,51 @@
+"""Host-side parts of bench.py: the sysfs clock / power readers and the
+multi-GPU refusal (no GPU needed)."""
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _card(tmp_path, sclk_lines, power_uw=None, cap_uw=None):
+    dev = tmp_path / "device"
+    dev.mkdir()
+    (dev / "pp_dpm_sclk").write_text("".join(l + "\n" for l in sclk_lines))
+    if power_uw is not None:
+        hw = dev / "hwmon" / "hwmon3"
+        hw.mkdir(parents=True)
+        (hw / "power1_input").write_text(f"{power_uw}\n")
+        (hw / "power1_cap").write_text(f"{cap_uw}\n")
+    return str(dev)
+
+
+def test_current_clock_is_the_starred_line(tmp_path):
+    # idle: a separate current-level line; under load: one of the DPM levels
+    assert bench._sclk_mhz(_card(tmp_path, ["S: 112Mhz *", "0: 500Mhz", "1: 2400Mhz"])) == 112.0
+
+
+def test_clock_level_marked(tmp_path):
+    assert bench._sclk_mhz(_card(tmp_path, ["0: 500Mhz", "1: 1735Mhz *", "2: 2400Mhz"])) == 1735.0
+
+
+def test_no_marked_level_gives_none(tmp_path):
+    assert bench._sclk_mhz(_card(tmp_path, ["0: 500Mhz", "1: 2400Mhz"])) is None
+
+
+def test_power_microwatts_to_watts(tmp_path):
+    dev = _card(tmp_path, ["0: 500Mhz *"], power_uw=1_234_500_000, cap_uw=1_400_000_000)
+    assert bench._power_w(dev) == 1234.5
+    assert bench._power_w(dev, "power1_cap") == 1400.0
+
+
+def test_no_card_no_telemetry():
+    # this container has no GPU: no sysfs card, so the bench reports null telemetry
+    if bench._gpu_sysfs() is None:
+        assert bench.telemetry(lambda: None, 0.01) is None
+
+
+def test_more_than_one_gpu_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
