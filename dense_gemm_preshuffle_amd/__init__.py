@@ -44,6 +44,8 @@ DTYPES = {"int8": GP_I8, "fp8": GP_FP8_E4M3, "bf16": GP_BF16, "mxfp4": GP_FP4_E2
 _ELEM_BITS = {GP_I8: 8, GP_FP8_E4M3: 8, GP_BF16: 16, GP_FP4_E2M1: 4, GP_F16: 16, GP_I4: 4}   # of B
 _OUT = {GP_I8: GP_I32, GP_FP8_E4M3: GP_BF16, GP_BF16: GP_BF16, GP_FP4_E2M1: GP_BF16, GP_F16: GP_F16,
         GP_I4: GP_BF16}
+# gp_status value of a HIP runtime or launch error
+GP_EHIP = 5
 # gp_act values of the C ABI
 ACTS = {"none": 0, "relu": 1, "silu": 2, "gelu": 3}
 EPI_AUTO, EPI_DIRECT, EPI_CSHUFFLE = 0, 1, 2
@@ -53,7 +55,10 @@ KERNEL_AUTO, KERNEL_TILE, KERNEL_SPLITK, KERNEL_WIDE = 0, 1, 2, 3
 class GemmError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: status {status} ({gemm_status_string(status)})")
+        msg = f"{where}: status {status} ({gemm_status_string(status)})"
+        if status == GP_EHIP and _lib is not None:
+            msg += f" [{_lib.gemm_last_hip_error().decode()}]"
+        super().__init__(msg)
 
 
 class GemmLibraryMissing(ImportError):
@@ -104,6 +109,8 @@ def load_library():
     lib.gemm_plan.argtypes = [ci, i64, i64, i64, ctypes.POINTER(GemmOpts), ctypes.POINTER(GemmPlanInfo)]
     lib.gemm_status_string.argtypes = [ci]
     lib.gemm_status_string.restype = ctypes.c_char_p
+    lib.gemm_last_hip_error.argtypes = []
+    lib.gemm_last_hip_error.restype = ctypes.c_char_p
     for f in ("gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_f16", "gemm_w4a8", "gemm_ex",
               "gemm_plan"):
         getattr(lib, f).restype = ci

@@ -386,14 +386,29 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 // Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
 std::atomic<int> g_arch[64];
 
+// Last HIP status the library saw in this thread (reported by
+// gemm_last_hip_error), and the gp_status it maps to.
+thread_local hipError_t g_last_hip = hipSuccess;
+int hip_status(hipError_t e) {
+  g_last_hip = e;
+  return e == hipSuccess ? GP_OK : GP_EHIP;
+}
+// HIP keeps one "last error" per thread, set by any runtime call, including
+// calls the library did not make (the caller's own, or a framework's). It is
+// cleared right before each launch, so that the status read right after the
+// launch is the launch's own.
+void clear_last_error() { (void)hipGetLastError(); }
+
 int check_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return GP_EHIP;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
   if (dev < 0 || dev >= 64) return GP_EHIP;
   int v = g_arch[dev].load(std::memory_order_relaxed);
   if (v == 0) {
     hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GP_EHIP;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_status(e);
     v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
     g_arch[dev].store(v, std::memory_order_relaxed);
   }
@@ -404,6 +419,7 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
            const float* bias, int act, void* c, int64_t M, int64_t N, hipStream_t s) {
   const int dt = kdt(in_dtype);
   hipError_t e;
+  clear_last_error();
   if (p.kernel == GP_KERNEL_TILE || p.kernel == GP_KERNEL_WIDE) {
     TileArgs t;
     t.a = (const char*)a;
@@ -458,7 +474,7 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
       default: e = launch_splitk_fp4(p.nb, p.waves, p.kch, t, s); break;
     }
   }
-  return e == hipSuccess ? GP_OK : GP_EHIP;
+  return hip_status(e);
 }
 
 // B preshuffle: one thread per destination 16-byte chunk (writes coalesced;
@@ -539,6 +555,8 @@ using namespace gp;
 
 extern "C" {
 
+const char* gemm_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
+
 const char* gemm_status_string(int status) {
   switch (status) {
     case GP_OK: return "ok";
@@ -574,10 +592,11 @@ int gemm_preshuffle_b(const void* b, void* b_shuf, int64_t N, int64_t K, int dty
   const int r = check_device();
   if (r) return r;
   const uint32_t chunks = (uint32_t)(N * Kb / 16);
+  clear_last_error();
   hipLaunchKernelGGL(preshuffle_kernel, dim3((chunks + 255) / 256), dim3(256), 0, (hipStream_t)stream,
                      (const char*)b, (char*)b_shuf, (uint32_t)(Kb / 64), (uint32_t)Kb, chunks,
                      dtype == GP_I4 ? 1 : 0);
-  return hipGetLastError() == hipSuccess ? GP_OK : GP_EHIP;
+  return hip_status(hipGetLastError());
 }
 
 int gemm_a8w8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b, void* c,

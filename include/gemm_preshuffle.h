@@ -246,6 +246,15 @@ int gemm_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* op
 /* Static, human-readable description of a gp_status value. */
 const char* gemm_status_string(int status);
 
+/*
+ * Name of the HIP status behind the last GP_EHIP of the calling thread
+ * ("hipSuccess" when the library's last HIP call in this thread succeeded).
+ * Static string; thread-local state. Each launch clears HIP's per-thread last
+ * error right before it, so a GP_EHIP reports the launch's own status, not
+ * one left by an earlier runtime call of the caller.
+ */
+const char* gemm_last_hip_error(void);
+
 #ifdef __cplusplus
 }
 #endif

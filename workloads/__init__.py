@@ -48,6 +48,8 @@ CONFIGS = {
     # next rows: FP16 inputs (fp16 out) and INT4 weights with int8 activations
     "fp16_8192x8192x8192": ("fp16", 8192, 8192, 8192, 7, None),
     "w4a8_16x7168x2048": ("w4a8", 16, 7168, 2048, 6, None),
+    # W4A8 at a medium batch (the tile kernel's INT4 path), the FP8 medium shape
+    "w4a8_512x4096x4096": ("w4a8", 512, 4096, 4096, 8, None),
 }
 
 # activations of the fused epilogues (with a bias; "none" = bias only)
