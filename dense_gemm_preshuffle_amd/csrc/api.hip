@@ -184,27 +184,34 @@ int pick_chunk(int dt, int nb, int waves, int64_t kw) {
 }
 
 int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, const gemm_opts* o) {
-  const int waves = (o && o->waves > 0) ? o->waves : 4;
   if (o && o->tile_n > 0 && o->tile_n % 16) return GP_ESHAPE;
   if (o && o->tile_m > 0 && o->tile_m != 16) return GP_ESHAPE;
   if (o && o->tile_k > 0 && ((int64_t)o->tile_k * bits) % 8) return GP_ESHAPE;
-  if (Kb % waves) return GP_ESHAPE;
-  const int64_t kw = Kb / waves;
   const int user_kch = (o && o->tile_k > 0) ? (int)((int64_t)o->tile_k * bits / 8) : 0;
+  // waves splitting K: the caller's, else 4, else one wave (short K: fewer
+  // than 4 chunks of the type's smallest compiled size)
+  int wcand[2] = {4, 1};
+  int nw = 2;
+  if (o && o->waves > 0) { wcand[0] = o->waves; nw = 1; }
   // column blocks per workgroup: the caller's, else 2 (two blocks fill whole
   // 128-byte lines of a bf16 C row), else 1
   int cand[2] = {2, 1};
   int ncand = 2;
   if (o && o->tile_n > 0) { cand[0] = o->tile_n / 16; ncand = 1; }
-  for (int c = 0; c < ncand; ++c) {
-    const int nb = cand[c];
-    if (N % (16 * nb)) continue;
-    const int kch = user_kch ? user_kch : pick_chunk(dt, nb, waves, kw);
-    if (kch == 0 || kw % kch || !split_compiled(dt, nb, waves, kch)) continue;
-    p->nb = nb;
-    p->waves = waves;
-    p->kch = kch;
-    return GP_OK;
+  for (int w = 0; w < nw; ++w) {
+    const int waves = wcand[w];
+    if (Kb % waves) continue;
+    const int64_t kw = Kb / waves;
+    for (int c = 0; c < ncand; ++c) {
+      const int nb = cand[c];
+      if (N % (16 * nb)) continue;
+      const int kch = user_kch ? user_kch : pick_chunk(dt, nb, waves, kw);
+      if (kch == 0 || kw % kch || !split_compiled(dt, nb, waves, kch)) continue;
+      p->nb = nb;
+      p->waves = waves;
+      p->kch = kch;
+      return GP_OK;
+    }
   }
   return GP_ESHAPE;
 }
@@ -258,6 +265,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   const int64_t Ka = K * a_bits(in_dtype) / 8;
   if (N % 16 || Kb % 64) return GP_ESHAPE;
   if ((in_dtype == GP_FP4_E2M1 || in_dtype == GP_I4) && K % 128) return GP_ESHAPE;
+  if (in_dtype == GP_FP8_E4M3 && K % 128) return GP_ESHAPE;   // whole 16x16x128 MFMA steps
   // W4A8 accumulates 16 x the products in int32 (|a| <= 128, |b| <= 8)
   if (in_dtype == GP_I4 && K > 65536) return GP_ESHAPE;
   const int ob = in_dtype == GP_I8 ? 4 : 2;

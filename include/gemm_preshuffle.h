@@ -24,14 +24,19 @@
  *     in ELEMENTS; an MXFP4 or INT4 row of K elements is K/2 bytes (element
  *     2i in the low nibble of byte i).
  *   - Shapes: N % 16 == 0 and K * (bits of a B element) % 512 == 0 (the B
- *     layout); M is free. When the tile does not divide M or N, the edge
- *     tiles overlap their neighbours inside M x N (no padding is needed).
+ *     layout); FP8, MXFP4 and W4A8 also need K % 128 == 0 (whole MFMA K
+ *     steps); M is free. When the tile does not divide M or N, the edge
+ *     tiles overlap their neighbours inside M x N (no padding is needed);
+ *     N below one tile or a short K runs on the small-M kernel.
+ *   - Thread-local state: the HIP status behind the last GP_EHIP
+ *     (gemm_last_hip_error).
  *   - Alignment: every data pointer must be 16-byte aligned.
  *   - Errors: arguments are validated on the host before any HIP call; a
  *     non-zero gp_status is returned and nothing is launched. A failing
  *     launch returns GP_EHIP. No C++ exception crosses this interface.
  *   - Thread safety: no global mutable state besides a per-device cache of
- *     the device's architecture; calls from several threads are safe.
+ *     the device's architecture (and the thread-local HIP status above);
+ *     calls from several threads are safe.
  */
 #ifndef GEMM_PRESHUFFLE_H
 #define GEMM_PRESHUFFLE_H

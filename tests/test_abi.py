@@ -192,7 +192,7 @@ def test_gemm_ex_validation(lib):
     # named wrappers validate the same way
     assert lib.gemm_w4a8(FAKE, FAKE, None, S, FAKE, 16, 16, 512, None, None) == GP_EDTYPE
     assert lib.gemm_f16(FAKE, FAKE, None, 16, 16, 64, None, None) == GP_EINVAL
-    assert lib.gemm_w4a8(FAKE, FAKE, S, S, FAKE, 16, 16, 384, None, None) == GP_ESHAPE   # K % 128 (INT4 layout)
+    assert lib.gemm_w4a8(FAKE, FAKE, S, S, FAKE, 16, 16, 320, None, None) == GP_ESHAPE   # K % 128 (INT4 layout)
 
 
 def test_w4a8_plan():
@@ -271,3 +271,18 @@ def test_k_group_plan():
         gp.gemm_plan("mxfp4", 512, 4096, 4096, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, waves=8))
     with pytest.raises(gp.GemmError):
         gp.gemm_plan("fp8", 512, 4096, 4096, dict(opts, waves=6))
+
+
+def test_degenerate_shapes_plan():
+    """One 16-column block and the shortest K of each type run on the
+    small-M kernel with one wave; FP8 needs whole 128-element MFMA steps."""
+    for dtype, M, N, K in [("int8", 1, 16, 64), ("fp8", 1, 16, 128), ("bf16", 1, 16, 32), ("fp16", 3, 16, 32),
+                           ("mxfp4", 1, 16, 128), ("w4a8", 1, 16, 128), ("bf16", 1000, 16, 64)]:
+        p = gp.gemm_plan(dtype, M, N, K)
+        assert p["kernel"] == gp.KERNEL_SPLITK and p["waves"] == 1, (dtype, p)
+        assert p["mfma_total"] * F.flops_per_mfma_gfx950(dtype, 16) >= F.flops(M, N, K)
+    q = gp.gemm_plan("fp8", 16, 7168, 2048)           # the M=16 shape keeps 4 waves
+    assert q["waves"] == 4
+    with pytest.raises(gp.GemmError) as e:
+        gp.gemm_plan("fp8", 16, 256, 64)               # half an FP8 MFMA step
+    assert e.value.status == GP_ESHAPE

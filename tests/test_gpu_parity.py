@@ -210,6 +210,20 @@ RAGGED_CASES = [
     ("w4a8", 150, 400, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128)),
     ("w4a8", 100, 208, 1024, None),        # planner's choice: the tile kernel with edge tiles
     ("fp8", 200, 48, 1024, None),          # no tile fits 48 columns: the planner takes split-K
+    # degenerate: one 16-column block, the shortest K of each type (one wave,
+    # one chunk). bf16 outputs keep >= 256 elements: the normwise bound of
+    # 2e-3 sits just above the RMS of bf16 rounding alone (about 1.7e-3), so
+    # a handful of outputs can cross it with an exact accumulator.
+    ("int8", 1, 16, 64, None),
+    ("int8", 16, 16, 64, None),
+    ("fp8", 16, 16, 128, None),
+    ("fp8", 300, 16, 256, None),
+    ("bf16", 16, 16, 32, None),
+    ("bf16", 1000, 16, 64, None),
+    ("fp16", 3, 16, 32, None),
+    ("mxfp4", 16, 16, 128, None),
+    ("w4a8", 16, 16, 128, None),
+    ("bf16", 33, 48, 96, None),
     ("bf16", 100, 272, 256, None),         # planner's own choice
 ]
 
