@@ -115,8 +115,10 @@ int pick_ms(int dt, int tm, int tn, int tkb, int want) {
 // large 128x256x64 elements, FP4 64-128 x 256 x 256 elements.
 int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) {
   struct Cand { int tm, tn, tkb; };
+  // (the 64-byte K tiles at the ends of the lists serve K not a multiple of
+  // the larger ones: one 64-byte K block is the layout's granularity)
   static const Cand i8[] = {{128, 256, 128}, {64, 256, 128}, {64, 128, 256}, {64, 128, 128}, {128, 128, 128},
-                            {64, 64, 128}, {32, 64, 128}, {16, 64, 256}};
+                            {64, 64, 128}, {32, 64, 128}, {16, 64, 256}, {128, 256, 64}, {64, 128, 64}};
   // FP8: 64 x 128 x 256 before 32 x 256 x 256: where both give one tile per
   // CU (e.g. 512 x 4096), it pulls a third fewer bytes from L2 per FLOP
   // ((64 + 128) vs (32 + 256) bytes per K byte); measured 15.4 vs 20.0 us on
@@ -124,9 +126,9 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
   static const Cand fp8[] = {{128, 256, 128}, {64, 256, 128}, {64, 128, 256}, {32, 256, 256}, {32, 256, 128},
                              {128, 128, 128}, {64, 128, 128}, {16, 64, 512}};
   static const Cand b16[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {64, 128, 128},
-                             {128, 256, 64}, {32, 128, 128}};
+                             {128, 256, 64}, {32, 128, 128}, {64, 128, 64}};
   static const Cand fp4[] = {{128, 256, 128}, {64, 256, 128}, {128, 128, 128}, {32, 256, 128},
-                             {64, 128, 128}};
+                             {64, 128, 128}, {128, 256, 64}, {64, 128, 64}};
   // W4A8: tile_k in bytes of B (64 bytes = 128 INT4); A tiles twice as long
   static const Cand i4[] = {{128, 256, 64}, {64, 256, 64}, {64, 128, 128}, {64, 128, 64}, {32, 128, 64},
                             {32, 64, 64}};

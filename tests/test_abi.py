@@ -302,3 +302,14 @@ def test_degenerate_shapes_plan():
     with pytest.raises(gp.GemmError) as e:
         gp.gemm_plan("fp8", 16, 256, 64)               # half an FP8 MFMA step
     assert e.value.status == GP_ESHAPE
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [("int8", 512, 4096, 4160), ("fp16", 512, 4096, 4128),
+                                         ("mxfp4", 512, 4096, 4224), ("bf16", 8192, 8192, 8224)])
+def test_k_not_a_multiple_of_the_large_tiles(dtype, M, N, K):
+    """K a whole number of 64-byte layout blocks but not of 128: the tile
+    kernel with 64-byte K tiles, not the small-M kernel."""
+    p = gp.gemm_plan(dtype, M, N, K)
+    assert p["kernel"] == gp.KERNEL_TILE and p["grid"] >= 64
+    assert p["tile_k"] * {"int8": 8, "fp16": 16, "bf16": 16, "mxfp4": 4}[dtype] // 8 == 64
+    assert p["mfma_total"] == F.mfma_count_gfx950(dtype, M, N, K, p["mfma"])

@@ -210,6 +210,15 @@ RAGGED_CASES = [
     ("w4a8", 150, 400, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128)),
     ("w4a8", 100, 208, 1024, None),        # planner's choice: the tile kernel with edge tiles
     ("fp8", 200, 48, 1024, None),          # no tile fits 48 columns: the planner takes split-K
+    # K a multiple of one 64-byte block but not of the larger K tiles: 64-byte
+    # K tiles (planner's choice, and named)
+    ("int8", 128, 256, 320, None),
+    ("fp16", 128, 256, 160, None),
+    ("mxfp4", 128, 256, 384, None),
+    ("int8", 100, 208, 448, None),
+    ("mxfp4", 256, 512, 384, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, mfma=16)),
+    ("fp16", 256, 512, 96, dict(kernel=1, tile_m=128, tile_n=256, tile_k=32)),
+    ("int8", 256, 512, 192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64)),
     # degenerate: one 16-column block, the shortest K of each type (one wave,
     # one chunk). bf16 outputs keep >= 256 elements: the normwise bound of
     # 2e-3 sits just above the RMS of bf16 rounding alone (about 1.7e-3), so
