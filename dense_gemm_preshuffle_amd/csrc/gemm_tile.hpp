@@ -3,12 +3,17 @@
 // Structure (GEMM Optimization Guide §1-§7, Kernel Tuning Guide §1-§6):
 //   * one workgroup = 4 waves x 64 lanes computes a TM x TN tile of C; the
 //     waves split TN (each owns TN/4 columns) and share the A tile (§1.1);
-//   * A goes global -> VGPR -> LDS, into one of two LDS buffers (ping-pong,
-//     §2), with an XOR swizzle on 16-byte chunks (§3);
-//   * B goes global -> VGPR directly from the preshuffled layout (§4.2);
-//   * the next K tile's A and B loads are issued before the current tile's
-//     MFMAs (register double buffer for B, loop-carried, §4.1-§4.4); one
-//     barrier per K tile;
+//     with KG = 2, two such groups split the K tiles and add their results;
+//   * A goes global -> VGPR -> LDS into one of two LDS buffers (ping-pong,
+//     §2; PIPE = 0), or global -> LDS by the buffer-load LDS DMA into PIPE
+//     buffers (async copy, Kernel Tuning Guide §4; PIPE = 2 .. 6), with an
+//     XOR swizzle on 16-byte chunks (§3);
+//   * B goes global -> VGPR directly from the preshuffled layout (§4.2), in
+//     one register set per pipeline stage;
+//   * the loads of the tile PIPE-1 ahead are issued during the current
+//     tile's MFMAs (loop-carried, §4.1-§4.4); one barrier per K tile;
+//   * W4A8: each INT4 B piece is widened in registers to two int8 operands
+//     and feeds two int8 MFMAs; the A tile holds two bytes per B byte;
 //   * epilogue: direct store or CShuffle through LDS (§7), with the fused
 //     bias and activation of Kernel Tuning Guide §6;
 //   * M and N need not be multiples of the tile: an edge tile is moved back
@@ -18,8 +23,8 @@
 //
 // Differences from the pages' kernel, for gfx950:
 //   * MS x MS MFMA blocks with MS = 16 or 32 (see Mma<> in gp_common.hpp):
-//     the K-doubled gfx950 instructions, and the 32x32 forms for BF16 / FP4,
-//     which issue at twice the rate of the 16x16 forms on this part;
+//     the K-doubled gfx950 instructions, and the 32x32 forms (INT8, BF16,
+//     FP16, FP4: twice the FLOPs per instruction, fewer operand reads);
 //   * the MFMA takes B as its first operand and A as its second, so a lane
 //     ends up holding runs of 4 consecutive COLUMNS of one row of C; the
 //     direct store is then one 8-byte (bf16) or 16-byte (int32) store;

@@ -173,8 +173,9 @@ __device__ v16f mfma_scale_32x32x64_v4(v4i a, v4i b, v16f c, int cbsz, int blgp,
 //            lane group l/16; result D[4*(l/16)+r][l%16] in 4 registers.
 //   MS = 32: lane l supplies row/column l%32 and the 16-byte K piece of lane
 //            group l/32; result D[8*i+4*(l/32)+j][l%32] in register 4*i+j.
-// On gfx950 the 32x32 BF16 (32x32x16) and FP4 (32x32x64) forms issue at twice
-// the rate of their 16x16 forms; FP8 16x16x128 already runs at full rate.
+// A 32x32 form (BF16 32x32x16, FP4 32x32x64, ...) does twice the FLOPs of
+// the 16x16 form per instruction and reads fewer operand bytes per FLOP; the
+// counters show 16 issue cycles per BF16 16x16x32 and 32 per FP8 16x16x128.
 template <int DT, int MS> struct Mma;
 template <int DT> struct Mma<DT, 16> {
   static constexpr int KB = Traits<DT>::KB;     // K bytes per instruction
