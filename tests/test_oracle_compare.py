@@ -41,6 +41,20 @@ def test_single_wrong_element_detected():
     assert not m["ok"] and m["elem_floored"] > 0.04
 
 
+def test_elementwise_bound_fails_alone():
+    """One element 5% off in a large bf16-exact result: the normwise error
+    stays far inside its bound, so only the elementwise bound can reject it."""
+    rng = np.random.default_rng(3)
+    r = rng.integers(-64, 65, size=(256, 256)).astype(np.float64)   # exact in bf16
+    r[r == 0] = 1.0
+    r[100, 200] = 80.0
+    c = r.copy()
+    c[100, 200] = 84.0                          # 5 % off, exact in bf16
+    m = compare_bf16(_to_bits(c), r)
+    assert m["normwise"] < 1e-3 and abs(m["elem_floored"] - 0.05) < 1e-12
+    assert not m["ok"]
+
+
 def test_normwise_value():
     r = np.ones((16, 16))
     c = np.ones((16, 16)) * 1.0078125         # every element off by one bf16 ulp, 2^-7
