@@ -42,12 +42,12 @@ int kdt(int dt) {
 }
 
 struct TileVar { int dt, ms, tm, tn, tkb, pipe, kg; };
-struct SplitVar { int dt, nb, waves, kch; };
+struct SplitVar { int dt, nb, waves, kch, mb; };
 struct WideVar { int dt, ms, tkb, pipe; };
 
 #define GP_TILE_ENTRY(DT, MS, TM, TN, TKB, PIPE) {DT, MS, TM, TN, TKB, PIPE, 1},
 #define GP_TILE_KG2_ENTRY(DT, MS, TM, TN, TKB, PIPE) {DT, MS, TM, TN, TKB, PIPE, 2},
-#define GP_SPLIT_ENTRY(DT, NB, W, KCH) {DT, NB, W, KCH},
+#define GP_SPLIT_ENTRY(DT, NB, W, KCH, MB) {DT, NB, W, KCH, MB},
 #define GP_WIDE_ENTRY(DT, MS, TKB, PIPE) {DT, MS, TKB, PIPE},
 constexpr TileVar kTiles[] = {GP_TILE_ALL(GP_TILE_ENTRY) GP_TILE_KG2_ALL(GP_TILE_KG2_ENTRY)};
 constexpr SplitVar kSplits[] = {GP_SPLITK_ALL(GP_SPLIT_ENTRY)};
@@ -75,9 +75,9 @@ int pick_pipe(int dt, int ms, int tm, int tn, int tkb, int want) {
     if (tile_compiled(dt, ms, tm, tn, tkb, ord[k])) return ord[k];
   return -1;
 }
-bool split_compiled(int dt, int nb, int waves, int kch) {
+bool split_compiled(int dt, int nb, int waves, int kch, int mb) {
   for (const auto& v : kSplits)
-    if (v.dt == dt && v.nb == nb && v.waves == waves && v.kch == kch) return true;
+    if (v.dt == dt && v.nb == nb && v.waves == waves && v.kch == kch && v.mb == mb) return true;
   return false;
 }
 
@@ -89,7 +89,7 @@ struct Plan {
   int kg = 1;                   // tile kernel: K groups of 4 waves
   int epi = EPI_DIRECT;
   int xcd = 1;
-  int nb = 0, waves = 4, kch = 0;  // split-K kernel
+  int nb = 0, waves = 4, kch = 0, mb = 1;  // split-K kernel (mb: 16-row blocks per workgroup)
   int64_t Kb = 0;
 };
 
@@ -173,21 +173,21 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
 // Compiled split-K chunk for (dt, nb, waves) that divides the wave's K range:
 // the largest one up to 512 bytes (measured best for the M=16 FP8 shape),
 // else the smallest; 0 if none.
-int pick_chunk(int dt, int nb, int waves, int64_t kw) {
+int pick_chunk(int dt, int nb, int waves, int mb, int64_t kw) {
   int kch = 0;
   for (const auto& v : kSplits)
-    if (v.dt == dt && v.nb == nb && v.waves == waves && kw % v.kch == 0 && v.kch <= 512 && v.kch > kch)
+    if (v.dt == dt && v.nb == nb && v.waves == waves && v.mb == mb && kw % v.kch == 0 && v.kch <= 512 && v.kch > kch)
       kch = v.kch;
   if (kch == 0)
     for (const auto& v : kSplits)
-      if (v.dt == dt && v.nb == nb && v.waves == waves && kw % v.kch == 0 && (kch == 0 || v.kch < kch))
+      if (v.dt == dt && v.nb == nb && v.waves == waves && v.mb == mb && kw % v.kch == 0 && (kch == 0 || v.kch < kch))
         kch = v.kch;
   return kch;
 }
 
 int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, const gemm_opts* o) {
   if (o && o->tile_n > 0 && o->tile_n % 16) return GP_ESHAPE;
-  if (o && o->tile_m > 0 && o->tile_m != 16) return GP_ESHAPE;
+  if (o && o->tile_m > 0 && o->tile_m != 16 && o->tile_m != 32) return GP_ESHAPE;
   if (o && o->tile_k > 0 && ((int64_t)o->tile_k * bits) % 8) return GP_ESHAPE;
   const int user_kch = (o && o->tile_k > 0) ? (int)((int64_t)o->tile_k * bits / 8) : 0;
   // waves splitting K: the caller's, else 4, else one wave (short K: fewer
@@ -200,19 +200,31 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
   int cand[2] = {2, 1};
   int ncand = 2;
   if (o && o->tile_n > 0) { cand[0] = o->tile_n / 16; ncand = 1; }
+  // 16-row blocks per workgroup: the caller's (tile_m / 16), else 2 when
+  // there is more than one block (B is read once per pair of blocks: FP8
+  // 32 x 7168 x 2048 5.6 vs 7.2 us, BF16 64 x 7168 x 2048 15.0 vs 20.0 us
+  // with 4 blocks of one column block each), else 1
+  int mcand[2] = {2, 1};
+  int nm = 2;
+  if (o && o->tile_m > 0) { mcand[0] = o->tile_m / 16; nm = 1; }
+  else if (M <= 16) { mcand[0] = 1; nm = 1; }
   for (int w = 0; w < nw; ++w) {
     const int waves = wcand[w];
     if (Kb % waves) continue;
     const int64_t kw = Kb / waves;
-    for (int c = 0; c < ncand; ++c) {
-      const int nb = cand[c];
-      if (N % (16 * nb)) continue;
-      const int kch = user_kch ? user_kch : pick_chunk(dt, nb, waves, kw);
-      if (kch == 0 || kw % kch || !split_compiled(dt, nb, waves, kch)) continue;
-      p->nb = nb;
-      p->waves = waves;
-      p->kch = kch;
-      return GP_OK;
+    for (int r = 0; r < nm; ++r) {
+      const int mb = mcand[r];
+      for (int c = 0; c < ncand; ++c) {
+        const int nb = cand[c];
+        if (N % (16 * nb)) continue;
+        const int kch = user_kch ? user_kch : pick_chunk(dt, nb, waves, mb, kw);
+        if (kch == 0 || kw % kch || !split_compiled(dt, nb, waves, kch, mb)) continue;
+        p->nb = nb;
+        p->waves = waves;
+        p->kch = kch;
+        p->mb = mb;
+        return GP_OK;
+      }
     }
   }
   return GP_ESHAPE;
@@ -274,9 +286,11 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   if (M * Ka >= kMaxBytes || N * Kb >= kMaxBytes || M * N * ob >= kMaxBytes) return GP_ESHAPE;
   const int dt = kdt(in_dtype);
   p->Kb = Kb;
-  // small M: the split-K kernel (W4A8 up to M = 64: measured 8.6 vs 11.8 us
-  // at 64 x 7168 x 2048, and 14.3 vs 12.3 us at M = 128)
-  const int64_t small_m = dt == DT_I4 ? 64 : 32;
+  // small M: the split-K kernel, up to the M where the tile kernel wins (on
+  // 64 x 7168 x 2048: FP8 8.1 vs 8.6 us and INT8 7.9 vs 8.6 favour tiles
+  // above M = 32; BF16 / FP16 15.0 vs 20.8, MXFP4 7.2 vs 9.4 and W4A8 7.6
+  // vs 11.9 favour the small-M kernel to M = 64)
+  const int64_t small_m = (dt == DT_FP8 || dt == DT_I8) ? 32 : 64;
   p->kernel = (o && o->kernel) ? o->kernel : (M <= small_m ? GP_KERNEL_SPLITK : GP_KERNEL_TILE);
   if (dt == DT_I4 && p->kernel == GP_KERNEL_WIDE) return GP_EDTYPE;   // no 256 x 256 W4A8 kernel
   if (p->kernel == GP_KERNEL_SPLITK) return choose_split(dt, bits, M, N, Kb, p, o);
@@ -374,16 +388,16 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     out->k_tiles = p.Kb / p.tkb;
     out->mfma_per_wave_tile = (int64_t)(p.tkb / kbm) * (p.tm / ms) * (p.tn / 4 / ms);
   } else {
-    out->tile_m = 16;
+    out->tile_m = 16 * p.mb;
     out->tile_n = 16 * p.nb;
     out->tile_k = (int)((int64_t)p.kch * 8 / bits);
     out->epilogue = GP_EPI_DIRECT;
     out->waves = p.waves;
     out->threads = 64 * p.waves;
-    out->lds_bytes = p.waves * p.nb * 64 * 16;
-    out->grid = (N / (16 * p.nb)) * ((M + 15) / 16);
+    out->lds_bytes = p.waves * p.nb * p.mb * 64 * 16;
+    out->grid = (N / (16 * p.nb)) * ((M + 16 * p.mb - 1) / (16 * p.mb));
     out->k_tiles = p.Kb / p.waves / p.kch;
-    out->mfma_per_wave_tile = (int64_t)(p.kch / kbm) * p.nb;
+    out->mfma_per_wave_tile = (int64_t)(p.kch / kbm) * p.nb * p.mb;
   }
   // MFMAs the launch issues (the algorithmic (M/ms)(N/ms)(K/K_instr) when
   // the tile divides M and N; edge tiles and partial row blocks add to it)
@@ -476,12 +490,12 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
     t.Kb = (uint32_t)p.Kb;
     t.act = act;
     switch (dt) {
-      case DT_I8: e = launch_splitk_i8(p.nb, p.waves, p.kch, t, s); break;
-      case DT_FP8: e = launch_splitk_fp8(p.nb, p.waves, p.kch, t, s); break;
-      case DT_BF16: e = launch_splitk_bf16(p.nb, p.waves, p.kch, t, s); break;
-      case DT_F16: e = launch_splitk_f16(p.nb, p.waves, p.kch, t, s); break;
-      case DT_I4: e = launch_splitk_i4(p.nb, p.waves, p.kch, t, s); break;
-      default: e = launch_splitk_fp4(p.nb, p.waves, p.kch, t, s); break;
+      case DT_I8: e = launch_splitk_i8(p.nb, p.waves, p.kch, p.mb, t, s); break;
+      case DT_FP8: e = launch_splitk_fp8(p.nb, p.waves, p.kch, p.mb, t, s); break;
+      case DT_BF16: e = launch_splitk_bf16(p.nb, p.waves, p.kch, p.mb, t, s); break;
+      case DT_F16: e = launch_splitk_f16(p.nb, p.waves, p.kch, p.mb, t, s); break;
+      case DT_I4: e = launch_splitk_i4(p.nb, p.waves, p.kch, p.mb, t, s); break;
+      default: e = launch_splitk_fp4(p.nb, p.waves, p.kch, p.mb, t, s); break;
     }
   }
   return hip_status(e);

@@ -44,7 +44,9 @@ struct SplitArgs {
   int act;            // Act
 };
 
-template <int DT, int NB, int WAVES, int KCH>
+// MB: 16-row blocks per workgroup (1 for M = 16; up to 4 so that a batch of
+// up to 64 rows reads B once); each wave multiplies every block of its K range.
+template <int DT, int NB, int WAVES, int KCH, int MB = 1>
 struct SplitCfg {
   static constexpr int THREADS = WAVES * 64;
   static constexpr int KB = Traits<DT>::KB;
@@ -55,13 +57,15 @@ struct SplitCfg {
   static constexpr int OB = (DT == DT_I8) ? 4 : 2;
   static constexpr int NSC = (DT == DT_FP4) ? 1 : 0;
   static constexpr bool FSC = DT == DT_FP8 || DT == DT_I4;   // fp32 row / column scales
-  static constexpr int LDS = WAVES * NB * 64 * 16;    // partial accumulators
+  static constexpr int NQ = MB * NB;                  // 16 x 16 output blocks
+  static constexpr int LDS = WAVES * NQ * 64 * 16;    // partial accumulators
   static_assert(KCH % KB == 0, "chunk must be whole MFMA steps");
+  static_assert(NQ <= WAVES, "one output block per wave in the epilogue");
 };
 
-template <int DT, int NB, int WAVES, int KCH>
+template <int DT, int NB, int WAVES, int KCH, int MB>
 __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
-  using C = SplitCfg<DT, NB, WAVES, KCH>;
+  using C = SplitCfg<DT, NB, WAVES, KCH, MB>;
   using Acc = typename Traits<DT>::Acc;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
 
@@ -81,8 +85,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
   uint32_t bx = blockIdx.x;
   if (gridDim.x % 8u == 0) bx = (bx % 8u) * (gridDim.x / 8u) + bx / 8u;
   const uint32_t n0 = bx * (16 * NB);
-  const uint32_t m0 = blockIdx.y * 16;
-  const uint32_t mrows = min(16u, p.M - m0);  // real rows of this block
+  const uint32_t m0 = blockIdx.y * (16 * MB);
+  const uint32_t mrows = min(16u * MB, p.M - m0);  // real rows of this workgroup
   const uint32_t kw = Kb / WAVES;            // B bytes per wave
   const uint32_t k_begin = wave * kw;
   const int chunks = (int)(kw / KCH);
@@ -107,16 +111,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
 
   // Epilogue vectors (row / column scales, bias): issued before any operand
   // load, so that the epilogue does not wait one more memory round trip for
-  // them. Wave w stores column block w (NB <= WAVES), so each wave needs its
-  // rows' scales and its block's column values only.
-  static_assert(NB <= WAVES, "one column block per wave in the epilogue");
-  const uint32_t nbw = (uint32_t)min(wave, NB - 1);
+  // them. Wave w stores output block w = (row block w / NB, column block
+  // w % NB), so each wave needs its block's row and column values only.
+  const uint32_t qw = (uint32_t)min(wave, C::NQ - 1);
+  const uint32_t nbw = qw % NB, mbw = qw / NB;
   float sa_v = 1.f;
   v4f sb_v = v4f{1.f, 1.f, 1.f, 1.f};
   if constexpr (C::FSC) {
     const __amdgpu_buffer_rsrc_t rs_a = make_rsrc((const float*)p.sa + m0, mrows * 4);
     const __amdgpu_buffer_rsrc_t rs_b = make_rsrc((const float*)p.sb + n0, 16 * NB * 4);
-    sa_v = __builtin_bit_cast(float, buf_load4_early(rs_a, lane_lo * 4, 0));
+    sa_v = __builtin_bit_cast(float, buf_load4_early(rs_a, (mbw * 16 + lane_lo) * 4, 0));
     sb_v = __builtin_bit_cast(v4f, buf_load16_early(rs_b, (nbw * 16 + 4 * lane_hi) * 4, 0));
   }
   // without a bias the resource is empty: the load returns zeros, no branch
@@ -127,13 +131,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
     bias_v = __builtin_bit_cast(v4f, buf_load16_early(rbias, (nbw * 16 + 4 * lane_hi) * 4, 0));
   }
 
-  v4i af[2][C::STEPS][C::AFR];
+  v4i af[2][C::STEPS][MB][C::AFR];
   v4i bf[2][C::STEPS][NB][C::FRAG];
-  int sa_r[2][C::STEPS * C::NSC + 1 - C::NSC];
+  int sa_r[2][C::STEPS][MB * C::NSC + 1 - C::NSC];
   int sb_r[2][C::STEPS][NB * C::NSC + 1 - C::NSC];
-  Acc acc[NB];
+  Acc acc[MB][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = Acc{0, 0, 0, 0};
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Acc{0, 0, 0, 0};
 
   auto load = [&](auto par_c, int ch) {
     constexpr int par = decltype(par_c)::value;
@@ -141,10 +147,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
 #pragma unroll
     for (int s = 0; s < C::STEPS; ++s)
 #pragma unroll
-      for (int f = 0; f < C::AFR; ++f) {
-        if constexpr (DT == DT_I4) af[par][s][f] = buf_load16(ra, a_off + s * 128 + f * 16, kb * 2);
-        else af[par][s][f] = buf_load16(ra, a_off + s * C::KB + f * 64, kb);
-      }
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int f = 0; f < C::AFR; ++f) {
+          const uint32_t ao = a_off + mb * 16 * Ka;
+          if constexpr (DT == DT_I4) af[par][s][mb][f] = buf_load16(ra, ao + s * 128 + f * 16, kb * 2);
+          else af[par][s][mb][f] = buf_load16(ra, ao + s * C::KB + f * 64, kb);
+        }
     const uint32_t kblk = (kb / 64) * 1024u;
 #pragma unroll
     for (int s = 0; s < C::STEPS; ++s)
@@ -157,7 +166,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
       const uint32_t sbase = kb / 16;  // scale byte of this chunk's first 32-element block
 #pragma unroll
       for (int s = 0; s < C::STEPS; ++s) {
-        sa_r[par][s] = buf_load4(rsa, lane_lo * srow + s * 4, sbase);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) sa_r[par][s][mb] = buf_load4(rsa, (mb * 16 + lane_lo) * srow + s * 4, sbase);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) sb_r[par][s][nb] = buf_load4(rsb, (nb * 16 + lane_lo) * srow + s * 4, sbase);
       }
@@ -167,19 +177,23 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
     constexpr int par = decltype(par_c)::value;
 #pragma unroll
     for (int s = 0; s < C::STEPS; ++s) {
-      int sy = 0;
-      if constexpr (DT == DT_FP4) sy = sa_r[par][s] >> (8 * lane_hi);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (DT == DT_I4) {
-          v4i lo, hi;
-          widen_int4(bf[par][s][nb][0], lo, hi);
-          acc[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(lo, af[par][s][0], acc[nb], 0, 0, 0);
-          acc[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(hi, af[par][s][1], acc[nb], 0, 0, 0);
-        } else {
-          int sx = 0;
-          if constexpr (DT == DT_FP4) sx = sb_r[par][s][nb] >> (8 * lane_hi);
-          acc[nb] = mfma<DT>(bf[par][s][nb], af[par][s], acc[nb], sx, sy);
+        // W4A8: the piece is widened once and used by every row block
+        v4i lo, hi;
+        if constexpr (DT == DT_I4) widen_int4(bf[par][s][nb][0], lo, hi);
+        int sx = 0;
+        if constexpr (DT == DT_FP4) sx = sb_r[par][s][nb] >> (8 * lane_hi);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          if constexpr (DT == DT_I4) {
+            acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(lo, af[par][s][mb][0], acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(hi, af[par][s][mb][1], acc[mb][nb], 0, 0, 0);
+          } else {
+            int sy = 0;
+            if constexpr (DT == DT_FP4) sy = sa_r[par][s][mb] >> (8 * lane_hi);
+            acc[mb][nb] = mfma<DT>(bf[par][s][nb], af[par][s][mb], acc[mb][nb], sx, sy);
+          }
         }
       }
     }
@@ -198,21 +212,24 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_splitk_kernel(SplitArgs p) {
   // ---- reduce the WAVES partial sums through LDS in wave order ----
   Acc* red = (Acc*)lds;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) red[(wave * NB + nb) * 64 + lane] = acc[nb];
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) red[(wave * C::NQ + mb * NB + nb) * 64 + lane] = acc[mb][nb];
   __syncthreads();
 
   const __amdgpu_buffer_rsrc_t rc =
       make_rsrc(p.c + ((size_t)m0 * p.N + n0) * C::OB, ((mrows - 1) * p.N + 16 * NB) * C::OB);
   with_act(p.act, [&](auto act_c) {
     constexpr int A = decltype(act_c)::value;
-    for (int nb = wave; nb < NB; nb += WAVES) {
-      Acc v = red[nb * 64 + lane];
+    if (wave < C::NQ) {
+      Acc v = red[wave * 64 + lane];
 #pragma unroll
-      for (int w = 1; w < WAVES; ++w) v += red[(w * NB + nb) * 64 + lane];
-      // lane holds C[m0 + lane_lo][n0 + nb*16 + 4*lane_hi + r]; rows past M are
-      // not stored (offset outside the resource)
-      const uint32_t col = nb * 16 + 4 * lane_hi;
-      const uint32_t off = (uint32_t)lane_lo < mrows ? (lane_lo * p.N + col) * C::OB : 0x80000000u;
+      for (int w = 1; w < WAVES; ++w) v += red[(w * C::NQ + wave) * 64 + lane];
+      // lane holds C[m0 + mbw*16 + lane_lo][n0 + nbw*16 + 4*lane_hi + r]; rows
+      // past M are not stored (offset outside the resource)
+      const uint32_t row = mbw * 16 + lane_lo;
+      const uint32_t col = nbw * 16 + 4 * lane_hi;
+      const uint32_t off = row < mrows ? (row * p.N + col) * C::OB : 0x80000000u;
       if constexpr (DT == DT_I8) {
         buf_store16_nt(v, rc, off);
       } else {

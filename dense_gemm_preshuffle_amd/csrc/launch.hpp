@@ -25,12 +25,12 @@ GP_DECLARE_TILE(i8) GP_DECLARE_TILE(fp8) GP_DECLARE_TILE(bf16) GP_DECLARE_TILE(f
 GP_DECLARE_TILE(i4)
 GP_DECLARE_WIDE(i8) GP_DECLARE_WIDE(fp8) GP_DECLARE_WIDE(bf16) GP_DECLARE_WIDE(f16) GP_DECLARE_WIDE(fp4)
 GP_DECLARE_WIDE(i4)
-hipError_t launch_splitk_i8(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
-hipError_t launch_splitk_fp8(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
-hipError_t launch_splitk_bf16(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
-hipError_t launch_splitk_fp4(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
-hipError_t launch_splitk_f16(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
-hipError_t launch_splitk_i4(int nb, int waves, int kch, const SplitArgs& a, hipStream_t s);
+hipError_t launch_splitk_i8(int nb, int waves, int kch, int mb, const SplitArgs& a, hipStream_t s);
+hipError_t launch_splitk_fp8(int nb, int waves, int kch, int mb, const SplitArgs& a, hipStream_t s);
+hipError_t launch_splitk_bf16(int nb, int waves, int kch, int mb, const SplitArgs& a, hipStream_t s);
+hipError_t launch_splitk_fp4(int nb, int waves, int kch, int mb, const SplitArgs& a, hipStream_t s);
+hipError_t launch_splitk_f16(int nb, int waves, int kch, int mb, const SplitArgs& a, hipStream_t s);
+hipError_t launch_splitk_i4(int nb, int waves, int kch, int mb, const SplitArgs& a, hipStream_t s);
 
 }  // namespace gp
 
@@ -48,11 +48,11 @@ hipError_t launch_splitk_i4(int nb, int waves, int kch, const SplitArgs& a, hipS
 #define GP_TILE_CASE_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true, 1)
 #define GP_TILE_CASE_KG2(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 2)
 #define GP_TILE_CASE_KG2_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true, 2)
-#define GP_SPLITK_CASE(DT, NB, W, KCH)                                                     \
-  if (nb == NB && waves == W && kch == KCH) {                                              \
-    const dim3 grid(a.N / (16 * NB), (a.M + 15) / 16);                                     \
-    hipLaunchKernelGGL((gemm_splitk_kernel<DT, NB, W, KCH>), grid, dim3(W * 64), 0, s, a); \
-    return hipGetLastError();                                                              \
+#define GP_SPLITK_CASE(DT, NB, W, KCH, MB)                                                     \
+  if (nb == NB && waves == W && kch == KCH && mb == MB) {                                      \
+    const dim3 grid(a.N / (16 * NB), (a.M + 16 * MB - 1) / (16 * MB));                         \
+    hipLaunchKernelGGL((gemm_splitk_kernel<DT, NB, W, KCH, MB>), grid, dim3(W * 64), 0, s, a); \
+    return hipGetLastError();                                                                  \
   }
 #define GP_WIDE_CASE_IMPL(DT, MS, TKB, PIPE, FU)                                                  \
   if (ms == MS && tkb == TKB && pipe == PIPE) {                                                   \

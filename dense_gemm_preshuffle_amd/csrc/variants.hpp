@@ -5,8 +5,8 @@
 // 32 (the MFMA block); pipe 0 = A staged through VGPRs (2 stages), 2 / 3 = A
 // by LDS DMA with 2 / 3 stages. Each is built with the direct and the
 // CShuffle epilogue.
-// Split-K kernel: Y(dtype, n_blocks_of_16, waves, chunk_bytes_per_wave);
-// the only kernel of the W4A8 type (DT_I4).
+// Small-M (split-K) kernel: Y(dtype, n_blocks_of_16, waves,
+// chunk_bytes_per_wave, m_blocks_of_16); W4A8 chunk bytes count bytes of B.
 // Wide kernel (256x256 tiles, 8 waves): W(dtype, mfma, tile_k_bytes, pipe),
 // pipe = LDS DMA stages of A and B.
 #pragma once
@@ -54,18 +54,24 @@
 // do not fit the remaining registers and the compiler moved values, or the
 // whole accumulator array, to scratch memory, at 50x the run time.)
 
-#define GP_SPLITK_I8(Y) Y(DT_I8, 1, 4, 64) Y(DT_I8, 1, 4, 256) Y(DT_I8, 2, 4, 256) Y(DT_I8, 1, 1, 64)
+#define GP_SPLITK_I8(Y) Y(DT_I8, 1, 4, 64, 1) Y(DT_I8, 1, 4, 256, 1) Y(DT_I8, 2, 4, 256, 1) Y(DT_I8, 1, 1, 64, 1) \
+  Y(DT_I8, 2, 4, 256, 2)
 #define GP_SPLITK_FP8(Y)                                                                           \
-  Y(DT_FP8, 1, 4, 128) Y(DT_FP8, 1, 4, 256) Y(DT_FP8, 1, 4, 512) Y(DT_FP8, 2, 4, 256)             \
-  Y(DT_FP8, 2, 4, 512) Y(DT_FP8, 1, 8, 256) Y(DT_FP8, 4, 4, 256) Y(DT_FP8, 2, 8, 256) Y(DT_FP8, 4, 8, 256) \
-  Y(DT_FP8, 1, 1, 128)
-#define GP_SPLITK_BF16(Y) Y(DT_BF16, 1, 4, 64) Y(DT_BF16, 1, 4, 256) Y(DT_BF16, 2, 4, 256) Y(DT_BF16, 1, 1, 64)
-#define GP_SPLITK_FP4(Y) Y(DT_FP4, 1, 4, 64) Y(DT_FP4, 1, 4, 256) Y(DT_FP4, 2, 4, 256) Y(DT_FP4, 1, 1, 64)
-#define GP_SPLITK_F16(Y) Y(DT_F16, 1, 4, 64) Y(DT_F16, 1, 4, 256) Y(DT_F16, 2, 4, 256) Y(DT_F16, 1, 1, 64)
+  Y(DT_FP8, 1, 4, 128, 1) Y(DT_FP8, 1, 4, 256, 1) Y(DT_FP8, 1, 4, 512, 1) Y(DT_FP8, 2, 4, 256, 1)             \
+  Y(DT_FP8, 2, 4, 512, 1) Y(DT_FP8, 1, 8, 256, 1) Y(DT_FP8, 4, 4, 256, 1) Y(DT_FP8, 2, 8, 256, 1) Y(DT_FP8, 4, 8, 256, 1) \
+  Y(DT_FP8, 1, 1, 128, 1) \
+  Y(DT_FP8, 2, 4, 256, 2)
+#define GP_SPLITK_BF16(Y) Y(DT_BF16, 1, 4, 64, 1) Y(DT_BF16, 1, 4, 256, 1) Y(DT_BF16, 2, 4, 256, 1) Y(DT_BF16, 1, 1, 64, 1) \
+  Y(DT_BF16, 2, 4, 256, 2)
+#define GP_SPLITK_FP4(Y) Y(DT_FP4, 1, 4, 64, 1) Y(DT_FP4, 1, 4, 256, 1) Y(DT_FP4, 2, 4, 256, 1) Y(DT_FP4, 1, 1, 64, 1) \
+  Y(DT_FP4, 2, 4, 256, 2)
+#define GP_SPLITK_F16(Y) Y(DT_F16, 1, 4, 64, 1) Y(DT_F16, 1, 4, 256, 1) Y(DT_F16, 2, 4, 256, 1) Y(DT_F16, 1, 1, 64, 1) \
+  Y(DT_F16, 2, 4, 256, 2)
 // W4A8: chunk bytes are bytes of B (the int8 A chunk is twice as long)
 #define GP_SPLITK_I4(Y)                                                                            \
-  Y(DT_I4, 1, 4, 64) Y(DT_I4, 1, 4, 128) Y(DT_I4, 1, 4, 256) Y(DT_I4, 2, 4, 64) Y(DT_I4, 2, 4, 128)  \
-  Y(DT_I4, 2, 4, 256) Y(DT_I4, 2, 8, 128) Y(DT_I4, 1, 1, 64)
+  Y(DT_I4, 1, 4, 64, 1) Y(DT_I4, 1, 4, 128, 1) Y(DT_I4, 1, 4, 256, 1) Y(DT_I4, 2, 4, 64, 1) Y(DT_I4, 2, 4, 128, 1)  \
+  Y(DT_I4, 2, 4, 256, 1) Y(DT_I4, 2, 8, 128, 1) Y(DT_I4, 1, 1, 64, 1) \
+  Y(DT_I4, 2, 4, 128, 2)
 
 #define GP_WIDE_I8(W) W(DT_I8, 16, 128, 2) W(DT_I8, 32, 128, 2)
 #define GP_WIDE_FP8(W) W(DT_FP8, 16, 128, 2)

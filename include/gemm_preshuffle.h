@@ -96,8 +96,9 @@ enum {
 
 /* Tuning options. Pass NULL, or a zero-filled struct, for all-automatic;
  * a zero field means "planner's choice". tile_k is in ELEMENTS (as on the
- * pages). For the split-K kernel tile_m is 16, tile_n is 16 * (column blocks
- * per workgroup) and tile_k is the K chunk each wave loads per step. A tile
+ * pages). For the split-K kernel tile_m is 16 or 32 (16-row blocks per
+ * workgroup), tile_n is 16 * (column blocks per workgroup) and tile_k is the
+ * K chunk each wave loads per step. A tile
  * that is not compiled into the library is GP_ESHAPE. */
 typedef struct gemm_opts {
   int tile_m, tile_n, tile_k;

@@ -221,8 +221,8 @@ def test_w4a8_plan():
     with pytest.raises(gp.GemmError) as e:
         gp.gemm_plan("w4a8", 16, 256, 2 * 65536)               # int32 range of the 16x widened products
     assert e.value.status == GP_ESHAPE
-    q = gp.gemm_plan("w4a8", 300, 512, 4096, dict(kernel=2))   # small-M kernel, any M: 19 row blocks
-    assert q["grid"] == (512 // q["tile_n"]) * 19
+    q = gp.gemm_plan("w4a8", 300, 512, 4096, dict(kernel=2))   # small-M kernel, any M: 2 row blocks
+    assert q["tile_m"] == 32 and q["grid"] == (512 // q["tile_n"]) * 10  # per workgroup, the last partial
     # larger M: the tile kernel, two int8 MFMAs per 64-byte INT4 piece; A
     # tiles (int8) are twice the bytes of the B tile's K extent
     t = gp.gemm_plan("w4a8", 512, 4096, 4096)
@@ -313,3 +313,18 @@ def test_k_not_a_multiple_of_the_large_tiles(dtype, M, N, K):
     assert p["kernel"] == gp.KERNEL_TILE and p["grid"] >= 64
     assert p["tile_k"] * {"int8": 8, "fp16": 16, "bf16": 16, "mxfp4": 4}[dtype] // 8 == 64
     assert p["mfma_total"] == F.mfma_count_gfx950(dtype, M, N, K, p["mfma"])
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16", "int8", "mxfp4", "fp16", "w4a8"])
+def test_small_m_row_blocks(dtype):
+    """The small-M kernel takes two 16-row blocks per workgroup beyond one
+    block of rows (B is read once per pair); the issued MFMAs still cover
+    every output."""
+    for M, mb in [(16, 1), (5, 1), (24, 2), (32, 2), (48, 2), (64, 2), (100, 2)]:
+        p = gp.gemm_plan(dtype, M, 7168, 2048, dict(kernel=2))
+        assert p["tile_m"] == 16 * mb, (M, p)
+        assert p["grid"] == (7168 // p["tile_n"]) * -(-M // (16 * mb))
+        assert p["mfma_total"] == p["grid"] * p["waves"] * p["k_tiles"] * p["mfma_per_wave_tile"]
+        assert p["mfma_total"] * F.flops_per_mfma_gfx950(dtype, 16) >= F.flops(M, 7168, 2048)
+    q = gp.gemm_plan(dtype, 64, 7168, 2048, dict(kernel=2, tile_m=16))
+    assert q["tile_m"] == 16

@@ -156,6 +156,17 @@ TILE_CASES = [
     ("w4a8", 16, 256, 4096, dict(kernel=2, tile_n=32, waves=8, tile_k=256)),
     ("w4a8", 48, 128, 512, dict(kernel=2, tile_k=128)),
     ("w4a8", 16, 128, 4096, dict(kernel=2, tile_n=32, tile_k=128)),   # 4 chunks per wave
+    # small-M kernel with 2 row blocks per workgroup (B read once per pair of row blocks)
+    ("fp8", 32, 512, 2048, dict(kernel=2)),
+    ("fp8", 64, 256, 1024, dict(kernel=2)),
+    ("fp8", 48, 512, 2048, dict(kernel=2)),
+    ("bf16", 64, 256, 512, dict(kernel=2)),
+    ("int8", 64, 256, 512, dict(kernel=2)),
+    ("mxfp4", 64, 256, 1024, dict(kernel=2)),
+    ("fp16", 32, 256, 512, dict(kernel=2)),
+    ("w4a8", 64, 256, 1024, dict(kernel=2)),
+    ("w4a8", 32, 512, 2048, dict(kernel=2)),
+    ("fp8", 64, 512, 2048, dict(kernel=2, tile_m=16)),
     # W4A8 on the tile kernel (tile_k in INT4 elements; A tiles twice the B bytes)
     ("w4a8", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128, pipeline=3)),
     ("w4a8", 256, 512, 1024, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128)),
@@ -207,6 +218,11 @@ RAGGED_CASES = [
     ("int8", 29, 64, 1024, dict(kernel=2)),
     ("mxfp4", 7, 128, 2048, dict(kernel=2)),
     ("w4a8", 3, 256, 2048, dict(kernel=2)),
+    ("fp8", 20, 256, 1024, dict(kernel=2)),       # two row blocks, the second partial
+    ("fp8", 100, 512, 2048, dict(kernel=2)),      # two row blocks per workgroup, 4 workgroup rows, last partial
+    ("bf16", 50, 128, 512, dict(kernel=2)),
+    ("mxfp4", 40, 128, 2048, dict(kernel=2)),
+    ("w4a8", 77, 256, 2048, dict(kernel=2)),
     ("w4a8", 150, 400, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128)),
     ("w4a8", 100, 208, 1024, None),        # planner's choice: the tile kernel with edge tiles
     ("fp8", 200, 48, 1024, None),          # no tile fits 48 columns: the planner takes split-K
@@ -259,6 +275,8 @@ EPI_CASES = [
     ("bf16", 512, 256, 320, dict(kernel=3)),
     ("fp8", 512, 512, 640, dict(kernel=3)),
     ("w4a8", 16, 512, 2048, dict(kernel=2)),
+    ("fp8", 48, 512, 2048, dict(kernel=2)),      # row blocks: per-row scales of each block
+    ("w4a8", 64, 256, 1024, dict(kernel=2)),
     ("bf16", 100, 272, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64)),   # with edge tiles
     ("fp8", 100, 208, 1024, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3, waves=8)),
     ("bf16", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64, pipeline=0, waves=8)),
