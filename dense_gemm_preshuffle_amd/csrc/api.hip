@@ -187,44 +187,48 @@ int pick_chunk(int dt, int nb, int waves, int mb, int64_t kw) {
 
 int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, const gemm_opts* o) {
   if (o && o->tile_n > 0 && o->tile_n % 16) return GP_ESHAPE;
-  if (o && o->tile_m > 0 && o->tile_m != 16 && o->tile_m != 32) return GP_ESHAPE;
+  if (o && o->tile_m > 0 && o->tile_m != 16 && o->tile_m != 32 && o->tile_m != 64) return GP_ESHAPE;
   if (o && o->tile_k > 0 && ((int64_t)o->tile_k * bits) % 8) return GP_ESHAPE;
   const int user_kch = (o && o->tile_k > 0) ? (int)((int64_t)o->tile_k * bits / 8) : 0;
-  // waves splitting K: the caller's, else 4, else one wave (short K: fewer
-  // than 4 chunks of the type's smallest compiled size)
-  int wcand[2] = {4, 1};
-  int nw = 2;
-  if (o && o->waves > 0) { wcand[0] = o->waves; nw = 1; }
+  // (waves, 16-row blocks per workgroup) in order of preference. One block
+  // for M <= 16; two beyond (B read once per pair); four on 8 waves beyond
+  // 32 rows (B read once for up to 64 rows: 64 x 7168 x 2048 FP8 7.7 us
+  // against 8.7 with two blocks and 8.1 on tiles, BF16 11.8 against 15.0;
+  // MXFP4 stays on two, 7.2 against 8.2); one wave last (K too short for 4).
+  struct WM { int waves, mb; };
+  WM cand[4];
+  int nc = 0;
+  if (o && o->tile_m > 0) {
+    const int mb = o->tile_m / 16;
+    cand[nc++] = {o->waves > 0 ? o->waves : (mb == 4 ? 8 : 4), mb};
+  } else if (o && o->waves > 0) {
+    if (M > 16) cand[nc++] = {o->waves, 2};
+    cand[nc++] = {o->waves, 1};
+  } else {
+    if (M > 32 && dt != DT_FP4) cand[nc++] = {8, 4};
+    if (M > 16) cand[nc++] = {4, 2};
+    cand[nc++] = {4, 1};
+    cand[nc++] = {1, 1};
+  }
   // column blocks per workgroup: the caller's, else 2 (two blocks fill whole
   // 128-byte lines of a bf16 C row), else 1
-  int cand[2] = {2, 1};
-  int ncand = 2;
-  if (o && o->tile_n > 0) { cand[0] = o->tile_n / 16; ncand = 1; }
-  // 16-row blocks per workgroup: the caller's (tile_m / 16), else 2 when
-  // there is more than one block (B is read once per pair of blocks: FP8
-  // 32 x 7168 x 2048 5.6 vs 7.2 us, BF16 64 x 7168 x 2048 15.0 vs 20.0 us
-  // with 4 blocks of one column block each), else 1
-  int mcand[2] = {2, 1};
-  int nm = 2;
-  if (o && o->tile_m > 0) { mcand[0] = o->tile_m / 16; nm = 1; }
-  else if (M <= 16) { mcand[0] = 1; nm = 1; }
-  for (int w = 0; w < nw; ++w) {
-    const int waves = wcand[w];
+  int nbc[2] = {2, 1};
+  int nn = 2;
+  if (o && o->tile_n > 0) { nbc[0] = o->tile_n / 16; nn = 1; }
+  for (int i = 0; i < nc; ++i) {
+    const int waves = cand[i].waves, mb = cand[i].mb;
     if (Kb % waves) continue;
     const int64_t kw = Kb / waves;
-    for (int r = 0; r < nm; ++r) {
-      const int mb = mcand[r];
-      for (int c = 0; c < ncand; ++c) {
-        const int nb = cand[c];
-        if (N % (16 * nb)) continue;
-        const int kch = user_kch ? user_kch : pick_chunk(dt, nb, waves, mb, kw);
-        if (kch == 0 || kw % kch || !split_compiled(dt, nb, waves, kch, mb)) continue;
-        p->nb = nb;
-        p->waves = waves;
-        p->kch = kch;
-        p->mb = mb;
-        return GP_OK;
-      }
+    for (int c = 0; c < nn; ++c) {
+      const int nb = nbc[c];
+      if (N % (16 * nb)) continue;
+      const int kch = user_kch ? user_kch : pick_chunk(dt, nb, waves, mb, kw);
+      if (kch == 0 || kw % kch || !split_compiled(dt, nb, waves, kch, mb)) continue;
+      p->nb = nb;
+      p->waves = waves;
+      p->kch = kch;
+      p->mb = mb;
+      return GP_OK;
     }
   }
   return GP_ESHAPE;
@@ -286,11 +290,11 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   if (M * Ka >= kMaxBytes || N * Kb >= kMaxBytes || M * N * ob >= kMaxBytes) return GP_ESHAPE;
   const int dt = kdt(in_dtype);
   p->Kb = Kb;
-  // small M: the split-K kernel, up to the M where the tile kernel wins (on
-  // 64 x 7168 x 2048: FP8 8.1 vs 8.6 us and INT8 7.9 vs 8.6 favour tiles
-  // above M = 32; BF16 / FP16 15.0 vs 20.8, MXFP4 7.2 vs 9.4 and W4A8 7.6
-  // vs 11.9 favour the small-M kernel to M = 64)
-  const int64_t small_m = (dt == DT_FP8 || dt == DT_I8) ? 32 : 64;
+  // small M (up to 64 rows): the split-K kernel; on 64 x 7168 x 2048 it
+  // measured FP8 7.7 vs 8.1 us on tiles, INT8 7.1 vs 7.9, BF16 11.8 vs 20.8,
+  // MXFP4 7.2 vs 9.4, W4A8 7.3 vs 11.9; at M = 128 the tiles are as fast or
+  // faster (FP8 12.7 vs 13.2)
+  const int64_t small_m = 64;
   p->kernel = (o && o->kernel) ? o->kernel : (M <= small_m ? GP_KERNEL_SPLITK : GP_KERNEL_TILE);
   if (dt == DT_I4 && p->kernel == GP_KERNEL_WIDE) return GP_EDTYPE;   // no 256 x 256 W4A8 kernel
   if (p->kernel == GP_KERNEL_SPLITK) return choose_split(dt, bits, M, N, Kb, p, o);
