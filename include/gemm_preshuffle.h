@@ -208,9 +208,10 @@ int gemm_f16(const void* a, const void* b_shuf, void* c, int64_t M, int64_t N, i
  *   c        device [M][N] bf16:
  *     C[m][n] = bf16_rne((acc[m][n] * scale_a[m]) * scale_b[n]),
  * acc = sum_k A[m][k] B[n][k] exact in int32. K % 128 == 0 and K <= 65536.
- * M <= 32 runs on the small-M kernel (GP_KERNEL_SPLITK, which needs
- * K % 512 == 0 with its 4 waves); larger M on the tile kernel, which widens
- * each INT4 piece of B to int8 in registers for two int8 MFMAs.
+ * M <= 64 runs on the small-M kernel (GP_KERNEL_SPLITK: 4 or 8 waves
+ * split K where K % 512 == 0, one wave otherwise); larger M on the tile
+ * kernel, which widens each INT4 piece of B to int8 in registers for two
+ * int8 MFMAs.
  */
 int gemm_w4a8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b, void* c,
               int64_t M, int64_t N, int64_t K, const gemm_opts* opts, void* stream);
