@@ -379,9 +379,14 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     const bool apart = (p.tm * (tka / 16)) % 256 != 0;
     const int stages = p.pipe ? p.pipe : 2;
     int abuf = p.kg * stages * (p.tm * tka + (apart ? 16 : 0));
-    if (dt == DT_FP4) {   // staged E8M0 scales: per stage, or a ring of 4-tile groups (2 slots + discard)
-      if (stages == 2 && p.tkb == 128) abuf += 3 * (4 * (p.tm + p.tn) * 8 + 16);
-      else abuf += stages * ((p.tm + p.tn) * (p.tkb / 16) + 16);
+    if (dt == DT_FP4) {   // staged E8M0 scales: per stage, or a ring of two slots of SG-tile groups
+      if (stages == 2 && p.tkb == 128) {
+        // 4-tile groups, two lanes per row; 16 spare bytes for lanes past the rows
+        const int spare = ((p.tm * 2) % 256 || (p.tn * 2) % 256) ? 16 : 0;
+        abuf += 2 * (4 * (p.tm + p.tn) * 8 + spare);
+      } else {
+        abuf += stages * ((p.tm + p.tn) * (p.tkb / 16) + 16);
+      }
     }
     int cbytes = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
     if (p.kg > 1 && p.tm * p.tn * 4 > cbytes) cbytes = p.tm * p.tn * 4;   // K-group reduction

@@ -64,6 +64,11 @@ __device__ __forceinline__ void edge_shift(uint32_t& x0, uint32_t& skip, uint32_
   x0 = __builtin_amdgcn_readfirstlane(x0 - s);
 }
 
+// Resident workgroups per CU of the tile kernel: one once the accumulators
+// alone take more than half of the 256 registers two workgroups would leave
+// each wave, or with two K groups; two otherwise.
+constexpr int tile_wgs_per_cu(int tm, int tn, int kg) { return (kg > 1 || tm * tn / 256 > 128) ? 1 : 2; }
+
 // PIPE: 0 = A staged through VGPRs, two LDS buffers (prefetch one tile
 // ahead); 2 .. 6 = A copied global -> LDS by the buffer-load LDS DMA, with
 // PIPE LDS buffers and B register sets (prefetch PIPE-1 tiles ahead).
@@ -114,23 +119,27 @@ struct TileCfg {
   // Scale groups: with a 2-stage pipeline and 8 scale bytes per row per tile,
   // the scales of SG = 4 consecutive K tiles are fetched together (16 bytes
   // per lane, two lanes per row) into a two-slot LDS ring, once every SG
-  // tiles. A tile's TM + TN scale rows are as many separate cache lines; one
-  // gather of them per tile cost the texture path about as much as the tile's
-  // operand loads (the MXFP4 4096x4096x8192 kernel ran 15% faster with the
-  // gathers removed).
+  // tiles (the main loop runs SG tiles per trip, so the tiles between issue
+  // no scale loads). A tile's TM + TN scale rows are as many separate cache
+  // lines; one gather of them per tile cost the texture path about as much
+  // as the tile's operand loads (the MXFP4 4096x4096x8192 kernel ran 15%
+  // faster with the gathers removed). (8-tile groups: their registers pushed
+  // the 128 x 256 tile's accumulators into scratch memory.)
   static constexpr int SG = (NSC && ST == 2 && SCB == 8) ? 4 : 1;
+  static constexpr int GTILE = SROWS * 8;                                  // staged bytes of one tile
   static constexpr int LPR = SG > 1 ? SG * SCB / 16 : 0;                     // 16-byte lanes per row
   static constexpr int GLA = SG > 1 ? (TM * LPR + THREADS - 1) / THREADS : 0;  // group loads per thread
   static constexpr int GLB = SG > 1 ? (TN * LPR + THREADS - 1) / THREADS : 0;
-  static constexpr int GTILE = SROWS * 8;                                  // staged bytes of one tile
-  static constexpr int GSLOT = SG > 1 ? SG * GTILE + 16 : 0;               // + a spare slot for idle lanes
+  // a spare 16 bytes after the tiles of a slot for lanes past the last row
+  static constexpr bool GSPARE = SG > 1 && (((TM * LPR) % THREADS) || ((TN * LPR) % THREADS));
+  static constexpr int GSLOT = SG > 1 ? SG * GTILE + (GSPARE ? 16 : 0) : 0;
   static constexpr bool PERTILE = NSC && SG == 1;  // otherwise: scale loads with each tile
   static constexpr int SLA = PERTILE ? (TM + THREADS - 1) / THREADS : 0;   // A scale rows per thread
   static constexpr int SLB = PERTILE ? (TN + THREADS - 1) / THREADS : 0;   // B scale rows per thread
   static constexpr int SLOADS = SLA + SLB;
   static constexpr int SAREA = PERTILE ? SROWS * SCB + 16 : 0;   // + a spare slot for idle lanes
   static constexpr int GSTAGE = ST * ABUF;                            // A stages of one K group
-  static constexpr int STAGE = KG * GSTAGE + ST * SAREA + 3 * GSLOT;  // scale ring: 2 + a discard slot
+  static constexpr int STAGE = KG * GSTAGE + ST * SAREA + 2 * GSLOT;  // scale ring: 2 slots
   // FP8 / W4A8 per-row / per-column scales, fetched into LDS by DMA when the kernel
   // starts (so the epilogue does not wait a memory round trip for them):
   // 256-byte blocks of A scales (TM floats, padded to 64) then B scales.
@@ -188,10 +197,7 @@ __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uin
 }
 
 template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED, int KG>
-// One workgroup per CU once the accumulators alone take more than half of the
-// 256 registers two workgroups would leave each wave, or with two K groups;
-// two otherwise.
-__global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) void gemm_tile_kernel(TileArgs p) {
+__global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_tile_kernel(TileArgs p) {
   using C = TileCfg<DT, MS, TM, TN, TKB, EPI, PIPE, FUSED, KG>;
   using Acc = typename Mma<DT, MS>::Acc;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
@@ -427,8 +433,7 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
       }
     }
   };
-  // ... into slot `slot` of the ring: [tile of the group][row][lane group];
-  // slot 2 discards
+  // ... into slot `slot` (0 or 1) of the ring: [tile of the group][row][lane group]
   auto store_g = [&](int slot) {
     if constexpr (C::SG > 1) {
       char* base = lds + C::ST * C::ABUF + slot * C::GSLOT;
@@ -563,22 +568,26 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
   };
   using J0 = std::integral_constant<int, 0>;
   using JALL = std::integral_constant<int, NVMEM>;
-  auto iter = [&](auto r_c, int kt) {
+  // r: stage of tile kt (kt % ST); gpos: kt % SG
+  auto iter = [&](auto r_c, auto gpos_c, int kt) {
     constexpr int r = decltype(r_c)::value;
+    constexpr bool group_end = C::SG > 1 && decltype(gpos_c)::value == C::SG - 1;
     constexpr int rn = (r + C::ST - 1) % C::ST;  // stage of the tile ST-1 ahead
     // past the end the last tile reloads itself into a free stage instead of
     // branching, keeping the body one straight-line block
     const int kn = min(kt + C::ST - 1, KT - 1);
-    // FP4 scale group starting at the next tile: fetched now, staged at the
-    // end of this tile (its slot's previous group ended with tile kt-SG)
-    const bool next_group = C::SG > 1 && (kt + 1) % C::SG == 0 && kt + 1 < KT;
-    load_g(next_group ? (kt + 1) / C::SG : -1);
+    // FP4 scale group starting at the next tile (last tile of a group only):
+    // fetched now, staged at the end of this tile (its slot's previous group
+    // ended with tile kt-SG). Its loads are issued before the tile's own, so
+    // the wait at the end of the tile covers them. After the last tile the
+    // loads read zeros into a slot nobody reads again.
+    if constexpr (group_end) load_g(kt + 1 < KT ? (kt + 1) / C::SG : -1);
     compute(r_c, kt, [&](auto j0_c, auto j1_c) { loads(std::integral_constant<int, rn>{}, kn, j0_c, j1_c); });
     store_a(rn);
     // FP4 scales of the next tile, loaded ST-2 iterations ago (its stage is
     // free: its last reader was tile kt+1-ST)
     store_s((r + 1) % C::ST);
-    store_g(next_group ? ((kt + 1) / C::SG) & 1 : 2);
+    if constexpr (group_end) store_g(((kt + 1) / C::SG) & 1);
     if constexpr (C::ASYNC) {
       // tile kt+1's DMA was issued ST-2 iterations ago, before that
       // iteration's B loads: everything issued after it may stay in flight
@@ -603,12 +612,20 @@ __global__ __launch_bounds__(256 * KG, (KG > 1 || TM * TN / 256 > 128) ? 1 : 2) 
   }
   __syncthreads();
 
-  // ---- main loop, ST K tiles per trip ----
+  // ---- main loop, TRIP K tiles per trip (whole pipeline rounds and scale
+  // groups, so that stage and group position are compile-time); the tail
+  // has fewer than TRIP tiles and so no group boundary ----
+  constexpr int TRIP = C::SG > C::ST ? C::SG : C::ST;
+  static_assert(TRIP % C::ST == 0 && TRIP % C::SG == 0, "trip covers whole stages and groups");
   int kt = 0;
-  for (; kt + C::ST <= KT; kt += C::ST)
-    static_for<0, C::ST>([&](auto r_c) { iter(r_c, kt + decltype(r_c)::value); });
-  static_for<0, C::ST - 1>([&](auto r_c) {
-    if (kt + decltype(r_c)::value < KT) iter(r_c, kt + decltype(r_c)::value);
+  for (; kt + TRIP <= KT; kt += TRIP)
+    static_for<0, TRIP>([&](auto r_c) {
+      constexpr int r = decltype(r_c)::value;
+      iter(std::integral_constant<int, r % C::ST>{}, std::integral_constant<int, r % C::SG>{}, kt + r);
+    });
+  static_for<0, TRIP - 1>([&](auto r_c) {
+    constexpr int r = decltype(r_c)::value;
+    if (kt + r < KT) iter(std::integral_constant<int, r % C::ST>{}, std::integral_constant<int, r % C::SG>{}, kt + r);
   });
   // no DMA may still be writing LDS when the epilogue reuses it
   if constexpr (C::ASYNC) {

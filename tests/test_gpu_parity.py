@@ -107,6 +107,12 @@ TILE_CASES = [
     ("mxfp4", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
     ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
     ("mxfp4", 128, 256, 1280, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),   # 5 K tiles: two scale groups, the second partial
+    # 4-tile loop trips with a tail of 0-3 tiles after one or two trips
+    ("mxfp4", 128, 256, 1536, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),   # 6 K tiles
+    ("mxfp4", 128, 256, 1792, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),   # 7
+    ("mxfp4", 128, 256, 2048, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),   # 8
+    ("mxfp4", 128, 256, 2304, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),   # 9
+    ("mxfp4", 64, 128, 2816, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256)),                          # 11, 16 x 16 blocks
     # 256x256 tiles, one workgroup per CU (accumulators in AGPRs)
     ("bf16", 256, 512, 192, dict(kernel=1, tile_m=256, tile_n=256, tile_k=32, mfma=16, pipeline=3)),
     ("bf16", 512, 256, 224, dict(kernel=1, tile_m=256, tile_n=256, tile_k=32, mfma=16, pipeline=4)),
