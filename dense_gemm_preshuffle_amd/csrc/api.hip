@@ -381,9 +381,17 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     int abuf = p.kg * stages * (p.tm * tka + (apart ? 16 : 0));
     if (dt == DT_FP4) {   // staged E8M0 scales: per stage, or a ring of two slots of SG-tile groups
       if (stages == 2 && p.tkb == 128) {
-        // 4-tile groups, two lanes per row; 16 spare bytes for lanes past the rows
-        const int spare = ((p.tm * 2) % 256 || (p.tn * 2) % 256) ? 16 : 0;
-        abuf += 2 * (4 * (p.tm + p.tn) * 8 + spare);
+        // two slots of SG-tile groups (SG / 2 lanes per row, 16 spare bytes for
+        // lanes past the rows): SG = 8 where the whole LDS still fits the share
+        // of a resident workgroup, else 4
+        auto slot = [&](int sg) {
+          return sg * (p.tm + p.tn) * 8 + (((p.tm * sg / 2) % 256 || (p.tn * sg / 2) % 256) ? 16 : 0);
+        };
+        const int cb = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
+        const int share = 160 * 1024 / ((p.kg > 1 || p.tm * p.tn / 256 > 128) ? 1 : 2);
+        const int st8 = abuf + 2 * slot(8);
+        const int sg = (st8 > cb ? st8 : cb) + bias_lds * p.tn * 4 <= share ? 8 : 4;
+        abuf += 2 * slot(sg);
       } else {
         abuf += stages * ((p.tm + p.tn) * (p.tkb / 16) + 16);
       }

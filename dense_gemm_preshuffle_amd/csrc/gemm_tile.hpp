@@ -117,22 +117,38 @@ struct TileCfg {
   static constexpr int SCB = NSC ? TKB / 16 : 0;
   static constexpr int SROWS = NSC ? TM + TN : 0;
   // Scale groups: with a 2-stage pipeline and 8 scale bytes per row per tile,
-  // the scales of SG = 4 consecutive K tiles are fetched together (16 bytes
-  // per lane, two lanes per row) into a two-slot LDS ring, once every SG
-  // tiles (the main loop runs SG tiles per trip, so the tiles between issue
-  // no scale loads). A tile's TM + TN scale rows are as many separate cache
-  // lines; one gather of them per tile cost the texture path about as much
-  // as the tile's operand loads (the MXFP4 4096x4096x8192 kernel ran 15%
-  // faster with the gathers removed). (8-tile groups: their registers pushed
-  // the 128 x 256 tile's accumulators into scratch memory.)
-  static constexpr int SG = (NSC && ST == 2 && SCB == 8) ? 4 : 1;
+  // the scales of SG consecutive K tiles are fetched together (16 bytes per
+  // lane, SG/2 lanes per row) into a two-slot LDS ring. A tile's TM + TN
+  // scale rows are as many separate cache lines; one gather of them per tile
+  // cost the texture path about as much as the tile's operand loads (the
+  // MXFP4 4096x4096x8192 kernel ran 15% faster with the gathers removed).
+  // The NGL loads of a thread for group g+1 are spread over the SG tiles of
+  // group g, one or two per tile, each staged at the end of its tile (the
+  // main loop runs SG tiles per trip, so every tile knows its share at
+  // compile time). SG = 8 where both slots fit the LDS share of a resident
+  // workgroup, else 4.
+  static constexpr bool GROUPED = NSC && ST == 2 && SCB == 8;
   static constexpr int GTILE = SROWS * 8;                                  // staged bytes of one tile
+  static constexpr int LDS_SHARE = 160 * 1024 / tile_wgs_per_cu(TM, TN, KG);
+  static constexpr int slot_bytes(int sg) {
+    return sg * GTILE + ((((TM * sg / 2) % THREADS) || ((TN * sg / 2) % THREADS)) ? 16 : 0);
+  }
+  static constexpr int lds_with(int sg) {
+    const int stage = KG * ST * ABUF + 2 * slot_bytes(sg);
+    const int cb = (EPI == EPI_CSHUFFLE) ? TM * CSTRIDE : 0;
+    return (stage > cb ? stage : cb) + ((FUSED && DT != DT_I8) ? TN / 64 * 256 : 0);
+  }
+  static constexpr int SG = !GROUPED ? 1 : (lds_with(8) <= LDS_SHARE ? 8 : 4);
   static constexpr int LPR = SG > 1 ? SG * SCB / 16 : 0;                     // 16-byte lanes per row
   static constexpr int GLA = SG > 1 ? (TM * LPR + THREADS - 1) / THREADS : 0;  // group loads per thread
   static constexpr int GLB = SG > 1 ? (TN * LPR + THREADS - 1) / THREADS : 0;
+  static constexpr int NGL = GLA + GLB;
+  // group loads [gl_first(p), gl_first(p+1)) run in the tile at group position p
+  static constexpr int gl_first(int p) { return (p * NGL + SG - 1) / (SG > 1 ? SG : 1); }
+  static constexpr int GPP = SG > 1 ? (NGL + SG - 1) / SG : 0;               // most per tile
   // a spare 16 bytes after the tiles of a slot for lanes past the last row
   static constexpr bool GSPARE = SG > 1 && (((TM * LPR) % THREADS) || ((TN * LPR) % THREADS));
-  static constexpr int GSLOT = SG > 1 ? SG * GTILE + (GSPARE ? 16 : 0) : 0;
+  static constexpr int GSLOT = SG > 1 ? slot_bytes(SG) : 0;
   static constexpr bool PERTILE = NSC && SG == 1;  // otherwise: scale loads with each tile
   static constexpr int SLA = PERTILE ? (TM + THREADS - 1) / THREADS : 0;   // A scale rows per thread
   static constexpr int SLB = PERTILE ? (TN + THREADS - 1) / THREADS : 0;   // B scale rows per thread
@@ -160,7 +176,7 @@ struct TileCfg {
   // LDS read on its own.
   static constexpr int ACCR = TM * TN / 256;
   static constexpr int BREG = ST * KSTEPS * NACC * FRAG * 4 + (DT == DT_I4 ? NACC * 8 : 0);  // + widened INT4
-  static constexpr int SREG = NSC ? MREP + NACC + 2 * ST * (SLA + SLB) + 4 * (GLA + GLB) : 0;
+  static constexpr int SREG = NSC ? MREP + NACC + 2 * ST * (SLA + SLB) + 4 * GPP : 0;
   static constexpr int RBASE = (ACCR > 128 ? 0 : ACCR) + BREG + SREG;
   static constexpr int RA = (AFRAG == 1 && RBASE + 12 <= 236) ? 2 : (RBASE + 2 * AFRAG * 4 <= 236) ? 1 : 0;
   static_assert(TM % MS == 0 && NPW % MS == 0 && TN % 64 == 0, "tile shape");
@@ -340,7 +356,6 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   // FP4 scales of each in-flight tile, by stage (stored to LDS one tile ahead),
   // or of the next scale group
   v2i sa_st[C::ST][C::SLA + (C::SLA == 0)], sb_st[C::ST][C::SLB + (C::SLB == 0)];
-  v4i ga_st[C::GLA + (C::GLA == 0)], gb_st[C::GLB + (C::GLB == 0)];
   Acc acc[C::MREP][C::NACC];
 #pragma unroll
   for (int mi = 0; mi < C::MREP; ++mi)
@@ -409,47 +424,41 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     if constexpr (C::SCB == 8) *(v2i*)(base + r * 8) = perm_s(v);
     else *(int*)(base + r * 4) = v[0];
   };
-  // Scale group g (tiles SG*g .. SG*g+SG-1): group load i of a thread covers
+  // Scale group g (tiles SG*g .. SG*g+SG-1): group load j of a thread (A
+  // rows for j < GLA, then B rows; i = its index within them) covers
   // lane-load q = i*THREADS + tid, row q / LPR, 16-byte piece q % LPR, i.e.
   // tiles 2*piece and 2*piece+1 of the group. The whole offset (row and K)
   // is the per-lane one, so that a piece past the end of the scale rows (the
   // last group of a K not a multiple of SG tiles) reads zeros.
-  // g < 0: every lane reads outside its resource (zeros, no memory access),
-  // so that tiles without a group to fetch run the same code
-  auto load_g = [&](int g) {
-    if constexpr (C::SG > 1) {
-      const uint32_t gbase = (uint32_t)g * (C::SG * C::SCB);
-#pragma unroll
-      for (int i = 0; i < C::GLA; ++i) {
-        const int q = i * C::THREADS + tid;
-        const uint32_t off = (q < TM * C::LPR && g >= 0) ? (q / C::LPR) * srow + (q % C::LPR) * 16 + gbase : kOOB;
-        ga_st[i] = buf_load16(rsa, off, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < C::GLB; ++i) {
-        const int q = i * C::THREADS + tid;
-        const uint32_t off = (q < TN * C::LPR && g >= 0) ? (q / C::LPR) * srow + (q % C::LPR) * 16 + gbase : kOOB;
-        gb_st[i] = buf_load16(rsb, off, 0);
-      }
-    }
+  // g < 0: every lane reads outside its resource (zeros, no memory access).
+  // Per-lane parts of a group load's global and LDS offsets (row tid / LPR,
+  // piece tid % LPR of the load's first row); each load adds a uniform part.
+  constexpr int GL_LPR = C::LPR > 0 ? C::LPR : 1;
+  constexpr int GL_RSTEP = C::THREADS / GL_LPR;   // rows per load
+  const uint32_t g_loff = (tid / GL_LPR) * srow + (tid % GL_LPR) * 16;
+  const int g_lds = (tid % GL_LPR) * 2 * C::GTILE + (tid / GL_LPR) * 8;
+  auto load_g1 = [&](auto j_c, int g) -> v4i {
+    constexpr int j = decltype(j_c)::value;
+    constexpr bool is_a = j < C::GLA;
+    constexpr int i = is_a ? j : j - C::GLA;
+    bool on = g >= 0;
+    if constexpr (C::GSPARE) on = on && i * C::THREADS + tid < (is_a ? TM : TN) * C::LPR;
+    const uint32_t u = __builtin_amdgcn_readfirstlane(i * GL_RSTEP * srow + (uint32_t)g * (C::SG * C::SCB));
+    return buf_load16(is_a ? rsa : rsb, on ? g_loff + u : kOOB, 0);
   };
   // ... into slot `slot` (0 or 1) of the ring: [tile of the group][row][lane group]
-  auto store_g = [&](int slot) {
-    if constexpr (C::SG > 1) {
-      char* base = lds + C::ST * C::ABUF + slot * C::GSLOT;
-      auto put2 = [&](int q, int nrows, int row0, v4i v) {
-        const int pc = q % C::LPR;
-        const bool on = q < nrows * C::LPR;
-        char* d0 = on ? base + (2 * pc) * C::GTILE + (row0 + q / C::LPR) * 8 : base + C::SG * C::GTILE;
-        char* d1 = on ? d0 + C::GTILE : d0;
-        *(v2i*)d0 = perm_s(v2i{v[0], v[1]});
-        *(v2i*)d1 = perm_s(v2i{v[2], v[3]});
-      };
-#pragma unroll
-      for (int i = 0; i < C::GLA; ++i) put2(i * C::THREADS + tid, TM, 0, ga_st[i]);
-#pragma unroll
-      for (int i = 0; i < C::GLB; ++i) put2(i * C::THREADS + tid, TN, TM, gb_st[i]);
+  auto store_g1 = [&](auto j_c, int slot, v4i v) {
+    constexpr int j = decltype(j_c)::value;
+    constexpr bool is_a = j < C::GLA;
+    constexpr int i = is_a ? j : j - C::GLA;
+    char* base = lds + C::ST * C::ABUF + slot * C::GSLOT;
+    char* d0 = base + g_lds + ((is_a ? 0 : TM) + i * GL_RSTEP) * 8;
+    if constexpr (C::GSPARE) {
+      if (!(i * C::THREADS + tid < (is_a ? TM : TN) * C::LPR)) d0 = base + C::SG * C::GTILE;   // spare slot
     }
+    char* d1 = d0 + ((!C::GSPARE || i * C::THREADS + tid < (is_a ? TM : TN) * C::LPR) ? C::GTILE : 0);
+    *(v2i*)d0 = perm_s(v2i{v[0], v[1]});
+    *(v2i*)d1 = perm_s(v2i{v[2], v[3]});
   };
   auto store_s = [&](int par) {
     if constexpr (DT == DT_FP4) {
@@ -571,23 +580,30 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   // r: stage of tile kt (kt % ST); gpos: kt % SG
   auto iter = [&](auto r_c, auto gpos_c, int kt) {
     constexpr int r = decltype(r_c)::value;
-    constexpr bool group_end = C::SG > 1 && decltype(gpos_c)::value == C::SG - 1;
+    constexpr int gpos = decltype(gpos_c)::value;
     constexpr int rn = (r + C::ST - 1) % C::ST;  // stage of the tile ST-1 ahead
     // past the end the last tile reloads itself into a free stage instead of
     // branching, keeping the body one straight-line block
     const int kn = min(kt + C::ST - 1, KT - 1);
-    // FP4 scale group starting at the next tile (last tile of a group only):
-    // fetched now, staged at the end of this tile (its slot's previous group
-    // ended with tile kt-SG). Its loads are issued before the tile's own, so
-    // the wait at the end of the tile covers them. After the last tile the
-    // loads read zeros into a slot nobody reads again.
-    if constexpr (group_end) load_g(kt + 1 < KT ? (kt + 1) / C::SG : -1);
+    // FP4: this tile's share of the loads of the next scale group, staged at
+    // the end of the tile into the slot the previous group left (its last
+    // reader, tile SG*(kt/SG)-1, is behind the barrier that ended it). They
+    // are issued before the tile's own loads, so the wait at the end of the
+    // tile covers them. A group past the last tile reads zeros.
+    constexpr int gj0 = C::gl_first(gpos), gj1 = C::gl_first(gpos + 1);
+    v4i gv[gj1 > gj0 ? gj1 - gj0 : 1];
+    const int gnext = kt / C::SG + 1;
+    if constexpr (gj1 > gj0) {
+      const int g = gnext * C::SG < KT ? gnext : -1;
+      static_for<gj0, gj1>([&](auto j_c) { gv[decltype(j_c)::value - gj0] = load_g1(j_c, g); });
+    }
     compute(r_c, kt, [&](auto j0_c, auto j1_c) { loads(std::integral_constant<int, rn>{}, kn, j0_c, j1_c); });
     store_a(rn);
     // FP4 scales of the next tile, loaded ST-2 iterations ago (its stage is
     // free: its last reader was tile kt+1-ST)
     store_s((r + 1) % C::ST);
-    if constexpr (group_end) store_g(((kt + 1) / C::SG) & 1);
+    if constexpr (gj1 > gj0)
+      static_for<gj0, gj1>([&](auto j_c) { store_g1(j_c, gnext & 1, gv[decltype(j_c)::value - gj0]); });
     if constexpr (C::ASYNC) {
       // tile kt+1's DMA was issued ST-2 iterations ago, before that
       // iteration's B loads: everything issued after it may stay in flight
@@ -598,14 +614,15 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   };
 
   // ---- prologue: tiles 0 .. ST-2 into stages 0 .. ST-2 ----
-  load_g(0);
+  v4i g0[C::NGL > 0 ? C::NGL : 1];   // scale group 0
+  if constexpr (C::SG > 1) static_for<0, C::NGL>([&](auto j_c) { g0[decltype(j_c)::value] = load_g1(j_c, 0); });
   static_for<0, C::ST - 1>([&](auto j_c) {
     constexpr int j = decltype(j_c)::value;
     loads(j_c, min(j, KT - 1), J0{}, JALL{});
     store_a(j);
   });
   store_s(0);
-  store_g(0);
+  if constexpr (C::SG > 1) static_for<0, C::NGL>([&](auto j_c) { store_g1(j_c, 0, g0[decltype(j_c)::value]); });
   if constexpr (C::ASYNC) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vm(std::integral_constant<int, NBL + (C::ST - 2) * NVMEM>{});

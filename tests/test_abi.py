@@ -256,10 +256,12 @@ def test_tile_must_fit_inside_the_problem():
 
 def test_fp4_plan_lds_matches_scale_groups():
     """MXFP4 with a 2-stage pipeline stages scales as a ring of two slots of
-    4-tile groups (4 x (TM+TN) x 8 bytes each) beside the A stages."""
+    8-tile groups (8 x (TM+TN) x 8 bytes each) beside the A stages: for the
+    128 x 256 tile exactly the 80 KiB share of each of two workgroups per CU."""
     p = gp.gemm_plan("mxfp4", 4096, 4096, 8192)
     assert p["pipeline"] == 2 and p["tile_k"] == 256 and (p["tile_m"], p["tile_n"]) == (128, 256)
-    stages = 2 * p["tile_m"] * 128 + 2 * (4 * (p["tile_m"] + p["tile_n"]) * 8)
+    stages = 2 * p["tile_m"] * 128 + 2 * (8 * (p["tile_m"] + p["tile_n"]) * 8)
+    assert stages == 80 * 1024
     cshuffle = p["tile_m"] * (p["tile_n"] * 2 + 16) if p["epilogue"] == gp.EPI_CSHUFFLE else 0
     assert p["lds_bytes"] == max(stages, cshuffle)
 
