@@ -280,6 +280,7 @@ EPI_CASES = [
     ("bf16", 256, 512, 192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, pipeline=3)),
     ("bf16", 128, 256, 128, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, mfma=32, epilogue=1)),
     ("mxfp4", 128, 256, 512, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
+    ("mxfp4", 128, 256, 2560, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),  # 3 scale groups
     ("mxfp4", 16, 128, 2048, dict(kernel=2)),
     ("fp16", 128, 256, 256, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64)),
     ("bf16", 512, 256, 320, dict(kernel=3)),
@@ -444,7 +445,8 @@ FP4_PLACEMENT_OPTS = [dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=16)
 def test_fp4_block_scale_placement_bit_exact(opts):
     say(f"fp4 scale placement {opts}")
     rng = np.random.default_rng(4)
-    M, N, K = (128, 256, 1024) if opts["kernel"] == 1 else (16, 64, 1024)
+    # tile kernel: 16 K tiles, so the marked blocks spread over two or four scale groups
+    M, N, K = (128, 256, 4096) if opts["kernel"] == 1 else (16, 64, 1024)
     nblk = K // 32
     blk = rng.integers(0, nblk, size=M)                  # row m is 1.0 on block blk[m] only
     ca = np.zeros((M, K), np.uint8)
