@@ -498,7 +498,7 @@ def test_bitwise_repeatable():
 
 
 @pytest.mark.parametrize("dtype,M,N,K,act", [("fp8", 16, 7168, 2048, None), ("w4a8", 16, 7168, 2048, "gelu"),
-                                            ("bf16", 512, 512, 1024, None), ("mxfp4", 256, 512, 1024, None),
+                                            ("bf16", 512, 512, 1024, None), ("mxfp4", 256, 512, 4096, None),
                                             ("fp8", 512, 1024, 1024, "silu"), ("fp16", 300, 272, 512, None),
                                             ("w4a8", 512, 1024, 1024, "relu"), ("int8", 512, 1024, 1024, None),
                                             ("bf16", 1000, 16, 64, None)])
@@ -528,7 +528,7 @@ def test_graph_replay_matches_eager():
     from dense_gemm_preshuffle_amd import workload
 
     say("graph replay")
-    for dtype, M, N, K in [("fp8", 16, 7168, 2048), ("bf16", 256, 512, 256), ("mxfp4", 128, 256, 512),
+    for dtype, M, N, K in [("fp8", 16, 7168, 2048), ("bf16", 256, 512, 256), ("mxfp4", 128, 256, 4608),
                            ("w4a8", 256, 512, 1024), ("int8", 16, 16, 64)]:
         host = workloads.make_inputs(dtype, M, N, K, seed=31)
         p = workload.prepare(dtype, workload.to_device(dtype, host))
