@@ -337,7 +337,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     // (two per CU, or one for tiles whose accumulators fill half the
     // registers); direct stores otherwise
     const int cbytes = p->tm * (p->tn * ob + 16);
-    const int wgs_per_cu = (p->tm * p->tn / 256 > 128) ? 1 : 2;
+    const int wgs_per_cu = tile_wgs_per_cu(p->tm, p->tn, p->kg);
     p->epi = (p->tn >= 128 && cbytes <= 160 * 1024 / wgs_per_cu) ? EPI_CSHUFFLE : EPI_DIRECT;
   }
   p->xcd = (o && o->xcd_swizzle) ? o->xcd_swizzle : 1;
@@ -388,7 +388,7 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
           return sg * (p.tm + p.tn) * 8 + (((p.tm * sg / 2) % 256 || (p.tn * sg / 2) % 256) ? 16 : 0);
         };
         const int cb = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
-        const int share = 160 * 1024 / ((p.kg > 1 || p.tm * p.tn / 256 > 128) ? 1 : 2);
+        const int share = 160 * 1024 / tile_wgs_per_cu(p.tm, p.tn, p.kg);
         const int st8 = abuf + 2 * slot(8);
         const int sg = (st8 > cb ? st8 : cb) + bias_lds * p.tn * 4 <= share ? 8 : 4;
         abuf += 2 * slot(sg);
