@@ -97,9 +97,10 @@ enum {
 /* Tuning options. Pass NULL, or a zero-filled struct, for all-automatic;
  * a zero field means "planner's choice". tile_k is in ELEMENTS (as on the
  * pages). For the split-K kernel tile_m is 16, 32 or 64 (16-row blocks per
- * workgroup; 64 runs on 8 waves unless waves says otherwise), tile_n is 16 * (column blocks per workgroup) and tile_k is the
- * K chunk each wave loads per step. A tile
- * that is not compiled into the library is GP_ESHAPE. */
+ * workgroup; 64 runs on 8 waves unless waves says otherwise), tile_n is
+ * 16 * (column blocks per workgroup) and tile_k is the K chunk each wave
+ * loads per step. A tile that is not compiled into the library is
+ * GP_ESHAPE. */
 typedef struct gemm_opts {
   int tile_m, tile_n, tile_k;
   int epilogue;     /* GP_EPI_*                                          */
