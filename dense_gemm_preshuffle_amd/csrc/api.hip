@@ -15,6 +15,10 @@ namespace {
 
 constexpr int64_t kMaxBytes = (int64_t)1 << 31;  // 32-bit buffer offsets
 
+// rows * row_bytes < kMaxBytes, decided without forming the product (rows and
+// row_bytes are positive; a product of two sizes near 2^62 would overflow)
+bool fits(int64_t rows, int64_t row_bytes) { return row_bytes < kMaxBytes && rows <= (kMaxBytes - 1) / row_bytes; }
+
 // Bits per element of B (and of A, except W4A8 whose A is int8).
 int elem_bits(int dt) {
   switch (dt) {
@@ -271,6 +275,9 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   if (M <= 0 || N <= 0 || K <= 0) return GP_EINVAL;
   const int bits = elem_bits(in_dtype);
   if (bits == 0) return GP_EDTYPE;
+  // every buffer is under 2^31 bytes, so no single size reaches it either;
+  // rejected first, so that no product below can overflow
+  if (M >= kMaxBytes || N >= kMaxBytes || K >= kMaxBytes) return GP_ESHAPE;
   if (o) {
     if (o->tile_m < 0 || o->tile_n < 0 || o->tile_k < 0 || o->waves < 0) return GP_EINVAL;
     if (o->epilogue < 0 || o->epilogue > 2 || o->kernel < 0 || o->kernel > 3) return GP_EINVAL;
@@ -287,7 +294,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   // W4A8 accumulates 16 x the products in int32 (|a| <= 128, |b| <= 8)
   if (in_dtype == GP_I4 && K > 65536) return GP_ESHAPE;
   const int ob = in_dtype == GP_I8 ? 4 : 2;
-  if (M * Ka >= kMaxBytes || N * Kb >= kMaxBytes || M * N * ob >= kMaxBytes) return GP_ESHAPE;
+  if (!fits(M, Ka) || !fits(N, Kb) || !fits(M, N * ob)) return GP_ESHAPE;
   const int dt = kdt(in_dtype);
   p->Kb = Kb;
   // small M (up to 64 rows): the split-K kernel; on 64 x 7168 x 2048 it
@@ -623,9 +630,9 @@ int gemm_preshuffle_b(const void* b, void* b_shuf, int64_t N, int64_t K, int dty
   if (!b || !b_shuf || !aligned16(b) || !aligned16(b_shuf) || N <= 0 || K <= 0) return GP_EINVAL;
   const int bits = elem_bits(dtype);
   if (bits == 0) return GP_EDTYPE;
-  if ((K * bits) % 8) return GP_ESHAPE;
+  if (N >= kMaxBytes || K >= kMaxBytes || (K * bits) % 8) return GP_ESHAPE;
   const int64_t Kb = K * bits / 8;
-  if (N % 16 || Kb % 64 || N * Kb >= kMaxBytes) return GP_ESHAPE;
+  if (N % 16 || Kb % 64 || !fits(N, Kb)) return GP_ESHAPE;
   const char* bb = (const char*)b;
   const char* be = bb + N * Kb;
   const char* sb = (const char*)b_shuf;

@@ -129,6 +129,18 @@ def _mutants():
         m, e = np.frexp(x)
         return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)
 
+    def f16_rne_10_bits(x):
+        x = np.asarray(x, dtype=np.float64)
+        m, e = np.frexp(x)
+        return np.ldexp(np.round(np.ldexp(m, 10)), e - 10)
+
+    orig_dispatch = g._gemm
+
+    def mxfp4_dispatch_swapped_scales(dtype, inputs, rows, cols):
+        if dtype == "mxfp4":
+            return g.gemm_mxfp4(inputs["a"], inputs["scale_b"], inputs["b"], inputs["scale_a"], rows, cols)
+        return orig_dispatch(dtype, inputs, rows, cols)
+
     orig_bytes = fo.bytes_moved
 
     def bytes_without_scales(dtype, M, N, K, out_bytes=2):
@@ -170,6 +182,8 @@ def _mutants():
         "bytes_without_scales": [("bytes_moved", bytes_without_scales)],
         "mfma_count_k_doubled": [("mfma_count_gfx950", mfma_count_k_doubled)],
         "flops_single": [("flops", flops_single)],
+        "f16_rne_10_bits": [("f16_rne", f16_rne_10_bits)],
+        "mxfp4_dispatch_swapped_scales": [("_gemm", mxfp4_dispatch_swapped_scales)],
     }, (oracle, f, g, c, lay, fo)
 
 
@@ -178,7 +192,7 @@ NAMES = (
     "e8m0_off_by_one", "bf16_wrong_shift", "int4_unsigned", "nibbles_high_first", "preshuffle_swapped",
     "gelu_tanh", "silu_sign", "bias_after_activation", "mx_scales_shifted", "w4a8_drop_scale_b",
     "int8_as_unsigned", "bf16_rne_truncate", "compare_ignores_elementwise", "bytes_without_scales",
-    "mfma_count_k_doubled", "flops_single",
+    "mfma_count_k_doubled", "flops_single", "f16_rne_10_bits", "mxfp4_dispatch_swapped_scales",
 )
 
 

@@ -72,6 +72,21 @@ def test_sizes_and_shapes(fake_ptrs):
     assert lib.gemm_bf16(FAKE, FAKE, FAKE, 65536, 65536, 65536, None, None) == GP_ESHAPE
 
 
+@pytest.mark.parametrize("M,N,K", [(2 ** 61 + 64, 16, 64), (64, 2 ** 61 + 16, 64), (64, 16, 2 ** 61 + 64),
+                                   (2 ** 31, 16, 64), (2 ** 30, 2 ** 30, 64), (2 ** 62, 2 ** 62, 2 ** 62)])
+def test_huge_sizes_are_rejected_without_overflow(M, N, K):
+    """Sizes whose byte counts overflow int64 when multiplied are GP_ESHAPE,
+    not a plan for the wrapped-around size (host-only planner query)."""
+    info = gp.GemmPlanInfo()
+    for dt in (0, 1, 2, 3, 5, 6):
+        assert gp.load_library().gemm_plan(dt, M, N, K, None, ctypes.byref(info)) == GP_ESHAPE, (dt, M, N, K)
+
+
+@pytest.mark.parametrize("N,K", [(2 ** 61 + 16, 64), (16, 2 ** 61 + 64), (2 ** 30, 64), (2 ** 62, 2 ** 62)])
+def test_huge_preshuffle_sizes_are_rejected(fake_ptrs, N, K):
+    assert fake_ptrs.gemm_preshuffle_b(FAKE, ctypes.c_void_p(0x900000), N, K, 0, None) == GP_ESHAPE
+
+
 def test_dtype_pairs(fake_ptrs):
     lib = fake_ptrs
     S = ctypes.c_void_p(0x200000)

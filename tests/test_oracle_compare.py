@@ -82,3 +82,52 @@ def test_nonfinite_fails():
 
 def test_tolerances():
     assert oracle.NORMWISE_TOL == 2e-3 and oracle.ELEM_TOL == 1e-2
+
+
+# ---------------------------------------------------------------- fp16 / bf16 rounding helpers
+def _f16_normals():
+    """Every finite positive normal binary16 value, ascending, as float64."""
+    bits = np.arange(0x0400, 0x7C00, dtype=np.uint16)
+    return bits.view(np.float16).astype(np.float64)
+
+
+def test_f16_rne_matches_numpy_on_every_normal_value():
+    v = _f16_normals()
+    for s in (1.0, -1.0):
+        assert np.array_equal(oracle.f16_rne(s * v), s * v)
+
+
+def test_f16_rne_ties_and_neighbours_match_numpy():
+    """Exact midpoints between consecutive normal binary16 values (ties go to
+    the even significand), and the float64 values one ulp either side of
+    each midpoint (they round down / up): numpy's binary64 -> binary16 cast
+    rounds once, to nearest even."""
+    v = _f16_normals()
+    mid = (v[:-1] + v[1:]) / 2.0                 # exact in float64
+    for x in (mid, np.nextafter(mid, 0.0), np.nextafter(mid, np.inf)):
+        for s in (1.0, -1.0):
+            ref = (s * x).astype(np.float16).astype(np.float64)
+            assert np.array_equal(oracle.f16_rne(s * x), ref)
+    # ties to even: the midpoint goes to the neighbour whose last significand bit is 0
+    lo_bits = np.arange(0x0400, 0x7BFF, dtype=np.uint16)
+    even_lo = (lo_bits & 1) == 0
+    got = oracle.f16_rne(mid)
+    assert np.array_equal(got[even_lo], v[:-1][even_lo]) and np.array_equal(got[~even_lo], v[1:][~even_lo])
+
+
+def test_f16_rne_random_values_match_numpy():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(200000) * np.exp2(rng.integers(-13, 15, 200000))
+    x = x[(np.abs(x) >= 2.0 ** -14) & (np.abs(x) < 65504.0)]
+    assert np.array_equal(oracle.f16_rne(x), x.astype(np.float16).astype(np.float64))
+    assert oracle.f16_rne(np.array([0.0]))[0] == 0.0
+
+
+def test_bf16_rne_ties_go_to_even():
+    """Midpoints of consecutive bf16 values are exact in fp32; torch's
+    fp32 -> bf16 cast rounds them to the even neighbour."""
+    bits = np.arange(0x0080, 0x7F80, dtype=np.uint32)           # positive normal bf16
+    v = (bits << 16).view(np.float32).astype(np.float64)
+    mid = ((v[:-1] + v[1:]) / 2.0).astype(np.float32)
+    ref = torch.from_numpy(mid).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(bf16_rne(mid.astype(np.float64)), ref)

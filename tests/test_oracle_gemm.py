@@ -285,3 +285,38 @@ def test_dispatch_new_types():
     assert np.array_equal(oracle.gemm("w4a8", h), oracle.gemm_w4a8(h["a"], h["b"], h["scale_a"], h["scale_b"]))
     h = workloads.make_inputs("fp16", 16, 32, 128, 1)
     assert np.array_equal(oracle.gemm("fp16", h), oracle.gemm_f16(h["a"], h["b"]))
+
+
+@pytest.mark.parametrize("dtype", ["int8", "fp8", "bf16", "mxfp4", "fp16", "w4a8"])
+@pytest.mark.parametrize("M,N", [(32, 32), (16, 48)])
+def test_dispatch_routes_every_type(dtype, M, N):
+    """oracle.gemm(dtype, inputs) is the type's own function on the same
+    arrays, with the operands and their scales in their places (M == N too,
+    where swapped row / column scales would keep every shape)."""
+    import workloads
+
+    K = 256
+    h = workloads.make_inputs(dtype, M, N, K, seed=M + N)
+    direct = {
+        "int8": lambda r, c: oracle.gemm_int8(h["a"], h["b"], r, c),
+        "fp8": lambda r, c: oracle.gemm_fp8(h["a"], h["b"], h["scale_a"], h["scale_b"], r, c),
+        "bf16": lambda r, c: oracle.gemm_bf16(h["a"], h["b"], r, c),
+        "mxfp4": lambda r, c: oracle.gemm_mxfp4(h["a"], h["scale_a"], h["b"], h["scale_b"], r, c),
+        "fp16": lambda r, c: oracle.gemm_f16(h["a"], h["b"], r, c),
+        "w4a8": lambda r, c: oracle.gemm_w4a8(h["a"], h["b"], h["scale_a"], h["scale_b"], r, c),
+    }[dtype]
+    assert np.array_equal(oracle.gemm(dtype, h), direct(None, None))
+    rows, cols = np.array([0, 3, M - 1]), np.array([1, N - 2])
+    assert np.array_equal(oracle.gemm(dtype, h, rows, cols), direct(rows, cols))
+    if "scale_a" in h:
+        # the row scales really are per row and the column scales per column:
+        # doubling scale_a of row 0 doubles row 0 only
+        h2 = dict(h)
+        sa = np.array(h["scale_a"], copy=True)
+        if dtype == "mxfp4":
+            sa[0] = sa[0] + 1                    # E8M0: one more in the exponent doubles
+        else:
+            sa[0] = sa[0] * 2
+        h2["scale_a"] = sa
+        r1, r2 = oracle.gemm(dtype, h), oracle.gemm(dtype, h2)
+        assert np.array_equal(r2[0], 2 * r1[0]) and np.array_equal(r2[1:], r1[1:])
