@@ -1,16 +1,24 @@
 """Benchmark of the preshuffle GEMM on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
-                    [--act none|relu|silu|gelu]
+                    [--configs metric|none] [--act none|relu|silu|gelu]
 
 A step is one GEMM call (A, preshuffled B and scales already resident in
 HBM) on the workload's synthetic inputs. The default workload is the FP8
 small-batch GEMM M=16, N=7168, K=2048, whose metric is HBM GB/s; the
 compute-bound workloads report TFLOP/s. To keep B from being served by the
 256 MB last-level cache, each step uses the next of R device-resident copies
-of the inputs, with R large enough that the copies together exceed 640 MB.
+of the inputs, with R large enough that the copies together exceed 640 MB,
+and one untimed pass over all R copies runs right before the timed region,
+so that every timed step finds its inputs last touched R steps earlier.
 
-One JSON line per workload carries the throughput, the roofline of the GEMM
+By default the one JSON line also carries, under `configs`, the same
+figures for each of the five workloads of the headline metric (INT8
+128x256x512, FP8 16x7168x2048, FP8 512x4096x4096, BF16 8192^3, MXFP4
+4096x4096x8192), each timed the same way; --configs none leaves them out.
+With --workload all, one line per workload is printed instead.
+
+The line carries the throughput, the roofline of the GEMM
 kernel (measured with HIP events on the launch stream over the timed
 region; for MFMA-bound shapes also the fraction of the dense peak at the
 shader clock sampled from sysfs while the same launches repeat), the B preshuffle pass timed separately (a one-time weight
@@ -65,39 +73,58 @@ def workload_numbers(name, act=None):
     return dtype, M, N, K, seed, flops, nbytes, bound
 
 
-def cpu_baseline(name, host, budget_s=12.0, act=None):
-    """Time the oracle (as it is) on a bounded sample of the workload."""
+def _time_oracle(dtype, host, sel, act, budget_s):
+    """Repeat the oracle on rows `sel` for about budget_s seconds; (calls, seconds)."""
     import oracle
 
-    dtype, M, N, K, seed, flops, nbytes, bound = workload_numbers(name, act)
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    # sample: a block of rows (all columns) sized to about one second per call
-    per_row = 2.0 * N * K
-    rows = int(min(M, max(16, 2e10 / per_row)))
-    sel = np.arange(rows)
     calls, t0 = 0, time.perf_counter()
     while True:
         oracle.gemm(dtype, host, rows=sel, act=act)
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s or (calls >= 1 and el * (calls + 1) / calls > 2 * budget_s):
-            break
+            return calls, el
+
+
+def cpu_baseline(name, host, budget_s=12.0, act=None, single_thread_s=0.0):
+    """Time the oracle (as it is) on a bounded sample of the workload, with
+    the BLAS threads it runs with by default (`cores`) and, when
+    single_thread_s > 0, also on one thread."""
+    dtype, M, N, K, seed, flops, nbytes, bound = workload_numbers(name, act)
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+        cores = os.cpu_count() or 1
+    # sample: a block of rows (all columns) sized to about one second per call
+    per_row = 2.0 * N * K
+    rows = int(min(M, max(16, 2e10 / per_row)))
+    sel = np.arange(rows)
     frac = rows / M
-    per_call_s = el / calls
-    if bound == "hbm":
-        value = nbytes * frac / per_call_s / 1e9
-        unit = "GB/s"
-    else:
-        value = flops * frac / per_call_s / 1e12
-        unit = "TFLOP/s"
-    return {"value": value, "unit": unit, "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows} of {M} rows x all {N} columns, K={K}, {calls} call(s) in {el:.1f} s "
-                      f"(decode + float64 matmul)", "host_cpu": _cpu_model()}
+
+    def rate(calls, el):
+        per_call_s = el / calls
+        return (nbytes * frac / per_call_s / 1e9) if bound == "hbm" else (flops * frac / per_call_s / 1e12)
+
+    calls, el = _time_oracle(dtype, host, sel, act, budget_s)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        affinity = None
+    out = {"value": rate(calls, el), "unit": "GB/s" if bound == "hbm" else "TFLOP/s", "cores": int(cores),
+           "kind": "oracle",
+           "sample": f"{rows} of {M} rows x all {N} columns, K={K}, {calls} call(s) in {el:.1f} s "
+                     f"(decode + float64 matmul)",
+           "host_cpu": _cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": affinity,
+           "seconds_full_problem": el / calls / frac}
+    if single_thread_s > 0 and threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            c1, e1 = _time_oracle(dtype, host, sel, act, single_thread_s)
+        out["single_thread"] = {"value": rate(c1, e1), "seconds_full_problem": e1 / c1 / frac,
+                                "sample": f"{rows} rows, {c1} call(s) in {e1:.1f} s"}
+    return out
 
 
 def _cpu_model():
@@ -111,7 +138,7 @@ def _cpu_model():
 
 
 def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib_mib=0, act=None, data="randn",
-              telemetry_s=0.4):
+              telemetry_s=0.4, cpu_budget_s=12.0, cpu_single_s=0.0):
     import torch
 
     import dense_gemm_preshuffle_amd as gp
@@ -144,7 +171,7 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
 
     # rotation copies so that every step reads its operands from HBM
     set_bytes = nbytes
-    R = max(1, min(64, math.ceil(ROTATE_BYTES / set_bytes)))
+    R = max(2, min(64, math.ceil(ROTATE_BYTES / set_bytes)))
     sets = [p0]
     for _ in range(R - 1):
         q = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in p0.items()}
@@ -187,17 +214,31 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
         del warm_graph
 
     # timed region: the same K launches captured once in a HIP graph and
-    # replayed, so the GPU sees back-to-back GEMMs without host launch gaps
-    graph = None
+    # replayed, so the GPU sees back-to-back GEMMs without host launch gaps.
+    # Launch i uses input set i % R. Right before it, one launch on each of
+    # the R sets in the same order (the pre-roll, untimed): every timed launch
+    # then finds its inputs last touched exactly R launches (R * set bytes,
+    # over 640 MB) earlier, whatever K is, so none of them is served by the
+    # 256 MB last-level cache.
+    graph = roll = None
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(steps):
                 workload.run(dtype, sets[i % R], opts=opts, c=outs[i % R], act=act)
+        roll = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(roll):
+            for i in range(R):
+                workload.run(dtype, sets[i], opts=opts, c=outs[i], act=act)
         graph.replay()
         torch.cuda.synchronize()
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    if roll is not None:
+        roll.replay()
+    else:
+        for i in range(R):
+            workload.run(dtype, sets[i], opts=opts, c=outs[i], act=act)
     t_start.record(stream)
     if graph is not None:
         graph.replay()
@@ -229,7 +270,8 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
         "config": {"workload": name, "M": M, "N": N, "K": K, "kernel": plan["kernel"],
                    "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]], "grid": plan["grid"],
                    "epilogue": plan["epilogue"], "fused_epilogue": f"bias+{act}" if act else None,
-                   "rotating_sets": R},
+                   "rotating_sets": R, "sets_touched_in_timed_region": min(steps, R),
+                   "reuse_distance_mib": round(R * set_bytes / 2**20, 1)},
         "roofline": roof,
         "tflops": tflops, "gbps": gbps, "us_per_gemm": sec * 1e6,
         "preshuffle_b": {"us": pre_us, "GB/s": 2 * b_bytes / (pre_us * 1e-6) / 1e9,
@@ -242,6 +284,9 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
     tr = _traffic(name + (f"+{act}" if act else ""), plan)
     if tr is not None:
         roof["traffic"] = tr
+        roof["traffic_source"] = ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, scaled by a plain copy of known "
+                                  "size: bytes between the L2 caches and the memory fabric, an upper bound on "
+                                  "HBM bytes (the 256 MB last-level cache may serve part of them)")
     if warm_s is not None:
         line["warm"] = {"us_per_gemm": warm_s * 1e6,
                         "value": (nbytes / warm_s / 1e9) if bound == "hbm" else (flops / warm_s / 1e12),
@@ -269,8 +314,43 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
             dst.copy_(src)
         torch.cuda.synchronize()
     if do_cpu and data == "randn":
-        line["cpu_baseline"] = cpu_baseline(name, host, act=act)
+        line["cpu_baseline"] = cpu_baseline(name, host, budget_s=cpu_budget_s, act=act,
+                                            single_thread_s=cpu_single_s)
+    del sets, outs, graph, roll
+    torch.cuda.empty_cache()
     return line
+
+
+# The five workloads the headline metric is quoted on: INT8 128x256x512 (bit
+# exact, launch-bound), FP8 16x7168x2048 (HBM-bound), FP8 512x4096x4096, BF16
+# 8192^3 and MXFP4 4096x4096x8192 (MFMA-bound). The one line the bench prints
+# carries the default workload's figures at its top level and these five in
+# `configs`.
+METRIC_CONFIGS = ["int8_128x256x512", "fp8_16x7168x2048", "fp8_512x4096x4096", "bf16_8192x8192x8192",
+                  "mxfp4_4096x4096x8192"]
+# a 1-thread oracle time is reported for the first three (the small ones)
+SINGLE_THREAD_CONFIGS = {"int8_128x256x512", "fp8_16x7168x2048", "fp8_512x4096x4096"}
+
+
+def config_summary(line):
+    """The per-config figures that go into the one JSON line's `configs`."""
+    r = line["roofline"]
+    out = {"us_per_gemm": line["us_per_gemm"], "value": line["value"], "unit": line["unit"],
+           "frac_of_peak": r["frac"], "peak": r["peak"], "bound": r["bound"], "dtype": line["dtype"],
+           "tflops": line["tflops"], "gbps": line["gbps"],
+           "kernel": line["config"]["kernel"], "tile": line["config"]["tile"], "grid": line["config"]["grid"],
+           "rotating_sets": line["config"]["rotating_sets"]}
+    for k in ("clock_normalised_frac", "traffic"):
+        if r.get(k) is not None:
+            out[k] = r[k]
+    if "telemetry" in line and line["telemetry"]:
+        out["sclk_mhz"] = line["telemetry"]["sclk_mhz"]
+        out["power_w"] = line["telemetry"]["power_w"]
+    if "warm" in line:
+        out["warm_us_per_gemm"] = line["warm"]["us_per_gemm"]
+    if "cpu_baseline" in line:
+        out["cpu_baseline"] = line["cpu_baseline"]
+    return out
 
 
 def _gpu_sysfs():
@@ -366,7 +446,10 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    help="one of %s, or 'all'" % ", ".join(sorted(workloads.CONFIGS)))
+                    help="one of %s, or 'all' (one line per workload)" % ", ".join(sorted(workloads.CONFIGS)))
+    ap.add_argument("--configs", default="metric", choices=["metric", "none"],
+                    help="metric (default): also time the five workloads of the headline metric and put "
+                         "their figures in the line's `configs`; none: the --workload line alone")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -391,10 +474,22 @@ def main():
     torch.cuda.set_device(0)
     names = sorted(workloads.CONFIGS) if args.workload == "all" else [args.workload]
     opts = json.loads(args.opts) if args.opts else None
+    kw = dict(opts=opts, use_graph=not args.eager, act=args.act, data=args.data, telemetry_s=args.telemetry_s)
     for name in names:
-        line = bench_one(name, args.steps, args.warmup, do_cpu=not args.no_cpu_baseline, opts=opts,
-                         use_graph=not args.eager, calib_mib=args.calib_copy, act=args.act, data=args.data,
-                         telemetry_s=args.telemetry_s)
+        line = bench_one(name, args.steps, args.warmup, do_cpu=not args.no_cpu_baseline,
+                         calib_mib=args.calib_copy, cpu_single_s=3.0 if name in SINGLE_THREAD_CONFIGS else 0.0,
+                         **kw)
+        if args.workload != "all" and args.configs == "metric" and opts is None and args.act is None:
+            cfgs = {}
+            for other in METRIC_CONFIGS:
+                if other == name:
+                    cfgs[other] = config_summary(line)
+                    continue
+                log(f"[bench] metric config {other}")
+                o = bench_one(other, args.steps, args.warmup, do_cpu=not args.no_cpu_baseline, cpu_budget_s=8.0,
+                              cpu_single_s=3.0 if other in SINGLE_THREAD_CONFIGS else 0.0, **kw)
+                cfgs[other] = config_summary(o)
+            line["configs"] = cfgs
         print(json.dumps(line), flush=True)
 
 
