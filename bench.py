@@ -145,7 +145,10 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
     from dense_gemm_preshuffle_amd import workload
 
     dtype, M, N, K, seed, flops, nbytes, bound = workload_numbers(name, act)
-    plan = gp.gemm_plan(dtype, M, N, K, opts)
+    # every GEMM goes through gemm_ex_ws with a workspace allocated (and
+    # zeroed) once here, so the planner may split K across workgroups; one
+    # workspace serves every launch, since they are ordered on one stream
+    plan = gp.gemm_plan_ws(dtype, M, N, K, opts)
     log(f"[bench] {name}: plan {plan}" + (f", fused epilogue bias + {act}" if act else ""))
     host = workloads.make_inputs(dtype, M, N, K, seed, bias=act is not None)
     dev = workload.to_device(dtype, host)
@@ -158,6 +161,7 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
 
     # preshuffle pass, timed on its own
     p0 = workload.prepare(dtype, dev)
+    p0["workspace"] = gp.workspace(dtype, M, N, K, opts)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 20
@@ -174,7 +178,7 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
     R = max(2, min(64, math.ceil(ROTATE_BYTES / set_bytes)))
     sets = [p0]
     for _ in range(R - 1):
-        q = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in p0.items()}
+        q = {k: (v.clone() if torch.is_tensor(v) and k != "workspace" else v) for k, v in p0.items()}
         sets.append(q)
     outs = [workload.run(dtype, s, opts=opts, act=act) for s in sets]
     torch.cuda.synchronize()
@@ -270,6 +274,8 @@ def bench_one(name, steps, warmup, do_cpu=True, opts=None, use_graph=True, calib
         "config": {"workload": name, "M": M, "N": N, "K": K, "kernel": plan["kernel"],
                    "tile": [plan["tile_m"], plan["tile_n"], plan["tile_k"]], "grid": plan["grid"],
                    "epilogue": plan["epilogue"], "fused_epilogue": f"bias+{act}" if act else None,
+                   "entry_point": "gemm_ex_ws", "ksplit": plan["ksplit"], "scheduler": plan["scheduler"],
+                   "workspace_bytes": plan["workspace_bytes"],
                    "rotating_sets": R, "sets_touched_in_timed_region": min(steps, R),
                    "reuse_distance_mib": round(R * set_bytes / 2**20, 1)},
         "roofline": roof,
@@ -432,7 +438,8 @@ def _traffic(name, plan):
         return None
     if not rec or rec.get("source_hash") != gp.source_hash():
         return None
-    if rec.get("tile") != [plan["tile_m"], plan["tile_n"], plan["tile_k"]] or rec.get("kernel") != plan["kernel"]:
+    if rec.get("tile") != [plan["tile_m"], plan["tile_n"], plan["tile_k"]] or rec.get("kernel") != plan["kernel"] \
+            or rec.get("ksplit", 1) != plan.get("ksplit", 1):
         return None
     return rec.get("traffic_bytes")
 

@@ -13,6 +13,11 @@ points have the names of the C ABI (include/gemm_preshuffle.h):
     gemm_ex(dtype, a, b_shuf, ..., bias, act)        -> any type with the fused
                                                         bias / activation epilogue
     gemm_plan(dtype, M, N, K, opts)                  -> dict (host-only planner query)
+    gemm_ex_ws(dtype, ..., workspace=ws)             -> gemm_ex with a device workspace, which
+                                                        lets the planner split K across workgroups
+    gemm_workspace_size(dtype, M, N, K, opts)        -> bytes gemm_ex_ws needs (0: none)
+    gemm_plan_ws(dtype, M, N, K, opts)               -> dict, the plan of gemm_ex_ws
+    workspace(dtype, M, N, K, opts)                  -> a zeroed device workspace of that size
 
 Tensors: A is [M, K] (INT8 / FP8 as any 1-byte dtype, BF16 / FP16 as
 bfloat16 / float16 or a 2-byte integer view, MXFP4 as uint8 [M, K/2]; W4A8:
@@ -29,7 +34,7 @@ import re
 __all__ = [
     "GemmError", "GemmLibraryMissing", "GemmOpts", "lib_path", "load_library",
     "gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_f16", "gemm_w4a8", "gemm_ex",
-    "gemm_plan", "ACTS",
+    "gemm_plan", "ACTS", "gemm_ex_ws", "gemm_workspace_size", "gemm_plan_ws", "workspace",
     "gemm_status_string", "source_hash", "DTYPES", "EPI_DIRECT", "EPI_CSHUFFLE", "KERNEL_TILE", "KERNEL_SPLITK",
     "KERNEL_WIDE",
 ]
@@ -44,8 +49,9 @@ DTYPES = {"int8": GP_I8, "fp8": GP_FP8_E4M3, "bf16": GP_BF16, "mxfp4": GP_FP4_E2
 _ELEM_BITS = {GP_I8: 8, GP_FP8_E4M3: 8, GP_BF16: 16, GP_FP4_E2M1: 4, GP_F16: 16, GP_I4: 4}   # of B
 _OUT = {GP_I8: GP_I32, GP_FP8_E4M3: GP_BF16, GP_BF16: GP_BF16, GP_FP4_E2M1: GP_BF16, GP_F16: GP_F16,
         GP_I4: GP_BF16}
-# gp_status value of a HIP runtime or launch error
+# gp_status values of a HIP runtime or launch error, and of a missing / too small workspace
 GP_EHIP = 5
+GP_EWORKSPACE = 6
 # gp_act values of the C ABI
 ACTS = {"none": 0, "relu": 1, "silu": 2, "gelu": 3}
 EPI_AUTO, EPI_DIRECT, EPI_CSHUFFLE = 0, 1, 2
@@ -68,7 +74,8 @@ class GemmLibraryMissing(ImportError):
 class GemmOpts(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
                 ("epilogue", ctypes.c_int), ("kernel", ctypes.c_int), ("xcd_swizzle", ctypes.c_int),
-                ("waves", ctypes.c_int), ("mfma", ctypes.c_int), ("pipeline", ctypes.c_int)]
+                ("waves", ctypes.c_int), ("mfma", ctypes.c_int), ("pipeline", ctypes.c_int),
+                ("ksplit", ctypes.c_int), ("scheduler", ctypes.c_int)]
 
 
 class GemmPlanInfo(ctypes.Structure):
@@ -77,7 +84,8 @@ class GemmPlanInfo(ctypes.Structure):
                 ("waves", ctypes.c_int), ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int),
                 ("grid", ctypes.c_int64), ("k_tiles", ctypes.c_int64),
                 ("mfma_per_wave_tile", ctypes.c_int64), ("mfma_total", ctypes.c_int64),
-                ("mfma", ctypes.c_int), ("pipeline", ctypes.c_int)]
+                ("mfma", ctypes.c_int), ("pipeline", ctypes.c_int), ("ksplit", ctypes.c_int),
+                ("scheduler", ctypes.c_int), ("workspace_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -107,12 +115,16 @@ def load_library():
     lib.gemm_w4a8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ctypes.POINTER(GemmOpts), vp]
     lib.gemm_ex.argtypes = [ci, ci, vp, vp, vp, vp, vp, ci, vp, i64, i64, i64, ctypes.POINTER(GemmOpts), vp]
     lib.gemm_plan.argtypes = [ci, i64, i64, i64, ctypes.POINTER(GemmOpts), ctypes.POINTER(GemmPlanInfo)]
+    lib.gemm_plan_ws.argtypes = [ci, i64, i64, i64, ctypes.POINTER(GemmOpts), ctypes.POINTER(GemmPlanInfo)]
+    lib.gemm_workspace_size.argtypes = [ci, i64, i64, i64, ctypes.POINTER(GemmOpts), ctypes.POINTER(ctypes.c_size_t)]
+    lib.gemm_ex_ws.argtypes = [ci, ci, vp, vp, vp, vp, vp, ci, vp, i64, i64, i64, ctypes.POINTER(GemmOpts), vp,
+                               ctypes.c_size_t, vp]
     lib.gemm_status_string.argtypes = [ci]
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_last_hip_error.argtypes = []
     lib.gemm_last_hip_error.restype = ctypes.c_char_p
     for f in ("gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_f16", "gemm_w4a8", "gemm_ex",
-              "gemm_plan"):
+              "gemm_plan", "gemm_plan_ws", "gemm_workspace_size", "gemm_ex_ws"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -188,6 +200,30 @@ def gemm_plan(dtype, M: int, N: int, K: int, opts=None) -> dict:
     info = GemmPlanInfo()
     _check(load_library().gemm_plan(_dt(dtype), M, N, K, _opts(opts), ctypes.byref(info)), "gemm_plan")
     return {name: getattr(info, name) for name, _ in GemmPlanInfo._fields_}
+
+
+def gemm_plan_ws(dtype, M: int, N: int, K: int, opts=None) -> dict:
+    """Host-only: the plan of gemm_ex_ws with these sizes and options (it may split K)."""
+    info = GemmPlanInfo()
+    _check(load_library().gemm_plan_ws(_dt(dtype), M, N, K, _opts(opts), ctypes.byref(info)), "gemm_plan_ws")
+    return {name: getattr(info, name) for name, _ in GemmPlanInfo._fields_}
+
+
+def gemm_workspace_size(dtype, M: int, N: int, K: int, opts=None) -> int:
+    """Host-only: workspace bytes a gemm_ex_ws call with these arguments needs (0: none)."""
+    n = ctypes.c_size_t()
+    _check(load_library().gemm_workspace_size(_dt(dtype), M, N, K, _opts(opts), ctypes.byref(n)),
+           "gemm_workspace_size")
+    return int(n.value)
+
+
+def workspace(dtype, M: int, N: int, K: int, opts=None, device="cuda"):
+    """A zero-filled device workspace for gemm_ex_ws with these arguments (None when none is needed).
+    Zero once here; every call leaves its counters zero again."""
+    import torch
+
+    n = gemm_workspace_size(dtype, M, N, K, opts)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
 def gemm_preshuffle_b(b, dtype, out=None, stream=None):
@@ -295,4 +331,27 @@ def gemm_ex(dtype, a, b_shuf, scale_a=None, scale_b=None, bias=None, act="none",
     a_ = ACTS[act] if isinstance(act, str) else int(act)
     _check(load_library().gemm_ex(dt, out_dt, _ptr(a), _ptr(b_shuf), _ptr(scale_a), _ptr(scale_b), _ptr(bias),
                                   a_, _ptr(c), M, N, K, _opts(opts), _stream(stream)), "gemm_ex")
+    return c
+
+
+def gemm_ex_ws(dtype, a, b_shuf, scale_a=None, scale_b=None, bias=None, act="none", c=None, N=None,
+               opts=None, workspace=None, stream=None):
+    """gemm_ex with a device workspace (a uint8 tensor from `workspace()`), so
+    that the planner may split K across workgroups."""
+    import torch
+
+    dt = _dt(dtype)
+    out_dt = _OUT[dt]
+    M = a.shape[0]
+    K = _row_bytes(a) * 8 // (8 if dt == GP_I4 else _ELEM_BITS[dt])
+    if N is None:
+        N = b_shuf.numel() * b_shuf.element_size() * 8 // (K * _ELEM_BITS[dt])
+    if c is None:
+        tdt = {GP_I32: torch.int32, GP_BF16: torch.bfloat16, GP_F16: torch.float16}[out_dt]
+        c = torch.empty(M, N, dtype=tdt, device=a.device)
+    a_ = ACTS[act] if isinstance(act, str) else int(act)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load_library().gemm_ex_ws(dt, out_dt, _ptr(a), _ptr(b_shuf), _ptr(scale_a), _ptr(scale_b), _ptr(bias),
+                                     a_, _ptr(c), M, N, K, _opts(opts), _ptr(workspace), nbytes, _stream(stream)),
+           "gemm_ex_ws")
     return c

@@ -54,6 +54,8 @@ struct WideVar { int dt, ms, tkb, pipe; };
 #define GP_SPLIT_ENTRY(DT, NB, W, KCH, MB) {DT, NB, W, KCH, MB},
 #define GP_WIDE_ENTRY(DT, MS, TKB, PIPE) {DT, MS, TKB, PIPE},
 constexpr TileVar kTiles[] = {GP_TILE_ALL(GP_TILE_ENTRY) GP_TILE_KG2_ALL(GP_TILE_KG2_ENTRY)};
+constexpr TileVar kNoSched[] = {GP_TILE_NOSCHED_ALL(GP_TILE_ENTRY)};
+constexpr TileVar kKSplit[] = {GP_TILE_KSPLIT_ALL(GP_TILE_ENTRY)};
 constexpr SplitVar kSplits[] = {GP_SPLITK_ALL(GP_SPLIT_ENTRY)};
 constexpr WideVar kWides[] = {GP_WIDE_ALL(GP_WIDE_ENTRY)};
 
@@ -79,6 +81,18 @@ int pick_pipe(int dt, int ms, int tm, int tn, int tkb, int want) {
     if (tile_compiled(dt, ms, tm, tn, tkb, ord[k])) return ord[k];
   return -1;
 }
+// A variant with the compiler's own hot-loop order (scheduler off) exists.
+bool nosched_compiled(int dt, int ms, int tm, int tn, int tkb, int pipe) {
+  for (const auto& v : kNoSched)
+    if (v.dt == dt && v.ms == ms && v.tm == tm && v.tn == tn && v.tkb == tkb && v.pipe == pipe) return true;
+  return false;
+}
+// A variant able to split K across workgroups exists.
+bool ksplit_compiled(int dt, int ms, int tm, int tn, int tkb, int pipe) {
+  for (const auto& v : kKSplit)
+    if (v.dt == dt && v.ms == ms && v.tm == tm && v.tn == tn && v.tkb == tkb && v.pipe == pipe) return true;
+  return false;
+}
 bool split_compiled(int dt, int nb, int waves, int kch, int mb) {
   for (const auto& v : kSplits)
     if (v.dt == dt && v.nb == nb && v.waves == waves && v.kch == kch && v.mb == mb) return true;
@@ -94,8 +108,20 @@ struct Plan {
   int epi = EPI_DIRECT;
   int xcd = 1;
   int nb = 0, waves = 4, kch = 0, mb = 1;  // split-K kernel (mb: 16-row blocks per workgroup)
+  int ks = 1;                   // tile kernel: K split across workgroups
+  int sched = 1;                // tile kernel: 1 pinned hot-loop schedule, 2 the compiler's
   int64_t Kb = 0;
 };
+
+// Workspace of a K split across workgroups: the tiles' arrival counters
+// (4 bytes each, the area rounded up to 256 bytes), then ks partial tiles of
+// TM x TN 4-byte sums per tile.
+int64_t tiles_of(const Plan& p, int64_t M, int64_t N) { return ((M + p.tm - 1) / p.tm) * ((N + p.tn - 1) / p.tn); }
+int64_t counter_bytes(const Plan& p, int64_t M, int64_t N) { return (tiles_of(p, M, N) * 4 + 255) / 256 * 256; }
+int64_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
+  if (p.ks <= 1) return 0;
+  return counter_bytes(p, M, N) + tiles_of(p, M, N) * p.ks * p.tm * p.tn * 4;
+}
 
 // K bytes of B one MFMA consumes (per MS x MS block); a W4A8 piece of 64
 // B bytes feeds two int8 MFMAs
@@ -238,6 +264,50 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
   return GP_ESHAPE;
 }
 
+// K split across workgroups chosen by the planner (calls with a workspace):
+// only where the tiles alone leave the GPU short of work, i.e. fewer than
+// 256 workgroups, or 256 only with a tile smaller than 64 x 128 (each CU then
+// pulls more operand bytes per FLOP from L2). The first tile (in the order
+// of the split variants' list) takes the fewest ranges S (powers of two, up
+// to 16, each range keeping at least 2048 bytes of B's K) that give 256
+// workgroups, or the most such ranges if those give at least 128 (128 large
+// tiles measured faster than 256 small ones on BF16). A split costs a round
+// trip of the partial sums at the end of the kernel (a few microseconds), so
+// short K stays unsplit: FP8 512 x 4096 x 4096 measured 15.6 us unsplit and
+// 20.0 us split in two; FP8 256 x 2048 x 16384 39.0 us unsplit (16 x 64
+// tiles) and 20.8 us split in four (64 x 128 tiles); BF16 512 x 2048 x 16384
+// 141.8 and 56.5 us (128 x 256 tiles, eight ranges); MXFP4 256 x 4096 x
+// 16384 43.8 and 23.7 us (128 x 128 tiles, four ranges).
+void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
+  const int64_t grid0 = ((M + p->tm - 1) / p->tm) * ((N + p->tn - 1) / p->tn);
+  if (grid0 >= 256 && p->tm * p->tn >= 64 * 128) return;
+  int best = -1, best_s = 0;
+  for (int i = 0; i < (int)(sizeof(kKSplit) / sizeof(kKSplit[0])); ++i) {
+    const TileVar& v = kKSplit[i];
+    if (v.dt != dt || v.tm > M || v.tn > N || Kb % v.tkb) continue;
+    const int64_t T = ((M + v.tm - 1) / v.tm) * ((N + v.tn - 1) / v.tn);
+    const int64_t KT = Kb / v.tkb;
+    int s_pick = 0;
+    for (int S = 2; S <= 16; S *= 2) {
+      if (KT % S || Kb / S < 2048) break;
+      s_pick = S;
+      if (T * S >= 256) break;
+    }
+    if (!s_pick || T * s_pick < 128) continue;
+    best = i;
+    best_s = s_pick;
+    break;
+  }
+  if (best < 0) return;
+  const TileVar& v = kKSplit[best];
+  p->tm = v.tm;
+  p->tn = v.tn;
+  p->tkb = v.tkb;
+  p->ms = v.ms;
+  p->pipe = v.pipe;
+  p->ks = best_s;
+}
+
 // Wide kernel (256x256 tiles, 8 waves, A and B through LDS): the caller's
 // MFMA block (default 16), tile_k and pipeline where given; otherwise the
 // compiled variant with the largest tile_k dividing K, then the most stages.
@@ -271,7 +341,9 @@ int choose_wide(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, con
   return GP_OK;
 }
 
-int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o, Plan* p) {
+// ws: the call brings a workspace (gemm_ex_ws), so the tile kernel may split
+// K across workgroups.
+int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o, Plan* p, bool ws = false) {
   if (M <= 0 || N <= 0 || K <= 0) return GP_EINVAL;
   const int bits = elem_bits(in_dtype);
   if (bits == 0) return GP_EDTYPE;
@@ -284,6 +356,9 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     if (o->xcd_swizzle < 0 || o->xcd_swizzle > 2) return GP_EINVAL;
     if (o->mfma != 0 && o->mfma != 16 && o->mfma != 32) return GP_EINVAL;
     if (o->pipeline < 0 || o->pipeline > 6) return GP_EINVAL;
+    if (o->ksplit < 0 || o->ksplit > 64) return GP_EINVAL;
+    if (o->scheduler < 0 || o->scheduler > 2) return GP_EINVAL;
+    if (o->ksplit > 1 && !ws) return GP_EWORKSPACE;   // a K split needs gemm_ex_ws
   }
   if ((K * bits) % 8) return GP_ESHAPE;
   const int64_t Kb = K * bits / 8;
@@ -304,6 +379,8 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   const int64_t small_m = 64;
   p->kernel = (o && o->kernel) ? o->kernel : (M <= small_m ? GP_KERNEL_SPLITK : GP_KERNEL_TILE);
   if (dt == DT_I4 && p->kernel == GP_KERNEL_WIDE) return GP_EDTYPE;   // no 256 x 256 W4A8 kernel
+  // a K split and the scheduler-off variants exist on the tile kernel only
+  if (o && (o->ksplit > 1 || o->scheduler == 2) && p->kernel != GP_KERNEL_TILE) return GP_ESHAPE;
   if (p->kernel == GP_KERNEL_SPLITK) return choose_split(dt, bits, M, N, Kb, p, o);
   if (p->kernel == GP_KERNEL_WIDE) return choose_wide(dt, bits, M, N, Kb, p, o);
 
@@ -324,6 +401,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     if (r) {
       // no tile fits inside M x N: the small-M kernel takes any M
       if (o && o->kernel == GP_KERNEL_TILE) return r;
+      if (o && (o->ksplit > 1 || o->scheduler == 2)) return GP_ESHAPE;
       p->kernel = GP_KERNEL_SPLITK;
       return choose_split(dt, bits, M, N, Kb, p, o);
     }
@@ -335,6 +413,21 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     if (o->waves != 8 || (Kb / p->tkb) % 2 || !tile_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe, 2))
       return GP_ESHAPE;
     p->kg = 2;
+  }
+  // K split across workgroups: ksplit equal ranges of whole K tiles (of
+  // whole K-group halves with two K groups)
+  if (o && o->ksplit > 1) {
+    if ((Kb / p->tkb) % ((int64_t)o->ksplit * p->kg)) return GP_ESHAPE;
+    if (p->kg != 1 || !ksplit_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe)) return GP_ESHAPE;
+    p->ks = o->ksplit;
+  } else if (ws && !user_tile && p->kg == 1 && !(o && (o->ksplit == 1 || o->pipeline || o->mfma || o->scheduler))) {
+    auto_ksplit(dt, M, N, Kb, p);
+  }
+  // Hot-loop schedule: pinned unless asked otherwise (measured per default
+  // tile, one process each: the pinned order was as fast or faster)
+  if (o && o->scheduler == 2) {
+    if (p->kg != 1 || p->ks != 1 || !nosched_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe)) return GP_ESHAPE;
+    p->sched = 2;
   }
   if (o && o->epilogue) {
     p->epi = o->epilogue;
@@ -425,6 +518,13 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
   }
   // MFMAs the launch issues (the algorithmic (M/ms)(N/ms)(K/K_instr) when
   // the tile divides M and N; edge tiles and partial row blocks add to it)
+  out->ksplit = p.ks;
+  out->scheduler = p.kernel == GP_KERNEL_SPLITK ? 2 : p.sched;   // the small-M kernel has no fences
+  if (p.kernel == GP_KERNEL_TILE && p.ks > 1) {
+    out->grid *= p.ks;
+    out->k_tiles /= p.ks;
+  }
+  out->workspace_bytes = workspace_bytes(p, M, N);
   out->mfma_total = out->grid * out->waves * (out->k_tiles / (p.kernel == GP_KERNEL_TILE ? p.kg : 1)) *
                     out->mfma_per_wave_tile;
 }
@@ -464,7 +564,7 @@ int check_device() {
 }
 
 int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void* sa, const void* sb,
-           const float* bias, int act, void* c, int64_t M, int64_t N, hipStream_t s) {
+           const float* bias, int act, void* c, int64_t M, int64_t N, void* ws, hipStream_t s) {
   const int dt = kdt(in_dtype);
   hipError_t e;
   clear_last_error();
@@ -483,6 +583,9 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
     t.tiles_n = (uint32_t)((N + p.tn - 1) / p.tn);
     t.xcd = p.xcd == 1 ? 1u : 0u;
     t.act = act;
+    t.ksplit = (uint32_t)p.ks;
+    t.cnt = p.ks > 1 ? (uint32_t*)ws : nullptr;
+    t.part = p.ks > 1 ? (char*)ws + counter_bytes(p, M, N) : nullptr;
     const bool fused = bias != nullptr || act != GP_ACT_NONE;
     if (p.kernel == GP_KERNEL_WIDE) {
       switch (dt) {
@@ -493,12 +596,12 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
         default: e = hipErrorInvalidValue; break;
       }
     } else switch (dt) {
-      case DT_I8: e = launch_tile_i8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, false, t, s); break;
-      case DT_FP8: e = launch_tile_fp8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, t, s); break;
-      case DT_BF16: e = launch_tile_bf16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, t, s); break;
-      case DT_F16: e = launch_tile_f16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, t, s); break;
-      case DT_FP4: e = launch_tile_fp4(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, t, s); break;
-      case DT_I4: e = launch_tile_i4(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, t, s); break;
+      case DT_I8: e = launch_tile_i8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, false, p.sched == 1, t, s); break;
+      case DT_FP8: e = launch_tile_fp8(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, p.sched == 1, t, s); break;
+      case DT_BF16: e = launch_tile_bf16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, p.sched == 1, t, s); break;
+      case DT_F16: e = launch_tile_f16(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, p.sched == 1, t, s); break;
+      case DT_FP4: e = launch_tile_fp4(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, p.sched == 1, t, s); break;
+      case DT_I4: e = launch_tile_i4(p.ms, p.tm, p.tn, p.tkb, p.pipe, p.epi, p.kg, fused, p.sched == 1, t, s); break;
       default: e = hipErrorInvalidValue; break;
     }
   } else {
@@ -564,7 +667,7 @@ __global__ __launch_bounds__(256) void preshuffle_kernel(const char* __restrict_
 // scales, epilogue), the plan, the device check, the launch.
 int run_gemm(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
              const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
-             const gemm_opts* opts, void* stream) {
+             const gemm_opts* opts, void* stream, bool ws_call = false, void* ws = nullptr, size_t ws_bytes = 0) {
   if (!a || !b_shuf || !c || !aligned16(a) || !aligned16(b_shuf) || !aligned16(c)) return GP_EINVAL;
   if (act < GP_ACT_NONE || act > GP_ACT_GELU) return GP_EINVAL;
   if (bias && !aligned16(bias)) return GP_EINVAL;
@@ -589,11 +692,18 @@ int run_gemm(int in_dtype, int out_dtype, const void* a, const void* b_shuf, con
     return GP_EDTYPE;
   }
   Plan p;
-  int r = make_plan(in_dtype, M, N, K, opts, &p);
+  int r = make_plan(in_dtype, M, N, K, opts, &p, ws_call);
   if (r) return r;
+  // the scheduler-off and K-split variants have the plain epilogue only
+  if ((p.sched == 2 || p.ks > 1) && (bias || act != GP_ACT_NONE)) return GP_ESHAPE;
+  const int64_t need = workspace_bytes(p, M, N);
+  if (need > 0) {
+    if (!ws || (int64_t)ws_bytes < need) return GP_EWORKSPACE;
+    if (!aligned16(ws)) return GP_EINVAL;
+  }
   r = check_device();
   if (r) return r;
-  return launch(in_dtype, p, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, (hipStream_t)stream);
+  return launch(in_dtype, p, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, ws, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -613,6 +723,7 @@ const char* gemm_status_string(int status) {
     case GP_EDTYPE: return "unsupported dtype or dtype/scale combination";
     case GP_EARCH: return "current device is not gfx950";
     case GP_EHIP: return "HIP runtime or launch error";
+    case GP_EWORKSPACE: return "the plan needs a workspace (gemm_ex_ws) of at least gemm_workspace_size bytes";
     default: return "unknown status";
   }
 }
@@ -680,6 +791,31 @@ int gemm_ex(int in_dtype, int out_dtype, const void* a, const void* b_shuf, cons
             const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
             const gemm_opts* opts, void* stream) {
   return run_gemm(in_dtype, out_dtype, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, K, opts, stream);
+}
+
+int gemm_plan_ws(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* opts, gemm_plan_info* out) {
+  if (!out) return GP_EINVAL;
+  Plan p;
+  const int r = make_plan(in_dtype, M, N, K, opts, &p, true);
+  if (r) return r;
+  fill_info(in_dtype, M, N, K, p, out);
+  return GP_OK;
+}
+
+int gemm_workspace_size(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* opts, size_t* bytes) {
+  if (!bytes) return GP_EINVAL;
+  Plan p;
+  const int r = make_plan(in_dtype, M, N, K, opts, &p, true);
+  if (r) return r;
+  *bytes = (size_t)workspace_bytes(p, M, N);
+  return GP_OK;
+}
+
+int gemm_ex_ws(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
+               const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
+               const gemm_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_gemm(in_dtype, out_dtype, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, K, opts, stream, true,
+                  workspace, workspace_bytes);
 }
 
 }  // extern "C"

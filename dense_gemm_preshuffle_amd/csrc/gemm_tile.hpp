@@ -50,6 +50,12 @@ struct TileArgs {
   uint32_t tiles_m, tiles_n;  // ceil(M / TM), ceil(N / TN)
   uint32_t xcd;       // 1: XCD-aware, grouped tile order
   int act;            // Act
+  // K split across workgroups (tile kernel): ksplit workgroups share each
+  // tile, each taking a contiguous range of its K tiles; their partial sums
+  // meet in `part` and the last one to finish adds them and stores the tile.
+  uint32_t ksplit;    // 1: no split
+  char* part;         // [tiles][ksplit][TM*TN] fp32 / int32 partial tiles
+  uint32_t* cnt;      // [tiles] arrival counters: zero before, zero after
 };
 
 // Edge tiles: a tile that would run past M (or N) starts TM (TN) before the
@@ -190,29 +196,49 @@ struct TileCfg {
   static_assert(DT != DT_I4 || MS == 16, "W4A8: 16 x 16 blocks");
 };
 
-__device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uint32_t& tn) {
-  uint32_t w = blockIdx.x;
-  const uint32_t G = p.tiles_m * p.tiles_n;
+// Tile (tm, tn) and K split z of this workgroup. With a K split the ksplit
+// workgroups of one tile are consecutive in the logical order, so with the
+// XCD-aware order they run on the same XCD and meet in its L2.
+__device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uint32_t& tn, uint32_t& z) {
+  const uint32_t w = blockIdx.x;
+  const uint32_t T = p.tiles_m * p.tiles_n;
+  const uint32_t S = p.ksplit;
+  const uint32_t G = T * S;
   if (p.xcd && (G % 8u) == 0) {
     // Workgroups go round-robin to the 8 XCDs; give each XCD a contiguous
     // range of tiles, then walk it in groups of 8 M-tiles so that the tiles
     // resident together on one XCD share A rows and B columns in its L2.
     const uint32_t logical = (w % 8u) * (G / 8u) + (w / 8u);
+    z = logical % S;
+    const uint32_t t = logical / S;
     const uint32_t GROUP = 8u;
     const uint32_t per_group = GROUP * p.tiles_n;
-    const uint32_t g = logical / per_group;
+    const uint32_t g = t / per_group;
     const uint32_t first_m = g * GROUP;
     const uint32_t gsz = min(GROUP, p.tiles_m - first_m);
-    const uint32_t r = logical % per_group;
+    const uint32_t r = t % per_group;
     tm = first_m + r % gsz;
     tn = r / gsz;
   } else {
-    tm = w / p.tiles_n;
-    tn = w % p.tiles_n;
+    z = w % S;
+    const uint32_t t = w / S;
+    tm = t / p.tiles_n;
+    tn = t % p.tiles_n;
   }
 }
+__device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uint32_t& tn) {
+  uint32_t z;
+  tile_coords(p, tm, tn, z);
+}
 
-template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED, int KG>
+// SCH: the hot-loop schedule pinned by scheduling fences (the pages'
+// hot_loop_scheduler, GEMM Optimization Guide §5.3; Kernel Tuning Guide §5
+// "enable_scheduler"); false leaves the order of the loop body to the
+// compiler (same instructions, no fences between the MFMA groups).
+// KS: the variant that can split K across workgroups (p.ksplit > 1); the
+// others assume p.ksplit == 1 and carry no code for the cross-workgroup sum.
+template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED, int KG, bool SCH = true,
+          bool KS = false>
 __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_tile_kernel(TileArgs p) {
   using C = TileCfg<DT, MS, TM, TN, TKB, EPI, PIPE, FUSED, KG>;
   using Acc = typename Mma<DT, MS>::Acc;
@@ -231,16 +257,18 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   const int lrow = lane & (MS - 1);
   const int lgrp = lane / MS;
 
-  uint32_t tm, tn;
-  tile_coords(p, tm, tn);
+  uint32_t tm, tn, kz;
+  tile_coords(p, tm, tn, kz);
   uint32_t m0 = tm * TM, n0 = tn * TN, mskip, nskip;
   edge_shift(m0, mskip, TM, p.M);
   edge_shift(n0, nskip, TN, p.N);
   const uint32_t Kb = p.Kb;
   const uint32_t Ka = Kb * C::AKB;   // bytes per row of A
-  // K tiles of this group: [kt0, kt0 + KT) (the planner makes KG divide them)
-  const int KT = (int)(Kb / TKB) / KG;
-  const int kt0 = grp * KT;
+  // K tiles of this workgroup: split kz of ksplit equal ranges; of this group:
+  // [kt0, kt0 + KT) (the planner makes ksplit * KG divide the K tiles)
+  const int KTS = (int)(Kb / TKB) / (KS ? (int)p.ksplit : 1);
+  const int KT = KTS / KG;
+  const int kt0 = __builtin_amdgcn_readfirstlane((int)kz * KTS + grp * KT);
 
   // Buffer resources based at this workgroup's first A row / first B block.
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (size_t)m0 * Ka, TM * Ka);
@@ -443,7 +471,8 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     constexpr int i = is_a ? j : j - C::GLA;
     bool on = g >= 0;
     if constexpr (C::GSPARE) on = on && i * C::THREADS + tid < (is_a ? TM : TN) * C::LPR;
-    const uint32_t u = __builtin_amdgcn_readfirstlane(i * GL_RSTEP * srow + (uint32_t)g * (C::SG * C::SCB));
+    const uint32_t u =
+        __builtin_amdgcn_readfirstlane(i * GL_RSTEP * srow + (uint32_t)kt0 * C::SCB + (uint32_t)g * (C::SG * C::SCB));
     return buf_load16(is_a ? rsa : rsb, on ? g_loff + u : kOOB, 0);
   };
   // ... into slot `slot` (0 or 1) of the ring: [tile of the group][row][lane group]
@@ -498,7 +527,9 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   // groups of MFMAs to land in. Scheduling fences pin this order: left free,
   // the compiler folds the ring into one register set and waits for every
   // read right before its MFMAs.
-  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  auto fence = [] {
+    if constexpr (SCH) __builtin_amdgcn_sched_barrier(0);
+  };
   constexpr int NBL = C::KSTEPS * C::NACC * C::FRAG;       // B loads per tile
   constexpr int NVMEM = C::ALOADS + NBL + C::SLOADS;        // global loads per tile
   auto compute = [&](auto par_c, int kt, auto&& issue_loads) {
@@ -685,6 +716,89 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     }
     static_assert(NCH * 256 * 16 <= C::REDB, "K-group reduction buffer");
     __syncthreads();
+  }
+
+  // ---- K split across workgroups: every workgroup of the tile stores its
+  // partial sums; the last to arrive adds all of them in the fixed order
+  // z = 0 .. ksplit-1, whatever the order of arrival, resets the counter for
+  // the next call and runs the epilogue; the others are done. No workgroup
+  // waits for another. The partial sums are stored and loaded with the
+  // agent-coherent cache policy, each thread's stores are complete before
+  // the arrival is counted (a relaxed agent-scope atomic), and the last
+  // workgroup loads them only after reading the count: so no cache-wide
+  // write-back or invalidate (what a __threadfence costs) is needed. ----
+  if constexpr (KS) {
+    constexpr int NCH = C::MREP * C::NACC * (C::NREG / 4);   // 4-register chunks per lane
+    using V4 = std::conditional_t<DT == DT_I8 || DT == DT_I4, v4i, v4f>;
+    const uint32_t tile = tm * p.tiles_n + tn;
+    // the tile's partial sums: [z][chunk][thread] 16-byte entries
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(p.part + (size_t)tile * p.ksplit * NCH * 4096u, p.ksplit * (uint32_t)NCH * 4096u);
+    if (grp == 0) {
+#pragma unroll
+      for (int mi = 0; mi < C::MREP; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < C::NACC; ++ni)
+#pragma unroll
+          for (int h = 0; h < C::NREG / 4; ++h) {
+            V4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * h + r];
+            const uint32_t ch = (mi * C::NACC + ni) * (C::NREG / 4) + h;
+            buf_store16_coh(__builtin_bit_cast(v4i, v), rp, ((kz * NCH + ch) * 256u + tid) * 16u);
+          }
+    }
+    wait_vm(std::integral_constant<int, 0>{});   // this thread's partial sums are stored
+    __syncthreads();
+    volatile uint32_t* arrived = (volatile uint32_t*)lds;
+    if (threadIdx.x == 0)
+      *arrived = __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t before = __builtin_amdgcn_readfirstlane(*arrived);
+    __syncthreads();   // every thread has read it before the epilogue reuses the LDS
+    if (before != p.ksplit - 1) return;
+    if (threadIdx.x == 0) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (grp == 0) {
+      // in batches of RB chunks: the RB loads of one K range are in flight
+      // together (one memory round trip per range and batch, not per chunk)
+      constexpr int RB = NCH < 8 ? NCH : 8;
+      static_assert(NCH % RB == 0, "whole batches of chunks");
+      auto get = [&](int ch) -> V4 {
+        const int mi = ch / (C::NACC * (C::NREG / 4)), ni = (ch / (C::NREG / 4)) % C::NACC, h = ch % (C::NREG / 4);
+        V4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * h + r];
+        return v;
+      };
+      auto put = [&](int ch, V4 v) {
+        const int mi = ch / (C::NACC * (C::NREG / 4)), ni = (ch / (C::NREG / 4)) % C::NACC, h = ch % (C::NREG / 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mi][ni][4 * h + r] = v[r];
+      };
+      static_for<0, NCH / RB>([&](auto b_c) {
+        constexpr int c0 = decltype(b_c)::value * RB;
+        V4 t[RB], u[RB];
+        // partial sums of range z, chunks c0 .. c0+RB-1 (this workgroup's own from registers)
+        auto fetch = [&](uint32_t z, V4* dst) {
+          if (z == kz) {
+#pragma unroll
+            for (int b = 0; b < RB; ++b) dst[b] = get(c0 + b);
+          } else {
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+              dst[b] = __builtin_bit_cast(V4, buf_load16_coh(rp, ((z * NCH + c0 + b) * 256u + tid) * 16u));
+          }
+        };
+        fetch(0, t);
+        for (uint32_t zz = 1; zz < p.ksplit; ++zz) {
+          fetch(zz, u);
+#pragma unroll
+          for (int b = 0; b < RB; ++b) t[b] += u[b];
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b) put(c0 + b, t[b]);
+      });
+    }
   }
 
   // ---- epilogue ---- (the first K group's waves store; a second group only

@@ -94,6 +94,19 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t bytes, cons
 }
 #pragma clang diagnostic pop
 
+// Agent-coherent variants: cache policy bit 4 (sc1) on gfx950, the form the
+// compiler gives relaxed agent-scope atomic loads and stores. Data written
+// this way by one workgroup and read this way by another, on any XCD, needs
+// no L2 write-back or invalidate; ordering comes from waiting for the stores
+// to complete (s_waitcnt vmcnt(0)) before the atomic that publishes them.
+constexpr int kPolicySC1 = 16;
+__device__ __forceinline__ v4i buf_load16_coh(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kPolicySC1);
+}
+__device__ __forceinline__ void buf_store16_coh(v4i v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, kPolicySC1);
+}
+
 // Non-temporal (streaming) variants: cache policy bit 1 (nt) on gfx950.
 constexpr int kPolicyNT = 2;
 __device__ __forceinline__ v4i buf_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {

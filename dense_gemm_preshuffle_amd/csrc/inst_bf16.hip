@@ -4,7 +4,7 @@
 
 namespace gp {
 
-GP_DEFINE_PLAIN(bf16, GP_TILE_BF16, GP_TILE_KG2_BF16, GP_WIDE_BF16)
+GP_DEFINE_PLAIN(bf16, GP_TILE_BF16, GP_TILE_KG2_BF16, GP_WIDE_BF16, GP_TILE_NOSCHED_BF16, GP_TILE_KSPLIT_BF16)
 
 hipError_t launch_splitk_bf16(int nb, int waves, int kch, int mb, const SplitArgs& a, hipStream_t s) {
   GP_SPLITK_BF16(GP_SPLITK_CASE)

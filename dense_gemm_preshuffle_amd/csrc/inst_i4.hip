@@ -4,7 +4,7 @@
 
 namespace gp {
 
-GP_DEFINE_PLAIN(i4, GP_TILE_I4, GP_TILE_KG2_I4, GP_WIDE_I4)
+GP_DEFINE_PLAIN(i4, GP_TILE_I4, GP_TILE_KG2_I4, GP_WIDE_I4, GP_TILE_NOSCHED_I4, GP_TILE_KSPLIT_I4)
 
 hipError_t launch_splitk_i4(int nb, int waves, int kch, int mb, const SplitArgs& a, hipStream_t s) {
   GP_SPLITK_I4(GP_SPLITK_CASE)

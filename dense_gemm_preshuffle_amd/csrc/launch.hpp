@@ -15,7 +15,7 @@ namespace gp {
 // Each returns hipErrorInvalidValue if the variant is not compiled.
 #define GP_DECLARE_TILE(NAME)                                                                       \
   hipError_t launch_tile_##NAME(int ms, int tm, int tn, int tkb, int pipe, int epi, int kg, bool fused, \
-                                const TileArgs& a, hipStream_t s);                                  \
+                                bool sched, const TileArgs& a, hipStream_t s);                      \
   hipError_t launch_tile_##NAME##_fused(int ms, int tm, int tn, int tkb, int pipe, int epi, int kg, \
                                         const TileArgs& a, hipStream_t s);
 #define GP_DECLARE_WIDE(NAME)                                                                       \
@@ -35,19 +35,23 @@ hipError_t launch_splitk_i4(int nb, int waves, int kch, int mb, const SplitArgs&
 }  // namespace gp
 
 // Bodies of one dtype's launch tables.
-#define GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, FU, KGV)                                      \
-  if (ms == MS && tm == TM && tn == TN && tkb == TKB && pipe == PIPE && kg == KGV) {               \
-    const dim3 grid(a.tiles_m * a.tiles_n);                                                        \
+// (the grid has one workgroup per tile and K split)
+#define GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, FU, KGV, SCHV, KSV)                           \
+  if (ms == MS && tm == TM && tn == TN && tkb == TKB && pipe == PIPE && kg == KGV && sched == SCHV && \
+      (a.ksplit > 1) == KSV) {                                                                     \
+    const dim3 grid(a.tiles_m * a.tiles_n * a.ksplit);                                             \
     if (epi == EPI_CSHUFFLE)                                                                       \
-      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_CSHUFFLE, PIPE, FU, KGV>), grid, dim3(256 * KGV), 0, s, a); \
+      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_CSHUFFLE, PIPE, FU, KGV, SCHV, KSV>), grid, dim3(256 * KGV), 0, s, a); \
     else                                                                                           \
-      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_DIRECT, PIPE, FU, KGV>), grid, dim3(256 * KGV), 0, s, a);   \
+      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_DIRECT, PIPE, FU, KGV, SCHV, KSV>), grid, dim3(256 * KGV), 0, s, a);   \
     return hipGetLastError();                                                                      \
   }
-#define GP_TILE_CASE(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 1)
-#define GP_TILE_CASE_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true, 1)
-#define GP_TILE_CASE_KG2(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 2)
-#define GP_TILE_CASE_KG2_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true, 2)
+#define GP_TILE_CASE(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 1, true, false)
+#define GP_TILE_CASE_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true, 1, true, false)
+#define GP_TILE_CASE_KG2(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 2, true, false)
+#define GP_TILE_CASE_KG2_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true, 2, true, false)
+#define GP_TILE_CASE_NOSCHED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 1, false, false)
+#define GP_TILE_CASE_KSPLIT(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 1, true, true)
 #define GP_SPLITK_CASE(DT, NB, W, KCH, MB)                                                     \
   if (nb == NB && waves == W && kch == KCH && mb == MB) {                                      \
     const dim3 grid(a.N / (16 * NB), (a.M + 16 * MB - 1) / (16 * MB));                         \
@@ -63,12 +67,15 @@ hipError_t launch_splitk_i4(int nb, int waves, int kch, int mb, const SplitArgs&
 #define GP_WIDE_CASE_FUSED(DT, MS, TKB, PIPE) GP_WIDE_CASE_IMPL(DT, MS, TKB, PIPE, true)
 
 // Plain launch tables of one dtype (the fused ones are in inst_<name>_fused.hip).
-#define GP_DEFINE_PLAIN(NAME, TILES, KG2TILES, WIDES)                                               \
+#define GP_DEFINE_PLAIN(NAME, TILES, KG2TILES, WIDES, NOSCHED, KSPLIT)                              \
   hipError_t launch_tile_##NAME(int ms, int tm, int tn, int tkb, int pipe, int epi, int kg, bool fused, \
-                                const TileArgs& a, hipStream_t s) {                                 \
-    if (fused) return launch_tile_##NAME##_fused(ms, tm, tn, tkb, pipe, epi, kg, a, s);            \
+                                bool sched, const TileArgs& a, hipStream_t s) {                     \
+    if (fused) return sched ? launch_tile_##NAME##_fused(ms, tm, tn, tkb, pipe, epi, kg, a, s)     \
+                            : hipErrorInvalidValue;                                                 \
     TILES(GP_TILE_CASE)                                                                             \
     KG2TILES(GP_TILE_CASE_KG2)                                                                      \
+    NOSCHED(GP_TILE_CASE_NOSCHED)                                                                   \
+    KSPLIT(GP_TILE_CASE_KSPLIT)                                                                     \
     return hipErrorInvalidValue;                                                                    \
   }                                                                                                 \
   hipError_t launch_wide_##NAME(int ms, int tkb, int pipe, bool fused, const TileArgs& a, hipStream_t s) { \
@@ -79,6 +86,7 @@ hipError_t launch_splitk_i4(int nb, int waves, int kch, int mb, const SplitArgs&
 #define GP_DEFINE_FUSED(NAME, TILES, KG2TILES, WIDES)                                               \
   hipError_t launch_tile_##NAME##_fused(int ms, int tm, int tn, int tkb, int pipe, int epi, int kg, \
                                         const TileArgs& a, hipStream_t s) {                         \
+    constexpr bool sched = true; /* fused variants keep the pinned schedule */                       \
     TILES(GP_TILE_CASE_FUSED)                                                                       \
     KG2TILES(GP_TILE_CASE_KG2_FUSED)                                                                \
     return hipErrorInvalidValue;                                                                    \

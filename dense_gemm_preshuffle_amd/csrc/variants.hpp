@@ -26,7 +26,7 @@
   X(DT_FP8, 16, 32, 128, 128, 3) X(DT_FP8, 16, 32, 128, 256, 3) X(DT_FP8, 16, 32, 256, 256, 3)  \
   X(DT_FP8, 16, 32, 256, 128, 4) X(DT_FP8, 16, 32, 256, 128, 6)   \
   X(DT_FP8, 16, 32, 128, 256, 4) X(DT_FP8, 16, 32, 128, 256, 6) X(DT_FP8, 16, 64, 256, 128, 4)   \
-  X(DT_FP8, 16, 64, 128, 256, 3)
+  X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 128, 128, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)
 
 #define GP_TILE_BF16(X)                                                                            \
   X(DT_BF16, 16, 32, 128, 128, 0) X(DT_BF16, 16, 64, 128, 128, 0) X(DT_BF16, 16, 128, 256, 128, 0) X(DT_BF16, 16, 128, 256, 64, 0)          \
@@ -94,6 +94,33 @@
   X(DT_I4, 16, 64, 128, 64, 3) X(DT_I4, 16, 32, 128, 64, 3) X(DT_I4, 16, 32, 64, 64, 0)
 #define GP_TILE_KG2_I4(X)
 #define GP_WIDE_I4(W)
+
+// Tiles that also have a variant with the compiler's own hot-loop order
+// (gemm_opts.scheduler = 2): the planner's default tiles of the benchmark
+// workloads, plain epilogue only.
+#define GP_TILE_NOSCHED_I8(X) X(DT_I8, 16, 16, 64, 256, 0) X(DT_I8, 16, 64, 128, 256, 3)
+#define GP_TILE_NOSCHED_FP8(X) X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 64, 256, 128, 3) \
+  X(DT_FP8, 16, 128, 256, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)
+#define GP_TILE_NOSCHED_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3)
+#define GP_TILE_NOSCHED_F16(X) X(DT_F16, 16, 128, 256, 128, 3)
+#define GP_TILE_NOSCHED_FP4(X) X(DT_FP4, 32, 128, 256, 128, 2)
+#define GP_TILE_NOSCHED_I4(X) X(DT_I4, 16, 64, 128, 128, 3)
+#define GP_TILE_NOSCHED_ALL(X) GP_TILE_NOSCHED_I8(X) GP_TILE_NOSCHED_FP8(X) GP_TILE_NOSCHED_BF16(X) \
+  GP_TILE_NOSCHED_F16(X) GP_TILE_NOSCHED_FP4(X) GP_TILE_NOSCHED_I4(X)
+
+// Tiles that also have a variant able to split K across workgroups
+// (gemm_ex_ws, gemm_opts.ksplit > 1), plain epilogue only, in the order the
+// planner prefers them for an automatic split (measured on long-K shapes:
+// FP8 64 x 128 beat 128 x 128, FP4 128 x 128 beat 128 x 256).
+#define GP_TILE_KSPLIT_I8(X) X(DT_I8, 16, 64, 128, 256, 3) X(DT_I8, 16, 128, 128, 128, 0)
+#define GP_TILE_KSPLIT_FP8(X) X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 64, 256, 128, 3) \
+  X(DT_FP8, 16, 32, 256, 256, 3) X(DT_FP8, 16, 128, 128, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)
+#define GP_TILE_KSPLIT_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3) X(DT_BF16, 16, 64, 128, 128, 0)
+#define GP_TILE_KSPLIT_F16(X) X(DT_F16, 16, 128, 256, 128, 3)
+#define GP_TILE_KSPLIT_FP4(X) X(DT_FP4, 32, 128, 128, 128, 0) X(DT_FP4, 32, 128, 256, 128, 2)
+#define GP_TILE_KSPLIT_I4(X) X(DT_I4, 16, 64, 128, 128, 3) X(DT_I4, 16, 64, 256, 64, 3)
+#define GP_TILE_KSPLIT_ALL(X) GP_TILE_KSPLIT_I8(X) GP_TILE_KSPLIT_FP8(X) GP_TILE_KSPLIT_BF16(X) \
+  GP_TILE_KSPLIT_F16(X) GP_TILE_KSPLIT_FP4(X) GP_TILE_KSPLIT_I4(X)
 
 #define GP_TILE_ALL(X) GP_TILE_I8(X) GP_TILE_FP8(X) GP_TILE_BF16(X) GP_TILE_FP4(X) GP_TILE_F16(X) GP_TILE_I4(X)
 #define GP_TILE_KG2_ALL(X) GP_TILE_KG2_I8(X) GP_TILE_KG2_FP8(X) GP_TILE_KG2_BF16(X) GP_TILE_KG2_F16(X) GP_TILE_KG2_FP4(X) \

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import gemm_a8w8, gemm_bf16, gemm_ex, gemm_f16, gemm_mxfp4, gemm_preshuffle_b, gemm_w4a8
+from . import gemm_a8w8, gemm_bf16, gemm_ex, gemm_ex_ws, gemm_f16, gemm_mxfp4, gemm_preshuffle_b, gemm_w4a8
 
 
 def to_device(dtype: str, host: dict, device="cuda") -> dict:
@@ -35,8 +35,13 @@ def prepare(dtype: str, dev: dict, stream=None) -> dict:
 
 def run(dtype: str, p: dict, opts=None, c=None, stream=None, act=None):
     """Launch the type's own entry point, or gemm_ex with the fused epilogue
-    (bias p["bias"] if present, activation `act`) when `act` is given."""
+    (bias p["bias"] if present, activation `act`) when `act` is given, or
+    gemm_ex_ws when p holds a "workspace" entry (a tensor, or None where the
+    plan needs none)."""
     N = p["N"]
+    if "workspace" in p:
+        return gemm_ex_ws(dtype, p["a"], p["b_shuf"], p.get("scale_a"), p.get("scale_b"), p.get("bias"),
+                          act or "none", c=c, N=N, opts=opts, workspace=p["workspace"], stream=stream)
     if act is not None:
         return gemm_ex(dtype, p["a"], p["b_shuf"], p.get("scale_a"), p.get("scale_b"), p.get("bias"), act,
                        c=c, N=N, opts=opts, stream=stream)

@@ -17,6 +17,9 @@
  *   - Ownership: the caller owns every buffer; all data pointers are DEVICE
  *     pointers (hipMalloc'd or equivalent) unless stated otherwise. The
  *     library keeps no pointer after the call returns and allocates nothing.
+ *     A plan that splits K across workgroups needs a caller-provided device
+ *     workspace (gemm_ex_ws, sized by gemm_workspace_size); the other entry
+ *     points never split K across workgroups and need none.
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
  *     null stream). Nothing synchronizes; results are ready when the stream
  *     reaches that point.
@@ -41,6 +44,7 @@
 #ifndef GEMM_PRESHUFFLE_H
 #define GEMM_PRESHUFFLE_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -53,7 +57,9 @@ typedef enum gp_status {
   GP_ESHAPE = 2,  /* layout or tile divisibility violated, or size over 2^31 bytes   */
   GP_EDTYPE = 3,  /* unsupported dtype or dtype/scale combination                    */
   GP_EARCH = 4,   /* the current device is not gfx950                                */
-  GP_EHIP = 5     /* a HIP runtime call or kernel launch failed                      */
+  GP_EHIP = 5,    /* a HIP runtime call or kernel launch failed                      */
+  GP_EWORKSPACE = 6 /* the plan splits K across workgroups and the call brings no
+                       workspace, or one smaller than gemm_workspace_size reports    */
 } gp_status;
 
 typedef enum gp_dtype {
@@ -112,6 +118,16 @@ typedef struct gemm_opts {
   int mfma;         /* tile kernel: MFMA block 16 (16x16) or 32 (32x32), 0 auto */
   int pipeline;     /* tile kernel: 1 A staged through VGPRs (2 stages), 2 .. 6 A
                        by LDS DMA with that many stages (where compiled), 0 auto */
+  int ksplit;       /* tile kernel: K split across workgroups (GEMM Optimization
+                       Guide §13, "tile_m x tile_n fills GPU"): 0 the planner's
+                       choice (no split outside gemm_ex_ws), 1 no split, S = 2 ..
+                       64 workgroups per tile, each taking 1/S of the K tiles
+                       (S must divide them); S > 1 only through gemm_ex_ws   */
+  int scheduler;    /* tile kernel hot-loop schedule (Kernel Tuning Guide §5,
+                       GEMM Optimization Guide §5.3): 0 the planner's choice,
+                       1 on (loads and LDS reads pinned between the MFMA groups),
+                       2 off (the compiler orders the loop); "off" exists for
+                       the tiles listed with a scheduler-off variant           */
 } gemm_opts;
 
 /* What the planner chose (host-side query, no GPU needed). */
@@ -130,6 +146,9 @@ typedef struct gemm_plan_info {
   int64_t mfma_total;               /* MFMA instructions the launch issues      */
   int mfma;                         /* MFMA block: 16 (16x16) or 32 (32x32)     */
   int pipeline;                     /* 1 VGPR-staged A; 2 .. 6 LDS DMA stages   */
+  int ksplit;                       /* workgroups per tile along K (1: no split)*/
+  int scheduler;                    /* 1 pinned hot-loop schedule, 2 compiler's */
+  int64_t workspace_bytes;          /* device workspace the call needs (0: none)*/
 } gemm_plan_info;
 
 /*
@@ -250,6 +269,49 @@ int gemm_ex(int in_dtype, int out_dtype, const void* a, const void* b_shuf, cons
  */
 int gemm_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* opts,
               gemm_plan_info* out);
+
+/*
+ * gemm_ex_ws -- gemm_ex with a caller-provided device workspace, which lets
+ * the planner split K across workgroups on the tile kernel where the tiles
+ * alone would leave CUs idle (GEMM Optimization Guide §13, Tiling: "tile_m x
+ * tile_n fills GPU (enough blocks)"; §1.3's tile table read with the 256 CUs
+ * of MI355X).
+ *   workspace        device, 16-byte aligned, at least gemm_workspace_size
+ *                    bytes for the same arguments (ignored, and may be NULL,
+ *                    when that size is 0). It holds one arrival counter per
+ *                    output tile followed by the partial sums (fp32, or int32
+ *                    for INT8 / W4A8) of every workgroup of each tile.
+ *                    The counters must be ZERO before the first call that
+ *                    uses the workspace (e.g. hipMemset it once after
+ *                    allocating it); every call leaves them zero again, so
+ *                    the same workspace serves any number of later calls
+ *                    that are ordered on one stream. Calls that may run at
+ *                    the same time need workspaces of their own.
+ *   workspace_bytes  its size in bytes.
+ * The workgroups of one tile each add up a contiguous range of the K tiles
+ * and store their partial sums; the last of them to finish adds the partial
+ * sums in the fixed order of the ranges (so the result is the same on every
+ * run, whichever finishes last) and applies the epilogue of gemm_ex. No
+ * workgroup waits for another. Other arguments, results and errors as
+ * gemm_ex; GP_EWORKSPACE when the workspace is missing or too small.
+ */
+int gemm_ex_ws(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
+               const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
+               const gemm_opts* opts, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gemm_workspace_size -- host-only: the workspace bytes (*bytes) a gemm_ex_ws
+ * call with these sizes and options needs; 0 when its plan does not split K
+ * across workgroups. Returns the status the planner would (no device check).
+ */
+int gemm_workspace_size(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* opts, size_t* bytes);
+
+/*
+ * gemm_plan_ws -- host-only: as gemm_plan, for the plan of gemm_ex_ws (which
+ * may split K across workgroups; out->ksplit, out->workspace_bytes).
+ * gemm_plan itself reports the plan of the entry points without a workspace.
+ */
+int gemm_plan_ws(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* opts, gemm_plan_info* out);
 
 /* Static, human-readable description of a gp_status value. */
 const char* gemm_status_string(int status);

@@ -348,3 +348,93 @@ def test_small_m_row_blocks(dtype):
         assert p["mfma_total"] * F.flops_per_mfma_gfx950(dtype, 16) >= F.flops(M, 7168, 2048)
     q = gp.gemm_plan(dtype, 64, 7168, 2048, dict(kernel=2, tile_m=16))
     assert q["tile_m"] == 16
+
+
+# ---------------------------------------------------------------- K split across workgroups, scheduler option
+@pytest.mark.parametrize("dtype,M,N,K,tile,ks", [
+    ("fp8", 256, 2048, 16384, (64, 128, 256), 4), ("bf16", 512, 2048, 16384, (128, 256, 64), 8),
+    ("w4a8", 256, 4096, 8192, (64, 128, 256), 2), ("fp8", 128, 4096, 8192, (64, 128, 256), 4),
+    ("mxfp4", 256, 4096, 16384, (128, 128, 256), 4), ("bf16", 256, 1024, 8192, (64, 128, 64), 8)])
+def test_automatic_k_split_on_long_k(dtype, M, N, K, tile, ks):
+    """gemm_ex_ws splits K where the tiles alone cannot fill 256 CUs with a
+    64 x 128 or larger tile; the entry points without a workspace never do."""
+    p = gp.gemm_plan_ws(dtype, M, N, K)
+    assert (p["tile_m"], p["tile_n"], p["tile_k"], p["ksplit"]) == (*tile, ks)
+    assert p["grid"] == -(-M // tile[0]) * -(-N // tile[1]) * ks == 256
+    T = -(-M // tile[0]) * -(-N // tile[1])
+    assert p["workspace_bytes"] == gp.gemm_workspace_size(dtype, M, N, K) == \
+        -(-T * 4 // 256) * 256 + T * ks * tile[0] * tile[1] * 4
+    q = gp.gemm_plan(dtype, M, N, K)
+    assert q["ksplit"] == 1 and q["workspace_bytes"] == 0
+    # the launch covers the same MFMAs as without a split
+    assert p["mfma_total"] * 1 == (p["grid"] * p["waves"] * p["k_tiles"] * p["mfma_per_wave_tile"])
+
+
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_benchmark_workloads_are_not_split(name):
+    """Short K (the workloads' K at most 8192 with grids of >= 256 tiles, or
+    the small-M kernel): no split, no workspace."""
+    dtype, M, N, K, seed, tile = CONFIGS[name]
+    p = gp.gemm_plan_ws(dtype, M, N, K)
+    assert p["ksplit"] == 1 and p["workspace_bytes"] == 0
+    assert {k: v for k, v in p.items() if k not in ("ksplit", "scheduler", "workspace_bytes")} == \
+        {k: v for k, v in gp.gemm_plan(dtype, M, N, K).items() if k not in ("ksplit", "scheduler", "workspace_bytes")}
+
+
+def test_k_split_options():
+    lib = gp.load_library()
+    info = gp.GemmPlanInfo()
+    o = gp.GemmOpts(kernel=1, tile_m=64, tile_n=128, tile_k=256, ksplit=2)
+    # a split needs the workspace entry point
+    assert lib.gemm_plan(1, 512, 4096, 4096, ctypes.byref(o), ctypes.byref(info)) == gp.GP_EWORKSPACE
+    assert lib.gemm_plan_ws(1, 512, 4096, 4096, ctypes.byref(o), ctypes.byref(info)) == GP_OK
+    assert info.ksplit == 2 and info.grid == 512 and info.k_tiles == 8
+    # the split must divide the K tiles (16 here)
+    o.ksplit = 3
+    assert lib.gemm_plan_ws(1, 512, 4096, 4096, ctypes.byref(o), ctypes.byref(info)) == GP_ESHAPE
+    # no split variant of this tile
+    o2 = gp.GemmOpts(kernel=1, tile_m=32, tile_n=128, tile_k=128, ksplit=2)
+    assert lib.gemm_plan_ws(1, 512, 4096, 4096, ctypes.byref(o2), ctypes.byref(info)) == GP_ESHAPE
+    # small-M kernel: no split across workgroups
+    o3 = gp.GemmOpts(kernel=2, ksplit=2)
+    assert lib.gemm_plan_ws(1, 16, 7168, 2048, ctypes.byref(o3), ctypes.byref(info)) == GP_ESHAPE
+    for bad in (-1, 65):
+        o4 = gp.GemmOpts(ksplit=bad)
+        assert lib.gemm_plan_ws(1, 512, 4096, 4096, ctypes.byref(o4), ctypes.byref(info)) == GP_EINVAL
+    n = ctypes.c_size_t(7)
+    assert lib.gemm_workspace_size(1, 512, 4096, 4096, None, ctypes.byref(n)) == GP_OK and n.value == 0
+    assert lib.gemm_workspace_size(1, 512, 4096, 4096, None, None) == GP_EINVAL
+
+
+def test_scheduler_option():
+    # default tiles of the benchmark workloads have a scheduler-off variant
+    for name in ("fp8_512x4096x4096", "bf16_8192x8192x8192", "mxfp4_4096x4096x8192", "fp16_8192x8192x8192",
+                 "w4a8_512x4096x4096", "int8_128x256x512"):
+        dtype, M, N, K, seed, tile = CONFIGS[name]
+        assert gp.gemm_plan(dtype, M, N, K)["scheduler"] == 1
+        assert gp.gemm_plan(dtype, M, N, K, dict(scheduler=2))["scheduler"] == 2
+        assert gp.gemm_plan(dtype, M, N, K, dict(scheduler=1))["scheduler"] == 1
+    with pytest.raises(gp.GemmError) as e:      # no scheduler-off variant of this tile
+        gp.gemm_plan("fp8", 512, 4096, 4096, dict(kernel=1, tile_m=32, tile_n=128, tile_k=128, scheduler=2))
+    assert e.value.status == GP_ESHAPE
+    with pytest.raises(gp.GemmError) as e:      # the small-M kernel has no pinned schedule to turn off
+        gp.gemm_plan("fp8", 16, 7168, 2048, dict(scheduler=2))
+    assert e.value.status == GP_ESHAPE
+    assert gp.gemm_plan("fp8", 16, 7168, 2048)["scheduler"] == 2
+    with pytest.raises(gp.GemmError) as e:
+        gp.gemm_plan("fp8", 512, 4096, 4096, dict(scheduler=3))
+    assert e.value.status == GP_EINVAL
+
+
+def test_workspace_validation(fake_ptrs):
+    lib = fake_ptrs
+    o = gp.GemmOpts(kernel=1, tile_m=64, tile_n=128, tile_k=256, ksplit=2)
+    need = gp.gemm_workspace_size("fp8", 512, 4096, 4096, o)
+    S = ctypes.c_void_p(0x200000)
+    args = (1, 2, FAKE, FAKE, S, S, None, 0, FAKE, 512, 4096, 4096, ctypes.byref(o))
+    assert lib.gemm_ex_ws(*args, None, need, None) == gp.GP_EWORKSPACE
+    assert lib.gemm_ex_ws(*args, FAKE, need - 1, None) == gp.GP_EWORKSPACE
+    assert lib.gemm_ex_ws(*args, MIS, need, None) == GP_EINVAL
+    # split with a fused epilogue: not compiled
+    args_b = (1, 2, FAKE, FAKE, S, S, FAKE, 1, FAKE, 512, 4096, 4096, ctypes.byref(o))
+    assert lib.gemm_ex_ws(*args_b, FAKE, need, None) == GP_ESHAPE
