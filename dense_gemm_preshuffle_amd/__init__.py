@@ -355,3 +355,4 @@ def gemm_ex_ws(dtype, a, b_shuf, scale_a=None, scale_b=None, bias=None, act="non
                                      a_, _ptr(c), M, N, K, _opts(opts), _ptr(workspace), nbytes, _stream(stream)),
            "gemm_ex_ws")
     return c
+

@@ -113,14 +113,18 @@ struct Plan {
   int64_t Kb = 0;
 };
 
-// Workspace of a K split across workgroups: the tiles' arrival counters
-// (4 bytes each, the area rounded up to 256 bytes), then ks partial tiles of
-// TM x TN 4-byte sums per tile.
+// Workspace of a K split across workgroups: a fixed area of arrival counters
+// (4 bytes per tile, for up to kMaxSplitTiles tiles), then ks partial tiles of
+// TM x TN 4-byte sums per tile. The counter area is the same for every
+// shape, so a workspace whose counters are zero (as every call leaves them)
+// can serve calls of any shape: a later call's counters never fall where an
+// earlier call left partial sums.
+constexpr int64_t kMaxSplitTiles = 16384;
+constexpr int64_t kCounterBytes = kMaxSplitTiles * 4;
 int64_t tiles_of(const Plan& p, int64_t M, int64_t N) { return ((M + p.tm - 1) / p.tm) * ((N + p.tn - 1) / p.tn); }
-int64_t counter_bytes(const Plan& p, int64_t M, int64_t N) { return (tiles_of(p, M, N) * 4 + 255) / 256 * 256; }
 int64_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
   if (p.ks <= 1) return 0;
-  return counter_bytes(p, M, N) + tiles_of(p, M, N) * p.ks * p.tm * p.tn * 4;
+  return kCounterBytes + tiles_of(p, M, N) * p.ks * p.tm * p.tn * 4;
 }
 
 // K bytes of B one MFMA consumes (per MS x MS block); a W4A8 piece of 64
@@ -419,6 +423,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   if (o && o->ksplit > 1) {
     if ((Kb / p->tkb) % ((int64_t)o->ksplit * p->kg)) return GP_ESHAPE;
     if (p->kg != 1 || !ksplit_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe)) return GP_ESHAPE;
+    if (tiles_of(*p, M, N) > kMaxSplitTiles) return GP_ESHAPE;
     p->ks = o->ksplit;
   } else if (ws && !user_tile && p->kg == 1 && !(o && (o->ksplit == 1 || o->pipeline || o->mfma || o->scheduler))) {
     auto_ksplit(dt, M, N, Kb, p);
@@ -585,7 +590,7 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
     t.act = act;
     t.ksplit = (uint32_t)p.ks;
     t.cnt = p.ks > 1 ? (uint32_t*)ws : nullptr;
-    t.part = p.ks > 1 ? (char*)ws + counter_bytes(p, M, N) : nullptr;
+    t.part = p.ks > 1 ? (char*)ws + kCounterBytes : nullptr;
     const bool fused = bias != nullptr || act != GP_ACT_NONE;
     if (p.kernel == GP_KERNEL_WIDE) {
       switch (dt) {
@@ -665,9 +670,10 @@ __global__ __launch_bounds__(256) void preshuffle_kernel(const char* __restrict_
 
 // Every GEMM entry point lands here: validation (pointers, dtype pair,
 // scales, epilogue), the plan, the device check, the launch.
+// ws_mode: 0 no workspace (never split), 1 the caller's (ws, ws_bytes).
 int run_gemm(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
              const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
-             const gemm_opts* opts, void* stream, bool ws_call = false, void* ws = nullptr, size_t ws_bytes = 0) {
+             const gemm_opts* opts, void* stream, int ws_mode = 0, void* ws = nullptr, size_t ws_bytes = 0) {
   if (!a || !b_shuf || !c || !aligned16(a) || !aligned16(b_shuf) || !aligned16(c)) return GP_EINVAL;
   if (act < GP_ACT_NONE || act > GP_ACT_GELU) return GP_EINVAL;
   if (bias && !aligned16(bias)) return GP_EINVAL;
@@ -692,7 +698,7 @@ int run_gemm(int in_dtype, int out_dtype, const void* a, const void* b_shuf, con
     return GP_EDTYPE;
   }
   Plan p;
-  int r = make_plan(in_dtype, M, N, K, opts, &p, ws_call);
+  int r = make_plan(in_dtype, M, N, K, opts, &p, ws_mode != 0);
   if (r) return r;
   // the scheduler-off and K-split variants have the plain epilogue only
   if ((p.sched == 2 || p.ks > 1) && (bias || act != GP_ACT_NONE)) return GP_ESHAPE;
@@ -814,7 +820,7 @@ int gemm_workspace_size(int in_dtype, int64_t M, int64_t N, int64_t K, const gem
 int gemm_ex_ws(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
                const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
                const gemm_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
-  return run_gemm(in_dtype, out_dtype, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, K, opts, stream, true,
+  return run_gemm(in_dtype, out_dtype, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, K, opts, stream, 1,
                   workspace, workspace_bytes);
 }
 

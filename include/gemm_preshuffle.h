@@ -278,15 +278,16 @@ int gemm_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* op
  * of MI355X).
  *   workspace        device, 16-byte aligned, at least gemm_workspace_size
  *                    bytes for the same arguments (ignored, and may be NULL,
- *                    when that size is 0). It holds one arrival counter per
- *                    output tile followed by the partial sums (fp32, or int32
- *                    for INT8 / W4A8) of every workgroup of each tile.
- *                    The counters must be ZERO before the first call that
+ *                    when that size is 0). Its first 64 KiB hold one arrival
+ *                    counter per output tile (a split plan has at most 16384
+ *                    tiles, else GP_ESHAPE); the partial sums (fp32, or int32
+ *                    for INT8 / W4A8) of every workgroup of each tile follow.
+ *                    The first 64 KiB must be ZERO before the first call that
  *                    uses the workspace (e.g. hipMemset it once after
  *                    allocating it); every call leaves them zero again, so
- *                    the same workspace serves any number of later calls
- *                    that are ordered on one stream. Calls that may run at
- *                    the same time need workspaces of their own.
+ *                    the same workspace serves any number of later calls, of
+ *                    any shapes, that are ordered on one stream. Calls that
+ *                    may run at the same time need workspaces of their own.
  *   workspace_bytes  its size in bytes.
  * The workgroups of one tile each add up a contiguous range of the K tiles
  * and store their partial sums; the last of them to finish adds the partial

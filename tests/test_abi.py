@@ -363,7 +363,7 @@ def test_automatic_k_split_on_long_k(dtype, M, N, K, tile, ks):
     assert p["grid"] == -(-M // tile[0]) * -(-N // tile[1]) * ks == 256
     T = -(-M // tile[0]) * -(-N // tile[1])
     assert p["workspace_bytes"] == gp.gemm_workspace_size(dtype, M, N, K) == \
-        -(-T * 4 // 256) * 256 + T * ks * tile[0] * tile[1] * 4
+        65536 + T * ks * tile[0] * tile[1] * 4
     q = gp.gemm_plan(dtype, M, N, K)
     assert q["ksplit"] == 1 and q["workspace_bytes"] == 0
     # the launch covers the same MFMAs as without a split
@@ -438,3 +438,12 @@ def test_workspace_validation(fake_ptrs):
     # split with a fused epilogue: not compiled
     args_b = (1, 2, FAKE, FAKE, S, S, FAKE, 1, FAKE, 512, 4096, 4096, ctypes.byref(o))
     assert lib.gemm_ex_ws(*args_b, FAKE, need, None) == GP_ESHAPE
+
+
+def test_split_tile_count_limit():
+    """A split plan has at most 16384 tiles (the fixed counter area)."""
+    ok = dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, ksplit=2)
+    assert gp.gemm_plan_ws("fp8", 64 * 128, 128 * 128, 4096, ok)["ksplit"] == 2       # 16384 tiles
+    with pytest.raises(gp.GemmError) as e:
+        gp.gemm_plan_ws("fp8", 64 * 129, 128 * 128, 4096, ok)                         # 16512 tiles
+    assert e.value.status == GP_ESHAPE

@@ -159,3 +159,27 @@ def test_automatic_split_parity(dtype, M, N, K):
     _, (o1, o2) = _run_ws(dtype, host, None)
     assert np.array_equal(o1, o2)
     check(dtype, host, o1)
+
+
+def test_one_workspace_serves_shapes_of_any_size():
+    """One zeroed workspace, calls with fewer, then more, then fewer tiles:
+    the counters always sit in the same fixed area, so no call finds an
+    earlier call's partial sums where its counters are."""
+    import torch
+
+    import dense_gemm_preshuffle_amd as gp
+    from dense_gemm_preshuffle_amd import workload
+
+    cases = [("fp8", 128, 2048, 8192), ("fp8", 256, 4096, 16384), ("fp8", 128, 1024, 16384), ("fp8", 200, 2000, 16384)]
+    need = max(gp.gemm_workspace_size(*c) for c in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for dtype, M, N, K in cases:
+        plan = gp.gemm_plan_ws(dtype, M, N, K)
+        say(f"shared workspace {dtype} {M}x{N}x{K}: ksplit {plan['ksplit']} grid {plan['grid']}")
+        assert plan["ksplit"] > 1
+        host = workloads.make_inputs(dtype, M, N, K, seed=M + N)
+        p = workload.prepare(dtype, workload.to_device(dtype, host))
+        c = gp.gemm_ex_ws(dtype, p["a"], p["b_shuf"], p["scale_a"], p["scale_b"], N=N, workspace=ws)
+        torch.cuda.synchronize()
+        check(dtype, host, workload.to_host(c))
+    assert not ws[:65536].any().item()
