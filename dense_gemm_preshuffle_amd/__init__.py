@@ -18,6 +18,8 @@ points have the names of the C ABI (include/gemm_preshuffle.h):
     gemm_workspace_size(dtype, M, N, K, opts)        -> bytes gemm_ex_ws needs (0: none)
     gemm_plan_ws(dtype, M, N, K, opts)               -> dict, the plan of gemm_ex_ws
     workspace(dtype, M, N, K, opts)                  -> a zeroed device workspace of that size
+    gemm_ex_noalloc(dtype, ...)                      -> gemm_ex_ws on the library's own static
+                                                        device workspace (allocates nothing)
 
 Tensors: A is [M, K] (INT8 / FP8 as any 1-byte dtype, BF16 / FP16 as
 bfloat16 / float16 or a 2-byte integer view, MXFP4 as uint8 [M, K/2]; W4A8:
@@ -34,7 +36,7 @@ import re
 __all__ = [
     "GemmError", "GemmLibraryMissing", "GemmOpts", "lib_path", "load_library",
     "gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_f16", "gemm_w4a8", "gemm_ex",
-    "gemm_plan", "ACTS", "gemm_ex_ws", "gemm_workspace_size", "gemm_plan_ws", "workspace",
+    "gemm_plan", "ACTS", "gemm_ex_ws", "gemm_ex_noalloc", "gemm_workspace_size", "gemm_plan_ws", "workspace",
     "gemm_status_string", "source_hash", "DTYPES", "EPI_DIRECT", "EPI_CSHUFFLE", "KERNEL_TILE", "KERNEL_SPLITK",
     "KERNEL_WIDE",
 ]
@@ -119,12 +121,13 @@ def load_library():
     lib.gemm_workspace_size.argtypes = [ci, i64, i64, i64, ctypes.POINTER(GemmOpts), ctypes.POINTER(ctypes.c_size_t)]
     lib.gemm_ex_ws.argtypes = [ci, ci, vp, vp, vp, vp, vp, ci, vp, i64, i64, i64, ctypes.POINTER(GemmOpts), vp,
                                ctypes.c_size_t, vp]
+    lib.gemm_ex_noalloc.argtypes = [ci, ci, vp, vp, vp, vp, vp, ci, vp, i64, i64, i64, ctypes.POINTER(GemmOpts), vp]
     lib.gemm_status_string.argtypes = [ci]
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_last_hip_error.argtypes = []
     lib.gemm_last_hip_error.restype = ctypes.c_char_p
     for f in ("gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_f16", "gemm_w4a8", "gemm_ex",
-              "gemm_plan", "gemm_plan_ws", "gemm_workspace_size", "gemm_ex_ws"):
+              "gemm_plan", "gemm_plan_ws", "gemm_workspace_size", "gemm_ex_ws", "gemm_ex_noalloc"):
         getattr(lib, f).restype = ci
     _lib = lib
     return lib
@@ -356,3 +359,20 @@ def gemm_ex_ws(dtype, a, b_shuf, scale_a=None, scale_b=None, bias=None, act="non
            "gemm_ex_ws")
     return c
 
+
+def gemm_ex_noalloc(dtype, a, b_shuf, c, scale_a=None, scale_b=None, bias=None, act="none", N=None, opts=None,
+                    stream=None):
+    """gemm_ex_ws on the library's own static device workspace: nothing is
+    allocated, so the output tensor `c` must be given. Calls that overlap in
+    time on one device share that workspace and must not be made."""
+    dt = _dt(dtype)
+    out_dt = _OUT[dt]
+    M = a.shape[0]
+    K = _row_bytes(a) * 8 // (8 if dt == GP_I4 else _ELEM_BITS[dt])
+    if N is None:
+        N = b_shuf.numel() * b_shuf.element_size() * 8 // (K * _ELEM_BITS[dt])
+    a_ = ACTS[act] if isinstance(act, str) else int(act)
+    _check(load_library().gemm_ex_noalloc(dt, out_dt, _ptr(a), _ptr(b_shuf), _ptr(scale_a), _ptr(scale_b),
+                                          _ptr(bias), a_, _ptr(c), M, N, K, _opts(opts), _stream(stream)),
+           "gemm_ex_noalloc")
+    return c

@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gemm_preshuffle.h"
 #include "launch.hpp"
@@ -670,7 +671,54 @@ __global__ __launch_bounds__(256) void preshuffle_kernel(const char* __restrict_
 
 // Every GEMM entry point lands here: validation (pointers, dtype pair,
 // scales, epilogue), the plan, the device check, the launch.
-// ws_mode: 0 no workspace (never split), 1 the caller's (ws, ws_bytes).
+// ---- the library's own workspace, for the allocation-free entry point ----
+// One static device array (per device: each device that loads the library's
+// code holds its own copy until the process ends). Host code never uses its
+// name as an address: the device address comes from hipGetSymbolAddress,
+// once per device, with that device current.
+constexpr int64_t kScratchBytes = ((int64_t)32 << 20) + kCounterBytes;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, uint32_t n) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[64];
+
+// Device address of the current device's scratch array; on the first call
+// on a device its counter area is cleared by a fill kernel on `s` (ordered
+// before the GEMM that follows on the same stream).
+int scratch_for_current_device(void** out, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= 64) return GP_EHIP;
+  ScratchSlot& sl = g_scratch[dev];
+  std::call_once(sl.once, [&] {
+    void* ptr = nullptr;
+    hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (r == hipSuccess) {
+      clear_last_error();
+      const uint32_t words = (uint32_t)(kCounterBytes / 4);
+      hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, s, (uint32_t*)ptr, words);
+      r = hipGetLastError();
+    }
+    sl.err = r;
+    sl.ptr = r == hipSuccess ? ptr : nullptr;
+  });
+  if (sl.err != hipSuccess) return hip_status(sl.err);
+  *out = sl.ptr;
+  return GP_OK;
+}
+
+// ws_mode: 0 no workspace (never split), 1 the caller's (ws, ws_bytes),
+// 2 the library's static scratch array.
 int run_gemm(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
              const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
              const gemm_opts* opts, void* stream, int ws_mode = 0, void* ws = nullptr, size_t ws_bytes = 0) {
@@ -703,12 +751,18 @@ int run_gemm(int in_dtype, int out_dtype, const void* a, const void* b_shuf, con
   // the scheduler-off and K-split variants have the plain epilogue only
   if ((p.sched == 2 || p.ks > 1) && (bias || act != GP_ACT_NONE)) return GP_ESHAPE;
   const int64_t need = workspace_bytes(p, M, N);
-  if (need > 0) {
+  if (need > 0 && ws_mode == 2) {
+    if (need > kScratchBytes) return GP_EWORKSPACE;   // more than the static array holds
+  } else if (need > 0) {
     if (!ws || (int64_t)ws_bytes < need) return GP_EWORKSPACE;
     if (!aligned16(ws)) return GP_EINVAL;
   }
   r = check_device();
   if (r) return r;
+  if (need > 0 && ws_mode == 2) {
+    r = scratch_for_current_device(&ws, (hipStream_t)stream);
+    if (r) return r;
+  }
   return launch(in_dtype, p, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, ws, (hipStream_t)stream);
 }
 
@@ -822,6 +876,12 @@ int gemm_ex_ws(int in_dtype, int out_dtype, const void* a, const void* b_shuf, c
                const gemm_opts* opts, void* workspace, size_t workspace_bytes, void* stream) {
   return run_gemm(in_dtype, out_dtype, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, K, opts, stream, 1,
                   workspace, workspace_bytes);
+}
+
+int gemm_ex_noalloc(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
+                    const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
+                    const gemm_opts* opts, void* stream) {
+  return run_gemm(in_dtype, out_dtype, a, b_shuf, scale_a, scale_b, bias, act, c, M, N, K, opts, stream, 2);
 }
 
 }  // extern "C"

@@ -301,6 +301,28 @@ int gemm_ex_ws(int in_dtype, int out_dtype, const void* a, const void* b_shuf, c
                const gemm_opts* opts, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gemm_ex_noalloc -- for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): gemm_ex_ws with the library's own workspace instead of the
+ * caller's. That workspace is one static device array of
+ * GEMM_NOALLOC_SCRATCH_BYTES (32 MiB + 64 KiB) per device, which each device
+ * that runs the library holds until the process ends; the call allocates
+ * nothing. Its first call on a device looks up the array's device address
+ * and clears its counter area with a fill kernel on `stream`; every call
+ * leaves the counters zero again. Plans whose workspace would exceed the
+ * array (gemm_workspace_size > GEMM_NOALLOC_SCRATCH_BYTES) are GP_EWORKSPACE:
+ * call gemm_ex_ws with a workspace of that size instead. Every call on one
+ * device shares that device's array, so calls that may overlap in time on
+ * one device (on different streams without an ordering between them, or from
+ * several host threads at once) race and give wrong results; calls ordered
+ * on one stream are safe. Arguments, results and other errors as gemm_ex_ws.
+ */
+#define GEMM_NOALLOC_SCRATCH_BYTES ((32u << 20) + (64u << 10))
+int gemm_ex_noalloc(int in_dtype, int out_dtype, const void* a, const void* b_shuf, const void* scale_a,
+                    const void* scale_b, const float* bias, int act, void* c, int64_t M, int64_t N, int64_t K,
+                    const gemm_opts* opts, void* stream);
+
+/*
  * gemm_workspace_size -- host-only: the workspace bytes (*bytes) a gemm_ex_ws
  * call with these sizes and options needs; 0 when its plan does not split K
  * across workgroups. Returns the status the planner would (no device check).
