@@ -359,6 +359,70 @@ def config_summary(line):
     return out
 
 
+def floor_probe(name, steps, warmup, grids=((224, 4), (256, 4), (256, 8), (512, 4), (1024, 4))):
+    """The HBM streaming-read floor for the workload's algorithmic bytes: the
+    probe kernel (dense_gemm_preshuffle_amd/probe/stream_read.hip) reads that
+    many bytes (rounded up to whole 16-byte lanes of its grid) once per
+    launch, timed like the GEMM (HIP graph of the K launches over rotating
+    buffers, one untimed pass over all of them right before, HIP events)."""
+    import ctypes
+
+    import torch
+
+    from dense_gemm_preshuffle_amd import build as _b
+
+    if not os.path.exists(_b.PROBE_LIB):
+        raise SystemExit(f"{_b.PROBE_LIB} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.gp_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.gp_probe_stream_read.restype = ctypes.c_int
+    dtype, M, N, K, seed, flops, nbytes, bound = workload_numbers(name)
+    stream = torch.cuda.current_stream()
+    out = []
+    for wgs, waves in grids:
+        unit = 16 * 64 * waves * wgs
+        b = -(-nbytes // unit) * unit
+        R = max(2, min(64, math.ceil(ROTATE_BYTES / b)))
+        bufs = [torch.ones(b, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        sink = torch.empty(wgs * waves * 64, dtype=torch.int32, device="cuda")
+
+        def launch(i):
+            # the stream current at the call (inside a graph capture, the capturing stream)
+            sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            st = lib.gp_probe_stream_read(ctypes.c_void_p(bufs[i % R].data_ptr()), b, wgs, waves,
+                                          ctypes.c_void_p(sink.data_ptr()), sp)
+            if st != 0:
+                raise RuntimeError(f"gp_probe_stream_read: status {st}")
+
+        for i in range(warmup):
+            launch(i)
+        graph, roll = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                launch(i)
+        with torch.cuda.graph(roll):
+            for i in range(R):
+                launch(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        roll.replay()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        out.append({"workgroups": wgs, "waves": waves, "bytes": b, "us_per_read": us, "GB/s": b / (us * 1e-6) / 1e9,
+                    "us_for_workload_bytes": us * nbytes / b})
+        log(f"[floor] {wgs} x {waves} waves: {us:.3f} us for {b} bytes ({b / (us * 1e-6) / 1e9:.0f} GB/s)")
+        del graph, roll, bufs
+    torch.cuda.empty_cache()
+    return {"workload": name, "algorithmic_bytes": nbytes, "steps": steps, "reads": out,
+            "method": "one non-temporal 16-byte-load pass per launch over a fresh buffer (rotating, "
+                      f"{ROTATE_BYTES >> 20} MiB and more), HIP graph of the launches, HIP events"}
+
+
 def _gpu_sysfs():
     """sysfs device directory of the GPU when the host has exactly one, else None."""
     cards = [d for d in sorted(glob.glob("/sys/class/drm/card*/device")) if os.path.exists(os.path.join(d, "pp_dpm_sclk"))]
@@ -462,6 +526,9 @@ def main():
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--opts", default=None, help="JSON gemm_opts override, e.g. '{\"tile_m\":64,...}'")
+    ap.add_argument("--floor", action="store_true",
+                    help="instead of the GEMM: time the HBM streaming-read probe over the workload's "
+                         "algorithmic bytes (the floor of the memory-bound shapes), one JSON line")
     ap.add_argument("--data", default="randn", choices=["randn", "zeros"],
                     help="zeros: same launches on all-zero A and B (diagnostic of data-dependent clocks)")
     ap.add_argument("--act", default=None, choices=["none", "relu", "silu", "gelu"],
@@ -479,6 +546,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.floor:
+        print(json.dumps({"floor": floor_probe(args.workload, args.steps, args.warmup)}), flush=True)
+        return
     names = sorted(workloads.CONFIGS) if args.workload == "all" else [args.workload]
     opts = json.loads(args.opts) if args.opts else None
     kw = dict(opts=opts, use_graph=not args.eager, act=args.act, data=args.data, telemetry_s=args.telemetry_s)

@@ -19,6 +19,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm_preshuffle.so")
+# the HBM streaming-read probe that bench.py --floor times (not the GEMM library)
+PROBE_SRC = os.path.join(PKG, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(PKG, "libgp_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -91,15 +94,21 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", "-o", tmp, PROBE_SRC], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
 def clean() -> None:
     shutil.rmtree(BUILD, ignore_errors=True)
-    if os.path.exists(LIB):
-        os.remove(LIB)
+    for f in (LIB, PROBE_LIB):
+        if os.path.exists(f):
+            os.remove(f)
 
 
 if __name__ == "__main__":

@@ -49,3 +49,22 @@ def test_no_card_no_telemetry():
 def test_more_than_one_gpu_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_floor_probe_library_validates_arguments():
+    """The streaming-read probe (bench.py --floor) is built beside the GEMM
+    library and refuses bad arguments before any GPU call."""
+    import ctypes
+
+    from dense_gemm_preshuffle_amd import build as b
+
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    f = lib.gp_probe_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    buf, sink = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert f(None, 1 << 20, 256, 4, sink, None) == 1                       # null buffer
+    assert f(ctypes.c_void_p(0x100008), 1 << 20, 256, 4, sink, None) == 1  # misaligned
+    assert f(buf, 1 << 20, 0, 4, sink, None) == 1                          # no workgroups
+    assert f(buf, 1 << 20, 256, 17, sink, None) == 1                       # too many waves
+    assert f(buf, (1 << 20) + 16, 256, 4, sink, None) == 1                 # not whole lanes of the grid
