@@ -289,14 +289,14 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     const int row = arow0 + i * RPP;
     a_wr[i] = row * C::TKA + ((ach ^ ((row / C::SWP) & C::SWM)) * 16);
   }
-  auto a_wr_off = [&](int i) -> uint32_t {
+  auto a_wr_off = [&](int i) GP_INLINE -> uint32_t {
     if constexpr (AWR_STEP) return a_wr[0] + i * RPP * C::TKA;
     else return a_wr[i];
   };
   // Lanes past the last A chunk (partial passes only) load from an offset
   // outside the buffer resource (the hardware returns zeros without a memory
   // access) and write to a spare LDS slot, so the K-tile body has no branch.
-  auto a_on = [&](int i) { return !C::APART || i * C::THREADS + tid < C::ACHUNKS; };
+  auto a_on = [&](int i) GP_INLINE { return !C::APART || i * C::THREADS + tid < C::ACHUNKS; };
   constexpr uint32_t kOOB = 0x80000000u;
   // LDS DMA of A: instruction i of wave w fills the 1 KiB block i*WAVES + w of
   // the A buffer, lane l landing at byte 16*l of it. So lane l fetches the
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   // A K byte (within one MFMA step) of the lane's 16-byte piece f. W4A8: the
   // B piece of lane group g holds K elements [32g, 32g+32) of the step's 128,
   // its low nibbles the first 16 (first MFMA), its high nibbles the rest.
-  auto lane_k = [&](int f) -> int {
+  auto lane_k = [&](int f) GP_INLINE -> int {
     if constexpr (DT == DT_I4) return 32 * lgrp + 16 * f;
     return MS == 16 ? f * 64 + 16 * lgrp : 16 * lgrp;
   };
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   const uint32_t b_step = (uint32_t)(MS / 16) * 16u * Kb;  // next MFMA column block
   // K-step part of the B offset (uniform): MS = 16: K block s*(KB/64)+f; MS = 32:
   // step s covers K bytes [32s, 32s+32) = block s/2, groups 2*(s%2) + lgrp.
-  auto b_koff = [&](int s, int f) -> uint32_t {
+  auto b_koff = [&](int s, int f) GP_INLINE -> uint32_t {
     if constexpr (MS == 16) return (uint32_t)(s * (C::KB / 64) + f) * 1024u;
     else return (uint32_t)s * 512u;
   };
@@ -390,23 +390,23 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
 #pragma unroll
     for (int ni = 0; ni < C::NACC; ++ni) acc[mi][ni] = Acc{};
 
-  auto load_a = [&](int kt, int i) {
+  auto load_a = [&](int kt, int i) GP_INLINE {
     if constexpr (!C::ASYNC) a_st[i] = buf_load16(ra, a_on(i) ? a_ld0 : kOOB, kt * C::TKA + i * RPP * Ka);
   };
-  auto store_a = [&](int par) {
+  auto store_a = [&](int par) GP_INLINE {
     if constexpr (C::ASYNC) return;
     char* base = glds + par * C::ABUF;
 #pragma unroll
     for (int i = 0; i < C::ALOADS; ++i)
       *(v4i*)(base + (a_on(i) ? a_wr_off(i) : (uint32_t)(TM * C::TKA))) = a_st[i];
   };
-  auto load_a_dma = [&](int stage, int kt, int i) {
+  auto load_a_dma = [&](int stage, int kt, int i) GP_INLINE {
     if constexpr (C::ASYNC)
       lds_dma16(p.a + (size_t)m0 * Ka, TM * Ka, glds + stage * C::ABUF + (i * C::WAVES + wave) * 1024,
                 a_dma0 + kt * C::TKA + i * RPD * Ka);
   };
   // B load q of a tile: K step q / (NACC*FRAG), column block (q / FRAG) % NACC, piece q % FRAG
-  auto load_b = [&](auto par_c, int kt, int q) {
+  auto load_b = [&](auto par_c, int kt, int q) GP_INLINE {
     constexpr int par = decltype(par_c)::value;
     const int s = q / (C::NACC * C::FRAG), ni = (q / C::FRAG) % C::NACC, f = q % C::FRAG;
     const uint32_t kbase = (uint32_t)kt * (TKB / 64) * 1024u;
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   // FP4: the WG's TM + TN scale rows of one K tile, SCB bytes each. A and B
   // rows use separate loads so that each load's buffer resource is uniform.
   // scale load i of a tile: A rows for i < SLA, then B rows
-  auto load_s = [&](int st, int kt, int i) {
+  auto load_s = [&](int st, int kt, int i) GP_INLINE {
     if constexpr (DT == DT_FP4) {
       const uint32_t sbase = (uint32_t)kt * C::SCB;
       if (i < C::SLA) {
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   };
   // The 8 scale bytes of one row of one tile (byte b: K bytes [16b, 16b+16))
   // rearranged into [lane group] entries whose byte s is the scale of K step s.
-  auto perm_s = [&](v2i v) -> v2i {
+  auto perm_s = [&](v2i v) GP_INLINE -> v2i {
     v2i w;
     if constexpr (MS == 16) {
       // group g (K step s uses block 4s+g): u16 (b_g, b_{4+g})
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   };
   // scale row r (A rows first, then B rows) -> LDS as [row][lane group];
   // row SROWS is the spare slot of idle lanes.
-  auto put_s = [&](char* base, int r, v2i v) {
+  auto put_s = [&](char* base, int r, v2i v) GP_INLINE {
     if constexpr (C::SCB == 8) *(v2i*)(base + r * 8) = perm_s(v);
     else *(int*)(base + r * 4) = v[0];
   };
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   constexpr int GL_RSTEP = C::THREADS / GL_LPR;   // rows per load
   const uint32_t g_loff = (tid / GL_LPR) * srow + (tid % GL_LPR) * 16;
   const int g_lds = (tid % GL_LPR) * 2 * C::GTILE + (tid / GL_LPR) * 8;
-  auto load_g1 = [&](auto j_c, int g) -> v4i {
+  auto load_g1 = [&](auto j_c, int g) GP_INLINE -> v4i {
     constexpr int j = decltype(j_c)::value;
     constexpr bool is_a = j < C::GLA;
     constexpr int i = is_a ? j : j - C::GLA;
@@ -476,7 +476,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     return buf_load16(is_a ? rsa : rsb, on ? g_loff + u : kOOB, 0);
   };
   // ... into slot `slot` (0 or 1) of the ring: [tile of the group][row][lane group]
-  auto store_g1 = [&](auto j_c, int slot, v4i v) {
+  auto store_g1 = [&](auto j_c, int slot, v4i v) GP_INLINE {
     constexpr int j = decltype(j_c)::value;
     constexpr bool is_a = j < C::GLA;
     constexpr int i = is_a ? j : j - C::GLA;
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     *(v2i*)d0 = perm_s(v2i{v[0], v[1]});
     *(v2i*)d1 = perm_s(v2i{v[2], v[3]});
   };
-  auto store_s = [&](int par) {
+  auto store_s = [&](int par) GP_INLINE {
     if constexpr (DT == DT_FP4) {
       char* base = lds + C::ST * C::ABUF + par * C::SAREA;
 #pragma unroll
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     }
   };
   // lane's scale entry of staged row r
-  auto read_s = [&](const char* sbase, int r) -> int {
+  auto read_s = [&](const char* sbase, int r) GP_INLINE -> int {
     if constexpr (C::SCB == 8) {
       if constexpr (MS == 16) return *(const uint16_t*)(sbase + r * 8 + lgrp * 2);
       else return *(const int*)(sbase + r * 8 + lgrp * 4);
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     }
   };
   // ds_read of A fragment (s, mi) from buffer par
-  auto read_a = [&](int par, int s, int mi, v4i* af) {
+  auto read_a = [&](int par, int s, int mi, v4i* af) GP_INLINE {
     const char* base = glds + par * C::ABUF;
 #pragma unroll
     for (int f = 0; f < C::AFRAG; ++f) af[f] = *(const v4i*)(base + a_rd[s][f] + mi * MS * C::TKA);
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   };
   constexpr int NBL = C::KSTEPS * C::NACC * C::FRAG;       // B loads per tile
   constexpr int NVMEM = C::ALOADS + NBL + C::SLOADS;        // global loads per tile
-  auto compute = [&](auto par_c, int kt, auto&& issue_loads) {
+  auto compute = [&](auto par_c, int kt, auto&& issue_loads) GP_INLINE {
     constexpr int par = decltype(par_c)::value;
     // E8M0 scales from LDS: byte s of the value is the scale of K step s
     int psa[C::MREP * C::NSC + 1 - C::NSC], psb[C::NACC * C::NSC + 1 - C::NSC];
@@ -553,7 +553,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
 #pragma unroll
     for (int j = 0; j < RA; ++j) read_a(par, j / C::MREP, j % C::MREP, af[j]);
     fence();
-    static_for<0, NF>([&](auto i_c) {
+    static_for<0, NF>([&](auto i_c) GP_INLINE {
       constexpr int i = decltype(i_c)::value;
       constexpr int s = i / C::MREP, mi = i % C::MREP;
       // this group's share of the tile's global loads
@@ -581,20 +581,20 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     });
   };
   // s_waitcnt vmcnt(n) alone (expcnt / lgkmcnt left alone)
-  auto wait_vm = [&](auto n_c) {
+  auto wait_vm = [&](auto n_c) GP_INLINE {
     constexpr int n = decltype(n_c)::value;
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   };
   // global loads [J0, J1) of one tile, in the fixed order scales, A, B (the
   // wait for A at the end of an iteration counts on that order)
-  auto loads = [&](auto stage_c, int kt_in, auto j0_c, auto j1_c) {
+  auto loads = [&](auto stage_c, int kt_in, auto j0_c, auto j1_c) GP_INLINE {
     constexpr int st = decltype(stage_c)::value;
     // the tile index (made global: the group's first tile + the local one) is
     // wave-uniform; say so, so that every offset built from it stays in
     // scalar registers (a VGPR offset would need a waterfall loop)
     const int kt = __builtin_amdgcn_readfirstlane(kt0 + kt_in);
-    static_for<decltype(j0_c)::value, decltype(j1_c)::value>([&](auto j_c) {
+    static_for<decltype(j0_c)::value, decltype(j1_c)::value>([&](auto j_c) GP_INLINE {
       constexpr int j = decltype(j_c)::value;
       if constexpr (j < C::SLOADS) {
         load_s(st, kt, j);
@@ -609,7 +609,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   using J0 = std::integral_constant<int, 0>;
   using JALL = std::integral_constant<int, NVMEM>;
   // r: stage of tile kt (kt % ST); gpos: kt % SG
-  auto iter = [&](auto r_c, auto gpos_c, int kt) {
+  auto iter = [&](auto r_c, auto gpos_c, int kt) GP_INLINE {
     constexpr int r = decltype(r_c)::value;
     constexpr int gpos = decltype(gpos_c)::value;
     constexpr int rn = (r + C::ST - 1) % C::ST;  // stage of the tile ST-1 ahead
@@ -626,15 +626,15 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     const int gnext = kt / C::SG + 1;
     if constexpr (gj1 > gj0) {
       const int g = gnext * C::SG < KT ? gnext : -1;
-      static_for<gj0, gj1>([&](auto j_c) { gv[decltype(j_c)::value - gj0] = load_g1(j_c, g); });
+      static_for<gj0, gj1>([&](auto j_c) GP_INLINE { gv[decltype(j_c)::value - gj0] = load_g1(j_c, g); });
     }
-    compute(r_c, kt, [&](auto j0_c, auto j1_c) { loads(std::integral_constant<int, rn>{}, kn, j0_c, j1_c); });
+    compute(r_c, kt, [&](auto j0_c, auto j1_c) GP_INLINE { loads(std::integral_constant<int, rn>{}, kn, j0_c, j1_c); });
     store_a(rn);
     // FP4 scales of the next tile, loaded ST-2 iterations ago (its stage is
     // free: its last reader was tile kt+1-ST)
     store_s((r + 1) % C::ST);
     if constexpr (gj1 > gj0)
-      static_for<gj0, gj1>([&](auto j_c) { store_g1(j_c, gnext & 1, gv[decltype(j_c)::value - gj0]); });
+      static_for<gj0, gj1>([&](auto j_c) GP_INLINE { store_g1(j_c, gnext & 1, gv[decltype(j_c)::value - gj0]); });
     if constexpr (C::ASYNC) {
       // tile kt+1's DMA was issued ST-2 iterations ago, before that
       // iteration's B loads: everything issued after it may stay in flight
@@ -646,14 +646,14 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
 
   // ---- prologue: tiles 0 .. ST-2 into stages 0 .. ST-2 ----
   v4i g0[C::NGL > 0 ? C::NGL : 1];   // scale group 0
-  if constexpr (C::SG > 1) static_for<0, C::NGL>([&](auto j_c) { g0[decltype(j_c)::value] = load_g1(j_c, 0); });
-  static_for<0, C::ST - 1>([&](auto j_c) {
+  if constexpr (C::SG > 1) static_for<0, C::NGL>([&](auto j_c) GP_INLINE { g0[decltype(j_c)::value] = load_g1(j_c, 0); });
+  static_for<0, C::ST - 1>([&](auto j_c) GP_INLINE {
     constexpr int j = decltype(j_c)::value;
     loads(j_c, min(j, KT - 1), J0{}, JALL{});
     store_a(j);
   });
   store_s(0);
-  if constexpr (C::SG > 1) static_for<0, C::NGL>([&](auto j_c) { store_g1(j_c, 0, g0[decltype(j_c)::value]); });
+  if constexpr (C::SG > 1) static_for<0, C::NGL>([&](auto j_c) GP_INLINE { store_g1(j_c, 0, g0[decltype(j_c)::value]); });
   if constexpr (C::ASYNC) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vm(std::integral_constant<int, NBL + (C::ST - 2) * NVMEM>{});
@@ -667,11 +667,11 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   static_assert(TRIP % C::ST == 0 && TRIP % C::SG == 0, "trip covers whole stages and groups");
   int kt = 0;
   for (; kt + TRIP <= KT; kt += TRIP)
-    static_for<0, TRIP>([&](auto r_c) {
+    static_for<0, TRIP>([&](auto r_c) GP_INLINE {
       constexpr int r = decltype(r_c)::value;
       iter(std::integral_constant<int, r % C::ST>{}, std::integral_constant<int, r % C::SG>{}, kt + r);
     });
-  static_for<0, TRIP - 1>([&](auto r_c) {
+  static_for<0, TRIP - 1>([&](auto r_c) GP_INLINE {
     constexpr int r = decltype(r_c)::value;
     if (kt + r < KT) iter(std::integral_constant<int, r % C::ST>{}, std::integral_constant<int, r % C::SG>{}, kt + r);
   });
@@ -763,23 +763,23 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
       // together (one memory round trip per range and batch, not per chunk)
       constexpr int RB = NCH < 8 ? NCH : 8;
       static_assert(NCH % RB == 0, "whole batches of chunks");
-      auto get = [&](int ch) -> V4 {
+      auto get = [&](int ch) GP_INLINE -> V4 {
         const int mi = ch / (C::NACC * (C::NREG / 4)), ni = (ch / (C::NREG / 4)) % C::NACC, h = ch % (C::NREG / 4);
         V4 v;
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * h + r];
         return v;
       };
-      auto put = [&](int ch, V4 v) {
+      auto put = [&](int ch, V4 v) GP_INLINE {
         const int mi = ch / (C::NACC * (C::NREG / 4)), ni = (ch / (C::NREG / 4)) % C::NACC, h = ch % (C::NREG / 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[mi][ni][4 * h + r] = v[r];
       };
-      static_for<0, NCH / RB>([&](auto b_c) {
+      static_for<0, NCH / RB>([&](auto b_c) GP_INLINE {
         constexpr int c0 = decltype(b_c)::value * RB;
         V4 t[RB], u[RB];
         // partial sums of range z, chunks c0 .. c0+RB-1 (this workgroup's own from registers)
-        auto fetch = [&](uint32_t z, V4* dst) {
+        auto fetch = [&](uint32_t z, V4* dst) GP_INLINE {
           if (z == kz) {
 #pragma unroll
             for (int b = 0; b < RB; ++b) dst[b] = get(c0 + b);
@@ -809,11 +809,11 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   const int elrow = etid & (MS - 1), elgrp = (etid & 63) / MS;
   // For every (mi, ni) the lane holds NREG/4 runs of 4 consecutive columns
   // of row mi*MS + elrow: run h covers columns ni*MS + col_run(h) + 0..3.
-  auto col_run = [&](int h) -> int { return MS == 16 ? 4 * elgrp : 8 * h + 4 * elgrp; };
+  auto col_run = [&](int h) GP_INLINE -> int { return MS == 16 ? 4 * elgrp : 8 * h + 4 * elgrp; };
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.c + ((size_t)m0 * p.N + n0) * C::OB, ((TM - 1) * p.N + TN) * C::OB);
   // C offset of tile row r, column c; rows / columns an edge tile shares with
   // its neighbour get an offset outside the resource (the store is dropped)
-  auto c_off = [&](uint32_t r, uint32_t c) -> uint32_t {
+  auto c_off = [&](uint32_t r, uint32_t c) GP_INLINE -> uint32_t {
     return (r >= mskip && c >= nskip) ? (r * p.N + c) * C::OB : 0x80000000u;
   };
   // The scale and bias DMAs were each wave's first memory instructions, so
@@ -834,11 +834,11 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
         sbv[ni][h] = *(const v4f*)(sb + wave * C::NPW + ni * MS + col_run(h));
   }
   // bias of a run of 4 columns (read from LDS where it is used)
-  auto bias4 = [&](int ni, int h) -> v4f {
+  auto bias4 = [&](int ni, int h) GP_INLINE -> v4f {
     if constexpr (C::NBI > 0) return *(const v4f*)(lds + C::BIAS_OFF + (wave * C::NPW + ni * MS + col_run(h)) * 4);
     else return v4f{0.f, 0.f, 0.f, 0.f};
   };
-  auto out_vec = [&](auto act_c, int mi, int ni, int h, auto emit) {
+  auto out_vec = [&](auto act_c, int mi, int ni, int h, auto emit) GP_INLINE {
     constexpr int A = decltype(act_c)::value;
     if constexpr (DT == DT_I8) {
       v4i v;
@@ -861,7 +861,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   };
 
   const bool storer = grp == 0;
-  auto store_tile = [&](auto act_c) {
+  auto store_tile = [&](auto act_c) GP_INLINE {
     if constexpr (EPI == EPI_DIRECT) {
       if (!storer) return;
 #pragma unroll
@@ -871,7 +871,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
 #pragma unroll
           for (int h = 0; h < C::NREG / 4; ++h) {
             const uint32_t off = c_off(mi * MS + elrow, wave * C::NPW + ni * MS + col_run(h));
-            out_vec(act_c, mi, ni, h, [&](auto v) {
+            out_vec(act_c, mi, ni, h, [&](auto v) GP_INLINE {
               if constexpr (sizeof(v) == 16) buf_store16(v, rc, off);
               else buf_store8(v, rc, off);
             });
@@ -887,7 +887,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
 #pragma unroll
           for (int h = 0; h < C::NREG / 4; ++h) {
             char* dst = lds + (mi * MS + elrow) * C::CSTRIDE + (wave * C::NPW + ni * MS + col_run(h)) * C::OB;
-            out_vec(act_c, mi, ni, h, [&](auto v) { *(decltype(v)*)dst = v; });
+            out_vec(act_c, mi, ni, h, [&](auto v) GP_INLINE { *(decltype(v)*)dst = v; });
           }
       __syncthreads();
       constexpr int CH_ROW = TN * C::OB / 16;

@@ -11,6 +11,12 @@
 #include <type_traits>
 #include <utility>
 
+// On a lambda: inline it at every call. The kernels are written as one body
+// of lambdas; left to its own heuristics the compiler may keep a large one
+// (the K-tile iteration of the biggest tiles) as a called function, and the
+// accumulator array it updates then lives in scratch memory.
+#define GP_INLINE __attribute__((always_inline))
+
 namespace gp {
 
 typedef int v2i __attribute__((ext_vector_type(2)));

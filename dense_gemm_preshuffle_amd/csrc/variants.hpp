@@ -46,7 +46,8 @@
   X(DT_FP4, 16, 32, 256, 128, 0) X(DT_FP4, 16, 64, 128, 128, 0) X(DT_FP4, 16, 64, 256, 128, 0)              \
   X(DT_FP4, 32, 64, 128, 128, 0) X(DT_FP4, 32, 64, 256, 128, 0)                                    \
   X(DT_FP4, 32, 128, 128, 128, 0) X(DT_FP4, 32, 128, 256, 128, 0) X(DT_FP4, 32, 128, 256, 128, 2) \
-  X(DT_FP4, 16, 128, 256, 64, 2) X(DT_FP4, 16, 64, 128, 64, 0)
+  X(DT_FP4, 16, 128, 256, 64, 2) X(DT_FP4, 16, 64, 128, 64, 0)                                  \
+  X(DT_FP4, 32, 256, 256, 128, 2) X(DT_FP4, 32, 256, 256, 128, 0)
 // (No FP4 128 x 256 tile with 16 x 16 blocks, nor with a 3-stage pipeline:
 // the first put its accumulators in scratch memory, the second spilled.)
 // (No 256 x 256 tile for FP4 or FP8, nor for BF16 with 16 x 16 blocks and

@@ -73,6 +73,10 @@ TILE_CASES = [
     ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32)),
     ("mxfp4", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=32, epilogue=1)),
     ("mxfp4", 256, 256, 768, dict(kernel=1, tile_m=128, tile_n=128, tile_k=256, mfma=32)),
+    # 256 x 256 FP4 tiles (one workgroup per CU, accumulators in AGPRs), 2-stage DMA and VGPR-staged A
+    ("mxfp4", 256, 512, 2304, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
+    ("mxfp4", 512, 256, 1024, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=1)),
+    ("mxfp4", 300, 272, 4352, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=2, epilogue=1)),
     ("int8", 128, 256, 384, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128, mfma=32)),
     ("int8", 128, 512, 256, dict(kernel=1, tile_m=64, tile_n=256, tile_k=128, mfma=32, epilogue=2)),
     # A by LDS DMA, 2 or 3 pipeline stages, K-tile counts 1..5
