@@ -134,7 +134,14 @@ struct TileCfg {
   // compile time). SG = 8 where both slots fit the LDS share of a resident
   // workgroup, else 4.
   static constexpr bool GROUPED = NSC && ST == 2 && SCB == 8;
-  static constexpr int GTILE = SROWS * 8;                                  // staged bytes of one tile
+  // staged bytes of one tile. Rows are permuted inside each tile of a group:
+  // tiles 2p and 2p+1 (written by the group loads of piece p) hold row r at
+  // position r ^ 8p. The LPR pieces of one row sit a multiple of 256 bytes
+  // apart, so unpermuted every piece of a row hit the same LDS banks (a
+  // 4-way conflict on every scale write); permuted, piece p lands 16 p banks
+  // further on. The XOR stays inside a 32-row block, and every reader's row
+  // base is a multiple of 32.
+  static constexpr int GTILE = SROWS * 8;
   static constexpr int LDS_SHARE = 160 * 1024 / tile_wgs_per_cu(TM, TN, KG);
   static constexpr int slot_bytes(int sg) {
     return sg * GTILE + ((((TM * sg / 2) % THREADS) || ((TN * sg / 2) % THREADS)) ? 16 : 0);
@@ -464,7 +471,9 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
   constexpr int GL_LPR = C::LPR > 0 ? C::LPR : 1;
   constexpr int GL_RSTEP = C::THREADS / GL_LPR;   // rows per load
   const uint32_t g_loff = (tid / GL_LPR) * srow + (tid % GL_LPR) * 16;
-  const int g_lds = (tid % GL_LPR) * 2 * C::GTILE + (tid / GL_LPR) * 8;
+  const int g_lds = (tid % GL_LPR) * 2 * C::GTILE + ((tid / GL_LPR) ^ (8 * (tid % GL_LPR))) * 8;
+  static_assert(C::SG <= 1 || (GL_RSTEP % 32 == 0 && TM % 32 == 0 && 8 * (GL_LPR - 1) < 32),
+                "scale row permutation stays inside 32-row blocks");
   auto load_g1 = [&](auto j_c, int g) GP_INLINE -> v4i {
     constexpr int j = decltype(j_c)::value;
     constexpr bool is_a = j < C::GLA;
@@ -539,10 +548,13 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     if constexpr (DT == DT_FP4) {
       const char* sb = C::SG > 1 ? lds + C::ST * C::ABUF + ((kt / C::SG) & 1) * C::GSLOT + (kt % C::SG) * C::GTILE
                                  : lds + C::ST * C::ABUF + par * C::SAREA;
+      // row r of a grouped tile sits at r ^ xp (bits 3-4 only: the same
+      // 32-row block)
+      const int xp = C::SG > 1 ? 8 * ((kt % C::SG) / 2) : 0;
 #pragma unroll
-      for (int mi = 0; mi < C::MREP; ++mi) psa[mi] = read_s(sb, mi * MS + lrow);
+      for (int mi = 0; mi < C::MREP; ++mi) psa[mi] = read_s(sb, (mi * MS + lrow) ^ xp);
 #pragma unroll
-      for (int ni = 0; ni < C::NACC; ++ni) psb[ni] = read_s(sb, TM + wave * C::NPW + ni * MS + lrow);
+      for (int ni = 0; ni < C::NACC; ++ni) psb[ni] = read_s(sb, (TM + wave * C::NPW + ni * MS + lrow) ^ xp);
     }
     constexpr int NF = C::KSTEPS * C::MREP;
     constexpr int RA = C::RA < NF ? C::RA : NF;

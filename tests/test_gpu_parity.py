@@ -73,6 +73,10 @@ TILE_CASES = [
     ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32)),
     ("mxfp4", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=32, epilogue=1)),
     ("mxfp4", 256, 256, 768, dict(kernel=1, tile_m=128, tile_n=128, tile_k=256, mfma=32)),
+    # grouped FP4 scales with 16 x 16 blocks: odd row blocks inside the permuted 32-row scale blocks
+    ("mxfp4", 128, 256, 2560, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=16)),
+    ("mxfp4", 96, 512, 4096, dict(kernel=1, tile_m=32, tile_n=256, tile_k=256, mfma=16)),
+    ("mxfp4", 128, 256, 2048, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, mfma=16, epilogue=2)),
     # 256 x 256 FP4 tiles (one workgroup per CU, accumulators in AGPRs), 2-stage DMA and VGPR-staged A
     ("mxfp4", 256, 512, 2304, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
     ("mxfp4", 512, 256, 1024, dict(kernel=1, tile_m=256, tile_n=256, tile_k=256, mfma=32, pipeline=1)),
