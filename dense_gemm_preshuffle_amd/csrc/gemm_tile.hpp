@@ -73,7 +73,13 @@ __device__ __forceinline__ void edge_shift(uint32_t& x0, uint32_t& skip, uint32_
 // Resident workgroups per CU of the tile kernel: one once the accumulators
 // alone take more than half of the 256 registers two workgroups would leave
 // each wave, or with two K groups; two otherwise.
-constexpr int tile_wgs_per_cu(int tm, int tn, int kg) { return (kg > 1 || tm * tn / 256 > 128) ? 1 : 2; }
+constexpr int tile_wgs_per_cu(int tm, int tn, int kg) { return (kg > 1 || tn >= 512 || tm * tn / 256 > 128) ? 1 : 2; }
+
+// Waves of one K group: 4, each owning TN / 4 columns; 8 for TN = 512, so
+// that each wave keeps the 64 columns (and accumulator registers) of the
+// 4-wave 256-column tile while one A tile in LDS serves twice the columns:
+// a quarter fewer operand bytes from L2 per FLOP than two 128 x 256 tiles.
+constexpr int tile_waves(int tn) { return tn >= 512 ? 8 : 4; }
 
 // PIPE: 0 = A staged through VGPRs, two LDS buffers (prefetch one tile
 // ahead); 2 .. 6 = A copied global -> LDS by the buffer-load LDS DMA, with
@@ -88,8 +94,8 @@ constexpr int tile_wgs_per_cu(int tm, int tn, int kg) { return (kg > 1 || tm * t
 template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED = false, int KG = 1>
 struct TileCfg {
   using S = Mma<DT, MS>;
-  static constexpr int THREADS = 256;
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = tile_waves(TN);
+  static constexpr int THREADS = 64 * WAVES;
   // W4A8 (DT_I4): TKB counts bytes of B; A holds two bytes (int8) per B byte
   // (two INT4), and one 16-byte B piece feeds two int8 MFMAs.
   static constexpr int AKB = (DT == DT_I4) ? 2 : 1;        // A bytes per B byte of K
@@ -187,7 +193,7 @@ struct TileCfg {
   // FP4 scales, the fragment ring) stays within 236 of the 256 VGPRs. FP8
   // stops at 1: one FP8 fragment feeds NACC 32-cycle MFMAs, which covers an
   // LDS read on its own.
-  static constexpr int ACCR = TM * TN / 256;
+  static constexpr int ACCR = TM * TN / THREADS;
   static constexpr int BREG = ST * KSTEPS * NACC * FRAG * 4 + (DT == DT_I4 ? NACC * 8 : 0);  // + widened INT4
   static constexpr int SREG = NSC ? MREP + NACC + 2 * ST * (SLA + SLB) + 4 * GPP : 0;
   static constexpr int RBASE = (ACCR > 128 ? 0 : ACCR) + BREG + SREG;
@@ -201,6 +207,7 @@ struct TileCfg {
   static_assert(PIPE == 0 || (PIPE >= 2 && PIPE <= 6), "pipeline");
   static_assert(KG == 1 || (KG == 2 && !NSC), "K groups: not with FP4's staged scales");
   static_assert(DT != DT_I4 || MS == 16, "W4A8: 16 x 16 blocks");
+  static_assert(WAVES == 4 || (KG == 1 && !NSC), "8-wave tiles: one K group, no FP4 scale staging");
 };
 
 // Tile (tm, tn) and K split z of this workgroup. With a K split the ksplit
@@ -246,15 +253,15 @@ __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uin
 // others assume p.ksplit == 1 and carry no code for the cross-workgroup sum.
 template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED, int KG, bool SCH = true,
           bool KS = false>
-__global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_tile_kernel(TileArgs p) {
+__global__ __launch_bounds__(64 * tile_waves(TN) * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_tile_kernel(TileArgs p) {
   using C = TileCfg<DT, MS, TM, TN, TKB, EPI, PIPE, FUSED, KG>;
   using Acc = typename Mma<DT, MS>::Acc;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
 
   // K group of this wave and the thread index inside its group; everything
   // below indexes by the group-local thread and wave
-  const int grp = KG > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 8) : 0;
-  const int tid = threadIdx.x & 255;
+  const int grp = KG > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x / C::THREADS) : 0;
+  const int tid = KG > 1 ? threadIdx.x % C::THREADS : threadIdx.x;
   char* const glds = lds + grp * C::GSTAGE;   // the group's A stages
   // wave index: uniform across the wave; readfirstlane puts it in a scalar
   // register so that offsets derived from it stay scalar
@@ -744,8 +751,8 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
     using V4 = std::conditional_t<DT == DT_I8 || DT == DT_I4, v4i, v4f>;
     const uint32_t tile = tm * p.tiles_n + tn;
     // the tile's partial sums: [z][chunk][thread] 16-byte entries
-    const __amdgpu_buffer_rsrc_t rp =
-        make_rsrc(p.part + (size_t)tile * p.ksplit * NCH * 4096u, p.ksplit * (uint32_t)NCH * 4096u);
+    constexpr uint32_t PB = NCH * C::THREADS * 16u;   // bytes of one partial tile (TM * TN * 4)
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(p.part + (size_t)tile * p.ksplit * PB, p.ksplit * PB);
     if (grp == 0) {
 #pragma unroll
       for (int mi = 0; mi < C::MREP; ++mi)
@@ -757,7 +764,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * h + r];
             const uint32_t ch = (mi * C::NACC + ni) * (C::NREG / 4) + h;
-            buf_store16_coh(__builtin_bit_cast(v4i, v), rp, ((kz * NCH + ch) * 256u + tid) * 16u);
+            buf_store16_coh(__builtin_bit_cast(v4i, v), rp, ((kz * NCH + ch) * C::THREADS + tid) * 16u);
           }
     }
     wait_vm(std::integral_constant<int, 0>{});   // this thread's partial sums are stored
@@ -798,7 +805,7 @@ __global__ __launch_bounds__(256 * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_ti
           } else {
 #pragma unroll
             for (int b = 0; b < RB; ++b)
-              dst[b] = __builtin_bit_cast(V4, buf_load16_coh(rp, ((z * NCH + c0 + b) * 256u + tid) * 16u));
+              dst[b] = __builtin_bit_cast(V4, buf_load16_coh(rp, ((z * NCH + c0 + b) * C::THREADS + tid) * 16u));
           }
         };
         fetch(0, t);

@@ -4,7 +4,7 @@
 // Tile kernel: X(dtype, mfma, tile_m, tile_n, tile_k_bytes, pipe): mfma = 16 or
 // 32 (the MFMA block); pipe 0 = A staged through VGPRs (2 stages), 2 / 3 = A
 // by LDS DMA with 2 / 3 stages. Each is built with the direct and the
-// CShuffle epilogue.
+// CShuffle epilogue. tile_n = 512 runs on 8 waves (64 columns each).
 // Small-M (split-K) kernel: Y(dtype, n_blocks_of_16, waves,
 // chunk_bytes_per_wave, m_blocks_of_16); W4A8 chunk bytes count bytes of B.
 // Wide kernel (256x256 tiles, 8 waves): W(dtype, mfma, tile_k_bytes, pipe),
@@ -26,7 +26,8 @@
   X(DT_FP8, 16, 32, 128, 128, 3) X(DT_FP8, 16, 32, 128, 256, 3) X(DT_FP8, 16, 32, 256, 256, 3)  \
   X(DT_FP8, 16, 32, 256, 128, 4) X(DT_FP8, 16, 32, 256, 128, 6)   \
   X(DT_FP8, 16, 32, 128, 256, 4) X(DT_FP8, 16, 32, 128, 256, 6) X(DT_FP8, 16, 64, 256, 128, 4)   \
-  X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 128, 128, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)
+  X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 128, 128, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)   \
+  X(DT_FP8, 16, 128, 512, 128, 3)
 
 #define GP_TILE_BF16(X)                                                                            \
   X(DT_BF16, 16, 32, 128, 128, 0) X(DT_BF16, 16, 64, 128, 128, 0) X(DT_BF16, 16, 128, 256, 128, 0) X(DT_BF16, 16, 128, 256, 64, 0)          \
@@ -34,13 +35,15 @@
   X(DT_BF16, 32, 128, 256, 128, 0) X(DT_BF16, 32, 128, 256, 64, 0)                                \
   X(DT_BF16, 32, 128, 256, 128, 2) X(DT_BF16, 32, 128, 256, 128, 3) X(DT_BF16, 16, 128, 256, 128, 3) \
   X(DT_BF16, 32, 256, 256, 128, 3) X(DT_BF16, 32, 256, 256, 128, 2) \
-  X(DT_BF16, 32, 256, 256, 64, 3) X(DT_BF16, 16, 256, 256, 64, 3) X(DT_BF16, 16, 256, 256, 64, 4)
+  X(DT_BF16, 32, 256, 256, 64, 3) X(DT_BF16, 16, 256, 256, 64, 3) X(DT_BF16, 16, 256, 256, 64, 4) \
+  X(DT_BF16, 16, 128, 512, 128, 3) X(DT_BF16, 32, 128, 512, 128, 3) X(DT_BF16, 16, 128, 512, 128, 2)
 
 #define GP_TILE_F16(X)                                                                             \
   X(DT_F16, 16, 32, 128, 128, 0) X(DT_F16, 16, 64, 128, 128, 0) X(DT_F16, 16, 64, 256, 128, 0)             \
   X(DT_F16, 16, 128, 128, 128, 0) X(DT_F16, 16, 128, 256, 128, 0) X(DT_F16, 16, 128, 256, 128, 3)          \
   X(DT_F16, 32, 128, 256, 128, 3) X(DT_F16, 32, 64, 128, 128, 0)                                  \
-  X(DT_F16, 16, 128, 256, 64, 0) X(DT_F16, 16, 64, 128, 64, 0)
+  X(DT_F16, 16, 128, 256, 64, 0) X(DT_F16, 16, 64, 128, 64, 0) X(DT_F16, 16, 128, 512, 128, 3)           \
+  X(DT_F16, 32, 128, 512, 128, 3)
 
 #define GP_TILE_FP4(X)                                                                             \
   X(DT_FP4, 16, 32, 256, 128, 0) X(DT_FP4, 16, 64, 128, 128, 0) X(DT_FP4, 16, 64, 256, 128, 0)              \
@@ -102,8 +105,8 @@
 #define GP_TILE_NOSCHED_I8(X) X(DT_I8, 16, 16, 64, 256, 0) X(DT_I8, 16, 64, 128, 256, 3)
 #define GP_TILE_NOSCHED_FP8(X) X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 64, 256, 128, 3) \
   X(DT_FP8, 16, 128, 256, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)
-#define GP_TILE_NOSCHED_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3)
-#define GP_TILE_NOSCHED_F16(X) X(DT_F16, 16, 128, 256, 128, 3)
+#define GP_TILE_NOSCHED_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3) X(DT_BF16, 16, 128, 512, 128, 3)
+#define GP_TILE_NOSCHED_F16(X) X(DT_F16, 16, 128, 256, 128, 3) X(DT_F16, 16, 128, 512, 128, 3)
 #define GP_TILE_NOSCHED_FP4(X) X(DT_FP4, 32, 128, 256, 128, 2)
 #define GP_TILE_NOSCHED_I4(X) X(DT_I4, 16, 64, 128, 128, 3)
 #define GP_TILE_NOSCHED_ALL(X) GP_TILE_NOSCHED_I8(X) GP_TILE_NOSCHED_FP8(X) GP_TILE_NOSCHED_BF16(X) \

@@ -73,6 +73,14 @@ TILE_CASES = [
     ("mxfp4", 128, 512, 768, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32)),
     ("mxfp4", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=32, epilogue=1)),
     ("mxfp4", 256, 256, 768, dict(kernel=1, tile_m=128, tile_n=128, tile_k=256, mfma=32)),
+    # 128 x 512 tiles on 8 waves (each wave 128 x 64, one A tile for all eight)
+    ("bf16", 256, 1024, 448, dict(kernel=1, tile_m=128, tile_n=512, tile_k=64, mfma=16, pipeline=3)),
+    ("bf16", 128, 512, 320, dict(kernel=1, tile_m=128, tile_n=512, tile_k=64, mfma=32, pipeline=3)),
+    ("bf16", 200, 608, 384, dict(kernel=1, tile_m=128, tile_n=512, tile_k=64, mfma=16, pipeline=2)),
+    ("bf16", 128, 1024, 256, dict(kernel=1, tile_m=128, tile_n=512, tile_k=64, mfma=16, pipeline=3, epilogue=1)),
+    ("fp16", 256, 512, 576, dict(kernel=1, tile_m=128, tile_n=512, tile_k=64, mfma=16, pipeline=3)),
+    ("fp16", 144, 528, 320, dict(kernel=1, tile_m=128, tile_n=512, tile_k=64, mfma=32, pipeline=3)),
+    ("fp8", 256, 1024, 640, dict(kernel=1, tile_m=128, tile_n=512, tile_k=128, pipeline=3)),
     # grouped FP4 scales with 16 x 16 blocks: odd row blocks inside the permuted 32-row scale blocks
     ("mxfp4", 128, 256, 2560, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=16)),
     ("mxfp4", 96, 512, 4096, dict(kernel=1, tile_m=32, tile_n=256, tile_k=256, mfma=16)),
