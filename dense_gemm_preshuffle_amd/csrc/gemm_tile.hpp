@@ -207,7 +207,7 @@ struct TileCfg {
   static_assert(PIPE == 0 || (PIPE >= 2 && PIPE <= 6), "pipeline");
   static_assert(KG == 1 || (KG == 2 && !NSC), "K groups: not with FP4's staged scales");
   static_assert(DT != DT_I4 || MS == 16, "W4A8: 16 x 16 blocks");
-  static_assert(WAVES == 4 || (KG == 1 && !NSC), "8-wave tiles: one K group, no FP4 scale staging");
+  static_assert(WAVES == 4 || KG == 1, "8-wave tiles: one K group");
 };
 
 // Tile (tm, tn) and K split z of this workgroup. With a K split the ksplit

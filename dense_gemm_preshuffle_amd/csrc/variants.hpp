@@ -50,7 +50,8 @@
   X(DT_FP4, 32, 64, 128, 128, 0) X(DT_FP4, 32, 64, 256, 128, 0)                                    \
   X(DT_FP4, 32, 128, 128, 128, 0) X(DT_FP4, 32, 128, 256, 128, 0) X(DT_FP4, 32, 128, 256, 128, 2) \
   X(DT_FP4, 16, 128, 256, 64, 2) X(DT_FP4, 16, 64, 128, 64, 0)                                  \
-  X(DT_FP4, 32, 256, 256, 128, 2) X(DT_FP4, 32, 256, 256, 128, 0)
+  X(DT_FP4, 32, 256, 256, 128, 2) X(DT_FP4, 32, 256, 256, 128, 0) X(DT_FP4, 32, 128, 512, 128, 2)          \
+  X(DT_FP4, 32, 128, 512, 128, 0)
 // (No FP4 128 x 256 tile with 16 x 16 blocks, nor with a 3-stage pipeline:
 // the first put its accumulators in scratch memory, the second spilled.)
 // (No 256 x 256 tile for FP4 or FP8, nor for BF16 with 16 x 16 blocks and
@@ -107,7 +108,7 @@
   X(DT_FP8, 16, 128, 256, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)
 #define GP_TILE_NOSCHED_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3) X(DT_BF16, 16, 128, 512, 128, 3)
 #define GP_TILE_NOSCHED_F16(X) X(DT_F16, 16, 128, 256, 128, 3) X(DT_F16, 16, 128, 512, 128, 3)
-#define GP_TILE_NOSCHED_FP4(X) X(DT_FP4, 32, 128, 256, 128, 2)
+#define GP_TILE_NOSCHED_FP4(X) X(DT_FP4, 32, 128, 256, 128, 2) X(DT_FP4, 32, 128, 512, 128, 2)
 #define GP_TILE_NOSCHED_I4(X) X(DT_I4, 16, 64, 128, 128, 3)
 #define GP_TILE_NOSCHED_ALL(X) GP_TILE_NOSCHED_I8(X) GP_TILE_NOSCHED_FP8(X) GP_TILE_NOSCHED_BF16(X) \
   GP_TILE_NOSCHED_F16(X) GP_TILE_NOSCHED_FP4(X) GP_TILE_NOSCHED_I4(X)

@@ -273,12 +273,17 @@ def test_fp4_plan_lds_matches_scale_groups():
     """MXFP4 with a 2-stage pipeline stages scales as a ring of two slots of
     8-tile groups (8 x (TM+TN) x 8 bytes each) beside the A stages: for the
     128 x 256 tile exactly the 80 KiB share of each of two workgroups per CU."""
-    p = gp.gemm_plan("mxfp4", 4096, 4096, 8192)
+    p = gp.gemm_plan("mxfp4", 4096, 4096, 8192, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256))
     assert p["pipeline"] == 2 and p["tile_k"] == 256 and (p["tile_m"], p["tile_n"]) == (128, 256)
     stages = 2 * p["tile_m"] * 128 + 2 * (8 * (p["tile_m"] + p["tile_n"]) * 8)
     assert stages == 80 * 1024
     cshuffle = p["tile_m"] * (p["tile_n"] * 2 + 16) if p["epilogue"] == gp.EPI_CSHUFFLE else 0
     assert p["lds_bytes"] == max(stages, cshuffle)
+    # the default 128 x 512 tile runs 8 waves, one workgroup per CU (160 KiB share)
+    q = gp.gemm_plan("mxfp4", 4096, 4096, 8192)
+    assert (q["tile_m"], q["tile_n"], q["waves"], q["threads"]) == (128, 512, 8, 512)
+    stages = 2 * 128 * 128 + 2 * (8 * (128 + 512) * 8)
+    assert q["lds_bytes"] == max(stages, 128 * (512 * 2 + 16)) <= 160 * 1024
 
 
 def test_k_group_plan():

@@ -81,6 +81,9 @@ TILE_CASES = [
     ("fp16", 256, 512, 576, dict(kernel=1, tile_m=128, tile_n=512, tile_k=64, mfma=16, pipeline=3)),
     ("fp16", 144, 528, 320, dict(kernel=1, tile_m=128, tile_n=512, tile_k=64, mfma=32, pipeline=3)),
     ("fp8", 256, 1024, 640, dict(kernel=1, tile_m=128, tile_n=512, tile_k=128, pipeline=3)),
+    ("mxfp4", 128, 1024, 4608, dict(kernel=1, tile_m=128, tile_n=512, tile_k=256, mfma=32, pipeline=2)),
+    ("mxfp4", 256, 512, 2048, dict(kernel=1, tile_m=128, tile_n=512, tile_k=256, mfma=32, pipeline=1)),
+    ("mxfp4", 160, 560, 1280, dict(kernel=1, tile_m=128, tile_n=512, tile_k=256, mfma=32, pipeline=2, epilogue=1)),
     # grouped FP4 scales with 16 x 16 blocks: odd row blocks inside the permuted 32-row scale blocks
     ("mxfp4", 128, 256, 2560, dict(kernel=1, tile_m=64, tile_n=256, tile_k=256, mfma=16)),
     ("mxfp4", 96, 512, 4096, dict(kernel=1, tile_m=32, tile_n=256, tile_k=256, mfma=16)),
