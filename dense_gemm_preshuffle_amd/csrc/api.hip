@@ -2,6 +2,7 @@
 // planner, the B preshuffle kernel and the exported C entry points.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -252,8 +253,13 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
     cand[nc++] = {4, 1};
     cand[nc++] = {1, 1};
   }
-  // column blocks per workgroup: the caller's, else 2 (two blocks fill whole
-  // 128-byte lines of a bf16 C row), else 1
+  // column blocks per workgroup: the caller's, else the count (1 or 2) that
+  // leaves the busiest CU the fewest bytes over its ceil(grid / 256) rounds of
+  // workgroups, counting B's bytes and half of A's (read from L2; they cost
+  // about half as much per byte on the M=16 shape), ties to 2. FP8 M=16,
+  // K=2048: N=2048 3.26 us on one block (128 workgroups) against 3.81 on
+  // two, N=4096 3.64 against 3.99 (256 against 128 workgroups), N=5120 4.19
+  // on two (160) against 4.97 on one (320), N=7168 4.44 on two (224).
   int nbc[2] = {2, 1};
   int nn = 2;
   if (o && o->tile_n > 0) { nbc[0] = o->tile_n / 16; nn = 1; }
@@ -261,6 +267,16 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
     const int waves = cand[i].waves, mb = cand[i].mb;
     if (Kb % waves) continue;
     const int64_t kw = Kb / waves;
+    if (nn == 2 && N % 32 == 0) {
+      const int64_t rows = std::min<int64_t>(M, 16 * mb), Ka = Kb * (dt == DT_I4 ? 2 : 1);
+      auto cost = [&](int nb) {
+        const int64_t grid = (N / (16 * nb)) * ((M + 16 * mb - 1) / (16 * mb));
+        return (double)((grid + 255) / 256) * ((double)(16 * nb) * Kb + 0.5 * (double)rows * Ka);
+      };
+      const bool one = cost(1) < cost(2);
+      nbc[0] = one ? 1 : 2;
+      nbc[1] = one ? 2 : 1;
+    }
     for (int c = 0; c < nn; ++c) {
       const int nb = nbc[c];
       if (N % (16 * nb)) continue;
