@@ -423,6 +423,75 @@ def floor_probe(name, steps, warmup, grids=((224, 4), (256, 4), (256, 8), (512, 
                       f"{ROTATE_BYTES >> 20} MiB and more), HIP graph of the launches, HIP events"}
 
 
+# (form, instruction, dtype of its dense peak, M x N x K of one instruction)
+MFMA_FORMS = [(0, "bf16 16x16x32", "bf16", 16, 16, 32), (1, "f16 16x16x32", "fp16", 16, 16, 32),
+              (2, "i8 16x16x64", "int8", 16, 16, 64), (3, "fp8 16x16x128", "fp8", 16, 16, 128),
+              (4, "fp4 16x16x128 (scaled)", "mxfp4", 16, 16, 128), (5, "bf16 32x32x16", "bf16", 32, 32, 16),
+              (6, "f16 32x32x16", "fp16", 32, 32, 16), (7, "i8 32x32x32", "int8", 32, 32, 32),
+              (8, "fp8 32x32x64", "fp8", 32, 32, 64), (9, "fp4 32x32x64 (scaled)", "mxfp4", 32, 32, 64)]
+
+
+def mfma_rate(iters=4000, grids=(256, 512)):
+    """What each MFMA form of the kernels sustains on its own
+    (dense_gemm_preshuffle_amd/probe/mfma_rate.hip): 8 independent
+    accumulators per wave, operands in registers, `iters` rounds of 8 MFMAs;
+    256 workgroups of 4 waves (one wave per SIMD) or 512 (two). Cycles per
+    MFMA per wave from the shader clock counter around the loop; FLOP/s from
+    HIP events around the launch (launch included)."""
+    import ctypes
+    import statistics
+
+    import torch
+
+    from dense_gemm_preshuffle_amd import build as _b
+
+    if not os.path.exists(_b.PROBE_LIB):
+        raise SystemExit(f"{_b.PROBE_LIB} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    f = lib.gp_probe_mfma_rate
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    rows = []
+    for wgs in grids:
+        out = torch.zeros(wgs * 256, device="cuda")
+        cyc = torch.zeros(wgs * 8, dtype=torch.int64, device="cuda")
+        for form, name, dt, m, n, k in MFMA_FORMS:
+            flop = 2 * m * n * k
+            peak = PEAK_TFLOPS[dt] * 1e12
+            nominal = flop / (peak / (1024 * 2.4e9))   # issue cycles at the dense peak
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            for timed in (False, True):
+                if timed:
+                    e0.record(stream)
+                st = f(form, out.data_ptr(), cyc.data_ptr(), iters, wgs, ctypes.c_void_p(stream.cuda_stream))
+                if st != 0:
+                    raise RuntimeError(f"gp_probe_mfma_rate: status {st}")
+                if timed:
+                    e1.record(stream)
+                torch.cuda.synchronize()
+            c = cyc.view(-1, 2).cpu()
+            cycles = statistics.median(c[:, 0].tolist())
+            ticks = statistics.median(c[:, 1].tolist())
+            per = cycles / (iters * 8)
+            total = wgs * 4 * iters * 8 * flop
+            tf = total / (e0.elapsed_time(e1) * 1e-3) / 1e12
+            row = {"workgroups": wgs, "waves_per_simd": wgs // 256, "form": name,
+                   "cycles_per_mfma_per_wave": round(per, 2), "nominal_issue_cycles": round(nominal, 1),
+                   # one wave per SIMD: the share of the loop's cycles the MFMA pipe is issuing; with
+                   # more workgroups than CUs they need not all overlap, so only the FLOP rate is kept
+                   "issue_fraction": round(nominal / per, 3) if wgs == 256 else None,
+                   "clock_ghz": round(cycles / (ticks / 100e6) / 1e9, 3),
+                   "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_TFLOPS[dt], 3)}
+            rows.append(row)
+            log(f"[mfma] {wgs} wgs {name}: {per:.2f} cycles per MFMA per wave (issue {nominal:.0f}), "
+                f"{tf:.0f} TFLOP/s = {tf / PEAK_TFLOPS[dt]:.3f} of peak")
+        del out, cyc
+    return {"iters": iters, "rows": rows,
+            "method": "8 independent accumulators per wave, operands in registers, shader-clock cycles around "
+                      "the loop, HIP events around the launch"}
+
+
 def _gpu_sysfs():
     """sysfs device directory of the GPU when the host has exactly one, else None."""
     cards = [d for d in sorted(glob.glob("/sys/class/drm/card*/device")) if os.path.exists(os.path.join(d, "pp_dpm_sclk"))]
@@ -529,6 +598,9 @@ def main():
     ap.add_argument("--floor", action="store_true",
                     help="instead of the GEMM: time the HBM streaming-read probe over the workload's "
                          "algorithmic bytes (the floor of the memory-bound shapes), one JSON line")
+    ap.add_argument("--mfma-rate", action="store_true",
+                    help="instead of the GEMM: time each MFMA form the kernels use on its own (registers only), "
+                         "one JSON line")
     ap.add_argument("--data", default="randn", choices=["randn", "zeros"],
                     help="zeros: same launches on all-zero A and B (diagnostic of data-dependent clocks)")
     ap.add_argument("--act", default=None, choices=["none", "relu", "silu", "gelu"],
@@ -546,6 +618,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.mfma_rate:
+        print(json.dumps({"mfma_rate": mfma_rate()}), flush=True)
+        return
     if args.floor:
         print(json.dumps({"floor": floor_probe(args.workload, args.steps, args.warmup)}), flush=True)
         return

@@ -20,7 +20,12 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm_preshuffle.so")
 # the HBM streaming-read probe that bench.py --floor times (not the GEMM library)
-PROBE_SRC = os.path.join(PKG, "probe", "stream_read.hip")
+PROBE_SRCS = [os.path.join(PKG, "probe", f) for f in ("stream_read.hip", "mfma_rate.hip")]
+# The probes keep MFMA accumulators in VGPRs: with AGPR accumulators the
+# compiler rotates a loop's eight 4-register accumulators through AGPR copies
+# every iteration (24 accvgpr reads and writes per 8 MFMAs), which the rate
+# probe would then measure instead of the MFMA.
+PROBE_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 PROBE_LIB = os.path.join(PKG, "libgp_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -95,7 +100,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     tmp = PROBE_LIB + ".tmp"
-    r = subprocess.run([HIPCC, *FLAGS, "-shared", "-o", tmp, PROBE_SRC], capture_output=True, text=True)
+    r = subprocess.run([HIPCC, *FLAGS, *PROBE_FLAGS, "-shared", "-o", tmp, *PROBE_SRCS], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"probe build failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, PROBE_LIB)

@@ -68,3 +68,24 @@ def test_floor_probe_library_validates_arguments():
     assert f(buf, 1 << 20, 0, 4, sink, None) == 1                          # no workgroups
     assert f(buf, 1 << 20, 256, 17, sink, None) == 1                       # too many waves
     assert f(buf, (1 << 20) + 16, 256, 4, sink, None) == 1                 # not whole lanes of the grid
+
+
+def test_mfma_rate_probe_validates_arguments():
+    """The MFMA issue-rate probe (bench.py --mfma-rate) shares the probe
+    library and refuses bad arguments before any GPU call."""
+    import ctypes
+
+    from dense_gemm_preshuffle_amd import build as b
+
+    lib = ctypes.CDLL(b.PROBE_LIB)
+    f = lib.gp_probe_mfma_rate
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    out, cyc = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    assert f(-1, out, cyc, 100, 256, None) == 1        # no such form
+    assert f(10, out, cyc, 100, 256, None) == 1
+    assert f(0, None, cyc, 100, 256, None) == 1        # null output
+    assert f(0, out, None, 100, 256, None) == 1        # null cycle buffer
+    assert f(0, out, cyc, 0, 256, None) == 1           # no iterations
+    assert f(0, out, cyc, 100, 0, None) == 1           # no workgroups
+    assert f(0, out, cyc, 100, 4097, None) == 1
