@@ -161,11 +161,17 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
   // 512 x 4096 x 4096.
   static const Cand fp8[] = {{128, 256, 128}, {64, 256, 128}, {64, 128, 256}, {32, 256, 256}, {32, 256, 128},
                              {128, 128, 128}, {64, 128, 128}, {16, 64, 512}};
-  // BF16 / FP16: 128 x 512 on 8 waves (one A tile for twice the columns)
-  // where it still gives at least 1024 tiles: 8192^3 771.7 us against 783.0
-  // for 128 x 256 (BF16), 809 against 818 (FP16), one process each
-  static const Cand b16[] = {{128, 512, 128, 1024}, {128, 256, 128}, {64, 256, 128}, {128, 128, 128},
-                             {64, 128, 128}, {128, 256, 64}, {32, 128, 128}, {64, 128, 64}};
+  // BF16 / FP16: 256 x 256 on 8 waves (each wave 32 columns of all 256
+  // rows, so a B byte a wave loads feeds 256 rows) where it gives at least
+  // 256 tiles: BF16 8192^3 727-734 us against 757 for 128 x 512 on 8 waves,
+  // 4096^3 100-101 against 109, 4096 x 8192 x 8192 371 against 390-392,
+  // 16384 x 4096 x 4096 385-386 against 402-403, 8192 x 8192 x 2048 213-214
+  // against 215-218; FP16 8192^3 766-767 against 786-788 (one process
+  // each). Then 128 x 512 on 8 waves where it still gives at least 1024
+  // tiles (8192^3 771.7 us against 783.0 for 128 x 256, before the 256 x
+  // 256 form).
+  static const Cand b16[] = {{256, 256, 128, 256}, {128, 512, 128, 1024}, {128, 256, 128}, {64, 256, 128},
+                             {128, 128, 128}, {64, 128, 128}, {128, 256, 64}, {32, 128, 128}, {64, 128, 64}};
   // MXFP4: 128 x 512 on 8 waves where it gives a tile per CU: 4096 x 4096 x
   // 8192 69.7-70.0 us against 71.6-72.5 for 128 x 256 (one process; equal
   // with warm caches: the gain is in the bytes fetched)
@@ -502,10 +508,10 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     out->tile_n = p.tn;
     out->tile_k = (int)((int64_t)p.tkb * 8 / bits);
     out->epilogue = p.epi;
-    out->waves = tile_waves(p.tn) * p.kg;
+    out->waves = tile_waves(p.tm, p.tn) * p.kg;
     out->threads = 64 * out->waves;
     const int tka = p.tkb * (dt == DT_I4 ? 2 : 1);   // A bytes per row of a K tile
-    const bool apart = (p.tm * (tka / 16)) % (64 * tile_waves(p.tn)) != 0;
+    const bool apart = (p.tm * (tka / 16)) % (64 * tile_waves(p.tm, p.tn)) != 0;
     const int stages = p.pipe ? p.pipe : 2;
     int abuf = p.kg * stages * (p.tm * tka + (apart ? 16 : 0));
     if (dt == DT_FP4) {   // staged E8M0 scales: per stage, or a ring of two slots of SG-tile groups
@@ -514,7 +520,7 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
         // lanes past the rows): SG = 8 where the whole LDS still fits the share
         // of a resident workgroup, else 4
         auto slot = [&](int sg) {
-          const int th = 64 * tile_waves(p.tn);
+          const int th = 64 * tile_waves(p.tm, p.tn);
           return sg * (p.tm + p.tn) * 8 + (((p.tm * sg / 2) % th || (p.tn * sg / 2) % th) ? 16 : 0);
         };
         const int cb = p.epi == EPI_CSHUFFLE ? p.tm * (p.tn * ob + 16) : 0;
@@ -533,7 +539,7 @@ void fill_info(int in_dtype, int64_t M, int64_t N, int64_t K, const Plan& p, gem
     out->lds_bytes += bias_lds * p.tn * 4;
     out->grid = ((M + p.tm - 1) / p.tm) * ((N + p.tn - 1) / p.tn);
     out->k_tiles = p.Kb / p.tkb;
-    out->mfma_per_wave_tile = (int64_t)(p.tkb / kbm) * (p.tm / ms) * (p.tn / tile_waves(p.tn) / ms);
+    out->mfma_per_wave_tile = (int64_t)(p.tkb / kbm) * (p.tm / ms) * (p.tn / tile_waves(p.tm, p.tn) / ms);
   } else {
     out->tile_m = 16 * p.mb;
     out->tile_n = 16 * p.nb;

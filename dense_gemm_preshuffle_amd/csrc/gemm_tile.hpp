@@ -79,7 +79,11 @@ constexpr int tile_wgs_per_cu(int tm, int tn, int kg) { return (kg > 1 || tn >= 
 // that each wave keeps the 64 columns (and accumulator registers) of the
 // 4-wave 256-column tile while one A tile in LDS serves twice the columns:
 // a quarter fewer operand bytes from L2 per FLOP than two 128 x 256 tiles.
-constexpr int tile_waves(int tn) { return tn >= 512 ? 8 : 4; }
+// 8 also for 256 x 256 tiles: each wave owns 32 columns of all 256 rows
+// (the same 128 accumulator registers per lane), so every B byte a wave
+// loads feeds 256 rows (half the B bytes per FLOP of the 128 x 512 tile)
+// while every wave reads the whole A tile from LDS.
+constexpr int tile_waves(int tm, int tn) { return (tn >= 512 || (tm >= 256 && tn >= 256)) ? 8 : 4; }
 
 // PIPE: 0 = A staged through VGPRs, two LDS buffers (prefetch one tile
 // ahead); 2 .. 6 = A copied global -> LDS by the buffer-load LDS DMA, with
@@ -94,7 +98,7 @@ constexpr int tile_waves(int tn) { return tn >= 512 ? 8 : 4; }
 template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED = false, int KG = 1>
 struct TileCfg {
   using S = Mma<DT, MS>;
-  static constexpr int WAVES = tile_waves(TN);
+  static constexpr int WAVES = tile_waves(TM, TN);
   static constexpr int THREADS = 64 * WAVES;
   // W4A8 (DT_I4): TKB counts bytes of B; A holds two bytes (int8) per B byte
   // (two INT4), and one 16-byte B piece feeds two int8 MFMAs.
@@ -253,7 +257,7 @@ __device__ __forceinline__ void tile_coords(const TileArgs& p, uint32_t& tm, uin
 // others assume p.ksplit == 1 and carry no code for the cross-workgroup sum.
 template <int DT, int MS, int TM, int TN, int TKB, int EPI, int PIPE, bool FUSED, int KG, bool SCH = true,
           bool KS = false>
-__global__ __launch_bounds__(64 * tile_waves(TN) * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_tile_kernel(TileArgs p) {
+__global__ __launch_bounds__(64 * tile_waves(TM, TN) * KG, tile_wgs_per_cu(TM, TN, KG)) void gemm_tile_kernel(TileArgs p) {
   using C = TileCfg<DT, MS, TM, TN, TKB, EPI, PIPE, FUSED, KG>;
   using Acc = typename Mma<DT, MS>::Acc;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];

@@ -41,9 +41,9 @@ hipError_t launch_splitk_i4(int nb, int waves, int kch, int mb, const SplitArgs&
       (a.ksplit > 1) == KSV) {                                                                     \
     const dim3 grid(a.tiles_m * a.tiles_n * a.ksplit);                                             \
     if (epi == EPI_CSHUFFLE)                                                                       \
-      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_CSHUFFLE, PIPE, FU, KGV, SCHV, KSV>), grid, dim3(64 * tile_waves(TN) * KGV), 0, s, a); \
+      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_CSHUFFLE, PIPE, FU, KGV, SCHV, KSV>), grid, dim3(64 * tile_waves(TM, TN) * KGV), 0, s, a); \
     else                                                                                           \
-      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_DIRECT, PIPE, FU, KGV, SCHV, KSV>), grid, dim3(64 * tile_waves(TN) * KGV), 0, s, a);   \
+      hipLaunchKernelGGL((gemm_tile_kernel<DT, MS, TM, TN, TKB, EPI_DIRECT, PIPE, FU, KGV, SCHV, KSV>), grid, dim3(64 * tile_waves(TM, TN) * KGV), 0, s, a);   \
     return hipGetLastError();                                                                      \
   }
 #define GP_TILE_CASE(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 1, true, false)

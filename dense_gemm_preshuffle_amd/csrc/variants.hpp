@@ -36,14 +36,15 @@
   X(DT_BF16, 32, 128, 256, 128, 2) X(DT_BF16, 32, 128, 256, 128, 3) X(DT_BF16, 16, 128, 256, 128, 3) \
   X(DT_BF16, 32, 256, 256, 128, 3) X(DT_BF16, 32, 256, 256, 128, 2) \
   X(DT_BF16, 32, 256, 256, 64, 3) X(DT_BF16, 16, 256, 256, 64, 3) X(DT_BF16, 16, 256, 256, 64, 4) \
-  X(DT_BF16, 16, 128, 512, 128, 3) X(DT_BF16, 32, 128, 512, 128, 3) X(DT_BF16, 16, 128, 512, 128, 2)
+  X(DT_BF16, 16, 128, 512, 128, 3) X(DT_BF16, 32, 128, 512, 128, 3) X(DT_BF16, 16, 128, 512, 128, 2) \
+  X(DT_BF16, 16, 256, 256, 128, 3) X(DT_BF16, 16, 256, 256, 128, 2) X(DT_BF16, 16, 256, 256, 128, 4)
 
 #define GP_TILE_F16(X)                                                                             \
   X(DT_F16, 16, 32, 128, 128, 0) X(DT_F16, 16, 64, 128, 128, 0) X(DT_F16, 16, 64, 256, 128, 0)             \
   X(DT_F16, 16, 128, 128, 128, 0) X(DT_F16, 16, 128, 256, 128, 0) X(DT_F16, 16, 128, 256, 128, 3)          \
   X(DT_F16, 32, 128, 256, 128, 3) X(DT_F16, 32, 64, 128, 128, 0)                                  \
   X(DT_F16, 16, 128, 256, 64, 0) X(DT_F16, 16, 64, 128, 64, 0) X(DT_F16, 16, 128, 512, 128, 3)           \
-  X(DT_F16, 32, 128, 512, 128, 3)
+  X(DT_F16, 32, 128, 512, 128, 3) X(DT_F16, 16, 256, 256, 128, 3) X(DT_F16, 16, 256, 256, 128, 4)
 
 #define GP_TILE_FP4(X)                                                                             \
   X(DT_FP4, 16, 32, 256, 128, 0) X(DT_FP4, 16, 64, 128, 128, 0) X(DT_FP4, 16, 64, 256, 128, 0)              \
@@ -106,8 +107,10 @@
 #define GP_TILE_NOSCHED_I8(X) X(DT_I8, 16, 16, 64, 256, 0) X(DT_I8, 16, 64, 128, 256, 3)
 #define GP_TILE_NOSCHED_FP8(X) X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 64, 256, 128, 3) \
   X(DT_FP8, 16, 128, 256, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)
-#define GP_TILE_NOSCHED_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3) X(DT_BF16, 16, 128, 512, 128, 3)
-#define GP_TILE_NOSCHED_F16(X) X(DT_F16, 16, 128, 256, 128, 3) X(DT_F16, 16, 128, 512, 128, 3)
+#define GP_TILE_NOSCHED_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3) X(DT_BF16, 16, 128, 512, 128, 3) \
+  X(DT_BF16, 16, 256, 256, 128, 3)
+#define GP_TILE_NOSCHED_F16(X) X(DT_F16, 16, 128, 256, 128, 3) X(DT_F16, 16, 128, 512, 128, 3) \
+  X(DT_F16, 16, 256, 256, 128, 3)
 #define GP_TILE_NOSCHED_FP4(X) X(DT_FP4, 32, 128, 256, 128, 2) X(DT_FP4, 32, 128, 512, 128, 2)
 #define GP_TILE_NOSCHED_I4(X) X(DT_I4, 16, 64, 128, 128, 3)
 #define GP_TILE_NOSCHED_ALL(X) GP_TILE_NOSCHED_I8(X) GP_TILE_NOSCHED_FP8(X) GP_TILE_NOSCHED_BF16(X) \

@@ -125,6 +125,10 @@ SCHED_OFF_CASES = [
     ("fp8", 256, 256, 768, dict(kernel=1, tile_m=128, tile_n=128, tile_k=256, pipeline=3)),
     ("bf16", 256, 512, 448, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, pipeline=3)),
     ("fp16", 256, 512, 448, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, pipeline=3)),
+    ("bf16", 512, 512, 640, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=3)),
+    ("fp16", 512, 512, 384, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=3)),
+    ("bf16", 256, 1024, 448, dict(kernel=1, tile_m=128, tile_n=512, tile_k=64, mfma=16, pipeline=3)),
+    ("fp16", 256, 1024, 320, dict(kernel=1, tile_m=128, tile_n=512, tile_k=64, mfma=16, pipeline=3)),
     ("mxfp4", 256, 512, 2816, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, mfma=32, pipeline=2)),
     ("w4a8", 128, 256, 1280, dict(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3)),
 ]

@@ -138,6 +138,12 @@ TILE_CASES = [
     ("bf16", 512, 256, 320, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
     ("bf16", 256, 256, 64, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=32, pipeline=2, epilogue=1)),
     ("bf16", 256, 512, 160, dict(kernel=1, tile_m=256, tile_n=256, tile_k=32, mfma=32, pipeline=3)),
+    # 256 x 256 tiles on 8 waves (each wave 32 columns of all 256 rows): 16 x 16 blocks with 128-byte K tiles
+    ("bf16", 512, 512, 640, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=3)),
+    ("bf16", 300, 272, 384, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=2)),
+    ("bf16", 256, 256, 64, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=3, epilogue=1)),
+    ("fp16", 512, 256, 448, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=3)),
+    ("fp16", 260, 288, 128, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=3, epilogue=1)),
     # wide kernel: 256x256 tiles, 8 waves, A and B through LDS; K-tile counts 1 .. 7
     ("bf16", 256, 256, 64, dict(kernel=3)),
     ("bf16", 512, 256, 320, dict(kernel=3)),
