@@ -452,3 +452,19 @@ def test_split_tile_count_limit():
     with pytest.raises(gp.GemmError) as e:
         gp.gemm_plan_ws("fp8", 64 * 129, 128 * 128, 4096, ok)                         # 16512 tiles
     assert e.value.status == GP_ESHAPE
+
+
+def test_planner_takes_large_edge_tiles_on_ragged_shapes():
+    """A tile whose overlapping edge tiles add at most 1/8 to the computed
+    area counts like one that divides M and N: BF16 8000 x 8192 x 8192 gets
+    the 256 x 256 tile of the 8192^3 shape (2.4% of its rows computed twice),
+    not the largest tile dividing 8000 (64 x 256); a tile that would compute
+    far more than M x N still loses to a smaller one."""
+    assert (gp.gemm_plan("bf16", 8192, 8192, 8192)["tile_m"], gp.gemm_plan("bf16", 8192, 8192, 8192)["tile_n"]) == (256, 256)
+    for M, N, K in [(8000, 8192, 8192), (4000, 4096, 4096), (8192, 8000, 4096)]:
+        p = gp.gemm_plan("bf16", M, N, K)
+        assert (p["tile_m"], p["tile_n"], p["waves"]) == (256, 256, 8), (M, N, p)
+    p = gp.gemm_plan("bf16", 300, 8192, 4096)      # 256-row tiles would compute 512 rows for 300
+    assert p["tile_m"] <= 64 and p["grid"] >= 256
+    p = gp.gemm_plan("mxfp4", 4000, 4096, 8192)
+    assert (p["tile_m"], p["tile_n"]) == (128, 512)
