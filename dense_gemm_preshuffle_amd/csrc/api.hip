@@ -317,9 +317,50 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
 // tiles) and 20.8 us split in four (64 x 128 tiles); BF16 512 x 2048 x 16384
 // 141.8 and 56.5 us (128 x 256 tiles, eight ranges); MXFP4 256 x 4096 x
 // 16384 43.8 and 23.7 us (128 x 128 tiles, four ranges).
+// Long K on a full grid of small tiles: where a split tile pulls fewer
+// operand bytes per FLOP than the planner's tile (1/TM + 1/TN smaller), its
+// first S (power of two) that gives 256 to 512 workgroups while each range
+// keeps at least 4096 bytes of B's K: BF16 512 x 8192 x 8192 70 us on
+// 128 x 256 tiles split in two against 88 on 64 x 256 tiles, 256 x 8192 x
+// 8192 53 us split in four against 59 on 64 x 128, 384 x 8192 x 8192 80
+// against 90; FP16 512 x 8192 x 8192 71 against 87-89. BF16 / FP16 only:
+// the same rule measured slower for FP8 (512 x 8192 x 8192 49 us on 128 x
+// 128 tiles split in two against 46; 256 x 8192 x 8192 34 against 29) and
+// INT8 (512 x 8192 x 8192 50.5 against 48.8), whose partial sums cost as
+// much per tile for half the bytes of K.
+bool ksplit_larger_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
+  if (dt != DT_BF16 && dt != DT_F16) return false;
+  const double bpf = 1.0 / p->tm + 1.0 / p->tn;
+  for (int i = 0; i < (int)(sizeof(kKSplit) / sizeof(kKSplit[0])); ++i) {
+    const TileVar& v = kKSplit[i];
+    if (v.dt != dt || v.tm > M || v.tn > N || Kb % v.tkb) continue;
+    if (1.0 / v.tm + 1.0 / v.tn >= bpf) continue;
+    const int64_t T = ((M + v.tm - 1) / v.tm) * ((N + v.tn - 1) / v.tn);
+    const int64_t cover = ((M + v.tm - 1) / v.tm) * v.tm * (((N + v.tn - 1) / v.tn) * v.tn);
+    if (cover * 8 > M * N * 9) continue;   // edge tiles computing more than 1/8 extra
+    const int64_t KT = Kb / v.tkb;
+    for (int S = 2; S <= 16; S *= 2) {
+      if (KT % S || Kb / S < 4096) break;
+      if (T * S < 256) continue;
+      if (T * S > 512) break;
+      p->tm = v.tm;
+      p->tn = v.tn;
+      p->tkb = v.tkb;
+      p->ms = v.ms;
+      p->pipe = v.pipe;
+      p->ks = S;
+      return true;
+    }
+  }
+  return false;
+}
+
 void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
   const int64_t grid0 = ((M + p->tm - 1) / p->tm) * ((N + p->tn - 1) / p->tn);
-  if (grid0 >= 256 && p->tm * p->tn >= 64 * 128) return;
+  if (grid0 >= 256 && p->tm * p->tn >= 64 * 128) {
+    ksplit_larger_tile(dt, M, N, Kb, p);
+    return;
+  }
   int best = -1, best_s = 0;
   for (int i = 0; i < (int)(sizeof(kKSplit) / sizeof(kKSplit[0])); ++i) {
     const TileVar& v = kKSplit[i];
@@ -449,6 +490,13 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   }
   // K groups: 8 waves asked for (two groups of 4 splitting the K tiles)
   if (o && o->waves && o->waves != 4) {
+    // the caller left the pipeline to the planner: the one whose two-group form is compiled
+    if (!o->pipeline && !tile_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe, 2))
+      for (const auto& v : kTiles)
+        if (v.kg == 2 && v.dt == dt && v.ms == p->ms && v.tm == p->tm && v.tn == p->tn && v.tkb == p->tkb) {
+          p->pipe = v.pipe;
+          break;
+        }
     if (o->waves != 8 || (Kb / p->tkb) % 2 || !tile_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe, 2))
       return GP_ESHAPE;
     p->kg = 2;
@@ -457,6 +505,10 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   // whole K-group halves with two K groups)
   if (o && o->ksplit > 1) {
     if ((Kb / p->tkb) % ((int64_t)o->ksplit * p->kg)) return GP_ESHAPE;
+    // the caller left the pipeline to the planner: the one whose split form is compiled
+    if (!o->pipeline && !ksplit_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe))
+      for (const auto& v : kKSplit)
+        if (v.dt == dt && v.ms == p->ms && v.tm == p->tm && v.tn == p->tn && v.tkb == p->tkb) { p->pipe = v.pipe; break; }
     if (p->kg != 1 || !ksplit_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe)) return GP_ESHAPE;
     if (tiles_of(*p, M, N) > kMaxSplitTiles) return GP_ESHAPE;
     p->ks = o->ksplit;
@@ -466,6 +518,9 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   // Hot-loop schedule: pinned unless asked otherwise (measured per default
   // tile, one process each: the pinned order was as fast or faster)
   if (o && o->scheduler == 2) {
+    if (!o->pipeline && !nosched_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe))
+      for (const auto& v : kNoSched)
+        if (v.dt == dt && v.ms == p->ms && v.tm == p->tm && v.tn == p->tn && v.tkb == p->tkb) { p->pipe = v.pipe; break; }
     if (p->kg != 1 || p->ks != 1 || !nosched_compiled(dt, p->ms, p->tm, p->tn, p->tkb, p->pipe)) return GP_ESHAPE;
     p->sched = 2;
   }

@@ -468,3 +468,18 @@ def test_planner_takes_large_edge_tiles_on_ragged_shapes():
     assert p["tile_m"] <= 64 and p["grid"] >= 256
     p = gp.gemm_plan("mxfp4", 4000, 4096, 8192)
     assert (p["tile_m"], p["tile_n"]) == (128, 512)
+
+
+def test_planner_splits_long_k_onto_larger_bf16_tiles():
+    """With a workspace, BF16 / FP16 GEMMs whose grid of small tiles is full
+    but whose K is long split K over a tile with fewer operand bytes per
+    FLOP (each range keeping >= 4096 bytes of K); FP8 / INT8 do not."""
+    p = gp.gemm_plan_ws("bf16", 512, 8192, 8192)
+    assert (p["tile_m"], p["tile_n"], p["ksplit"], p["grid"]) == (128, 256, 2, 256)
+    p = gp.gemm_plan_ws("bf16", 256, 8192, 8192)
+    assert (p["tile_m"], p["tile_n"], p["ksplit"], p["grid"]) == (128, 256, 4, 256)
+    assert gp.gemm_plan_ws("fp16", 512, 8192, 8192)["ksplit"] == 2
+    for dt in ("fp8", "int8"):
+        assert gp.gemm_plan_ws(dt, 512, 8192, 8192)["ksplit"] == 1
+    assert gp.gemm_plan_ws("bf16", 512, 4096, 4096)["ksplit"] == 1     # 2048-byte ranges: no split
+    assert gp.gemm_plan("bf16", 512, 8192, 8192)["ksplit"] == 1        # no workspace, no split
