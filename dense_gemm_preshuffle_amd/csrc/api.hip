@@ -149,18 +149,25 @@ int pick_ms(int dt, int tm, int tn, int tkb, int want) {
 // Default tile preference (largest first) per input type, tile_k in bytes.
 // Named shapes: FP8 medium 64x256x128 (GEMM Optimization Guide §1.3), BF16
 // large 128x256x64 elements, FP4 64-128 x 256 x 256 elements.
+// Workgroups that count as a full grid for the planner's first choice:
+// three quarters of the 256 CUs. With a stricter 256, 7168 columns (224
+// tiles of 128 columns) sent FP8 256 x 7168 x 2048 to 16 x 64 tiles (1792
+// workgroups, 19.1 us) instead of 64 x 128 ones (224 workgroups, 9.7 us).
+constexpr int64_t kFullGrid = 192;
+
 int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) {
   struct Cand { int tm, tn, tkb, min_grid = 0; };
   // (the 64-byte K tiles at the ends of the lists serve K not a multiple of
   // the larger ones: one 64-byte K block is the layout's granularity)
   static const Cand i8[] = {{128, 256, 128}, {64, 256, 128}, {64, 128, 256}, {64, 128, 128}, {128, 128, 128},
                             {64, 64, 128}, {32, 64, 128}, {16, 64, 256}, {128, 256, 64}, {64, 128, 64}};
-  // FP8: 64 x 128 x 256 before 32 x 256 x 256: where both give one tile per
-  // CU (e.g. 512 x 4096), it pulls a third fewer bytes from L2 per FLOP
-  // ((64 + 128) vs (32 + 256) bytes per K byte); measured 15.4 vs 20.0 us on
-  // 512 x 4096 x 4096.
-  static const Cand fp8[] = {{128, 256, 128}, {64, 256, 128}, {64, 128, 256}, {32, 256, 256}, {32, 256, 128},
-                             {128, 128, 128}, {64, 128, 128}, {16, 64, 512}};
+  // FP8: in the order of operand bytes per FLOP (1/TM + 1/TN): 128 x 128
+  // before 64 x 256 (1024 x 4096 x 7168 36.5 us against 39.8, 512 x 7168 x
+  // 2048 13.8 against 14.6 on 64 x 128), 64 x 128 x 256 before 32 x 256 x
+  // 256 (512 x 4096 x 4096 15.4 against 20.0 us), 32 x 128 before 16 x 64
+  // (128 x 7168 x 2048 8.0 against 13.1).
+  static const Cand fp8[] = {{128, 256, 128}, {128, 128, 256}, {128, 128, 128}, {64, 256, 128}, {64, 128, 256},
+                             {32, 256, 256}, {32, 256, 128}, {64, 128, 128}, {32, 128, 256}, {16, 64, 512}};
   // BF16 / FP16: 256 x 256 on 8 waves (each wave 32 columns of all 256
   // rows, so a B byte a wave loads feeds 256 rows) where it gives at least
   // 256 tiles: BF16 8192^3 727-734 us against 757 for 128 x 512 on 8 waves,
@@ -210,7 +217,7 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
       if (!pick_ms(dt, c.tm, c.tn, c.tkb, want_ms)) continue;
       const int64_t g = ((M + c.tm - 1) / c.tm) * ((N + c.tn - 1) / c.tn);
       if (g < c.min_grid) continue;
-      if (g >= 256) { best = i; break; }
+      if (g >= kFullGrid) { best = i; break; }
       if (g > best_grid) { best_grid = g; best = i; }
     }
     if (best >= 0) {
@@ -328,7 +335,8 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
 // 128 tiles split in two against 46; 256 x 8192 x 8192 34 against 29) and
 // INT8 (512 x 8192 x 8192 50.5 against 48.8), whose partial sums cost as
 // much per tile for half the bytes of K.
-bool ksplit_larger_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
+// num / den: the most area the split tile's grid may cover, relative to M x N
+bool ksplit_larger_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int num = 9, int den = 8) {
   if (dt != DT_BF16 && dt != DT_F16) return false;
   const double bpf = 1.0 / p->tm + 1.0 / p->tn;
   for (int i = 0; i < (int)(sizeof(kKSplit) / sizeof(kKSplit[0])); ++i) {
@@ -337,7 +345,7 @@ bool ksplit_larger_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
     if (1.0 / v.tm + 1.0 / v.tn >= bpf) continue;
     const int64_t T = ((M + v.tm - 1) / v.tm) * ((N + v.tn - 1) / v.tn);
     const int64_t cover = ((M + v.tm - 1) / v.tm) * v.tm * (((N + v.tn - 1) / v.tn) * v.tn);
-    if (cover * 8 > M * N * 9) continue;   // edge tiles computing more than 1/8 extra
+    if (cover * den > M * N * num) continue;   // edge tiles computing too much extra
     const int64_t KT = Kb / v.tkb;
     for (int S = 2; S <= 16; S *= 2) {
       if (KT % S || Kb / S < 4096) break;
@@ -359,6 +367,15 @@ void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
   const int64_t grid0 = ((M + p->tm - 1) / p->tm) * ((N + p->tn - 1) / p->tn);
   if (grid0 >= 256 && p->tm * p->tn >= 64 * 128) {
     ksplit_larger_tile(dt, M, N, Kb, p);
+    return;
+  }
+  // 192 .. 255 workgroups: only the BF16 / FP16 split onto a larger tile,
+  // whose edge tiles may then cover up to a third more (BF16 192 x 8192 x
+  // 8192: 52 us on 128 x 256 tiles split in four against 58 on 64 x 128;
+  // FP8 256 x 7168 x 8192 measured 27.9 us unsplit against 32.5 with its
+  // 64 x 128 tiles split in two)
+  if (grid0 >= kFullGrid && p->tm * p->tn >= 64 * 128) {
+    ksplit_larger_tile(dt, M, N, Kb, p, 4, 3);
     return;
   }
   int best = -1, best_s = 0;

@@ -483,3 +483,19 @@ def test_planner_splits_long_k_onto_larger_bf16_tiles():
         assert gp.gemm_plan_ws(dt, 512, 8192, 8192)["ksplit"] == 1
     assert gp.gemm_plan_ws("bf16", 512, 4096, 4096)["ksplit"] == 1     # 2048-byte ranges: no split
     assert gp.gemm_plan("bf16", 512, 8192, 8192)["ksplit"] == 1        # no workspace, no split
+
+
+def test_planner_full_grid_and_fp8_order():
+    """Three quarters of the CUs count as a full grid (7168 columns make 224
+    tiles of 128 columns), and FP8 tiles are tried in the order of their
+    operand bytes per FLOP."""
+    def tile(dt, M, N, K):
+        p = gp.gemm_plan_ws(dt, M, N, K)
+        return p["tile_m"], p["tile_n"], p["grid"], p["ksplit"]
+    assert tile("fp8", 256, 7168, 2048) == (64, 128, 224, 1)      # not 1792 tiles of 16 x 64
+    assert tile("fp8", 128, 7168, 2048) == (32, 128, 224, 1)
+    assert tile("fp8", 1024, 4096, 7168)[:2] == (128, 128)         # before 64 x 256
+    assert tile("fp8", 512, 4096, 4096) == (64, 128, 256, 1)       # the benchmark shape: unchanged
+    assert tile("fp8", 16, 7168, 2048)[:3] == (16, 32, 224)
+    assert tile("bf16", 192, 8192, 8192) == (128, 256, 256, 4)     # 192 .. 255 tiles: BF16 larger-tile split
+    assert tile("fp8", 256, 7168, 8192) == (64, 128, 224, 1)       # ... and no split for FP8
