@@ -321,14 +321,22 @@ __global__ __launch_bounds__(64 * tile_waves(TM, TN) * KG, tile_wgs_per_cu(TM, T
   // global chunk that belongs at LDS chunk p = (i*WAVES + w)*64 + l: row p/CPR,
   // physical chunk p%CPR, i.e. logical chunk (p%CPR) ^ swizzle(row). The rows
   // of instruction i are those of instruction 0 plus i*RPD, RPD = 256/CPR.
+  // Where RPD rows are a whole number of swizzle periods, one source offset
+  // serves every instruction (plus i * RPD rows); otherwise (512-byte A rows:
+  // 8 rows per instruction, a 16-row swizzle period) each instruction has its own.
   constexpr int RPD = C::THREADS / C::CPR;
-  uint32_t a_dma0 = 0;
+  constexpr bool DMA_STEP = (RPD / C::SWP) % (C::SWM + 1) == 0;
+  uint32_t a_dma[DMA_STEP ? 1 : C::ALOADS];
   if constexpr (C::ASYNC) {
     const int pch = wave * 64 + lane;
     const int row = pch / C::CPR;
-    a_dma0 = row * Ka + (((pch % C::CPR) ^ ((row / C::SWP) & C::SWM)) * 16);
+#pragma unroll
+    for (int i = 0; i < (DMA_STEP ? 1 : C::ALOADS); ++i) {
+      const int r = row + i * RPD;
+      a_dma[i] = r * Ka + (((pch % C::CPR) ^ ((r / C::SWP) & C::SWM)) * 16);
+    }
   }
-  static_assert(!C::ASYNC || ((RPD / C::SWP) % (C::SWM + 1)) == 0, "DMA swizzle step");
+  static_assert(!C::ASYNC || RPD * C::ALOADS == TM, "LDS DMA covers the A tile");
   // A K byte (within one MFMA step) of the lane's 16-byte piece f. W4A8: the
   // B piece of lane group g holds K elements [32g, 32g+32) of the step's 128,
   // its low nibbles the first 16 (first MFMA), its high nibbles the rest.
@@ -421,7 +429,7 @@ __global__ __launch_bounds__(64 * tile_waves(TM, TN) * KG, tile_wgs_per_cu(TM, T
   auto load_a_dma = [&](int stage, int kt, int i) GP_INLINE {
     if constexpr (C::ASYNC)
       lds_dma16(p.a + (size_t)m0 * Ka, TM * Ka, glds + stage * C::ABUF + (i * C::WAVES + wave) * 1024,
-                a_dma0 + kt * C::TKA + i * RPD * Ka);
+                (DMA_STEP ? a_dma[0] + i * RPD * Ka : a_dma[DMA_STEP ? 0 : i]) + kt * C::TKA);
   };
   // B load q of a tile: K step q / (NACC*FRAG), column block (q / FRAG) % NACC, piece q % FRAG
   auto load_b = [&](auto par_c, int kt, int q) GP_INLINE {

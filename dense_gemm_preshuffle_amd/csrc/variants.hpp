@@ -27,7 +27,7 @@
   X(DT_FP8, 16, 32, 256, 128, 4) X(DT_FP8, 16, 32, 256, 128, 6)   \
   X(DT_FP8, 16, 32, 128, 256, 4) X(DT_FP8, 16, 32, 128, 256, 6) X(DT_FP8, 16, 64, 256, 128, 4)   \
   X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 128, 128, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)   \
-  X(DT_FP8, 16, 128, 512, 128, 3)
+  X(DT_FP8, 16, 128, 512, 128, 3) X(DT_FP8, 16, 64, 128, 512, 3) X(DT_FP8, 16, 64, 128, 512, 2)
 
 #define GP_TILE_BF16(X)                                                                            \
   X(DT_BF16, 16, 32, 128, 128, 0) X(DT_BF16, 16, 64, 128, 128, 0) X(DT_BF16, 16, 128, 256, 128, 0) X(DT_BF16, 16, 128, 256, 64, 0)          \

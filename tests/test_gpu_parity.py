@@ -138,6 +138,10 @@ TILE_CASES = [
     ("bf16", 512, 256, 320, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=32, pipeline=3)),
     ("bf16", 256, 256, 64, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=32, pipeline=2, epilogue=1)),
     ("bf16", 256, 512, 160, dict(kernel=1, tile_m=256, tile_n=256, tile_k=32, mfma=32, pipeline=3)),
+    # 512-byte K tiles (A rows of 512 bytes: each LDS-DMA instruction has its own source offsets)
+    ("fp8", 256, 512, 2048, dict(kernel=1, tile_m=64, tile_n=128, tile_k=512, pipeline=3)),
+    ("fp8", 200, 384, 1536, dict(kernel=1, tile_m=64, tile_n=128, tile_k=512, pipeline=2)),
+    ("fp8", 64, 128, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=512, pipeline=3, epilogue=1)),
     # 256 x 256 tiles on 8 waves (each wave 32 columns of all 256 rows): 16 x 16 blocks with 128-byte K tiles
     ("bf16", 512, 512, 640, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=3)),
     ("bf16", 300, 272, 384, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=2)),
