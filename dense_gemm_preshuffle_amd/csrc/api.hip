@@ -205,6 +205,37 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
   // fits. (Preferring exact tiles outright sent BF16 8000 x 8192 x 8192 to
   // 64 x 256 tiles, 1616 us, against 728 us on 256 x 256 tiles, 2.4% of
   // whose rows are computed twice.)
+  // FP8: the tile whose busiest CU streams the fewest operand bytes,
+  // ceil(grid / 256) * (TM + TN) per byte of K, among those whose edge tiles
+  // add at most a quarter to the computed area (ties to the earlier one).
+  // On one MI355X this ranked the FP8 tiles of 16 shapes from 80 x 7168 x
+  // 2048 to 1536 x 8192 x 4096 in their measured order to within 5%, e.g.
+  // 96 x 7168 x 2048 7.9 us on 168 tiles of 32 x 128 against 10.3 on 672 of
+  // 16 x 64 (the first tile giving 192 workgroups). The other types keep
+  // the rule below: some of their tiles exist only with A staged through
+  // registers, which this count does not see.
+  if (dt == DT_FP8) {
+    int best = -1;
+    int64_t best_cost = 0;
+    for (int i = 0; i < n; ++i) {
+      const Cand& c = list[i];
+      if (c.tm > M || c.tn > N || Kb % c.tkb) continue;
+      if (!pick_ms(dt, c.tm, c.tn, c.tkb, want_ms)) continue;
+      const int64_t gm = (M + c.tm - 1) / c.tm, gn = (N + c.tn - 1) / c.tn;
+      if (gm * c.tm * gn * c.tn * 4 > M * N * 5) continue;
+      const int64_t g = gm * gn;
+      if (g < c.min_grid) continue;
+      const int64_t cost = ((g + 255) / 256) * (c.tm + c.tn);
+      if (best < 0 || cost < best_cost) { best = i; best_cost = cost; }
+    }
+    if (best >= 0) {
+      p->tm = list[best].tm;
+      p->tn = list[best].tn;
+      p->tkb = list[best].tkb;
+      p->ms = pick_ms(dt, p->tm, p->tn, p->tkb, want_ms);
+      return GP_OK;
+    }
+  }
   for (int pass = 0; pass < 2; ++pass) {
     int best = -1;
     int64_t best_grid = -1;

@@ -499,3 +499,7 @@ def test_planner_full_grid_and_fp8_order():
     assert tile("fp8", 16, 7168, 2048)[:3] == (16, 32, 224)
     assert tile("bf16", 192, 8192, 8192) == (128, 256, 256, 4)     # 192 .. 255 tiles: BF16 larger-tile split
     assert tile("fp8", 256, 7168, 8192) == (64, 128, 224, 1)       # ... and no split for FP8
+    # FP8: fewest operand bytes for the busiest CU, edge tiles up to a quarter more area
+    for M in (80, 96, 112):
+        assert tile("fp8", M, 7168, 2048)[:2] == (32, 128), M
+    assert tile("fp8", 1536, 8192, 4096)[:2] == (128, 256)
