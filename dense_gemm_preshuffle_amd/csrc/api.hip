@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -205,27 +206,49 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
   // fits. (Preferring exact tiles outright sent BF16 8000 x 8192 x 8192 to
   // 64 x 256 tiles, 1616 us, against 728 us on 256 x 256 tiles, 2.4% of
   // whose rows are computed twice.)
-  // FP8: the tile whose busiest CU streams the fewest operand bytes,
-  // ceil(grid / 256) * (TM + TN) per byte of K, among those whose edge tiles
-  // add at most a quarter to the computed area (ties to the earlier one).
-  // On one MI355X this ranked the FP8 tiles of 16 shapes from 80 x 7168 x
-  // 2048 to 1536 x 8192 x 4096 in their measured order to within 5%, e.g.
-  // 96 x 7168 x 2048 7.9 us on 168 tiles of 32 x 128 against 10.3 on 672 of
-  // 16 x 64 (the first tile giving 192 workgroups). The other types keep
-  // the rule below: some of their tiles exist only with A staged through
-  // registers, which this count does not see.
-  if (dt == DT_FP8) {
+  // First choice (all types but MXFP4): the tile whose busiest CU streams
+  // the fewest operand bytes per byte of K, ceil(grid / 256) * (TM + TN),
+  // among tiles whose edge tiles add at most a quarter to the computed area
+  // (ties to the earlier one), with three corrections measured on one
+  // MI355X: divided by 1.2 where a CU holds 8 waves or more (two resident
+  // workgroups, or an 8-wave tile: more loads in flight; with 1.35 two
+  // 128 x 128 tiles per CU won over one 128 x 256 on 1024 x 7168 x 2048 and
+  // measured 3-7% slower); times (256 / grid)^0.3 where
+  // CUs stay idle; times 1.4 for tiles whose A is staged through registers
+  // (BF16 64 x 128: 83 us against 59 with LDS DMA on 256 x 8192 x 8192).
+  // This ranks the tiles of the FP8 / BF16 / FP16 / INT8 shapes timed for it
+  // (80 x 7168 x 2048 to 8192^3) in their measured order, e.g. FP8 96 x
+  // 7168 x 2048 7.9 us on 168 tiles of 32 x 128 against 10.3 on 672 of
+  // 16 x 64 (the threshold rule's choice), BF16 768 x 4096 x 4096 40.6 on
+  // 128 x 128 against 45.7 on 64 x 256, BF16 300 x 8192 x 4096 45.4 on 320
+  // tiles of 64 x 128 against 53.7 on 160 of 64 x 256 (split later). MXFP4
+  // keeps the threshold rule (its 128 x 128 tile measured 18.7 us against
+  // 17.0 for 64 x 256 on 512 x 7168 x 4096, which the count gets wrong).
+  if (dt != DT_FP4) {
     int best = -1;
-    int64_t best_cost = 0;
+    double best_cost = 0;
     for (int i = 0; i < n; ++i) {
       const Cand& c = list[i];
       if (c.tm > M || c.tn > N || Kb % c.tkb) continue;
-      if (!pick_ms(dt, c.tm, c.tn, c.tkb, want_ms)) continue;
+      const int ms = pick_ms(dt, c.tm, c.tn, c.tkb, want_ms);
+      if (!ms) continue;
+      bool dma = false;
+      for (int pipe = 2; pipe <= 6; ++pipe) dma = dma || tile_compiled(dt, ms, c.tm, c.tn, c.tkb, pipe);
       const int64_t gm = (M + c.tm - 1) / c.tm, gn = (N + c.tn - 1) / c.tn;
       if (gm * c.tm * gn * c.tn * 4 > M * N * 5) continue;
       const int64_t g = gm * gn;
       if (g < c.min_grid) continue;
-      const int64_t cost = ((g + 255) / 256) * (c.tm + c.tn);
+      const int64_t rounds = (g + 255) / 256;
+      // resident workgroups per CU: by registers, and by LDS (the A stages or
+      // the CShuffle tile, whichever is larger)
+      const int pipe = pick_pipe(dt, ms, c.tm, c.tn, c.tkb, 0);
+      const int tka = c.tkb * (dt == DT_I4 ? 2 : 1);
+      const int64_t lds = std::max<int64_t>((int64_t)(pipe > 2 ? pipe : 2) * c.tm * tka,
+                                            c.tn >= 128 ? (int64_t)c.tm * (c.tn * (dt == DT_I8 ? 4 : 2) + 16) : 0);
+      const int64_t wpc = std::max<int64_t>(1, std::min<int64_t>(tile_wgs_per_cu(c.tm, c.tn, 1), 160 * 1024 / lds));
+      const int64_t waves = std::min<int64_t>(rounds, wpc) * tile_waves(c.tm, c.tn);
+      double cost = (double)rounds * (c.tm + c.tn) * (dma ? 1.0 : 1.4) / (waves >= 8 ? 1.2 : 1.0);
+      if (g < 256) cost *= std::pow(256.0 / (double)g, 0.3);
       if (best < 0 || cost < best_cost) { best = i; best_cost = cost; }
     }
     if (best >= 0) {
@@ -368,7 +391,12 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
 // much per tile for half the bytes of K.
 // num / den: the most area the split tile's grid may cover, relative to M x N
 bool ksplit_larger_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int num = 9, int den = 8) {
+  // From 128-row tiles only while the split keeps one workgroup per CU: BF16
+  // 512 x 8192 x 8192 69 us on 128 x 256 tiles split in two against 78 on
+  // 128 x 128, but 2048 x 4096 x 4096 71 us split in two (512 workgroups)
+  // against 59 unsplit on 128 x 256.
   if (dt != DT_BF16 && dt != DT_F16) return false;
+  const int64_t max_wg = p->tm < 128 ? 512 : 256;
   const double bpf = 1.0 / p->tm + 1.0 / p->tn;
   for (int i = 0; i < (int)(sizeof(kKSplit) / sizeof(kKSplit[0])); ++i) {
     const TileVar& v = kKSplit[i];
@@ -381,7 +409,7 @@ bool ksplit_larger_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int n
     for (int S = 2; S <= 16; S *= 2) {
       if (KT % S || Kb / S < 4096) break;
       if (T * S < 256) continue;
-      if (T * S > 512) break;
+      if (T * S > max_wg) break;
       p->tm = v.tm;
       p->tn = v.tn;
       p->tkb = v.tkb;

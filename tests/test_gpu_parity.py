@@ -142,6 +142,14 @@ TILE_CASES = [
     ("fp8", 256, 512, 2048, dict(kernel=1, tile_m=64, tile_n=128, tile_k=512, pipeline=3)),
     ("fp8", 200, 384, 1536, dict(kernel=1, tile_m=64, tile_n=128, tile_k=512, pipeline=2)),
     ("fp8", 64, 128, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=512, pipeline=3, epilogue=1)),
+    # 128 x 128 tiles with A by LDS DMA (128-byte K tiles); ragged M / N tails
+    ("bf16", 256, 384, 576, dict(kernel=1, tile_m=128, tile_n=128, tile_k=64, mfma=16, pipeline=3)),
+    ("bf16", 200, 144, 128, dict(kernel=1, tile_m=128, tile_n=128, tile_k=64, mfma=16, pipeline=3, epilogue=1)),
+    ("fp16", 128, 256, 320, dict(kernel=1, tile_m=128, tile_n=128, tile_k=64, mfma=16, pipeline=3)),
+    ("int8", 256, 256, 640, dict(kernel=1, tile_m=128, tile_n=128, tile_k=128, pipeline=3)),
+    ("int8", 96, 208, 384, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128, pipeline=3, epilogue=2)),
+    ("mxfp4", 256, 256, 1280, dict(kernel=1, tile_m=128, tile_n=128, tile_k=256, mfma=32, pipeline=2)),
+    ("mxfp4", 160, 144, 512, dict(kernel=1, tile_m=128, tile_n=128, tile_k=256, mfma=32, pipeline=2, epilogue=1)),
     # 256 x 256 tiles on 8 waves (each wave 32 columns of all 256 rows): 16 x 16 blocks with 128-byte K tiles
     ("bf16", 512, 512, 640, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=3)),
     ("bf16", 300, 272, 384, dict(kernel=1, tile_m=256, tile_n=256, tile_k=64, mfma=16, pipeline=2)),
