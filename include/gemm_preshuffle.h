@@ -275,7 +275,8 @@ int gemm_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* op
  * the planner split K across workgroups on the tile kernel where the tiles
  * alone would leave CUs idle (GEMM Optimization Guide §13, Tiling: "tile_m x
  * tile_n fills GPU (enough blocks)"; §1.3's tile table read with the 256 CUs
- * of MI355X).
+ * of MI355X), and, for BF16 / FP16 with long K, where the split lets a larger
+ * tile (fewer operand bytes per FLOP) fill the GPU instead of a smaller one.
  *   workspace        device, 16-byte aligned, at least gemm_workspace_size
  *                    bytes for the same arguments (ignored, and may be NULL,
  *                    when that size is 0). Its first 64 KiB hold one arrival
