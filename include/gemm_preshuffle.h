@@ -119,7 +119,8 @@ typedef struct gemm_opts {
   int pipeline;     /* tile kernel: 1 A staged through VGPRs (2 stages), 2 .. 6 A
                        by LDS DMA with that many stages (where compiled), 0 auto */
   int ksplit;       /* tile kernel: K split across workgroups (GEMM Optimization
-                       Guide §13, "tile_m x tile_n fills GPU"): 0 the planner's
+                       Guide §13, tiling checklist: enough workgroups to fill
+                       the GPU): 0 the planner's
                        choice (no split outside gemm_ex_ws), 1 no split, S = 2 ..
                        64 workgroups per tile, each taking 1/S of the K tiles
                        (S must divide them); S > 1 only through gemm_ex_ws   */
@@ -273,9 +274,9 @@ int gemm_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* op
 /*
  * gemm_ex_ws -- gemm_ex with a caller-provided device workspace, which lets
  * the planner split K across workgroups on the tile kernel where the tiles
- * alone would leave CUs idle (GEMM Optimization Guide §13, Tiling: "tile_m x
- * tile_n fills GPU (enough blocks)"; §1.3's tile table read with the 256 CUs
- * of MI355X), and, for BF16 / FP16 with long K, where the split lets a larger
+ * alone would leave CUs idle (GEMM Optimization Guide §13, the tiling item of
+ * its checklist: the grid must give the GPU enough workgroups; §1.3's tile
+ * table read with the 256 CUs of MI355X), and, for BF16 / FP16 with long K, where the split lets a larger
  * tile (fewer operand bytes per FLOP) fill the GPU instead of a smaller one.
  *   workspace        device, 16-byte aligned, at least gemm_workspace_size
  *                    bytes for the same arguments (ignored, and may be NULL,
