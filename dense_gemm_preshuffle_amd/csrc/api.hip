@@ -198,32 +198,31 @@ int choose_tile(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p, int want_ms) 
     case DT_I4: list = i4; n = sizeof(i4) / sizeof(Cand); break;
     default: list = fp4; n = sizeof(fp4) / sizeof(Cand); break;
   }
-  // First choice: the largest tile that still gives >= 256 workgroups (one
-  // per CU); otherwise the tile with the most workgroups. Edge tiles overlap
-  // their neighbours (the tile must still fit inside M x N), which computes
-  // some rows or columns twice: tiles whose grid covers at most 1/8 more
-  // than M x N come first, exact or not, the rest only if none of those
-  // fits. (Preferring exact tiles outright sent BF16 8000 x 8192 x 8192 to
-  // 64 x 256 tiles, 1616 us, against 728 us on 256 x 256 tiles, 2.4% of
-  // whose rows are computed twice.)
-  // First choice (all types but MXFP4): the tile whose busiest CU streams
-  // the fewest operand bytes per byte of K, ceil(grid / 256) * (TM + TN),
-  // among tiles whose edge tiles add at most a quarter to the computed area
-  // (ties to the earlier one), with three corrections measured on one
-  // MI355X: divided by 1.2 where a CU holds 8 waves or more (two resident
-  // workgroups, or an 8-wave tile: more loads in flight; with 1.35 two
-  // 128 x 128 tiles per CU won over one 128 x 256 on 1024 x 7168 x 2048 and
-  // measured 3-7% slower); times (256 / grid)^0.3 where
-  // CUs stay idle; times 1.4 for tiles whose A is staged through registers
-  // (BF16 64 x 128: 83 us against 59 with LDS DMA on 256 x 8192 x 8192).
-  // This ranks the tiles of the FP8 / BF16 / FP16 / INT8 shapes timed for it
-  // (80 x 7168 x 2048 to 8192^3) in their measured order, e.g. FP8 96 x
-  // 7168 x 2048 7.9 us on 168 tiles of 32 x 128 against 10.3 on 672 of
-  // 16 x 64 (the threshold rule's choice), BF16 768 x 4096 x 4096 40.6 on
-  // 128 x 128 against 45.7 on 64 x 256, BF16 300 x 8192 x 4096 45.4 on 320
-  // tiles of 64 x 128 against 53.7 on 160 of 64 x 256 (split later). MXFP4
-  // keeps the threshold rule (its 128 x 128 tile measured 18.7 us against
-  // 17.0 for 64 x 256 on 512 x 7168 x 4096, which the count gets wrong).
+  // Tile choice, all types but MXFP4: the tile whose busiest CU streams the
+  // fewest operand bytes per byte of K, ceil(grid / 256) * (TM + TN), among
+  // tiles whose edge tiles (overlapping their neighbours inside M x N) add at
+  // most a quarter to the computed area; ties go to the earlier candidate.
+  // Three corrections, each from a measured pair on one MI355X: divided by
+  // 1.2 where a CU holds 8 waves or more (two resident workgroups, or one
+  // 8-wave tile: more loads in flight; 1.35 made two 128 x 128 tiles per CU
+  // beat one 128 x 256 on 1024 x 7168 x 2048, which measured 3-7% slower);
+  // times (256 / grid)^0.3 where CUs stay idle; times 1.4 for tiles whose A
+  // is staged through registers (BF16 64 x 128: 83 us against 59 with LDS
+  // DMA on 256 x 8192 x 8192). This ranks the tiles of the FP8 / BF16 / FP16
+  // / INT8 shapes timed for it (80 x 7168 x 2048 to 8192^3) in their
+  // measured order, e.g. FP8 96 x 7168 x 2048 7.9 us on 168 tiles of 32 x 128
+  // against 10.3 on 672 of 16 x 64 (the threshold rule's choice), BF16 768 x
+  // 4096 x 4096 40.6 on 128 x 128 against 45.7 on 64 x 256, BF16 300 x 8192 x
+  // 4096 45.4 on 320 tiles of 64 x 128 against 53.7 on 160 of 64 x 256.
+  //
+  // Threshold rule (MXFP4, whose 128 x 128 tile the count ranks wrongly:
+  // 18.7 us against 17.0 for 64 x 256 on 512 x 7168 x 4096; and any type
+  // when no tile passes the count's filters): the first tile in the list's
+  // order that gives kFullGrid workgroups, else the one with the most.
+  // Tiles whose grid covers at most 1/8 more than M x N come first, exact or
+  // not, the rest only if none of those fits (preferring exact tiles
+  // outright sent BF16 8000 x 8192 x 8192 to 64 x 256 tiles, 1616 us,
+  // against 728 us on 256 x 256 tiles, 2.4% of whose rows are computed twice).
   if (dt != DT_FP4) {
     int best = -1;
     double best_cost = 0;
