@@ -65,7 +65,7 @@ class GemmError(RuntimeError):
         self.status = status
         msg = f"{where}: status {status} ({gemm_status_string(status)})"
         if status == GP_EHIP and _lib is not None:
-            msg += f" [{_lib.gemm_last_hip_error().decode()}]"
+            msg += f" [{_lib.gemm_last_hip_error().decode()} from {_lib.gemm_last_hip_call().decode()}]"
         super().__init__(msg)
 
 
@@ -107,6 +107,14 @@ def load_library():
         raise GemmLibraryMissing(
             f"{path} is not built; run `python -m dense_gemm_preshuffle_amd.build` "
             "(or __graft_entry__.build()) first")
+    # PyTorch ships its own HIP and HSA runtimes under the sonames of ROCm's
+    # (libamdhip64.so.7, libhsa-runtime64.so.1). Loaded after torch, this
+    # library binds to those copies: one runtime per process. Loaded before
+    # torch, it would bind to /opt/rocm's copies and torch would then load
+    # its own: two runtimes, and the second to start finds no device
+    # (hipGetDevice: hipErrorNoDevice). So torch is imported first.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.gemm_preshuffle_b.argtypes = [vp, vp, i64, i64, ci, vp]
@@ -126,6 +134,8 @@ def load_library():
     lib.gemm_status_string.restype = ctypes.c_char_p
     lib.gemm_last_hip_error.argtypes = []
     lib.gemm_last_hip_error.restype = ctypes.c_char_p
+    lib.gemm_last_hip_call.argtypes = []
+    lib.gemm_last_hip_call.restype = ctypes.c_char_p
     for f in ("gemm_preshuffle_b", "gemm_a8w8", "gemm_bf16", "gemm_mxfp4", "gemm_f16", "gemm_w4a8", "gemm_ex",
               "gemm_plan", "gemm_plan_ws", "gemm_workspace_size", "gemm_ex_ws", "gemm_ex_noalloc"):
         getattr(lib, f).restype = ci

@@ -705,11 +705,14 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 // Per-device cache of "is gfx950": 0 unknown, 1 yes, 2 no.
 std::atomic<int> g_arch[64];
 
-// Last HIP status the library saw in this thread (reported by
-// gemm_last_hip_error), and the gp_status it maps to.
+// Last HIP status the library saw in this thread and the runtime call that
+// returned it (reported by gemm_last_hip_error / gemm_last_hip_call), and the
+// gp_status it maps to.
 thread_local hipError_t g_last_hip = hipSuccess;
-int hip_status(hipError_t e) {
+thread_local const char* g_last_call = "";
+int hip_status(hipError_t e, const char* call) {
   g_last_hip = e;
+  g_last_call = e == hipSuccess ? "" : call;
   return e == hipSuccess ? GP_OK : GP_EHIP;
 }
 // HIP keeps one "last error" per thread, set by any runtime call, including
@@ -721,13 +724,13 @@ void clear_last_error() { (void)hipGetLastError(); }
 int check_device() {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e);
-  if (dev < 0 || dev >= 64) return GP_EHIP;
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return hip_status(hipErrorInvalidDevice, "hipGetDevice (device index past 63)");
   int v = g_arch[dev].load(std::memory_order_relaxed);
   if (v == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
-    if (e != hipSuccess) return hip_status(e);
+    if (e != hipSuccess) return hip_status(e, "hipGetDeviceProperties");
     v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
     g_arch[dev].store(v, std::memory_order_relaxed);
   }
@@ -796,7 +799,7 @@ int launch(int in_dtype, const Plan& p, const void* a, const void* b, const void
       default: e = launch_splitk_fp4(p.nb, p.waves, p.kch, p.mb, t, s); break;
     }
   }
-  return hip_status(e);
+  return hip_status(e, "kernel launch");
 }
 
 // B preshuffle: one thread per destination 16-byte chunk (writes coalesced;
@@ -862,8 +865,8 @@ ScratchSlot g_scratch[64];
 int scratch_for_current_device(void** out, hipStream_t s) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e);
-  if (dev < 0 || dev >= 64) return GP_EHIP;
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return hip_status(hipErrorInvalidDevice, "hipGetDevice (device index past 63)");
   ScratchSlot& sl = g_scratch[dev];
   std::call_once(sl.once, [&] {
     void* ptr = nullptr;
@@ -877,7 +880,7 @@ int scratch_for_current_device(void** out, hipStream_t s) {
     sl.err = r;
     sl.ptr = r == hipSuccess ? ptr : nullptr;
   });
-  if (sl.err != hipSuccess) return hip_status(sl.err);
+  if (sl.err != hipSuccess) return hip_status(sl.err, "scratch set-up (hipGetSymbolAddress, fill kernel)");
   *out = sl.ptr;
   return GP_OK;
 }
@@ -940,6 +943,8 @@ extern "C" {
 
 const char* gemm_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
 
+const char* gemm_last_hip_call(void) { return g_last_call; }
+
 const char* gemm_status_string(int status) {
   switch (status) {
     case GP_OK: return "ok";
@@ -980,7 +985,7 @@ int gemm_preshuffle_b(const void* b, void* b_shuf, int64_t N, int64_t K, int dty
   hipLaunchKernelGGL(preshuffle_kernel, dim3((chunks + 255) / 256), dim3(256), 0, (hipStream_t)stream,
                      (const char*)b, (char*)b_shuf, (uint32_t)(Kb / 64), (uint32_t)Kb, chunks,
                      dtype == GP_I4 ? 1 : 0);
-  return hip_status(hipGetLastError());
+  return hip_status(hipGetLastError(), "kernel launch");
 }
 
 int gemm_a8w8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b, void* c,

@@ -31,8 +31,8 @@
  *     steps); M is free. When the tile does not divide M or N, the edge
  *     tiles overlap their neighbours inside M x N (no padding is needed);
  *     N below one tile or a short K runs on the small-M kernel.
- *   - Thread-local state: the HIP status behind the last GP_EHIP
- *     (gemm_last_hip_error).
+ *   - Thread-local state: the HIP status behind the last GP_EHIP and the
+ *     runtime call that returned it (gemm_last_hip_error, gemm_last_hip_call).
  *   - Alignment: every data pointer must be 16-byte aligned.
  *   - Errors: arguments are validated on the host before any HIP call; a
  *     non-zero gp_status is returned and nothing is launched. A failing
@@ -349,6 +349,15 @@ const char* gemm_status_string(int status);
  * one left by an earlier runtime call of the caller.
  */
 const char* gemm_last_hip_error(void);
+
+/*
+ * The runtime call behind the last GP_EHIP of the calling thread: "hipGetDevice"
+ * or "hipGetDeviceProperties" (the device check before the first launch on a
+ * device), "kernel launch", or "scratch set-up (...)" (gemm_ex_noalloc's first
+ * call on a device); "" when the library's last HIP call in this thread
+ * succeeded. Static string; thread-local state.
+ */
+const char* gemm_last_hip_call(void);
 
 #ifdef __cplusplus
 }

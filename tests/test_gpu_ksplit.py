@@ -153,7 +153,9 @@ def test_scheduler_off_parity(dtype, M, N, K, opts):
                                          ("bf16", 256, 1024, 8192), ("w4a8", 256, 4096, 8192),
                                          ("int8", 128, 1024, 16384), ("fp8", 200, 2000, 16384),
                                          # a full grid of small tiles, split over larger ones (BF16 / FP16)
-                                         ("bf16", 512, 4096, 16384), ("fp16", 256, 4096, 8192)])
+                                         ("bf16", 512, 4096, 16384), ("fp16", 256, 4096, 8192),
+                                         # from a 128 x 128 first choice onto 128 x 256 tiles in two ranges
+                                         ("bf16", 512, 8192, 8192)])
 def test_automatic_split_parity(dtype, M, N, K):
     """The planner's own split (no options) on long-K shapes, every output."""
     import dense_gemm_preshuffle_amd as gp

@@ -56,6 +56,7 @@ def test_stale_error_of_an_earlier_call_is_not_a_launch_error():
                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         assert st == 0, (call, st, lib.gemm_last_hip_error())
         assert lib.gemm_last_hip_error() == b"hipSuccess"
+        assert lib.gemm_last_hip_call() == b""
     torch.cuda.synchronize()
     assert np.array_equal(b_shuf.cpu().numpy(), oracle.preshuffle(host["b"]))
     out = workload.to_host(c)
