@@ -496,6 +496,43 @@ int choose_wide(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, con
   return GP_OK;
 }
 
+// FP8 with 16 rows and long K, called with a workspace: 16 x 64 tiles whose
+// K tiles are split across workgroups instead of the small-M kernel, whose
+// workgroups each stream a whole K range of 16 or 32 columns (N / 16 or
+// N / 32 of them: few where N is small). S is the largest power of two that
+// keeps at least 2048 bytes of K per range and at most 256 workgroups, taken
+// where it is 4 or more. Measured (one MI355X, graph replay, rotating
+// inputs; small-M kernel against the split tiles): 16 x 2048 x 16384 15.9 ->
+// 11.5 us (S = 8), 16 x 1024 x 16384 15.5 -> 9.9, 16 x 1024 x 32768 28.5 ->
+// 14.9 (S = 16; 13.2 with 8), 16 x 2048 x 32768 29.4 -> 17.4, 16 x 3072 x
+// 16384 16.5 -> 13.2 (S = 4), 16 x 512 x 32768 28.0 -> 12.0, 16 x 2048 x
+// 8192 9.1 -> 8.3; below 8192 bytes of K it lost (16 x 2048 x 7168 8.2
+// against 8.8 split in 7).
+bool small_m_long_k(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
+  if (dt != DT_FP8 || M != 16 || Kb < 8192 || N < 64) return false;
+  if (!ksplit_compiled(DT_FP8, 16, 16, 64, 512, 0)) return false;
+  const int64_t T = (N + 63) / 64, KT = Kb / 512;
+  if (Kb % 512 || T > kMaxSplitTiles) return false;
+  int S = 0;
+  for (int s = 2; s <= 64; s *= 2) {
+    if (KT % s || Kb / s < 2048 || T * s > 256) break;
+    S = s;
+  }
+  if (S < 4) return false;
+  p->kernel = GP_KERNEL_TILE;
+  p->ms = 16;
+  p->tm = 16;
+  p->tn = 64;
+  p->tkb = 512;
+  p->pipe = 0;
+  p->kg = 1;
+  p->ks = S;
+  p->sched = 1;
+  p->epi = EPI_DIRECT;
+  p->xcd = 1;
+  return true;
+}
+
 // ws: the call brings a workspace (gemm_ex_ws), so the tile kernel may split
 // K across workgroups.
 int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o, Plan* p, bool ws = false) {
@@ -536,6 +573,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   if (dt == DT_I4 && p->kernel == GP_KERNEL_WIDE) return GP_EDTYPE;   // no 256 x 256 W4A8 kernel
   // a K split and the scheduler-off variants exist on the tile kernel only
   if (o && (o->ksplit > 1 || o->scheduler == 2) && p->kernel != GP_KERNEL_TILE) return GP_ESHAPE;
+  if (p->kernel == GP_KERNEL_SPLITK && !o && ws && small_m_long_k(dt, M, N, Kb, p)) return GP_OK;
   if (p->kernel == GP_KERNEL_SPLITK) return choose_split(dt, bits, M, N, Kb, p, o);
   if (p->kernel == GP_KERNEL_WIDE) return choose_wide(dt, bits, M, N, Kb, p, o);
 
@@ -916,8 +954,9 @@ int run_gemm(int in_dtype, int out_dtype, const void* a, const void* b_shuf, con
   Plan p;
   int r = make_plan(in_dtype, M, N, K, opts, &p, ws_mode != 0);
   if (r) return r;
-  // the scheduler-off and K-split variants have the plain epilogue only
-  if ((p.sched == 2 || p.ks > 1) && (bias || act != GP_ACT_NONE)) return GP_ESHAPE;
+  // the scheduler-off variants have the plain epilogue only (the K-split
+  // ones have both)
+  if (p.sched == 2 && (bias || act != GP_ACT_NONE)) return GP_ESHAPE;
   const int64_t need = workspace_bytes(p, M, N);
   if (need > 0 && ws_mode == 2) {
     if (need > kScratchBytes) return GP_EWORKSPACE;   // more than the static array holds

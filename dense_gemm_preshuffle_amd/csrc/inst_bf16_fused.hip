@@ -5,6 +5,6 @@
 
 namespace gp {
 
-GP_DEFINE_FUSED(bf16, GP_TILE_BF16, GP_TILE_KG2_BF16, GP_WIDE_BF16)
+GP_DEFINE_FUSED(bf16, GP_TILE_BF16, GP_TILE_KG2_BF16, GP_WIDE_BF16, GP_TILE_KSPLIT_BF16)
 
 }  // namespace gp

@@ -5,6 +5,6 @@
 
 namespace gp {
 
-GP_DEFINE_FUSED(f16, GP_TILE_F16, GP_TILE_KG2_F16, GP_WIDE_F16)
+GP_DEFINE_FUSED(f16, GP_TILE_F16, GP_TILE_KG2_F16, GP_WIDE_F16, GP_TILE_KSPLIT_F16)
 
 }  // namespace gp

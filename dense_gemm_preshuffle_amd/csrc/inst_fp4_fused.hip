@@ -5,6 +5,6 @@
 
 namespace gp {
 
-GP_DEFINE_FUSED(fp4, GP_TILE_FP4, GP_TILE_KG2_FP4, GP_WIDE_FP4)
+GP_DEFINE_FUSED(fp4, GP_TILE_FP4, GP_TILE_KG2_FP4, GP_WIDE_FP4, GP_TILE_KSPLIT_FP4)
 
 }  // namespace gp

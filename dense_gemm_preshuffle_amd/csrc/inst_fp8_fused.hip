@@ -5,6 +5,6 @@
 
 namespace gp {
 
-GP_DEFINE_FUSED(fp8, GP_TILE_FP8, GP_TILE_KG2_FP8, GP_WIDE_FP8)
+GP_DEFINE_FUSED(fp8, GP_TILE_FP8, GP_TILE_KG2_FP8, GP_WIDE_FP8, GP_TILE_KSPLIT_FP8)
 
 }  // namespace gp

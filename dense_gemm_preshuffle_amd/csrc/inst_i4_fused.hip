@@ -5,6 +5,6 @@
 
 namespace gp {
 
-GP_DEFINE_FUSED(i4, GP_TILE_I4, GP_TILE_KG2_I4, GP_WIDE_I4)
+GP_DEFINE_FUSED(i4, GP_TILE_I4, GP_TILE_KG2_I4, GP_WIDE_I4, GP_TILE_KSPLIT_I4)
 
 }  // namespace gp

@@ -52,6 +52,7 @@ hipError_t launch_splitk_i4(int nb, int waves, int kch, int mb, const SplitArgs&
 #define GP_TILE_CASE_KG2_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true, 2, true, false)
 #define GP_TILE_CASE_NOSCHED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 1, false, false)
 #define GP_TILE_CASE_KSPLIT(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, false, 1, true, true)
+#define GP_TILE_CASE_KSPLIT_FUSED(DT, MS, TM, TN, TKB, PIPE) GP_TILE_CASE_IMPL(DT, MS, TM, TN, TKB, PIPE, true, 1, true, true)
 #define GP_SPLITK_CASE(DT, NB, W, KCH, MB)                                                     \
   if (nb == NB && waves == W && kch == KCH && mb == MB) {                                      \
     const dim3 grid(a.N / (16 * NB), (a.M + 16 * MB - 1) / (16 * MB));                         \
@@ -83,12 +84,13 @@ hipError_t launch_splitk_i4(int nb, int waves, int kch, int mb, const SplitArgs&
     WIDES(GP_WIDE_CASE)                                                                             \
     return hipErrorInvalidValue;                                                                    \
   }
-#define GP_DEFINE_FUSED(NAME, TILES, KG2TILES, WIDES)                                               \
+#define GP_DEFINE_FUSED(NAME, TILES, KG2TILES, WIDES, KSPLIT)                                       \
   hipError_t launch_tile_##NAME##_fused(int ms, int tm, int tn, int tkb, int pipe, int epi, int kg, \
                                         const TileArgs& a, hipStream_t s) {                         \
     constexpr bool sched = true; /* fused variants keep the pinned schedule */                       \
     TILES(GP_TILE_CASE_FUSED)                                                                       \
     KG2TILES(GP_TILE_CASE_KG2_FUSED)                                                                \
+    KSPLIT(GP_TILE_CASE_KSPLIT_FUSED)                                                               \
     return hipErrorInvalidValue;                                                                    \
   }                                                                                                 \
   hipError_t launch_wide_##NAME##_fused(int ms, int tkb, int pipe, const TileArgs& a, hipStream_t s) { \

@@ -123,7 +123,7 @@
 // planner prefers them for an automatic split (measured on long-K shapes:
 // FP8 64 x 128 beat 128 x 128, FP4 128 x 128 beat 128 x 256).
 #define GP_TILE_KSPLIT_I8(X) X(DT_I8, 16, 64, 128, 256, 3) X(DT_I8, 16, 128, 128, 128, 0)
-#define GP_TILE_KSPLIT_FP8(X) X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 64, 256, 128, 3) \
+#define GP_TILE_KSPLIT_FP8(X) X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 64, 256, 128, 3) X(DT_FP8, 16, 16, 64, 512, 0) \
   X(DT_FP8, 16, 32, 256, 256, 3) X(DT_FP8, 16, 128, 128, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)
 #define GP_TILE_KSPLIT_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3) X(DT_BF16, 16, 64, 128, 128, 0)
 #define GP_TILE_KSPLIT_F16(X) X(DT_F16, 16, 128, 256, 128, 3)

@@ -128,7 +128,9 @@ typedef struct gemm_opts {
                        GEMM Optimization Guide §5.3): 0 the planner's choice,
                        1 on (loads and LDS reads pinned between the MFMA groups),
                        2 off (the compiler orders the loop); "off" exists for
-                       the tiles listed with a scheduler-off variant           */
+                       the tiles listed with a scheduler-off variant, with the
+                       plain epilogue only (with a bias or an activation:
+                       GP_ESHAPE)                                              */
 } gemm_opts;
 
 /* What the planner chose (host-side query, no GPU needed). */

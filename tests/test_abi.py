@@ -440,9 +440,14 @@ def test_workspace_validation(fake_ptrs):
     assert lib.gemm_ex_ws(*args, None, need, None) == gp.GP_EWORKSPACE
     assert lib.gemm_ex_ws(*args, FAKE, need - 1, None) == gp.GP_EWORKSPACE
     assert lib.gemm_ex_ws(*args, MIS, need, None) == GP_EINVAL
-    # split with a fused epilogue: not compiled
+    # a split with a fused epilogue passes the host checks (compiled; on a
+    # host without a gfx950 GPU the call stops at the device check)
     args_b = (1, 2, FAKE, FAKE, S, S, FAKE, 1, FAKE, 512, 4096, 4096, ctypes.byref(o))
-    assert lib.gemm_ex_ws(*args_b, FAKE, need, None) == GP_ESHAPE
+    assert lib.gemm_ex_ws(*args_b, FAKE, need, None) in (gp.GP_EHIP, 4)   # GP_EHIP or GP_EARCH
+    # the scheduler-off variants have the plain epilogue only
+    o2 = gp.GemmOpts(kernel=1, tile_m=64, tile_n=128, tile_k=256, pipeline=3, scheduler=2)
+    args_c = (1, 2, FAKE, FAKE, S, S, FAKE, 1, FAKE, 512, 4096, 4096, ctypes.byref(o2))
+    assert lib.gemm_ex_ws(*args_c, FAKE, need, None) == GP_ESHAPE
 
 
 def test_split_tile_count_limit():
@@ -503,3 +508,21 @@ def test_planner_full_grid_and_fp8_order():
     for M in (80, 96, 112):
         assert tile("fp8", M, 7168, 2048)[:2] == (32, 128), M
     assert tile("fp8", 1536, 8192, 4096)[:2] == (128, 256)
+
+
+def test_planner_splits_long_k_at_16_rows_over_16x64_tiles():
+    """FP8 with 16 rows and at least 8192 bytes of K, given a workspace: 16 x
+    64 tiles split along K into the largest power of two of ranges that keeps
+    2048 bytes of K per range and at most 256 workgroups; not without a
+    workspace, not for shorter K, not for other row counts."""
+    p = gp.gemm_plan_ws("fp8", 16, 2048, 16384)
+    assert (p["kernel"], p["tile_m"], p["tile_n"], p["tile_k"], p["ksplit"], p["grid"]) == (1, 16, 64, 512, 8, 256)
+    assert gp.gemm_plan_ws("fp8", 16, 1024, 32768)["ksplit"] == 16
+    assert gp.gemm_plan_ws("fp8", 16, 3072, 16384)["ksplit"] == 4
+    assert gp.gemm_plan_ws("fp8", 16, 2048, 8192)["ksplit"] == 4
+    assert gp.gemm_plan("fp8", 16, 2048, 16384)["kernel"] == 2            # no workspace
+    assert gp.gemm_plan_ws("fp8", 16, 2048, 7168)["kernel"] == 2          # K too short
+    assert gp.gemm_plan_ws("fp8", 16, 7168, 2048)["kernel"] == 2          # the M=16 workload is unchanged
+    assert gp.gemm_plan_ws("fp8", 32, 2048, 16384)["kernel"] == 2         # 16 rows only
+    assert gp.gemm_plan_ws("fp8", 8, 2048, 16384)["kernel"] == 2
+    assert gp.gemm_plan_ws("bf16", 16, 2048, 16384)["kernel"] == 2        # FP8 only

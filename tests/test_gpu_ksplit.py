@@ -155,7 +155,10 @@ def test_scheduler_off_parity(dtype, M, N, K, opts):
                                          # a full grid of small tiles, split over larger ones (BF16 / FP16)
                                          ("bf16", 512, 4096, 16384), ("fp16", 256, 4096, 8192),
                                          # from a 128 x 128 first choice onto 128 x 256 tiles in two ranges
-                                         ("bf16", 512, 8192, 8192)])
+                                         ("bf16", 512, 8192, 8192),
+                                         # FP8 with 16 rows and long K: 16 x 64 tiles in 8 ranges (N = 1008:
+                                         # the last column tile overlaps its neighbour)
+                                         ("fp8", 16, 2048, 16384), ("fp8", 16, 1008, 16384)])
 def test_automatic_split_parity(dtype, M, N, K):
     """The planner's own split (no options) on long-K shapes, every output."""
     import dense_gemm_preshuffle_amd as gp
@@ -191,3 +194,31 @@ def test_one_workspace_serves_shapes_of_any_size():
         torch.cuda.synchronize()
         check(dtype, host, workload.to_host(c))
     assert not ws[:65536].any().item()
+
+
+@pytest.mark.parametrize("dtype,M,N,K,act", [("fp8", 16, 2048, 16384, "gelu"), ("fp8", 128, 4096, 8192, "silu"),
+                                             ("bf16", 512, 4096, 16384, "relu"), ("mxfp4", 256, 4096, 16384, "gelu"),
+                                             ("w4a8", 256, 4096, 8192, "none"), ("fp16", 256, 4096, 8192, "silu")])
+def test_split_with_fused_epilogue(dtype, M, N, K, act):
+    """gemm_ex_ws with a bias and an activation on shapes the planner splits:
+    the last workgroup of each tile adds the partial sums, then runs the
+    fused epilogue (bias, activation) like an unsplit tile."""
+    import torch
+
+    import dense_gemm_preshuffle_amd as gp
+    from dense_gemm_preshuffle_amd import workload
+
+    plan = gp.gemm_plan_ws(dtype, M, N, K)
+    say(f"split + fused {act} {dtype} {M}x{N}x{K}: ksplit {plan['ksplit']} tile {plan['tile_m']}x{plan['tile_n']}")
+    assert plan["ksplit"] > 1
+    host = workloads.make_inputs(dtype, M, N, K, seed=M + N + K + 5, bias=True)
+    dev = workload.to_device(dtype, host)
+    p = workload.prepare(dtype, dev)
+    p["workspace"] = gp.workspace(dtype, M, N, K, None)
+    outs = []
+    for _ in range(2):
+        c = workload.run(dtype, p, act=act)
+        torch.cuda.synchronize()
+        outs.append(workload.to_host(c))
+    assert np.array_equal(outs[0], outs[1])
+    check(dtype, host, outs[0], act=act)
