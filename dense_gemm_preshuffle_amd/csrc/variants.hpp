@@ -29,7 +29,7 @@
   X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 128, 128, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)   \
   X(DT_FP8, 16, 128, 512, 128, 3) X(DT_FP8, 16, 64, 128, 512, 3) X(DT_FP8, 16, 64, 128, 512, 2)
 
-#define GP_TILE_BF16(X)                                                                            \
+#define GP_TILE_BF16(X) X(DT_BF16, 16, 16, 64, 256, 0) \
   X(DT_BF16, 16, 32, 128, 128, 0) X(DT_BF16, 16, 64, 128, 128, 0) X(DT_BF16, 16, 128, 256, 128, 0) X(DT_BF16, 16, 128, 256, 64, 0)          \
   X(DT_BF16, 32, 64, 128, 128, 0) X(DT_BF16, 32, 64, 256, 128, 0) X(DT_BF16, 32, 128, 128, 128, 0)          \
   X(DT_BF16, 32, 128, 256, 128, 0) X(DT_BF16, 32, 128, 256, 64, 0)                                \
@@ -40,7 +40,7 @@
   X(DT_BF16, 16, 256, 256, 128, 3) X(DT_BF16, 16, 256, 256, 128, 2) X(DT_BF16, 16, 256, 256, 128, 4) \
   X(DT_BF16, 16, 64, 128, 128, 3) X(DT_BF16, 16, 64, 256, 128, 3) X(DT_BF16, 16, 128, 128, 128, 3)
 
-#define GP_TILE_F16(X)                                                                             \
+#define GP_TILE_F16(X) X(DT_F16, 16, 16, 64, 256, 0) \
   X(DT_F16, 16, 32, 128, 128, 0) X(DT_F16, 16, 64, 128, 128, 0) X(DT_F16, 16, 64, 256, 128, 0)             \
   X(DT_F16, 16, 128, 128, 128, 0) X(DT_F16, 16, 128, 256, 128, 0) X(DT_F16, 16, 128, 256, 128, 3)          \
   X(DT_F16, 32, 128, 256, 128, 3) X(DT_F16, 32, 64, 128, 128, 0)                                  \
@@ -97,7 +97,7 @@
 #define GP_TILE_KG2_FP4(X)
 
 // W4A8 on the tile kernel (tile_k in bytes of B; A tiles are twice as long)
-#define GP_TILE_I4(X)                                                                              \
+#define GP_TILE_I4(X) X(DT_I4, 16, 16, 64, 128, 0) \
   X(DT_I4, 16, 128, 256, 64, 3) X(DT_I4, 16, 64, 256, 64, 3) X(DT_I4, 16, 64, 128, 128, 3)         \
   X(DT_I4, 16, 64, 128, 64, 3) X(DT_I4, 16, 32, 128, 64, 3) X(DT_I4, 16, 32, 64, 64, 0)
 #define GP_TILE_KG2_I4(X)
@@ -122,13 +122,13 @@
 // (gemm_ex_ws, gemm_opts.ksplit > 1), plain epilogue only, in the order the
 // planner prefers them for an automatic split (measured on long-K shapes:
 // FP8 64 x 128 beat 128 x 128, FP4 128 x 128 beat 128 x 256).
-#define GP_TILE_KSPLIT_I8(X) X(DT_I8, 16, 64, 128, 256, 3) X(DT_I8, 16, 128, 128, 128, 0)
+#define GP_TILE_KSPLIT_I8(X) X(DT_I8, 16, 64, 128, 256, 3) X(DT_I8, 16, 128, 128, 128, 0) X(DT_I8, 16, 16, 64, 256, 0)
 #define GP_TILE_KSPLIT_FP8(X) X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 64, 256, 128, 3) X(DT_FP8, 16, 16, 64, 512, 0) \
   X(DT_FP8, 16, 32, 256, 256, 3) X(DT_FP8, 16, 128, 128, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)
-#define GP_TILE_KSPLIT_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3) X(DT_BF16, 16, 64, 128, 128, 0)
-#define GP_TILE_KSPLIT_F16(X) X(DT_F16, 16, 128, 256, 128, 3)
+#define GP_TILE_KSPLIT_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3) X(DT_BF16, 16, 64, 128, 128, 0) X(DT_BF16, 16, 16, 64, 256, 0)
+#define GP_TILE_KSPLIT_F16(X) X(DT_F16, 16, 128, 256, 128, 3) X(DT_F16, 16, 16, 64, 256, 0)
 #define GP_TILE_KSPLIT_FP4(X) X(DT_FP4, 32, 128, 128, 128, 0) X(DT_FP4, 32, 128, 256, 128, 2)
-#define GP_TILE_KSPLIT_I4(X) X(DT_I4, 16, 64, 128, 128, 3) X(DT_I4, 16, 64, 256, 64, 3)
+#define GP_TILE_KSPLIT_I4(X) X(DT_I4, 16, 64, 128, 128, 3) X(DT_I4, 16, 64, 256, 64, 3) X(DT_I4, 16, 16, 64, 128, 0)
 #define GP_TILE_KSPLIT_ALL(X) GP_TILE_KSPLIT_I8(X) GP_TILE_KSPLIT_FP8(X) GP_TILE_KSPLIT_BF16(X) \
   GP_TILE_KSPLIT_F16(X) GP_TILE_KSPLIT_FP4(X) GP_TILE_KSPLIT_I4(X)
 

@@ -511,10 +511,11 @@ def test_planner_full_grid_and_fp8_order():
 
 
 def test_planner_splits_long_k_at_16_rows_over_16x64_tiles():
-    """FP8 with 16 rows and at least 8192 bytes of K, given a workspace: 16 x
-    64 tiles split along K into the largest power of two of ranges that keeps
-    2048 bytes of K per range and at most 256 workgroups; not without a
-    workspace, not for shorter K, not for other row counts."""
+    """16 rows and long K, given a workspace: 16 x 64 tiles split along K into
+    the largest power of two of ranges that keeps 2048 bytes of B's K per
+    range and at most 256 workgroups (4 or more), from 8192 bytes per B row
+    for FP8 and 16384 for INT8, BF16, FP16 and W4A8; not without a workspace,
+    not for shorter K, not for other row counts, not for MXFP4."""
     p = gp.gemm_plan_ws("fp8", 16, 2048, 16384)
     assert (p["kernel"], p["tile_m"], p["tile_n"], p["tile_k"], p["ksplit"], p["grid"]) == (1, 16, 64, 512, 8, 256)
     assert gp.gemm_plan_ws("fp8", 16, 1024, 32768)["ksplit"] == 16
@@ -525,4 +526,14 @@ def test_planner_splits_long_k_at_16_rows_over_16x64_tiles():
     assert gp.gemm_plan_ws("fp8", 16, 7168, 2048)["kernel"] == 2          # the M=16 workload is unchanged
     assert gp.gemm_plan_ws("fp8", 32, 2048, 16384)["kernel"] == 2         # 16 rows only
     assert gp.gemm_plan_ws("fp8", 8, 2048, 16384)["kernel"] == 2
-    assert gp.gemm_plan_ws("bf16", 16, 2048, 16384)["kernel"] == 2        # FP8 only
+    q = gp.gemm_plan_ws("int8", 16, 2048, 16384)
+    assert (q["kernel"], q["tile_m"], q["tile_n"], q["tile_k"], q["ksplit"]) == (1, 16, 64, 256, 8)
+    assert gp.gemm_plan_ws("int8", 16, 2048, 8192)["kernel"] == 2         # 8192 bytes: INT8 keeps the small-M kernel
+    for dt in ("bf16", "fp16"):
+        q = gp.gemm_plan_ws(dt, 16, 2048, 8192)                             # 16384 bytes per row
+        assert (q["kernel"], q["tile_k"], q["ksplit"]) == (1, 128, 8)
+        assert gp.gemm_plan_ws(dt, 16, 2048, 4096)["kernel"] == 2
+    q = gp.gemm_plan_ws("w4a8", 16, 1024, 32768)
+    assert (q["kernel"], q["tile_k"], q["ksplit"]) == (1, 256, 8)
+    assert gp.gemm_plan_ws("w4a8", 16, 2048, 16384)["kernel"] == 2
+    assert gp.gemm_plan_ws("mxfp4", 16, 2048, 32768)["kernel"] == 2
