@@ -496,34 +496,36 @@ int choose_wide(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, con
   return GP_OK;
 }
 
-// 16 rows and long K, called with a workspace: 16 x 64 tiles (A through
-// registers) whose K tiles are split across workgroups, instead of the
-// small-M kernel, whose workgroups each stream a whole K range of 16 or 32
-// columns (N / 16 or N / 32 of them: few where N is small). S is the largest
-// power of two that keeps at least 2048 bytes of B's K per range and at most
-// 256 workgroups, taken where it is 4 or more and B's rows hold at least
-// 8192 bytes (FP8) or 16384 (INT8, BF16, FP16, W4A8). Measured (one MI355X,
-// graph replay, rotating inputs; small-M kernel -> split tiles): FP8 16 x
-// 2048 x 16384 15.9 -> 11.5 us (S = 8), 16 x 1024 x 32768 28.5 -> 14.9, 16 x
-// 512 x 32768 28.0 -> 12.0, 16 x 2048 x 8192 9.1 -> 8.3; INT8 16 x 2048 x
-// 16384 15.2 -> 11.8, 16 x 1024 x 32768 27.3 -> 15.2; BF16 16 x 2048 x 8192
-// 15.3 -> 11.8, 16 x 1024 x 16384 27.3 -> 15.2; W4A8 16 x 1024 x 32768 19.0
-// -> 15.9. Below those K the split lost (FP8 16 x 2048 x 7168 8.8 against
-// 8.2, INT8 16 x 2048 x 8192 9.3 against 8.6, BF16 16 x 2048 x 4096 9.4
-// against 8.8, W4A8 16 x 2048 x 16384 11.2 against 10.8).
+// 16 to 64 rows and long K, called with a workspace: 16 x 64 tiles (A
+// through registers) whose K tiles are split across workgroups, instead of
+// the small-M kernel, whose workgroups each stream a whole K range of 16 or
+// 32 columns for every row (N / 16 or N / 32 of them: few where N is small).
+// S is the largest power of two that keeps at least 2048 bytes of B's K per
+// range and at most 256 workgroups, taken where B's rows hold at least 8192
+// bytes (FP8) or 16384 (INT8, BF16, FP16, W4A8) and S is 4 or more (2 or
+// more with more than 16 rows). Measured (one MI355X, graph replay, rotating
+// inputs; small-M kernel -> split tiles): FP8 16 x 2048 x 16384 15.9 -> 11.5
+// us (S = 8), 16 x 1024 x 32768 28.5 -> 14.9, 16 x 512 x 32768 28.0 -> 12.0,
+// 16 x 2048 x 8192 9.1 -> 8.3, 32 x 2048 x 16384 22.6 -> 12.1 (S = 4), 64 x
+// 1024 x 16384 36.5 -> 11.1, 64 x 2048 x 16384 36.8 -> 16.4 (S = 2), 48 x
+// 1024 x 32768 60.4 -> 17.1, 32 x 4096 x 8192 12.8 -> 11.8; INT8 16 x 2048 x
+// 16384 15.2 -> 11.8, 64 x 2048 x 16384 37.5 -> 22.3; BF16 16 x 1024 x
+// 16384 27.3 -> 15.2, 64 x 1024 x 16384 72.9 -> 22.8; W4A8 16 x 1024 x
+// 32768 19.0 -> 15.9. Below those K the split lost at 16 rows (FP8 16 x 2048
+// x 7168 8.8 against 8.2, INT8 16 x 2048 x 8192 9.3 against 8.6, BF16 16 x
+// 2048 x 4096 9.4 against 8.8, W4A8 16 x 2048 x 16384 11.2 against 10.8).
 bool small_m_long_k(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
-  if (M != 16 || N < 64 || dt == DT_FP4) return false;
+  if (M < 16 || M > 64 || N < 64 || dt == DT_FP4) return false;
   const int tkb = dt == DT_FP8 ? 512 : dt == DT_I4 ? 128 : 256;   // 512 bytes of A per K tile (W4A8: 256)
   if (Kb < (dt == DT_FP8 ? 8192 : 16384) || Kb % tkb) return false;
   if (!ksplit_compiled(dt, 16, 16, 64, tkb, 0)) return false;
-  const int64_t T = (N + 63) / 64, KT = Kb / tkb;
-  if (T > kMaxSplitTiles) return false;
+  const int64_t T = ((M + 15) / 16) * ((N + 63) / 64), KT = Kb / tkb;
   int S = 0;
   for (int s = 2; s <= 64; s *= 2) {
     if (KT % s || Kb / s < 2048 || T * s > 256) break;
     S = s;
   }
-  if (S < 4) return false;
+  if (S < (M <= 16 ? 4 : 2)) return false;
   p->kernel = GP_KERNEL_TILE;
   p->ms = 16;
   p->tm = 16;

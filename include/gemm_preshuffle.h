@@ -278,8 +278,11 @@ int gemm_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* op
  * the planner split K across workgroups on the tile kernel where the tiles
  * alone would leave CUs idle (GEMM Optimization Guide §13, the tiling item of
  * its checklist: the grid must give the GPU enough workgroups; §1.3's tile
- * table read with the 256 CUs of MI355X), and, for BF16 / FP16 with long K, where the split lets a larger
- * tile (fewer operand bytes per FLOP) fill the GPU instead of a smaller one.
+ * table read with the 256 CUs of MI355X); for BF16 / FP16 with long K, where
+ * the split lets a larger tile (fewer operand bytes per FLOP) fill the GPU
+ * instead of a smaller one; and for 16 to 64 rows with long K, where 16 x 64
+ * tiles split along K replace the small-M kernel (FP8 from 8192 bytes per B
+ * row, INT8 / BF16 / FP16 / W4A8 from 16384; not MXFP4).
  *   workspace        device, 16-byte aligned, at least gemm_workspace_size
  *                    bytes for the same arguments (ignored, and may be NULL,
  *                    when that size is 0). Its first 64 KiB hold one arrival

@@ -510,12 +510,13 @@ def test_planner_full_grid_and_fp8_order():
     assert tile("fp8", 1536, 8192, 4096)[:2] == (128, 256)
 
 
-def test_planner_splits_long_k_at_16_rows_over_16x64_tiles():
-    """16 rows and long K, given a workspace: 16 x 64 tiles split along K into
-    the largest power of two of ranges that keeps 2048 bytes of B's K per
-    range and at most 256 workgroups (4 or more), from 8192 bytes per B row
-    for FP8 and 16384 for INT8, BF16, FP16 and W4A8; not without a workspace,
-    not for shorter K, not for other row counts, not for MXFP4."""
+def test_planner_splits_long_k_at_16_to_64_rows_over_16x64_tiles():
+    """16 to 64 rows and long K, given a workspace: 16 x 64 tiles split along
+    K into the largest power of two of ranges that keeps 2048 bytes of B's K
+    per range and at most 256 workgroups (4 or more at 16 rows, 2 or more
+    above), from 8192 bytes per B row for FP8 and 16384 for INT8, BF16, FP16
+    and W4A8; not without a workspace, not for shorter K, not for other row
+    counts, not for MXFP4."""
     p = gp.gemm_plan_ws("fp8", 16, 2048, 16384)
     assert (p["kernel"], p["tile_m"], p["tile_n"], p["tile_k"], p["ksplit"], p["grid"]) == (1, 16, 64, 512, 8, 256)
     assert gp.gemm_plan_ws("fp8", 16, 1024, 32768)["ksplit"] == 16
@@ -524,8 +525,21 @@ def test_planner_splits_long_k_at_16_rows_over_16x64_tiles():
     assert gp.gemm_plan("fp8", 16, 2048, 16384)["kernel"] == 2            # no workspace
     assert gp.gemm_plan_ws("fp8", 16, 2048, 7168)["kernel"] == 2          # K too short
     assert gp.gemm_plan_ws("fp8", 16, 7168, 2048)["kernel"] == 2          # the M=16 workload is unchanged
-    assert gp.gemm_plan_ws("fp8", 32, 2048, 16384)["kernel"] == 2         # 16 rows only
     assert gp.gemm_plan_ws("fp8", 8, 2048, 16384)["kernel"] == 2
+    # above 16 rows: ceil(M / 16) * ceil(N / 64) tiles, 2 or more ranges
+    for M, N, K, S in ((32, 2048, 16384, 4), (64, 1024, 16384, 4), (64, 2048, 16384, 2),
+                       (48, 1024, 32768, 4), (40, 2048, 16384, 2), (17, 2048, 16384, 4),
+                       (32, 4096, 8192, 2)):
+        q = gp.gemm_plan_ws("fp8", M, N, K)
+        assert (q["kernel"], q["tile_m"], q["tile_n"], q["ksplit"]) == (1, 16, 64, S), (M, N, K, q)
+        assert q["grid"] == -(-M // 16) * -(-N // 64) * S
+    assert gp.gemm_plan_ws("fp8", 64, 4096, 16384)["kernel"] == 2         # 256 tiles: no room to split
+    assert gp.gemm_plan_ws("fp8", 32, 2048, 7168)["kernel"] == 2          # K too short
+    assert gp.gemm_plan_ws("fp8", 65, 2048, 16384)["tile_m"] != 16        # past 64 rows: the tile planner's own choice
+    assert gp.gemm_plan("fp8", 64, 2048, 16384)["kernel"] == 2            # no workspace
+    assert gp.gemm_plan_ws("int8", 64, 2048, 16384)["ksplit"] == 2
+    assert gp.gemm_plan_ws("bf16", 64, 1024, 16384)["ksplit"] == 4
+    assert gp.gemm_plan_ws("bf16", 32, 2048, 4096)["kernel"] == 2
     q = gp.gemm_plan_ws("int8", 16, 2048, 16384)
     assert (q["kernel"], q["tile_m"], q["tile_n"], q["tile_k"], q["ksplit"]) == (1, 16, 64, 256, 8)
     assert gp.gemm_plan_ws("int8", 16, 2048, 8192)["kernel"] == 2         # 8192 bytes: INT8 keeps the small-M kernel

@@ -160,7 +160,13 @@ def test_scheduler_off_parity(dtype, M, N, K, opts):
                                          # the last column tile overlaps its neighbour)
                                          ("fp8", 16, 2048, 16384), ("fp8", 16, 1008, 16384),
                                          ("int8", 16, 2048, 16384), ("bf16", 16, 2048, 8192),
-                                         ("fp16", 16, 1008, 8192), ("w4a8", 16, 1024, 32768)])
+                                         ("fp16", 16, 1008, 8192), ("w4a8", 16, 1024, 32768),
+                                         # 17 to 64 rows: ceil(M / 16) row tiles of 16 (M = 40, 17: the last
+                                         # row tile overlaps its neighbour)
+                                         ("fp8", 48, 1024, 32768), ("fp8", 40, 2048, 16384),
+                                         ("fp8", 17, 1008, 16384), ("int8", 64, 2048, 16384),
+                                         ("bf16", 32, 2048, 8192), ("fp16", 64, 1024, 16384),
+                                         ("w4a8", 33, 1024, 32768)])
 def test_automatic_split_parity(dtype, M, N, K):
     """The planner's own split (no options) on long-K shapes, every output."""
     import dense_gemm_preshuffle_amd as gp
@@ -201,7 +207,8 @@ def test_one_workspace_serves_shapes_of_any_size():
 @pytest.mark.parametrize("dtype,M,N,K,act", [("fp8", 16, 2048, 16384, "gelu"), ("fp8", 128, 4096, 8192, "silu"),
                                              ("bf16", 512, 4096, 16384, "relu"), ("mxfp4", 256, 4096, 16384, "gelu"),
                                              ("w4a8", 256, 4096, 8192, "none"), ("fp16", 256, 4096, 8192, "silu"),
-                                             ("bf16", 16, 2048, 8192, "relu"), ("w4a8", 16, 1024, 32768, "gelu")])
+                                             ("bf16", 16, 2048, 8192, "relu"), ("w4a8", 16, 1024, 32768, "gelu"),
+                                             ("fp8", 40, 2048, 16384, "silu"), ("bf16", 64, 1024, 16384, "gelu")])
 def test_split_with_fused_epilogue(dtype, M, N, K, act):
     """gemm_ex_ws with a bias and an activation on shapes the planner splits:
     the last workgroup of each tile adds the partial sums, then runs the
