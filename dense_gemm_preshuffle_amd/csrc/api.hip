@@ -304,13 +304,27 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
   if (o && o->tile_m > 0 && o->tile_m != 16 && o->tile_m != 32 && o->tile_m != 64) return GP_ESHAPE;
   if (o && o->tile_k > 0 && ((int64_t)o->tile_k * bits) % 8) return GP_ESHAPE;
   const int user_kch = (o && o->tile_k > 0) ? (int)((int64_t)o->tile_k * bits / 8) : 0;
-  // (waves, 16-row blocks per workgroup) in order of preference. One block
-  // for M <= 16; two beyond (B read once per pair); four on 8 waves beyond
-  // 32 rows (B read once for up to 64 rows: 64 x 7168 x 2048 FP8 7.7 us
-  // against 8.7 with two blocks and 8.1 on tiles, BF16 11.8 against 15.0;
-  // MXFP4 stays on two, 7.2 against 8.2); one wave last (K too short for 4).
+  // (waves, 16-row blocks per workgroup mb, 16-column blocks nb): the
+  // caller's, else the compiled pair that leaves the busiest CU the fewest
+  // bytes over its ceil(grid / 256) rounds of workgroups, counting B's bytes
+  // and half of A's (read from L2; they cost about half as much per byte on
+  // the M=16 shape), ties to more rows, then to two column blocks. More rows
+  // per workgroup read B once for all of them but give fewer workgroups; four
+  // blocks run on 8 waves, not for MXFP4 (7.2 us against 8.2 on two at
+  // 64 x 7168 x 2048). One wave is the last resort (K too short for 4).
+  // Measured (one MI355X; FP8 unless named; rows per workgroup):
+  //   M=16, K=2048: N=2048 3.26 us on one column block (128 workgroups)
+  //     against 3.81 on two, N=4096 3.64 against 3.99, N=5120 4.19 on two
+  //     (160) against 4.97 on one (320), N=7168 4.44 on two (224);
+  //   64 x 7168 x 2048: 7.4 on 64 rows, 8.4 on 32, 11.2 on 16;
+  //   64 x 4096 x 4096: 7.8 on 32, 11.5 on 64, 10.5 on 16;
+  //   64 x 2048 x 4096: 5.9 on 16, 7.5 on 32, 11.4 on 64; BF16 64 x 1024 x
+  //   7168 13.6 on 16 against 33.9 on 64; 24 x 4096 x 2048 4.2 on 16, 4.9
+  //   on 32. Over 288 shapes (six types, 24-64 rows, N 1024-7168, K
+  //   2048-7168) this choice summed to 2628 us (with MXFP4's 128-byte
+  //   chunks), against 3485 for 64 rows above 32 and 32 above 16.
   struct WM { int waves, mb; };
-  WM cand[4];
+  WM cand[3];
   int nc = 0;
   if (o && o->tile_m > 0) {
     const int mb = o->tile_m / 16;
@@ -322,41 +336,46 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
     if (M > 32 && dt != DT_FP4) cand[nc++] = {8, 4};
     if (M > 16) cand[nc++] = {4, 2};
     cand[nc++] = {4, 1};
-    cand[nc++] = {1, 1};
   }
-  // column blocks per workgroup: the caller's, else the count (1 or 2) that
-  // leaves the busiest CU the fewest bytes over its ceil(grid / 256) rounds of
-  // workgroups, counting B's bytes and half of A's (read from L2; they cost
-  // about half as much per byte on the M=16 shape), ties to 2. FP8 M=16,
-  // K=2048: N=2048 3.26 us on one block (128 workgroups) against 3.81 on
-  // two, N=4096 3.64 against 3.99 (256 against 128 workgroups), N=5120 4.19
-  // on two (160) against 4.97 on one (320), N=7168 4.44 on two (224).
   int nbc[2] = {2, 1};
   int nn = 2;
   if (o && o->tile_n > 0) { nbc[0] = o->tile_n / 16; nn = 1; }
+  const int64_t Ka = Kb * (dt == DT_I4 ? 2 : 1);
+  // the chunk (K bytes per wave step) of one (waves, mb, nb), 0 if not compiled
+  auto chunk = [&](int waves, int mb, int nb) {
+    if (Kb % waves || N % (16 * nb)) return 0;
+    const int64_t kw = Kb / waves;
+    const int kch = user_kch ? user_kch : pick_chunk(dt, nb, waves, mb, kw);
+    if (kch == 0 || kw % kch || !split_compiled(dt, nb, waves, kch, mb)) return 0;
+    return kch;
+  };
+  double best = -1;
   for (int i = 0; i < nc; ++i) {
     const int waves = cand[i].waves, mb = cand[i].mb;
-    if (Kb % waves) continue;
-    const int64_t kw = Kb / waves;
-    if (nn == 2 && N % 32 == 0) {
-      const int64_t rows = std::min<int64_t>(M, 16 * mb), Ka = Kb * (dt == DT_I4 ? 2 : 1);
-      auto cost = [&](int nb) {
-        const int64_t grid = (N / (16 * nb)) * ((M + 16 * mb - 1) / (16 * mb));
-        return (double)((grid + 255) / 256) * ((double)(16 * nb) * Kb + 0.5 * (double)rows * Ka);
-      };
-      const bool one = cost(1) < cost(2);
-      nbc[0] = one ? 1 : 2;
-      nbc[1] = one ? 2 : 1;
-    }
     for (int c = 0; c < nn; ++c) {
       const int nb = nbc[c];
-      if (N % (16 * nb)) continue;
-      const int kch = user_kch ? user_kch : pick_chunk(dt, nb, waves, mb, kw);
-      if (kch == 0 || kw % kch || !split_compiled(dt, nb, waves, kch, mb)) continue;
+      const int kch = chunk(waves, mb, nb);
+      if (!kch) continue;
+      const int64_t rows = std::min<int64_t>(M, 16 * mb);
+      const int64_t grid = (N / (16 * nb)) * ((M + 16 * mb - 1) / (16 * mb));
+      const double cost = (double)((grid + 255) / 256) * ((double)(16 * nb) * Kb + 0.5 * (double)rows * Ka);
+      if (best >= 0 && cost >= best) continue;
+      best = cost;
       p->nb = nb;
       p->waves = waves;
       p->kch = kch;
       p->mb = mb;
+    }
+  }
+  if (best >= 0) return GP_OK;
+  if (!(o && (o->tile_m > 0 || o->waves > 0))) {
+    for (int c = 0; c < nn; ++c) {
+      const int kch = chunk(1, 1, nbc[c]);
+      if (!kch) continue;
+      p->nb = nbc[c];
+      p->waves = 1;
+      p->kch = kch;
+      p->mb = 1;
       return GP_OK;
     }
   }

@@ -72,7 +72,8 @@
 #define GP_SPLITK_BF16(Y) Y(DT_BF16, 1, 4, 64, 1) Y(DT_BF16, 1, 4, 256, 1) Y(DT_BF16, 2, 4, 256, 1) Y(DT_BF16, 1, 1, 64, 1) \
   Y(DT_BF16, 2, 4, 256, 2) Y(DT_BF16, 2, 8, 256, 4)
 #define GP_SPLITK_FP4(Y) Y(DT_FP4, 1, 4, 64, 1) Y(DT_FP4, 1, 4, 256, 1) Y(DT_FP4, 2, 4, 256, 1) Y(DT_FP4, 1, 1, 64, 1) \
-  Y(DT_FP4, 2, 4, 256, 2) Y(DT_FP4, 2, 8, 64, 4)
+  Y(DT_FP4, 2, 4, 256, 2) Y(DT_FP4, 2, 8, 64, 4) \
+  Y(DT_FP4, 1, 4, 128, 1) Y(DT_FP4, 2, 4, 128, 1) Y(DT_FP4, 2, 4, 128, 2)
 #define GP_SPLITK_F16(Y) Y(DT_F16, 1, 4, 64, 1) Y(DT_F16, 1, 4, 256, 1) Y(DT_F16, 2, 4, 256, 1) Y(DT_F16, 1, 1, 64, 1) \
   Y(DT_F16, 2, 4, 256, 2) Y(DT_F16, 2, 8, 256, 4)
 // W4A8: chunk bytes are bytes of B (the int8 A chunk is twice as long)

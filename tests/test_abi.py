@@ -236,7 +236,7 @@ def test_w4a8_plan():
     with pytest.raises(gp.GemmError) as e:
         gp.gemm_plan("w4a8", 16, 256, 2 * 65536)               # int32 range of the 16x widened products
     assert e.value.status == GP_ESHAPE
-    q = gp.gemm_plan("w4a8", 300, 512, 4096, dict(kernel=2))   # small-M kernel, any M: 4 row blocks
+    q = gp.gemm_plan("w4a8", 300, 512, 4096, dict(kernel=2, tile_m=64))   # small-M kernel, any M: 4 row blocks
     assert q["tile_m"] == 64 and q["grid"] == (512 // q["tile_n"]) * 5   # per workgroup, the last partial
     # larger M: the tile kernel, two int8 MFMAs per 64-byte INT4 piece; A
     # tiles (int8) are twice the bytes of the B tile's K extent
@@ -339,18 +339,21 @@ def test_k_not_a_multiple_of_the_large_tiles(dtype, M, N, K):
 
 @pytest.mark.parametrize("dtype", ["fp8", "bf16", "int8", "mxfp4", "fp16", "w4a8"])
 def test_small_m_row_blocks(dtype):
-    """The small-M kernel takes two 16-row blocks per workgroup beyond one
-    block of rows, and four on 8 waves beyond 32 rows (MXFP4: two), so B is
-    read once per pair or quadruple; the issued MFMAs still cover every
-    output."""
+    """The small-M kernel's rows per workgroup: 16, 32, or 64 on 8 waves
+    (not MXFP4); more read B once for more rows but give fewer workgroups.
+    On 7168 columns (224 workgroups of 32 columns) the largest block that
+    holds the rows wins; on 4096, 32 rows; on 1024, 16 (one 256-workgroup
+    round). The issued MFMAs still cover every output."""
     four = 2 if dtype == "mxfp4" else 4
-    for M, mb in [(16, 1), (5, 1), (24, 2), (32, 2), (48, four), (64, four), (100, four)]:
-        p = gp.gemm_plan(dtype, M, 7168, 2048, dict(kernel=2))
-        assert p["tile_m"] == 16 * mb, (M, p)
+    for M, N, mb in [(16, 7168, 1), (5, 7168, 1), (24, 7168, 2), (32, 7168, 2), (48, 7168, four),
+                     (64, 7168, four), (100, 7168, four), (64, 4096, 2), (48, 4096, 2), (64, 1024, 1),
+                     (33, 2048, 1), (24, 4096, 1)]:
+        p = gp.gemm_plan(dtype, M, N, 2048, dict(kernel=2))
+        assert p["tile_m"] == 16 * mb, (M, N, p)
         assert p["waves"] == (8 if mb == 4 else 4)
-        assert p["grid"] == (7168 // p["tile_n"]) * -(-M // (16 * mb))
+        assert p["grid"] == (N // p["tile_n"]) * -(-M // (16 * mb))
         assert p["mfma_total"] == p["grid"] * p["waves"] * p["k_tiles"] * p["mfma_per_wave_tile"]
-        assert p["mfma_total"] * F.flops_per_mfma_gfx950(dtype, 16) >= F.flops(M, 7168, 2048)
+        assert p["mfma_total"] * F.flops_per_mfma_gfx950(dtype, 16) >= F.flops(M, N, 2048)
     q = gp.gemm_plan(dtype, 64, 7168, 2048, dict(kernel=2, tile_m=16))
     assert q["tile_m"] == 16
 

@@ -200,20 +200,26 @@ TILE_CASES = [
     ("w4a8", 48, 128, 512, dict(kernel=2, tile_k=128)),
     ("w4a8", 16, 128, 4096, dict(kernel=2, tile_n=32, tile_k=128)),   # 4 chunks per wave
     # small-M kernel with 2 or 4 row blocks per workgroup (B read once per 2 or 4 row blocks)
-    ("fp8", 32, 512, 2048, dict(kernel=2)),
-    ("fp8", 64, 256, 1024, dict(kernel=2)),
-    ("fp8", 48, 512, 2048, dict(kernel=2)),
-    ("bf16", 64, 256, 512, dict(kernel=2)),
-    ("int8", 64, 256, 512, dict(kernel=2)),
-    ("mxfp4", 64, 256, 1024, dict(kernel=2)),
-    ("fp16", 32, 256, 512, dict(kernel=2)),
-    ("w4a8", 64, 256, 1024, dict(kernel=2)),
-    ("w4a8", 32, 512, 2048, dict(kernel=2)),
+    ("fp8", 32, 512, 2048, dict(kernel=2, tile_m=32)),
+    ("fp8", 64, 256, 1024, dict(kernel=2, tile_m=64)),
+    ("fp8", 48, 512, 2048, dict(kernel=2, tile_m=64)),
+    ("bf16", 64, 256, 512, dict(kernel=2, tile_m=32)),
+    ("int8", 64, 256, 2048, dict(kernel=2, tile_m=32)),
+    ("mxfp4", 64, 256, 1024, dict(kernel=2, tile_m=32)),
+    ("fp16", 32, 256, 512, dict(kernel=2, tile_m=32)),
+    ("w4a8", 64, 256, 1024, dict(kernel=2, tile_m=32)),
+    ("w4a8", 32, 512, 2048, dict(kernel=2, tile_m=32)),
     ("fp8", 64, 512, 2048, dict(kernel=2, tile_m=16)),
     ("fp8", 64, 512, 2048, dict(kernel=2, tile_m=32)),
-    ("int8", 48, 256, 2048, dict(kernel=2)),                 # 4 row blocks on 8 waves, last one empty
-    ("bf16", 64, 512, 4096, dict(kernel=2)),
-    ("w4a8", 40, 512, 2048, dict(kernel=2)),
+    ("int8", 48, 256, 2048, dict(kernel=2, tile_m=64)),      # 4 row blocks on 8 waves, last one empty
+    ("bf16", 64, 512, 4096, dict(kernel=2, tile_m=64)),
+    ("w4a8", 40, 512, 2048, dict(kernel=2, tile_m=64)),
+    # the planner's own row blocks (16 rows on few columns; 32 on 4096; 64 on 7168)
+    ("fp8", 64, 1024, 2048, dict(kernel=2)),
+    ("bf16", 40, 1024, 2048, dict(kernel=2)),
+    ("int8", 64, 4096, 1024, dict(kernel=2)),
+    ("mxfp4", 33, 1024, 7168, dict(kernel=2)),                # 128-byte chunks (7 per wave)
+    ("w4a8", 64, 7168, 512, dict(kernel=2)),
     # W4A8 on the tile kernel (tile_k in INT4 elements; A tiles twice the B bytes)
     ("w4a8", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128, pipeline=3)),
     ("w4a8", 256, 512, 1024, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128)),
