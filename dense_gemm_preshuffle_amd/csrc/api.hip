@@ -299,6 +299,16 @@ int pick_chunk(int dt, int nb, int waves, int mb, int64_t kw) {
   return kch;
 }
 
+// Bytes the busiest CU pulls for a small-M plan of mb 16-row and nb 16-column
+// blocks per workgroup: its ceil(grid / 256) rounds of workgroups, each
+// reading its B columns over the whole K and half of its A rows (A comes from
+// L2, at about half the cost per byte on the M=16 shape).
+double small_m_cost(int dt, int64_t M, int64_t N, int64_t Kb, int mb, int nb) {
+  const int64_t Ka = Kb * (dt == DT_I4 ? 2 : 1), rows = std::min<int64_t>(M, 16 * mb);
+  const int64_t grid = (N / (16 * nb)) * ((M + 16 * mb - 1) / (16 * mb));
+  return (double)((grid + 255) / 256) * ((double)(16 * nb) * Kb + 0.5 * (double)rows * Ka);
+}
+
 int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, const gemm_opts* o) {
   if (o && o->tile_n > 0 && o->tile_n % 16) return GP_ESHAPE;
   if (o && o->tile_m > 0 && o->tile_m != 16 && o->tile_m != 32 && o->tile_m != 64) return GP_ESHAPE;
@@ -340,7 +350,6 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
   int nbc[2] = {2, 1};
   int nn = 2;
   if (o && o->tile_n > 0) { nbc[0] = o->tile_n / 16; nn = 1; }
-  const int64_t Ka = Kb * (dt == DT_I4 ? 2 : 1);
   // the chunk (K bytes per wave step) of one (waves, mb, nb), 0 if not compiled
   auto chunk = [&](int waves, int mb, int nb) {
     if (Kb % waves || N % (16 * nb)) return 0;
@@ -356,9 +365,7 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
       const int nb = nbc[c];
       const int kch = chunk(waves, mb, nb);
       if (!kch) continue;
-      const int64_t rows = std::min<int64_t>(M, 16 * mb);
-      const int64_t grid = (N / (16 * nb)) * ((M + 16 * mb - 1) / (16 * mb));
-      const double cost = (double)((grid + 255) / 256) * ((double)(16 * nb) * Kb + 0.5 * (double)rows * Ka);
+      const double cost = small_m_cost(dt, M, N, Kb, mb, nb);
       if (best >= 0 && cost >= best) continue;
       best = cost;
       p->nb = nb;
@@ -516,24 +523,30 @@ int choose_wide(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, con
 }
 
 // 16 to 64 rows and long K, called with a workspace: 16 x 64 tiles (A
-// through registers) whose K tiles are split across workgroups, instead of
-// the small-M kernel, whose workgroups each stream a whole K range of 16 or
-// 32 columns for every row (N / 16 or N / 32 of them: few where N is small).
-// S is the largest power of two that keeps at least 2048 bytes of B's K per
-// range and at most 256 workgroups, taken where B's rows hold at least 8192
-// bytes (FP8) or 16384 (INT8, BF16, FP16, W4A8) and S is 4 or more (2 or
-// more with more than 16 rows). Measured (one MI355X, graph replay, rotating
-// inputs; small-M kernel -> split tiles): FP8 16 x 2048 x 16384 15.9 -> 11.5
-// us (S = 8), 16 x 1024 x 32768 28.5 -> 14.9, 16 x 512 x 32768 28.0 -> 12.0,
-// 16 x 2048 x 8192 9.1 -> 8.3, 32 x 2048 x 16384 22.6 -> 12.1 (S = 4), 64 x
-// 1024 x 16384 36.5 -> 11.1, 64 x 2048 x 16384 36.8 -> 16.4 (S = 2), 48 x
-// 1024 x 32768 60.4 -> 17.1, 32 x 4096 x 8192 12.8 -> 11.8; INT8 16 x 2048 x
-// 16384 15.2 -> 11.8, 64 x 2048 x 16384 37.5 -> 22.3; BF16 16 x 1024 x
-// 16384 27.3 -> 15.2, 64 x 1024 x 16384 72.9 -> 22.8; W4A8 16 x 1024 x
-// 32768 19.0 -> 15.9. Below those K the split lost at 16 rows (FP8 16 x 2048
-// x 7168 8.8 against 8.2, INT8 16 x 2048 x 8192 9.3 against 8.6, BF16 16 x
-// 2048 x 4096 9.4 against 8.8, W4A8 16 x 2048 x 16384 11.2 against 10.8).
-bool small_m_long_k(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
+// through registers) whose K tiles are split across workgroups, in place of
+// the small-M plan sm (null if that kernel cannot take the shape). S is the
+// largest power of two that keeps at least 2048 bytes of B's K per range and
+// at most 256 workgroups; taken where B's rows hold at least 8192 bytes (FP8)
+// or 16384 (INT8, BF16, FP16, W4A8), S is 4 or more at 16 rows (2 or more
+// above), and the busiest CU's bytes on the split (counted as for the
+// small-M kernel) are at most a fraction of the small-M plan's: 0.8 (FP8
+// from 16384 bytes of K: 0.95), W4A8 0.5. The small-M kernel streams more
+// bytes per second per CU than the split tiles, whose partial sums and last
+// arrivals cost too, so the split wins only where it cuts the bytes by that
+// much: where the small-M plan takes one column block per workgroup (its A
+// read once per 16 columns, ratio 0.38-0.75 here), not two (0.9; 0.83 for
+// W4A8). Measured (one MI355X, graph replay, rotating inputs; small-M ->
+// split): FP8 16 x 2048 x 16384 15.9 -> 11.5 us, 16 x 1024 x 32768 28.4 ->
+// 14.9, 64 x 1024 x 16384 15.6 -> 11.2, 33 x 2048 x 32768 (ratio 0.9) 33.5
+// -> 27.9 but 33 x 2048 x 8192 9.6 -> 10.1 (so not taken); INT8 24 x 1024 x
+// 32768 26.0 -> 15.6, 33 x 2048 x 16384 16.9 -> 22.1 (ratio 0.9, not
+// taken); BF16 16 x 1024 x 16384 27.3 -> 15.2, 64 x 2048 x 8192 16.3 ->
+// 22.2 (not taken); W4A8 16 x 1024 x 65536 35.7 -> 19.6 (ratio 0.16), 33 x
+// 1024 x 32768 19.0 -> 23.4 (0.62, not taken). Below those K the split lost
+// at 16 rows (FP8 16 x 2048 x 7168 8.8 against 8.2, INT8 16 x 2048 x 8192
+// 9.3 against 8.6, BF16 16 x 2048 x 4096 9.4 against 8.8, W4A8 16 x 2048 x
+// 16384 11.2 against 10.8).
+bool small_m_long_k(int dt, int64_t M, int64_t N, int64_t Kb, const Plan* sm, Plan* p) {
   if (M < 16 || M > 64 || N < 64 || dt == DT_FP4) return false;
   const int tkb = dt == DT_FP8 ? 512 : dt == DT_I4 ? 128 : 256;   // 512 bytes of A per K tile (W4A8: 256)
   if (Kb < (dt == DT_FP8 ? 8192 : 16384) || Kb % tkb) return false;
@@ -545,6 +558,12 @@ bool small_m_long_k(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
     S = s;
   }
   if (S < (M <= 16 ? 4 : 2)) return false;
+  if (sm) {
+    const int64_t Ka = Kb * (dt == DT_I4 ? 2 : 1);
+    const double split = (double)((T * S + 255) / 256) * (double)(64 * Kb + 8 * Ka) / S;
+    const double bound = dt == DT_I4 ? 0.5 : (dt == DT_FP8 && Kb >= 16384) ? 0.95 : 0.8;
+    if (split > bound * small_m_cost(dt, M, N, Kb, sm->mb, sm->nb)) return false;
+  }
   p->kernel = GP_KERNEL_TILE;
   p->ms = 16;
   p->tm = 16;
@@ -599,8 +618,13 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   if (dt == DT_I4 && p->kernel == GP_KERNEL_WIDE) return GP_EDTYPE;   // no 256 x 256 W4A8 kernel
   // a K split and the scheduler-off variants exist on the tile kernel only
   if (o && (o->ksplit > 1 || o->scheduler == 2) && p->kernel != GP_KERNEL_TILE) return GP_ESHAPE;
-  if (p->kernel == GP_KERNEL_SPLITK && !o && ws && small_m_long_k(dt, M, N, Kb, p)) return GP_OK;
-  if (p->kernel == GP_KERNEL_SPLITK) return choose_split(dt, bits, M, N, Kb, p, o);
+  if (p->kernel == GP_KERNEL_SPLITK) {
+    Plan sm = *p;
+    const int rc = choose_split(dt, bits, M, N, Kb, &sm, o);
+    if (!o && ws && small_m_long_k(dt, M, N, Kb, rc == GP_OK ? &sm : nullptr, p)) return GP_OK;
+    *p = sm;
+    return rc;
+  }
   if (p->kernel == GP_KERNEL_WIDE) return choose_wide(dt, bits, M, N, Kb, p, o);
 
   const bool user_tile = o && (o->tile_m || o->tile_n || o->tile_k);

@@ -282,7 +282,8 @@ int gemm_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* op
  * the split lets a larger tile (fewer operand bytes per FLOP) fill the GPU
  * instead of a smaller one; and for 16 to 64 rows with long K, where 16 x 64
  * tiles split along K replace the small-M kernel (FP8 from 8192 bytes per B
- * row, INT8 / BF16 / FP16 / W4A8 from 16384; not MXFP4).
+ * row, INT8 / BF16 / FP16 / W4A8 from 16384; not MXFP4) if they cut the
+ * bytes the busiest CU reads enough to pay for the split.
  *   workspace        device, 16-byte aligned, at least gemm_workspace_size
  *                    bytes for the same arguments (ignored, and may be NULL,
  *                    when that size is 0). Its first 64 KiB hold one arrival

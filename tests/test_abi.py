@@ -518,8 +518,9 @@ def test_planner_splits_long_k_at_16_to_64_rows_over_16x64_tiles():
     K into the largest power of two of ranges that keeps 2048 bytes of B's K
     per range and at most 256 workgroups (4 or more at 16 rows, 2 or more
     above), from 8192 bytes per B row for FP8 and 16384 for INT8, BF16, FP16
-    and W4A8; not without a workspace, not for shorter K, not for other row
-    counts, not for MXFP4."""
+    and W4A8, where the busiest CU's bytes fall to 0.8 of the small-M plan's
+    or less (FP8 from 16384 bytes: 0.95; W4A8: 0.5); not without a
+    workspace, not for shorter K, not for other row counts, not for MXFP4."""
     p = gp.gemm_plan_ws("fp8", 16, 2048, 16384)
     assert (p["kernel"], p["tile_m"], p["tile_n"], p["tile_k"], p["ksplit"], p["grid"]) == (1, 16, 64, 512, 8, 256)
     assert gp.gemm_plan_ws("fp8", 16, 1024, 32768)["ksplit"] == 16
@@ -532,7 +533,7 @@ def test_planner_splits_long_k_at_16_to_64_rows_over_16x64_tiles():
     # above 16 rows: ceil(M / 16) * ceil(N / 64) tiles, 2 or more ranges
     for M, N, K, S in ((32, 2048, 16384, 4), (64, 1024, 16384, 4), (64, 2048, 16384, 2),
                        (48, 1024, 32768, 4), (40, 2048, 16384, 2), (17, 2048, 16384, 4),
-                       (32, 4096, 8192, 2)):
+                       (64, 1024, 8192, 4)):
         q = gp.gemm_plan_ws("fp8", M, N, K)
         assert (q["kernel"], q["tile_m"], q["tile_n"], q["ksplit"]) == (1, 16, 64, S), (M, N, K, q)
         assert q["grid"] == -(-M // 16) * -(-N // 64) * S
@@ -540,7 +541,15 @@ def test_planner_splits_long_k_at_16_to_64_rows_over_16x64_tiles():
     assert gp.gemm_plan_ws("fp8", 32, 2048, 7168)["kernel"] == 2          # K too short
     assert gp.gemm_plan_ws("fp8", 65, 2048, 16384)["tile_m"] != 16        # past 64 rows: the tile planner's own choice
     assert gp.gemm_plan("fp8", 64, 2048, 16384)["kernel"] == 2            # no workspace
-    assert gp.gemm_plan_ws("int8", 64, 2048, 16384)["ksplit"] == 2
+    # the small-M plan takes two column blocks per workgroup (A read once per
+    # 32 columns): the split's bytes are 0.9 of its, not enough below 16384
+    # bytes of K for FP8, nor at all for INT8; W4A8 needs 0.5
+    assert gp.gemm_plan_ws("fp8", 32, 4096, 8192)["kernel"] == 2
+    assert gp.gemm_plan_ws("fp8", 64, 2048, 8192)["kernel"] == 2
+    assert gp.gemm_plan_ws("int8", 64, 2048, 16384)["kernel"] == 2
+    assert gp.gemm_plan_ws("int8", 64, 1024, 16384)["ksplit"] == 4
+    assert gp.gemm_plan_ws("w4a8", 33, 1024, 32768)["kernel"] == 2
+    assert gp.gemm_plan_ws("w4a8", 24, 1024, 32768)["ksplit"] == 8
     assert gp.gemm_plan_ws("bf16", 64, 1024, 16384)["ksplit"] == 4
     assert gp.gemm_plan_ws("bf16", 32, 2048, 4096)["kernel"] == 2
     q = gp.gemm_plan_ws("int8", 16, 2048, 16384)

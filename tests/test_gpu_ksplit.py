@@ -164,9 +164,9 @@ def test_scheduler_off_parity(dtype, M, N, K, opts):
                                          # 17 to 64 rows: ceil(M / 16) row tiles of 16 (M = 40, 17: the last
                                          # row tile overlaps its neighbour)
                                          ("fp8", 48, 1024, 32768), ("fp8", 40, 2048, 16384),
-                                         ("fp8", 17, 1008, 16384), ("int8", 64, 2048, 16384),
+                                         ("fp8", 17, 1008, 16384), ("int8", 64, 1024, 16384),
                                          ("bf16", 32, 2048, 8192), ("fp16", 64, 1024, 16384),
-                                         ("w4a8", 33, 1024, 32768)])
+                                         ("w4a8", 24, 1024, 32768)])
 def test_automatic_split_parity(dtype, M, N, K):
     """The planner's own split (no options) on long-K shapes, every output."""
     import dense_gemm_preshuffle_amd as gp
