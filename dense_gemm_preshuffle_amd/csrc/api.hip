@@ -578,6 +578,42 @@ bool small_m_long_k(int dt, int64_t M, int64_t N, int64_t Kb, const Plan* sm, Pl
   return true;
 }
 
+// Above 64 rows the small-M kernel still beats the tile planner where the
+// output is small: its workgroups re-read B once per 64 rows but stream it
+// at a higher rate per CU, while the tiles of a small output leave CUs idle
+// or split K at a cost. A rule per type on M x N and M x N x K, fitted to 216
+// shapes per type (M 80-512, N 512-7168, K 1024-7168; one MI355X, graph
+// replay, gemm_ex_ws plans on both sides; held-out halves of the shapes kept
+// 97-100% of the better kernel's gain) and checked on 130 more (N 128-512 up
+// to M = 4096, K up to 16384, M = 65 and 72). Summed over the 216, tile
+// planner -> with the rule (the better kernel per shape): W4A8 3257 -> 2120
+// (2120) us, MXFP4 2589 -> 2221 (2213), INT8 2483 -> 2279 (2264), BF16 4122
+// -> 3873 (3836), FP16 4376 -> 4160 (4106), FP8 2211 -> 2176 (2160); e.g.
+// W4A8 128 x 1024 x 7168 22.9 -> 4.9 us, BF16 128 x 2048 x 4096 17.0 ->
+// 12.5, INT8 128 x 1024 x 4096 8.5 -> 5.5, W4A8 2048 x 256 x 7168 1.8x.
+// Past 8192 columns of K the tiles' own K split wins for FP8, BF16, FP16 and
+// INT8 (FP8 128 x 512 x 16384 11.0 us on split tiles against 15.3), not for
+// W4A8 and MXFP4 (MXFP4 128 x 512 x 16384 14.2 against 44.3); below 1024 the
+// two are within the noise of a 3 us launch.
+bool small_m_above_64(int dt, int64_t M, int64_t N, int64_t K) {
+  if (M <= 64 || M > 4096 || K < 1024) return false;
+  const double mn = (double)M * N, mnk = mn * (double)K;
+  if (dt == DT_I4 || dt == DT_FP4) return mn <= (double)(1 << 19);
+  if (K > 8192) return false;
+  switch (dt) {
+    case DT_I8: return mn <= (double)(3 << 18) && mnk <= 3.0 * (double)(1 << 29);
+    case DT_BF16:
+    case DT_F16: return mn <= (double)(3 << 18) && mnk <= (double)(1 << 30);
+    default: return mn <= (double)(1 << 17) && mnk <= (double)(1 << 30);   // FP8
+  }
+}
+
+// no option set: the planner chooses everything
+bool no_options(const gemm_opts* o) {
+  return !o || !(o->tile_m || o->tile_n || o->tile_k || o->epilogue || o->kernel || o->xcd_swizzle || o->waves ||
+                 o->mfma || o->pipeline || o->ksplit || o->scheduler);
+}
+
 // ws: the call brings a workspace (gemm_ex_ws), so the tile kernel may split
 // K across workgroups.
 int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o, Plan* p, bool ws = false) {
@@ -611,10 +647,11 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   p->Kb = Kb;
   // small M (up to 64 rows): the split-K kernel; on 64 x 7168 x 2048 it
   // measured FP8 7.7 vs 8.1 us on tiles, INT8 7.1 vs 7.9, BF16 11.8 vs 20.8,
-  // MXFP4 7.2 vs 9.4, W4A8 7.3 vs 11.9; at M = 128 the tiles are as fast or
-  // faster (FP8 12.7 vs 13.2)
+  // MXFP4 7.2 vs 9.4, W4A8 7.3 vs 11.9; at M = 128 on that N the tiles are as
+  // fast or faster (FP8 12.7 vs 13.2). Above 64 rows, small outputs.
   const int64_t small_m = 64;
-  p->kernel = (o && o->kernel) ? o->kernel : (M <= small_m ? GP_KERNEL_SPLITK : GP_KERNEL_TILE);
+  const bool small_above = no_options(o) && small_m_above_64(dt, M, N, K);
+  p->kernel = (o && o->kernel) ? o->kernel : (M <= small_m || small_above ? GP_KERNEL_SPLITK : GP_KERNEL_TILE);
   if (dt == DT_I4 && p->kernel == GP_KERNEL_WIDE) return GP_EDTYPE;   // no 256 x 256 W4A8 kernel
   // a K split and the scheduler-off variants exist on the tile kernel only
   if (o && (o->ksplit > 1 || o->scheduler == 2) && p->kernel != GP_KERNEL_TILE) return GP_ESHAPE;
@@ -622,8 +659,11 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     Plan sm = *p;
     const int rc = choose_split(dt, bits, M, N, Kb, &sm, o);
     if (!o && ws && small_m_long_k(dt, M, N, Kb, rc == GP_OK ? &sm : nullptr, p)) return GP_OK;
-    *p = sm;
-    return rc;
+    if (rc == GP_OK || !small_above) {
+      *p = sm;
+      return rc;
+    }
+    p->kernel = GP_KERNEL_TILE;   // the small-M kernel cannot take it: the tile planner's choice
   }
   if (p->kernel == GP_KERNEL_WIDE) return choose_wide(dt, bits, M, N, Kb, p, o);
 

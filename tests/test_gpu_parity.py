@@ -220,6 +220,13 @@ TILE_CASES = [
     ("int8", 64, 4096, 1024, dict(kernel=2)),
     ("mxfp4", 33, 1024, 7168, dict(kernel=2)),                # 128-byte chunks (7 per wave)
     ("w4a8", 64, 7168, 512, dict(kernel=2)),
+    # above 64 rows, small outputs: the planner's small-M plan (ragged last row blocks)
+    ("w4a8", 200, 1024, 2048, dict()),
+    ("mxfp4", 640, 256, 2048, dict()),
+    ("int8", 130, 1024, 1024, dict()),
+    ("bf16", 96, 2048, 1024, dict()),
+    ("fp16", 257, 512, 2048, dict()),
+    ("fp8", 100, 1024, 2048, dict()),
     # W4A8 on the tile kernel (tile_k in INT4 elements; A tiles twice the B bytes)
     ("w4a8", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128, pipeline=3)),
     ("w4a8", 256, 512, 1024, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128)),
@@ -336,11 +343,13 @@ EPI_CASES = [
     ("bf16", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64, pipeline=0, waves=8)),
     ("w4a8", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128)),
     ("w4a8", 150, 400, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=128, epilogue=1)),
+    ("bf16", 96, 1024, 2048, dict()),                                # the planner's small-M plan above 64 rows
+    ("w4a8", 130, 512, 4096, dict()),
 ]
 
 
 @pytest.mark.parametrize("act", ["none", "relu", "silu", "gelu"])
-@pytest.mark.parametrize("case", EPI_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-k{c[4]['kernel']}")
+@pytest.mark.parametrize("case", EPI_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-k{c[4].get('kernel', 0)}")
 def test_fused_epilogue_parity(case, act):
     dtype, M, N, K, opts = case
     say(f"epilogue {act} {dtype} {M}x{N}x{K} {opts}")
@@ -408,7 +417,7 @@ PERM_CASES = [("int8", 128, 256, 256, dict(kernel=1, tile_m=64, tile_n=256, tile
               ("w4a8", 128, 512, 512, dict(kernel=1, tile_m=128, tile_n=256, tile_k=128))]
 
 
-@pytest.mark.parametrize("case", PERM_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-k{c[4]['kernel']}")
+@pytest.mark.parametrize("case", PERM_CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-k{c[4].get('kernel', 0)}")
 def test_permutation_b_bit_exact(case):
     dtype, M, N, K, opts = case
     say(f"perm {dtype} {M}x{N}x{K}")

@@ -27,7 +27,7 @@ def test_noalloc_matches_caller_workspace_twice(dtype):
     from dense_gemm_preshuffle_amd import workload
 
     lib = gp.load_library()
-    shapes = {"fp8": [(256, 2048, 16384), (128, 2048, 8192)], "bf16": [(256, 1024, 8192), (128, 1024, 8192)]}[dtype]
+    shapes = {"fp8": [(256, 2048, 16384), (128, 2048, 8192)], "bf16": [(256, 1024, 8192), (192, 1024, 8192)]}[dtype]
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for M, N, K in shapes:
         plan = gp.gemm_plan_ws(dtype, M, N, K)
