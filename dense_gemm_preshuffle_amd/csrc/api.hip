@@ -462,6 +462,20 @@ void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
     ksplit_larger_tile(dt, M, N, Kb, p, 4, 3);
     return;
   }
+  // FP8 on its 64 x 128 tile (one MI355X, 266 shapes, M 80-1024, K 4096-16384,
+  // against the rule alone): four ranges where the tiles number 48 to 64 and
+  // K holds at least 4096 bytes (1024 or more per range), e.g. 128 x 3072 x
+  // 4096 10.6 us against 12.7 on 16 x 64 tiles in two, 256 x 2048 x 7168
+  // 13.7 against 16.5 in two; and no more than 256 workgroups where halving
+  // S keeps at least 168 of them, e.g. 160 x 4096 x 8192 18.7 us in 192
+  // workgroups against 22.4 in 384, 128 x 7168 x 8192 22.2 in 224 against
+  // 24.9 in 448, 384 x 7168 x 4096 unsplit 21.5 against 26.0 in 672 (but 384
+  // x 3072 x 16384 41.4 in 288 against 48.4 in 144, so not below 168), nor
+  // below two ranges past 8192 bytes of K (160 x 7168 x 16384 50.9 us in two
+  // against 52.7 unsplit); four ranges not where the 64-row tiles cover more
+  // than 1.5 M (80 x 3072 x 4096 10.5 against 9.4). Not for 16 x 64 tiles,
+  // whose splits into 320-384 workgroups measured faster than half as many
+  // (192 x 1024 x 7168 11.0 against 12.2).
   int best = -1, best_s = 0;
   for (int i = 0; i < (int)(sizeof(kKSplit) / sizeof(kKSplit[0])); ++i) {
     const TileVar& v = kKSplit[i];
@@ -473,6 +487,13 @@ void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
       if (KT % S || Kb / S < 2048) break;
       s_pick = S;
       if (T * S >= 256) break;
+    }
+    if (dt == DT_FP8 && v.tm == 64 && v.tn == 128) {
+      const bool rows_fit = ((M + 63) / 64) * 64 * 2 <= M * 3;   // the 64-row tiles cover at most 1.5 M
+      if (T >= 48 && T <= 64 && rows_fit && Kb >= 4096 && KT % 4 == 0 && s_pick < 4) s_pick = 4;
+      const int s_min = Kb > 8192 ? 2 : 1;
+      while (s_pick > s_min && T * s_pick > 256 && T * (s_pick / 2) >= 168) s_pick /= 2;
+      if (s_pick == 1) return;   // the unsplit plan
     }
     if (!s_pick || T * s_pick < 128) continue;
     best = i;

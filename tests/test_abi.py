@@ -358,6 +358,19 @@ def test_small_m_row_blocks(dtype):
     assert q["tile_m"] == 16
 
 
+def test_fp8_split_on_64x128_tiles():
+    """FP8's automatic split on 64 x 128 tiles: four ranges where 48 to 64
+    tiles cover the output (rows at most 1.5 M, K from 4096 bytes), and no
+    more than 256 workgroups where halving the split keeps 168 or more (not
+    below two ranges past 8192 bytes of K)."""
+    for M, N, K, tile, ks, grid in [(128, 3072, 4096, (64, 128), 4, 192), (256, 2048, 7168, (64, 128), 4, 256),
+                                    (160, 4096, 8192, (64, 128), 2, 192), (128, 7168, 8192, (64, 128), 2, 224),
+                                    (160, 7168, 16384, (64, 128), 2, 336), (384, 3072, 16384, (64, 128), 2, 288),
+                                    (384, 7168, 4096, (128, 128), 1, 168), (80, 3072, 4096, (16, 64), 2, 480)]:
+        p = gp.gemm_plan_ws("fp8", M, N, K)
+        assert ((p["tile_m"], p["tile_n"]), p["ksplit"], p["grid"]) == (tile, ks, grid), (M, N, K, p)
+
+
 def test_small_m_kernel_above_64_rows_on_small_outputs():
     """Above 64 rows the planner still takes the small-M kernel where the
     output is small: W4A8 / MXFP4 up to M*N = 2^19 (any K); INT8 up to
