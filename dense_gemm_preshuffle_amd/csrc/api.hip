@@ -462,6 +462,21 @@ void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
     ksplit_larger_tile(dt, M, N, Kb, p, 4, 3);
     return;
   }
+  // BF16 / FP16 skip their 128 x 256 split tile here for the 64 x 128 one
+  // where fewer than 32 of the large tiles cover the output (from 32 the
+  // large tile held its own: 256 x 4096 x 16384 62.0 us against 63.3, 384 x
+  // 4096 x 8192 43.5 against 49.8), and from 64 small tiles take twice the
+  // ranges up to 512 workgroups (one
+  // MI355X, M 128-384, N 1024-4096, K 4096-16384): BF16 128 x 2048 x 16384
+  // 32.4 us on 64 x 128 in eight ranges against 54.0 on 128 x 256 in eight,
+  // 384 x 2048 x 16384 52.2 in four against 83.9, 256 x 4096 x 8192 37.2 in
+  // four (512 workgroups) against 46.4 in two, 128 x 4096 x 8192 28.4 in
+  // eight against 29.9 in four; not on 128 workgroups, where 16 x 64 tiles
+  // in more took less (FP16 80 x 512 x 16384 15.9 us on 320 against 23.1,
+  // 256 x 1024 x 7168 21.5 on 512 against 24.9). INT8 on its 64 x 128 tile
+  // as FP8 (below):
+  // 192 x 2048 x 4096 10.5 us in four against 11.4, 384 x 1024 x 16384 19.5
+  // in four (192 workgroups) against 23.2 in eight (384).
   // FP8 on its 64 x 128 tile (one MI355X, 266 shapes, M 80-1024, K 4096-16384,
   // against the rule alone): four ranges where the tiles number 48 to 64 and
   // K holds at least 4096 bytes (1024 or more per range), e.g. 128 x 3072 x
@@ -480,6 +495,8 @@ void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
   for (int i = 0; i < (int)(sizeof(kKSplit) / sizeof(kKSplit[0])); ++i) {
     const TileVar& v = kKSplit[i];
     if (v.dt != dt || v.tm > M || v.tn > N || Kb % v.tkb) continue;
+    const bool half = dt == DT_BF16 || dt == DT_F16;
+    if (half && v.tm == 128 && v.tn == 256 && ((M + 127) / 128) * ((N + 255) / 256) < 32) continue;
     const int64_t T = ((M + v.tm - 1) / v.tm) * ((N + v.tn - 1) / v.tn);
     const int64_t KT = Kb / v.tkb;
     int s_pick = 0;
@@ -488,14 +505,17 @@ void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
       s_pick = S;
       if (T * S >= 256) break;
     }
-    if (dt == DT_FP8 && v.tm == 64 && v.tn == 128) {
+    if (half && v.tm == 64 && v.tn == 128 && T >= 64 && s_pick && T * s_pick <= 256 && T * s_pick * 2 <= 512 &&
+        KT % (s_pick * 2) == 0 && Kb / (s_pick * 2) >= 2048)
+      s_pick *= 2;
+    if ((dt == DT_FP8 || dt == DT_I8) && v.tm == 64 && v.tn == 128) {
       const bool rows_fit = ((M + 63) / 64) * 64 * 2 <= M * 3;   // the 64-row tiles cover at most 1.5 M
       if (T >= 48 && T <= 64 && rows_fit && Kb >= 4096 && KT % 4 == 0 && s_pick < 4) s_pick = 4;
       const int s_min = Kb > 8192 ? 2 : 1;
       while (s_pick > s_min && T * s_pick > 256 && T * (s_pick / 2) >= 168) s_pick /= 2;
       if (s_pick == 1) return;   // the unsplit plan
     }
-    if (!s_pick || T * s_pick < 128) continue;
+    if (!s_pick || T * s_pick < (half && v.tm == 64 && v.tn == 128 ? 144 : 128)) continue;
     best = i;
     best_s = s_pick;
     break;

@@ -127,7 +127,7 @@
 #define GP_TILE_KSPLIT_FP8(X) X(DT_FP8, 16, 64, 128, 256, 3) X(DT_FP8, 16, 64, 256, 128, 3) X(DT_FP8, 16, 16, 64, 512, 0) \
   X(DT_FP8, 16, 32, 256, 256, 3) X(DT_FP8, 16, 128, 128, 128, 3) X(DT_FP8, 16, 128, 128, 256, 3)
 #define GP_TILE_KSPLIT_BF16(X) X(DT_BF16, 16, 128, 256, 128, 3) X(DT_BF16, 16, 64, 128, 128, 0) X(DT_BF16, 16, 16, 64, 256, 0)
-#define GP_TILE_KSPLIT_F16(X) X(DT_F16, 16, 128, 256, 128, 3) X(DT_F16, 16, 16, 64, 256, 0)
+#define GP_TILE_KSPLIT_F16(X) X(DT_F16, 16, 128, 256, 128, 3) X(DT_F16, 16, 64, 128, 128, 0) X(DT_F16, 16, 16, 64, 256, 0)
 #define GP_TILE_KSPLIT_FP4(X) X(DT_FP4, 32, 128, 128, 128, 0) X(DT_FP4, 32, 128, 256, 128, 2)
 #define GP_TILE_KSPLIT_I4(X) X(DT_I4, 16, 64, 128, 128, 3) X(DT_I4, 16, 64, 256, 64, 3) X(DT_I4, 16, 16, 64, 128, 0)
 #define GP_TILE_KSPLIT_ALL(X) GP_TILE_KSPLIT_I8(X) GP_TILE_KSPLIT_FP8(X) GP_TILE_KSPLIT_BF16(X) \

@@ -358,6 +358,22 @@ def test_small_m_row_blocks(dtype):
     assert q["tile_m"] == 16
 
 
+def test_half_and_int8_split_on_64x128_tiles():
+    """BF16 / FP16 split 64 x 128 tiles (not 128 x 256 where fewer than 32
+    of those cover the output), in twice the ranges from 64 tiles up to 512
+    workgroups, and only from 144 workgroups (else 16 x 64 tiles); INT8
+    takes FP8's four-range and 256-workgroup rules."""
+    for dt, M, N, K, tile, ks, grid in [("bf16", 128, 2048, 16384, (64, 128), 8, 256),
+                                        ("bf16", 256, 2048, 8192, (64, 128), 8, 512),
+                                        ("fp16", 192, 2048, 8192, (64, 128), 8, 384),
+                                        ("fp16", 320, 512, 8192, (64, 128), 8, 160),
+                                        ("bf16", 80, 512, 16384, (16, 64), 8, 320),
+                                        ("bf16", 512, 2048, 16384, (128, 256), 8, 256),
+                                        ("int8", 192, 2048, 8192, (64, 128), 4, 192)]:
+        p = gp.gemm_plan_ws(dt, M, N, K)
+        assert ((p["tile_m"], p["tile_n"]), p["ksplit"], p["grid"]) == (tile, ks, grid), (dt, M, N, K, p)
+
+
 def test_fp8_split_on_64x128_tiles():
     """FP8's automatic split on 64 x 128 tiles: four ranges where 48 to 64
     tiles cover the output (rows at most 1.5 M, K from 4096 bytes), and no

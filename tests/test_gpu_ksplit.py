@@ -57,6 +57,8 @@ KSPLIT_CASES = [
     ("bf16", 256, 512, 1024, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, ksplit=4)),
     ("bf16", 128, 256, 512, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64, ksplit=2)),
     ("fp16", 256, 512, 1024, dict(kernel=1, tile_m=128, tile_n=256, tile_k=64, ksplit=2)),
+    ("fp16", 192, 384, 2048, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64, ksplit=8)),
+    ("fp16", 100, 208, 1024, dict(kernel=1, tile_m=64, tile_n=128, tile_k=64, ksplit=4)),   # ragged M, N
     # MXFP4: 8-tile scale groups; a split of 16 K tiles into 2 (whole groups)
     # and 4 (half groups: each range starts inside its first group's row)
     ("mxfp4", 128, 256, 4096, dict(kernel=1, tile_m=128, tile_n=256, tile_k=256, ksplit=2)),
@@ -166,7 +168,9 @@ def test_scheduler_off_parity(dtype, M, N, K, opts):
                                          ("fp8", 48, 1024, 32768), ("fp8", 40, 2048, 16384),
                                          ("fp8", 17, 1008, 16384), ("int8", 64, 1024, 16384),
                                          ("bf16", 32, 2048, 8192), ("fp16", 64, 1024, 16384),
-                                         ("w4a8", 24, 1024, 32768)])
+                                         ("w4a8", 24, 1024, 32768),
+                                         # 64 x 128 tiles: BF16 / FP16 in 2x the ranges from 64 tiles, INT8 in four
+                                         ("bf16", 256, 2048, 8192), ("fp16", 192, 2048, 8192), ("int8", 192, 2048, 8192)])
 def test_automatic_split_parity(dtype, M, N, K):
     """The planner's own split (no options) on long-K shapes, every output."""
     import dense_gemm_preshuffle_amd as gp
@@ -208,7 +212,8 @@ def test_one_workspace_serves_shapes_of_any_size():
                                              ("bf16", 512, 4096, 16384, "relu"), ("mxfp4", 256, 4096, 16384, "gelu"),
                                              ("w4a8", 256, 4096, 8192, "none"), ("fp16", 256, 4096, 8192, "silu"),
                                              ("bf16", 16, 2048, 8192, "relu"), ("w4a8", 16, 1024, 32768, "gelu"),
-                                             ("fp8", 40, 2048, 16384, "silu"), ("bf16", 64, 1024, 16384, "gelu")])
+                                             ("fp8", 40, 2048, 16384, "silu"), ("bf16", 64, 1024, 16384, "gelu"),
+                                             ("fp16", 192, 2048, 8192, "gelu")])
 def test_split_with_fused_epilogue(dtype, M, N, K, act):
     """gemm_ex_ws with a bias and an activation on shapes the planner splits:
     the last workgroup of each tile adds the partial sums, then runs the
