@@ -486,11 +486,18 @@ void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
   // workgroups against 22.4 in 384, 128 x 7168 x 8192 22.2 in 224 against
   // 24.9 in 448, 384 x 7168 x 4096 unsplit 21.5 against 26.0 in 672 (but 384
   // x 3072 x 16384 41.4 in 288 against 48.4 in 144, so not below 168), nor
-  // below two ranges past 8192 bytes of K (160 x 7168 x 16384 50.9 us in two
-  // against 52.7 unsplit); four ranges not where the 64-row tiles cover more
+  // below two ranges past 8192 columns of K (160 x 7168 x 16384 50.9 us in
+  // two against 52.7 unsplit; W4A8 192 x 7168 x 16384 34.9 against 41.8); four ranges not where the 64-row tiles cover more
   // than 1.5 M (80 x 3072 x 4096 10.5 against 9.4). Not for 16 x 64 tiles,
   // whose splits into 320-384 workgroups measured faster than half as many
   // (192 x 1024 x 7168 11.0 against 12.2).
+  // at least 2048 K elements per range: 2048 bytes of B, 1024 for 4-bit B
+  // (MXFP4 384 x 2048 x 8192 16.2 us in four ranges against 23.8 unsplit on
+  // 32 x 256 tiles; W4A8 128 x 7168 x 4096 11.6 in two against 14.2)
+  // MXFP4 / W4A8 take the 256-workgroup rule below as well (MXFP4 192 x 3072
+  // x 16384 22.4 us on 192 workgroups against 29.5 on 384, W4A8 128 x 7168 x
+  // 8192 16.8 on 224 against 19.8 on 448).
+  const int64_t min_kb = (dt == DT_FP4 || dt == DT_I4) ? 1024 : 2048;
   int best = -1, best_s = 0;
   for (int i = 0; i < (int)(sizeof(kKSplit) / sizeof(kKSplit[0])); ++i) {
     const TileVar& v = kKSplit[i];
@@ -501,17 +508,21 @@ void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
     const int64_t KT = Kb / v.tkb;
     int s_pick = 0;
     for (int S = 2; S <= 16; S *= 2) {
-      if (KT % S || Kb / S < 2048) break;
+      if (KT % S || Kb / S < min_kb) break;
       s_pick = S;
       if (T * S >= 256) break;
     }
     if (half && v.tm == 64 && v.tn == 128 && T >= 64 && s_pick && T * s_pick <= 256 && T * s_pick * 2 <= 512 &&
         KT % (s_pick * 2) == 0 && Kb / (s_pick * 2) >= 2048)
       s_pick *= 2;
-    if ((dt == DT_FP8 || dt == DT_I8) && v.tm == 64 && v.tn == 128) {
+    const bool byte_tile = (dt == DT_FP8 || dt == DT_I8) && v.tm == 64 && v.tn == 128;
+    if (byte_tile) {
       const bool rows_fit = ((M + 63) / 64) * 64 * 2 <= M * 3;   // the 64-row tiles cover at most 1.5 M
       if (T >= 48 && T <= 64 && rows_fit && Kb >= 4096 && KT % 4 == 0 && s_pick < 4) s_pick = 4;
-      const int s_min = Kb > 8192 ? 2 : 1;
+    }
+    if (byte_tile || ((dt == DT_FP4 || dt == DT_I4) && v.tm >= 64)) {
+      const int64_t k_elems = (dt == DT_FP4 || dt == DT_I4) ? 2 * Kb : Kb;
+      const int s_min = k_elems > 8192 ? 2 : 1;
       while (s_pick > s_min && T * s_pick > 256 && T * (s_pick / 2) >= 168) s_pick /= 2;
       if (s_pick == 1) return;   // the unsplit plan
     }
@@ -633,14 +644,20 @@ bool small_m_long_k(int dt, int64_t M, int64_t N, int64_t Kb, const Plan* sm, Pl
 // W4A8 128 x 1024 x 7168 22.9 -> 4.9 us, BF16 128 x 2048 x 4096 17.0 ->
 // 12.5, INT8 128 x 1024 x 4096 8.5 -> 5.5, W4A8 2048 x 256 x 7168 1.8x.
 // Past 8192 columns of K the tiles' own K split wins for FP8, BF16, FP16 and
-// INT8 (FP8 128 x 512 x 16384 11.0 us on split tiles against 15.3), not for
-// W4A8 and MXFP4 (MXFP4 128 x 512 x 16384 14.2 against 44.3); below 1024 the
-// two are within the noise of a 3 us launch.
-bool small_m_above_64(int dt, int64_t M, int64_t N, int64_t K) {
+// INT8 (FP8 128 x 512 x 16384 11.0 us on split tiles against 15.3); for W4A8
+// and MXFP4 (whose splits take ranges of 2048 K elements) from M x N x K =
+// 2^31 (MXFP4 128 x 4096 x 8192 15.6 us in four ranges of 128 x 128 tiles
+// against 24.9, but 128 x 1024 x 16384 on the small-M kernel 2.5x faster
+// than split tiles; W4A8 128 x 4096 x 16384 18.6 against 33.4); below 1024
+// the two are within the noise of a 3 us launch.
+// ws: a workspace is at hand, so the tiles may split K (without one the K
+// bounds do not apply: unsplit tiles lose further, e.g. W4A8 384 x 1024 x 7168
+// 34.9 us on 192 unsplit 32 x 64 tiles against 17.6 on the small-M kernel).
+bool small_m_above_64(int dt, int64_t M, int64_t N, int64_t K, bool ws) {
   if (M <= 64 || M > 4096 || K < 1024) return false;
   const double mn = (double)M * N, mnk = mn * (double)K;
-  if (dt == DT_I4 || dt == DT_FP4) return mn <= (double)(1 << 19);
-  if (K > 8192) return false;
+  if (dt == DT_I4 || dt == DT_FP4) return mn <= (double)(1 << 19) && (!ws || mnk <= 2.0 * (double)(1 << 30));
+  if (ws && K > 8192) return false;
   switch (dt) {
     case DT_I8: return mn <= (double)(3 << 18) && mnk <= 3.0 * (double)(1 << 29);
     case DT_BF16:
@@ -691,7 +708,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   // MXFP4 7.2 vs 9.4, W4A8 7.3 vs 11.9; at M = 128 on that N the tiles are as
   // fast or faster (FP8 12.7 vs 13.2). Above 64 rows, small outputs.
   const int64_t small_m = 64;
-  const bool small_above = no_options(o) && small_m_above_64(dt, M, N, K);
+  const bool small_above = no_options(o) && small_m_above_64(dt, M, N, K, ws);
   p->kernel = (o && o->kernel) ? o->kernel : (M <= small_m || small_above ? GP_KERNEL_SPLITK : GP_KERNEL_TILE);
   if (dt == DT_I4 && p->kernel == GP_KERNEL_WIDE) return GP_EDTYPE;   // no 256 x 256 W4A8 kernel
   // a K split and the scheduler-off variants exist on the tile kernel only
@@ -758,6 +775,20 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     p->ks = o->ksplit;
   } else if (ws && !user_tile && p->kg == 1 && !(o && (o->ksplit == 1 || o->pipeline || o->mfma || o->scheduler))) {
     auto_ksplit(dt, M, N, Kb, p);
+  }
+  // W4A8 / MXFP4 past the M x N x K bound of the small-M rule but on fewer
+  // than 128 workgroups of tiles (no split tile fits, e.g. MXFP4 below 128
+  // rows): the small-M kernel (MXFP4 96 x 2048 x 16384 24.5 us against 44.4
+  // on 24 unsplit 32 x 256 tiles)
+  if (no_options(o) && (dt == DT_I4 || dt == DT_FP4) && M > small_m && M <= 4096 && (double)M * N <= (double)(1 << 19) &&
+      tiles_of(*p, M, N) * p->ks < 128) {
+    Plan q;
+    q.kernel = GP_KERNEL_SPLITK;
+    q.Kb = Kb;
+    if (choose_split(dt, bits, M, N, Kb, &q, o) == GP_OK) {
+      *p = q;
+      return GP_OK;
+    }
   }
   // Hot-loop schedule: pinned unless asked otherwise (measured per default
   // tile, one process each: the pinned order was as fast or faster)

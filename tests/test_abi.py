@@ -389,13 +389,14 @@ def test_fp8_split_on_64x128_tiles():
 
 def test_small_m_kernel_above_64_rows_on_small_outputs():
     """Above 64 rows the planner still takes the small-M kernel where the
-    output is small: W4A8 / MXFP4 up to M*N = 2^19 (any K); INT8 up to
-    3*2^18 with M*N*K up to 3*2^29; BF16 / FP16 3*2^18 and 2^30; FP8 2^17 and
-    2^30; K from 1024 (up to 8192 but for W4A8 / MXFP4), M up to 4096, and
-    only when no option is set."""
+    output is small: W4A8 / MXFP4 up to M*N = 2^19 with M*N*K up to 2^31;
+    INT8 up to 3*2^18 with M*N*K up to 3*2^29; BF16 / FP16 3*2^18 and 2^30;
+    FP8 2^17 and 2^30; K from 1024 (up to 8192 but for W4A8 / MXFP4), M up
+    to 4096, and only when no option is set; the K bounds only given a
+    workspace (without one the tiles cannot split K)."""
     for ws in (False, True):
         plan = gp.gemm_plan_ws if ws else gp.gemm_plan
-        for dt, M, N, K, kern in [("w4a8", 128, 1024, 7168, 2), ("w4a8", 2048, 256, 7168, 2), ("w4a8", 2048, 512, 2048, 1),
+        for dt, M, N, K, kern in [("w4a8", 128, 1024, 7168, 2), ("w4a8", 2048, 256, 2048, 2), ("w4a8", 2048, 512, 2048, 1),
                                   ("w4a8", 128, 512, 16384, 2), ("mxfp4", 1024, 512, 2048, 2), ("mxfp4", 4097, 128, 2048, 1),
                                   ("int8", 128, 1024, 4096, 2), ("int8", 128, 256, 512, 1), ("int8", 128, 1024, 16384, 1),
                                   ("int8", 1024, 512, 4096, 1), ("bf16", 128, 2048, 4096, 2), ("bf16", 256, 2048, 4096, 1),
@@ -405,6 +406,13 @@ def test_small_m_kernel_above_64_rows_on_small_outputs():
             assert p["kernel"] == kern, (dt, M, N, K, ws, p)
             if kern == 2:
                 assert p["grid"] == (N // p["tile_n"]) * -(-M // p["tile_m"])
+    # W4A8 / MXFP4 past M*N*K = 2^31: split tiles given a workspace, the small-M kernel without one, or
+    # where the tiles would leave fewer than 128 workgroups (no MXFP4 split tile below 128 rows)
+    for dt, M, N, K in [("w4a8", 2048, 256, 7168), ("w4a8", 128, 4096, 16384), ("mxfp4", 128, 4096, 8192)]:
+        assert gp.gemm_plan(dt, M, N, K)["kernel"] == 2
+        p = gp.gemm_plan_ws(dt, M, N, K)
+        assert p["kernel"] == 1 and p["ksplit"] > 1 and p["grid"] >= 128, (dt, M, N, K, p)
+    assert gp.gemm_plan_ws("mxfp4", 96, 2048, 16384)["kernel"] == 2
     assert gp.gemm_plan("w4a8", 128, 1024, 7168, dict(xcd_swizzle=1))["kernel"] == 1   # an option set: the tile planner
     assert gp.gemm_plan("w4a8", 128, 1024, 7168, dict(kernel=2))["kernel"] == 2
 
