@@ -170,7 +170,9 @@ def test_scheduler_off_parity(dtype, M, N, K, opts):
                                          ("bf16", 32, 2048, 8192), ("fp16", 64, 1024, 16384),
                                          ("w4a8", 24, 1024, 32768),
                                          # 64 x 128 tiles: BF16 / FP16 in 2x the ranges from 64 tiles, INT8 in four
-                                         ("bf16", 256, 2048, 8192), ("fp16", 192, 2048, 8192), ("int8", 192, 2048, 8192)])
+                                         ("bf16", 256, 2048, 8192), ("fp16", 192, 2048, 8192), ("int8", 192, 2048, 8192),
+                                         # 4-bit B in ranges of 2048 K elements (1024 bytes)
+                                         ("mxfp4", 384, 2048, 8192), ("w4a8", 128, 7168, 4096)])
 def test_automatic_split_parity(dtype, M, N, K):
     """The planner's own split (no options) on long-K shapes, every output."""
     import dense_gemm_preshuffle_amd as gp
