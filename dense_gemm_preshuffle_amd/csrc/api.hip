@@ -649,12 +649,15 @@ bool small_m_long_k(int dt, int64_t M, int64_t N, int64_t Kb, const Plan* sm, Pl
 // 2^31 (MXFP4 128 x 4096 x 8192 15.6 us in four ranges of 128 x 128 tiles
 // against 24.9, but 128 x 1024 x 16384 on the small-M kernel 2.5x faster
 // than split tiles; W4A8 128 x 4096 x 16384 18.6 against 33.4); below 1024
-// the two are within the noise of a 3 us launch.
+// the two are within the noise of a 3 us launch for INT8 and FP8, while
+// BF16 / FP16 at K = 512-768 lose on the few tiles of a small output (BF16
+// 111 x 256 x 512 3.0 us on the small-M kernel against 5.6 on 8 tiles,
+// FP16 136 x 896 x 768 5.0 against 7.3).
 // ws: a workspace is at hand, so the tiles may split K (without one the K
 // bounds do not apply: unsplit tiles lose further, e.g. W4A8 384 x 1024 x 7168
 // 34.9 us on 192 unsplit 32 x 64 tiles against 17.6 on the small-M kernel).
 bool small_m_above_64(int dt, int64_t M, int64_t N, int64_t K, bool ws) {
-  if (M <= 64 || M > 4096 || K < 1024) return false;
+  if (M <= 64 || M > 4096 || K < ((dt == DT_BF16 || dt == DT_F16) ? 512 : 1024)) return false;
   const double mn = (double)M * N, mnk = mn * (double)K;
   if (dt == DT_I4 || dt == DT_FP4) return mn <= (double)(1 << 19) && (!ws || mnk <= 2.0 * (double)(1 << 30));
   if (ws && K > 8192) return false;
@@ -717,11 +720,18 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     Plan sm = *p;
     const int rc = choose_split(dt, bits, M, N, Kb, &sm, o);
     if (!o && ws && small_m_long_k(dt, M, N, Kb, rc == GP_OK ? &sm : nullptr, p)) return GP_OK;
-    if (rc == GP_OK || !small_above) {
+    // one wave per workgroup (K splits evenly over no more waves): the tiles,
+    // where one fits (FP8 32 x 576 x 4352 13.5 us on the small-M kernel's
+    // single waves against 9.1 on five 32 x 128 tiles); not for W4A8, whose
+    // single waves beat the tiles (511 x 576 x 11520 33.4 us against 54.1).
+    // 64-byte chunks on many workgroups stay (INT8 24 x 384 x 12544 14.8 us
+    // on 48 workgroups of them against 28.8 on 12 tiles).
+    const bool one_wave = rc == GP_OK && sm.waves == 1 && dt != DT_I4 && no_options(o) && M >= 16 && N >= 64;
+    if ((rc == GP_OK && !one_wave) || (rc != GP_OK && !small_above)) {
       *p = sm;
       return rc;
     }
-    p->kernel = GP_KERNEL_TILE;   // the small-M kernel cannot take it: the tile planner's choice
+    p->kernel = GP_KERNEL_TILE;   // the tile planner's choice (the small-M plan again if no tile fits)
   }
   if (p->kernel == GP_KERNEL_WIDE) return choose_wide(dt, bits, M, N, Kb, p, o);
 
@@ -777,15 +787,18 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     auto_ksplit(dt, M, N, Kb, p);
   }
   // W4A8 / MXFP4 past the M x N x K bound of the small-M rule but on fewer
-  // than 128 workgroups of tiles (no split tile fits, e.g. MXFP4 below 128
-  // rows): the small-M kernel (MXFP4 96 x 2048 x 16384 24.5 us against 44.4
-  // on 24 unsplit 32 x 256 tiles)
+  // than 128 workgroups of split tiles, or 256 unsplit ones (no split tile
+  // fits, e.g. MXFP4 below 128 rows): the small-M kernel (MXFP4 96 x 2048 x
+  // 16384 24.5 us against 44.4 on 24 unsplit 32 x 256 tiles, W4A8 511 x 576
+  // x 11520 33.4 against 54.1 on 144 unsplit 32 x 64 tiles)
   if (no_options(o) && (dt == DT_I4 || dt == DT_FP4) && M > small_m && M <= 4096 && (double)M * N <= (double)(1 << 19) &&
-      tiles_of(*p, M, N) * p->ks < 128) {
+      tiles_of(*p, M, N) * p->ks < (p->ks > 1 ? 128 : 256)) {
     Plan q;
     q.kernel = GP_KERNEL_SPLITK;
     q.Kb = Kb;
-    if (choose_split(dt, bits, M, N, Kb, &q, o) == GP_OK) {
+    // (MXFP4 not on one wave or 64-byte chunks: 76 x 5568 x 15872 44.4 us on
+    // 88 unsplit 64 x 128 tiles against 88.2 on the small-M kernel's 64-byte chunks)
+    if (choose_split(dt, bits, M, N, Kb, &q, o) == GP_OK && (dt == DT_I4 || (q.waves > 1 && q.kch > 64))) {
       *p = q;
       return GP_OK;
     }

@@ -63,19 +63,19 @@
 // whole accumulator array, to scratch memory, at 50x the run time.)
 
 #define GP_SPLITK_I8(Y) Y(DT_I8, 1, 4, 64, 1) Y(DT_I8, 1, 4, 256, 1) Y(DT_I8, 2, 4, 256, 1) Y(DT_I8, 1, 1, 64, 1) \
-  Y(DT_I8, 2, 4, 256, 2) Y(DT_I8, 2, 8, 256, 4)
+  Y(DT_I8, 2, 4, 256, 2) Y(DT_I8, 2, 8, 256, 4) Y(DT_I8, 1, 4, 128, 1) Y(DT_I8, 2, 4, 128, 1) Y(DT_I8, 2, 4, 128, 2)
 #define GP_SPLITK_FP8(Y)                                                                           \
   Y(DT_FP8, 1, 4, 128, 1) Y(DT_FP8, 1, 4, 256, 1) Y(DT_FP8, 1, 4, 512, 1) Y(DT_FP8, 2, 4, 256, 1)             \
   Y(DT_FP8, 2, 4, 512, 1) Y(DT_FP8, 1, 8, 256, 1) Y(DT_FP8, 4, 4, 256, 1) Y(DT_FP8, 2, 8, 256, 1) Y(DT_FP8, 4, 8, 256, 1) \
   Y(DT_FP8, 1, 1, 128, 1) \
   Y(DT_FP8, 2, 4, 256, 2) Y(DT_FP8, 2, 8, 128, 4)
 #define GP_SPLITK_BF16(Y) Y(DT_BF16, 1, 4, 64, 1) Y(DT_BF16, 1, 4, 256, 1) Y(DT_BF16, 2, 4, 256, 1) Y(DT_BF16, 1, 1, 64, 1) \
-  Y(DT_BF16, 2, 4, 256, 2) Y(DT_BF16, 2, 8, 256, 4)
+  Y(DT_BF16, 2, 4, 256, 2) Y(DT_BF16, 2, 8, 256, 4) Y(DT_BF16, 1, 4, 128, 1) Y(DT_BF16, 2, 4, 128, 1) Y(DT_BF16, 2, 4, 128, 2)
 #define GP_SPLITK_FP4(Y) Y(DT_FP4, 1, 4, 64, 1) Y(DT_FP4, 1, 4, 256, 1) Y(DT_FP4, 2, 4, 256, 1) Y(DT_FP4, 1, 1, 64, 1) \
   Y(DT_FP4, 2, 4, 256, 2) Y(DT_FP4, 2, 8, 64, 4) \
   Y(DT_FP4, 1, 4, 128, 1) Y(DT_FP4, 2, 4, 128, 1) Y(DT_FP4, 2, 4, 128, 2)
 #define GP_SPLITK_F16(Y) Y(DT_F16, 1, 4, 64, 1) Y(DT_F16, 1, 4, 256, 1) Y(DT_F16, 2, 4, 256, 1) Y(DT_F16, 1, 1, 64, 1) \
-  Y(DT_F16, 2, 4, 256, 2) Y(DT_F16, 2, 8, 256, 4)
+  Y(DT_F16, 2, 4, 256, 2) Y(DT_F16, 2, 8, 256, 4) Y(DT_F16, 1, 4, 128, 1) Y(DT_F16, 2, 4, 128, 1) Y(DT_F16, 2, 4, 128, 2)
 // W4A8: chunk bytes are bytes of B (the int8 A chunk is twice as long)
 #define GP_SPLITK_I4(Y)                                                                            \
   Y(DT_I4, 1, 4, 64, 1) Y(DT_I4, 1, 4, 128, 1) Y(DT_I4, 1, 4, 256, 1) Y(DT_I4, 2, 4, 64, 1) Y(DT_I4, 2, 4, 128, 1)  \

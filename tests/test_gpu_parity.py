@@ -220,6 +220,12 @@ TILE_CASES = [
     ("int8", 64, 4096, 1024, dict(kernel=2)),
     ("mxfp4", 33, 1024, 7168, dict(kernel=2)),                # 128-byte chunks (7 per wave)
     ("w4a8", 64, 7168, 512, dict(kernel=2)),
+    # 128-byte K chunks (K per wave an odd multiple of 128 bytes), explicit and the planner's
+    ("bf16", 32, 256, 1280, dict(kernel=2, tile_k=64)),
+    ("fp16", 48, 512, 1280, dict(kernel=2, tile_m=32, tile_k=64)),
+    ("int8", 40, 256, 1536, dict(kernel=2, tile_n=32, tile_k=128)),
+    ("bf16", 113, 1024, 1280, dict()),
+    ("fp8", 32, 576, 4352, dict()),                         # one wave would be left: the tile planner
     # above 64 rows, small outputs: the planner's small-M plan (ragged last row blocks)
     ("w4a8", 200, 1024, 2048, dict()),
     ("mxfp4", 640, 256, 2048, dict()),
