@@ -720,13 +720,14 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
     Plan sm = *p;
     const int rc = choose_split(dt, bits, M, N, Kb, &sm, o);
     if (!o && ws && small_m_long_k(dt, M, N, Kb, rc == GP_OK ? &sm : nullptr, p)) return GP_OK;
-    // one wave per workgroup (K splits evenly over no more waves): the tiles,
-    // where one fits (FP8 32 x 576 x 4352 13.5 us on the small-M kernel's
-    // single waves against 9.1 on five 32 x 128 tiles); not for W4A8, whose
-    // single waves beat the tiles (511 x 576 x 11520 33.4 us against 54.1).
-    // 64-byte chunks on many workgroups stay (INT8 24 x 384 x 12544 14.8 us
-    // on 48 workgroups of them against 28.8 on 12 tiles).
-    const bool one_wave = rc == GP_OK && sm.waves == 1 && dt != DT_I4 && no_options(o) && M >= 16 && N >= 64;
+    // FP8 on one wave per workgroup (its 128-byte MFMA steps do not split
+    // evenly over more): the tiles, where one fits (32 x 576 x 4352 13.5 us
+    // on the small-M kernel's single waves against 9.1 on five 32 x 128
+    // tiles). Not the 4-bit types, whose single waves beat the tiles (W4A8
+    // 511 x 576 x 11520 33.4 us against 54.1, MXFP4 39 x 6528 x 7936 23.6
+    // against 26.4), nor 64-byte chunks on many workgroups (INT8 24 x 384 x
+    // 12544 14.8 us on 48 workgroups of them against 28.8 on 12 tiles).
+    const bool one_wave = rc == GP_OK && sm.waves == 1 && dt == DT_FP8 && no_options(o) && M >= 16 && N >= 64;
     if ((rc == GP_OK && !one_wave) || (rc != GP_OK && !small_above)) {
       *p = sm;
       return rc;
