@@ -394,9 +394,10 @@ int choose_split(int dt, int bits, int64_t M, int64_t N, int64_t Kb, Plan* p, co
 // 256 workgroups, or 256 only with a tile smaller than 64 x 128 (each CU then
 // pulls more operand bytes per FLOP from L2). The first tile (in the order
 // of the split variants' list) takes the fewest ranges S (powers of two, up
-// to 16, each range keeping at least 2048 bytes of B's K) that give 256
+// to 16, each range keeping at least 2048 K elements) that give 256
 // workgroups, or the most such ranges if those give at least 128 (128 large
-// tiles measured faster than 256 small ones on BF16). A split costs a round
+// tiles measured faster than 256 small ones on BF16), adjusted per type
+// (in the function). A split costs a round
 // trip of the partial sums at the end of the kernel (a few microseconds), so
 // short K stays unsplit: FP8 512 x 4096 x 4096 measured 15.6 us unsplit and
 // 20.0 us split in two; FP8 256 x 2048 x 16384 39.0 us unsplit (16 x 64
@@ -462,41 +463,38 @@ void auto_ksplit(int dt, int64_t M, int64_t N, int64_t Kb, Plan* p) {
     ksplit_larger_tile(dt, M, N, Kb, p, 4, 3);
     return;
   }
-  // BF16 / FP16 skip their 128 x 256 split tile here for the 64 x 128 one
-  // where fewer than 32 of the large tiles cover the output (from 32 the
-  // large tile held its own: 256 x 4096 x 16384 62.0 us against 63.3, 384 x
-  // 4096 x 8192 43.5 against 49.8), and from 64 small tiles take twice the
-  // ranges up to 512 workgroups (one
-  // MI355X, M 128-384, N 1024-4096, K 4096-16384): BF16 128 x 2048 x 16384
-  // 32.4 us on 64 x 128 in eight ranges against 54.0 on 128 x 256 in eight,
-  // 384 x 2048 x 16384 52.2 in four against 83.9, 256 x 4096 x 8192 37.2 in
-  // four (512 workgroups) against 46.4 in two, 128 x 4096 x 8192 28.4 in
-  // eight against 29.9 in four; not on 128 workgroups, where 16 x 64 tiles
-  // in more took less (FP16 80 x 512 x 16384 15.9 us on 320 against 23.1,
-  // 256 x 1024 x 7168 21.5 on 512 against 24.9). INT8 on its 64 x 128 tile
-  // as FP8 (below):
-  // 192 x 2048 x 4096 10.5 us in four against 11.4, 384 x 1024 x 16384 19.5
-  // in four (192 workgroups) against 23.2 in eight (384).
-  // FP8 on its 64 x 128 tile (one MI355X, 266 shapes, M 80-1024, K 4096-16384,
-  // against the rule alone): four ranges where the tiles number 48 to 64 and
-  // K holds at least 4096 bytes (1024 or more per range), e.g. 128 x 3072 x
-  // 4096 10.6 us against 12.7 on 16 x 64 tiles in two, 256 x 2048 x 7168
-  // 13.7 against 16.5 in two; and no more than 256 workgroups where halving
-  // S keeps at least 168 of them, e.g. 160 x 4096 x 8192 18.7 us in 192
-  // workgroups against 22.4 in 384, 128 x 7168 x 8192 22.2 in 224 against
-  // 24.9 in 448, 384 x 7168 x 4096 unsplit 21.5 against 26.0 in 672 (but 384
-  // x 3072 x 16384 41.4 in 288 against 48.4 in 144, so not below 168), nor
-  // below two ranges past 8192 columns of K (160 x 7168 x 16384 50.9 us in
-  // two against 52.7 unsplit; W4A8 192 x 7168 x 16384 34.9 against 41.8); four ranges not where the 64-row tiles cover more
-  // than 1.5 M (80 x 3072 x 4096 10.5 against 9.4). Not for 16 x 64 tiles,
-  // whose splits into 320-384 workgroups measured faster than half as many
-  // (192 x 1024 x 7168 11.0 against 12.2).
-  // at least 2048 K elements per range: 2048 bytes of B, 1024 for 4-bit B
-  // (MXFP4 384 x 2048 x 8192 16.2 us in four ranges against 23.8 unsplit on
-  // 32 x 256 tiles; W4A8 128 x 7168 x 4096 11.6 in two against 14.2)
-  // MXFP4 / W4A8 take the 256-workgroup rule below as well (MXFP4 192 x 3072
-  // x 16384 22.4 us on 192 workgroups against 29.5 on 384, W4A8 128 x 7168 x
-  // 8192 16.8 on 224 against 19.8 on 448).
+  // Otherwise the first split tile (in the list's order) that reaches at
+  // least 128 workgroups, in the fewest power-of-two ranges S that reach 256,
+  // each range holding at least 2048 K elements (2048 bytes of B, 1024 of
+  // 4-bit B: MXFP4 384 x 2048 x 8192 16.2 us in four ranges against 23.8
+  // unsplit on 32 x 256 tiles, W4A8 128 x 7168 x 4096 11.6 in two against
+  // 14.2). Adjustments by type, each measured on one MI355X:
+  // - BF16 / FP16 skip their 128 x 256 tile while fewer than 32 of them
+  //   cover the output, for 64 x 128 (128 x 2048 x 16384 32.4 us in eight
+  //   ranges against 54.0 on 128 x 256 in eight, 384 x 2048 x 16384 52.2 in
+  //   four against 83.9; from 32 the large tile held its own: 256 x 4096 x
+  //   16384 62.0 against 63.3, 384 x 4096 x 8192 43.5 against 49.8); from 64
+  //   of the small tiles they take twice the ranges, up to 512 workgroups
+  //   (256 x 4096 x 8192 37.2 in four against 46.4 in two, 128 x 4096 x 8192
+  //   28.4 in eight against 29.9 in four); and they leave 64 x 128 below 144
+  //   workgroups for 16 x 64 tiles in more (FP16 80 x 512 x 16384 15.9 on
+  //   320 against 23.1 on 128, 256 x 1024 x 7168 21.5 on 512 against 24.9).
+  // - FP8 / INT8 on 64 x 128: four ranges where 48 to 64 tiles cover the
+  //   output, from 4096 bytes of K and with the 64-row tiles covering at
+  //   most 1.5 M (FP8 128 x 3072 x 4096 10.6 us against 12.7 on 16 x 64
+  //   tiles in two, 256 x 2048 x 7168 13.7 against 16.5; INT8 192 x 2048 x
+  //   4096 10.5 against 11.4; but FP8 80 x 3072 x 4096 10.5 against 9.4).
+  // - FP8 / INT8 on 64 x 128 and MXFP4 / W4A8 on 64- and 128-row tiles: no
+  //   more than 256 workgroups where halving S keeps at least 168 of them
+  //   (FP8 160 x 4096 x 8192 18.7 us on 192 against 22.4 on 384, 384 x 7168
+  //   x 4096 unsplit 21.5 against 26.0 on 672; INT8 384 x 1024 x 16384 19.5
+  //   on 192 against 23.2 on 384; MXFP4 192 x 3072 x 16384 22.4 against
+  //   29.5; W4A8 128 x 7168 x 8192 16.8 on 224 against 19.8 on 448), not
+  //   below 168 (FP8 384 x 3072 x 16384 41.4 us on 288 against 48.4 on 144)
+  //   and not below two ranges past 8192 K elements (FP8 160 x 7168 x 16384
+  //   50.9 us in two against 52.7 unsplit; W4A8 192 x 7168 x 16384 34.9
+  //   against 41.8). Not on 16 x 64 tiles, whose splits into 320-384
+  //   workgroups beat half as many (FP8 192 x 1024 x 7168 11.0 against 12.2).
   const int64_t min_kb = (dt == DT_FP4 || dt == DT_I4) ? 1024 : 2048;
   int best = -1, best_s = 0;
   for (int i = 0; i < (int)(sizeof(kKSplit) / sizeof(kKSplit[0])); ++i) {
@@ -719,7 +717,7 @@ int make_plan(int in_dtype, int64_t M, int64_t N, int64_t K, const gemm_opts* o,
   if (p->kernel == GP_KERNEL_SPLITK) {
     Plan sm = *p;
     const int rc = choose_split(dt, bits, M, N, Kb, &sm, o);
-    if (!o && ws && small_m_long_k(dt, M, N, Kb, rc == GP_OK ? &sm : nullptr, p)) return GP_OK;
+    if (no_options(o) && ws && small_m_long_k(dt, M, N, Kb, rc == GP_OK ? &sm : nullptr, p)) return GP_OK;
     // FP8 on one wave per workgroup (its 128-byte MFMA steps do not split
     // evenly over more): the tiles, where one fits (32 x 576 x 4352 13.5 us
     // on the small-M kernel's single waves against 9.1 on five 32 x 128

@@ -358,6 +358,19 @@ def test_small_m_row_blocks(dtype):
     assert q["tile_m"] == 16
 
 
+def test_zero_filled_options_plan_like_null():
+    """A zero-filled gemm_opts is all-automatic, as NULL is: the same plan on
+    shapes that take each of the planner's rules (16-64 row K split, small-M
+    kernel above 64 rows, row blocks, 4-bit fallback, the tile splits)."""
+    shapes = [("fp8", 16, 2048, 16384), ("fp8", 48, 1024, 32768), ("bf16", 64, 1024, 16384), ("w4a8", 128, 1024, 7168),
+              ("int8", 128, 1024, 4096), ("fp8", 64, 2048, 4096), ("mxfp4", 96, 2048, 16384), ("fp8", 128, 3072, 4096),
+              ("bf16", 256, 2048, 8192), ("fp16", 192, 2048, 8192), ("fp8", 32, 576, 4352), ("bf16", 113, 1024, 1280),
+              ("fp8", 16, 7168, 2048), ("bf16", 8192, 8192, 8192)]
+    for dt, M, N, K in shapes:
+        assert gp.gemm_plan_ws(dt, M, N, K) == gp.gemm_plan_ws(dt, M, N, K, {}), (dt, M, N, K)
+        assert gp.gemm_plan(dt, M, N, K) == gp.gemm_plan(dt, M, N, K, {}), (dt, M, N, K)
+
+
 def test_half_and_int8_split_on_64x128_tiles():
     """BF16 / FP16 split 64 x 128 tiles (not 128 x 256 where fewer than 32
     of those cover the output), in twice the ranges from 64 tiles up to 512
