@@ -30,7 +30,10 @@
  *     layout); FP8, MXFP4 and W4A8 also need K % 128 == 0 (whole MFMA K
  *     steps); M is free. When the tile does not divide M or N, the edge
  *     tiles overlap their neighbours inside M x N (no padding is needed);
- *     N below one tile or a short K runs on the small-M kernel.
+ *     N below one tile or a short K runs on the small-M kernel. Which kernel
+ *     and tile a call runs is the planner's choice unless gemm_opts says
+ *     otherwise (gemm_plan / gemm_plan_ws report it): the small-M kernel up
+ *     to 64 rows and, above, on small outputs; the tile kernel otherwise.
  *   - Thread-local state: the HIP status behind the last GP_EHIP and the
  *     runtime call that returned it (gemm_last_hip_error, gemm_last_hip_call).
  *   - Alignment: every data pointer must be 16-byte aligned.
@@ -231,10 +234,11 @@ int gemm_f16(const void* a, const void* b_shuf, void* c, int64_t M, int64_t N, i
  *   c        device [M][N] bf16:
  *     C[m][n] = bf16_rne((acc[m][n] * scale_a[m]) * scale_b[n]),
  * acc = sum_k A[m][k] B[n][k] exact in int32. K % 128 == 0 and K <= 65536.
- * M <= 64 runs on the small-M kernel (GP_KERNEL_SPLITK: 4 or 8 waves
- * split K where K % 512 == 0, one wave otherwise); larger M on the tile
- * kernel, which widens each INT4 piece of B to int8 in registers for two
- * int8 MFMAs.
+ * M <= 64, and larger M on small outputs (M * N <= 2^19; with a workspace
+ * also M * N * K <= 2^31), run on the small-M kernel (GP_KERNEL_SPLITK: 4
+ * or 8 waves split K where their share divides into whole chunks, one wave
+ * otherwise); other shapes on the tile kernel, which widens each INT4 piece
+ * of B to int8 in registers for two int8 MFMAs.
  */
 int gemm_w4a8(const void* a, const void* b_shuf, const float* scale_a, const float* scale_b, void* c,
               int64_t M, int64_t N, int64_t K, const gemm_opts* opts, void* stream);
