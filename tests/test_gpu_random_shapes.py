@@ -69,3 +69,33 @@ def test_planner_choice_parity(dtype, M, N, K):
         outs.append(workload.to_host(c))
     assert np.array_equal(outs[0], outs[1]), "results differ between two calls"
     check(dtype, host, outs[0], rows=rows, ref=ref)
+
+
+_ACTS = ("relu", "silu", "gelu")
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [s for s in _shapes() if s[0] != "int8"], ids=lambda v: str(v))
+def test_planner_choice_fused_epilogue(dtype, M, N, K):
+    """The same shapes with a bias and an activation (the floating-point
+    types), given a workspace: every planner path runs the fused epilogue,
+    after the partial sums where it splits K."""
+    import torch
+
+    import dense_gemm_preshuffle_amd as gp
+    from dense_gemm_preshuffle_amd import workload
+
+    act = _ACTS[(M + N + K) % 3]
+    plan = gp.gemm_plan_ws(dtype, M, N, K)
+    say(f"random fused {act} {dtype} {M}x{N}x{K}: kernel {plan['kernel']} tile {plan['tile_m']}x{plan['tile_n']} "
+        f"ksplit {plan['ksplit']}")
+    host = workloads.make_inputs(dtype, M, N, K, seed=M * 13 + N + K * 3, bias=True)
+    p = workload.prepare(dtype, workload.to_device(dtype, host))
+    p["workspace"] = gp.workspace(dtype, M, N, K, None)
+    outs = []
+    for _ in range(2):
+        c = workload.run(dtype, p, act=act)
+        torch.cuda.synchronize()
+        outs.append(workload.to_host(c))
+    assert np.array_equal(outs[0], outs[1]), "results differ between two calls"
+    rows = _rows(M, M * 3 + N + K)
+    check(dtype, host, outs[0], rows=rows, ref=oracle.gemm(dtype, host, rows, None, act=act), act=act)
